@@ -1,0 +1,379 @@
+"""Plain, slow, obviously correct CPU oracle (TEST INFRASTRUCTURE ONLY).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may import this module.  It shares no code with the HIP path.
+
+Source of every definition: the page "mlx_streaming/core/cache/quant_kv.py"
+(sparkle), sections "SO(4) block rotation" (``_quat_left``,
+``_quat_right_conj``, ``build_block_so4``, ``rotate_last``), "asymmetric
+quantized KV cache (K4/V3)" (``_packed_words``, ``AsymmetricQuantizedKVCache``:
+``_init_quant``, ``update_and_fetch``, ``trim``) and "asymmetric quantized
+SDPA" (``asym_quantized_sdpa``); and the page "mlx_streaming/mtp/kv_cache.py",
+``commit_verified_prefix``.  The quantizer formula (scale = (max-min)/(2^bits-1),
+bias = min, code = clip(round-half-even((x-bias)/scale))) and the little-endian
+bit-stream packing are the ones the benchmark spec fixes; the pages call
+``mx.quantize`` without defining it.
+
+Readings taken where the pages leave a step open (each also listed in the
+design notes):
+  R1  the right-hand block matrix is used exactly as printed (it equals the
+      transpose of the left-multiplication matrix);
+  R2  quaternions are normalised and multiplied in fp64 and the block is
+      rounded once to fp32 (the page does this in float32 through numpy);
+  R3  rotations are fp64 sums of exact products in a fixed order, rounded
+      once to fp32, and the rotated K/V are not rounded to the input dtype;
+  R4  scale and bias are stored in the input dtype, and the codes are computed
+      against the stored (rounded) scale and bias;
+  R5  a zero scale divides by 1 (codes 0, dequant = bias);
+  R6  attention accumulates in fp64 here (fp32 on the GPU) and returns fp32.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+GROUP = 64
+STEP = 256  # cache growth step, AsymmetricQuantizedKVCache.step
+
+
+# ---------------------------------------------------------------- rotation --
+
+def quat_left(q) -> np.ndarray:
+    """4x4 left-multiplication matrix of quaternion q = (w, x, y, z), entries as
+    printed for ``_quat_left`` (page quant_kv.py, "SO(4) block rotation")."""
+    w, x, y, z = (float(v) for v in q)
+    return np.array([
+        [w, -x, -y, -z],
+        [x, w, -z, y],
+        [y, z, w, -x],
+        [z, -y, x, w],
+    ], dtype=np.float64)
+
+
+def quat_right_conj(q) -> np.ndarray:
+    """4x4 matrix printed for ``_quat_right_conj`` (same page and section).
+
+    Reading R1: the entries are taken as printed.  They equal
+    ``quat_left(q).T``; the page's docstring describes a right
+    multiplication by conj(q), which these entries do not implement."""
+    w, x, y, z = (float(v) for v in q)
+    return np.array([
+        [w, x, y, z],
+        [-x, w, z, -y],
+        [-y, -z, w, x],
+        [-z, y, -x, w],
+    ], dtype=np.float64)
+
+
+def normalize_quat(a) -> np.ndarray:
+    """a / |a| in fp64: squares summed left to right, correctly rounded sqrt
+    and division (reading R2)."""
+    a0, a1, a2, a3 = (float(v) for v in a)
+    n = math.sqrt(((a0 * a0 + a1 * a1) + a2 * a2) + a3 * a3)
+    if n == 0.0:
+        raise ValueError("zero-norm quaternion draw")
+    return np.array([a0 / n, a1 / n, a2 / n, a3 / n], dtype=np.float64)
+
+
+def matmul4_ordered(A: np.ndarray, Bm: np.ndarray) -> np.ndarray:
+    """4x4 fp64 product with each entry summed over k = 0..3 in that order."""
+    C = np.zeros((4, 4), dtype=np.float64)
+    for i in range(4):
+        for j in range(4):
+            s = float(A[i, 0]) * float(Bm[0, j])
+            for k in range(1, 4):
+                s = s + float(A[i, k]) * float(Bm[k, j])
+            C[i, j] = s
+    return C
+
+
+def rotation_blocks(draws: np.ndarray) -> np.ndarray:
+    """Blocks of the block-diagonal rotation (``build_block_so4``).
+
+    draws: float32 ``[D/4, 2, 4]`` (left draw, right draw per block, in the
+    page's draw order).  Returns float32 ``[D/4, 4, 4]``:
+    block b = quat_left(qL) @ quat_right_conj(qR), qL/qR the normalised draws,
+    computed in fp64 and rounded once to fp32 (reading R2)."""
+    draws = np.asarray(draws, dtype=np.float32)
+    if draws.ndim != 3 or draws.shape[1:] != (2, 4):
+        raise ValueError("draws must be [D/4, 2, 4]")
+    out = np.empty((draws.shape[0], 4, 4), dtype=np.float32)
+    for b in range(draws.shape[0]):
+        qL = normalize_quat(draws[b, 0])
+        qR = normalize_quat(draws[b, 1])
+        out[b] = matmul4_ordered(quat_left(qL), quat_right_conj(qR)).astype(np.float32)
+    return out
+
+
+def dense_rotation(blocks: np.ndarray) -> np.ndarray:
+    """The dense D x D block-diagonal matrix M (fp64) holding ``blocks`` on its
+    diagonal, block b at rows/cols [4b, 4b+4) (``build_block_so4``)."""
+    nb = blocks.shape[0]
+    M = np.zeros((4 * nb, 4 * nb), dtype=np.float64)
+    for b in range(nb):
+        M[4 * b:4 * b + 4, 4 * b:4 * b + 4] = blocks[b]
+    return M
+
+
+def rotate(x: np.ndarray, blocks: np.ndarray) -> np.ndarray:
+    """Row-vector rotation y = x @ M (``rotate_last``), reading R3:
+    y[4b+j] = fp32(((x0*B[0,j] + x1*B[1,j]) + x2*B[2,j]) + x3*B[3,j]) in fp64,
+    x_i = x[4b+i].  ``x`` holds fp16/bf16/fp32 values; returns float32."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    Bm = np.asarray(blocks, dtype=np.float64)
+    xr = x.reshape(x.shape[:-1] + (D // 4, 4))
+    y = xr[..., 0, None] * Bm[:, 0, :]
+    y = y + xr[..., 1, None] * Bm[:, 1, :]
+    y = y + xr[..., 2, None] * Bm[:, 2, :]
+    y = y + xr[..., 3, None] * Bm[:, 3, :]
+    return y.reshape(x.shape).astype(np.float32)
+
+
+def inverse_rotate(y: np.ndarray, blocks: np.ndarray) -> np.ndarray:
+    """z = y @ M^T (the inverse rotation of the attention output, page
+    quant_kv.py design notes and ``asym_quantized_sdpa`` docstring):
+    z[4b+i] = fp32(sum_{j=0..3} y[4b+j]*B[i,j]) in fp64, j in order."""
+    y = np.asarray(y, dtype=np.float64)
+    D = y.shape[-1]
+    Bm = np.asarray(blocks, dtype=np.float64)
+    yr = y.reshape(y.shape[:-1] + (D // 4, 4))
+    z = yr[..., 0, None] * Bm[:, :, 0]
+    z = z + yr[..., 1, None] * Bm[:, :, 1]
+    z = z + yr[..., 2, None] * Bm[:, :, 2]
+    z = z + yr[..., 3, None] * Bm[:, :, 3]
+    return z.reshape(y.shape).astype(np.float32)
+
+
+# --------------------------------------------------------------- quantizer --
+
+def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float32 values to ``dtype`` ("bf16" or "f16"), round-half-even,
+    and return them as float32 (exact).  bf16: keep the top 16 bits of the
+    fp32 encoding after adding half an ulp (ties to even); f16: numpy's cast."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16).astype(np.float32)
+    if dtype != "bf16":
+        raise ValueError(dtype)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) & np.uint64(0xFFFF0000)).astype(np.uint32)
+    return r.view(np.float32)
+
+
+def quantize(y: np.ndarray, bits: int, dtype: str, group: int = GROUP):
+    """Group-wise asymmetric affine quantizer (``mx.quantize`` as called in
+    ``update_and_fetch``; formula fixed by the benchmark spec).
+
+    y: float32 ``[..., D]``.  For each group of ``group`` consecutive values:
+      mn, mx = min, max                                   (exact)
+      s32    = fp32(fp32(mx - mn) / fp32(2^bits - 1))
+      s, b   = s32 and mn rounded to ``dtype``            (reading R4)
+      code   = clip(rint(fp32(fp32(y - b) / (s or 1))), 0, 2^bits - 1)   (R5)
+    Returns (codes uint8 [..., D], scales float32 [..., D/group],
+    biases float32 [..., D/group]); scales/biases hold ``dtype`` values."""
+    y = np.asarray(y, dtype=np.float32)
+    D = y.shape[-1]
+    if D % group:
+        raise ValueError("head_dim must be a multiple of the group size")
+    g = y.reshape(y.shape[:-1] + (D // group, group))
+    mn = g.min(axis=-1)
+    mx = g.max(axis=-1)
+    levels = np.float32(2 ** bits - 1)
+    s32 = (mx - mn) / levels
+    s = round_to_dtype(s32, dtype)
+    b = round_to_dtype(mn, dtype)
+    sdiv = np.where(s == np.float32(0), np.float32(1), s).astype(np.float32)
+    q = (g - b[..., None]) / sdiv[..., None]
+    codes = np.clip(np.rint(q), 0, 2 ** bits - 1).astype(np.uint8)
+    return codes.reshape(y.shape), s, b
+
+
+def dequantize(codes: np.ndarray, scales: np.ndarray, biases: np.ndarray,
+               group: int = GROUP) -> np.ndarray:
+    """x_hat = code * scale + bias of the code's group, in fp64."""
+    c = np.asarray(codes, dtype=np.float64)
+    D = c.shape[-1]
+    cg = c.reshape(c.shape[:-1] + (D // group, group))
+    x = cg * np.asarray(scales, np.float64)[..., None] + np.asarray(biases, np.float64)[..., None]
+    return x.reshape(c.shape)
+
+
+# ------------------------------------------------------------------ packing --
+
+def packed_words(dim: int, bits: int) -> int:
+    """uint32 words per packed row: dim*bits//32 (``_packed_words``)."""
+    return dim * bits // 32
+
+
+def pack(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Little-endian bit stream: bit t of code j sits at stream position
+    p = bits*j + t, i.e. bit (p mod 32) of word p // 32."""
+    c = np.asarray(codes, dtype=np.uint32)
+    D = c.shape[-1]
+    if (D * bits) % 32:
+        raise ValueError("row does not fill whole words")
+    stream = (c[..., :, None] >> np.arange(bits, dtype=np.uint32)) & np.uint32(1)
+    stream = stream.reshape(c.shape[:-1] + (D * bits // 32, 32)).astype(np.uint64)
+    words = (stream << np.arange(32, dtype=np.uint64)).sum(axis=-1)
+    return words.astype(np.uint32)
+
+
+def unpack(words: np.ndarray, bits: int, dim: int) -> np.ndarray:
+    """Inverse of ``pack``."""
+    w = np.asarray(words, dtype=np.uint32)
+    stream = ((w[..., :, None] >> np.arange(32, dtype=np.uint32)) & np.uint32(1))
+    stream = stream.reshape(w.shape[:-1] + (w.shape[-1] * 32,))[..., :dim * bits]
+    stream = stream.reshape(w.shape[:-1] + (dim, bits)).astype(np.uint32)
+    codes = (stream << np.arange(bits, dtype=np.uint32)).sum(axis=-1)
+    return codes.astype(np.uint8)
+
+
+def quantize_rows(x: np.ndarray, blocks, bits: int, dtype: str):
+    """Rotate (``blocks`` may be None = identity) then quantize and pack rows.
+    Returns (words uint32, scales float32, biases float32)."""
+    y = np.asarray(x, dtype=np.float32) if blocks is None else rotate(x, blocks)
+    codes, s, b = quantize(y, bits, dtype)
+    return pack(codes, bits), s, b
+
+
+# -------------------------------------------------------------------- cache --
+
+def required_capacity(capacity: int, offset: int, n: int) -> int:
+    """Capacity after ``update_and_fetch`` prepares room for n more rows
+    (page quant_kv.py, ``AsymmetricQuantizedKVCache.update_and_fetch``, step 256):
+    nothing changes while offset + n fits; otherwise ceil(n/256)*256 rows are
+    added, after first cutting the buffer back to ``offset`` when ``offset``
+    is not a multiple of 256.  ``capacity == 0`` means no buffer yet."""
+    if n < 0 or offset < 0 or offset > capacity:
+        raise ValueError("bad capacity/offset/n")
+    if capacity > 0 and offset + n <= capacity:
+        return capacity
+    new_steps = (STEP + n - 1) // STEP * STEP
+    if capacity == 0:
+        return new_steps
+    base = offset if offset % STEP != 0 else capacity
+    return base + new_steps
+
+
+class QuantKVCache:
+    """Oracle of ``AsymmetricQuantizedKVCache`` (page quant_kv.py): six arrays
+    (K words/scales/biases, V words/scales/biases) of shape [B, H, cap, .],
+    ``offset`` rows valid.  Rows beyond ``offset`` are never read."""
+
+    def __init__(self, k_bits: int = 4, v_bits: int = 3, dtype: str = "bf16"):
+        self.k_bits, self.v_bits, self.dtype = k_bits, v_bits, dtype
+        self.offset = 0
+        self.arrays = None  # dict name -> ndarray
+
+    @property
+    def capacity(self) -> int:
+        return 0 if self.arrays is None else self.arrays["kw"].shape[2]
+
+    def _grow(self, B, H, D, n):
+        cap = required_capacity(self.capacity, self.offset, n)
+        if cap == self.capacity:
+            return
+        shapes = {
+            "kw": (packed_words(D, self.k_bits), np.uint32),
+            "ks": (D // GROUP, np.float32), "kb": (D // GROUP, np.float32),
+            "vw": (packed_words(D, self.v_bits), np.uint32),
+            "vs": (D // GROUP, np.float32), "vb": (D // GROUP, np.float32),
+        }
+        new = {}
+        for name, (w, dt) in shapes.items():
+            a = np.zeros((B, H, cap, w), dtype=dt)
+            if self.arrays is not None:
+                keep = min(self.offset if self.offset % STEP else self.capacity, cap)
+                a[:, :, :keep] = self.arrays[name][:, :, :keep]
+            new[name] = a
+        self.arrays = new
+
+    def append(self, k: np.ndarray, v: np.ndarray, blocks) -> None:
+        """``update_and_fetch``: rotate k/v (reading R3), quantize, write rows
+        [offset, offset+n) and advance ``offset``."""
+        B, H, n, D = k.shape
+        self._grow(B, H, D, n)
+        kw, ks, kb = quantize_rows(k, blocks, self.k_bits, self.dtype)
+        vw, vs, vb = quantize_rows(v, blocks, self.v_bits, self.dtype)
+        o = self.offset
+        for name, val in (("kw", kw), ("ks", ks), ("kb", kb), ("vw", vw), ("vs", vs), ("vb", vb)):
+            self.arrays[name][:, :, o:o + n] = val
+        self.offset = o + n
+
+    def trim(self, n: int) -> int:
+        """``trim``: n' = min(offset, n); offset -= n'; returns n'."""
+        if n < 0:
+            raise ValueError("trim count must be >= 0")
+        n = min(self.offset, n)
+        self.offset -= n
+        return n
+
+    def dequant_kv(self, b: int, h: int):
+        """Dequantised K and V rows [0, offset) of (b, h), fp64 [offset, D]."""
+        a, o = self.arrays, self.offset
+        D = a["ks"].shape[-1] * GROUP
+        kc = unpack(a["kw"][b, h, :o], self.k_bits, D)
+        vc = unpack(a["vw"][b, h, :o], self.v_bits, D)
+        return (dequantize(kc, a["ks"][b, h, :o], a["kb"][b, h, :o]),
+                dequantize(vc, a["vs"][b, h, :o], a["vb"][b, h, :o]))
+
+
+def commit_verified_prefix(cache: QuantKVCache, verified_len: int, accepted_len: int) -> int:
+    """Trimmable branch of ``commit_verified_prefix`` (page mtp/kv_cache.py):
+    ValueError when accepted_len > verified_len, else trim the rejected suffix."""
+    rejected = verified_len - accepted_len
+    if rejected < 0:
+        raise ValueError("accepted_len cannot exceed verified_len")
+    return cache.trim(rejected) if rejected else 0
+
+
+# ---------------------------------------------------------------- attention --
+
+def attention_row(q_row: np.ndarray, khat: np.ndarray, vhat: np.ndarray, n_keys: int,
+                  scale: float, blocks) -> np.ndarray:
+    """One query row of ``asym_quantized_sdpa`` followed by the inverse rotation.
+
+    q_row: [D] input-dtype values (unrotated); khat/vhat: fp64 dequantised
+    rows; keys [0, n_keys) are visible.  q' = rotate(q) (fp32), then in fp64:
+    scores = (q' * scale) . khat_t, max-subtracted softmax, o = sum p_t vhat_t;
+    returns inverse_rotate(fp32(o)) (or fp32(o) when blocks is None)."""
+    qr = np.asarray(q_row, np.float32) if blocks is None else rotate(q_row, blocks)
+    qs = qr.astype(np.float64) * float(scale)
+    sc = khat[:n_keys] @ qs
+    m = sc.max()
+    p = np.exp(sc - m)
+    o = (p @ vhat[:n_keys]) / p.sum()
+    o32 = o.astype(np.float32)
+    return o32 if blocks is None else inverse_rotate(o32, blocks)
+
+
+def attention(q: np.ndarray, cache: QuantKVCache, scale: float, causal: bool, blocks,
+              rows=None) -> np.ndarray:
+    """Fused decode/verify attention over the cache (``asym_quantized_sdpa``):
+    q: [B, Hq, L, D]; q head h reads kv head h // (Hq/Hkv); with ``causal``,
+    row i of the L-block sees keys t <= offset - L + i.  Returns float32
+    [B, Hq, L, D] (only ``rows`` = iterable of (b, h, i) are filled if given,
+    the rest stay NaN)."""
+    B, Hq, L, D = q.shape
+    Hkv = cache.arrays["kw"].shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    n_rep = Hq // Hkv
+    T = cache.offset
+    if L < 1 or L > T:
+        raise ValueError("need 1 <= L <= offset")
+    out = np.full((B, Hq, L, D), np.nan, dtype=np.float32)
+    if rows is None:
+        rows = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(L)]
+    deq = {}
+    for (b, h, i) in rows:
+        kvh = h // n_rep
+        if (b, kvh) not in deq:
+            deq = {(b, kvh): cache.dequant_kv(b, kvh)}
+        khat, vhat = deq[(b, kvh)]
+        n_keys = T - L + i + 1 if causal else T
+        out[b, h, i] = attention_row(q[b, h, i], khat, vhat, n_keys, scale, blocks)
+    return out
