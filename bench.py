@@ -1,0 +1,238 @@
+"""Benchmark of the quantized-KV decode step on one MI355X.
+
+One step is one decode step of the whole path on the batched-decode workload
+(B=8, 16 q heads / 2 kv heads, head_dim 256, T=32768 cached tokens, bf16,
+group 64, K 4-bit / V 3-bit): the current token's K/V rows are rotated,
+quantized, packed and appended at row T-1 (so attention sees T tokens), the
+fused attention of the rotated query over the packed cache runs with the
+causal mask at the offset and the inverse rotation of its output, and the
+token is trimmed again so every step sees the same T.  The rotation blocks
+are built once before timing.
+
+Inputs are synthetic (``workloads``), resident in HBM before timing.  The
+cache is replicated (default 4 copies, 512 MiB) and the steps cycle through
+the copies so that the 256 MB Infinity Cache cannot serve the 128 MiB a step
+reads.
+
+Prints ONE JSON line: ``value`` = effective HBM GB/s of the step (algorithmic
+bytes / step time), plus tokens/s, the roofline of the attention kernel
+(HIP events around its launches on the stream it runs on) and the CPU oracle
+timed on a bounded sample of the same work.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+ATTN_SRC = os.path.join(ROOT, "rotated_bit_quantized_amd", "csrc", "rbq_attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_batched_decode.json")
+
+
+def algorithmic_bytes(w, T: int) -> dict:
+    """Bytes one step must move at minimum.  Per cached token per kv head:
+    K 32 words (128 B) + 4 bf16 scales + 4 bf16 biases, V 24 words (96 B) +
+    4 + 4 bf16 = 256 B.  Plus q (bf16) in and the fp32 output, and for the
+    appended token 2 x 512 B of bf16 K/V read and 256 B written."""
+    cache = w.B * w.Hkv * T * 256
+    q = w.B * w.Hq * w.L * w.D * 2
+    out = w.B * w.Hq * w.L * w.D * 4
+    append = w.B * w.Hkv * 1 * (2 * w.D * 2 + 256)
+    return {"attn": cache + q + out, "append": append, "step": cache + q + out + append}
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(per_launch_alg: float):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != source_hash(ATTN_SRC):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, seconds: float = 12.0) -> dict:
+    """The oracle (as it is) on one (batch, kv head) slab of the same workload,
+    repeated for about ``seconds``: dequantise the slab's T packed K/V rows and
+    attend its query rows over them, one thread.  The oracle's own packed
+    rows of the slab are built first (not timed)."""
+    from threadpoolctl import threadpool_limits
+
+    import workloads as W
+    from oracle import rbq_oracle as O
+
+    blocks = O.rotation_blocks(W.rotation_draws(W.ROTATION_SEED, w.D))
+    q = W.queries(w).float().numpy()
+    n_rep = w.Hq // w.Hkv
+    # slab (b=0, kv head 0) of the workload's fill, quantized by the oracle (not timed)
+    rk = np.random.default_rng([w.cid, W.STREAM_K])
+    rv = np.random.default_rng([w.cid, W.STREAM_V])
+    k = W.to_dtype(rk.standard_normal((w.T, w.D)), w.dtype).float().numpy()
+    v = W.to_dtype(rv.standard_normal((w.T, w.D)), w.dtype).float().numpy()
+    kw, ks, kb = O.quantize_rows(k, blocks, 4, w.dtype)
+    vw, vs, vb = O.quantize_rows(v, blocks, 3, w.dtype)
+    done_slabs, elapsed = 0, 0.0
+    with threadpool_limits(limits=1):
+        while elapsed < seconds:
+            t0 = time.perf_counter()
+            khat = O.dequantize(O.unpack(kw, 4, w.D), ks, kb)
+            vhat = O.dequantize(O.unpack(vw, 3, w.D), vs, vb)
+            for r in range(n_rep):
+                O.attention_row(q[0, r, 0], khat, vhat, w.T, 1 / 16, blocks)
+            elapsed += time.perf_counter() - t0
+            done_slabs += 1
+    per_slab_bytes = w.T * 256 + n_rep * w.D * (2 + 4)
+    return {
+        "value": round(done_slabs * per_slab_bytes / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done_slabs} passes over one (batch, kv head) slab: dequantise "
+                  f"{w.T} packed K/V rows and attend {n_rep} query rows, numpy fp64, "
+                  f"1 thread, {elapsed:.1f} s",
+        "tokens_per_s": round(done_slabs / (w.B * w.Hkv) * w.B / elapsed, 4),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--splits", type=int, default=0, help="key splits (0 = automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        return 2
+
+    import rotated_bit_quantized_amd as rbq
+    from rotated_bit_quantized_amd import capi
+    import workloads as W
+
+    w = W.WORKLOADS[3]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rot = rbq.build_block_so4(w.D, W.ROTATION_SEED, dev)
+
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    k, v = W.fill_tokens(w)
+    q = W.queries(w).to(dev)
+    k_new = k[:, :, w.T - 1:].contiguous().to(dev)
+    v_new = v[:, :, w.T - 1:].contiguous().to(dev)
+    base = rbq.RotatedQuantKVCache(w.B, w.Hkv, dtype=w.torch_dtype, device=dev, rot=rot)
+    base.append(k[:, :, :w.T - 1].contiguous().to(dev), v[:, :, :w.T - 1].contiguous().to(dev))
+    del k, v
+    caches = [base]
+    for _ in range(args.replicas - 1):
+        c = rbq.RotatedQuantKVCache(w.B, w.Hkv, dtype=w.torch_dtype, device=dev, rot=rot)
+        c.arrays = {n: a.clone() for n, a in base.arrays.items()}
+        c.desc = capi.rbq_kv_cache.from_buffer_copy(base.desc)
+        c._bind(c.desc, c.arrays, base.capacity)
+        caches.append(c)
+    assert base.capacity >= w.T
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    ws = base.workspace(w.Hq, w.L, args.splits)
+    ws = None if ws is None else ws.clone()
+    splits_used = capi.rbq_quant_attn_splits(base.desc, w.Hq, w.L) if args.splits == 0 \
+        else args.splits
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        c = caches[i % len(caches)]
+        capi.rbq_kv_quant_append(c.desc, k_new, v_new, rot)
+        if ev is not None:
+            ev[0].record(stream)
+        capi.rbq_quant_attn_decode(c.desc, q, 1 / 16, True, rot, out, args.splits, ws)
+        if ev is not None:
+            ev[1].record(stream)
+        capi.rbq_kv_trim(c.desc, 1)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+
+    attn_ms = np.array([a.elapsed_time(b) for a, b in events])
+    nbytes = algorithmic_bytes(w, w.T)
+    ms_per_step = total * 1e3 / args.steps
+    value = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
+    attn_avg_s = float(attn_ms.mean()) * 1e-3
+    achieved = nbytes["attn"] / attn_avg_s / 1e9
+    traffic = measured_traffic(nbytes["attn"])
+
+    result = {
+        "metric": "quantized-KV decode attention: effective HBM GB/s (% of peak) and tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: B={w.B}, {w.Hq} q heads / {w.Hkv} kv heads, head_dim {w.D}, "
+                        f"T={w.T} cached tokens, L={w.L}, bf16 N(0,1), group 64, K4/V3, "
+                        f"rotation seed 0",
+            "B": w.B, "H_q": w.Hq, "H_kv": w.Hkv, "head_dim": w.D, "T": w.T, "L": w.L,
+            "splits": splits_used, "cache_replicas": len(caches),
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(w.B * w.L / (ms_per_step * 1e-3), 1),
+        "step_bytes": nbytes["step"],
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "rbq_quant_attn_decode launch (HIP events on its stream)",
+            "alg_bytes_per_launch": nbytes["attn"],
+            "avg_launch_us": round(attn_avg_s * 1e6, 3),
+            "p10_us": round(float(np.percentile(attn_ms, 10)) * 1e3, 3),
+            "p90_us": round(float(np.percentile(attn_ms, 90)) * 1e3, 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,206 @@
+/*
+ * rbq.h - C ABI of the rotated, asymmetric K4/V3 quantized KV cache and the
+ * fused decode/verify attention over it, for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the page "mlx_streaming/core/cache/quant_kv.py"
+ * (sparkle): the SO(4) block rotation (build_block_so4, rotate_last), the
+ * asymmetric quantized cache (AsymmetricQuantizedKVCache: update_and_fetch,
+ * trim) and the quantized SDPA (asym_quantized_sdpa), plus the trimmable
+ * branch of commit_verified_prefix on the page "mlx_streaming/mtp/kv_cache.py".
+ *
+ * Conventions shared by every entry point:
+ *   - Return value: RBQ_OK (0) or a negative RBQ_E* status; functions that
+ *     return a count return it when >= 0 and a negative status otherwise.
+ *     Nothing throws across the ABI.  rbq_status_string() names a status.
+ *   - Memory: the library allocates no device memory and owns no buffer.
+ *     Every pointer is owned by the caller.  "device" pointers are HIP device
+ *     allocations on the current device; "host" pointers are ordinary memory.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the legacy
+ *     default stream).  Device work is enqueued on it and the call returns
+ *     without synchronising; buffers must outlive that work.  Launch failures
+ *     return RBQ_EHIP and rbq_last_hip_error() gives the hipError_t (thread
+ *     local).
+ *   - Thread safety: calls on distinct caches may run concurrently.
+ *   - Supported shapes in this library: head_dim 256, group 64, k_bits 4,
+ *     v_bits 3, dtype fp16 or bf16, gfx950.  Anything else returns
+ *     RBQ_EUNSUPPORTED.
+ */
+#ifndef RBQ_H
+#define RBQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define RBQ_OK             0
+#define RBQ_EINVAL        -1  /* bad argument: null pointer, negative size, shape mismatch  */
+#define RBQ_EUNSUPPORTED  -2  /* valid but not built here (head_dim, bits, group, dtype)    */
+#define RBQ_ECAPACITY     -3  /* offset + n exceeds the cache capacity; nothing was written */
+#define RBQ_ERANGE        -4  /* L < 1 or L > offset (no visible key for some query row)    */
+#define RBQ_EWORKSPACE    -5  /* workspace missing or smaller than required                 */
+#define RBQ_EHIP          -6  /* a HIP call or kernel launch failed                         */
+
+/* ---- element types of the key/value/query inputs and of scales/biases ---- */
+#define RBQ_F16   1
+#define RBQ_BF16  2
+
+/*
+ * Cache descriptor (host struct, owned by the caller).  It mirrors the six
+ * arrays of AsymmetricQuantizedKVCache (_init_quant on the quant_kv.py page):
+ *   k_words  uint32 [B][H_kv][capacity][head_dim*k_bits/32]   (32 words at D=256)
+ *   k_scales dtype  [B][H_kv][capacity][head_dim/group_size]
+ *   k_biases dtype  [B][H_kv][capacity][head_dim/group_size]
+ *   v_words  uint32 [B][H_kv][capacity][head_dim*v_bits/32]   (24 words at D=256)
+ *   v_scales, v_biases as for K.
+ * All six are contiguous device buffers (row stride = capacity rows).  Each
+ * packed row is a little-endian bit stream: bit t of code j is bit
+ * ((bits*j + t) mod 32) of word (bits*j + t) / 32.  Rows [0, offset) are
+ * valid; rows at or beyond offset are never read.
+ */
+typedef struct rbq_kv_cache {
+    int32_t B, H_kv, head_dim, group_size, k_bits, v_bits;
+    int32_t dtype;          /* RBQ_F16 or RBQ_BF16: type of scales/biases and of the inputs */
+    int32_t reserved;       /* must be 0 */
+    int64_t capacity;       /* rows allocated per (b, kv head) */
+    int64_t offset;         /* rows written per (b, kv head) */
+    uint32_t* k_words;
+    void* k_scales;
+    void* k_biases;
+    uint32_t* v_words;
+    void* v_scales;
+    void* v_biases;
+} rbq_kv_cache;
+
+/*
+ * rbq_rotation_build - the blocks of the block-diagonal SO(4) rotation
+ * (quant_kv.py, "SO(4) block rotation": _quat_left, _quat_right_conj,
+ * build_block_so4).  Host only.
+ *   draws   host float [head_dim/4][2][4]: per block the raw left and right
+ *           quaternion draws (four standard normals each, cast to float32, in
+ *           the page's draw order from numpy's default_rng(seed)).
+ *   blocks  host float [head_dim/4][4][4], written: block b =
+ *           L(qL) * Rc(qR) with qL, qR the normalised draws and L, Rc the
+ *           printed 4x4 matrices; computed in double, rounded once to float.
+ *           The dense rotation M is blockdiag(blocks); rows rotate as x @ M.
+ * Errors: RBQ_EINVAL for null pointers, head_dim <= 0 or head_dim % 4 != 0,
+ * or a zero-norm draw (nothing defined is written in that case).
+ */
+int rbq_rotation_build(const float* draws, int32_t head_dim, float* blocks);
+
+/*
+ * rbq_kv_required_capacity - capacity (rows) the cache needs before n more
+ * rows are appended (AsymmetricQuantizedKVCache.update_and_fetch, step 256):
+ * unchanged while offset + n <= capacity (and capacity > 0); otherwise
+ * ceil(n/256)*256 rows are added to the buffer, which is first cut back to
+ * `offset` rows when offset % 256 != 0.  capacity == 0 means no buffer yet.
+ * Returns the capacity, or RBQ_EINVAL when n < 0, offset < 0 or
+ * offset > capacity.  Host only.
+ */
+int64_t rbq_kv_required_capacity(int64_t capacity, int64_t offset, int64_t n);
+
+/*
+ * rbq_kv_grow - copy a cache into larger buffers (the growth step of
+ * update_and_fetch).  `dst` must describe the new buffers (same B, H_kv,
+ * head_dim, group, bits, dtype; dst->capacity >= the rows kept) and
+ * `src` the old ones.  Rows [0, keep) are copied, where keep = src->offset
+ * when src->offset % 256 != 0 and src->capacity otherwise (the page keeps
+ * the whole old buffer in that case), and rows [keep, dst->capacity) are
+ * zero-filled.  dst->offset is set to src->offset.  Device work on `stream`.
+ * Errors: RBQ_EINVAL (mismatched descriptors, dst too small, aliasing
+ * buffers), RBQ_EUNSUPPORTED, RBQ_EHIP.
+ */
+int rbq_kv_grow(const rbq_kv_cache* src, rbq_kv_cache* dst, void* stream);
+
+/*
+ * rbq_kv_quant_append - rotate, quantize, bit-pack and append n rows
+ * (update_and_fetch with mx.quantize; quantizer scale = (max-min)/(2^bits-1),
+ * bias = min, code = clip(round-half-even((x - bias)/scale), 0, 2^bits-1) per
+ * group of group_size values, scale and bias stored in `dtype` and the codes
+ * computed against the stored values; a zero scale divides by 1).
+ *   k, v        device dtype [B][H_kv][n][head_dim], contiguous, unrotated.
+ *   rot_blocks  device float [head_dim/4][4][4] from rbq_rotation_build, or
+ *               NULL for no rotation (the page's cache, whose inputs arrive
+ *               already rotated).  Each 4-block of a row is rotated as an
+ *               fp64 sum of exact products and rounded once to fp32.
+ * Writes rows [offset, offset+n) of all six arrays and, on success, sets
+ * c->offset += n (host side, immediately; the device writes are async).
+ * Errors: RBQ_EINVAL (null pointers, n < 0), RBQ_ECAPACITY when
+ * offset + n > capacity (nothing is written), RBQ_EUNSUPPORTED, RBQ_EHIP.
+ * n == 0 is a no-op returning RBQ_OK.
+ */
+int rbq_kv_quant_append(rbq_kv_cache* c, const void* k, const void* v, int64_t n,
+                        const float* rot_blocks, void* stream);
+
+/*
+ * rbq_kv_trim - AsymmetricQuantizedKVCache.trim: n' = min(offset, n),
+ * offset -= n', returns n'.  Data is not cleared.  Host only, synchronous.
+ * Errors: RBQ_EINVAL for a null cache or n < 0.
+ */
+int64_t rbq_kv_trim(rbq_kv_cache* c, int64_t n);
+
+/*
+ * rbq_kv_commit_verified - trimmable branch of commit_verified_prefix
+ * (mtp/kv_cache.py): after verifying `verified_len` draft tokens of which
+ * `accepted_len` were accepted, trim the rejected suffix.  Returns the rows
+ * trimmed, or RBQ_EINVAL when accepted_len > verified_len or either is < 0.
+ */
+int64_t rbq_kv_commit_verified(rbq_kv_cache* c, int64_t verified_len, int64_t accepted_len);
+
+/*
+ * rbq_quant_attn_splits - the split count rbq_quant_attn_decode uses when
+ * called with splits == 0 for this cache state and query shape (>= 1), or a
+ * negative status for invalid arguments.
+ */
+int32_t rbq_quant_attn_splits(const rbq_kv_cache* c, int32_t H_q, int32_t L);
+
+/*
+ * rbq_quant_attn_workspace_bytes - bytes of device workspace
+ * rbq_quant_attn_decode needs for this cache state, query shape and split
+ * count (splits == 0: the automatic count).  0 means no workspace is needed.
+ * Returns (size_t)0 also for invalid arguments; the decode call reports those.
+ */
+size_t rbq_quant_attn_workspace_bytes(const rbq_kv_cache* c, int32_t H_q, int32_t L,
+                                      int32_t splits);
+
+/*
+ * rbq_quant_attn_decode - fused decode/verify attention over the packed
+ * cache (asym_quantized_sdpa) followed by the inverse rotation.
+ *   q           device dtype [B][H_q][L][head_dim], contiguous, unrotated.
+ *               Query head h reads kv head h / (H_q / H_kv).
+ *   scale       multiplies q before the scores (conventionally head_dim^-1/2).
+ *   causal      1: row i of the L-block sees keys t <= offset - L + i (the
+ *               page's causal mask at the cache offset); 0: all offset keys.
+ *   rot_blocks  device float [head_dim/4][4][4] or NULL.  With blocks, q is
+ *               rotated on entry (fp64 sum of exact products -> fp32) and the
+ *               output is rotated back (out = o @ M^T); with NULL neither
+ *               happens and the output stays in the cache's value space, as
+ *               the page's SDPA returns it.
+ *   out         device float [B][H_q][L][head_dim], written (fp32).
+ *   splits      number of key-range partials per (b, kv head) merged by a
+ *               log-sum-exp combine (0 = automatic; the result does not
+ *               depend on it beyond fp32 rounding).
+ *   ws          device workspace of ws_bytes >= rbq_quant_attn_workspace_bytes
+ *               (may be NULL when that is 0).
+ * Scores, softmax and the P.V accumulation run in fp32.  Keys [0, offset)
+ * are read.  Errors: RBQ_EINVAL (null pointers, H_q % H_kv != 0, splits < 0),
+ * RBQ_ERANGE (L < 1 or L > offset), RBQ_EWORKSPACE, RBQ_EUNSUPPORTED, RBQ_EHIP.
+ */
+int rbq_quant_attn_decode(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L,
+                          float scale, int32_t causal, const float* rot_blocks, float* out,
+                          int32_t splits, void* ws, size_t ws_bytes, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* rbq_status_string(int status);
+
+/* hipError_t of the last failed HIP call on this thread (0 if none). */
+int rbq_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RBQ_H */

@@ -1,0 +1,163 @@
+"""Python face of the quantized KV cache: torch owns the device buffers, the
+library does every step of the method.
+
+``RotatedQuantKVCache`` follows ``AsymmetricQuantizedKVCache`` on the page
+"mlx_streaming/core/cache/quant_kv.py": six arrays (K packed words, K scales,
+K biases, V packed words, V scales, V biases) of shape ``[B, H_kv, capacity,
+.]``, an ``offset``, growth in 256-row steps, ``trim``; plus the SO(4) block
+rotation applied on append and attention and undone on the output.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import capi
+
+HEAD_DIM = 256
+GROUP = 64
+K_BITS = 4
+V_BITS = 3
+STEP = 256
+
+
+def quaternion_draws(seed: int = 0, head_dim: int = HEAD_DIM) -> np.ndarray:
+    """The random numbers the block rotation draws (page quant_kv.py,
+    ``build_block_so4``): numpy ``default_rng(seed)``, and for each 4-D block
+    four standard normals for the left quaternion, then four for the right,
+    each cast to float32.  Returns ``[head_dim/4, 2, 4]``."""
+    if head_dim % 4:
+        raise ValueError("head_dim must be a multiple of 4")
+    rng = np.random.default_rng(seed)
+    out = np.empty((head_dim // 4, 2, 4), dtype=np.float32)
+    for b in range(head_dim // 4):
+        out[b, 0] = rng.standard_normal(4).astype(np.float32)
+        out[b, 1] = rng.standard_normal(4).astype(np.float32)
+    return out
+
+
+def build_block_so4(head_dim: int = HEAD_DIM, seed: int = 0, device="cuda") -> torch.Tensor:
+    """Rotation blocks ``float32 [head_dim/4, 4, 4]`` on ``device``
+    (``build_block_so4`` without the dense matrix: only its diagonal blocks)."""
+    blocks = capi.rbq_rotation_build(quaternion_draws(seed, head_dim))
+    return torch.from_numpy(blocks).to(device)
+
+
+class RotatedQuantKVCache:
+    """Rotated K4/V3 group-64 quantized KV cache on one GPU.
+
+    ``rot`` is the device tensor of rotation blocks (or None: inputs are taken
+    as already rotated and outputs stay in the rotated space, as the page's
+    cache and SDPA do)."""
+
+    def __init__(self, B: int, H_kv: int, dtype: torch.dtype = torch.bfloat16,
+                 device="cuda", rot: Optional[torch.Tensor] = None,
+                 head_dim: int = HEAD_DIM, group_size: int = GROUP,
+                 k_bits: int = K_BITS, v_bits: int = V_BITS):
+        if dtype not in capi.DTYPE_CODES:
+            raise ValueError("dtype must be torch.float16 or torch.bfloat16")
+        self.device = torch.device(device)
+        self.dtype = dtype
+        self.rot = rot
+        self.desc = capi.rbq_kv_cache(B=B, H_kv=H_kv, head_dim=head_dim, group_size=group_size,
+                                      k_bits=k_bits, v_bits=v_bits,
+                                      dtype=capi.DTYPE_CODES[dtype], reserved=0,
+                                      capacity=0, offset=0)
+        self.arrays = None
+        self._ws = None
+
+    # -- page API ------------------------------------------------------------
+    @property
+    def offset(self) -> int:
+        return int(self.desc.offset)
+
+    @property
+    def capacity(self) -> int:
+        return int(self.desc.capacity)
+
+    def empty(self) -> bool:
+        return self.arrays is None
+
+    @property
+    def nbytes(self) -> int:
+        """Bytes held by the six buffers (capacity rows, not offset rows)."""
+        if self.arrays is None:
+            return 0
+        return sum(a.numel() * a.element_size() for a in self.arrays.values())
+
+    def _alloc(self, capacity: int) -> dict:
+        d = self.desc
+        kw = d.head_dim * d.k_bits // 32
+        vw = d.head_dim * d.v_bits // 32
+        ng = d.head_dim // d.group_size
+        shp = (d.B, d.H_kv, capacity)
+        return {
+            "k_words": torch.empty(shp + (kw,), dtype=torch.int32, device=self.device),
+            "k_scales": torch.empty(shp + (ng,), dtype=self.dtype, device=self.device),
+            "k_biases": torch.empty(shp + (ng,), dtype=self.dtype, device=self.device),
+            "v_words": torch.empty(shp + (vw,), dtype=torch.int32, device=self.device),
+            "v_scales": torch.empty(shp + (ng,), dtype=self.dtype, device=self.device),
+            "v_biases": torch.empty(shp + (ng,), dtype=self.dtype, device=self.device),
+        }
+
+    @staticmethod
+    def _bind(desc: capi.rbq_kv_cache, arrays: dict, capacity: int) -> None:
+        desc.capacity = capacity
+        for name, t in arrays.items():
+            setattr(desc, name, t.data_ptr())
+
+    def reserve(self, n: int) -> None:
+        """Grow the buffers so that n more rows fit (update_and_fetch's growth rule)."""
+        cap = capi.rbq_kv_required_capacity(self.capacity, self.offset, n)
+        if cap == self.capacity:
+            return
+        new = self._alloc(cap)
+        dst = capi.rbq_kv_cache.from_buffer_copy(self.desc)
+        self._bind(dst, new, cap)
+        capi.rbq_kv_grow(self.desc, dst)
+        self.arrays = new
+        self.desc = dst
+
+    def append(self, k: torch.Tensor, v: torch.Tensor) -> None:
+        """update_and_fetch: rotate, quantize, pack and write ``k``/``v``
+        ``[B, H_kv, n, head_dim]`` at ``offset``; ``offset`` advances by n."""
+        n = k.shape[2]
+        self.reserve(n)
+        capi.rbq_kv_quant_append(self.desc, k, v, self.rot)
+
+    update_and_fetch = append
+
+    def trim(self, n: int) -> int:
+        return capi.rbq_kv_trim(self.desc, n)
+
+    def commit_verified(self, verified_len: int, accepted_len: int) -> int:
+        return capi.rbq_kv_commit_verified(self.desc, verified_len, accepted_len)
+
+    # -- attention -------------------------------------------------------------
+    def workspace(self, H_q: int, L: int, splits: int = 0) -> Optional[torch.Tensor]:
+        nb = capi.rbq_quant_attn_workspace_bytes(self.desc, H_q, L, splits)
+        if nb == 0:
+            return None
+        if self._ws is None or self._ws.numel() < nb:
+            self._ws = torch.empty(nb, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def attend(self, q: torch.Tensor, scale: Optional[float] = None, causal: bool = True,
+               splits: int = 0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Fused attention of ``q [B, H_q, L, head_dim]`` over rows [0, offset),
+        returning float32 ``[B, H_q, L, head_dim]`` rotated back."""
+        if scale is None:
+            scale = self.desc.head_dim ** -0.5
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
+        ws = self.workspace(q.shape[1], q.shape[2], splits)
+        capi.rbq_quant_attn_decode(self.desc, q, scale, causal, self.rot, out, splits, ws)
+        return out
+
+    # -- inspection ------------------------------------------------------------
+    def rows(self, upto: Optional[int] = None) -> dict:
+        """Views of the six arrays' rows [0, upto or offset)."""
+        n = self.offset if upto is None else upto
+        return {k: a[:, :, :n] for k, a in self.arrays.items()}

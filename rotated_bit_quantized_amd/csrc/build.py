@@ -1,0 +1,71 @@
+"""Build librbq.so in-tree for gfx950 (host C++ with g++, kernels with hipcc).
+
+Usage: ``python rotated_bit_quantized_amd/csrc/build.py`` (or ``build()`` from
+``__graft_entry__``).  Always recompiles.  The shared library lands next to the
+Python binding: ``rotated_bit_quantized_amd/librbq.so``.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PKG = os.path.dirname(HERE)
+ROOT = os.path.dirname(PKG)
+INCLUDE = os.path.join(ROOT, "include")
+OUT_DIR = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "librbq.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+HIP_SOURCES = ["rbq_append.hip", "rbq_attn.hip"]
+HOST_SOURCES = ["rbq_host.cpp"]
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
+    "-I", INCLUDE, "-I", HERE,
+    # no packed fp32 instructions anywhere in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # IEEE fp32 division and sqrt, fp32 subnormals kept: the quantizer's
+    # decisions must match the definition bit for bit
+    "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
+    "-ffp-contract=fast",
+]
+HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-ffp-contract=off",
+              "-I", INCLUDE, "-I", HERE, "-I", "/opt/rocm/include"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("build step failed: " + " ".join(cmd[:3]) + " ...")
+    out = (r.stdout + r.stderr).strip()
+    if verbose and out:
+        print(out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OUT_DIR, exist_ok=True)
+    objs = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(OUT_DIR, src + ".o")
+        _run(["g++", *HOST_FLAGS, "-c", os.path.join(HERE, src), "-o", obj], verbose)
+        objs.append(obj)
+    for src in HIP_SOURCES:
+        obj = os.path.join(OUT_DIR, src + ".o")
+        _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(HERE, src), "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    shutil.move(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

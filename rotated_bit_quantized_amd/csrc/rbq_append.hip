@@ -1,0 +1,209 @@
+// Append path of the quantized cache (update_and_fetch on the quant_kv.py
+// page): rotate each new K/V row by the SO(4) blocks, quantize it in groups
+// of 64 (K 4-bit, V 3-bit, per-group scale and bias in the input dtype),
+// bit-pack it as a little-endian bit stream and write it at row `offset`.
+// Also the growth copy of the cache buffers.
+//
+// Mapping: one wave64 per (b, kv head, token) row; lane l owns elements
+// [4l, 4l+4) = rotation block l, so a group of 64 is 16 lanes and the group
+// min/max is a 16-lane butterfly.  K and V of the same row are done by the
+// same wave.  A row reads 2 x 512 B and writes 256 B; the kernel is HBM-bound.
+#include <hip/hip_runtime.h>
+
+#include "rbq_common.h"
+
+namespace rbq {
+namespace {
+
+constexpr int kRowsPerBlock = 4;  // waves per workgroup
+
+// Quantize and pack one row of 256 values held 4 per lane.
+// The arithmetic is the quantizer definition step by step, each step one
+// IEEE fp32 operation: min/max (exact), (max - min) / (2^bits - 1) with a
+// correctly rounded division, scale and bias rounded to the dtype, and
+// rint((y - bias) / scale) clipped to [0, 2^bits - 1].
+template <int DT, int BITS>
+__device__ __forceinline__ void quantize_pack_row(const float y[4], int lane,
+                                                  uint32_t* __restrict__ words,
+                                                  uint16_t* __restrict__ scales,
+                                                  uint16_t* __restrict__ biases) {
+    constexpr float kLevels = (float)((1 << BITS) - 1);
+    float mn = fminf(fminf(y[0], y[1]), fminf(y[2], y[3]));
+    float mx = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, m));
+        mx = fmaxf(mx, __shfl_xor(mx, m));
+    }
+    const float s32 = __fdiv_rn(mx - mn, kLevels);
+    const uint32_t s_bits = f32_to_elem_bits<DT>(s32);
+    const uint32_t b_bits = f32_to_elem_bits<DT>(mn);
+    const float s = elem_to_f32<DT>(s_bits);
+    const float beta = elem_to_f32<DT>(b_bits);
+    const float sdiv = (s == 0.0f) ? 1.0f : s;
+
+    uint32_t chunk = 0;  // 4 codes = 4*BITS bits, code i at bit BITS*i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float c = rintf(__fdiv_rn(y[i] - beta, sdiv));
+        c = fminf(fmaxf(c, 0.0f), kLevels);
+        chunk |= (uint32_t)c << (BITS * i);
+    }
+
+    // Lane j's chunk sits at stream bits [C*j, C*j + C), C = 4*BITS.  Lane w
+    // (w < words per row) gathers every chunk overlapping bits [32w, 32w+32).
+    constexpr int C = 4 * BITS;
+    constexpr int kWords = 64 * C / 32;
+    constexpr int kSpan = (32 + C - 1) / C + 1;  // max chunks touching one word
+    const int w = lane < kWords ? lane : 0;
+    const int j0 = (32 * w) / C;
+    const int j1 = (32 * w + 31) / C;
+    uint32_t word = 0;
+#pragma unroll
+    for (int k = 0; k < kSpan; ++k) {
+        const int j = j0 + k;
+        const uint32_t val = __shfl(chunk, j < 64 ? j : 63);
+        if (j <= j1) {
+            const int sh = C * j - 32 * w;
+            word |= sh >= 0 ? (val << sh) : (val >> (-sh));
+        }
+    }
+    if (lane < kWords) words[lane] = word;
+
+    const uint32_t sg = __shfl(s_bits, (lane & 3) * 16);
+    const uint32_t bg = __shfl(b_bits, (lane & 3) * 16);
+    if (lane < 4) {
+        scales[lane] = (uint16_t)sg;
+        biases[lane] = (uint16_t)bg;
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void quant_append_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t n,
+    const float* __restrict__ rot, uint32_t* __restrict__ kw, uint16_t* __restrict__ ks,
+    uint16_t* __restrict__ kb, uint32_t* __restrict__ vw, uint16_t* __restrict__ vs,
+    uint16_t* __restrict__ vb, int64_t capacity, int64_t offset, int64_t rows_total) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= rows_total) return;  // uniform per wave
+    const int64_t bh = row / n;
+    const int64_t t = row - bh * n;
+    const int64_t src = row * kHeadDim + lane * 4;
+    const int64_t dst = bh * capacity + offset + t;
+
+    float Bm[16];
+    load_block(rot, lane, Bm);
+
+    float x[4], y[4];
+    load4<DT>(k + src, x);
+    rotate4(x, Bm, y);
+    quantize_pack_row<DT, kKBits>(y, lane, kw + dst * kKWords, ks + dst * kGroups,
+                                  kb + dst * kGroups);
+    load4<DT>(v + src, x);
+    rotate4(x, Bm, y);
+    quantize_pack_row<DT, kVBits>(y, lane, vw + dst * kVWords, vs + dst * kGroups,
+                                  vb + dst * kGroups);
+}
+
+// dst rows [0, keep) <- src rows, dst rows [keep, dst_cap) <- 0, for an array
+// of `wpr` 32-bit words per row and `bh` (b, kv head) slabs.
+__global__ __launch_bounds__(256) void grow_copy_kernel(const uint32_t* __restrict__ src,
+                                                        uint32_t* __restrict__ dst, int wpr,
+                                                        int64_t bh, int64_t src_cap,
+                                                        int64_t dst_cap, int64_t keep) {
+    const int64_t total = bh * dst_cap * wpr;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t slab = i / (dst_cap * wpr);
+        const int64_t rem = i - slab * dst_cap * wpr;
+        const int64_t r = rem / wpr;
+        const int64_t e = rem - r * wpr;
+        dst[i] = (r < keep) ? src[(slab * src_cap + r) * wpr + e] : 0u;
+    }
+}
+
+int launch_status(hipError_t e) {
+    if (e != hipSuccess) {
+        set_hip_error((int)e);
+        return RBQ_EHIP;
+    }
+    return RBQ_OK;
+}
+
+}  // namespace
+}  // namespace rbq
+
+using namespace rbq;
+
+extern "C" int rbq_kv_quant_append(rbq_kv_cache* c, const void* k, const void* v, int64_t n,
+                                   const float* rot_blocks, void* stream) {
+    int st = check_cache(c);
+    if (st != RBQ_OK) return st;
+    if (n < 0) return RBQ_EINVAL;
+    if (n == 0) return RBQ_OK;
+    if (k == nullptr || v == nullptr) return RBQ_EINVAL;
+    if (c->offset + n > c->capacity) return RBQ_ECAPACITY;
+    const int64_t rows = (int64_t)c->B * c->H_kv * n;
+    const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    if (blocks > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    const dim3 grid((unsigned)blocks), block(64 * kRowsPerBlock);
+    auto* kw = c->k_words;
+    auto* ks = (uint16_t*)c->k_scales;
+    auto* kb = (uint16_t*)c->k_biases;
+    auto* vw = c->v_words;
+    auto* vs = (uint16_t*)c->v_scales;
+    auto* vb = (uint16_t*)c->v_biases;
+    if (c->dtype == RBQ_BF16)
+        hipLaunchKernelGGL(quant_append_kernel<RBQ_BF16>, grid, block, 0, s,
+                           (const uint16_t*)k, (const uint16_t*)v, n, rot_blocks, kw, ks, kb, vw,
+                           vs, vb, c->capacity, c->offset, rows);
+    else
+        hipLaunchKernelGGL(quant_append_kernel<RBQ_F16>, grid, block, 0, s, (const uint16_t*)k,
+                           (const uint16_t*)v, n, rot_blocks, kw, ks, kb, vw, vs, vb,
+                           c->capacity, c->offset, rows);
+    st = launch_status(hipGetLastError());
+    if (st != RBQ_OK) return st;
+    c->offset += n;
+    return RBQ_OK;
+}
+
+extern "C" int rbq_kv_grow(const rbq_kv_cache* src, rbq_kv_cache* dst, void* stream) {
+    int st = check_cache(src);
+    if (st != RBQ_OK) return st;
+    st = check_cache(dst);
+    if (st != RBQ_OK) return st;
+    if (src->B != dst->B || src->H_kv != dst->H_kv || src->dtype != dst->dtype ||
+        dst->capacity <= 0)
+        return RBQ_EINVAL;
+    const int64_t keep = (src->capacity == 0) ? 0
+                         : (src->offset % kStep != 0) ? src->offset
+                                                      : src->capacity;
+    if (keep > dst->capacity) return RBQ_EINVAL;
+    if (src->capacity > 0 && (src->k_words == dst->k_words || src->v_words == dst->v_words))
+        return RBQ_EINVAL;
+    const int64_t bh = (int64_t)src->B * src->H_kv;
+    hipStream_t s = (hipStream_t)stream;
+    struct Arr {
+        const void* from;
+        void* to;
+        int wpr;
+    } arrs[6] = {
+        {src->k_words, dst->k_words, kKWords},     {src->k_scales, dst->k_scales, kGroups / 2},
+        {src->k_biases, dst->k_biases, kGroups / 2}, {src->v_words, dst->v_words, kVWords},
+        {src->v_scales, dst->v_scales, kGroups / 2}, {src->v_biases, dst->v_biases, kGroups / 2},
+    };
+    for (const Arr& a : arrs) {
+        const int64_t total = bh * dst->capacity * a.wpr;
+        int64_t nb = (total + 255) / 256;
+        if (nb > 65536) nb = 65536;
+        hipLaunchKernelGGL(grow_copy_kernel, dim3((unsigned)nb), dim3(256), 0, s,
+                           (const uint32_t*)a.from, (uint32_t*)a.to, a.wpr, bh, src->capacity,
+                           dst->capacity, keep);
+        st = launch_status(hipGetLastError());
+        if (st != RBQ_OK) return st;
+    }
+    dst->offset = src->offset;
+    return RBQ_OK;
+}

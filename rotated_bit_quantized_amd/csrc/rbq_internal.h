@@ -1,0 +1,31 @@
+// Internal helpers shared by the host-side C++ and the HIP translation units
+// of librbq.  Not part of the public ABI (that is include/rbq.h).
+#pragma once
+
+#include <stdint.h>
+
+#include "rbq.h"
+
+namespace rbq {
+
+constexpr int kHeadDim = 256;
+constexpr int kGroup = 64;
+constexpr int kKBits = 4;
+constexpr int kVBits = 3;
+constexpr int kStep = 256;               // cache growth step (update_and_fetch)
+constexpr int kKWords = kHeadDim * kKBits / 32;   // 32
+constexpr int kVWords = kHeadDim * kVBits / 32;   // 24
+constexpr int kGroups = kHeadDim / kGroup;        // 4
+
+// Records the hipError_t of the last failed HIP call on this thread.
+void set_hip_error(int err);
+
+// Validates the descriptor fields shared by every device entry point:
+// non-null buffers, positive B/H_kv, 0 <= offset <= capacity, reserved == 0,
+// and the supported configuration (RBQ_EUNSUPPORTED otherwise).
+int check_cache(const rbq_kv_cache* c);
+
+// Split count chosen when the caller passes 0.
+int32_t auto_splits(const rbq_kv_cache* c, int32_t H_q, int32_t L);
+
+}  // namespace rbq

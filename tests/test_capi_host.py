@@ -1,0 +1,166 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+its host-only entry points agree with the oracle; device entry points reject
+bad arguments before any device work (no GPU call is made here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import rbq_oracle as O
+
+rbq = pytest.importorskip("rotated_bit_quantized_amd")
+from rotated_bit_quantized_amd import capi  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "rbq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rbq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    syms = declared_symbols()
+    for name in ("rbq_rotation_build", "rbq_kv_quant_append", "rbq_kv_trim",
+                 "rbq_quant_attn_decode"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(capi.LIB_PATH)
+    missing = [s for s in declared_symbols() if not hasattr(lib, s)]
+    assert not missing, missing
+
+
+@pytest.mark.parametrize("seed", [0, 1, 12345])
+def test_rotation_build_bit_exact_vs_oracle(seed):
+    draws = W.rotation_draws(seed, 256)
+    got = capi.rbq_rotation_build(draws)
+    np.testing.assert_array_equal(got, O.rotation_blocks(draws))
+
+
+def test_package_draws_match_the_input_generator():
+    # The package's seed -> draws step and the shared generator take the same
+    # numbers from numpy's default_rng in the same order.
+    np.testing.assert_array_equal(rbq.quaternion_draws(0, 256), W.rotation_draws(0, 256))
+
+
+def test_rotation_build_other_head_dims_and_errors():
+    for D in (4, 64, 128):
+        draws = W.rotation_draws(3, D)
+        np.testing.assert_array_equal(capi.rbq_rotation_build(draws), O.rotation_blocks(draws))
+    bad = np.zeros((2, 2, 4), np.float32)
+    bad[0] = 1.0
+    with pytest.raises(capi.RbqError):
+        capi.rbq_rotation_build(bad)  # block 1 has a zero-norm draw
+    assert capi.library().rbq_rotation_build(None, 256, None) == capi.RBQ_EINVAL
+    d = np.ones((1, 2, 4), np.float32)
+    out = np.empty((1, 4, 4), np.float32)
+    assert capi.library().rbq_rotation_build(d.ctypes.data, 6, out.ctypes.data) == capi.RBQ_EINVAL
+
+
+def test_required_capacity_matches_oracle():
+    for cap in (0, 256, 512, 8192, 10240, 10496):
+        for off in sorted({0, 1, cap // 2, max(cap - 1, 0), cap, 255, 257}):
+            if off > cap:
+                continue
+            for n in (0, 1, 2, 255, 256, 257, 2048, 4096 + 3):
+                if cap == 0 and off != 0:
+                    continue
+                assert capi.rbq_kv_required_capacity(cap, off, n) == \
+                    O.required_capacity(cap, off, n), (cap, off, n)
+    for args in ((0, 0, -1), (10, 11, 1), (-1, 0, 0)):
+        with pytest.raises(capi.RbqError):
+            capi.rbq_kv_required_capacity(*args)
+
+
+def _host_desc(B=1, H=1, cap=0, off=0, dtype=capi.RBQ_BF16, **kw):
+    d = capi.rbq_kv_cache(B=B, H_kv=H, head_dim=256, group_size=64, k_bits=4, v_bits=3,
+                          dtype=dtype, reserved=0, capacity=cap, offset=off)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_growth_golden_through_the_library():
+    # Capacity/offset sequence of the append+verify workload (tests/golden/cache_growth.txt),
+    # replayed with the library's capacity rule and trim.
+    d = _host_desc()
+    with open(os.path.join(GOLDEN, "cache_growth.txt")) as f:
+        steps = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    for op, n, _, ret, cap, off in steps:
+        n, ret, cap, off = int(n), int(ret), int(cap), int(off)
+        if op == "append":
+            d.capacity = capi.rbq_kv_required_capacity(d.capacity, d.offset, n)
+            d.offset += n
+            got = n
+        else:
+            got = capi.rbq_kv_trim(d, n)
+        assert (got, d.capacity, d.offset) == (ret, cap, off)
+
+
+def test_trim_and_commit_semantics():
+    d = _host_desc(cap=256, off=10)
+    with pytest.raises(capi.RbqError):
+        capi.rbq_kv_trim(d, -1)
+    with pytest.raises(capi.RbqError):
+        capi.rbq_kv_commit_verified(d, 3, 4)
+    assert capi.rbq_kv_commit_verified(d, 4, 4) == 0 and d.offset == 10
+    assert capi.rbq_kv_commit_verified(d, 4, 1) == 3 and d.offset == 7
+    assert capi.rbq_kv_trim(d, 100) == 7 and d.offset == 0
+
+
+def test_device_entry_points_validate_before_any_device_work():
+    lib = capi.library()
+    fake = 0x1000  # never dereferenced: every call below fails validation first
+    ptrs = dict(k_words=fake, k_scales=fake, k_biases=fake, v_words=fake, v_scales=fake,
+                v_biases=fake)
+    d = _host_desc(B=1, H=2, cap=256, off=100, **ptrs)
+    by = ctypes.byref
+    # append: capacity exceeded, negative n, null inputs
+    assert lib.rbq_kv_quant_append(by(d), fake, fake, 157, None, None) == capi.RBQ_ECAPACITY
+    assert d.offset == 100
+    assert lib.rbq_kv_quant_append(by(d), fake, fake, -1, None, None) == capi.RBQ_EINVAL
+    assert lib.rbq_kv_quant_append(by(d), None, fake, 1, None, None) == capi.RBQ_EINVAL
+    assert lib.rbq_kv_quant_append(by(d), fake, fake, 0, None, None) == capi.RBQ_OK
+    # unsupported configurations
+    for field, val in (("head_dim", 128), ("group_size", 32), ("k_bits", 8), ("v_bits", 4),
+                       ("dtype", 7)):
+        e = _host_desc(B=1, H=2, cap=256, off=100, **ptrs)
+        setattr(e, field, val)
+        assert lib.rbq_kv_quant_append(by(e), fake, fake, 1, None, None) == \
+            capi.RBQ_EUNSUPPORTED, field
+    e = _host_desc(B=1, H=2, cap=256, off=100, **ptrs)
+    e.reserved = 1
+    assert lib.rbq_kv_quant_append(by(e), fake, fake, 1, None, None) == capi.RBQ_EINVAL
+    e = _host_desc(B=1, H=2, cap=256, off=300, **ptrs)
+    assert lib.rbq_kv_quant_append(by(e), fake, fake, 1, None, None) == capi.RBQ_EINVAL
+    # attention: H_q % H_kv, L range, splits < 0, null q/out, workspace
+    dec = lib.rbq_quant_attn_decode
+    assert dec(by(d), fake, 3, 1, 0.0625, 1, None, fake, 0, None, 0, None) == capi.RBQ_EINVAL
+    assert dec(by(d), fake, 4, 0, 0.0625, 1, None, fake, 0, None, 0, None) == capi.RBQ_ERANGE
+    assert dec(by(d), fake, 4, 101, 0.0625, 1, None, fake, 0, None, 0, None) == capi.RBQ_ERANGE
+    assert dec(by(d), fake, 4, 1, 0.0625, 1, None, fake, -2, None, 0, None) == capi.RBQ_EINVAL
+    assert dec(by(d), None, 4, 1, 0.0625, 1, None, fake, 0, None, 0, None) == capi.RBQ_EINVAL
+    need = lib.rbq_quant_attn_workspace_bytes(by(d), 4, 1, 8)
+    assert need > 0
+    assert dec(by(d), fake, 4, 1, 0.0625, 1, None, fake, 8, None, 0, None) == capi.RBQ_EWORKSPACE
+    assert dec(by(d), fake, 4, 1, 0.0625, 1, None, fake, 8, fake, need - 1, None) == \
+        capi.RBQ_EWORKSPACE
+    assert lib.rbq_quant_attn_splits(by(d), 4, 1) >= 1
+    assert lib.rbq_quant_attn_splits(by(d), 3, 1) == capi.RBQ_EINVAL
+    # grow: mismatched descriptors
+    g = _host_desc(B=2, H=2, cap=512, off=0, **ptrs)
+    assert lib.rbq_kv_grow(by(d), by(g), None) == capi.RBQ_EINVAL
+
+
+def test_status_strings():
+    lib = capi.library()
+    for st in range(0, -7, -1):
+        assert lib.rbq_status_string(st).decode() not in ("", "unknown status")
+    assert lib.rbq_status_string(-99).decode() == "unknown status"
