@@ -21,8 +21,11 @@ LIB = os.path.join(PKG, "librbq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["rbq_append.hip", "rbq_attn.hip"]
+HIP_SOURCES = ["rbq_append.hip", "rbq_attn.hip", "rbq_attn_mfma.hip"]
 HOST_SOURCES = ["rbq_host.cpp"]
+# per-file extras: the attention kernels never rely on NaN semantics (masked
+# scores are -inf), which lets max reductions compile to single DPP ops
+HIP_FILE_FLAGS = {"rbq_attn_mfma.hip": ["-fno-honor-nans"]}
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
@@ -59,7 +62,8 @@ def build(verbose: bool = False) -> str:
         objs.append(obj)
     for src in HIP_SOURCES:
         obj = os.path.join(OUT_DIR, src + ".o")
-        _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(HERE, src), "-o", obj], verbose)
+        _run([HIPCC, *HIP_FLAGS, *HIP_FILE_FLAGS.get(src, []), "-c", os.path.join(HERE, src), "-o",
+              obj], verbose)
         objs.append(obj)
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)

@@ -314,8 +314,8 @@ int make_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Pla
     p->S = (int)S;
     p->chunk = (T + S - 1) / S;
     p->ws_bytes = (S == 1) ? 0
-                           : (size_t)c->B * c->H_kv * p->n_rb * S * p->RB * (kHeadDim + 2) *
-                                 sizeof(float);
+                           : kWsCounterBytes + (size_t)c->B * c->H_kv * p->n_rb * S * p->RB *
+                                                   (kHeadDim + 2) * sizeof(float);
     return RBQ_OK;
 }
 
@@ -354,14 +354,43 @@ int32_t auto_splits(const rbq_kv_cache* c, int32_t H_q, int32_t L) {
 
 using namespace rbq;
 
+namespace {
+
+bool use_mfma(const rbq_kv_cache* c, int32_t H_q, int32_t L) {
+    return (int64_t)(H_q / c->H_kv) * L <= kMfmaMaxRows;
+}
+
+// Shared argument checks of the attention entry points.
+int check_attn(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits) {
+    int st = check_cache(c);
+    if (st != RBQ_OK) return st;
+    if (H_q <= 0 || H_q % c->H_kv != 0 || splits < 0) return RBQ_EINVAL;
+    if (L < 1 || (int64_t)L > c->offset) return RBQ_ERANGE;
+    return RBQ_OK;
+}
+
+}  // namespace
+
 extern "C" int32_t rbq_quant_attn_splits(const rbq_kv_cache* c, int32_t H_q, int32_t L) {
+    int st = check_attn(c, H_q, L, 0);
+    if (st != RBQ_OK) return st;
+    if (use_mfma(c, H_q, L)) {
+        MfmaPlan mp;
+        st = mfma_plan(c, H_q, L, 0, &mp);
+        return st != RBQ_OK ? st : mp.S;
+    }
     Plan p;
-    const int st = make_plan(c, H_q, L, 0, &p);
+    st = make_plan(c, H_q, L, 0, &p);
     return st != RBQ_OK ? st : p.S;
 }
 
 extern "C" size_t rbq_quant_attn_workspace_bytes(const rbq_kv_cache* c, int32_t H_q, int32_t L,
                                                  int32_t splits) {
+    if (check_attn(c, H_q, L, splits) != RBQ_OK) return 0;
+    if (use_mfma(c, H_q, L)) {
+        MfmaPlan mp;
+        return mfma_plan(c, H_q, L, splits, &mp) == RBQ_OK ? mp.ws_bytes : 0;
+    }
     Plan p;
     if (make_plan(c, H_q, L, splits, &p) != RBQ_OK) return 0;
     return p.ws_bytes;
@@ -371,10 +400,19 @@ extern "C" int rbq_quant_attn_decode(const rbq_kv_cache* c, const void* q, int32
                                      float scale, int32_t causal, const float* rot_blocks,
                                      float* out, int32_t splits, void* ws, size_t ws_bytes,
                                      void* stream) {
-    Plan p;
-    int st = make_plan(c, H_q, L, splits, &p);
+    int st = check_attn(c, H_q, L, splits);
     if (st != RBQ_OK) return st;
     if (q == nullptr || out == nullptr) return RBQ_EINVAL;
+    if (use_mfma(c, H_q, L)) {
+        MfmaPlan mp;
+        st = mfma_plan(c, H_q, L, splits, &mp);
+        if (st != RBQ_OK) return st;
+        if (mp.ws_bytes > 0 && (ws == nullptr || ws_bytes < mp.ws_bytes)) return RBQ_EWORKSPACE;
+        return mfma_launch(c, q, H_q, L, scale, causal, rot_blocks, out, mp, ws, stream);
+    }
+    Plan p;
+    st = make_plan(c, H_q, L, splits, &p);
+    if (st != RBQ_OK) return st;
     if (p.ws_bytes > 0 && (ws == nullptr || ws_bytes < p.ws_bytes)) return RBQ_EWORKSPACE;
 
     AttnArgs a;
@@ -388,8 +426,8 @@ extern "C" int rbq_quant_attn_decode(const rbq_kv_cache* c, const void* q, int32
     a.rot = rot_blocks;
     a.out = out;
     const size_t n_part = (size_t)c->B * c->H_kv * p.n_rb * p.S * p.RB;
-    a.ws_o = (float*)ws;
-    a.ws_ml = p.ws_bytes ? (float*)ws + n_part * kHeadDim : nullptr;
+    a.ws_o = p.ws_bytes ? (float*)((char*)ws + kWsCounterBytes) : nullptr;
+    a.ws_ml = p.ws_bytes ? a.ws_o + n_part * kHeadDim : nullptr;
     a.capacity = c->capacity;
     a.T = c->offset;
     a.chunk = p.chunk;

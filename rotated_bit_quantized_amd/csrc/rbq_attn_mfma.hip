@@ -1,0 +1,811 @@
+// Fused decode attention over the packed K4/V3 cache on the gfx950 matrix
+// cores (asym_quantized_sdpa on the quant_kv.py page, with the SO(4)
+// rotation of q on entry and the inverse rotation of the output), for up to
+// 8 query rows per kv head (GQA group x verify block).
+//
+// Decomposition: one workgroup of 4 wave64s per (b, kv head, key split);
+// each wave walks 32-key tiles of the split with an online softmax (base 2,
+// rescaled only when the running maximum grows by more than 2^8), the 4 wave
+// partials are merged in LDS, and the split partials are merged in-kernel by
+// the last-arriving workgroup of each group of 16 (a tree of such merges),
+// whose last step normalises and rotates the output back.
+//
+// All products run as 16x16x32 MFMAs.  Lane l = 16 j + n: j selects a k-slot
+// group of the operands and a quarter of the accumulator rows, n a column.
+// Scores: A = query (rows 0-7: fp16 hi part of the 8 query rows, rows 8-15:
+//   lo part; each row scaled by a power of two so that hi spans [2^14, 2^15)),
+//   B = K codes of 16 keys (column = key).  The codes enter as fp16
+//   subnormals: masking nibble pairs of a packed word in place gives
+//   c * 2^-24 (nibbles 0 and 2 of a byte pair) or 16 c * 2^-24 (nibbles 1 and
+//   3), with the matching 1 or 1/16 folded into the query operand.  One
+//   accumulator per 64-value group g; score = s_g acc_g (fp32, per key) plus
+//   sum_g b_g sum_{d in g} q_d, the latter an MFMA of the raw bias words
+//   against the query's group sums (split into exact limbs).
+// Values: the 3-bit codes of 16 keys are decoded 4 at a time through a
+//   4096-entry LDS table (12 stream bits -> 4 fp16 codes), multiplied by the
+//   key's group scale in fp16 (exact for bf16 scales: 3 + 8 significant bits;
+//   fp16 scales are split into an exact 8-bit head and 3-bit tail), and
+//   transposed key-major -> column-major by an MFMA against a 0/1 selection
+//   matrix; its accumulator layout is the B layout of the P.V MFMA, whose A
+//   is P split hi + lo over the 16 rows (staged through LDS to the key-slot
+//   order of that B layout).  The group bias enters through the same
+//   transpose and one more MFMA as sum_t p_t b_{t,g}.
+// Precondition of the fp16 value path: V group ranges (max - min of the
+// rotated values) and |V bias| stay below 65504; larger values overflow to
+// inf and show up as non-finite outputs.
+#include <hip/hip_runtime.h>
+
+#include "rbq_common.h"
+
+namespace rbq {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 32;                                  // keys per wave iteration
+constexpr int kRows = 8;                                   // query rows per kv head
+constexpr int kFanIn = 32;                                 // records per merge step
+constexpr int kRecFloats = 2 * kRows + kRows * kHeadDim;   // (m, l)[8], o[8][256]
+constexpr int kWaveRecFloats = 2 * kRows + kRows * kGroups + kRows * kHeadDim;
+constexpr int kLutBytes = 4096 * 8;
+constexpr int kQaBytes = 8 * 64 * 16;                      // score query operands, per lane
+constexpr int kPBytes = kTile * kRows * 4;                 // per-wave P staging [key][row]
+constexpr int kLoopSmem = kLutBytes + kQaBytes + kWaves * kPBytes;
+constexpr int kRecSmem = kWaves * kWaveRecFloats * 4;
+constexpr int kSmemBytes = kLoopSmem > kRecSmem ? kLoopSmem : kRecSmem;
+constexpr int kCounterBytes = (int)kWsCounterBytes;
+constexpr int kMaxLevels = 8;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+struct MArgs {
+    const uint16_t* q;
+    const uint32_t* kw;
+    const uint16_t* ks;
+    const uint16_t* kb;
+    const uint32_t* vw;
+    const uint16_t* vs;
+    const uint16_t* vb;
+    const float* rot;
+    float* out;
+    float* rec;
+    int* cnt;
+    int64_t capacity;
+    int T, chunk;
+    int Hkv, n_rep, L, G, S, causal;
+    int n_lvl[kMaxLevels];
+    int64_t rec_base[kMaxLevels];
+    int cnt_base[kMaxLevels];
+    float qscale;  // scale * log2(e)
+};
+
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16bf(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                     __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// max / sum over the 16 lanes of a row
+__device__ __forceinline__ float max16(float x) {
+    x = fmaxf(x, dpp<0xB1>(x));
+    x = fmaxf(x, dpp<0x4E>(x));
+    x = fmaxf(x, dpp<0x141>(x));
+    return fmaxf(x, dpp<0x140>(x));
+}
+__device__ __forceinline__ float sum16(float x) {
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    return x + dpp<0x140>(x);
+}
+
+// x[l] + x[l ^ 32]
+__device__ __forceinline__ float add_swap32(float x) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+template <int DT>
+__device__ __forceinline__ float meta_f32(uint32_t word, int half) {
+    return elem_to_f32<DT>(half ? word >> 16 : word);
+}
+
+// Byte offset (index * 8) in the decode table of 12-bit chunk c (codes
+// 4c..4c+3) of a 64-code V group held in words w[0..5].
+template <int C>
+__device__ __forceinline__ uint32_t chunk_offset(const uint32_t w[6]) {
+    constexpr int start = 12 * C - 3;
+    if constexpr (C == 0) {
+        return (w[0] << 3) & 0x7FF8u;
+    } else {
+        constexpr int wi = start >> 5, sh = start & 31;
+        if constexpr (wi + 1 < 6) return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & 0x7FF8u;
+        else return (w[wi] >> sh) & 0x7FF8u;
+    }
+}
+
+template <int C>
+__device__ __forceinline__ u32x2 lut_entry(const unsigned char* lut, const uint32_t w[6]) {
+    const uint2 e = *reinterpret_cast<const uint2*>(lut + chunk_offset<C>(w));
+    return (u32x2){e.x, e.y};
+}
+
+__device__ __forceinline__ uint32_t mul2(uint32_t a, f16x2 s) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a) * s);
+}
+
+// Split-partial records are exchanged between workgroups of one launch,
+// which may run on different XCDs (each with its own L2).  They are written
+// and read with relaxed agent-scope atomics (write-through / read-through the
+// XCD L2), the writer waits for its stores to complete before it bumps the
+// group counter, and only the last arrival of a group reads the group's
+// records; no L2 write-back fence is needed.
+__device__ __forceinline__ void st_rec(float* p, float a, float b) {
+    const unsigned long long v =
+        (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), v, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_rec(const float* p) {
+    const unsigned long long v = __hip_atomic_load(
+        reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
+// Fold one record (m, l, o[8]) into a running (M, Lsum, acc[8]).
+__device__ __forceinline__ void fold(float& M, float& Ls, float acc[8], float m, float l,
+                                     const float o[8]) {
+    if (m == -INFINITY) return;
+    if (m > M) {
+        const float a = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - m);
+        Ls *= a;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] *= a;
+        M = m;
+    }
+    const float w = __builtin_amdgcn_exp2f(m - M);
+    Ls = fmaf(w, l, Ls);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = fmaf(w, o[k], acc[k]);
+}
+
+// Transpose a key-major operand (A: key rows, 8 k-slots per lane group)
+// into the B layout of the P.V MFMA for both 16-key blocks: result slots =
+// keys 4j..4j+3 of block 0, then of block 1, column n = the selected slot.
+__device__ __forceinline__ f16x8 transpose2(f16x8 a0, f16x8 a1, f16x8 sel) {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 c0 = mfma16(a0, sel, z);
+    const f32x4 c1 = mfma16(a1, sel, z);
+    const u32x4 b = {pk_f16(c0[0], c0[1]), pk_f16(c0[2], c0[3]), pk_f16(c1[0], c1[1]),
+                     pk_f16(c1[2], c1[3])};
+    return as_f16x8(b);
+}
+
+// P.V for codes 8i..8i+7 of every group: decode (both blocks), scale,
+// transpose, accumulate into the two output tiles of step i.
+template <int DT, int I>
+__device__ __forceinline__ void pv_step(const unsigned char* lut, const uint32_t wv0[6],
+                                        const uint32_t wv1[6], f16x2 s0, f16x2 s1, f16x2 t0,
+                                        f16x2 t1, f16x8 sel0, f16x8 sel1, f16x8 pa, f32x4& o0,
+                                        f32x4& o1) {
+    const u32x2 x0 = lut_entry<2 * I>(lut, wv0), y0 = lut_entry<2 * I + 1>(lut, wv0);
+    const u32x2 x1 = lut_entry<2 * I>(lut, wv1), y1 = lut_entry<2 * I + 1>(lut, wv1);
+    {
+        const f16x8 a0 = as_f16x8((u32x4){mul2(x0[0], s0), mul2(x0[1], s0), mul2(y0[0], s0),
+                                          mul2(y0[1], s0)});
+        const f16x8 a1 = as_f16x8((u32x4){mul2(x1[0], s1), mul2(x1[1], s1), mul2(y1[0], s1),
+                                          mul2(y1[1], s1)});
+        o0 = mfma16(pa, transpose2(a0, a1, sel0), o0);
+        o1 = mfma16(pa, transpose2(a0, a1, sel1), o1);
+    }
+    if constexpr (DT == RBQ_F16) {
+        const f16x8 a0 = as_f16x8((u32x4){mul2(x0[0], t0), mul2(x0[1], t0), mul2(y0[0], t0),
+                                          mul2(y0[1], t0)});
+        const f16x8 a1 = as_f16x8((u32x4){mul2(x1[0], t1), mul2(x1[1], t1), mul2(y1[0], t1),
+                                          mul2(y1[1], t1)});
+        o0 = mfma16(pa, transpose2(a0, a1, sel0), o0);
+        o1 = mfma16(pa, transpose2(a0, a1, sel1), o1);
+    }
+}
+
+// Global loads of one 32-key tile for this lane (rows at or past T read as
+// zero through the buffer range check).
+struct TileLoads {
+    u32x2 kwv[2][4];   // K words 8g + 2j, 8g + 2j + 1 of key n of each block
+    u32x2 ksw[2];      // K scales of key n (4 x 16 bit)
+    u32x2 kbw[2];      // K biases of key n
+    uint32_t wv[2][6]; // V words of group j of key n
+    uint32_t vsb[2];   // V scale of (key n, group j)
+    uint32_t vbb[2];   // V bias of (key n, group j)
+};
+
+__device__ __forceinline__ void load_tile(TileLoads& L, int t0, int n, int j,
+                                          __amdgpu_buffer_rsrc_t kw_r, __amdgpu_buffer_rsrc_t ks_r,
+                                          __amdgpu_buffer_rsrc_t kb_r, __amdgpu_buffer_rsrc_t vw_r,
+                                          __amdgpu_buffer_rsrc_t vs_r, __amdgpu_buffer_rsrc_t vb_r) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const int key = t0 + 16 * blk + n;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            L.kwv[blk][g] = __builtin_amdgcn_raw_buffer_load_b64(kw_r, key * 128 + 32 * g + 8 * j, 0, 0);
+        L.ksw[blk] = __builtin_amdgcn_raw_buffer_load_b64(ks_r, key * 8, 0, 0);
+        L.kbw[blk] = __builtin_amdgcn_raw_buffer_load_b64(kb_r, key * 8, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const u32x2 z = __builtin_amdgcn_raw_buffer_load_b64(vw_r, key * 96 + 24 * j + 8 * k, 0, 0);
+            L.wv[blk][2 * k] = z[0];
+            L.wv[blk][2 * k + 1] = z[1];
+        }
+        L.vsb[blk] = __builtin_amdgcn_raw_buffer_load_b16(vs_r, key * 8 + 2 * j, 0, 0);
+        L.vbb[blk] = __builtin_amdgcn_raw_buffer_load_b16(vb_r, key * 8 + 2 * j, 0, 0);
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(MArgs a) {
+    __shared__ __align__(16) unsigned char smem[kSmemBytes];
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int j = lane >> 4;
+    const int n = lane & 15;
+    const int r = n & 7;                // query row of this lane in the query operands
+    const bool lo_part = n >= 8;
+    const int rb = 4 * (j & 1);         // accumulator rows of this lane: rb .. rb+3
+
+    const int bh = blockIdx.x / a.S;
+    const int split = blockIdx.x - bh * a.S;
+    const int b = bh / a.Hkv;
+    const int kvh = bh - b * a.Hkv;
+    const int T = a.T;
+    const int t_begin = split * a.chunk;
+    const int t_end = (t_begin + a.chunk < T) ? t_begin + a.chunk : T;
+
+    // ---- decode table: entry e = 4 fp16 codes (e >> 3k) & 7 ----
+    for (int e = tid; e < 4096; e += kThreads) {
+        uint32_t h[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            h[k] = __builtin_bit_cast(uint16_t, (_Float16)(float)((e >> (3 * k)) & 7));
+        reinterpret_cast<uint2*>(smem)[e] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    }
+
+    // ---- query row r: rotate, scale by scale*log2(e); lane holds
+    //      qv[g][e] = q'[r][64g + 16j + e] ----
+    const bool row_ok = r < a.G;
+    float qv[4][16];
+    {
+        const int qh = row_ok ? kvh * a.n_rep + r / a.L : kvh * a.n_rep;
+        const int qi = row_ok ? r % a.L : 0;
+        const uint16_t* qrow = a.q + (((int64_t)b * a.Hkv * a.n_rep + qh) * a.L + qi) * kHeadDim;
+        uint2 raw[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb)
+                raw[4 * g + bb] = *reinterpret_cast<const uint2*>(qrow + 4 * (16 * g + 4 * j + bb));
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const uint2 x2 = row_ok ? raw[4 * g + bb] : make_uint2(0u, 0u);
+                float x[4] = {elem_to_f32<DT>(x2.x), elem_to_f32<DT>(x2.x >> 16),
+                              elem_to_f32<DT>(x2.y), elem_to_f32<DT>(x2.y >> 16)};
+                float y[4];
+                if (a.rot != nullptr) {
+                    float Bm[16];
+                    load_block(a.rot, 16 * g + 4 * j + bb, Bm);
+                    rotate4(x, Bm, y);
+                } else {
+                    y[0] = x[0]; y[1] = x[1]; y[2] = x[2]; y[3] = x[3];
+                }
+#pragma unroll
+                for (int c = 0; c < 4; ++c) qv[g][4 * bb + c] = y[c] * a.qscale;
+            }
+    }
+    float mxq = 0.f;
+    float qsum[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            mxq = fmaxf(mxq, fabsf(qv[g][e]));
+            s += qv[g][e];
+        }
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 32);
+        qsum[g] = s;
+    }
+    mxq = fmaxf(mxq, __shfl_xor(mxq, 16));
+    mxq = fmaxf(mxq, __shfl_xor(mxq, 32));
+    int ex = 0;
+    if (mxq > 0.f) (void)frexpf(mxq, &ex);
+    const int E = (mxq > 0.f) ? 15 - ex : 0;
+    // query operands of the score MFMAs (g, h2): slot k holds code ci[k] of
+    // word 8g + 2j + h2, times 1/16 for the slots fed by nibbles 1 and 3
+    f16x8 qa[4][2];
+    {
+        constexpr int ci[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    float x = ldexpf(qv[g][8 * h2 + ci[k]], E);
+                    if (k & 2) x *= 0.0625f;
+                    const _Float16 hi = (_Float16)x;
+                    const _Float16 lo = (_Float16)(x - (float)hi);
+                    qa[g][h2][k] = lo_part ? lo : hi;
+                }
+    }
+    // identical in the 4 waves: wave 0 keeps the copy the tile loop reads
+    unsigned char* qa_lds = smem + kLutBytes;
+    if (wave == 0) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+                *reinterpret_cast<f16x8*>(qa_lds + ((2 * g + h2) * 64 + lane) * 16) = qa[g][h2];
+    }
+    // query operand of the bias MFMA: slots of lane group 0 = the 4 group sums
+    // (hi, then middle limb), lane group 1 = low limb, other groups zero
+    u32x4 qb_op;
+    float gb = 1.0f;  // scale of the bias MFMA result (fp16 caches)
+    if constexpr (DT == RBQ_BF16) {
+        uint32_t hb[4], mb[4], lb[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint32_t u = __float_as_uint(qsum[g]);
+            const float hi = __uint_as_float(u & 0xFFFF0000u);
+            const uint32_t u2 = __float_as_uint(qsum[g] - hi);
+            const float mid = __uint_as_float(u2 & 0xFFFF0000u);
+            hb[g] = u >> 16;
+            mb[g] = u2 >> 16;
+            lb[g] = f32_to_bf16_bits(qsum[g] - hi - mid);
+        }
+        if (j == 0) qb_op = (u32x4){hb[0] | hb[1] << 16, hb[2] | hb[3] << 16, mb[0] | mb[1] << 16,
+                                    mb[2] | mb[3] << 16};
+        else if (j == 1) qb_op = (u32x4){lb[0] | lb[1] << 16, lb[2] | lb[3] << 16, 0u, 0u};
+        else qb_op = (u32x4){0u, 0u, 0u, 0u};
+    } else {
+        // fp16: sums scaled by 2^(E-6) (below 2^15 in magnitude), hi + lo
+        uint32_t hb[4], lb[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float x = ldexpf(qsum[g], E - 6);
+            const _Float16 hi = (_Float16)x;
+            hb[g] = __builtin_bit_cast(uint16_t, hi);
+            lb[g] = __builtin_bit_cast(uint16_t, (_Float16)(x - (float)hi));
+        }
+        if (j == 0) qb_op = (u32x4){hb[0] | hb[1] << 16, hb[2] | hb[3] << 16, lb[0] | lb[1] << 16,
+                                    lb[2] | lb[3] << 16};
+        else qb_op = (u32x4){0u, 0u, 0u, 0u};
+        gb = 0.f;  // set per accumulator row below
+    }
+    // per accumulator row: power-of-two factors and causal visibility
+    float frow[4], grow[4];
+    int vis[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int row = rb + c;
+        const int Er = __shfl(E, row);
+        frow[c] = ldexpf(1.0f, 24 - Er);
+        grow[c] = (DT == RBQ_BF16) ? 1.0f : ldexpf(1.0f, 6 - Er);
+        const bool ok = row < a.G;
+        vis[c] = (ok && a.causal) ? T - a.L + (row % a.L) + 1 : T;
+    }
+    (void)gb;
+    const int vis_min = min(min(vis[0], vis[1]), min(vis[2], vis[3]));
+    // selection operands: column n takes (lane group n>>2, slot n&3) for sel0,
+    // slot 4+(n&3) for sel1; selb: column n<4 takes (lane group n, slot 0)
+    f16x8 sel0, sel1, selb;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const bool mine = j == (n >> 2);
+        sel0[k] = (mine && k == (n & 3)) ? (_Float16)1.0f : (_Float16)0.0f;
+        sel1[k] = (mine && k == 4 + (n & 3)) ? (_Float16)1.0f : (_Float16)0.0f;
+        selb[k] = (k == 0 && j == n) ? (_Float16)1.0f : (_Float16)0.0f;
+    }
+    __syncthreads();  // decode table complete
+
+    const int64_t row0 = (int64_t)bh * a.capacity;
+    const __amdgpu_buffer_rsrc_t kw_r = make_rsrc(a.kw + row0 * kKWords, (uint32_t)T * 128u);
+    const __amdgpu_buffer_rsrc_t ks_r = make_rsrc(a.ks + row0 * kGroups, (uint32_t)T * 8u);
+    const __amdgpu_buffer_rsrc_t kb_r = make_rsrc(a.kb + row0 * kGroups, (uint32_t)T * 8u);
+    const __amdgpu_buffer_rsrc_t vw_r = make_rsrc(a.vw + row0 * kVWords, (uint32_t)T * 96u);
+    const __amdgpu_buffer_rsrc_t vs_r = make_rsrc(a.vs + row0 * kGroups, (uint32_t)T * 8u);
+    const __amdgpu_buffer_rsrc_t vb_r = make_rsrc(a.vb + row0 * kGroups, (uint32_t)T * 8u);
+
+    f32x4 O[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) O[i][0] = O[i][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    f32x4 Ob = {0.f, 0.f, 0.f, 0.f};
+    float m_ref[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    float l_part[4] = {0.f, 0.f, 0.f, 0.f};
+    const unsigned char* lut = smem;
+    float* pst = reinterpret_cast<float*>(smem + kLutBytes + kQaBytes + wave * kPBytes);
+
+    const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
+    TileLoads cur;
+    if (wave < n_tiles) load_tile(cur, t_begin + wave * kTile, n, j, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
+    for (int it = wave; it < n_tiles; it += kWaves) {
+        const int t0 = t_begin + it * kTile;
+        // next tile of this wave in flight while this one is computed
+        TileLoads nxt;
+        if (it + kWaves < n_tiles)
+            load_tile(nxt, t0 + kWaves * kTile, n, j, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
+        const auto& kwv = cur.kwv;
+        const auto& ksw = cur.ksw;
+        const auto& kbw = cur.kbw;
+        const auto& wv = cur.wv;
+        const auto& vsb = cur.vsb;
+        const auto& vbb = cur.vbb;
+
+        // ---- scores: acc[row][key n] per group; scale, hi+lo, bias ----
+        float sc[2][4];
+        const bool full = (t0 + kTile <= t_end) && (t0 + kTile <= vis_min);
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            f32x4 acc[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                acc[g] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const uint32_t w = kwv[blk][g][h2];
+                    const uint32_t w8 = w >> 8;
+                    const u32x4 kv = {w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu,
+                                      w8 & 0x00F000F0u};
+                    const f16x8 qop =
+                        *reinterpret_cast<const f16x8*>(qa_lds + ((2 * g + h2) * 64 + lane) * 16);
+                    acc[g] = mfma16(qop, as_f16x8(kv), acc[g]);
+                }
+            }
+            const u32x4 kbop = {kbw[blk][0], kbw[blk][1], kbw[blk][0], kbw[blk][1]};
+            f32x4 cb;
+            if constexpr (DT == RBQ_BF16) cb = mfma16bf(qb_op, kbop, (f32x4){0.f, 0.f, 0.f, 0.f});
+            else cb = mfma16(as_f16x8(qb_op), as_f16x8(kbop), (f32x4){0.f, 0.f, 0.f, 0.f});
+            const float s0 = meta_f32<DT>(ksw[blk][0], 0), s1 = meta_f32<DT>(ksw[blk][0], 1);
+            const float s2 = meta_f32<DT>(ksw[blk][1], 0), s3 = meta_f32<DT>(ksw[blk][1], 1);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                float t = s0 * acc[0][c];
+                t = fmaf(s1, acc[1][c], t);
+                t = fmaf(s2, acc[2][c], t);
+                t = fmaf(s3, acc[3][c], t);
+                t = add_swap32(t);
+                sc[blk][c] = fmaf(t, frow[c], cb[c] * grow[c]);
+            }
+        }
+        if (!full) {
+            const int kb0 = t0 + n;
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int key = kb0 + 16 * blk;
+                    if (!(key < t_end && key < vis[c])) sc[blk][c] = -INFINITY;
+                }
+        }
+
+        // ---- online softmax per row (base 2), lazy rescale ----
+        float mx[4];
+        bool need_any = false;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            mx[c] = max16(fmaxf(sc[0][c], sc[1][c]));
+            need_any |= mx[c] > m_ref[c] + 8.0f;
+        }
+        if (__any(need_any)) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const bool need = mx[c] > m_ref[c] + 8.0f;
+                const float m_new = need ? mx[c] : m_ref[c];
+                const float alpha = need ? __builtin_amdgcn_exp2f(m_ref[c] - m_new) : 1.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    O[i][0][c] *= alpha;
+                    O[i][1][c] *= alpha;
+                }
+                Ob[c] *= alpha;
+                l_part[c] *= alpha;
+                m_ref[c] = m_new;
+            }
+        }
+        float p[2][4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float mu = (m_ref[c] == -INFINITY) ? 0.f : m_ref[c];
+            p[0][c] = __builtin_amdgcn_exp2f(sc[0][c] - mu);
+            p[1][c] = __builtin_amdgcn_exp2f(sc[1][c] - mu);
+            l_part[c] += p[0][c] + p[1][c];
+        }
+        // P to the key-slot order of the value operands: stage [key][row] in LDS
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+            *reinterpret_cast<float4*>(pst + (16 * blk + n) * kRows + rb) =
+                make_float4(p[blk][0], p[blk][1], p[blk][2], p[blk][3]);
+        f16x8 pa;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float pv = pst[(16 * blk + 4 * j + k) * kRows + r];
+                const _Float16 hi = (_Float16)pv;
+                const _Float16 lo = (_Float16)(pv - (float)hi);
+                pa[4 * blk + k] = lo_part ? lo : hi;
+            }
+
+        // ---- P.V ----
+        f16x2 sv[2], tv[2];
+        u32x4 vbop[2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            _Float16 sh, st = (_Float16)0.0f, bh16;
+            if constexpr (DT == RBQ_BF16) {
+                sh = (_Float16)bf16_bits_to_f32(vsb[blk]);
+                bh16 = (_Float16)bf16_bits_to_f32(vbb[blk]);
+            } else {
+                // head: top 8 significant bits; tail: the other 3 (both exact)
+                sh = __builtin_bit_cast(_Float16, (uint16_t)(vsb[blk] & 0xFFF8u));
+                st = (_Float16)(f16_bits_to_f32(vsb[blk]) - (float)sh);
+                bh16 = __builtin_bit_cast(_Float16, (uint16_t)vbb[blk]);
+            }
+            sv[blk] = (f16x2){sh, sh};
+            tv[blk] = (f16x2){st, st};
+            vbop[blk] = (u32x4){(uint32_t)__builtin_bit_cast(uint16_t, bh16), 0u, 0u, 0u};
+        }
+        Ob = mfma16(pa, transpose2(as_f16x8(vbop[0]), as_f16x8(vbop[1]), selb), Ob);
+        pv_step<DT, 0>(lut, wv[0], wv[1], sv[0], sv[1], tv[0], tv[1], sel0, sel1, pa, O[0][0], O[0][1]);
+        pv_step<DT, 1>(lut, wv[0], wv[1], sv[0], sv[1], tv[0], tv[1], sel0, sel1, pa, O[1][0], O[1][1]);
+        pv_step<DT, 2>(lut, wv[0], wv[1], sv[0], sv[1], tv[0], tv[1], sel0, sel1, pa, O[2][0], O[2][1]);
+        pv_step<DT, 3>(lut, wv[0], wv[1], sv[0], sv[1], tv[0], tv[1], sel0, sel1, pa, O[3][0], O[3][1]);
+        pv_step<DT, 4>(lut, wv[0], wv[1], sv[0], sv[1], tv[0], tv[1], sel0, sel1, pa, O[4][0], O[4][1]);
+        pv_step<DT, 5>(lut, wv[0], wv[1], sv[0], sv[1], tv[0], tv[1], sel0, sel1, pa, O[5][0], O[5][1]);
+        pv_step<DT, 6>(lut, wv[0], wv[1], sv[0], sv[1], tv[0], tv[1], sel0, sel1, pa, O[6][0], O[6][1]);
+        pv_step<DT, 7>(lut, wv[0], wv[1], sv[0], sv[1], tv[0], tv[1], sel0, sel1, pa, O[7][0], O[7][1]);
+        cur = nxt;
+    }
+
+    // ---- wave record: hi + lo rows combined, row sums over the 16 key lanes ----
+    float l_row[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) l_row[c] = sum16(l_part[c]);
+    __syncthreads();  // decode table and P staging no longer needed
+    float* wrec = reinterpret_cast<float*>(smem) + wave * kWaveRecFloats;
+    float* wo = wrec + 2 * kRows + kRows * kGroups;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float ob = add_swap32(Ob[c]);
+        if (j < 2) {
+            if (n == 0) {
+                wrec[rb + c] = m_ref[c];
+                wrec[kRows + rb + c] = l_row[c];
+            }
+            if (n < 4) wrec[2 * kRows + (rb + c) * kGroups + n] = ob;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int sel = 0; sel < 2; ++sel)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float v = add_swap32(O[i][sel][c]);
+                if (j < 2) wo[(rb + c) * kHeadDim + 64 * (n >> 2) + 8 * i + 4 * sel + (n & 3)] = v;
+            }
+    __syncthreads();
+
+    // ---- merge the wave records: thread = (row, 8 columns) ----
+    const int row = tid >> 5;
+    const int d8 = (tid & 31) * 8;
+    const int grp = d8 >> 6;
+    float M = -INFINITY, Ls = 0.f, acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const float* rw = reinterpret_cast<const float*>(smem) + w * kWaveRecFloats;
+        const float bias = rw[2 * kRows + row * kGroups + grp];
+        const float* o = rw + 2 * kRows + kRows * kGroups + row * kHeadDim + d8;
+        float ov[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ov[k] = o[k] + bias;
+        fold(M, Ls, acc, rw[row], rw[kRows + row], ov);
+    }
+
+    // ---- split merge tree; the last step writes the output ----
+    int lvl = 0, idx = split;
+    while (a.n_lvl[lvl] > 1) {
+        const int n_k = a.n_lvl[lvl];
+        float* rp = a.rec + (a.rec_base[lvl] + (int64_t)bh * n_k + idx) * kRecFloats;
+        if ((tid & 31) == 0) st_rec(rp + 2 * row, M, Ls);
+        float* ro = rp + 2 * kRows + row * kHeadDim + d8;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) st_rec(ro + 2 * k, acc[2 * k], acc[2 * k + 1]);
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's record stores are complete
+        __syncthreads();
+        const int g = idx / kFanIn;
+        const int members = (n_k - g * kFanIn < kFanIn) ? n_k - g * kFanIn : kFanIn;
+        const int n_groups = (n_k + kFanIn - 1) / kFanIn;
+        if (tid == 0) {
+            int* c = a.cnt + a.cnt_base[lvl] + bh * n_groups + g;
+            const int old = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const bool last = old == members - 1;
+            if (last) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = last;
+        }
+        __syncthreads();
+        if (!s_last) return;
+        M = -INFINITY;
+        Ls = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+        const float* base = a.rec + (a.rec_base[lvl] + (int64_t)bh * n_k + g * kFanIn) * kRecFloats;
+        // members are read 8 at a time with all their loads in flight
+        for (int m0 = 0; m0 < members; m0 += 8) {
+            float2 ml[8], o01[8], o23[8], o45[8], o67[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int mbr = (m0 + k < members) ? m0 + k : m0;
+                const float* rm = base + (int64_t)mbr * kRecFloats;
+                const float* o = rm + 2 * kRows + row * kHeadDim + d8;
+                ml[k] = ld_rec(rm + 2 * row);
+                o01[k] = ld_rec(o);
+                o23[k] = ld_rec(o + 2);
+                o45[k] = ld_rec(o + 4);
+                o67[k] = ld_rec(o + 6);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float ov[8] = {o01[k].x, o01[k].y, o23[k].x, o23[k].y,
+                                     o45[k].x, o45[k].y, o67[k].x, o67[k].y};
+                if (m0 + k < members) fold(M, Ls, acc, ml[k].x, ml[k].y, ov);
+            }
+        }
+        idx = g;
+        ++lvl;
+    }
+
+    if (row < a.G) {
+        const float inv = 1.0f / Ls;
+        const int h = kvh * a.n_rep + row / a.L;
+        const int i = row % a.L;
+        float* dst = a.out + (((int64_t)b * a.Hkv * a.n_rep + h) * a.L + i) * kHeadDim + d8;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            float y[4] = {acc[4 * half] * inv, acc[4 * half + 1] * inv, acc[4 * half + 2] * inv,
+                          acc[4 * half + 3] * inv};
+            float z[4];
+            if (a.rot != nullptr) {
+                float Bm[16];
+                load_block(a.rot, d8 / 4 + half, Bm);
+                unrotate4(y, Bm, z);
+            } else {
+                z[0] = y[0]; z[1] = y[1]; z[2] = y[2]; z[3] = y[3];
+            }
+            reinterpret_cast<float4*>(dst)[half] = make_float4(z[0], z[1], z[2], z[3]);
+        }
+    }
+}
+
+}  // namespace
+
+// ---- host side: planning and launch ----
+
+int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, MfmaPlan* p) {
+    const int n_rep = H_q / c->H_kv;
+    const int64_t T = c->offset;
+    const int64_t BH = (int64_t)c->B * c->H_kv;
+    int64_t S = splits;
+    if (S == 0) {
+        S = (2 * 256 + BH - 1) / BH;  // about two workgroups per compute unit
+        const int64_t max_s = (T + 127) / 128;
+        if (S > max_s) S = max_s;
+    }
+    if (S < 1) S = 1;
+    int64_t chunk = (T + S - 1) / S;
+    chunk = (chunk + kTile - 1) / kTile * kTile;
+    S = (T + chunk - 1) / chunk;
+    if (BH * S > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
+    if (T * (int64_t)(kKWords * 4) > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;  // 32-bit buffer offsets
+    p->S = (int)S;
+    p->chunk = chunk;
+    p->levels = 0;
+    int64_t n = S, recs = 0, cnts = 0;
+    while (n > 1) {
+        if (p->levels >= kMaxLevels - 1) return RBQ_EUNSUPPORTED;
+        p->n_lvl[p->levels] = (int)n;
+        p->rec_base[p->levels] = recs;
+        p->cnt_base[p->levels] = (int)cnts;
+        recs += BH * n;
+        const int64_t groups = (n + kFanIn - 1) / kFanIn;
+        cnts += BH * groups;
+        n = groups;
+        ++p->levels;
+    }
+    p->n_lvl[p->levels] = 1;
+    if (cnts * (int64_t)sizeof(int) > kCounterBytes) return RBQ_EUNSUPPORTED;
+    (void)n_rep;
+    (void)L;
+    p->ws_bytes = (S == 1) ? 0 : (size_t)kCounterBytes + (size_t)recs * kRecFloats * sizeof(float);
+    return RBQ_OK;
+}
+
+int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, float scale,
+                int32_t causal, const float* rot_blocks, float* out, const MfmaPlan& p, void* ws,
+                void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    MArgs a;
+    a.q = (const uint16_t*)q;
+    a.kw = c->k_words;
+    a.ks = (const uint16_t*)c->k_scales;
+    a.kb = (const uint16_t*)c->k_biases;
+    a.vw = c->v_words;
+    a.vs = (const uint16_t*)c->v_scales;
+    a.vb = (const uint16_t*)c->v_biases;
+    a.rot = rot_blocks;
+    a.out = out;
+    a.cnt = (int*)ws;
+    a.rec = ws ? (float*)((char*)ws + kCounterBytes) : nullptr;
+    a.capacity = c->capacity;
+    a.T = (int)c->offset;
+    a.chunk = (int)p.chunk;
+    a.Hkv = c->H_kv;
+    a.n_rep = H_q / c->H_kv;
+    a.L = L;
+    a.G = a.n_rep * L;
+    a.S = p.S;
+    a.causal = causal ? 1 : 0;
+    for (int k = 0; k < kMaxLevels; ++k) {
+        a.n_lvl[k] = (k <= p.levels) ? p.n_lvl[k] : 1;
+        a.rec_base[k] = (k < p.levels) ? p.rec_base[k] : 0;
+        a.cnt_base[k] = (k < p.levels) ? p.cnt_base[k] : 0;
+    }
+    a.qscale = scale * kLog2e;
+    const int64_t BH = (int64_t)c->B * c->H_kv;
+    const dim3 grid((unsigned)(BH * p.S)), block(kThreads);
+    if (c->dtype == RBQ_BF16)
+        hipLaunchKernelGGL(attn_mfma_kernel<RBQ_BF16>, grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL(attn_mfma_kernel<RBQ_F16>, grid, block, 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        set_hip_error((int)e);
+        return RBQ_EHIP;
+    }
+    return RBQ_OK;
+}
+
+}  // namespace rbq

@@ -25,7 +25,28 @@ void set_hip_error(int err);
 // and the supported configuration (RBQ_EUNSUPPORTED otherwise).
 int check_cache(const rbq_kv_cache* c);
 
-// Split count chosen when the caller passes 0.
+// Split count chosen when the caller passes 0 (VALU attention path).
 int32_t auto_splits(const rbq_kv_cache* c, int32_t H_q, int32_t L);
+
+// Launch plan of the matrix-core attention path (up to 8 query rows per kv
+// head): key splits, their length, and the tree of partial-record merges.
+constexpr int kMfmaMaxRows = 8;
+// The first kWsCounterBytes of every attention workspace hold the merge
+// counters of the matrix-core path (zero between calls); partial results of
+// either path start after them.
+constexpr size_t kWsCounterBytes = 65536;
+struct MfmaPlan {
+    int S;
+    int64_t chunk;
+    int levels;          // merge levels with more than one record
+    int n_lvl[8];        // records per (b, kv head) at each level
+    int64_t rec_base[8]; // first record of each level
+    int cnt_base[8];     // first counter of each level
+    size_t ws_bytes;
+};
+int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, MfmaPlan* p);
+int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, float scale,
+                int32_t causal, const float* rot_blocks, float* out, const MfmaPlan& p, void* ws,
+                void* stream);
 
 }  // namespace rbq

@@ -279,18 +279,24 @@ def test_quantizer_special_groups_without_rotation(dtype, dev):
 
 def test_error_statuses_through_the_binding(dev, rot):
     c = rbq.RotatedQuantKVCache(1, 2, device=dev, rot=rot)
-    k = W.random_rows(8, (1, 2, 10, 256), "bf16").to(dev)
+    k = W.random_rows(8, (1, 2, 300, 256), "bf16").to(dev)
     c.append(k, k)
     q = W.random_rows(9, (1, 4, 1, 256), "bf16").to(dev)
     with pytest.raises(capi.RbqError) as e:
         c.attend(W.random_rows(9, (1, 3, 1, 256), "bf16").to(dev))
     assert e.value.status == capi.RBQ_EINVAL
     with pytest.raises(capi.RbqError) as e:
-        c.attend(W.random_rows(9, (1, 4, 11, 256), "bf16").to(dev))
+        c.attend(W.random_rows(9, (1, 4, 301, 256), "bf16").to(dev))
     assert e.value.status == capi.RBQ_ERANGE
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    need = capi.rbq_quant_attn_workspace_bytes(c.desc, 4, 1, 4)
+    assert need > 0
     with pytest.raises(capi.RbqError) as e:
         capi.rbq_quant_attn_decode(c.desc, q, 1 / 16, True, rot, out, splits=4, ws=None)
+    assert e.value.status == capi.RBQ_EWORKSPACE
+    small = torch.zeros(need - 1, dtype=torch.uint8, device=dev)
+    with pytest.raises(capi.RbqError) as e:
+        capi.rbq_quant_attn_decode(c.desc, q, 1 / 16, True, rot, out, splits=4, ws=small)
     assert e.value.status == capi.RBQ_EWORKSPACE
     # appending beyond capacity through the raw call writes nothing
     off = c.offset
