@@ -4,11 +4,12 @@
 // 8 query rows per kv head (GQA group x verify block).
 //
 // Decomposition: one workgroup of 4 wave64s per (b, kv head, key split);
-// each wave walks 32-key tiles of the split with an online softmax (base 2,
-// rescaled only when the running maximum grows by more than 2^8), the 4 wave
-// partials are merged in LDS, and the split partials are merged in-kernel by
-// the last-arriving workgroup of each group of 16 (a tree of such merges),
-// whose last step normalises and rotates the output back.
+// each wave walks 32-key tiles of the split (the next tile's loads in flight)
+// with an online softmax (base 2, rescaled only when the running maximum
+// grows by more than 2^8); the 4 wave partials are merged in LDS, and the
+// split partials are merged in-kernel by the last-arriving workgroup of each
+// group of 32 (a tree of such merges), whose last step normalises and
+// rotates the output back.
 //
 // All products run as 16x16x32 MFMAs.  Lane l = 16 j + n: j selects a k-slot
 // group of the operands and a quarter of the accumulator rows, n a column.
@@ -21,15 +22,18 @@
 //   accumulator per 64-value group g; score = s_g acc_g (fp32, per key) plus
 //   sum_g b_g sum_{d in g} q_d, the latter an MFMA of the raw bias words
 //   against the query's group sums (split into exact limbs).
-// Values: the 3-bit codes of 16 keys are decoded 4 at a time through a
-//   4096-entry LDS table (12 stream bits -> 4 fp16 codes), multiplied by the
-//   key's group scale in fp16 (exact for bf16 scales: 3 + 8 significant bits;
-//   fp16 scales are split into an exact 8-bit head and 3-bit tail), and
-//   transposed key-major -> column-major by an MFMA against a 0/1 selection
-//   matrix; its accumulator layout is the B layout of the P.V MFMA, whose A
-//   is P split hi + lo over the 16 rows (staged through LDS to the key-slot
-//   order of that B layout).  The group bias enters through the same
-//   transpose and one more MFMA as sum_t p_t b_{t,g}.
+// Values: B = V codes of 8 keys per lane group x 16 columns.  The LDS
+//   transposing read (ds_read_b64_tr_b16) returns, to lane i of a 16-lane
+//   group, element i & 3 of the 8 bytes addressed by lanes 4e + (i >> 2),
+//   e = 0..3.  Lane 4e + q addresses the entry of a 4096-entry decode table
+//   (12 packed stream bits -> 4 fp16 codes) for chunk t of group q of key e,
+//   so one read both decodes and transposes: lane i receives the codes of
+//   4 keys in column 64 (i >> 2) + 4 t + (i & 3).  The same read on small
+//   per-wave tables moves the per-(key, group) scales and biases, and P
+//   (split hi + lo over the 16 rows), into the matching layouts.  Codes are
+//   scaled in fp16 (exact for bf16 scales: 3 + 8 significant bits; fp16
+//   scales are split into an exact 8-bit head and 3-bit tail); the group bias
+//   enters as sum_t p_t b_{t,g} through one more MFMA.
 // Precondition of the fp16 value path: V group ranges (max - min of the
 // rotated values) and |V bias| stay below 65504; larger values overflow to
 // inf and show up as non-finite outputs.
@@ -46,6 +50,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -56,8 +62,12 @@ constexpr int kRecFloats = 2 * kRows + kRows * kHeadDim;   // (m, l)[8], o[8][25
 constexpr int kWaveRecFloats = 2 * kRows + kRows * kGroups + kRows * kHeadDim;
 constexpr int kLutBytes = 4096 * 8;
 constexpr int kQaBytes = 8 * 64 * 16;                      // score query operands, per lane
-constexpr int kPBytes = kTile * kRows * 4;                 // per-wave P staging [key][row]
-constexpr int kLoopSmem = kLutBytes + kQaBytes + kWaves * kPBytes;
+// per wave: scale / scale-tail / bias tables [2 blocks][64 lanes] x 8 B and
+// P hi/lo [2 blocks][16 keys][2 parts][2 row quads] x 8 B
+constexpr int kStageBytes = 2 * 64 * 8;
+constexpr int kP16Bytes = 2 * 16 * 2 * 2 * 8;
+constexpr int kWaveBytes = 3 * kStageBytes + kP16Bytes;
+constexpr int kLoopSmem = kLutBytes + kQaBytes + kWaves * kWaveBytes;
 constexpr int kRecSmem = kWaves * kWaveRecFloats * 4;
 constexpr int kSmemBytes = kLoopSmem > kRecSmem ? kLoopSmem : kRecSmem;
 constexpr int kCounterBytes = (int)kWsCounterBytes;
@@ -101,6 +111,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
                                              0x00020000);
 }
 
+// LDS transposing read of 8 bytes at byte offset `off` of the shared buffer:
+// lane i of each 16-lane group gets element i & 3 of the 8 bytes addressed by
+// lanes 4e + (i >> 2) of its group, as element e.
+__device__ __forceinline__ u32x2 tr16(unsigned char* smem, uint32_t off) {
+    lds_u8* base = (lds_u8*)smem;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(base + off));
+    return __builtin_bit_cast(u32x2, v);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
@@ -131,6 +151,10 @@ __device__ __forceinline__ uint32_t pk_f16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
 }
 
+__device__ __forceinline__ uint32_t mul2(uint32_t a, uint32_t s) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a) * __builtin_bit_cast(f16x2, s));
+}
+
 template <int DT>
 __device__ __forceinline__ float meta_f32(uint32_t word, int half) {
     return elem_to_f32<DT>(half ? word >> 16 : word);
@@ -148,16 +172,6 @@ __device__ __forceinline__ uint32_t chunk_offset(const uint32_t w[6]) {
         if constexpr (wi + 1 < 6) return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & 0x7FF8u;
         else return (w[wi] >> sh) & 0x7FF8u;
     }
-}
-
-template <int C>
-__device__ __forceinline__ u32x2 lut_entry(const unsigned char* lut, const uint32_t w[6]) {
-    const uint2 e = *reinterpret_cast<const uint2*>(lut + chunk_offset<C>(w));
-    return (u32x2){e.x, e.y};
-}
-
-__device__ __forceinline__ uint32_t mul2(uint32_t a, f16x2 s) {
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a) * s);
 }
 
 // Split-partial records are exchanged between workgroups of one launch,
@@ -195,54 +209,16 @@ __device__ __forceinline__ void fold(float& M, float& Ls, float acc[8], float m,
     for (int k = 0; k < 8; ++k) acc[k] = fmaf(w, o[k], acc[k]);
 }
 
-// Transpose a key-major operand (A: key rows, 8 k-slots per lane group)
-// into the B layout of the P.V MFMA for both 16-key blocks: result slots =
-// keys 4j..4j+3 of block 0, then of block 1, column n = the selected slot.
-__device__ __forceinline__ f16x8 transpose2(f16x8 a0, f16x8 a1, f16x8 sel) {
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    const f32x4 c0 = mfma16(a0, sel, z);
-    const f32x4 c1 = mfma16(a1, sel, z);
-    const u32x4 b = {pk_f16(c0[0], c0[1]), pk_f16(c0[2], c0[3]), pk_f16(c1[0], c1[1]),
-                     pk_f16(c1[2], c1[3])};
-    return as_f16x8(b);
-}
-
-// P.V for codes 8i..8i+7 of every group: decode (both blocks), scale,
-// transpose, accumulate into the two output tiles of step i.
-template <int DT, int I>
-__device__ __forceinline__ void pv_step(const unsigned char* lut, const uint32_t wv0[6],
-                                        const uint32_t wv1[6], f16x2 s0, f16x2 s1, f16x2 t0,
-                                        f16x2 t1, f16x8 sel0, f16x8 sel1, f16x8 pa, f32x4& o0,
-                                        f32x4& o1) {
-    const u32x2 x0 = lut_entry<2 * I>(lut, wv0), y0 = lut_entry<2 * I + 1>(lut, wv0);
-    const u32x2 x1 = lut_entry<2 * I>(lut, wv1), y1 = lut_entry<2 * I + 1>(lut, wv1);
-    {
-        const f16x8 a0 = as_f16x8((u32x4){mul2(x0[0], s0), mul2(x0[1], s0), mul2(y0[0], s0),
-                                          mul2(y0[1], s0)});
-        const f16x8 a1 = as_f16x8((u32x4){mul2(x1[0], s1), mul2(x1[1], s1), mul2(y1[0], s1),
-                                          mul2(y1[1], s1)});
-        o0 = mfma16(pa, transpose2(a0, a1, sel0), o0);
-        o1 = mfma16(pa, transpose2(a0, a1, sel1), o1);
-    }
-    if constexpr (DT == RBQ_F16) {
-        const f16x8 a0 = as_f16x8((u32x4){mul2(x0[0], t0), mul2(x0[1], t0), mul2(y0[0], t0),
-                                          mul2(y0[1], t0)});
-        const f16x8 a1 = as_f16x8((u32x4){mul2(x1[0], t1), mul2(x1[1], t1), mul2(y1[0], t1),
-                                          mul2(y1[1], t1)});
-        o0 = mfma16(pa, transpose2(a0, a1, sel0), o0);
-        o1 = mfma16(pa, transpose2(a0, a1, sel1), o1);
-    }
-}
-
 // Global loads of one 32-key tile for this lane (rows at or past T read as
-// zero through the buffer range check).
+// zero through the buffer range check).  K data: key n of each block; V
+// data: group n & 3 of key 4j + (n >> 2) of each block.
 struct TileLoads {
-    u32x2 kwv[2][4];   // K words 8g + 2j, 8g + 2j + 1 of key n of each block
-    u32x2 ksw[2];      // K scales of key n (4 x 16 bit)
-    u32x2 kbw[2];      // K biases of key n
-    uint32_t wv[2][6]; // V words of group j of key n
-    uint32_t vsb[2];   // V scale of (key n, group j)
-    uint32_t vbb[2];   // V bias of (key n, group j)
+    u32x2 kwv[2][4];   // K words 8g + 2j, 8g + 2j + 1
+    u32x2 ksw[2];      // K scales (4 x 16 bit)
+    u32x2 kbw[2];      // K biases
+    uint32_t wv[2][6]; // V words of the lane's (key, group)
+    uint32_t vsb[2];   // V scale of the lane's (key, group)
+    uint32_t vbb[2];   // V bias of the lane's (key, group)
 };
 
 __device__ __forceinline__ void load_tile(TileLoads& L, int t0, int n, int j,
@@ -257,14 +233,35 @@ __device__ __forceinline__ void load_tile(TileLoads& L, int t0, int n, int j,
             L.kwv[blk][g] = __builtin_amdgcn_raw_buffer_load_b64(kw_r, key * 128 + 32 * g + 8 * j, 0, 0);
         L.ksw[blk] = __builtin_amdgcn_raw_buffer_load_b64(ks_r, key * 8, 0, 0);
         L.kbw[blk] = __builtin_amdgcn_raw_buffer_load_b64(kb_r, key * 8, 0, 0);
+        const int vkey = t0 + 16 * blk + 4 * j + (n >> 2);
+        const int vg = n & 3;
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
-            const u32x2 z = __builtin_amdgcn_raw_buffer_load_b64(vw_r, key * 96 + 24 * j + 8 * k, 0, 0);
+            const u32x2 z =
+                __builtin_amdgcn_raw_buffer_load_b64(vw_r, vkey * 96 + 24 * vg + 8 * k, 0, 0);
             L.wv[blk][2 * k] = z[0];
             L.wv[blk][2 * k + 1] = z[1];
         }
-        L.vsb[blk] = __builtin_amdgcn_raw_buffer_load_b16(vs_r, key * 8 + 2 * j, 0, 0);
-        L.vbb[blk] = __builtin_amdgcn_raw_buffer_load_b16(vb_r, key * 8 + 2 * j, 0, 0);
+        L.vsb[blk] = __builtin_amdgcn_raw_buffer_load_b16(vs_r, vkey * 8 + 2 * vg, 0, 0);
+        L.vbb[blk] = __builtin_amdgcn_raw_buffer_load_b16(vb_r, vkey * 8 + 2 * vg, 0, 0);
+    }
+}
+
+// P.V for output tile t (columns 64 q + 4 t + (0..3), q = 0..3): decode and
+// transpose the codes of both 16-key blocks in one read each, scale, MFMA.
+template <int DT, int TT>
+__device__ __forceinline__ void pv_tile(unsigned char* smem, const uint32_t wv0[6],
+                                        const uint32_t wv1[6], const u32x2 sc[2],
+                                        const u32x2 st[2], f16x8 pa, f32x4& o) {
+    const u32x2 r0 = tr16(smem, chunk_offset<TT>(wv0));
+    const u32x2 r1 = tr16(smem, chunk_offset<TT>(wv1));
+    const u32x4 b = {mul2(r0[0], sc[0][0]), mul2(r0[1], sc[0][1]), mul2(r1[0], sc[1][0]),
+                     mul2(r1[1], sc[1][1])};
+    o = mfma16(pa, as_f16x8(b), o);
+    if constexpr (DT == RBQ_F16) {
+        const u32x4 e = {mul2(r0[0], st[0][0]), mul2(r0[1], st[0][1]), mul2(r1[0], st[1][0]),
+                         mul2(r1[1], st[1][1])};
+        o = mfma16(pa, as_f16x8(e), o);
     }
 }
 
@@ -298,7 +295,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             h[k] = __builtin_bit_cast(uint16_t, (_Float16)(float)((e >> (3 * k)) & 7));
         reinterpret_cast<uint2*>(smem)[e] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
     }
-
     // ---- query row r: rotate, scale by scale*log2(e); lane holds
     //      qv[g][e] = q'[r][64g + 16j + e] ----
     const bool row_ok = r < a.G;
@@ -427,17 +423,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     (void)gb;
     const int vis_min = min(min(vis[0], vis[1]), min(vis[2], vis[3]));
-    // selection operands: column n takes (lane group n>>2, slot n&3) for sel0,
-    // slot 4+(n&3) for sel1; selb: column n<4 takes (lane group n, slot 0)
-    f16x8 sel0, sel1, selb;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const bool mine = j == (n >> 2);
-        sel0[k] = (mine && k == (n & 3)) ? (_Float16)1.0f : (_Float16)0.0f;
-        sel1[k] = (mine && k == 4 + (n & 3)) ? (_Float16)1.0f : (_Float16)0.0f;
-        selb[k] = (k == 0 && j == n) ? (_Float16)1.0f : (_Float16)0.0f;
-    }
-    __syncthreads();  // decode table complete
+    __syncthreads();  // decode table and query operands complete
 
     const int64_t row0 = (int64_t)bh * a.capacity;
     const __amdgpu_buffer_rsrc_t kw_r = make_rsrc(a.kw + row0 * kKWords, (uint32_t)T * 128u);
@@ -447,14 +433,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const __amdgpu_buffer_rsrc_t vs_r = make_rsrc(a.vs + row0 * kGroups, (uint32_t)T * 8u);
     const __amdgpu_buffer_rsrc_t vb_r = make_rsrc(a.vb + row0 * kGroups, (uint32_t)T * 8u);
 
-    f32x4 O[8][2];
+    // per-wave staging for the transposing reads (byte offsets in smem)
+    const uint32_t wbase = kLutBytes + kQaBytes + wave * kWaveBytes;
+    const uint32_t s_off = wbase;                      // scales (or scale heads)
+    const uint32_t t_off = wbase + kStageBytes;        // scale tails (fp16 caches)
+    const uint32_t b_off = wbase + 2 * kStageBytes;    // biases
+    const uint32_t p_off = wbase + 3 * kStageBytes;    // P hi/lo
+    // P slot of (block, key, part, row quad)
+    auto p_slot = [&](int blk, int key, int part, int quad) -> uint32_t {
+        return p_off + ((((blk * 16 + key) * 2 + part) * 2 + quad) << 3);
+    };
+
+    f32x4 O[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) O[i][0] = O[i][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 16; ++t) O[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
     f32x4 Ob = {0.f, 0.f, 0.f, 0.f};
     float m_ref[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     float l_part[4] = {0.f, 0.f, 0.f, 0.f};
-    const unsigned char* lut = smem;
-    float* pst = reinterpret_cast<float*>(smem + kLutBytes + kQaBytes + wave * kPBytes);
 
     const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
     TileLoads cur;
@@ -465,12 +460,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         TileLoads nxt;
         if (it + kWaves < n_tiles)
             load_tile(nxt, t0 + kWaves * kTile, n, j, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
-        const auto& kwv = cur.kwv;
-        const auto& ksw = cur.ksw;
-        const auto& kbw = cur.kbw;
-        const auto& wv = cur.wv;
-        const auto& vsb = cur.vsb;
-        const auto& vbb = cur.vbb;
+
+        // ---- value scales and biases of the lane's (key, group) -> staging ----
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            uint32_t sh, st = 0u, bb;
+            if constexpr (DT == RBQ_BF16) {
+                sh = __builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(cur.vsb[blk]));
+                bb = __builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(cur.vbb[blk]));
+            } else {
+                // head: top 8 significant bits; tail: the other 3 (both exact)
+                sh = cur.vsb[blk] & 0xFFF8u;
+                st = __builtin_bit_cast(uint16_t, (_Float16)(f16_bits_to_f32(cur.vsb[blk]) -
+                                                             f16_bits_to_f32(sh)));
+                bb = cur.vbb[blk] & 0xFFFFu;
+            }
+            const uint32_t off = (blk * 64 + lane) << 3;
+            *reinterpret_cast<uint2*>(smem + s_off + off) = make_uint2(sh * 0x10001u, sh * 0x10001u);
+            if constexpr (DT == RBQ_F16)
+                *reinterpret_cast<uint2*>(smem + t_off + off) = make_uint2(st * 0x10001u, st * 0x10001u);
+            *reinterpret_cast<uint2*>(smem + b_off + off) = make_uint2(bb * 0x10001u, bb * 0x10001u);
+        }
 
         // ---- scores: acc[row][key n] per group; scale, hi+lo, bias ----
         float sc[2][4];
@@ -483,7 +493,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 acc[g] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) {
-                    const uint32_t w = kwv[blk][g][h2];
+                    const uint32_t w = cur.kwv[blk][g][h2];
                     const uint32_t w8 = w >> 8;
                     const u32x4 kv = {w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu,
                                       w8 & 0x00F000F0u};
@@ -492,12 +502,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     acc[g] = mfma16(qop, as_f16x8(kv), acc[g]);
                 }
             }
-            const u32x4 kbop = {kbw[blk][0], kbw[blk][1], kbw[blk][0], kbw[blk][1]};
+            const u32x4 kbop = {cur.kbw[blk][0], cur.kbw[blk][1], cur.kbw[blk][0], cur.kbw[blk][1]};
             f32x4 cb;
             if constexpr (DT == RBQ_BF16) cb = mfma16bf(qb_op, kbop, (f32x4){0.f, 0.f, 0.f, 0.f});
             else cb = mfma16(as_f16x8(qb_op), as_f16x8(kbop), (f32x4){0.f, 0.f, 0.f, 0.f});
-            const float s0 = meta_f32<DT>(ksw[blk][0], 0), s1 = meta_f32<DT>(ksw[blk][0], 1);
-            const float s2 = meta_f32<DT>(ksw[blk][1], 0), s3 = meta_f32<DT>(ksw[blk][1], 1);
+            const float s0 = meta_f32<DT>(cur.ksw[blk][0], 0), s1 = meta_f32<DT>(cur.ksw[blk][0], 1);
+            const float s2 = meta_f32<DT>(cur.ksw[blk][1], 0), s3 = meta_f32<DT>(cur.ksw[blk][1], 1);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 float t = s0 * acc[0][c];
@@ -534,67 +544,76 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 const float m_new = need ? mx[c] : m_ref[c];
                 const float alpha = need ? __builtin_amdgcn_exp2f(m_ref[c] - m_new) : 1.0f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    O[i][0][c] *= alpha;
-                    O[i][1][c] *= alpha;
-                }
+                for (int t = 0; t < 16; ++t) O[t][c] *= alpha;
                 Ob[c] *= alpha;
                 l_part[c] *= alpha;
                 m_ref[c] = m_new;
             }
         }
-        float p[2][4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const float mu = (m_ref[c] == -INFINITY) ? 0.f : m_ref[c];
-            p[0][c] = __builtin_amdgcn_exp2f(sc[0][c] - mu);
-            p[1][c] = __builtin_amdgcn_exp2f(sc[1][c] - mu);
-            l_part[c] += p[0][c] + p[1][c];
-        }
-        // P to the key-slot order of the value operands: stage [key][row] in LDS
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-            *reinterpret_cast<float4*>(pst + (16 * blk + n) * kRows + rb) =
-                make_float4(p[blk][0], p[blk][1], p[blk][2], p[blk][3]);
-        f16x8 pa;
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float pv = pst[(16 * blk + 4 * j + k) * kRows + r];
-                const _Float16 hi = (_Float16)pv;
-                const _Float16 lo = (_Float16)(pv - (float)hi);
-                pa[4 * blk + k] = lo_part ? lo : hi;
-            }
-
-        // ---- P.V ----
-        f16x2 sv[2], tv[2];
-        u32x4 vbop[2];
+        // p in fp16 hi + lo for rows rb..rb+3 and key n of each block
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-            _Float16 sh, st = (_Float16)0.0f, bh16;
-            if constexpr (DT == RBQ_BF16) {
-                sh = (_Float16)bf16_bits_to_f32(vsb[blk]);
-                bh16 = (_Float16)bf16_bits_to_f32(vbb[blk]);
-            } else {
-                // head: top 8 significant bits; tail: the other 3 (both exact)
-                sh = __builtin_bit_cast(_Float16, (uint16_t)(vsb[blk] & 0xFFF8u));
-                st = (_Float16)(f16_bits_to_f32(vsb[blk]) - (float)sh);
-                bh16 = __builtin_bit_cast(_Float16, (uint16_t)vbb[blk]);
+            uint32_t hi2[2], lo2[2];
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                float p2[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int c = 2 * c2 + u;
+                    const float mu = (m_ref[c] == -INFINITY) ? 0.f : m_ref[c];
+                    p2[u] = __builtin_amdgcn_exp2f(sc[blk][c] - mu);
+                    l_part[c] += p2[u];
+                }
+                const _Float16 h0 = (_Float16)p2[0], h1 = (_Float16)p2[1];
+                const _Float16 e0 = (_Float16)(p2[0] - (float)h0), e1 = (_Float16)(p2[1] - (float)h1);
+                hi2[c2] = __builtin_bit_cast(uint32_t, (f16x2){h0, h1});
+                lo2[c2] = __builtin_bit_cast(uint32_t, (f16x2){e0, e1});
             }
-            sv[blk] = (f16x2){sh, sh};
-            tv[blk] = (f16x2){st, st};
-            vbop[blk] = (u32x4){(uint32_t)__builtin_bit_cast(uint16_t, bh16), 0u, 0u, 0u};
+            if (j < 2) {
+                *reinterpret_cast<uint2*>(smem + p_slot(blk, n, 0, j)) = make_uint2(hi2[0], hi2[1]);
+                *reinterpret_cast<uint2*>(smem + p_slot(blk, n, 1, j)) = make_uint2(lo2[0], lo2[1]);
+            }
         }
-        Ob = mfma16(pa, transpose2(as_f16x8(vbop[0]), as_f16x8(vbop[1]), selb), Ob);
-        pv_step<DT, 0>(lut, wv[0], wv[1], sv[0], sv[1], tv[0], tv[1], sel0, sel1, pa, O[0][0], O[0][1]);
-        pv_step<DT, 1>(lut, wv[0], wv[1], sv[0], sv[1], tv[0], tv[1], sel0, sel1, pa, O[1][0], O[1][1]);
-        pv_step<DT, 2>(lut, wv[0], wv[1], sv[0], sv[1], tv[0], tv[1], sel0, sel1, pa, O[2][0], O[2][1]);
-        pv_step<DT, 3>(lut, wv[0], wv[1], sv[0], sv[1], tv[0], tv[1], sel0, sel1, pa, O[3][0], O[3][1]);
-        pv_step<DT, 4>(lut, wv[0], wv[1], sv[0], sv[1], tv[0], tv[1], sel0, sel1, pa, O[4][0], O[4][1]);
-        pv_step<DT, 5>(lut, wv[0], wv[1], sv[0], sv[1], tv[0], tv[1], sel0, sel1, pa, O[5][0], O[5][1]);
-        pv_step<DT, 6>(lut, wv[0], wv[1], sv[0], sv[1], tv[0], tv[1], sel0, sel1, pa, O[6][0], O[6][1]);
-        pv_step<DT, 7>(lut, wv[0], wv[1], sv[0], sv[1], tv[0], tv[1], sel0, sel1, pa, O[7][0], O[7][1]);
+        // A operand of P.V: row n (hi rows 0-7, lo rows 8-15) x keys 4j + e of
+        // both blocks; lane 4e + q addresses (key 4j + e, part q >> 1, quad q & 1)
+        f16x8 pa;
+        {
+            const int e = n >> 2, q = n & 3;
+            const u32x2 a0 = tr16(smem, p_slot(0, 4 * j + e, q >> 1, q & 1));
+            const u32x2 a1 = tr16(smem, p_slot(1, 4 * j + e, q >> 1, q & 1));
+            pa = as_f16x8((u32x4){a0[0], a0[1], a1[0], a1[1]});
+        }
+
+        // ---- P.V ----
+        const uint32_t own = (uint32_t)lane << 3;
+        u32x2 sc2[2], st2[2] = {{0u, 0u}, {0u, 0u}};
+        sc2[0] = tr16(smem, s_off + own);
+        sc2[1] = tr16(smem, s_off + 512 + own);
+        if constexpr (DT == RBQ_F16) {
+            st2[0] = tr16(smem, t_off + own);
+            st2[1] = tr16(smem, t_off + 512 + own);
+        }
+        {
+            const u32x2 b0 = tr16(smem, b_off + own);
+            const u32x2 b1 = tr16(smem, b_off + 512 + own);
+            Ob = mfma16(pa, as_f16x8((u32x4){b0[0], b0[1], b1[0], b1[1]}), Ob);
+        }
+        pv_tile<DT, 0>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[0]);
+        pv_tile<DT, 1>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[1]);
+        pv_tile<DT, 2>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[2]);
+        pv_tile<DT, 3>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[3]);
+        pv_tile<DT, 4>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[4]);
+        pv_tile<DT, 5>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[5]);
+        pv_tile<DT, 6>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[6]);
+        pv_tile<DT, 7>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[7]);
+        pv_tile<DT, 8>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[8]);
+        pv_tile<DT, 9>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[9]);
+        pv_tile<DT, 10>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[10]);
+        pv_tile<DT, 11>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[11]);
+        pv_tile<DT, 12>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[12]);
+        pv_tile<DT, 13>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[13]);
+        pv_tile<DT, 14>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[14]);
+        pv_tile<DT, 15>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[15]);
         cur = nxt;
     }
 
@@ -602,7 +621,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     float l_row[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) l_row[c] = sum16(l_part[c]);
-    __syncthreads();  // decode table and P staging no longer needed
+    __syncthreads();  // decode table and staging no longer needed
     float* wrec = reinterpret_cast<float*>(smem) + wave * kWaveRecFloats;
     float* wo = wrec + 2 * kRows + kRows * kGroups;
 #pragma unroll
@@ -613,18 +632,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 wrec[rb + c] = m_ref[c];
                 wrec[kRows + rb + c] = l_row[c];
             }
-            if (n < 4) wrec[2 * kRows + (rb + c) * kGroups + n] = ob;
+            if ((n & 3) == 0) wrec[2 * kRows + (rb + c) * kGroups + (n >> 2)] = ob;
         }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int t = 0; t < 16; ++t)
 #pragma unroll
-        for (int sel = 0; sel < 2; ++sel)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const float v = add_swap32(O[i][sel][c]);
-                if (j < 2) wo[(rb + c) * kHeadDim + 64 * (n >> 2) + 8 * i + 4 * sel + (n & 3)] = v;
-            }
+        for (int c = 0; c < 4; ++c) {
+            const float v = add_swap32(O[t][c]);
+            if (j < 2) wo[(rb + c) * kHeadDim + 64 * (n >> 2) + 4 * t + (n & 3)] = v;
+        }
     __syncthreads();
 
     // ---- merge the wave records: thread = (row, 8 columns) ----
