@@ -3,12 +3,15 @@
 // rotation of q on entry and the inverse rotation of the output), for up to
 // 8 query rows per kv head (GQA group x verify block).
 //
-// Decomposition: one workgroup of 4 wave64s per (b, kv head, key split);
-// each wave walks 32-key tiles of the split (the next tile's loads in flight)
+// Decomposition: one workgroup of 8 wave64s (about one per compute unit) per
+// (b, kv head, key split).  Set-up is shared: wave w rotates query row w and
+// builds one of the 8 score operand sets; all build the V decode table.  Each
+// wave walks 32-key tiles of the split (its first tile's loads are issued
+// before the set-up, the next tile's are in flight while one is computed)
 // with an online softmax (base 2, rescaled only when the running maximum
-// grows by more than 2^8); the 4 wave partials are merged in LDS, and the
+// grows by more than 2^8); the 8 wave partials are merged in LDS, and the
 // split partials are merged in-kernel by the last-arriving workgroup of each
-// group of 32 (a tree of such merges), whose last step normalises and
+// group of 16 (a tree of such merges), whose last step normalises and
 // rotates the output back.
 //
 // All products run as 16x16x32 MFMAs.  Lane l = 16 j + n: j selects a k-slot
@@ -53,13 +56,16 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;                                  // one workgroup per compute unit
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;                                  // keys per wave iteration
 constexpr int kRows = 8;                                   // query rows per kv head
-constexpr int kFanIn = 32;                                 // records per merge step
+constexpr int kFanIn = 16;                                 // records per merge step
 constexpr int kRecFloats = 2 * kRows + kRows * kHeadDim;   // (m, l)[8], o[8][256]
-constexpr int kWaveRecFloats = 2 * kRows + kRows * kGroups + kRows * kHeadDim;
+// wave records in LDS: output rows padded (4 floats after each 64 columns,
+// 4 more per row) so that the column-scattered stores are bank-conflict free
+constexpr int kORow = kHeadDim + 4 * kGroups + 4;
+constexpr int kWaveRecFloats = 2 * kRows + kRows * kGroups + kRows * kORow;
 constexpr int kLutBytes = 4096 * 8;
 constexpr int kQaBytes = 8 * 64 * 16;                      // score query operands, per lane
 // per wave: scale / scale-tail / bias tables [2 blocks][64 lanes] x 8 B and
@@ -67,12 +73,19 @@ constexpr int kQaBytes = 8 * 64 * 16;                      // score query operan
 constexpr int kStageBytes = 2 * 64 * 8;
 constexpr int kP16Bytes = 2 * 16 * 2 * 2 * 8;
 constexpr int kWaveBytes = 3 * kStageBytes + kP16Bytes;
-constexpr int kLoopSmem = kLutBytes + kQaBytes + kWaves * kWaveBytes;
+constexpr int kStageOff = kLutBytes + kQaBytes;
+constexpr int kLoopSmem = kStageOff + kWaves * kWaveBytes;
 constexpr int kRecSmem = kWaves * kWaveRecFloats * 4;
 constexpr int kSmemBytes = kLoopSmem > kRecSmem ? kLoopSmem : kRecSmem;
 constexpr int kCounterBytes = (int)kWsCounterBytes;
 constexpr int kMaxLevels = 8;
 constexpr float kLog2e = 1.44269504088896340736f;
+static_assert(kWaves == kRows && kThreads == kRows * kHeadDim / 4, "one query block per thread");
+static_assert(kWaves == 8, "one score operand set (group, half) per wave");
+static_assert((kRows * kHeadDim + kRows * 8 + kHeadDim * 4) * 4 <= kWaves * kWaveBytes,
+              "query rows, their statistics and the rotation blocks fit the staging area");
+static_assert(kThreads * 2 == kHeadDim * 4, "8 bytes of the rotation blocks per thread");
+static_assert(kHeadDim == 4 * 64, "output: 4 columns per lane of a row's wave");
 
 struct MArgs {
     const uint16_t* q;
@@ -192,21 +205,21 @@ __device__ __forceinline__ float2 ld_rec(const float* p) {
     return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
 }
 
-// Fold one record (m, l, o[8]) into a running (M, Lsum, acc[8]).
-__device__ __forceinline__ void fold(float& M, float& Ls, float acc[8], float m, float l,
-                                     const float o[8]) {
+// Fold one record (m, l, o[4]) into a running (M, Lsum, acc[4]).
+__device__ __forceinline__ void fold(float& M, float& Ls, float acc[4], float m, float l,
+                                     const float o[4]) {
     if (m == -INFINITY) return;
     if (m > M) {
         const float a = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - m);
         Ls *= a;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] *= a;
+        for (int k = 0; k < 4; ++k) acc[k] *= a;
         M = m;
     }
     const float w = __builtin_amdgcn_exp2f(m - M);
     Ls = fmaf(w, l, Ls);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = fmaf(w, o[k], acc[k]);
+    for (int k = 0; k < 4; ++k) acc[k] = fmaf(w, o[k], acc[k]);
 }
 
 // Global loads of one 32-key tile for this lane (rows at or past T read as
@@ -287,6 +300,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int t_begin = split * a.chunk;
     const int t_end = (t_begin + a.chunk < T) ? t_begin + a.chunk : T;
 
+    // ---- loads first: query row `wave`, 4-element block `lane`, and 8 bytes
+    //      of the rotation blocks (the workgroup reads them once, not once
+    //      per wave: every workgroup reads the same 4 KB); then the wave's
+    //      first tile.  Their latency overlaps the table build, and waiting
+    //      for the query does not wait for the tile. ----
+    uint2 qraw = make_uint2(0u, 0u);
+    if (wave < a.G) {
+        const int h = kvh * a.n_rep + wave / a.L;
+        const uint16_t* qrow =
+            a.q + (((int64_t)b * a.Hkv * a.n_rep + h) * a.L + wave % a.L) * kHeadDim;
+        qraw = *reinterpret_cast<const uint2*>(qrow + 4 * lane);
+    }
+    const bool rotated = a.rot != nullptr;
+    float2 rot2 = make_float2(0.f, 0.f);
+    if (rotated) rot2 = reinterpret_cast<const float2*>(a.rot)[tid];
+    const int64_t row0 = (int64_t)bh * a.capacity;
+    const __amdgpu_buffer_rsrc_t kw_r = make_rsrc(a.kw + row0 * kKWords, (uint32_t)T * 128u);
+    const __amdgpu_buffer_rsrc_t ks_r = make_rsrc(a.ks + row0 * kGroups, (uint32_t)T * 8u);
+    const __amdgpu_buffer_rsrc_t kb_r = make_rsrc(a.kb + row0 * kGroups, (uint32_t)T * 8u);
+    const __amdgpu_buffer_rsrc_t vw_r = make_rsrc(a.vw + row0 * kVWords, (uint32_t)T * 96u);
+    const __amdgpu_buffer_rsrc_t vs_r = make_rsrc(a.vs + row0 * kGroups, (uint32_t)T * 8u);
+    const __amdgpu_buffer_rsrc_t vb_r = make_rsrc(a.vb + row0 * kGroups, (uint32_t)T * 8u);
+    const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
+    // unconditional: a wave without tiles reads keys of the next split or,
+    // past T, zeros from the buffer range check, and never uses them
+    TileLoads cur;
+    load_tile(cur, t_begin + wave * kTile, n, j, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
+
     // ---- decode table: entry e = 4 fp16 codes (e >> 3k) & 7 ----
     for (int e = tid; e < 4096; e += kThreads) {
         uint32_t h[4];
@@ -295,119 +336,112 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             h[k] = __builtin_bit_cast(uint16_t, (_Float16)(float)((e >> (3 * k)) & 7));
         reinterpret_cast<uint2*>(smem)[e] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
     }
-    // ---- query row r: rotate, scale by scale*log2(e); lane holds
-    //      qv[g][e] = q'[r][64g + 16j + e] ----
-    const bool row_ok = r < a.G;
-    float qv[4][16];
+
+    // ---- query row `wave` rotated and scaled by scale*log2(e) into LDS (the
+    //      staging area of the tile loop, unused until then), with its
+    //      statistics: the 4 group sums and E, the power of two that brings
+    //      the largest |q| into [2^14, 2^15) (rows past G are zero) ----
+    float* qrot = reinterpret_cast<float*>(smem + kStageOff);
+    float* qstat = qrot + kRows * kHeadDim;  // [row][8]: group sums 0..3, E at 4
+    float* rot_lds = qstat + kRows * 8;      // the 64 rotation blocks
+    if (rotated) reinterpret_cast<float2*>(rot_lds)[tid] = rot2;
+    __syncthreads();
     {
-        const int qh = row_ok ? kvh * a.n_rep + r / a.L : kvh * a.n_rep;
-        const int qi = row_ok ? r % a.L : 0;
-        const uint16_t* qrow = a.q + (((int64_t)b * a.Hkv * a.n_rep + qh) * a.L + qi) * kHeadDim;
-        uint2 raw[16];
+        const float x[4] = {elem_to_f32<DT>(qraw.x), elem_to_f32<DT>(qraw.x >> 16),
+                            elem_to_f32<DT>(qraw.y), elem_to_f32<DT>(qraw.y >> 16)};
+        float y[4];
+        if (rotated) {
+            float Bm[16];
+            const float4* blk = reinterpret_cast<const float4*>(rot_lds + 16 * lane);
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb)
-                raw[4 * g + bb] = *reinterpret_cast<const uint2*>(qrow + 4 * (16 * g + 4 * j + bb));
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-                const uint2 x2 = row_ok ? raw[4 * g + bb] : make_uint2(0u, 0u);
-                float x[4] = {elem_to_f32<DT>(x2.x), elem_to_f32<DT>(x2.x >> 16),
-                              elem_to_f32<DT>(x2.y), elem_to_f32<DT>(x2.y >> 16)};
-                float y[4];
-                if (a.rot != nullptr) {
-                    float Bm[16];
-                    load_block(a.rot, 16 * g + 4 * j + bb, Bm);
-                    rotate4(x, Bm, y);
-                } else {
-                    y[0] = x[0]; y[1] = x[1]; y[2] = x[2]; y[3] = x[3];
-                }
-#pragma unroll
-                for (int c = 0; c < 4; ++c) qv[g][4 * bb + c] = y[c] * a.qscale;
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float4 v = blk[q4];
+                Bm[4 * q4] = v.x;
+                Bm[4 * q4 + 1] = v.y;
+                Bm[4 * q4 + 2] = v.z;
+                Bm[4 * q4 + 3] = v.w;
             }
-    }
-    float mxq = 0.f;
-    float qsum[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            mxq = fmaxf(mxq, fabsf(qv[g][e]));
-            s += qv[g][e];
+            rotate4(x, Bm, y);
+        } else {
+            y[0] = x[0]; y[1] = x[1]; y[2] = x[2]; y[3] = x[3];
         }
-        s += __shfl_xor(s, 16);
-        s += __shfl_xor(s, 32);
-        qsum[g] = s;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) y[c] *= a.qscale;
+        reinterpret_cast<float4*>(qrot)[wave * 64 + lane] = make_float4(y[0], y[1], y[2], y[3]);
+        float mx = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
+        mx = max16(mx);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float gs = sum16(((y[0] + y[1]) + y[2]) + y[3]);  // group j = lane >> 4
+        if (n == 0) qstat[wave * 8 + j] = gs;
+        if (lane == 0) {
+            int ex = 0;
+            if (mx > 0.f) (void)frexpf(mx, &ex);
+            qstat[wave * 8 + 4] = __int_as_float((mx > 0.f) ? 15 - ex : 0);
+        }
     }
-    mxq = fmaxf(mxq, __shfl_xor(mxq, 16));
-    mxq = fmaxf(mxq, __shfl_xor(mxq, 32));
-    int ex = 0;
-    if (mxq > 0.f) (void)frexpf(mxq, &ex);
-    const int E = (mxq > 0.f) ? 15 - ex : 0;
-    // query operands of the score MFMAs (g, h2): slot k holds code ci[k] of
-    // word 8g + 2j + h2, times 1/16 for the slots fed by nibbles 1 and 3
-    f16x8 qa[4][2];
+    __syncthreads();
+    // ---- score operands, one (group g, half h2) set per wave: slot k of
+    //      lane (j, n) holds element ci[k] of the 8 that word 8g + 2j + h2
+    //      covers, of row r scaled by 2^E_r, times 1/16 for the slots fed by
+    //      nibbles 1 and 3; fp16 hi part for n < 8, lo part for n >= 8 ----
+    unsigned char* qa_lds = smem + kLutBytes;
     {
         constexpr int ci[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+        const int g = wave >> 1, h2 = wave & 1;
+        const int Er = __float_as_int(qstat[r * 8 + 4]);
+        const float4* src = reinterpret_cast<const float4*>(qrot + r * kHeadDim + 64 * g + 16 * j + 8 * h2);
+        const float4 v0 = src[0], v1 = src[1];
+        const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        f16x8 qa;
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    float x = ldexpf(qv[g][8 * h2 + ci[k]], E);
-                    if (k & 2) x *= 0.0625f;
-                    const _Float16 hi = (_Float16)x;
-                    const _Float16 lo = (_Float16)(x - (float)hi);
-                    qa[g][h2][k] = lo_part ? lo : hi;
-                }
-    }
-    // identical in the 4 waves: wave 0 keeps the copy the tile loop reads
-    unsigned char* qa_lds = smem + kLutBytes;
-    if (wave == 0) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
-                *reinterpret_cast<f16x8*>(qa_lds + ((2 * g + h2) * 64 + lane) * 16) = qa[g][h2];
-    }
-    // query operand of the bias MFMA: slots of lane group 0 = the 4 group sums
-    // (hi, then middle limb), lane group 1 = low limb, other groups zero
-    u32x4 qb_op;
-    float gb = 1.0f;  // scale of the bias MFMA result (fp16 caches)
-    if constexpr (DT == RBQ_BF16) {
-        uint32_t hb[4], mb[4], lb[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const uint32_t u = __float_as_uint(qsum[g]);
-            const float hi = __uint_as_float(u & 0xFFFF0000u);
-            const uint32_t u2 = __float_as_uint(qsum[g] - hi);
-            const float mid = __uint_as_float(u2 & 0xFFFF0000u);
-            hb[g] = u >> 16;
-            mb[g] = u2 >> 16;
-            lb[g] = f32_to_bf16_bits(qsum[g] - hi - mid);
-        }
-        if (j == 0) qb_op = (u32x4){hb[0] | hb[1] << 16, hb[2] | hb[3] << 16, mb[0] | mb[1] << 16,
-                                    mb[2] | mb[3] << 16};
-        else if (j == 1) qb_op = (u32x4){lb[0] | lb[1] << 16, lb[2] | lb[3] << 16, 0u, 0u};
-        else qb_op = (u32x4){0u, 0u, 0u, 0u};
-    } else {
-        // fp16: sums scaled by 2^(E-6) (below 2^15 in magnitude), hi + lo
-        uint32_t hb[4], lb[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const float x = ldexpf(qsum[g], E - 6);
+        for (int k = 0; k < 8; ++k) {
+            float x = ldexpf(v[ci[k]], Er);
+            if (k & 2) x *= 0.0625f;
             const _Float16 hi = (_Float16)x;
-            hb[g] = __builtin_bit_cast(uint16_t, hi);
-            lb[g] = __builtin_bit_cast(uint16_t, (_Float16)(x - (float)hi));
+            const _Float16 lo = (_Float16)(x - (float)hi);
+            qa[k] = lo_part ? lo : hi;
         }
-        if (j == 0) qb_op = (u32x4){hb[0] | hb[1] << 16, hb[2] | hb[3] << 16, lb[0] | lb[1] << 16,
-                                    lb[2] | lb[3] << 16};
-        else qb_op = (u32x4){0u, 0u, 0u, 0u};
-        gb = 0.f;  // set per accumulator row below
+        *reinterpret_cast<f16x8*>(qa_lds + ((2 * g + h2) * 64 + lane) * 16) = qa;
+    }
+    // query operand of the bias MFMA for row r: slots of lane group 0 = the 4
+    // group sums (hi, then middle limb), lane group 1 = low limb, others zero
+    u32x4 qb_op;
+    {
+        float qsum[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) qsum[g] = qstat[r * 8 + g];
+        const int E = __float_as_int(qstat[r * 8 + 4]);
+        if constexpr (DT == RBQ_BF16) {
+            uint32_t hb[4], mb[4], lb[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const uint32_t u = __float_as_uint(qsum[g]);
+                const float hi = __uint_as_float(u & 0xFFFF0000u);
+                const uint32_t u2 = __float_as_uint(qsum[g] - hi);
+                const float mid = __uint_as_float(u2 & 0xFFFF0000u);
+                hb[g] = u >> 16;
+                mb[g] = u2 >> 16;
+                lb[g] = f32_to_bf16_bits(qsum[g] - hi - mid);
+            }
+            if (j == 0) qb_op = (u32x4){hb[0] | hb[1] << 16, hb[2] | hb[3] << 16, mb[0] | mb[1] << 16,
+                                        mb[2] | mb[3] << 16};
+            else if (j == 1) qb_op = (u32x4){lb[0] | lb[1] << 16, lb[2] | lb[3] << 16, 0u, 0u};
+            else qb_op = (u32x4){0u, 0u, 0u, 0u};
+        } else {
+            // fp16: sums scaled by 2^(E-6) (below 2^15 in magnitude), hi + lo
+            uint32_t hb[4], lb[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float x = ldexpf(qsum[g], E - 6);
+                const _Float16 hi = (_Float16)x;
+                hb[g] = __builtin_bit_cast(uint16_t, hi);
+                lb[g] = __builtin_bit_cast(uint16_t, (_Float16)(x - (float)hi));
+            }
+            if (j == 0) qb_op = (u32x4){hb[0] | hb[1] << 16, hb[2] | hb[3] << 16, lb[0] | lb[1] << 16,
+                                        lb[2] | lb[3] << 16};
+            else qb_op = (u32x4){0u, 0u, 0u, 0u};
+        }
     }
     // per accumulator row: power-of-two factors and causal visibility
     float frow[4], grow[4];
@@ -415,26 +449,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int row = rb + c;
-        const int Er = __shfl(E, row);
+        const int Er = __float_as_int(qstat[row * 8 + 4]);
         frow[c] = ldexpf(1.0f, 24 - Er);
         grow[c] = (DT == RBQ_BF16) ? 1.0f : ldexpf(1.0f, 6 - Er);
         const bool ok = row < a.G;
         vis[c] = (ok && a.causal) ? T - a.L + (row % a.L) + 1 : T;
     }
-    (void)gb;
     const int vis_min = min(min(vis[0], vis[1]), min(vis[2], vis[3]));
-    __syncthreads();  // decode table and query operands complete
-
-    const int64_t row0 = (int64_t)bh * a.capacity;
-    const __amdgpu_buffer_rsrc_t kw_r = make_rsrc(a.kw + row0 * kKWords, (uint32_t)T * 128u);
-    const __amdgpu_buffer_rsrc_t ks_r = make_rsrc(a.ks + row0 * kGroups, (uint32_t)T * 8u);
-    const __amdgpu_buffer_rsrc_t kb_r = make_rsrc(a.kb + row0 * kGroups, (uint32_t)T * 8u);
-    const __amdgpu_buffer_rsrc_t vw_r = make_rsrc(a.vw + row0 * kVWords, (uint32_t)T * 96u);
-    const __amdgpu_buffer_rsrc_t vs_r = make_rsrc(a.vs + row0 * kGroups, (uint32_t)T * 8u);
-    const __amdgpu_buffer_rsrc_t vb_r = make_rsrc(a.vb + row0 * kGroups, (uint32_t)T * 8u);
+    __syncthreads();  // query operands complete; query rows no longer read
 
     // per-wave staging for the transposing reads (byte offsets in smem)
-    const uint32_t wbase = kLutBytes + kQaBytes + wave * kWaveBytes;
+    const uint32_t wbase = kStageOff + wave * kWaveBytes;
     const uint32_t s_off = wbase;                      // scales (or scale heads)
     const uint32_t t_off = wbase + kStageBytes;        // scale tails (fp16 caches)
     const uint32_t b_off = wbase + 2 * kStageBytes;    // biases
@@ -451,12 +476,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     float m_ref[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     float l_part[4] = {0.f, 0.f, 0.f, 0.f};
 
-    const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
-    TileLoads cur;
-    if (wave < n_tiles) load_tile(cur, t_begin + wave * kTile, n, j, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
     for (int it = wave; it < n_tiles; it += kWaves) {
         const int t0 = t_begin + it * kTile;
-        // next tile of this wave in flight while this one is computed
+        // the wave's next tile is in flight while this one is computed
         TileLoads nxt;
         if (it + kWaves < n_tiles)
             load_tile(nxt, t0 + kWaves * kTile, n, j, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
@@ -640,25 +662,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const float v = add_swap32(O[t][c]);
-            if (j < 2) wo[(rb + c) * kHeadDim + 64 * (n >> 2) + 4 * t + (n & 3)] = v;
+            if (j < 2) wo[(rb + c) * kORow + 68 * (n >> 2) + 4 * t + (n & 3)] = v;
         }
     __syncthreads();
 
-    // ---- merge the wave records: thread = (row, 8 columns) ----
-    const int row = tid >> 5;
-    const int d8 = (tid & 31) * 8;
-    const int grp = d8 >> 6;
-    float M = -INFINITY, Ls = 0.f, acc[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+    // ---- merge the wave records: thread = (row, 4 columns) ----
+    const int row = wave;
+    const int c4 = 4 * lane;
+    const int grp = c4 >> 6;
+    float M = -INFINITY, Ls = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
         const float* rw = reinterpret_cast<const float*>(smem) + w * kWaveRecFloats;
         const float bias = rw[2 * kRows + row * kGroups + grp];
-        const float* o = rw + 2 * kRows + kRows * kGroups + row * kHeadDim + d8;
-        float ov[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) ov[k] = o[k] + bias;
+        const float4 o = *reinterpret_cast<const float4*>(rw + 2 * kRows + kRows * kGroups +
+                                                          row * kORow + c4 + 4 * grp);
+        const float ov[4] = {o.x + bias, o.y + bias, o.z + bias, o.w + bias};
         fold(M, Ls, acc, rw[row], rw[kRows + row], ov);
     }
 
@@ -667,10 +686,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     while (a.n_lvl[lvl] > 1) {
         const int n_k = a.n_lvl[lvl];
         float* rp = a.rec + (a.rec_base[lvl] + (int64_t)bh * n_k + idx) * kRecFloats;
-        if ((tid & 31) == 0) st_rec(rp + 2 * row, M, Ls);
-        float* ro = rp + 2 * kRows + row * kHeadDim + d8;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) st_rec(ro + 2 * k, acc[2 * k], acc[2 * k + 1]);
+        if (lane == 0) st_rec(rp + 2 * row, M, Ls);
+        float* ro = rp + 2 * kRows + row * kHeadDim + c4;
+        st_rec(ro, acc[0], acc[1]);
+        st_rec(ro + 2, acc[2], acc[3]);
         __builtin_amdgcn_s_waitcnt(0);  // this thread's record stores are complete
         __syncthreads();
         const int g = idx / kFanIn;
@@ -688,28 +707,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         M = -INFINITY;
         Ls = 0.f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+        for (int k = 0; k < 4; ++k) acc[k] = 0.f;
         const float* base = a.rec + (a.rec_base[lvl] + (int64_t)bh * n_k + g * kFanIn) * kRecFloats;
-        // members are read 8 at a time with all their loads in flight
-        for (int m0 = 0; m0 < members; m0 += 8) {
-            float2 ml[8], o01[8], o23[8], o45[8], o67[8];
+        // all members' loads in flight at once
+        float2 ml[kFanIn], o01[kFanIn], o23[kFanIn];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int mbr = (m0 + k < members) ? m0 + k : m0;
-                const float* rm = base + (int64_t)mbr * kRecFloats;
-                const float* o = rm + 2 * kRows + row * kHeadDim + d8;
-                ml[k] = ld_rec(rm + 2 * row);
-                o01[k] = ld_rec(o);
-                o23[k] = ld_rec(o + 2);
-                o45[k] = ld_rec(o + 4);
-                o67[k] = ld_rec(o + 6);
-            }
+        for (int k = 0; k < kFanIn; ++k) {
+            const int mbr = (k < members) ? k : 0;
+            const float* rm = base + (int64_t)mbr * kRecFloats;
+            const float* o = rm + 2 * kRows + row * kHeadDim + c4;
+            ml[k] = ld_rec(rm + 2 * row);
+            o01[k] = ld_rec(o);
+            o23[k] = ld_rec(o + 2);
+        }
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float ov[8] = {o01[k].x, o01[k].y, o23[k].x, o23[k].y,
-                                     o45[k].x, o45[k].y, o67[k].x, o67[k].y};
-                if (m0 + k < members) fold(M, Ls, acc, ml[k].x, ml[k].y, ov);
-            }
+        for (int k = 0; k < kFanIn; ++k) {
+            const float ov[4] = {o01[k].x, o01[k].y, o23[k].x, o23[k].y};
+            if (k < members) fold(M, Ls, acc, ml[k].x, ml[k].y, ov);
         }
         idx = g;
         ++lvl;
@@ -719,21 +733,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const float inv = 1.0f / Ls;
         const int h = kvh * a.n_rep + row / a.L;
         const int i = row % a.L;
-        float* dst = a.out + (((int64_t)b * a.Hkv * a.n_rep + h) * a.L + i) * kHeadDim + d8;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            float y[4] = {acc[4 * half] * inv, acc[4 * half + 1] * inv, acc[4 * half + 2] * inv,
-                          acc[4 * half + 3] * inv};
-            float z[4];
-            if (a.rot != nullptr) {
-                float Bm[16];
-                load_block(a.rot, d8 / 4 + half, Bm);
-                unrotate4(y, Bm, z);
-            } else {
-                z[0] = y[0]; z[1] = y[1]; z[2] = y[2]; z[3] = y[3];
-            }
-            reinterpret_cast<float4*>(dst)[half] = make_float4(z[0], z[1], z[2], z[3]);
-        }
+        float* dst = a.out + (((int64_t)b * a.Hkv * a.n_rep + h) * a.L + i) * kHeadDim + c4;
+        const float y[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+        float z[4];
+        float Bm[16];
+        load_block(a.rot, lane, Bm);
+        unrotate4(y, Bm, z);
+        *reinterpret_cast<float4*>(dst) = make_float4(z[0], z[1], z[2], z[3]);
     }
 }
 
@@ -747,16 +753,17 @@ int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Mfm
     const int64_t BH = (int64_t)c->B * c->H_kv;
     int64_t S = splits;
     if (S == 0) {
-        S = (2 * 256 + BH - 1) / BH;  // about two workgroups per compute unit
-        const int64_t max_s = (T + 127) / 128;
+        S = (256 + BH - 1) / BH;  // about one workgroup per compute unit
+        const int64_t max_s = (T + kWaves * kTile - 1) / (kWaves * kTile);
         if (S > max_s) S = max_s;
     }
     if (S < 1) S = 1;
     int64_t chunk = (T + S - 1) / S;
-    chunk = (chunk + kTile - 1) / kTile * kTile;
+    chunk = (chunk + kWaves * kTile - 1) / (kWaves * kTile) * (kWaves * kTile);  // whole rounds
     S = (T + chunk - 1) / chunk;
     if (BH * S > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
-    if (T * (int64_t)(kKWords * 4) > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;  // 32-bit buffer offsets
+    // 32-bit buffer offsets, also for the tile reads past T (at most 4 tiles)
+    if ((T + kWaves * kTile) * (int64_t)(kKWords * 4) > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
     p->S = (int)S;
     p->chunk = chunk;
     p->levels = 0;
