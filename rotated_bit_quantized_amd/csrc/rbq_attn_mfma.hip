@@ -61,11 +61,16 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;                                  // keys per wave iteration
 constexpr int kRows = 8;                                   // query rows per kv head
 constexpr int kFanIn = 16;                                 // records per merge step
-constexpr int kRecFloats = 2 * kRows + kRows * kHeadDim;   // (m, l)[8], o[8][256]
-// wave records in LDS: output rows padded (4 floats after each 64 columns,
-// 4 more per row) so that the column-scattered stores are bank-conflict free
-constexpr int kORow = kHeadDim + 4 * kGroups + 4;
-constexpr int kWaveRecFloats = 2 * kRows + kRows * kGroups + kRows * kORow;
+// split record in the workspace: (m, l) per row, then o column-major
+// [256 columns][8 rows]
+constexpr int kRecFloats = 2 * kRows + kRows * kHeadDim;
+// wave record in LDS, in its own region so that a wave stores it as soon as
+// its tiles are done: o column-major [256 columns][2 row quads][4 rows], the
+// row quad of column c stored at slot quad ^ ((c >> 3) & 1) (conflict-free
+// 16-byte reads of 64 consecutive columns), ob [4 groups][8 rows], m[8], l[8];
+// then per wave the merge weights [8 waves][8 rows], M[8], L[8]
+constexpr int kWaveRecFloats = kHeadDim * kRows + kGroups * kRows + 2 * kRows;
+constexpr int kWeightFloats = kWaves * kRows + 2 * kRows;
 constexpr int kLutBytes = 4096 * 8;
 constexpr int kQaBytes = 8 * 64 * 16;                      // score query operands, per lane
 // per wave: scale / scale-tail / bias tables [2 blocks][64 lanes] x 8 B and
@@ -75,8 +80,10 @@ constexpr int kP16Bytes = 2 * 16 * 2 * 2 * 8;
 constexpr int kWaveBytes = 3 * kStageBytes + kP16Bytes;
 constexpr int kStageOff = kLutBytes + kQaBytes;
 constexpr int kLoopSmem = kStageOff + kWaves * kWaveBytes;
-constexpr int kRecSmem = kWaves * kWaveRecFloats * 4;
-constexpr int kSmemBytes = kLoopSmem > kRecSmem ? kLoopSmem : kRecSmem;
+constexpr int kRecOff = kLoopSmem;
+constexpr int kWeightOff = kRecOff + kWaves * kWaveRecFloats * 4;
+constexpr int kSmemBytes = kWeightOff + kWaves * kWeightFloats * 4;
+static_assert(kSmemBytes <= 160 * 1024, "LDS of one compute unit");
 constexpr int kCounterBytes = (int)kWsCounterBytes;
 constexpr int kMaxLevels = 8;
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -85,7 +92,8 @@ static_assert(kWaves == 8, "one score operand set (group, half) per wave");
 static_assert((kRows * kHeadDim + kRows * 8 + kHeadDim * 4) * 4 <= kWaves * kWaveBytes,
               "query rows, their statistics and the rotation blocks fit the staging area");
 static_assert(kThreads * 2 == kHeadDim * 4, "8 bytes of the rotation blocks per thread");
-static_assert(kHeadDim == 4 * 64, "output: 4 columns per lane of a row's wave");
+static_assert(kThreads == 2 * kHeadDim && kRows == 8, "merge: one column and 4 rows per thread");
+static_assert(kRows * kFanIn <= 2 * 64 && kFanIn == 16, "merge weights: 16-lane rows of waves 0 and 1");
 
 struct MArgs {
     const uint16_t* q;
@@ -203,23 +211,6 @@ __device__ __forceinline__ float2 ld_rec(const float* p) {
     const unsigned long long v = __hip_atomic_load(
         reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
-}
-
-// Fold one record (m, l, o[4]) into a running (M, Lsum, acc[4]).
-__device__ __forceinline__ void fold(float& M, float& Ls, float acc[4], float m, float l,
-                                     const float o[4]) {
-    if (m == -INFINITY) return;
-    if (m > M) {
-        const float a = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - m);
-        Ls *= a;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) acc[k] *= a;
-        M = m;
-    }
-    const float w = __builtin_amdgcn_exp2f(m - M);
-    Ls = fmaf(w, l, Ls);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) acc[k] = fmaf(w, o[k], acc[k]);
 }
 
 // Global loads of one 32-key tile for this lane (rows at or past T read as
@@ -591,10 +582,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 hi2[c2] = __builtin_bit_cast(uint32_t, (f16x2){h0, h1});
                 lo2[c2] = __builtin_bit_cast(uint32_t, (f16x2){e0, e1});
             }
-            if (j < 2) {
-                *reinterpret_cast<uint2*>(smem + p_slot(blk, n, 0, j)) = make_uint2(hi2[0], hi2[1]);
-                *reinterpret_cast<uint2*>(smem + p_slot(blk, n, 1, j)) = make_uint2(lo2[0], lo2[1]);
-            }
+            // lanes l and l ^ 32 hold the same values and store them to the
+            // same slots (no divergent branch)
+            *reinterpret_cast<uint2*>(smem + p_slot(blk, n, 0, j & 1)) = make_uint2(hi2[0], hi2[1]);
+            *reinterpret_cast<uint2*>(smem + p_slot(blk, n, 1, j & 1)) = make_uint2(lo2[0], lo2[1]);
         }
         // A operand of P.V: row n (hi rows 0-7, lo rows 8-15) x keys 4j + e of
         // both blocks; lane 4e + q addresses (key 4j + e, part q >> 1, quad q & 1)
@@ -639,46 +630,89 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         cur = nxt;
     }
 
-    // ---- wave record: hi + lo rows combined, row sums over the 16 key lanes ----
-    float l_row[4];
+    // ---- wave record, stored as soon as this wave's tiles are done: hi + lo
+    //      rows combined two registers at a time (after the lane-half swap,
+    //      lanes 0-31 hold the sums of the first register and lanes 32-63 those
+    //      of the second), row sums over the 16 key lanes ----
+    float* wrec = reinterpret_cast<float*>(smem + kRecOff) + wave * kWaveRecFloats;
+    float* wob = wrec + kHeadDim * kRows;
+    float* wml = wob + kGroups * kRows;
+    const int hl = j >> 1;  // 0: lanes 0-31, 1: lanes 32-63
+    auto comb = [](float x, float y) -> float {
+        const auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false,
+                                                         false);
+        return __uint_as_float(s2[0]) + __uint_as_float(s2[1]);
+    };
 #pragma unroll
-    for (int c = 0; c < 4; ++c) l_row[c] = sum16(l_part[c]);
-    __syncthreads();  // decode table and staging no longer needed
-    float* wrec = reinterpret_cast<float*>(smem) + wave * kWaveRecFloats;
-    float* wo = wrec + 2 * kRows + kRows * kGroups;
+    for (int t = 0; t < 16; ++t) {
+        const int col = 64 * (n >> 2) + 4 * t + (n & 3);
+        const float ra = comb(O[t][0], O[t][1]);  // row rb + hl
+        const float rc = comb(O[t][2], O[t][3]);  // row rb + 2 + hl
+        float* dst = wrec + col * kRows + 4 * ((j & 1) ^ ((col >> 3) & 1)) + hl;
+        dst[0] = ra;
+        dst[2] = rc;
+    }
+    {
+        const float ra = comb(Ob[0], Ob[1]);
+        const float rc = comb(Ob[2], Ob[3]);
+        float* dst = wob + (n >> 2) * kRows + rb + hl;
+        dst[0] = ra;
+        dst[2] = rc;
+    }
+    {
+        float l_row[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const float ob = add_swap32(Ob[c]);
-        if (j < 2) {
-            if (n == 0) {
-                wrec[rb + c] = m_ref[c];
-                wrec[kRows + rb + c] = l_row[c];
-            }
-            if ((n & 3) == 0) wrec[2 * kRows + (rb + c) * kGroups + (n >> 2)] = ob;
+        for (int c = 0; c < 4; ++c) l_row[c] = sum16(l_part[c]);
+        if (n == 0 && j < 2) {
+            *reinterpret_cast<float4*>(wml + rb) = make_float4(m_ref[0], m_ref[1], m_ref[2], m_ref[3]);
+            *reinterpret_cast<float4*>(wml + kRows + rb) =
+                make_float4(l_row[0], l_row[1], l_row[2], l_row[3]);
         }
     }
-#pragma unroll
-    for (int t = 0; t < 16; ++t)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const float v = add_swap32(O[t][c]);
-            if (j < 2) wo[(rb + c) * kORow + 68 * (n >> 2) + 4 * t + (n & 3)] = v;
-        }
     __syncthreads();
 
-    // ---- merge the wave records: thread = (row, 4 columns) ----
-    const int row = wave;
-    const int c4 = 4 * lane;
-    const int grp = c4 >> 6;
-    float M = -INFINITY, Ls = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+    // ---- merge the wave records.  Each wave first derives the weights
+    //      2^(m_w - M) of all (wave w, row) pairs (lane = 8 w + row) into its
+    //      own LDS area; then thread = (column col, rows 4h .. 4h+3) ----
+    const int col = tid & (kHeadDim - 1);
+    const int h = tid >> 8;
+    const int grp = col >> 6;
+    float M[4], Ls[4], acc[4];
+    {
+        const float* rml = reinterpret_cast<const float*>(smem + kRecOff) + (lane >> 3) * kWaveRecFloats +
+                           kHeadDim * kRows + kGroups * kRows;
+        const float mw = rml[lane & 7];
+        const float lw = rml[kRows + (lane & 7)];
+        float Mx = fmaxf(mw, __shfl_xor(mw, 8));
+        Mx = fmaxf(Mx, __shfl_xor(Mx, 16));
+        Mx = fmaxf(Mx, __shfl_xor(Mx, 32));
+        const float wv = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - Mx);
+        float Lw = wv * lw;
+        Lw += __shfl_xor(Lw, 8);
+        Lw += __shfl_xor(Lw, 16);
+        Lw += __shfl_xor(Lw, 32);
+        float* wts = reinterpret_cast<float*>(smem + kWeightOff) + wave * kWeightFloats;
+        wts[lane] = wv;
+        if (lane < kRows) {
+            wts[kWaves * kRows + lane] = Mx;
+            wts[kWaves * kRows + kRows + lane] = Lw;
+        }
+        const float4 Mv = *reinterpret_cast<const float4*>(wts + kWaves * kRows + 4 * h);
+        const float4 Lv = *reinterpret_cast<const float4*>(wts + kWaves * kRows + kRows + 4 * h);
+        M[0] = Mv.x; M[1] = Mv.y; M[2] = Mv.z; M[3] = Mv.w;
+        Ls[0] = Lv.x; Ls[1] = Lv.y; Ls[2] = Lv.z; Ls[3] = Lv.w;
+        acc[0] = acc[1] = acc[2] = acc[3] = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        const float* rw = reinterpret_cast<const float*>(smem) + w * kWaveRecFloats;
-        const float bias = rw[2 * kRows + row * kGroups + grp];
-        const float4 o = *reinterpret_cast<const float4*>(rw + 2 * kRows + kRows * kGroups +
-                                                          row * kORow + c4 + 4 * grp);
-        const float ov[4] = {o.x + bias, o.y + bias, o.z + bias, o.w + bias};
-        fold(M, Ls, acc, rw[row], rw[kRows + row], ov);
+        for (int w = 0; w < kWaves; ++w) {
+            const float* rw = reinterpret_cast<const float*>(smem + kRecOff) + w * kWaveRecFloats;
+            const float4 o = *reinterpret_cast<const float4*>(rw + col * kRows + 4 * (h ^ ((col >> 3) & 1)));
+            const float4 ob = *reinterpret_cast<const float4*>(rw + kHeadDim * kRows + grp * kRows + 4 * h);
+            const float4 wt = *reinterpret_cast<const float4*>(wts + w * kRows + 4 * h);
+            acc[0] = fmaf(wt.x, o.x + ob.x, acc[0]);
+            acc[1] = fmaf(wt.y, o.y + ob.y, acc[1]);
+            acc[2] = fmaf(wt.z, o.z + ob.z, acc[2]);
+            acc[3] = fmaf(wt.w, o.w + ob.w, acc[3]);
+        }
     }
 
     // ---- split merge tree; the last step writes the output ----
@@ -686,8 +720,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     while (a.n_lvl[lvl] > 1) {
         const int n_k = a.n_lvl[lvl];
         float* rp = a.rec + (a.rec_base[lvl] + (int64_t)bh * n_k + idx) * kRecFloats;
-        if (lane == 0) st_rec(rp + 2 * row, M, Ls);
-        float* ro = rp + 2 * kRows + row * kHeadDim + c4;
+        if (col == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st_rec(rp + 2 * (4 * h + i), M[i], Ls[i]);
+        }
+        float* ro = rp + 2 * kRows + col * kRows + 4 * h;
         st_rec(ro, acc[0], acc[1]);
         st_rec(ro + 2, acc[2], acc[3]);
         __builtin_amdgcn_s_waitcnt(0);  // this thread's record stores are complete
@@ -704,42 +741,79 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
         __syncthreads();
         if (!s_last) return;
-        M = -INFINITY;
-        Ls = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) acc[k] = 0.f;
+        // The group's records, all loads in flight at once: thread t < 128
+        // reads (m, l) of row t >> 4 of member t & 15; every thread reads its
+        // 4 rows of column col of every member.
         const float* base = a.rec + (a.rec_base[lvl] + (int64_t)bh * n_k + g * kFanIn) * kRecFloats;
-        // all members' loads in flight at once
-        float2 ml[kFanIn], o01[kFanIn], o23[kFanIn];
+        const int wrow = tid >> 4, wmbr = tid & 15;
+        float2 ml = make_float2(-INFINITY, 0.f);
+        if (tid < kRows * kFanIn && wmbr < members) ml = ld_rec(base + (int64_t)wmbr * kRecFloats + 2 * wrow);
+        float2 o01[kFanIn], o23[kFanIn];
 #pragma unroll
         for (int k = 0; k < kFanIn; ++k) {
             const int mbr = (k < members) ? k : 0;
-            const float* rm = base + (int64_t)mbr * kRecFloats;
-            const float* o = rm + 2 * kRows + row * kHeadDim + c4;
-            ml[k] = ld_rec(rm + 2 * row);
+            const float* o = base + (int64_t)mbr * kRecFloats + 2 * kRows + col * kRows + 4 * h;
             o01[k] = ld_rec(o);
             o23[k] = ld_rec(o + 2);
         }
+        // merge weights per (row, member): 2^(m - max over members), and the
+        // merged row sums (16-lane reductions over the members)
+        float* wts = reinterpret_cast<float*>(smem);  // [row][member], then L[row], M[row]
+        if (tid < kRows * kFanIn) {
+            const float Mx = max16(ml.x);
+            const float wv = (ml.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml.x - Mx);
+            const float Lsum = sum16(wv * ml.y);
+            wts[wrow * kFanIn + wmbr] = wv;
+            if (wmbr == 0) {
+                wts[kRows * kFanIn + wrow] = Lsum;
+                wts[kRows * kFanIn + kRows + wrow] = Mx;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[i] = 0.f;
+            Ls[i] = wts[kRows * kFanIn + 4 * h + i];
+            M[i] = wts[kRows * kFanIn + kRows + 4 * h + i];
+        }
 #pragma unroll
         for (int k = 0; k < kFanIn; ++k) {
-            const float ov[4] = {o01[k].x, o01[k].y, o23[k].x, o23[k].y};
-            if (k < members) fold(M, Ls, acc, ml[k].x, ml[k].y, ov);
+            const float o[4] = {o01[k].x, o01[k].y, o23[k].x, o23[k].y};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = fmaf(wts[(4 * h + i) * kFanIn + k], o[i], acc[i]);
         }
+        __syncthreads();  // weights read before the next level reuses the space
         idx = g;
         ++lvl;
     }
 
-    if (row < a.G) {
-        const float inv = 1.0f / Ls;
-        const int h = kvh * a.n_rep + row / a.L;
-        const int i = row % a.L;
-        float* dst = a.out + (((int64_t)b * a.Hkv * a.n_rep + h) * a.L + i) * kHeadDim + c4;
-        const float y[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-        float z[4];
-        float Bm[16];
-        load_block(a.rot, lane, Bm);
-        unrotate4(y, Bm, z);
-        *reinterpret_cast<float4*>(dst) = make_float4(z[0], z[1], z[2], z[3]);
+    // ---- normalise, rotate back (a 4-column block lies in one lane quad),
+    //      store rows below G ----
+    float Bm[4] = {0.f, 0.f, 0.f, 0.f};
+    const bool rot_out = a.rot != nullptr;
+    if (rot_out) {
+        const float4 v = *reinterpret_cast<const float4*>(a.rot + 16 * (col >> 2) + 4 * (col & 3));
+        Bm[0] = v.x; Bm[1] = v.y; Bm[2] = v.z; Bm[3] = v.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * h + i;
+        const float y = acc[i] * (1.0f / Ls[i]);
+        float z = y;
+        if (rot_out) {
+            // z = sum_k y[block column k] * B[col & 3][k], in fp64
+            const float y0 = dpp<0x00>(y), y1 = dpp<0x55>(y), y2 = dpp<0xAA>(y), y3 = dpp<0xFF>(y);
+            double s2 = (double)y0 * (double)Bm[0];
+            s2 = s2 + (double)y1 * (double)Bm[1];
+            s2 = s2 + (double)y2 * (double)Bm[2];
+            s2 = s2 + (double)y3 * (double)Bm[3];
+            z = (float)s2;
+        }
+        if (row < a.G) {
+            const int hq = kvh * a.n_rep + row / a.L;
+            const int qi = row % a.L;
+            a.out[(((int64_t)b * a.Hkv * a.n_rep + hq) * a.L + qi) * kHeadDim + col] = z;
+        }
     }
 }
 
