@@ -35,7 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-ATTN_SRC = os.path.join(ROOT, "rotated_bit_quantized_amd", "csrc", "rbq_attn.hip")
+ATTN_SRC = os.path.join(ROOT, "rotated_bit_quantized_amd", "csrc", "rbq_attn_mfma.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_batched_decode.json")
 
 
@@ -115,8 +115,9 @@ def cpu_baseline(w, seconds: float = 12.0) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=2000,
+                    help="untimed steps first: the GPU clock takes about 100 ms of work to settle")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--splits", type=int, default=0, help="key splits (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
