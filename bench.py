@@ -7,7 +7,8 @@ quantized, packed and appended at row T-1 (so attention sees T tokens), the
 fused attention of the rotated query over the packed cache runs with the
 causal mask at the offset and the inverse rotation of its output, and the
 token is trimmed again so every step sees the same T.  The rotation blocks
-are built once before timing.
+are built once before timing.  The step's launches are issued from Python
+(``--graph`` replays them from a captured HIP graph instead).
 
 Inputs are synthetic (``workloads``), resident in HBM before timing.  The
 cache is replicated (default 4 copies, 512 MiB) and the steps cycle through
@@ -16,8 +17,8 @@ reads.
 
 Prints ONE JSON line: ``value`` = effective HBM GB/s of the step (algorithmic
 bytes / step time), plus tokens/s, the roofline of the attention kernel
-(HIP events around its launches on the stream it runs on) and the CPU oracle
-timed on a bounded sample of the same work.
+(HIP events around back-to-back launches of it on the stream it runs on) and
+the CPU oracle timed on a bounded sample of the same work.
 """
 from __future__ import annotations
 
@@ -121,6 +122,9 @@ def main() -> int:
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--splits", type=int, default=0, help="key splits (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step from a captured HIP graph (on this stack a replay "
+                         "costs more than the two launches it holds)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -160,34 +164,63 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
-    def step(i, ev=None):
+    def step(i):
         c = caches[i % len(caches)]
         capi.rbq_kv_quant_append(c.desc, k_new, v_new, rot)
-        if ev is not None:
-            ev[0].record(stream)
         capi.rbq_quant_attn_decode(c.desc, q, 1 / 16, True, rot, out, args.splits, ws)
-        if ev is not None:
-            ev[1].record(stream)
         capi.rbq_kv_trim(c.desc, 1)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    # --graph: one HIP graph per cache replica holds the step's two launches
+    # (append at row T-1, attention over T rows) with their arguments as
+    # captured; the trim back to T-1 is host-side bookkeeping only.
+    graphs = []
+    if args.graph:
+        cap = torch.cuda.Stream()
+        for c in caches:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                capi.rbq_kv_quant_append(c.desc, k_new, v_new, rot)
+                capi.rbq_quant_attn_decode(c.desc, q, 1 / 16, True, rot, out, args.splits, ws)
+            capi.rbq_kv_trim(c.desc, 1)
+            graphs.append(g)
+        torch.cuda.synchronize()
 
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    def run(i):
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            step(i)
+
+    for i in range(args.warmup):
+        run(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, events[i])
+        run(i)
     torch.cuda.synchronize()
     total = time.perf_counter() - t0
 
-    attn_ms = np.array([a.elapsed_time(b) for a, b in events])
+    # The attention kernel alone: back-to-back launches on the stream it runs
+    # on, HIP events at both ends (an event pair around every launch would add
+    # the dispatch gap it forces to each measurement).
+    n_attn = max(100, args.steps // 2)
+    for c in caches:  # T rows, as in the step
+        capi.rbq_kv_quant_append(c.desc, k_new, v_new, rot)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(n_attn):
+        c = caches[i % len(caches)]
+        capi.rbq_quant_attn_decode(c.desc, q, 1 / 16, True, rot, out, args.splits, ws)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    attn_us = ev0.elapsed_time(ev1) * 1e3 / n_attn
+    for c in caches:
+        capi.rbq_kv_trim(c.desc, 1)
+
     nbytes = algorithmic_bytes(w, w.T)
     ms_per_step = total * 1e3 / args.steps
     value = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
-    attn_avg_s = float(attn_ms.mean()) * 1e-3
+    attn_avg_s = attn_us * 1e-6
     achieved = nbytes["attn"] / attn_avg_s / 1e9
     traffic = measured_traffic(nbytes["attn"])
 
@@ -221,12 +254,12 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "rbq_quant_attn_decode launch (HIP events on its stream)",
+            "kernel": "attn_mfma_kernel (rbq_quant_attn_decode): HIP events around "
+                      f"{n_attn} back-to-back launches on its stream",
             "alg_bytes_per_launch": nbytes["attn"],
             "avg_launch_us": round(attn_avg_s * 1e6, 3),
-            "p10_us": round(float(np.percentile(attn_ms, 10)) * 1e3, 3),
-            "p90_us": round(float(np.percentile(attn_ms, 90)) * 1e3, 3),
         },
+        "step": "HIP graph replay (append + attention)" if graphs else "eager launches",
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)

@@ -833,7 +833,10 @@ int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Mfm
     }
     if (S < 1) S = 1;
     int64_t chunk = (T + S - 1) / S;
-    chunk = (chunk + kWaves * kTile - 1) / (kWaves * kTile) * (kWaves * kTile);  // whole rounds
+    // automatic plans give every split whole rounds of the 8 waves; an explicit
+    // split count is kept as closely as whole tiles allow
+    const int64_t unit = (splits == 0) ? (int64_t)kWaves * kTile : (int64_t)kTile;
+    chunk = (chunk + unit - 1) / unit * unit;
     S = (T + chunk - 1) / chunk;
     if (BH * S > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
     // 32-bit buffer offsets, also for the tile reads past T (at most 4 tiles)
