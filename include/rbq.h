@@ -162,10 +162,9 @@ int32_t rbq_quant_attn_splits(const rbq_kv_cache* c, int32_t H_q, int32_t L);
  * rbq_quant_attn_decode needs for this cache state, query shape and split
  * count (splits == 0: the automatic count).  0 means no workspace is needed.
  * Returns (size_t)0 also for invalid arguments; the decode call reports those.
- * The workspace must be zero-filled when it is first allocated: its first
- * 64 KiB hold the counters of the in-kernel merge of split partials, and
- * every completed call leaves them zero again, so a workspace can be reused
- * by later calls of any shape (not by calls that overlap in time).
+ * The workspace holds the split partials between the attention kernel and
+ * the merge kernel that follows it on the same stream; its contents before a
+ * call do not matter, and calls that overlap in time must not share one.
  */
 size_t rbq_quant_attn_workspace_bytes(const rbq_kv_cache* c, int32_t H_q, int32_t L,
                                       int32_t splits);

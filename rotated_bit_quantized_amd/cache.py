@@ -141,9 +141,7 @@ class RotatedQuantKVCache:
         if nb == 0:
             return None
         if self._ws is None or self._ws.numel() < nb:
-            # zero-filled once: the attention keeps its merge counters there and
-            # leaves them zero after every call
-            self._ws = torch.zeros(nb, dtype=torch.uint8, device=self.device)
+            self._ws = torch.empty(nb, dtype=torch.uint8, device=self.device)
         return self._ws
 
     def attend(self, q: torch.Tensor, scale: Optional[float] = None, causal: bool = True,

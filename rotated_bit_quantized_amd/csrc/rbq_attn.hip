@@ -314,7 +314,7 @@ int make_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Pla
     p->S = (int)S;
     p->chunk = (T + S - 1) / S;
     p->ws_bytes = (S == 1) ? 0
-                           : kWsCounterBytes + (size_t)c->B * c->H_kv * p->n_rb * S * p->RB *
+                           : (size_t)c->B * c->H_kv * p->n_rb * S * p->RB *
                                                    (kHeadDim + 2) * sizeof(float);
     return RBQ_OK;
 }
@@ -426,7 +426,7 @@ extern "C" int rbq_quant_attn_decode(const rbq_kv_cache* c, const void* q, int32
     a.rot = rot_blocks;
     a.out = out;
     const size_t n_part = (size_t)c->B * c->H_kv * p.n_rb * p.S * p.RB;
-    a.ws_o = p.ws_bytes ? (float*)((char*)ws + kWsCounterBytes) : nullptr;
+    a.ws_o = p.ws_bytes ? (float*)ws : nullptr;
     a.ws_ml = p.ws_bytes ? a.ws_o + n_part * kHeadDim : nullptr;
     a.capacity = c->capacity;
     a.T = c->offset;

@@ -9,10 +9,11 @@
 // wave walks 32-key tiles of the split (its first tile's loads are issued
 // before the set-up, the next tile's are in flight while one is computed)
 // with an online softmax (base 2, rescaled only when the running maximum
-// grows by more than 2^8); the 8 wave partials are merged in LDS, and the
-// split partials are merged in-kernel by the last-arriving workgroup of each
-// group of 16 (a tree of such merges), whose last step normalises and
-// rotates the output back.
+// grows by more than 2^8); the 8 wave partials are merged in LDS.  With one
+// split the workgroup normalises the rows, rotates them back and stores the
+// output; with several it stores its record (m, l, unnormalised o), and a
+// second small kernel merges the records of each (b, kv head), normalises and
+// rotates back.
 //
 // All products run as 16x16x32 MFMAs.  Lane l = 16 j + n: j selects a k-slot
 // group of the operands and a quarter of the accumulator rows, n a column.
@@ -60,7 +61,6 @@ constexpr int kWaves = 8;                                  // one workgroup per 
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;                                  // keys per wave iteration
 constexpr int kRows = 8;                                   // query rows per kv head
-constexpr int kFanIn = 16;                                 // records per merge step
 // split record in the workspace: (m, l) per row, then o column-major
 // [256 columns][8 rows]
 constexpr int kRecFloats = 2 * kRows + kRows * kHeadDim;
@@ -84,8 +84,6 @@ constexpr int kRecOff = kLoopSmem;
 constexpr int kWeightOff = kRecOff + kWaves * kWaveRecFloats * 4;
 constexpr int kSmemBytes = kWeightOff + kWaves * kWeightFloats * 4;
 static_assert(kSmemBytes <= 160 * 1024, "LDS of one compute unit");
-constexpr int kCounterBytes = (int)kWsCounterBytes;
-constexpr int kMaxLevels = 8;
 constexpr float kLog2e = 1.44269504088896340736f;
 static_assert(kWaves == kRows && kThreads == kRows * kHeadDim / 4, "one query block per thread");
 static_assert(kWaves == 8, "one score operand set (group, half) per wave");
@@ -93,7 +91,6 @@ static_assert((kRows * kHeadDim + kRows * 8 + kHeadDim * 4) * 4 <= kWaves * kWav
               "query rows, their statistics and the rotation blocks fit the staging area");
 static_assert(kThreads * 2 == kHeadDim * 4, "8 bytes of the rotation blocks per thread");
 static_assert(kThreads == 2 * kHeadDim && kRows == 8, "merge: one column and 4 rows per thread");
-static_assert(kRows * kFanIn <= 2 * 64 && kFanIn == 16, "merge weights: 16-lane rows of waves 0 and 1");
 
 struct MArgs {
     const uint16_t* q;
@@ -106,13 +103,9 @@ struct MArgs {
     const float* rot;
     float* out;
     float* rec;
-    int* cnt;
     int64_t capacity;
     int T, chunk;
     int Hkv, n_rep, L, G, S, causal;
-    int n_lvl[kMaxLevels];
-    int64_t rec_base[kMaxLevels];
-    int cnt_base[kMaxLevels];
     float qscale;  // scale * log2(e)
 };
 
@@ -161,6 +154,29 @@ __device__ __forceinline__ float sum16(float x) {
     return x + dpp<0x140>(x);
 }
 
+// Normalise row `row` of column `col` (acc / Ls), rotate back and store it if
+// row < G.  The 4 columns of a rotation block lie in one lane quad (lane & 3
+// = col & 3): z = sum_k y[block column k] * B[col & 3][k], in fp64.
+__device__ __forceinline__ void store_out(float* out, const float* rot, int b, int Hkv, int n_rep,
+                                          int L, int G, int kvh, int col, int row, float acc,
+                                          float Ls) {
+    const float y = acc * (1.0f / Ls);
+    float z = y;
+    if (rot != nullptr) {
+        const float4 v = *reinterpret_cast<const float4*>(rot + 16 * (col >> 2) + 4 * (col & 3));
+        const float y0 = dpp<0x00>(y), y1 = dpp<0x55>(y), y2 = dpp<0xAA>(y), y3 = dpp<0xFF>(y);
+        double s2 = (double)y0 * (double)v.x;
+        s2 = s2 + (double)y1 * (double)v.y;
+        s2 = s2 + (double)y2 * (double)v.z;
+        s2 = s2 + (double)y3 * (double)v.w;
+        z = (float)s2;
+    }
+    if (row < G) {
+        const int hq = kvh * n_rep + row / L;
+        out[(((int64_t)b * Hkv * n_rep + hq) * L + row % L) * kHeadDim + col] = z;
+    }
+}
+
 // x[l] + x[l ^ 32]
 __device__ __forceinline__ float add_swap32(float x) {
     const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
@@ -193,24 +209,6 @@ __device__ __forceinline__ uint32_t chunk_offset(const uint32_t w[6]) {
         if constexpr (wi + 1 < 6) return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & 0x7FF8u;
         else return (w[wi] >> sh) & 0x7FF8u;
     }
-}
-
-// Split-partial records are exchanged between workgroups of one launch,
-// which may run on different XCDs (each with its own L2).  They are written
-// and read with relaxed agent-scope atomics (write-through / read-through the
-// XCD L2), the writer waits for its stores to complete before it bumps the
-// group counter, and only the last arrival of a group reads the group's
-// records; no L2 write-back fence is needed.
-__device__ __forceinline__ void st_rec(float* p, float a, float b) {
-    const unsigned long long v =
-        (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
-    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), v, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float2 ld_rec(const float* p) {
-    const unsigned long long v = __hip_atomic_load(
-        reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
 }
 
 // Global loads of one 32-key tile for this lane (rows at or past T read as
@@ -272,7 +270,6 @@ __device__ __forceinline__ void pv_tile(unsigned char* smem, const uint32_t wv0[
 template <int DT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(MArgs a) {
     __shared__ __align__(16) unsigned char smem[kSmemBytes];
-    __shared__ int s_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -715,106 +712,97 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
     }
 
-    // ---- split merge tree; the last step writes the output ----
-    int lvl = 0, idx = split;
-    while (a.n_lvl[lvl] > 1) {
-        const int n_k = a.n_lvl[lvl];
-        float* rp = a.rec + (a.rec_base[lvl] + (int64_t)bh * n_k + idx) * kRecFloats;
-        if (col == 0) {
+    // ---- one split: the output; several: this split's record (the merge
+    //      kernel that follows reads it) ----
+    if (a.S == 1) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) st_rec(rp + 2 * (4 * h + i), M[i], Ls[i]);
-        }
-        float* ro = rp + 2 * kRows + col * kRows + 4 * h;
-        st_rec(ro, acc[0], acc[1]);
-        st_rec(ro + 2, acc[2], acc[3]);
-        __builtin_amdgcn_s_waitcnt(0);  // this thread's record stores are complete
-        __syncthreads();
-        const int g = idx / kFanIn;
-        const int members = (n_k - g * kFanIn < kFanIn) ? n_k - g * kFanIn : kFanIn;
-        const int n_groups = (n_k + kFanIn - 1) / kFanIn;
-        if (tid == 0) {
-            int* c = a.cnt + a.cnt_base[lvl] + bh * n_groups + g;
-            const int old = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const bool last = old == members - 1;
-            if (last) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_last = last;
-        }
-        __syncthreads();
-        if (!s_last) return;
-        // The group's records, all loads in flight at once: thread t < 128
-        // reads (m, l) of row t >> 4 of member t & 15; every thread reads its
-        // 4 rows of column col of every member.
-        const float* base = a.rec + (a.rec_base[lvl] + (int64_t)bh * n_k + g * kFanIn) * kRecFloats;
-        const int wrow = tid >> 4, wmbr = tid & 15;
+        for (int i = 0; i < 4; ++i)
+            store_out(a.out, a.rot, b, a.Hkv, a.n_rep, a.L, a.G, kvh, col, 4 * h + i, acc[i], Ls[i]);
+        return;
+    }
+    float* rp = a.rec + ((int64_t)bh * a.S + split) * kRecFloats;
+    if (col == 0) {
+        *reinterpret_cast<float4*>(rp + 8 * h) = make_float4(M[0], Ls[0], M[1], Ls[1]);
+        *reinterpret_cast<float4*>(rp + 8 * h + 4) = make_float4(M[2], Ls[2], M[3], Ls[3]);
+    }
+    *reinterpret_cast<float4*>(rp + 2 * kRows + col * kRows + 4 * h) =
+        make_float4(acc[0], acc[1], acc[2], acc[3]);
+}
+
+// Merge of the split records of one (b, kv head) and one 64-column block:
+// 128 threads, thread = (column, rows 4h .. 4h+3).  Records are read 16 at a
+// time with all their loads in flight: thread t also reads (m, l) of row
+// t >> 4 of member t & 15, from which the 16-lane reductions give the block's
+// maximum M, the weights 2^(m - M) and the weighted row sum; blocks of 16 are
+// folded into the running result rescaled to the larger maximum.
+struct CArgs {
+    const float* rec;
+    const float* rot;
+    float* out;
+    int S, Hkv, n_rep, L, G;
+};
+
+__global__ __launch_bounds__(128) void attn_mfma_merge_kernel(CArgs a) {
+    __shared__ float wts[kRows * 16];
+    __shared__ float stat[2 * kRows];
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x >> 2;
+    const int col = ((blockIdx.x & 3) << 6) + (tid & 63);
+    const int h = tid >> 6;
+    const int b = bh / a.Hkv;
+    const int kvh = bh - b * a.Hkv;
+    const float* base = a.rec + (int64_t)bh * a.S * kRecFloats;
+    const int wrow = tid >> 4, wmbr = tid & 15;
+    float M[4], Ls[4], acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        M[i] = -INFINITY;
+        Ls[i] = 0.f;
+        acc[i] = 0.f;
+    }
+    for (int m0 = 0; m0 < a.S; m0 += 16) {
+        const int members = (a.S - m0 < 16) ? a.S - m0 : 16;
         float2 ml = make_float2(-INFINITY, 0.f);
-        if (tid < kRows * kFanIn && wmbr < members) ml = ld_rec(base + (int64_t)wmbr * kRecFloats + 2 * wrow);
-        float2 o01[kFanIn], o23[kFanIn];
+        if (wmbr < members)
+            ml = *reinterpret_cast<const float2*>(base + (int64_t)(m0 + wmbr) * kRecFloats + 2 * wrow);
+        float4 o[16];
 #pragma unroll
-        for (int k = 0; k < kFanIn; ++k) {
-            const int mbr = (k < members) ? k : 0;
-            const float* o = base + (int64_t)mbr * kRecFloats + 2 * kRows + col * kRows + 4 * h;
-            o01[k] = ld_rec(o);
-            o23[k] = ld_rec(o + 2);
+        for (int k = 0; k < 16; ++k) {
+            const int mbr = m0 + ((k < members) ? k : 0);
+            o[k] = *reinterpret_cast<const float4*>(base + (int64_t)mbr * kRecFloats + 2 * kRows +
+                                                    col * kRows + 4 * h);
         }
-        // merge weights per (row, member): 2^(m - max over members), and the
-        // merged row sums (16-lane reductions over the members)
-        float* wts = reinterpret_cast<float*>(smem);  // [row][member], then L[row], M[row]
-        if (tid < kRows * kFanIn) {
-            const float Mx = max16(ml.x);
-            const float wv = (ml.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml.x - Mx);
-            const float Lsum = sum16(wv * ml.y);
-            wts[wrow * kFanIn + wmbr] = wv;
-            if (wmbr == 0) {
-                wts[kRows * kFanIn + wrow] = Lsum;
-                wts[kRows * kFanIn + kRows + wrow] = Mx;
-            }
+        const float Mx = max16(ml.x);
+        const float wv = (ml.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml.x - Mx);
+        const float Lsum = sum16(wv * ml.y);
+        __syncthreads();  // the previous block's weights are read
+        wts[wrow * 16 + wmbr] = wv;
+        if (wmbr == 0) {
+            stat[wrow] = Mx;
+            stat[kRows + wrow] = Lsum;
         }
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            acc[i] = 0.f;
-            Ls[i] = wts[kRows * kFanIn + 4 * h + i];
-            M[i] = wts[kRows * kFanIn + kRows + 4 * h + i];
-        }
+            const int row = 4 * h + i;
+            float ac = 0.f;
 #pragma unroll
-        for (int k = 0; k < kFanIn; ++k) {
-            const float o[4] = {o01[k].x, o01[k].y, o23[k].x, o23[k].y};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = fmaf(wts[(4 * h + i) * kFanIn + k], o[i], acc[i]);
+            for (int k = 0; k < 16; ++k) {
+                const float ok = (i == 0) ? o[k].x : (i == 1) ? o[k].y : (i == 2) ? o[k].z : o[k].w;
+                ac = fmaf(wts[row * 16 + k], ok, ac);
+            }
+            const float Mc = stat[row], Lc = stat[kRows + row];
+            const float Mn = fmaxf(M[i], Mc);
+            const float fa = (M[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M[i] - Mn);
+            const float fc = (Mc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(Mc - Mn);
+            Ls[i] = fmaf(Lc, fc, Ls[i] * fa);
+            acc[i] = fmaf(ac, fc, acc[i] * fa);
+            M[i] = Mn;
         }
-        __syncthreads();  // weights read before the next level reuses the space
-        idx = g;
-        ++lvl;
-    }
-
-    // ---- normalise, rotate back (a 4-column block lies in one lane quad),
-    //      store rows below G ----
-    float Bm[4] = {0.f, 0.f, 0.f, 0.f};
-    const bool rot_out = a.rot != nullptr;
-    if (rot_out) {
-        const float4 v = *reinterpret_cast<const float4*>(a.rot + 16 * (col >> 2) + 4 * (col & 3));
-        Bm[0] = v.x; Bm[1] = v.y; Bm[2] = v.z; Bm[3] = v.w;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 4 * h + i;
-        const float y = acc[i] * (1.0f / Ls[i]);
-        float z = y;
-        if (rot_out) {
-            // z = sum_k y[block column k] * B[col & 3][k], in fp64
-            const float y0 = dpp<0x00>(y), y1 = dpp<0x55>(y), y2 = dpp<0xAA>(y), y3 = dpp<0xFF>(y);
-            double s2 = (double)y0 * (double)Bm[0];
-            s2 = s2 + (double)y1 * (double)Bm[1];
-            s2 = s2 + (double)y2 * (double)Bm[2];
-            s2 = s2 + (double)y3 * (double)Bm[3];
-            z = (float)s2;
-        }
-        if (row < a.G) {
-            const int hq = kvh * a.n_rep + row / a.L;
-            const int qi = row % a.L;
-            a.out[(((int64_t)b * a.Hkv * a.n_rep + hq) * a.L + qi) * kHeadDim + col] = z;
-        }
-    }
+    for (int i = 0; i < 4; ++i)
+        store_out(a.out, a.rot, b, a.Hkv, a.n_rep, a.L, a.G, kvh, col, 4 * h + i, acc[i], Ls[i]);
 }
 
 }  // namespace
@@ -843,24 +831,9 @@ int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Mfm
     if ((T + kWaves * kTile) * (int64_t)(kKWords * 4) > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
     p->S = (int)S;
     p->chunk = chunk;
-    p->levels = 0;
-    int64_t n = S, recs = 0, cnts = 0;
-    while (n > 1) {
-        if (p->levels >= kMaxLevels - 1) return RBQ_EUNSUPPORTED;
-        p->n_lvl[p->levels] = (int)n;
-        p->rec_base[p->levels] = recs;
-        p->cnt_base[p->levels] = (int)cnts;
-        recs += BH * n;
-        const int64_t groups = (n + kFanIn - 1) / kFanIn;
-        cnts += BH * groups;
-        n = groups;
-        ++p->levels;
-    }
-    p->n_lvl[p->levels] = 1;
-    if (cnts * (int64_t)sizeof(int) > kCounterBytes) return RBQ_EUNSUPPORTED;
     (void)n_rep;
     (void)L;
-    p->ws_bytes = (S == 1) ? 0 : (size_t)kCounterBytes + (size_t)recs * kRecFloats * sizeof(float);
+    p->ws_bytes = (S == 1) ? 0 : (size_t)BH * S * kRecFloats * sizeof(float);
     return RBQ_OK;
 }
 
@@ -878,8 +851,7 @@ int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
     a.vb = (const uint16_t*)c->v_biases;
     a.rot = rot_blocks;
     a.out = out;
-    a.cnt = (int*)ws;
-    a.rec = ws ? (float*)((char*)ws + kCounterBytes) : nullptr;
+    a.rec = (float*)ws;
     a.capacity = c->capacity;
     a.T = (int)c->offset;
     a.chunk = (int)p.chunk;
@@ -889,11 +861,6 @@ int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
     a.G = a.n_rep * L;
     a.S = p.S;
     a.causal = causal ? 1 : 0;
-    for (int k = 0; k < kMaxLevels; ++k) {
-        a.n_lvl[k] = (k <= p.levels) ? p.n_lvl[k] : 1;
-        a.rec_base[k] = (k < p.levels) ? p.rec_base[k] : 0;
-        a.cnt_base[k] = (k < p.levels) ? p.cnt_base[k] : 0;
-    }
     a.qscale = scale * kLog2e;
     const int64_t BH = (int64_t)c->B * c->H_kv;
     const dim3 grid((unsigned)(BH * p.S)), block(kThreads);
@@ -901,6 +868,18 @@ int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
         hipLaunchKernelGGL(attn_mfma_kernel<RBQ_BF16>, grid, block, 0, s, a);
     else
         hipLaunchKernelGGL(attn_mfma_kernel<RBQ_F16>, grid, block, 0, s, a);
+    if (p.S > 1) {
+        CArgs m;
+        m.rec = a.rec;
+        m.rot = rot_blocks;
+        m.out = out;
+        m.S = p.S;
+        m.Hkv = a.Hkv;
+        m.n_rep = a.n_rep;
+        m.L = L;
+        m.G = a.G;
+        hipLaunchKernelGGL(attn_mfma_merge_kernel, dim3((unsigned)(BH * 4)), dim3(128), 0, s, m);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
         set_hip_error((int)e);

@@ -29,19 +29,11 @@ int check_cache(const rbq_kv_cache* c);
 int32_t auto_splits(const rbq_kv_cache* c, int32_t H_q, int32_t L);
 
 // Launch plan of the matrix-core attention path (up to 8 query rows per kv
-// head): key splits, their length, and the tree of partial-record merges.
+// head): key splits, their length, and the workspace for the split records.
 constexpr int kMfmaMaxRows = 8;
-// The first kWsCounterBytes of every attention workspace hold the merge
-// counters of the matrix-core path (zero between calls); partial results of
-// either path start after them.
-constexpr size_t kWsCounterBytes = 65536;
 struct MfmaPlan {
     int S;
     int64_t chunk;
-    int levels;          // merge levels with more than one record
-    int n_lvl[8];        // records per (b, kv head) at each level
-    int64_t rec_base[8]; // first record of each level
-    int cnt_base[8];     // first counter of each level
     size_t ws_bytes;
 };
 int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, MfmaPlan* p);
