@@ -1,7 +1,10 @@
 // Fused decode attention over the packed K4/V3 cache on the gfx950 matrix
 // cores (asym_quantized_sdpa on the quant_kv.py page, with the SO(4)
-// rotation of q on entry and the inverse rotation of the output), for up to
-// 8 query rows per kv head (GQA group x verify block).
+// rotation of q on entry and the inverse rotation of the output).  The G =
+// (H_q / H_kv) x L query rows of a kv head (GQA group x verify block) are
+// taken 8 at a time: one workgroup per block of 8 rows; blocks of the same
+// keys run side by side, so their repeated reads are mostly served by the
+// caches.
 //
 // Decomposition: one workgroup of 8 wave64s (about one per compute unit) per
 // (b, kv head, key split).  Set-up is shared: wave w rotates query row w and
@@ -106,6 +109,7 @@ struct MArgs {
     int64_t capacity;
     int T, chunk;
     int Hkv, n_rep, L, G, S, causal;
+    int RB;        // blocks of 8 query rows per kv head
     float qscale;  // scale * log2(e)
 };
 
@@ -182,10 +186,6 @@ __device__ __forceinline__ float add_swap32(float x) {
     const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                     false);
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-
-__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
 }
 
 __device__ __forceinline__ uint32_t mul2(uint32_t a, uint32_t s) {
@@ -280,8 +280,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const bool lo_part = n >= 8;
     const int rb = 4 * (j & 1);         // accumulator rows of this lane: rb .. rb+3
 
-    const int bh = blockIdx.x / a.S;
-    const int split = blockIdx.x - bh * a.S;
+    const int bhr = blockIdx.x / a.S;           // (b, kv head, block of 8 rows)
+    const int split = blockIdx.x - bhr * a.S;
+    const int bh = bhr / a.RB;
+    const int r0 = 8 * (bhr - bh * a.RB);       // first query row of the block
     const int b = bh / a.Hkv;
     const int kvh = bh - b * a.Hkv;
     const int T = a.T;
@@ -294,10 +296,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     //      first tile.  Their latency overlaps the table build, and waiting
     //      for the query does not wait for the tile. ----
     uint2 qraw = make_uint2(0u, 0u);
-    if (wave < a.G) {
-        const int h = kvh * a.n_rep + wave / a.L;
+    if (r0 + wave < a.G) {
+        const int R = r0 + wave;
+        const int h = kvh * a.n_rep + R / a.L;
         const uint16_t* qrow =
-            a.q + (((int64_t)b * a.Hkv * a.n_rep + h) * a.L + wave % a.L) * kHeadDim;
+            a.q + (((int64_t)b * a.Hkv * a.n_rep + h) * a.L + R % a.L) * kHeadDim;
         qraw = *reinterpret_cast<const uint2*>(qrow + 4 * lane);
     }
     const bool rotated = a.rot != nullptr;
@@ -440,8 +443,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int Er = __float_as_int(qstat[row * 8 + 4]);
         frow[c] = ldexpf(1.0f, 24 - Er);
         grow[c] = (DT == RBQ_BF16) ? 1.0f : ldexpf(1.0f, 6 - Er);
-        const bool ok = row < a.G;
-        vis[c] = (ok && a.causal) ? T - a.L + (row % a.L) + 1 : T;
+        const int R = r0 + row;
+        vis[c] = (R < a.G && a.causal) ? T - a.L + (R % a.L) + 1 : T;
     }
     const int vis_min = min(min(vis[0], vis[1]), min(vis[2], vis[3]));
     __syncthreads();  // query operands complete; query rows no longer read
@@ -717,10 +720,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (a.S == 1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            store_out(a.out, a.rot, b, a.Hkv, a.n_rep, a.L, a.G, kvh, col, 4 * h + i, acc[i], Ls[i]);
+            store_out(a.out, a.rot, b, a.Hkv, a.n_rep, a.L, a.G, kvh, col, r0 + 4 * h + i, acc[i],
+                      Ls[i]);
         return;
     }
-    float* rp = a.rec + ((int64_t)bh * a.S + split) * kRecFloats;
+    float* rp = a.rec + ((int64_t)bhr * a.S + split) * kRecFloats;
     if (col == 0) {
         *reinterpret_cast<float4*>(rp + 8 * h) = make_float4(M[0], Ls[0], M[1], Ls[1]);
         *reinterpret_cast<float4*>(rp + 8 * h + 4) = make_float4(M[2], Ls[2], M[3], Ls[3]);
@@ -739,19 +743,21 @@ struct CArgs {
     const float* rec;
     const float* rot;
     float* out;
-    int S, Hkv, n_rep, L, G;
+    int S, Hkv, n_rep, L, G, RB;
 };
 
 __global__ __launch_bounds__(128) void attn_mfma_merge_kernel(CArgs a) {
     __shared__ float wts[kRows * 16];
     __shared__ float stat[2 * kRows];
     const int tid = threadIdx.x;
-    const int bh = blockIdx.x >> 2;
+    const int bhr = blockIdx.x >> 2;
+    const int bh = bhr / a.RB;
+    const int r0 = 8 * (bhr - bh * a.RB);
     const int col = ((blockIdx.x & 3) << 6) + (tid & 63);
     const int h = tid >> 6;
     const int b = bh / a.Hkv;
     const int kvh = bh - b * a.Hkv;
-    const float* base = a.rec + (int64_t)bh * a.S * kRecFloats;
+    const float* base = a.rec + (int64_t)bhr * a.S * kRecFloats;
     const int wrow = tid >> 4, wmbr = tid & 15;
     float M[4], Ls[4], acc[4];
 #pragma unroll
@@ -802,7 +808,8 @@ __global__ __launch_bounds__(128) void attn_mfma_merge_kernel(CArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        store_out(a.out, a.rot, b, a.Hkv, a.n_rep, a.L, a.G, kvh, col, 4 * h + i, acc[i], Ls[i]);
+        store_out(a.out, a.rot, b, a.Hkv, a.n_rep, a.L, a.G, kvh, col, r0 + 4 * h + i, acc[i],
+                  Ls[i]);
 }
 
 }  // namespace
@@ -810,12 +817,13 @@ __global__ __launch_bounds__(128) void attn_mfma_merge_kernel(CArgs a) {
 // ---- host side: planning and launch ----
 
 int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, MfmaPlan* p) {
-    const int n_rep = H_q / c->H_kv;
+    const int64_t G = (int64_t)(H_q / c->H_kv) * L;
+    const int64_t RB = (G + kRows - 1) / kRows;  // blocks of 8 query rows, one workgroup each
     const int64_t T = c->offset;
-    const int64_t BH = (int64_t)c->B * c->H_kv;
+    const int64_t units = (int64_t)c->B * c->H_kv * RB;
     int64_t S = splits;
     if (S == 0) {
-        S = (256 + BH - 1) / BH;  // about one workgroup per compute unit
+        S = (256 + units - 1) / units;  // about one workgroup per compute unit
         const int64_t max_s = (T + kWaves * kTile - 1) / (kWaves * kTile);
         if (S > max_s) S = max_s;
     }
@@ -826,14 +834,13 @@ int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Mfm
     const int64_t unit = (splits == 0) ? (int64_t)kWaves * kTile : (int64_t)kTile;
     chunk = (chunk + unit - 1) / unit * unit;
     S = (T + chunk - 1) / chunk;
-    if (BH * S > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
+    if (units * S > 0x7FFFFFFF || RB > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
     // 32-bit buffer offsets, also for the tile reads past T (at most 4 tiles)
     if ((T + kWaves * kTile) * (int64_t)(kKWords * 4) > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
     p->S = (int)S;
+    p->RB = (int)RB;
     p->chunk = chunk;
-    (void)n_rep;
-    (void)L;
-    p->ws_bytes = (S == 1) ? 0 : (size_t)BH * S * kRecFloats * sizeof(float);
+    p->ws_bytes = (S == 1) ? 0 : (size_t)units * S * kRecFloats * sizeof(float);
     return RBQ_OK;
 }
 
@@ -860,10 +867,11 @@ int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
     a.L = L;
     a.G = a.n_rep * L;
     a.S = p.S;
+    a.RB = p.RB;
     a.causal = causal ? 1 : 0;
     a.qscale = scale * kLog2e;
-    const int64_t BH = (int64_t)c->B * c->H_kv;
-    const dim3 grid((unsigned)(BH * p.S)), block(kThreads);
+    const int64_t units = (int64_t)c->B * c->H_kv * p.RB;
+    const dim3 grid((unsigned)(units * p.S)), block(kThreads);
     if (c->dtype == RBQ_BF16)
         hipLaunchKernelGGL(attn_mfma_kernel<RBQ_BF16>, grid, block, 0, s, a);
     else
@@ -878,7 +886,8 @@ int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
         m.n_rep = a.n_rep;
         m.L = L;
         m.G = a.G;
-        hipLaunchKernelGGL(attn_mfma_merge_kernel, dim3((unsigned)(BH * 4)), dim3(128), 0, s, m);
+        m.RB = a.RB;
+        hipLaunchKernelGGL(attn_mfma_merge_kernel, dim3((unsigned)(units * 4)), dim3(128), 0, s, m);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
@@ -888,4 +897,49 @@ int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
     return RBQ_OK;
 }
 
+// ---- C ABI: argument checks, planning, dispatch ----
+
+namespace {
+
+int check_attn(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits) {
+    int st = check_cache(c);
+    if (st != RBQ_OK) return st;
+    if (H_q <= 0 || H_q % c->H_kv != 0 || splits < 0) return RBQ_EINVAL;
+    if (L < 1 || (int64_t)L > c->offset) return RBQ_ERANGE;
+    return RBQ_OK;
+}
+
+}  // namespace
+
 }  // namespace rbq
+
+using namespace rbq;
+
+extern "C" int32_t rbq_quant_attn_splits(const rbq_kv_cache* c, int32_t H_q, int32_t L) {
+    int st = check_attn(c, H_q, L, 0);
+    if (st != RBQ_OK) return st;
+    MfmaPlan mp;
+    st = mfma_plan(c, H_q, L, 0, &mp);
+    return st != RBQ_OK ? st : mp.S;
+}
+
+extern "C" size_t rbq_quant_attn_workspace_bytes(const rbq_kv_cache* c, int32_t H_q, int32_t L,
+                                                 int32_t splits) {
+    if (check_attn(c, H_q, L, splits) != RBQ_OK) return 0;
+    MfmaPlan mp;
+    return mfma_plan(c, H_q, L, splits, &mp) == RBQ_OK ? mp.ws_bytes : 0;
+}
+
+extern "C" int rbq_quant_attn_decode(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L,
+                                     float scale, int32_t causal, const float* rot_blocks,
+                                     float* out, int32_t splits, void* ws, size_t ws_bytes,
+                                     void* stream) {
+    int st = check_attn(c, H_q, L, splits);
+    if (st != RBQ_OK) return st;
+    if (q == nullptr || out == nullptr) return RBQ_EINVAL;
+    MfmaPlan mp;
+    st = mfma_plan(c, H_q, L, splits, &mp);
+    if (st != RBQ_OK) return st;
+    if (mp.ws_bytes > 0 && (ws == nullptr || ws_bytes < mp.ws_bytes)) return RBQ_EWORKSPACE;
+    return mfma_launch(c, q, H_q, L, scale, causal, rot_blocks, out, mp, ws, stream);
+}

@@ -25,15 +25,12 @@ void set_hip_error(int err);
 // and the supported configuration (RBQ_EUNSUPPORTED otherwise).
 int check_cache(const rbq_kv_cache* c);
 
-// Split count chosen when the caller passes 0 (VALU attention path).
-int32_t auto_splits(const rbq_kv_cache* c, int32_t H_q, int32_t L);
-
-// Launch plan of the matrix-core attention path (up to 8 query rows per kv
-// head): key splits, their length, and the workspace for the split records.
-constexpr int kMfmaMaxRows = 8;
+// Launch plan of the matrix-core attention path: key splits, their length,
+// blocks of 8 query rows, and the workspace for the split records.
 struct MfmaPlan {
-    int S;
-    int64_t chunk;
+    int S;           // key splits
+    int RB;          // blocks of 8 query rows per kv head
+    int64_t chunk;   // keys per split
     size_t ws_bytes;
 };
 int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, MfmaPlan* p);
