@@ -82,11 +82,20 @@ constexpr int kStageBytes = 2 * 64 * 8;
 constexpr int kP16Bytes = 2 * 16 * 2 * 2 * 8;
 constexpr int kWaveBytes = 3 * kStageBytes + kP16Bytes;
 constexpr int kStageOff = kLutBytes + kQaBytes;
-constexpr int kLoopSmem = kStageOff + kWaves * kWaveBytes;
-constexpr int kRecOff = kLoopSmem;
-constexpr int kWeightOff = kRecOff + kWaves * kWaveRecFloats * 4;
-constexpr int kSmemBytes = kWeightOff + kWaves * kWeightFloats * 4;
-static_assert(kSmemBytes <= 160 * 1024, "LDS of one compute unit");
+constexpr int kSmemBytes = kStageOff + kWaves * kWaveBytes;
+// Second LDS array (a separate object, so that the compiler can tell the
+// direct-to-LDS tile transfers from every other LDS access): per wave a tile
+// buffer during the tile loop, then the wave's record; then the merge weights.
+// A tile buffer holds one 32-key tile as the memory holds it: K words, V
+// words, K scales, K biases, V scales, V biases.
+constexpr int kWaveAreaBytes = kWaveRecFloats * 4;
+constexpr int kBufK = 0, kBufV = 4096, kBufKs = 7168, kBufKb = 7424, kBufVs = 7680, kBufVb = 7936;
+constexpr int kTileBufBytes = 8192;
+constexpr int kWeightOff = kWaves * kWaveAreaBytes;
+constexpr int kTbufBytes = kWeightOff + kWaves * kWeightFloats * 4;
+static_assert(kSmemBytes + kTbufBytes <= 160 * 1024, "LDS of one compute unit");
+static_assert(kTileBufBytes <= kWaveAreaBytes && kWaveAreaBytes % 16 == 0,
+              "a tile buffer fits a wave's record area");
 constexpr float kLog2e = 1.44269504088896340736f;
 static_assert(kWaves == kRows && kThreads == kRows * kHeadDim / 4, "one query block per thread");
 static_assert(kWaves == 8, "one score operand set (group, half) per wave");
@@ -181,6 +190,15 @@ __device__ __forceinline__ void store_out(float* out, const float* rot, int b, i
     }
 }
 
+// Workgroup barrier that orders LDS accesses only: the waves exchange data
+// through LDS alone, so outstanding global loads (tile prefetches) stay in
+// flight across it (__syncthreads would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // x[l] + x[l ^ 32]
 __device__ __forceinline__ float add_swap32(float x) {
     const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
@@ -211,9 +229,8 @@ __device__ __forceinline__ uint32_t chunk_offset(const uint32_t w[6]) {
     }
 }
 
-// Global loads of one 32-key tile for this lane (rows at or past T read as
-// zero through the buffer range check).  K data: key n of each block; V
-// data: group n & 3 of key 4j + (n >> 2) of each block.
+// Registers of one 32-key tile for this lane.  K data: key n of each block;
+// V data: group n & 3 of key 4j + (n >> 2) of each block.
 struct TileLoads {
     u32x2 kwv[2][4];   // K words 8g + 2j, 8g + 2j + 1
     u32x2 ksw[2];      // K scales (4 x 16 bit)
@@ -223,29 +240,58 @@ struct TileLoads {
     uint32_t vbb[2];   // V bias of the lane's (key, group)
 };
 
-__device__ __forceinline__ void load_tile(TileLoads& L, int t0, int n, int j,
-                                          __amdgpu_buffer_rsrc_t kw_r, __amdgpu_buffer_rsrc_t ks_r,
-                                          __amdgpu_buffer_rsrc_t kb_r, __amdgpu_buffer_rsrc_t vw_r,
-                                          __amdgpu_buffer_rsrc_t vs_r, __amdgpu_buffer_rsrc_t vb_r) {
+// 16-byte slot of K word chunk c (words 4c .. 4c+3) of tile key k in the tile
+// buffer: the chunks of a key are permuted by (k >> 1) & 7 so that the
+// 8-byte reads of 32 lanes (16 keys x 2 halves of a chunk) hit 64 distinct
+// banks.
+__device__ __forceinline__ int k_slot(int k, int c) { return 8 * k + (c ^ ((k >> 1) & 7)); }
+
+// Direct-to-LDS loads of the tile at key t0 into this wave's buffer (lane l
+// of an instruction lands at buffer offset + 16 l, or 4 l): 11 instructions,
+// each reading whole 128-byte lines.  Keys past the buffer ranges read as zero.
+__device__ __forceinline__ void dma_tile(lds_u8* buf, int t0, int lane, __amdgpu_buffer_rsrc_t kw_r,
+                                         __amdgpu_buffer_rsrc_t ks_r, __amdgpu_buffer_rsrc_t kb_r,
+                                         __amdgpu_buffer_rsrc_t vw_r, __amdgpu_buffer_rsrc_t vs_r,
+                                         __amdgpu_buffer_rsrc_t vb_r) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int p = 64 * m + lane;
+        const int k = p >> 3;
+        const int c = (p & 7) ^ ((k >> 1) & 7);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kw_r, buf + kBufK + 1024 * m, 16,
+                                                  (t0 + k) * 128 + 16 * c, 0, 0, 0);
+    }
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vw_r, buf + kBufV + 1024 * m, 16,
+                                                  t0 * 96 + 16 * (64 * m + lane), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ks_r, buf + kBufKs, 4, t0 * 8 + 4 * lane, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kb_r, buf + kBufKb, 4, t0 * 8 + 4 * lane, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vs_r, buf + kBufVs, 4, t0 * 8 + 4 * lane, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vb_r, buf + kBufVb, 4, t0 * 8 + 4 * lane, 0, 0, 0);
+}
+
+// The lane's operands of the buffered tile.
+__device__ __forceinline__ void read_tile(TileLoads& L, const unsigned char* buf, int n, int j) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-        const int key = t0 + 16 * blk + n;
+        const int k = 16 * blk + n;
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-            L.kwv[blk][g] = __builtin_amdgcn_raw_buffer_load_b64(kw_r, key * 128 + 32 * g + 8 * j, 0, 0);
-        L.ksw[blk] = __builtin_amdgcn_raw_buffer_load_b64(ks_r, key * 8, 0, 0);
-        L.kbw[blk] = __builtin_amdgcn_raw_buffer_load_b64(kb_r, key * 8, 0, 0);
-        const int vkey = t0 + 16 * blk + 4 * j + (n >> 2);
+            L.kwv[blk][g] = *reinterpret_cast<const u32x2*>(
+                buf + kBufK + 16 * k_slot(k, 2 * g + (j >> 1)) + 8 * (j & 1));
+        L.ksw[blk] = *reinterpret_cast<const u32x2*>(buf + kBufKs + 8 * k);
+        L.kbw[blk] = *reinterpret_cast<const u32x2*>(buf + kBufKb + 8 * k);
+        const int vk = 16 * blk + 4 * j + (n >> 2);
         const int vg = n & 3;
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            const u32x2 z =
-                __builtin_amdgcn_raw_buffer_load_b64(vw_r, vkey * 96 + 24 * vg + 8 * k, 0, 0);
-            L.wv[blk][2 * k] = z[0];
-            L.wv[blk][2 * k + 1] = z[1];
+        for (int m = 0; m < 3; ++m) {
+            const u32x2 z = *reinterpret_cast<const u32x2*>(buf + kBufV + 96 * vk + 24 * vg + 8 * m);
+            L.wv[blk][2 * m] = z[0];
+            L.wv[blk][2 * m + 1] = z[1];
         }
-        L.vsb[blk] = __builtin_amdgcn_raw_buffer_load_b16(vs_r, vkey * 8 + 2 * vg, 0, 0);
-        L.vbb[blk] = __builtin_amdgcn_raw_buffer_load_b16(vb_r, vkey * 8 + 2 * vg, 0, 0);
+        L.vsb[blk] = *reinterpret_cast<const uint16_t*>(buf + kBufVs + 8 * vk + 2 * vg);
+        L.vbb[blk] = *reinterpret_cast<const uint16_t*>(buf + kBufVb + 8 * vk + 2 * vg);
     }
 }
 
@@ -270,6 +316,7 @@ __device__ __forceinline__ void pv_tile(unsigned char* smem, const uint32_t wv0[
 template <int DT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(MArgs a) {
     __shared__ __align__(16) unsigned char smem[kSmemBytes];
+    __shared__ __align__(16) unsigned char tbuf[kTbufBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -316,8 +363,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
     // unconditional: a wave without tiles reads keys of the next split or,
     // past T, zeros from the buffer range check, and never uses them
-    TileLoads cur;
-    load_tile(cur, t_begin + wave * kTile, n, j, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
+    // this wave's tile buffer, filled with its first tile unconditionally (a
+    // wave without tiles reads keys of the next split or, past T, zeros, and
+    // never uses them)
+    lds_u8* wbuf = (lds_u8*)tbuf + wave * kWaveAreaBytes;
+    const unsigned char* wbuf_g = tbuf + wave * kWaveAreaBytes;
+    dma_tile(wbuf, t_begin + wave * kTile, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
 
     // ---- decode table: entry e = 4 fp16 codes (e >> 3k) & 7 ----
     for (int e = tid; e < 4096; e += kThreads) {
@@ -336,7 +387,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     float* qstat = qrot + kRows * kHeadDim;  // [row][8]: group sums 0..3, E at 4
     float* rot_lds = qstat + kRows * 8;      // the 64 rotation blocks
     if (rotated) reinterpret_cast<float2*>(rot_lds)[tid] = rot2;
-    __syncthreads();
+    lds_barrier();
     {
         const float x[4] = {elem_to_f32<DT>(qraw.x), elem_to_f32<DT>(qraw.x >> 16),
                             elem_to_f32<DT>(qraw.y), elem_to_f32<DT>(qraw.y >> 16)};
@@ -371,7 +422,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             qstat[wave * 8 + 4] = __int_as_float((mx > 0.f) ? 15 - ex : 0);
         }
     }
-    __syncthreads();
+    lds_barrier();
     // ---- score operands, one (group g, half h2) set per wave: slot k of
     //      lane (j, n) holds element ci[k] of the 8 that word 8g + 2j + h2
     //      covers, of row r scaled by 2^E_r, times 1/16 for the slots fed by
@@ -447,7 +498,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         vis[c] = (R < a.G && a.causal) ? T - a.L + (R % a.L) + 1 : T;
     }
     const int vis_min = min(min(vis[0], vis[1]), min(vis[2], vis[3]));
-    __syncthreads();  // query operands complete; query rows no longer read
+    lds_barrier();  // query operands complete; query rows no longer read
+    // the 8 score operand sets, held in registers for the whole tile loop
+    f16x8 qa_r[4][2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+            qa_r[g][h2] = *reinterpret_cast<const f16x8*>(qa_lds + ((2 * g + h2) * 64 + lane) * 16);
 
     // per-wave staging for the transposing reads (byte offsets in smem)
     const uint32_t wbase = kStageOff + wave * kWaveBytes;
@@ -469,10 +527,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     for (int it = wave; it < n_tiles; it += kWaves) {
         const int t0 = t_begin + it * kTile;
-        // the wave's next tile is in flight while this one is computed
-        TileLoads nxt;
+        // this tile's transfer is complete; its operands are read out, then the
+        // buffer is refilled with the wave's next tile while this one is computed
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        TileLoads cur;
+        read_tile(cur, wbuf_g, n, j);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         if (it + kWaves < n_tiles)
-            load_tile(nxt, t0 + kWaves * kTile, n, j, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
+            dma_tile(wbuf, t0 + kWaves * kTile, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
 
         // ---- value scales and biases of the lane's (key, group) -> staging ----
 #pragma unroll
@@ -510,9 +572,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     const uint32_t w8 = w >> 8;
                     const u32x4 kv = {w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu,
                                       w8 & 0x00F000F0u};
-                    const f16x8 qop =
-                        *reinterpret_cast<const f16x8*>(qa_lds + ((2 * g + h2) * 64 + lane) * 16);
-                    acc[g] = mfma16(qop, as_f16x8(kv), acc[g]);
+                    acc[g] = mfma16(qa_r[g][h2], as_f16x8(kv), acc[g]);
                 }
             }
             const u32x4 kbop = {cur.kbw[blk][0], cur.kbw[blk][1], cur.kbw[blk][0], cur.kbw[blk][1]};
@@ -627,14 +687,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         pv_tile<DT, 13>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[13]);
         pv_tile<DT, 14>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[14]);
         pv_tile<DT, 15>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[15]);
-        cur = nxt;
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // no transfer into the buffer in flight
 
     // ---- wave record, stored as soon as this wave's tiles are done: hi + lo
     //      rows combined two registers at a time (after the lane-half swap,
     //      lanes 0-31 hold the sums of the first register and lanes 32-63 those
     //      of the second), row sums over the 16 key lanes ----
-    float* wrec = reinterpret_cast<float*>(smem + kRecOff) + wave * kWaveRecFloats;
+    float* wrec = reinterpret_cast<float*>(tbuf) + wave * kWaveRecFloats;
     float* wob = wrec + kHeadDim * kRows;
     float* wml = wob + kGroups * kRows;
     const int hl = j >> 1;  // 0: lanes 0-31, 1: lanes 32-63
@@ -669,7 +729,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 make_float4(l_row[0], l_row[1], l_row[2], l_row[3]);
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- merge the wave records.  Each wave first derives the weights
     //      2^(m_w - M) of all (wave w, row) pairs (lane = 8 w + row) into its
@@ -679,7 +739,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int grp = col >> 6;
     float M[4], Ls[4], acc[4];
     {
-        const float* rml = reinterpret_cast<const float*>(smem + kRecOff) + (lane >> 3) * kWaveRecFloats +
+        const float* rml = reinterpret_cast<const float*>(tbuf) + (lane >> 3) * kWaveRecFloats +
                            kHeadDim * kRows + kGroups * kRows;
         const float mw = rml[lane & 7];
         const float lw = rml[kRows + (lane & 7)];
@@ -691,7 +751,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         Lw += __shfl_xor(Lw, 8);
         Lw += __shfl_xor(Lw, 16);
         Lw += __shfl_xor(Lw, 32);
-        float* wts = reinterpret_cast<float*>(smem + kWeightOff) + wave * kWeightFloats;
+        float* wts = reinterpret_cast<float*>(tbuf + kWeightOff) + wave * kWeightFloats;
         wts[lane] = wv;
         if (lane < kRows) {
             wts[kWaves * kRows + lane] = Mx;
@@ -704,7 +764,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         acc[0] = acc[1] = acc[2] = acc[3] = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float* rw = reinterpret_cast<const float*>(smem + kRecOff) + w * kWaveRecFloats;
+            const float* rw = reinterpret_cast<const float*>(tbuf) + w * kWaveRecFloats;
             const float4 o = *reinterpret_cast<const float4*>(rw + col * kRows + 4 * (h ^ ((col >> 3) & 1)));
             const float4 ob = *reinterpret_cast<const float4*>(rw + kHeadDim * kRows + grp * kRows + 4 * h);
             const float4 wt = *reinterpret_cast<const float4*>(wts + w * kRows + 4 * h);
@@ -781,13 +841,13 @@ __global__ __launch_bounds__(128) void attn_mfma_merge_kernel(CArgs a) {
         const float Mx = max16(ml.x);
         const float wv = (ml.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml.x - Mx);
         const float Lsum = sum16(wv * ml.y);
-        __syncthreads();  // the previous block's weights are read
+        lds_barrier();  // the previous block's weights are read
         wts[wrow * 16 + wmbr] = wv;
         if (wmbr == 0) {
             stat[wrow] = Mx;
             stat[kRows + wrow] = Lsum;
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 4 * h + i;
