@@ -167,16 +167,23 @@ __device__ __forceinline__ float sum16(float x) {
     return x + dpp<0x140>(x);
 }
 
+// Row col & 3 of the rotation block of column `col` (zeros without rotation);
+// loaded before the results it multiplies are ready.
+__device__ __forceinline__ float4 rot_row(const float* rot, int col) {
+    if (rot == nullptr) return make_float4(0.f, 0.f, 0.f, 0.f);
+    return *reinterpret_cast<const float4*>(rot + 16 * (col >> 2) + 4 * (col & 3));
+}
+
 // Normalise row `row` of column `col` (acc / Ls), rotate back and store it if
 // row < G.  The 4 columns of a rotation block lie in one lane quad (lane & 3
-// = col & 3): z = sum_k y[block column k] * B[col & 3][k], in fp64.
-__device__ __forceinline__ void store_out(float* out, const float* rot, int b, int Hkv, int n_rep,
-                                          int L, int G, int kvh, int col, int row, float acc,
-                                          float Ls) {
+// = col & 3): z = sum_k y[block column k] * B[col & 3][k], in fp64, with
+// v = B[col & 3] from rot_row.
+__device__ __forceinline__ void store_out(float* out, bool rotated, float4 v, int b, int Hkv,
+                                          int n_rep, int L, int G, int kvh, int col, int row,
+                                          float acc, float Ls) {
     const float y = acc * (1.0f / Ls);
     float z = y;
-    if (rot != nullptr) {
-        const float4 v = *reinterpret_cast<const float4*>(rot + 16 * (col >> 2) + 4 * (col & 3));
+    if (rotated) {
         const float y0 = dpp<0x00>(y), y1 = dpp<0x55>(y), y2 = dpp<0xAA>(y), y3 = dpp<0xFF>(y);
         double s2 = (double)y0 * (double)v.x;
         s2 = s2 + (double)y1 * (double)v.y;
@@ -191,12 +198,16 @@ __device__ __forceinline__ void store_out(float* out, const float* rot, int b, i
 }
 
 // Workgroup barrier that orders LDS accesses only: the waves exchange data
-// through LDS alone, so outstanding global loads (tile prefetches) stay in
-// flight across it (__syncthreads would wait for them).
+// through LDS alone, so outstanding global loads, tile transfers into LDS
+// included, stay in flight across it.  (A workgroup-scope LDS fence would
+// wait for those transfers too, since they count as LDS writes; __syncthreads
+// would wait for every global load.)  lgkmcnt(0) completes this wave's own
+// LDS accesses; the memory clobber keeps the compiler from moving memory
+// accesses across the barrier.  Data that a wave reads after the barrier
+// from another wave's direct-to-LDS transfer is not covered: the tile loop
+// waits for its own transfers (vmcnt) before reading them.
 __device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // x[l] + x[l ^ 32]
@@ -432,9 +443,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         constexpr int ci[8] = {0, 4, 1, 5, 2, 6, 3, 7};
         const int g = wave >> 1, h2 = wave & 1;
         const int Er = __float_as_int(qstat[r * 8 + 4]);
-        const float4* src = reinterpret_cast<const float4*>(qrot + r * kHeadDim + 64 * g + 16 * j + 8 * h2);
-        const float4 v0 = src[0], v1 = src[1];
-        const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        // read through an LDS-typed pointer: through a generic one the compiler
+        // cannot tell these reads from the tile transfer in flight and waits
+        // for it
+        typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+        const lds_f32x4* src = (const lds_f32x4*)((lds_u8*)smem + kStageOff +
+                                                  4 * (r * kHeadDim + 64 * g + 16 * j + 8 * h2));
+        const f32x4 v0 = src[0], v1 = src[1];
+        const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         f16x8 qa;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -778,10 +794,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // ---- one split: the output; several: this split's record (the merge
     //      kernel that follows reads it) ----
     if (a.S == 1) {
+        const float4 rv = rot_row(a.rot, col);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            store_out(a.out, a.rot, b, a.Hkv, a.n_rep, a.L, a.G, kvh, col, r0 + 4 * h + i, acc[i],
-                      Ls[i]);
+            store_out(a.out, rotated, rv, b, a.Hkv, a.n_rep, a.L, a.G, kvh, col, r0 + 4 * h + i,
+                      acc[i], Ls[i]);
         return;
     }
     float* rp = a.rec + ((int64_t)bhr * a.S + split) * kRecFloats;
@@ -819,6 +836,7 @@ __global__ __launch_bounds__(128) void attn_mfma_merge_kernel(CArgs a) {
     const int kvh = bh - b * a.Hkv;
     const float* base = a.rec + (int64_t)bhr * a.S * kRecFloats;
     const int wrow = tid >> 4, wmbr = tid & 15;
+    const float4 rv = rot_row(a.rot, col);
     float M[4], Ls[4], acc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -868,8 +886,8 @@ __global__ __launch_bounds__(128) void attn_mfma_merge_kernel(CArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        store_out(a.out, a.rot, b, a.Hkv, a.n_rep, a.L, a.G, kvh, col, r0 + 4 * h + i, acc[i],
-                  Ls[i]);
+        store_out(a.out, a.rot != nullptr, rv, b, a.Hkv, a.n_rep, a.L, a.G, kvh, col, r0 + 4 * h + i,
+                  acc[i], Ls[i]);
 }
 
 }  // namespace
