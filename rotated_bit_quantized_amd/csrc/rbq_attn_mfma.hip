@@ -462,58 +462,63 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
         *reinterpret_cast<f16x8*>(qa_lds + ((2 * g + h2) * 64 + lane) * 16) = qa;
     }
-    // query operand of the bias MFMA for row r: slots of lane group 0 = the 4
-    // group sums (hi, then middle limb), lane group 1 = low limb, others zero
-    u32x4 qb_op;
+    // query operand of the bias MFMA: lane group j supplies k-slots 8j..8j+3
+    // (the other 4 are zero) against the 4 group biases of the key, which
+    // every lane group of the key operand repeats.  Group j holds limb j of
+    // the 4 group sums.  Rows 0-7 are query rows 0-7, rows 8-14 query rows
+    // 1-7 and row 15 is zero, so that accumulator registers 0 and 2 of lane
+    // half hl hold rows rb + hl and rb + 2 + hl, the rows the lane keeps its
+    // softmax state for.
+    u32x4 qb_op = {0u, 0u, 0u, 0u};
     {
-        float qsum[4];
+        const int rq = (n < 8) ? n : n - 7;
+        if (rq < kRows) {
+            float qsum[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) qsum[g] = qstat[r * 8 + g];
-        const int E = __float_as_int(qstat[r * 8 + 4]);
-        if constexpr (DT == RBQ_BF16) {
-            uint32_t hb[4], mb[4], lb[4];
+            for (int g = 0; g < 4; ++g) qsum[g] = qstat[rq * 8 + g];
+            const int E = __float_as_int(qstat[rq * 8 + 4]);
+            uint32_t x[4];
+            if constexpr (DT == RBQ_BF16) {
+                // exact three-limb bf16 split: hi, middle, low
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const uint32_t u = __float_as_uint(qsum[g]);
-                const float hi = __uint_as_float(u & 0xFFFF0000u);
-                const uint32_t u2 = __float_as_uint(qsum[g] - hi);
-                const float mid = __uint_as_float(u2 & 0xFFFF0000u);
-                hb[g] = u >> 16;
-                mb[g] = u2 >> 16;
-                lb[g] = f32_to_bf16_bits(qsum[g] - hi - mid);
+                for (int g = 0; g < 4; ++g) {
+                    const uint32_t u = __float_as_uint(qsum[g]);
+                    const float hi = __uint_as_float(u & 0xFFFF0000u);
+                    const uint32_t u2 = __float_as_uint(qsum[g] - hi);
+                    const float mid = __uint_as_float(u2 & 0xFFFF0000u);
+                    x[g] = (j == 0) ? u >> 16
+                         : (j == 1) ? u2 >> 16
+                         : (j == 2) ? f32_to_bf16_bits(qsum[g] - hi - mid) : 0u;
+                }
+            } else {
+                // fp16: sums scaled by 2^(E-6) (below 2^15 in magnitude), hi + lo
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float v = ldexpf(qsum[g], E - 6);
+                    const _Float16 hi = (_Float16)v;
+                    x[g] = (j == 0) ? (uint32_t)__builtin_bit_cast(uint16_t, hi)
+                         : (j == 1) ? (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v - (float)hi))
+                                    : 0u;
+                }
             }
-            if (j == 0) qb_op = (u32x4){hb[0] | hb[1] << 16, hb[2] | hb[3] << 16, mb[0] | mb[1] << 16,
-                                        mb[2] | mb[3] << 16};
-            else if (j == 1) qb_op = (u32x4){lb[0] | lb[1] << 16, lb[2] | lb[3] << 16, 0u, 0u};
-            else qb_op = (u32x4){0u, 0u, 0u, 0u};
-        } else {
-            // fp16: sums scaled by 2^(E-6) (below 2^15 in magnitude), hi + lo
-            uint32_t hb[4], lb[4];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const float x = ldexpf(qsum[g], E - 6);
-                const _Float16 hi = (_Float16)x;
-                hb[g] = __builtin_bit_cast(uint16_t, hi);
-                lb[g] = __builtin_bit_cast(uint16_t, (_Float16)(x - (float)hi));
-            }
-            if (j == 0) qb_op = (u32x4){hb[0] | hb[1] << 16, hb[2] | hb[3] << 16, lb[0] | lb[1] << 16,
-                                        lb[2] | lb[3] << 16};
-            else qb_op = (u32x4){0u, 0u, 0u, 0u};
+            qb_op = (u32x4){x[0] | x[1] << 16, x[2] | x[3] << 16, 0u, 0u};
         }
     }
-    // per accumulator row: power-of-two factors and causal visibility
-    float frow[4], grow[4];
-    int vis[4];
+    // the lane's two softmax rows rb + 2p + hl (p = 0, 1): power-of-two
+    // factors and causal visibility
+    const int hl = j >> 1;  // 0: lanes 0-31, 1: lanes 32-63
+    float frow[2], grow[2];
+    int vis[2];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int row = rb + c;
+    for (int p = 0; p < 2; ++p) {
+        const int row = rb + 2 * p + hl;
         const int Er = __float_as_int(qstat[row * 8 + 4]);
-        frow[c] = ldexpf(1.0f, 24 - Er);
-        grow[c] = (DT == RBQ_BF16) ? 1.0f : ldexpf(1.0f, 6 - Er);
+        frow[p] = ldexpf(1.0f, 24 - Er);
+        grow[p] = (DT == RBQ_BF16) ? 1.0f : ldexpf(1.0f, 6 - Er);
         const int R = r0 + row;
-        vis[c] = (R < a.G && a.causal) ? T - a.L + (R % a.L) + 1 : T;
+        vis[p] = (R < a.G && a.causal) ? T - a.L + (R % a.L) + 1 : T;
     }
-    const int vis_min = min(min(vis[0], vis[1]), min(vis[2], vis[3]));
+    const int vis_min = min(vis[0], vis[1]);
     lds_barrier();  // query operands complete; query rows no longer read
     // the 8 score operand sets, held in registers for the whole tile loop
     f16x8 qa_r[4][2];
@@ -538,8 +543,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int t = 0; t < 16; ++t) O[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
     f32x4 Ob = {0.f, 0.f, 0.f, 0.f};
-    float m_ref[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    float l_part[4] = {0.f, 0.f, 0.f, 0.f};
+    // softmax state of the lane's two rows: reference maximum (raw score,
+    // -inf until a key is seen), the partial row sum over the lane's keys, the
+    // rescale threshold relative to the reference (8; -inf before the first
+    // key) and, in bias-accumulator registers 0 and 2, -reference / grow (the
+    // reference taken as 0 before the first key), so that the scores come out
+    // already relative to the reference
+    float m_ref[2] = {-INFINITY, -INFINITY};
+    float l_part[2] = {0.f, 0.f};
+    float thr[2] = {-INFINITY, -INFINITY};
+    f32x4 cinit = {0.f, 0.f, 0.f, 0.f};
 
     for (int it = wave; it < n_tiles; it += kWaves) {
         const int t0 = t_begin + it * kTile;
@@ -573,8 +586,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             *reinterpret_cast<uint2*>(smem + b_off + off) = make_uint2(bb * 0x10001u, bb * 0x10001u);
         }
 
-        // ---- scores: acc[row][key n] per group; scale, hi+lo, bias ----
-        float sc[2][4];
+        // ---- scores: acc[row][key n] per group; scale, hi+lo, bias.  The hi
+        //      and lo rows of accumulator registers (2p, 2p + 1) are combined
+        //      by one lane-half swap: lanes 0-31 then hold row rb + 2p, lanes
+        //      32-63 row rb + 2p + 1, i.e. the lane's row p ----
+        float sc[2][2];  // [block][p], relative to the reference
         const bool full = (t0 + kTile <= t_end) && (t0 + kTile <= vis_min);
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
@@ -591,20 +607,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     acc[g] = mfma16(qa_r[g][h2], as_f16x8(kv), acc[g]);
                 }
             }
-            const u32x4 kbop = {cur.kbw[blk][0], cur.kbw[blk][1], cur.kbw[blk][0], cur.kbw[blk][1]};
+            const u32x4 kbop = {cur.kbw[blk][0], cur.kbw[blk][1], 0u, 0u};
             f32x4 cb;
-            if constexpr (DT == RBQ_BF16) cb = mfma16bf(qb_op, kbop, (f32x4){0.f, 0.f, 0.f, 0.f});
-            else cb = mfma16(as_f16x8(qb_op), as_f16x8(kbop), (f32x4){0.f, 0.f, 0.f, 0.f});
+            if constexpr (DT == RBQ_BF16) cb = mfma16bf(qb_op, kbop, cinit);
+            else cb = mfma16(as_f16x8(qb_op), as_f16x8(kbop), cinit);
             const float s0 = meta_f32<DT>(cur.ksw[blk][0], 0), s1 = meta_f32<DT>(cur.ksw[blk][0], 1);
             const float s2 = meta_f32<DT>(cur.ksw[blk][1], 0), s3 = meta_f32<DT>(cur.ksw[blk][1], 1);
+            float t4[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 float t = s0 * acc[0][c];
                 t = fmaf(s1, acc[1][c], t);
                 t = fmaf(s2, acc[2][c], t);
-                t = fmaf(s3, acc[3][c], t);
-                t = add_swap32(t);
-                sc[blk][c] = fmaf(t, frow[c], cb[c] * grow[c]);
+                t4[c] = fmaf(s3, acc[3][c], t);
+            }
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(
+                    __float_as_uint(t4[2 * p]), __float_as_uint(t4[2 * p + 1]), false, false);
+                const float tt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                const float bias = (DT == RBQ_BF16) ? cb[2 * p] : cb[2 * p] * grow[p];
+                sc[blk][p] = fmaf(tt, frow[p], bias);
             }
         }
         if (!full) {
@@ -612,59 +635,72 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
+                for (int p = 0; p < 2; ++p) {
                     const int key = kb0 + 16 * blk;
-                    if (!(key < t_end && key < vis[c])) sc[blk][c] = -INFINITY;
+                    if (!(key < t_end && key < vis[p])) sc[blk][p] = -INFINITY;
                 }
         }
 
-        // ---- online softmax per row (base 2), lazy rescale ----
-        float mx[4];
+        // ---- online softmax per row (base 2), lazy rescale: the reference
+        //      moves only when the tile maximum exceeds it by more than 2^8 ----
+        float mx[2];
         bool need_any = false;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            mx[c] = max16(fmaxf(sc[0][c], sc[1][c]));
-            need_any |= mx[c] > m_ref[c] + 8.0f;
+        for (int p = 0; p < 2; ++p) {
+            mx[p] = max16(fmaxf(sc[0][p], sc[1][p]));
+            need_any |= mx[p] > thr[p];
         }
         if (__any(need_any)) {
+            float al[2];
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const bool need = mx[p] > thr[p];
+                // new reference: this tile's maximum (raw = relative + old
+                // reference, the latter 0 before the first key)
+                const float mu = (m_ref[p] == -INFINITY) ? 0.f : m_ref[p];
+                const float m_new = need ? mx[p] + mu : m_ref[p];
+                al[p] = need ? __builtin_amdgcn_exp2f(m_ref[p] - m_new) : 1.0f;
+                const float shift = need ? mx[p] : 0.f;
+                sc[0][p] -= shift;
+                sc[1][p] -= shift;
+                l_part[p] *= al[p];
+                m_ref[p] = m_new;
+                if (need) thr[p] = 8.0f;
+                cinit[2 * p] = (m_new == -INFINITY) ? 0.f : -m_new / grow[p];
+            }
+            // accumulator register c holds row rb + (0, 2, 1, 3)[c] (the P
+            // operand's row order, below): rows rb + hl and rb + 2 + hl are
+            // this lane's, the others the partner half's (lane ^ 32)
+            const float pa0 = __shfl_xor(al[0], 32), pa1 = __shfl_xor(al[1], 32);
+            const float alc[4] = {hl ? pa0 : al[0], hl ? pa1 : al[1], hl ? al[0] : pa0,
+                                  hl ? al[1] : pa1};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const bool need = mx[c] > m_ref[c] + 8.0f;
-                const float m_new = need ? mx[c] : m_ref[c];
-                const float alpha = need ? __builtin_amdgcn_exp2f(m_ref[c] - m_new) : 1.0f;
 #pragma unroll
-                for (int t = 0; t < 16; ++t) O[t][c] *= alpha;
-                Ob[c] *= alpha;
-                l_part[c] *= alpha;
-                m_ref[c] = m_new;
+                for (int t = 0; t < 16; ++t) O[t][c] *= alc[c];
+                Ob[c] *= alc[c];
             }
         }
-        // p in fp16 hi + lo for rows rb..rb+3 and key n of each block
+        // p in fp16 hi + lo (exact: lo = p - hi) for the lane's two rows and
+        // key n of each block.  P slot (block, key, part, row quad) holds rows
+        // rb + 0, rb + 2, rb + 1, rb + 3 in that order: lanes 0-31 store the
+        // first two, lanes 32-63 the last two.
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-            uint32_t hi2[2], lo2[2];
-#pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-                float p2[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int c = 2 * c2 + u;
-                    const float mu = (m_ref[c] == -INFINITY) ? 0.f : m_ref[c];
-                    p2[u] = __builtin_amdgcn_exp2f(sc[blk][c] - mu);
-                    l_part[c] += p2[u];
-                }
-                const _Float16 h0 = (_Float16)p2[0], h1 = (_Float16)p2[1];
-                const _Float16 e0 = (_Float16)(p2[0] - (float)h0), e1 = (_Float16)(p2[1] - (float)h1);
-                hi2[c2] = __builtin_bit_cast(uint32_t, (f16x2){h0, h1});
-                lo2[c2] = __builtin_bit_cast(uint32_t, (f16x2){e0, e1});
-            }
-            // lanes l and l ^ 32 hold the same values and store them to the
-            // same slots (no divergent branch)
-            *reinterpret_cast<uint2*>(smem + p_slot(blk, n, 0, j & 1)) = make_uint2(hi2[0], hi2[1]);
-            *reinterpret_cast<uint2*>(smem + p_slot(blk, n, 1, j & 1)) = make_uint2(lo2[0], lo2[1]);
+            const float p0 = __builtin_amdgcn_exp2f(sc[blk][0]);
+            const float p1 = __builtin_amdgcn_exp2f(sc[blk][1]);
+            l_part[0] += p0;
+            l_part[1] += p1;
+            const _Float16 h0 = (_Float16)p0, h1 = (_Float16)p1;
+            const _Float16 e0 = (_Float16)(p0 - (float)h0), e1 = (_Float16)(p1 - (float)h1);
+            *reinterpret_cast<uint32_t*>(smem + p_slot(blk, n, 0, j & 1) + 4 * hl) =
+                __builtin_bit_cast(uint32_t, (f16x2){h0, h1});
+            *reinterpret_cast<uint32_t*>(smem + p_slot(blk, n, 1, j & 1) + 4 * hl) =
+                __builtin_bit_cast(uint32_t, (f16x2){e0, e1});
         }
-        // A operand of P.V: row n (hi rows 0-7, lo rows 8-15) x keys 4j + e of
-        // both blocks; lane 4e + q addresses (key 4j + e, part q >> 1, quad q & 1)
+        // A operand of P.V: row n (hi rows 0-7, lo rows 8-15; within each
+        // quad of rows the slot order rb + 0, 2, 1, 3) x keys 4j + e of both
+        // blocks; lane 4e + q addresses (key 4j + e, part q >> 1, quad q & 1)
         f16x8 pa;
         {
             const int e = n >> 2, q = n & 3;
@@ -713,7 +749,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     float* wrec = reinterpret_cast<float*>(tbuf) + wave * kWaveRecFloats;
     float* wob = wrec + kHeadDim * kRows;
     float* wml = wob + kGroups * kRows;
-    const int hl = j >> 1;  // 0: lanes 0-31, 1: lanes 32-63
     auto comb = [](float x, float y) -> float {
         const auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false,
                                                          false);
@@ -722,27 +757,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
         const int col = 64 * (n >> 2) + 4 * t + (n & 3);
-        const float ra = comb(O[t][0], O[t][1]);  // row rb + hl
-        const float rc = comb(O[t][2], O[t][3]);  // row rb + 2 + hl
+        const float ra = comb(O[t][0], O[t][2]);  // row rb + hl
+        const float rc = comb(O[t][1], O[t][3]);  // row rb + 2 + hl
         float* dst = wrec + col * kRows + 4 * ((j & 1) ^ ((col >> 3) & 1)) + hl;
         dst[0] = ra;
         dst[2] = rc;
     }
     {
-        const float ra = comb(Ob[0], Ob[1]);
-        const float rc = comb(Ob[2], Ob[3]);
+        const float ra = comb(Ob[0], Ob[2]);
+        const float rc = comb(Ob[1], Ob[3]);
         float* dst = wob + (n >> 2) * kRows + rb + hl;
         dst[0] = ra;
         dst[2] = rc;
     }
     {
-        float l_row[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) l_row[c] = sum16(l_part[c]);
-        if (n == 0 && j < 2) {
-            *reinterpret_cast<float4*>(wml + rb) = make_float4(m_ref[0], m_ref[1], m_ref[2], m_ref[3]);
-            *reinterpret_cast<float4*>(wml + kRows + rb) =
-                make_float4(l_row[0], l_row[1], l_row[2], l_row[3]);
+        const float l0 = sum16(l_part[0]), l1 = sum16(l_part[1]);
+        if (n == 0) {
+            wml[rb + hl] = m_ref[0];
+            wml[rb + 2 + hl] = m_ref[1];
+            wml[kRows + rb + hl] = l0;
+            wml[kRows + rb + 2 + hl] = l1;
         }
     }
     lds_barrier();
