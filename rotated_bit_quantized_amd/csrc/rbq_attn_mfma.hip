@@ -148,6 +148,13 @@ __device__ __forceinline__ u32x2 tr16(unsigned char* smem, uint32_t off) {
     return __builtin_bit_cast(u32x2, v);
 }
 
+// 4-byte LDS store at byte offset `off` of the shared buffer, through an
+// LDS-typed pointer: through a generic one the compiler cannot tell the store
+// from the direct-to-LDS tile transfers in flight and waits for them first.
+__device__ __forceinline__ void lds_st32(unsigned char* smem, uint32_t off, uint32_t v) {
+    *(__attribute__((address_space(3))) uint32_t*)((lds_u8*)smem + off) = v;
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
@@ -215,6 +222,19 @@ __device__ __forceinline__ float add_swap32(float x) {
     const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                     false);
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// (fp16(p0 - h0), fp16(p1 - h1)) for hi2 = (h0, h1) the fp16 roundings of
+// p0, p1: one mixed-precision FMA per half, fma(-h, 1, p) with h taken as
+// fp16 and p as fp32, rounded once to fp16 (p - h is exact in fp32, so this
+// equals rounding the fp32 difference).  `one` holds 1.0f.
+__device__ __forceinline__ uint32_t f16_residuals(uint32_t hi2, float p0, float p1, float one) {
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, -%1, %2, %3 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, -%1, %2, %4 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(r)
+        : "v"(hi2), "v"(one), "v"(p0), "v"(p1));
+    return r;
 }
 
 __device__ __forceinline__ uint32_t mul2(uint32_t a, uint32_t s) {
@@ -387,7 +407,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             h[k] = __builtin_bit_cast(uint16_t, (_Float16)(float)((e >> (3 * k)) & 7));
-        reinterpret_cast<uint2*>(smem)[e] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        lds_st32(smem, 8 * e, h[0] | (h[1] << 16));
+        lds_st32(smem, 8 * e + 4, h[2] | (h[3] << 16));
     }
 
     // ---- query row `wave` rotated and scaled by scale*log2(e) into LDS (the
@@ -462,10 +483,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
         *reinterpret_cast<f16x8*>(qa_lds + ((2 * g + h2) * 64 + lane) * 16) = qa;
     }
-    // query operand of the bias MFMA: lane group j supplies k-slots 8j..8j+3
-    // (the other 4 are zero) against the 4 group biases of the key, which
-    // every lane group of the key operand repeats.  Group j holds limb j of
-    // the 4 group sums.  Rows 0-7 are query rows 0-7, rows 8-14 query rows
+    // query operand of the bias MFMA: lane group j supplies k-slots
+    // 8j+4..8j+7 (slots 8j..8j+3 are zero) against the 4 group biases of the
+    // key, which every lane group of the key operand repeats (its slots
+    // 8j..8j+3 hold the key's 4 group scales, which meet the zeros: the
+    // operand is the tile's scale and bias words as they sit in registers).
+    // Group j holds limb j of the 4 group sums.  Rows 0-7 are query rows 0-7, rows 8-14 query rows
     // 1-7 and row 15 is zero, so that accumulator registers 0 and 2 of lane
     // half hl hold rows rb + hl and rb + 2 + hl, the rows the lane keeps its
     // softmax state for.
@@ -501,7 +524,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                                     : 0u;
                 }
             }
-            qb_op = (u32x4){x[0] | x[1] << 16, x[2] | x[3] << 16, 0u, 0u};
+            qb_op = (u32x4){0u, 0u, x[0] | x[1] << 16, x[2] | x[3] << 16};
         }
     }
     // the lane's two softmax rows rb + 2p + hl (p = 0, 1): power-of-two
@@ -538,6 +561,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     auto p_slot = [&](int blk, int key, int part, int quad) -> uint32_t {
         return p_off + ((((blk * 16 + key) * 2 + part) * 2 + quad) << 3);
     };
+    // this lane's P store: key n, its row quad, lanes 32-63 the upper 4 bytes
+    // (block 1: + 512, lo part: + 16)
+    const uint32_t p_wr = p_slot(0, n, 0, j & 1) + 4 * hl;
+    const float one = 1.0f;
 
     f32x4 O[16];
 #pragma unroll
@@ -565,25 +592,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         if (it + kWaves < n_tiles)
             dma_tile(wbuf, t0 + kWaves * kTile, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
 
-        // ---- value scales and biases of the lane's (key, group) -> staging ----
+        // ---- value scales and biases of the lane's (key, group) -> staging,
+        //      each fp16 value repeated 4 times (the 8 bytes a transposing
+        //      read takes one element of) ----
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-            uint32_t sh, st = 0u, bb;
+            const uint32_t off = (blk * 64 + lane) << 3;
+            uint32_t s2, b2;
             if constexpr (DT == RBQ_BF16) {
-                sh = __builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(cur.vsb[blk]));
-                bb = __builtin_bit_cast(uint16_t, (_Float16)bf16_bits_to_f32(cur.vbb[blk]));
+                const uint32_t x = __builtin_bit_cast(
+                    uint32_t, (f16x2){(_Float16)bf16_bits_to_f32(cur.vsb[blk]),
+                                      (_Float16)bf16_bits_to_f32(cur.vbb[blk])});
+                s2 = __builtin_amdgcn_perm(x, x, 0x01000100u);  // low half twice
+                b2 = __builtin_amdgcn_perm(x, x, 0x03020302u);  // high half twice
             } else {
                 // head: top 8 significant bits; tail: the other 3 (both exact)
-                sh = cur.vsb[blk] & 0xFFF8u;
-                st = __builtin_bit_cast(uint16_t, (_Float16)(f16_bits_to_f32(cur.vsb[blk]) -
-                                                             f16_bits_to_f32(sh)));
-                bb = cur.vbb[blk] & 0xFFFFu;
+                const uint32_t sh = cur.vsb[blk] & 0xFFF8u;
+                const uint32_t st = __builtin_bit_cast(
+                    uint16_t, (_Float16)(f16_bits_to_f32(cur.vsb[blk]) - f16_bits_to_f32(sh)));
+                s2 = sh * 0x10001u;
+                b2 = (cur.vbb[blk] & 0xFFFFu) * 0x10001u;
+                lds_st32(smem, t_off + off, st * 0x10001u);
+                lds_st32(smem, t_off + off + 4, st * 0x10001u);
             }
-            const uint32_t off = (blk * 64 + lane) << 3;
-            *reinterpret_cast<uint2*>(smem + s_off + off) = make_uint2(sh * 0x10001u, sh * 0x10001u);
-            if constexpr (DT == RBQ_F16)
-                *reinterpret_cast<uint2*>(smem + t_off + off) = make_uint2(st * 0x10001u, st * 0x10001u);
-            *reinterpret_cast<uint2*>(smem + b_off + off) = make_uint2(bb * 0x10001u, bb * 0x10001u);
+            lds_st32(smem, s_off + off, s2);
+            lds_st32(smem, s_off + off + 4, s2);
+            lds_st32(smem, b_off + off, b2);
+            lds_st32(smem, b_off + off + 4, b2);
         }
 
         // ---- scores: acc[row][key n] per group; scale, hi+lo, bias.  The hi
@@ -607,7 +642,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     acc[g] = mfma16(qa_r[g][h2], as_f16x8(kv), acc[g]);
                 }
             }
-            const u32x4 kbop = {cur.kbw[blk][0], cur.kbw[blk][1], 0u, 0u};
+            const u32x4 kbop = {cur.ksw[blk][0], cur.ksw[blk][1], cur.kbw[blk][0], cur.kbw[blk][1]};
             f32x4 cb;
             if constexpr (DT == RBQ_BF16) cb = mfma16bf(qb_op, kbop, cinit);
             else cb = mfma16(as_f16x8(qb_op), as_f16x8(kbop), cinit);
@@ -691,12 +726,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             const float p1 = __builtin_amdgcn_exp2f(sc[blk][1]);
             l_part[0] += p0;
             l_part[1] += p1;
-            const _Float16 h0 = (_Float16)p0, h1 = (_Float16)p1;
-            const _Float16 e0 = (_Float16)(p0 - (float)h0), e1 = (_Float16)(p1 - (float)h1);
-            *reinterpret_cast<uint32_t*>(smem + p_slot(blk, n, 0, j & 1) + 4 * hl) =
-                __builtin_bit_cast(uint32_t, (f16x2){h0, h1});
-            *reinterpret_cast<uint32_t*>(smem + p_slot(blk, n, 1, j & 1) + 4 * hl) =
-                __builtin_bit_cast(uint32_t, (f16x2){e0, e1});
+            const uint32_t hi2 = __builtin_bit_cast(uint32_t, (f16x2){(_Float16)p0, (_Float16)p1});
+            lds_st32(smem, p_wr + 512 * blk, hi2);
+            lds_st32(smem, p_wr + 512 * blk + 16, f16_residuals(hi2, p0, p1, one));
         }
         // A operand of P.V: row n (hi rows 0-7, lo rows 8-15; within each
         // quad of rows the slot order rb + 0, 2, 1, 3) x keys 4j + e of both
