@@ -217,6 +217,24 @@ def main() -> int:
     for c in caches:
         capi.rbq_kv_trim(c.desc, 1)
 
+    # Cache snapshot (the prefix copy of the six arrays, rows [0, T)): copies
+    # from the rotating replicas into two alternating snapshot buffer sets, so
+    # that neither side is served by the Infinity Cache; HIP events around
+    # back-to-back copies on the stream.
+    snaps = [base.snapshot(), base.snapshot()]
+    n_copy = 40
+    for i in range(4):
+        capi.rbq_kv_copy_prefix(caches[i % len(caches)].desc, snaps[i % 2].desc)
+    ev0.record(stream)
+    for i in range(n_copy):
+        capi.rbq_kv_copy_prefix(caches[i % len(caches)].desc, snaps[i % 2].desc)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    copy_us = ev0.elapsed_time(ev1) * 1e3 / n_copy
+    copy_bytes = 2 * w.B * w.Hkv * (w.T - 1) * 256  # read + write of the prefix
+    copy_gbs = copy_bytes / (copy_us * 1e-6) / 1e9
+    del snaps
+
     nbytes = algorithmic_bytes(w, w.T)
     ms_per_step = total * 1e3 / args.steps
     value = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
@@ -260,6 +278,17 @@ def main() -> int:
             "avg_launch_us": round(attn_avg_s * 1e6, 3),
         },
         "step": "HIP graph replay (append + attention)" if graphs else "eager launches",
+        "snapshot": {
+            "what": f"cache snapshot: prefix copy of the six arrays, {w.T - 1} rows x "
+                    f"{w.B * w.Hkv} (b, kv head) slabs (rbq_kv_copy_prefix, copy_prefix_kernel)",
+            "bound": "hbm",
+            "bytes_per_copy": copy_bytes,
+            "avg_us": round(copy_us, 3),
+            "achieved": round(copy_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(copy_gbs / HBM_PEAK_GBS, 4),
+        },
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)

@@ -151,6 +151,23 @@ int64_t rbq_kv_trim(rbq_kv_cache* c, int64_t n);
 int64_t rbq_kv_commit_verified(rbq_kv_cache* c, int64_t verified_len, int64_t accepted_len);
 
 /*
+ * rbq_kv_copy_prefix - copy rows [0, src->offset) of all six arrays of `src`
+ * into the same rows of `dst` and set dst->offset = src->offset; rows of dst
+ * at or past that offset are not touched.  This is the device copy behind
+ * cache snapshots (quant_kv.py, the snapshot interface: `state` getter and
+ * setter; mtp/kv_cache.py `_snapshot`, `_restore`,
+ * `commit_verified_snapshot`): a snapshot is a copy of the offset-prefix
+ * into buffers of its own, a restore copies a snapshot back.  `dst` must
+ * describe buffers of the same B, H_kv, head_dim, group, bits and dtype with
+ * dst->capacity >= src->offset; the two caches' arrays must not overlap.
+ * One kernel launch on `stream`.  Errors: RBQ_EINVAL (bad or mismatched
+ * descriptors, overlapping arrays), RBQ_ECAPACITY (dst too small, nothing is
+ * written), RBQ_EUNSUPPORTED, RBQ_EHIP.  src->offset == 0 only sets
+ * dst->offset = 0.
+ */
+int rbq_kv_copy_prefix(const rbq_kv_cache* src, rbq_kv_cache* dst, void* stream);
+
+/*
  * rbq_quant_attn_splits - the split count rbq_quant_attn_decode uses when
  * called with splits == 0 for this cache state and query shape (>= 1), or a
  * negative status for invalid arguments.

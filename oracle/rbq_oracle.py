@@ -8,8 +8,10 @@ Source of every definition: the page "mlx_streaming/core/cache/quant_kv.py"
 ``_quat_right_conj``, ``build_block_so4``, ``rotate_last``), "asymmetric
 quantized KV cache (K4/V3)" (``_packed_words``, ``AsymmetricQuantizedKVCache``:
 ``_init_quant``, ``update_and_fetch``, ``trim``) and "asymmetric quantized
-SDPA" (``asym_quantized_sdpa``); and the page "mlx_streaming/mtp/kv_cache.py",
-``commit_verified_prefix``.  The quantizer formula (scale = (max-min)/(2^bits-1),
+SDPA" (``asym_quantized_sdpa``) and its snapshot interface (``state``,
+``meta_state``); and the page "mlx_streaming/mtp/kv_cache.py",
+``commit_verified_prefix``, ``_snapshot``, ``_restore`` and
+``commit_verified_snapshot``.  The quantizer formula (scale = (max-min)/(2^bits-1),
 bias = min, code = clip(round-half-even((x-bias)/scale))) and the little-endian
 bit-stream packing are the ones the benchmark spec fixes; the pages call
 ``mx.quantize`` without defining it.
@@ -319,6 +321,59 @@ class QuantKVCache:
         vc = unpack(a["vw"][b, h, :o], self.v_bits, D)
         return (dequantize(kc, a["ks"][b, h, :o], a["kb"][b, h, :o]),
                 dequantize(vc, a["vs"][b, h, :o], a["vb"][b, h, :o]))
+
+
+def cache_state(cache: QuantKVCache):
+    """The snapshot interface's ``state`` getter (page quant_kv.py): the six
+    arrays cut to ``offset`` rows.  Returned as copies: the page's slices are
+    new arrays that the cache's later in-place writes cannot reach."""
+    if cache.arrays is None:
+        return None
+    return {name: a[:, :, :cache.offset].copy() for name, a in cache.arrays.items()}
+
+
+def set_cache_state(cache: QuantKVCache, state) -> None:
+    """The ``state`` setter: the buffers become the given arrays and
+    ``offset`` their row count (``None``: no buffers, offset 0)."""
+    if state is None:
+        cache.arrays, cache.offset = None, 0
+        return
+    cache.arrays = {name: a.copy() for name, a in state.items()}
+    cache.offset = cache.arrays["kw"].shape[2]
+
+
+def meta_state(cache: QuantKVCache, group: int = GROUP):
+    """``meta_state``: group size and bit widths as strings."""
+    return str(group), str(cache.k_bits), str(cache.v_bits)
+
+
+def snapshot(caches):
+    """``_snapshot`` (page mtp/kv_cache.py): per cache a copy of its state and
+    its meta state; a cache without buffers gives the empty marker (None)."""
+    return [(cache_state(c), meta_state(c)) for c in caches]
+
+
+def restore(caches, snaps) -> None:
+    """``_restore``: each cache receives a fresh copy of its snapshot's state
+    (the snapshot itself stays untouched), or loses its buffers for the empty
+    marker."""
+    for c, (st, meta) in zip(caches, snaps):
+        if meta != meta_state(c):
+            raise ValueError("snapshot of another cache configuration")
+        set_cache_state(c, st)
+
+
+def commit_verified_snapshot(caches, snapshots, accepted_len: int,
+                             verified_len=None) -> bool:
+    """``commit_verified_snapshot``: nothing to do when every verified token
+    was accepted; False for accepted_len outside [1, len(snapshots)];
+    otherwise restore the snapshot taken after accepted_len tokens."""
+    if verified_len is not None and accepted_len == verified_len:
+        return True
+    if accepted_len <= 0 or accepted_len > len(snapshots):
+        return False
+    restore(caches, snapshots[accepted_len - 1])
+    return True
 
 
 def commit_verified_prefix(cache: QuantKVCache, verified_len: int, accepted_len: int) -> int:

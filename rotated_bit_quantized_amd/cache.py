@@ -156,8 +156,103 @@ class RotatedQuantKVCache:
         capi.rbq_quant_attn_decode(self.desc, q, scale, causal, self.rot, out, splits, ws)
         return out
 
+    # -- snapshots (the page's snapshot interface) ------------------------------
+    @property
+    def meta_state(self) -> tuple:
+        """``meta_state``: group size and bit widths as strings."""
+        d = self.desc
+        return str(d.group_size), str(d.k_bits), str(d.v_bits)
+
+    @property
+    def state(self) -> Optional[dict]:
+        """``state``: views of the six arrays' rows [0, offset) (None without
+        buffers).  Views, not copies: :meth:`snapshot` makes the copy."""
+        return None if self.arrays is None else self.rows()
+
+    def snapshot(self) -> "CacheSnapshot":
+        """Copy of the offset-prefix of the six buffers into buffers of their
+        own (``_snapshot`` on the mtp/kv_cache.py page), by one device copy."""
+        if self.arrays is None or self.offset == 0:
+            return CacheSnapshot(None, None, self.meta_state)
+        arrays = self._alloc(self.offset)
+        desc = capi.rbq_kv_cache.from_buffer_copy(self.desc)
+        desc.offset = 0
+        self._bind(desc, arrays, self.offset)
+        capi.rbq_kv_copy_prefix(self.desc, desc)
+        return CacheSnapshot(arrays, desc, self.meta_state)
+
+    def restore(self, snap: "CacheSnapshot") -> None:
+        """``_restore``: the cache's rows [0, offset) and offset become the
+        snapshot's; the snapshot is left as it is.  The copy goes into the
+        cache's own buffers when they hold it (the page installs a fresh copy
+        of exactly ``offset`` rows; rows and offset are the same either way,
+        only the spare capacity differs), else into new buffers of exactly the
+        snapshot's rows."""
+        if snap.meta_state != self.meta_state:
+            raise ValueError("snapshot of another cache configuration")
+        if snap.desc is None:
+            self.arrays = None
+            self.desc.capacity = 0
+            self.desc.offset = 0
+            for name in capi_array_names():
+                setattr(self.desc, name, None)
+            return
+        if self.arrays is None or self.capacity < snap.offset:
+            new = self._alloc(snap.offset)
+            desc = capi.rbq_kv_cache.from_buffer_copy(self.desc)
+            self._bind(desc, new, snap.offset)
+            capi.rbq_kv_copy_prefix(snap.desc, desc)
+            self.arrays, self.desc = new, desc
+        else:
+            capi.rbq_kv_copy_prefix(snap.desc, self.desc)
+
     # -- inspection ------------------------------------------------------------
     def rows(self, upto: Optional[int] = None) -> dict:
         """Views of the six arrays' rows [0, upto or offset)."""
         n = self.offset if upto is None else upto
         return {k: a[:, :, :n] for k, a in self.arrays.items()}
+
+
+def capi_array_names() -> tuple:
+    """Names of the six buffer pointers in the cache descriptor."""
+    return ("k_words", "k_scales", "k_biases", "v_words", "v_scales", "v_biases")
+
+
+class CacheSnapshot:
+    """A copy of a cache's offset-prefix: six device buffers of exactly
+    ``offset`` rows with their descriptor, and the cache's meta state.
+    ``desc`` is None for the empty marker (a cache without rows)."""
+
+    def __init__(self, arrays: Optional[dict], desc, meta_state: tuple):
+        self.arrays = arrays
+        self.desc = desc
+        self.meta_state = meta_state
+
+    @property
+    def offset(self) -> int:
+        return 0 if self.desc is None else int(self.desc.offset)
+
+
+def snapshot_caches(caches) -> list:
+    """``_snapshot``: one snapshot per cache."""
+    return [c.snapshot() for c in caches]
+
+
+def restore_caches(caches, snaps) -> None:
+    """``_restore``: each cache back to its snapshot."""
+    for c, s in zip(caches, snaps):
+        c.restore(s)
+
+
+def commit_verified_snapshot(caches, snapshots, accepted_len: int,
+                             verified_len: Optional[int] = None) -> bool:
+    """``commit_verified_snapshot`` (page mtp/kv_cache.py): True without a
+    restore when every verified token was accepted; False for accepted_len
+    outside [1, len(snapshots)]; otherwise restore ``snapshots[accepted_len -
+    1]`` (the snapshots taken after each verified token) and return True."""
+    if verified_len is not None and accepted_len == verified_len:
+        return True
+    if accepted_len <= 0 or accepted_len > len(snapshots):
+        return False
+    restore_caches(caches, snapshots[accepted_len - 1])
+    return True

@@ -68,6 +68,7 @@ def _load():
         "rbq_rotation_build": (c_int32, [c_void_p, c_int32, c_void_p]),
         "rbq_kv_required_capacity": (c_int64, [c_int64, c_int64, c_int64]),
         "rbq_kv_grow": (c_int32, [P, P, c_void_p]),
+        "rbq_kv_copy_prefix": (c_int32, [P, P, c_void_p]),
         "rbq_kv_quant_append": (c_int32, [P, c_void_p, c_void_p, c_int64, c_void_p, c_void_p]),
         "rbq_kv_trim": (c_int64, [P, c_int64]),
         "rbq_kv_commit_verified": (c_int64, [P, c_int64, c_int64]),
@@ -145,6 +146,12 @@ def rbq_kv_commit_verified(desc: rbq_kv_cache, verified_len: int, accepted_len: 
 
 def rbq_kv_grow(src: rbq_kv_cache, dst: rbq_kv_cache) -> None:
     _check("rbq_kv_grow", _lib.rbq_kv_grow(ctypes.byref(src), ctypes.byref(dst), _stream()))
+
+
+def rbq_kv_copy_prefix(src: rbq_kv_cache, dst: rbq_kv_cache) -> None:
+    """Rows [0, src.offset) of the six arrays into dst; dst.offset = src.offset."""
+    _check("rbq_kv_copy_prefix",
+           _lib.rbq_kv_copy_prefix(ctypes.byref(src), ctypes.byref(dst), _stream()))
 
 
 def rbq_kv_quant_append(desc: rbq_kv_cache, k: torch.Tensor, v: torch.Tensor,

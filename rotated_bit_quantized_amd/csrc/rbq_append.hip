@@ -2,7 +2,8 @@
 // page): rotate each new K/V row by the SO(4) blocks, quantize it in groups
 // of 64 (K 4-bit, V 3-bit, per-group scale and bias in the input dtype),
 // bit-pack it as a little-endian bit stream and write it at row `offset`.
-// Also the growth copy of the cache buffers.
+// Also the growth copy of the cache buffers and the prefix copy behind cache
+// snapshots.
 //
 // Mapping: one wave64 per (b, kv head, token) row; lane l owns elements
 // [4l, 4l+4) = rotation block l, so a group of 64 is 16 lanes and the group
@@ -123,6 +124,60 @@ __global__ __launch_bounds__(256) void grow_copy_kernel(const uint32_t* __restri
     }
 }
 
+// Prefix copy of the six arrays (the snapshot / restore copy): for array a
+// and (b, kv head) slab, dst rows [0, n) <- src rows [0, n); rows at or past n
+// of dst are not touched.  One launch for all six arrays: the grid is the
+// concatenation, array by array, of slab-major runs of 8 KiB chunks of each
+// slab's prefix (n rows x wpr words, contiguous in both caches).  A chunk is
+// 2048 words, 8 per thread: two 16-byte non-temporal loads in flight per
+// thread and non-temporal stores (the copy streams through the caches) when
+// both slab bases are 16-byte aligned, 4-byte words otherwise.
+constexpr int kCopyChunkWords = 2048;
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+struct CopyArr {
+    const uint32_t* src;
+    uint32_t* dst;
+    int64_t src_stride, dst_stride;  // words between consecutive slabs
+    uint32_t chunks;                 // chunks per slab
+    uint32_t first_block;            // first workgroup of this array
+};
+struct CopyArgs {
+    CopyArr arr[6];  // K words, K scales, K biases, V words, V scales, V biases
+    int64_t n;       // rows to copy
+};
+
+__global__ __launch_bounds__(256) void copy_prefix_kernel(CopyArgs a) {
+    int ai = 0;
+#pragma unroll
+    for (int k = 1; k < 6; ++k)
+        if (blockIdx.x >= a.arr[k].first_block) ai = k;
+    const CopyArr& r = a.arr[ai];
+    const int wpr = (ai == 0) ? kKWords : (ai == 3) ? kVWords : kGroups / 2;  // words per row
+    const uint32_t local = blockIdx.x - r.first_block;
+    const uint32_t slab = local / r.chunks;
+    const uint32_t chunk = local - slab * r.chunks;
+    const int64_t words = a.n * wpr;
+    const uint32_t* src = r.src + slab * r.src_stride;
+    uint32_t* dst = r.dst + slab * r.dst_stride;
+    const int64_t w0 = (int64_t)chunk * kCopyChunkWords;
+    const int tid = threadIdx.x;
+    const bool vec = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
+    if (vec && w0 + kCopyChunkWords <= words) {
+        const u32x4v* s4 = reinterpret_cast<const u32x4v*>(src + w0);
+        u32x4v* d4 = reinterpret_cast<u32x4v*>(dst + w0);
+        const u32x4v v0 = __builtin_nontemporal_load(s4 + tid);
+        const u32x4v v1 = __builtin_nontemporal_load(s4 + 256 + tid);
+        __builtin_nontemporal_store(v0, d4 + tid);
+        __builtin_nontemporal_store(v1, d4 + 256 + tid);
+    } else {
+        for (int i = 0; i < kCopyChunkWords / 256; ++i) {
+            const int64_t w = w0 + i * 256 + tid;
+            if (w < words) dst[w] = src[w];
+        }
+    }
+}
+
 int launch_status(hipError_t e) {
     if (e != hipSuccess) {
         set_hip_error((int)e);
@@ -205,5 +260,51 @@ extern "C" int rbq_kv_grow(const rbq_kv_cache* src, rbq_kv_cache* dst, void* str
         if (st != RBQ_OK) return st;
     }
     dst->offset = src->offset;
+    return RBQ_OK;
+}
+
+extern "C" int rbq_kv_copy_prefix(const rbq_kv_cache* src, rbq_kv_cache* dst, void* stream) {
+    int st = check_cache(src);
+    if (st != RBQ_OK) return st;
+    st = check_cache(dst);
+    if (st != RBQ_OK) return st;
+    if (src->B != dst->B || src->H_kv != dst->H_kv || src->dtype != dst->dtype) return RBQ_EINVAL;
+    const int64_t n = src->offset;
+    if (n > dst->capacity) return RBQ_ECAPACITY;
+    if (n == 0) {
+        dst->offset = 0;
+        return RBQ_OK;
+    }
+    const int64_t bh = (int64_t)src->B * src->H_kv;
+    const void* from[6] = {src->k_words, src->k_scales, src->k_biases,
+                           src->v_words, src->v_scales, src->v_biases};
+    void* to[6] = {dst->k_words, dst->k_scales, dst->k_biases,
+                   dst->v_words, dst->v_scales, dst->v_biases};
+    const int wpr[6] = {kKWords, kGroups / 2, kGroups / 2, kVWords, kGroups / 2, kGroups / 2};
+    CopyArgs a;
+    a.n = n;
+    int64_t blocks = 0;
+    for (int i = 0; i < 6; ++i) {
+        // the two caches' arrays must not overlap
+        const char* s0 = (const char*)from[i];
+        const char* s1 = s0 + (size_t)bh * src->capacity * wpr[i] * 4;
+        const char* d0 = (const char*)to[i];
+        const char* d1 = d0 + (size_t)bh * dst->capacity * wpr[i] * 4;
+        if (s0 < d1 && d0 < s1) return RBQ_EINVAL;
+        a.arr[i].src = (const uint32_t*)from[i];
+        a.arr[i].dst = (uint32_t*)to[i];
+        a.arr[i].src_stride = src->capacity * wpr[i];
+        a.arr[i].dst_stride = dst->capacity * wpr[i];
+        const int64_t chunks = (n * wpr[i] + kCopyChunkWords - 1) / kCopyChunkWords;
+        if (blocks + chunks * bh > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
+        a.arr[i].chunks = (uint32_t)chunks;
+        a.arr[i].first_block = (uint32_t)blocks;
+        blocks += chunks * bh;
+    }
+    hipLaunchKernelGGL(copy_prefix_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       (hipStream_t)stream, a);
+    st = launch_status(hipGetLastError());
+    if (st != RBQ_OK) return st;
+    dst->offset = n;
     return RBQ_OK;
 }

@@ -217,13 +217,6 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// x[l] + x[l ^ 32]
-__device__ __forceinline__ float add_swap32(float x) {
-    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                    false);
-    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-
 // (fp16(p0 - h0), fp16(p1 - h1)) for hi2 = (h0, h1) the fp16 roundings of
 // p0, p1: one mixed-precision FMA per half, fma(-h, 1, p) with h taken as
 // fp16 and p as fp32, rounded once to fp16 (p - h is exact in fp32, so this

@@ -157,6 +157,19 @@ def test_device_entry_points_validate_before_any_device_work():
     # grow: mismatched descriptors
     g = _host_desc(B=2, H=2, cap=512, off=0, **ptrs)
     assert lib.rbq_kv_grow(by(d), by(g), None) == capi.RBQ_EINVAL
+    # prefix copy: mismatched descriptors, destination too small, overlap
+    assert lib.rbq_kv_copy_prefix(by(d), by(g), None) == capi.RBQ_EINVAL
+    small = _host_desc(B=1, H=2, cap=99, off=0, k_words=0x9000000, k_scales=0xA000000,
+                       k_biases=0xB000000, v_words=0xC000000, v_scales=0xD000000,
+                       v_biases=0xE000000)
+    assert lib.rbq_kv_copy_prefix(by(d), by(small), None) == capi.RBQ_ECAPACITY
+    assert small.offset == 0
+    same = _host_desc(B=1, H=2, cap=256, off=0, **ptrs)
+    assert lib.rbq_kv_copy_prefix(by(d), by(same), None) == capi.RBQ_EINVAL
+    empty = _host_desc(B=1, H=2, cap=256, off=0, **ptrs)
+    tgt = _host_desc(B=1, H=2, cap=0, off=0)
+    tgt.offset = 0
+    assert lib.rbq_kv_copy_prefix(by(empty), by(tgt), None) == capi.RBQ_OK and tgt.offset == 0
 
 
 def test_status_strings():

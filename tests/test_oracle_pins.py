@@ -362,6 +362,92 @@ def test_append_rows_independent_and_growth_keeps_rows():
         np.testing.assert_array_equal(a.arrays[name][:, :, :300], b.arrays[name][:, :, :300])
 
 
+# ------------------------------------------------- snapshot / restore --
+
+def _tokens(seed, B, H, n):
+    k = W.random_rows([seed, 1], (B, H, n, 256), "bf16").float().numpy()
+    v = W.random_rows([seed, 2], (B, H, n, 256), "bf16").float().numpy()
+    return k, v
+
+
+def _fresh(k, v, blocks):
+    c = O.QuantKVCache()
+    c.append(k, v, blocks)
+    return c
+
+
+def _same_rows(a, b):
+    assert a.offset == b.offset
+    for name in a.arrays:
+        np.testing.assert_array_equal(a.arrays[name][:, :, :a.offset],
+                                      b.arrays[name][:, :, :b.offset])
+
+
+def test_restore_gives_back_the_prefix_of_a_cache_that_never_went_further():
+    # A snapshot after t tokens, more tokens, restore: the rows and offset are
+    # those of a cache filled with the first t tokens only; appending after the
+    # restore equals appending to that cache; the snapshot itself is not
+    # changed by what the cache does afterwards.
+    blocks = seed0_blocks()
+    k, v = _tokens(31, 2, 2, 310)
+    t = 300
+    c = _fresh(k[:, :, :t], v[:, :, :t], blocks)
+    snaps = O.snapshot([c])
+    c.append(k[:, :, t:], v[:, :, t:], blocks)
+    assert c.offset == 310
+    c.trim(20)
+    kx, vx = _tokens(32, 2, 2, 6)
+    c.append(kx, vx, blocks)  # rewrites rows 290-295, which the snapshot covers
+    O.restore([c], snaps)
+    ref = _fresh(k[:, :, :t], v[:, :, :t], blocks)
+    _same_rows(c, ref)
+    # the page's state setter leaves exactly `offset` rows of buffer, so the
+    # next append grows from there: 300 + one 256-row step
+    assert c.capacity == 300
+    c.append(kx[:, :, :5], vx[:, :, :5], blocks)
+    assert c.capacity == 556
+    ref.append(kx[:, :, :5], vx[:, :, :5], blocks)
+    _same_rows(c, ref)
+    # restoring twice from one snapshot gives the same state (the restore
+    # installs a copy, as the page's _restore does)
+    O.restore([c], snaps)
+    O.restore([c], snaps)
+    _same_rows(c, _fresh(k[:, :, :t], v[:, :, :t], blocks))
+
+
+def test_snapshot_of_empty_cache_and_meta_state():
+    c = O.QuantKVCache()
+    snaps = O.snapshot([c])
+    assert snaps == [(None, ("64", "4", "3"))]
+    k, v = _tokens(33, 1, 1, 10)
+    c.append(k, v, None)
+    O.restore([c], snaps)
+    assert c.arrays is None and c.offset == 0 and c.capacity == 0
+    other = O.QuantKVCache(k_bits=8)
+    with pytest.raises(ValueError):
+        O.restore([other], snaps)
+
+
+def test_commit_verified_snapshot_cases():
+    # Page mtp/kv_cache.py: all accepted -> True, nothing restored;
+    # accepted_len outside [1, len(snapshots)] -> False, nothing restored;
+    # otherwise the snapshot taken after accepted_len verified tokens.
+    blocks = seed0_blocks()
+    k, v = _tokens(34, 1, 2, 40)
+    c = _fresh(k[:, :, :37], v[:, :, :37], blocks)
+    snapshots = []
+    for i in range(3):
+        c.append(k[:, :, 37 + i:38 + i], v[:, :, 37 + i:38 + i], blocks)
+        snapshots.append(O.snapshot([c]))
+    assert c.offset == 40
+    assert O.commit_verified_snapshot([c], snapshots, 3, verified_len=3) is True
+    assert c.offset == 40
+    assert O.commit_verified_snapshot([c], snapshots, 0) is False and c.offset == 40
+    assert O.commit_verified_snapshot([c], snapshots, 4) is False and c.offset == 40
+    assert O.commit_verified_snapshot([c], snapshots, 2, verified_len=3) is True
+    _same_rows(c, _fresh(k[:, :, :39], v[:, :, :39], blocks))
+
+
 # -------------------------------------------------------------- attention --
 
 def _small_cache(seed, B, Hkv, T, dtype="bf16", blocks=None):
