@@ -168,6 +168,20 @@ int64_t rbq_kv_commit_verified(rbq_kv_cache* c, int64_t verified_len, int64_t ac
 int rbq_kv_copy_prefix(const rbq_kv_cache* src, rbq_kv_cache* dst, void* stream);
 
 /*
+ * rbq_kv_copy_batch - the prefix copy between caches of different batch
+ * sizes: destination batch entry b receives rows [0, src->offset) of source
+ * entry src_b0 + b * src_b_step (every kv head); dst->offset = src->offset.
+ * src_b_step = 0 with a batch-1 source repeats it P times (`tile_caches` on
+ * the mtp/kv_cache.py page: a batch-1 cache spread over the P draft paths of
+ * a batched verification); a batch-1 destination with src_b0 = row keeps
+ * one path (`commit_tree_row`, after the trim of the rejected suffix).
+ * Requirements and errors as rbq_kv_copy_prefix, except that the batch sizes
+ * may differ; RBQ_EINVAL when a source entry falls outside [0, src->B).
+ */
+int rbq_kv_copy_batch(const rbq_kv_cache* src, int32_t src_b0, int32_t src_b_step,
+                      rbq_kv_cache* dst, void* stream);
+
+/*
  * rbq_quant_attn_splits - the split count rbq_quant_attn_decode uses when
  * called with splits == 0 for this cache state and query shape (>= 1), or a
  * negative status for invalid arguments.
@@ -212,6 +226,37 @@ size_t rbq_quant_attn_workspace_bytes(const rbq_kv_cache* c, int32_t H_q, int32_
 int rbq_quant_attn_decode(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L,
                           float scale, int32_t causal, const float* rot_blocks, float* out,
                           int32_t splits, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- attention mask element types (rbq_quant_attn_decode_mask) ---- */
+#define RBQ_MASK_NONE      0
+#define RBQ_MASK_BOOL      1  /* uint8: nonzero = the key is attended, 0 = skipped          */
+#define RBQ_MASK_ADD_F32   2  /* float32 added to the scaled scores before the softmax      */
+#define RBQ_MASK_ADD_DTYPE 3  /* the same in the cache dtype (fp16 / bf16)                 */
+
+/*
+ * rbq_quant_attn_decode_mask - rbq_quant_attn_decode with an array mask over
+ * (query row, key), as asym_quantized_sdpa on the quant_kv.py page takes one
+ * (a boolean mask keeps a score where true; an additive one is added to the
+ * scaled scores), for batched verification of several draft paths.
+ *   mask         device array or NULL (then mask_type must be RBQ_MASK_NONE
+ *                and the call equals rbq_quant_attn_decode).  Element
+ *                (b, q head h, query row i, key t) is at mask + b*mask_stride_b
+ *                + h*mask_stride_h + i*mask_stride_l + t, in elements of the
+ *                mask type; keys t in [0, offset) are read; a stride of 0
+ *                broadcasts.  Strides are >= 0 and the elements read must lie
+ *                in the first 2^31 - 256 bytes (else RBQ_EUNSUPPORTED).
+ *   causal       applies as well when nonzero (both must keep a key).
+ * A query row whose every key is skipped has no key to attend: its output is
+ * NaN (the page fills skipped scores with the dtype's minimum, so it would
+ * average all keys with equal weight; rows of a verification always see the
+ * cached prefix).  Errors: as rbq_quant_attn_decode, and RBQ_EINVAL for a bad
+ * mask type or negative stride.
+ */
+int rbq_quant_attn_decode_mask(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L,
+                               float scale, int32_t causal, const void* mask, int32_t mask_type,
+                               int64_t mask_stride_b, int64_t mask_stride_h,
+                               int64_t mask_stride_l, const float* rot_blocks, float* out,
+                               int32_t splits, void* ws, size_t ws_bytes, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* rbq_status_string(int status);

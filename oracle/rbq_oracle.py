@@ -10,8 +10,8 @@ quantized KV cache (K4/V3)" (``_packed_words``, ``AsymmetricQuantizedKVCache``:
 ``_init_quant``, ``update_and_fetch``, ``trim``) and "asymmetric quantized
 SDPA" (``asym_quantized_sdpa``) and its snapshot interface (``state``,
 ``meta_state``); and the page "mlx_streaming/mtp/kv_cache.py",
-``commit_verified_prefix``, ``_snapshot``, ``_restore`` and
-``commit_verified_snapshot``.  The quantizer formula (scale = (max-min)/(2^bits-1),
+``commit_verified_prefix``, ``_snapshot``, ``_restore``,
+``commit_verified_snapshot``, ``tile_caches`` and ``commit_tree_row``.  The quantizer formula (scale = (max-min)/(2^bits-1),
 bias = min, code = clip(round-half-even((x-bias)/scale))) and the little-endian
 bit-stream packing are the ones the benchmark spec fixes; the pages call
 ``mx.quantize`` without defining it.
@@ -388,16 +388,28 @@ def commit_verified_prefix(cache: QuantKVCache, verified_len: int, accepted_len:
 # ---------------------------------------------------------------- attention --
 
 def attention_row(q_row: np.ndarray, khat: np.ndarray, vhat: np.ndarray, n_keys: int,
-                  scale: float, blocks) -> np.ndarray:
+                  scale: float, blocks, mask_row=None) -> np.ndarray:
     """One query row of ``asym_quantized_sdpa`` followed by the inverse rotation.
 
     q_row: [D] input-dtype values (unrotated); khat/vhat: fp64 dequantised
     rows; keys [0, n_keys) are visible.  q' = rotate(q) (fp32), then in fp64:
     scores = (q' * scale) . khat_t, max-subtracted softmax, o = sum p_t vhat_t;
-    returns inverse_rotate(fp32(o)) (or fp32(o) when blocks is None)."""
+    returns inverse_rotate(fp32(o)) (or fp32(o) when blocks is None).
+
+    mask_row (the SDPA's array mask, one row over keys [0, n_keys)): boolean,
+    a false entry's score becomes the most negative finite value (the page's
+    ``finfo.min`` fill: such a key gets weight 0 unless every key of the row is
+    masked, when the softmax of equal scores weights all keys alike); or
+    floating point, added to the scaled scores."""
     qr = np.asarray(q_row, np.float32) if blocks is None else rotate(q_row, blocks)
     qs = qr.astype(np.float64) * float(scale)
     sc = khat[:n_keys] @ qs
+    if mask_row is not None:
+        mrow = np.asarray(mask_row)[:n_keys]
+        if mrow.dtype == np.bool_:
+            sc = np.where(mrow, sc, np.finfo(np.float64).min)
+        else:
+            sc = sc + mrow.astype(np.float64)
     m = sc.max()
     p = np.exp(sc - m)
     o = (p @ vhat[:n_keys]) / p.sum()
@@ -406,12 +418,13 @@ def attention_row(q_row: np.ndarray, khat: np.ndarray, vhat: np.ndarray, n_keys:
 
 
 def attention(q: np.ndarray, cache: QuantKVCache, scale: float, causal: bool, blocks,
-              rows=None) -> np.ndarray:
+              rows=None, mask=None) -> np.ndarray:
     """Fused decode/verify attention over the cache (``asym_quantized_sdpa``):
     q: [B, Hq, L, D]; q head h reads kv head h // (Hq/Hkv); with ``causal``,
-    row i of the L-block sees keys t <= offset - L + i.  Returns float32
-    [B, Hq, L, D] (only ``rows`` = iterable of (b, h, i) are filled if given,
-    the rest stay NaN)."""
+    row i of the L-block sees keys t <= offset - L + i; ``mask`` (optional,
+    broadcastable to [B, Hq, L, offset], boolean or additive) applies to the
+    keys as well.  Returns float32 [B, Hq, L, D] (only ``rows`` = iterable of
+    (b, h, i) are filled if given, the rest stay NaN)."""
     B, Hq, L, D = q.shape
     Hkv = cache.arrays["kw"].shape[1]
     if Hq % Hkv:
@@ -420,6 +433,10 @@ def attention(q: np.ndarray, cache: QuantKVCache, scale: float, causal: bool, bl
     T = cache.offset
     if L < 1 or L > T:
         raise ValueError("need 1 <= L <= offset")
+    if mask is not None:
+        mask = np.broadcast_to(np.asarray(mask), (B, Hq, L, np.asarray(mask).shape[-1]))
+        if mask.shape[-1] < T:
+            raise ValueError("the mask must cover keys [0, offset)")
     out = np.full((B, Hq, L, D), np.nan, dtype=np.float32)
     if rows is None:
         rows = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(L)]
@@ -430,5 +447,34 @@ def attention(q: np.ndarray, cache: QuantKVCache, scale: float, causal: bool, bl
             deq = {(b, kvh): cache.dequant_kv(b, kvh)}
         khat, vhat = deq[(b, kvh)]
         n_keys = T - L + i + 1 if causal else T
-        out[b, h, i] = attention_row(q[b, h, i], khat, vhat, n_keys, scale, blocks)
+        mrow = None if mask is None else mask[b, h, i]
+        out[b, h, i] = attention_row(q[b, h, i], khat, vhat, n_keys, scale, blocks, mrow)
     return out
+
+
+def tile_cache(cache: QuantKVCache, P: int) -> None:
+    """``tile_caches`` (page mtp/kv_cache.py) for one cache: its batch-1 state
+    repeated P times along the batch axis, through the state setter (so the
+    buffers hold exactly ``offset`` rows)."""
+    st = cache_state(cache)
+    if st is None:
+        return
+    if st["kw"].shape[0] != 1:
+        raise ValueError("tile_caches needs batch-1 caches")
+    set_cache_state(cache, {name: np.repeat(a, P, axis=0) for name, a in st.items()})
+
+
+def commit_tree_row(caches, verified_len: int, accepted_len: int, row: int) -> bool:
+    """``commit_tree_row`` for trimmable caches (page mtp/kv_cache.py): trim the
+    rejected suffix, then keep batch row ``row`` (the winning path) as a
+    batch-1 cache."""
+    rejected = verified_len - accepted_len
+    if rejected < 0:
+        raise ValueError("accepted_len cannot exceed verified_len")
+    for c in caches:
+        if rejected:
+            c.trim(rejected)
+        st = cache_state(c)
+        if st is not None:
+            set_cache_state(c, {name: a[row:row + 1] for name, a in st.items()})
+    return True

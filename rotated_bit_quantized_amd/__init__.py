@@ -16,6 +16,7 @@ from .capi import (  # noqa: F401
     RbqError,
     rbq_kv_cache,
     rbq_kv_commit_verified,
+    rbq_kv_copy_batch,
     rbq_kv_copy_prefix,
     rbq_kv_grow,
     rbq_kv_quant_append,
@@ -30,8 +31,10 @@ from .cache import (  # noqa: F401
     CacheSnapshot,
     RotatedQuantKVCache,
     build_block_so4,
+    commit_tree_row,
     commit_verified_snapshot,
     quaternion_draws,
     restore_caches,
     snapshot_caches,
+    tile_caches,
 )

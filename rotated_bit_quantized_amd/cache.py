@@ -87,12 +87,12 @@ class RotatedQuantKVCache:
             return 0
         return sum(a.numel() * a.element_size() for a in self.arrays.values())
 
-    def _alloc(self, capacity: int) -> dict:
+    def _alloc(self, capacity: int, B: Optional[int] = None) -> dict:
         d = self.desc
         kw = d.head_dim * d.k_bits // 32
         vw = d.head_dim * d.v_bits // 32
         ng = d.head_dim // d.group_size
-        shp = (d.B, d.H_kv, capacity)
+        shp = (d.B if B is None else B, d.H_kv, capacity)
         return {
             "k_words": torch.empty(shp + (kw,), dtype=torch.int32, device=self.device),
             "k_scales": torch.empty(shp + (ng,), dtype=self.dtype, device=self.device),
@@ -145,16 +145,55 @@ class RotatedQuantKVCache:
         return self._ws
 
     def attend(self, q: torch.Tensor, scale: Optional[float] = None, causal: bool = True,
-               splits: int = 0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+               splits: int = 0, out: Optional[torch.Tensor] = None,
+               mask: Optional[torch.Tensor] = None) -> torch.Tensor:
         """Fused attention of ``q [B, H_q, L, head_dim]`` over rows [0, offset),
-        returning float32 ``[B, H_q, L, head_dim]`` rotated back."""
+        returning float32 ``[B, H_q, L, head_dim]`` rotated back.  ``mask``
+        (optional, as the page's SDPA takes an array mask): broadcastable to
+        ``[B, H_q, L, keys >= offset]``, boolean (keep where true) or additive
+        (float32 or the cache dtype); ``causal`` applies as well."""
         if scale is None:
             scale = self.desc.head_dim ** -0.5
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
         ws = self.workspace(q.shape[1], q.shape[2], splits)
-        capi.rbq_quant_attn_decode(self.desc, q, scale, causal, self.rot, out, splits, ws)
+        capi.rbq_quant_attn_decode(self.desc, q, scale, causal, self.rot, out, splits, ws, mask)
         return out
+
+    # -- batched verification of draft paths (mtp/kv_cache.py) -----------------
+    def _regather(self, B: int, src_b0: int, src_b_step: int) -> None:
+        """Replace the buffers by new ones of batch B, same capacity, whose
+        batch entry b holds rows [0, offset) of entry src_b0 + b*src_b_step."""
+        new = capi.rbq_kv_cache.from_buffer_copy(self.desc)
+        new.B = B
+        arrays = None
+        if self.arrays is not None:
+            arrays = self._alloc(self.capacity, B)
+            self._bind(new, arrays, self.capacity)
+            capi.rbq_kv_copy_batch(self.desc, src_b0, src_b_step, new)
+        self.arrays, self.desc = arrays, new
+
+    def tile(self, P: int) -> None:
+        """``tile_caches`` for this cache: a batch-1 cache becomes batch P,
+        every entry a copy of it (the page's state setter leaves buffers of
+        exactly offset rows; here they keep the current capacity)."""
+        if self.desc.B != 1:
+            raise ValueError("tile needs a batch-1 cache")
+        if P < 1:
+            raise ValueError("P must be >= 1")
+        self._regather(P, 0, 0)
+
+    def commit_row(self, verified_len: int, accepted_len: int, row: int) -> None:
+        """``commit_tree_row`` for this cache: trim the rejected suffix, then
+        keep batch entry ``row`` (the winning path) as a batch-1 cache."""
+        rejected = verified_len - accepted_len
+        if rejected < 0:
+            raise ValueError("accepted_len cannot exceed verified_len")
+        if not 0 <= row < self.desc.B:
+            raise ValueError(f"row {row} outside the batch of {self.desc.B}")
+        if rejected:
+            self.trim(rejected)
+        self._regather(1, row, 0)
 
     # -- snapshots (the page's snapshot interface) ------------------------------
     @property
@@ -255,4 +294,22 @@ def commit_verified_snapshot(caches, snapshots, accepted_len: int,
     if accepted_len <= 0 or accepted_len > len(snapshots):
         return False
     restore_caches(caches, snapshots[accepted_len - 1])
+    return True
+
+
+def tile_caches(caches, P: int) -> None:
+    """``tile_caches`` (page mtp/kv_cache.py): every batch-1 cache spread over
+    P batch entries for a batched verification of P draft paths."""
+    for c in caches:
+        c.tile(P)
+
+
+def commit_tree_row(caches, verified_len: int, accepted_len: int, row: int) -> bool:
+    """``commit_tree_row`` for trimmable caches (page mtp/kv_cache.py): after a
+    batched verification, trim the rejected suffix and keep path ``row`` as
+    the batch-1 cache; ValueError when accepted_len > verified_len."""
+    if verified_len - accepted_len < 0:
+        raise ValueError("accepted_len cannot exceed verified_len")
+    for c in caches:
+        c.commit_row(verified_len, accepted_len, row)
     return True

@@ -31,6 +31,11 @@ RBQ_EHIP = -6
 RBQ_F16 = 1
 RBQ_BF16 = 2
 
+RBQ_MASK_NONE = 0
+RBQ_MASK_BOOL = 1
+RBQ_MASK_ADD_F32 = 2
+RBQ_MASK_ADD_DTYPE = 3
+
 DTYPE_CODES = {torch.float16: RBQ_F16, torch.bfloat16: RBQ_BF16}
 
 
@@ -69,6 +74,7 @@ def _load():
         "rbq_kv_required_capacity": (c_int64, [c_int64, c_int64, c_int64]),
         "rbq_kv_grow": (c_int32, [P, P, c_void_p]),
         "rbq_kv_copy_prefix": (c_int32, [P, P, c_void_p]),
+        "rbq_kv_copy_batch": (c_int32, [P, c_int32, c_int32, P, c_void_p]),
         "rbq_kv_quant_append": (c_int32, [P, c_void_p, c_void_p, c_int64, c_void_p, c_void_p]),
         "rbq_kv_trim": (c_int64, [P, c_int64]),
         "rbq_kv_commit_verified": (c_int64, [P, c_int64, c_int64]),
@@ -77,6 +83,10 @@ def _load():
         "rbq_quant_attn_decode": (c_int32, [P, c_void_p, c_int32, c_int32, c_float, c_int32,
                                             c_void_p, c_void_p, c_int32, c_void_p, c_size_t,
                                             c_void_p]),
+        "rbq_quant_attn_decode_mask": (c_int32, [P, c_void_p, c_int32, c_int32, c_float, c_int32,
+                                                 c_void_p, c_int32, c_int64, c_int64, c_int64,
+                                                 c_void_p, c_void_p, c_int32, c_void_p, c_size_t,
+                                                 c_void_p]),
         "rbq_status_string": (ctypes.c_char_p, [c_int32]),
         "rbq_last_hip_error": (c_int32, []),
     }
@@ -154,6 +164,14 @@ def rbq_kv_copy_prefix(src: rbq_kv_cache, dst: rbq_kv_cache) -> None:
            _lib.rbq_kv_copy_prefix(ctypes.byref(src), ctypes.byref(dst), _stream()))
 
 
+def rbq_kv_copy_batch(src: rbq_kv_cache, src_b0: int, src_b_step: int, dst: rbq_kv_cache) -> None:
+    """Destination batch entry b <- rows [0, src.offset) of source entry
+    src_b0 + b * src_b_step; dst.offset = src.offset."""
+    _check("rbq_kv_copy_batch", _lib.rbq_kv_copy_batch(ctypes.byref(src), int(src_b0),
+                                                       int(src_b_step), ctypes.byref(dst),
+                                                       _stream()))
+
+
 def rbq_kv_quant_append(desc: rbq_kv_cache, k: torch.Tensor, v: torch.Tensor,
                         rot_blocks) -> None:
     """k, v: device ``[B, H_kv, n, head_dim]`` in the cache dtype; rot_blocks:
@@ -178,12 +196,43 @@ def rbq_quant_attn_workspace_bytes(desc: rbq_kv_cache, H_q: int, L: int, splits:
     return int(_lib.rbq_quant_attn_workspace_bytes(ctypes.byref(desc), H_q, L, splits))
 
 
+def _mask_args(desc: rbq_kv_cache, mask, B: int, H_q: int, L: int):
+    """(pointer, type, stride_b, stride_h, stride_l) of an optional mask
+    tensor broadcastable to [B, H_q, L, keys]: bool/uint8 (nonzero = keep),
+    float32 or the cache dtype (added to the scaled scores)."""
+    if mask is None:
+        return None, RBQ_MASK_NONE, 0, 0, 0
+    if not mask.is_cuda:
+        raise ValueError("mask must be a device (HIP) tensor")
+    if mask.dim() == 2:
+        mask = mask[None, None]
+    if mask.dim() != 4:
+        raise ValueError("mask must be [L, keys] or [B|1, H_q|1, L, keys]")
+    m = mask.expand(B, H_q, L, mask.shape[-1])
+    if m.shape[-1] < desc.offset:
+        raise ValueError(f"mask covers {m.shape[-1]} keys, the cache holds {desc.offset}")
+    if m.stride(-1) != 1:
+        raise ValueError("the mask's key axis must be contiguous")
+    if mask.dtype in (torch.bool, torch.uint8):
+        mt = RBQ_MASK_BOOL
+    elif mask.dtype == torch.float32:
+        mt = RBQ_MASK_ADD_F32
+    elif mask.dtype == _TORCH_OF[desc.dtype]:
+        mt = RBQ_MASK_ADD_DTYPE
+    else:
+        raise ValueError(f"mask dtype {mask.dtype} is not supported")
+    return m.data_ptr(), mt, m.stride(0), m.stride(1), m.stride(2)
+
+
 def rbq_quant_attn_decode(desc: rbq_kv_cache, q: torch.Tensor, scale: float, causal: bool,
                           rot_blocks, out: torch.Tensor, splits: int = 0,
-                          ws: torch.Tensor = None) -> None:
+                          ws: torch.Tensor = None, mask: torch.Tensor = None) -> None:
     """q: device ``[B, H_q, L, head_dim]`` in the cache dtype; out: device
     float32 of the same shape (written); ws: device workspace of at least
-    ``rbq_quant_attn_workspace_bytes`` bytes (None when that is 0)."""
+    ``rbq_quant_attn_workspace_bytes`` bytes (None when that is 0); mask:
+    optional device tensor broadcastable to ``[B, H_q, L, keys]`` (keys >=
+    offset): bool/uint8 keeps where nonzero, float32 or the cache dtype is
+    added to the scaled scores (calls rbq_quant_attn_decode_mask)."""
     if q.dim() != 4 or q.shape[0] != desc.B or q.shape[3] != desc.head_dim:
         raise ValueError(f"q shape {tuple(q.shape)} does not match the cache")
     if tuple(out.shape) != tuple(q.shape):
@@ -194,10 +243,17 @@ def rbq_quant_attn_decode(desc: rbq_kv_cache, q: torch.Tensor, scale: float, cau
     wp, wn = None, 0
     if ws is not None:
         wp, wn = _dev_ptr(ws, None, "ws"), ws.numel() * ws.element_size()
-    _check("rbq_quant_attn_decode",
-           _lib.rbq_quant_attn_decode(ctypes.byref(desc), qp, q.shape[1], q.shape[2],
-                                      float(scale), 1 if causal else 0, rp, op, int(splits),
-                                      wp, wn, _stream()))
+    if mask is None:
+        _check("rbq_quant_attn_decode",
+               _lib.rbq_quant_attn_decode(ctypes.byref(desc), qp, q.shape[1], q.shape[2],
+                                          float(scale), 1 if causal else 0, rp, op, int(splits),
+                                          wp, wn, _stream()))
+        return
+    mp, mt, sb, sh, sl = _mask_args(desc, mask, q.shape[0], q.shape[1], q.shape[2])
+    _check("rbq_quant_attn_decode_mask",
+           _lib.rbq_quant_attn_decode_mask(ctypes.byref(desc), qp, q.shape[1], q.shape[2],
+                                           float(scale), 1 if causal else 0, mp, mt, sb, sh, sl,
+                                           rp, op, int(splits), wp, wn, _stream()))
 
 
 _TORCH_OF = {RBQ_F16: torch.float16, RBQ_BF16: torch.bfloat16}

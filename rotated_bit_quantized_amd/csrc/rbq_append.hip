@@ -124,8 +124,9 @@ __global__ __launch_bounds__(256) void grow_copy_kernel(const uint32_t* __restri
     }
 }
 
-// Prefix copy of the six arrays (the snapshot / restore copy): for array a
-// and (b, kv head) slab, dst rows [0, n) <- src rows [0, n); rows at or past n
+// Prefix copy of the six arrays (snapshots, restore, batch tiling and row
+// selection): for array a and destination slab (b, kv head), dst rows [0, n)
+// <- rows [0, n) of source slab (b0 + b * bstep, kv head); rows at or past n
 // of dst are not touched.  One launch for all six arrays: the grid is the
 // concatenation, array by array, of slab-major runs of 8 KiB chunks of each
 // slab's prefix (n rows x wpr words, contiguous in both caches).  A chunk is
@@ -145,6 +146,7 @@ struct CopyArr {
 struct CopyArgs {
     CopyArr arr[6];  // K words, K scales, K biases, V words, V scales, V biases
     int64_t n;       // rows to copy
+    int H, b0, bstep;  // kv heads; source batch entry of destination entry b: b0 + b * bstep
 };
 
 __global__ __launch_bounds__(256) void copy_prefix_kernel(CopyArgs a) {
@@ -158,7 +160,9 @@ __global__ __launch_bounds__(256) void copy_prefix_kernel(CopyArgs a) {
     const uint32_t slab = local / r.chunks;
     const uint32_t chunk = local - slab * r.chunks;
     const int64_t words = a.n * wpr;
-    const uint32_t* src = r.src + slab * r.src_stride;
+    const uint32_t bd = slab / (uint32_t)a.H;
+    const int64_t sslab = (int64_t)(a.b0 + (int)bd * a.bstep) * a.H + (slab - bd * (uint32_t)a.H);
+    const uint32_t* src = r.src + sslab * r.src_stride;
     uint32_t* dst = r.dst + slab * r.dst_stride;
     const int64_t w0 = (int64_t)chunk * kCopyChunkWords;
     const int tid = threadIdx.x;
@@ -263,19 +267,27 @@ extern "C" int rbq_kv_grow(const rbq_kv_cache* src, rbq_kv_cache* dst, void* str
     return RBQ_OK;
 }
 
-extern "C" int rbq_kv_copy_prefix(const rbq_kv_cache* src, rbq_kv_cache* dst, void* stream) {
+namespace rbq {
+namespace {
+
+// Shared body of the prefix copies: destination batch entry b receives
+// source entry b0 + b * bstep.
+int copy_batch(const rbq_kv_cache* src, int32_t b0, int32_t bstep, rbq_kv_cache* dst,
+               void* stream) {
     int st = check_cache(src);
     if (st != RBQ_OK) return st;
     st = check_cache(dst);
     if (st != RBQ_OK) return st;
-    if (src->B != dst->B || src->H_kv != dst->H_kv || src->dtype != dst->dtype) return RBQ_EINVAL;
+    if (src->H_kv != dst->H_kv || src->dtype != dst->dtype) return RBQ_EINVAL;
+    const int64_t last = (int64_t)b0 + (int64_t)(dst->B - 1) * bstep;
+    if (b0 < 0 || b0 >= src->B || last < 0 || last >= src->B) return RBQ_EINVAL;
     const int64_t n = src->offset;
     if (n > dst->capacity) return RBQ_ECAPACITY;
     if (n == 0) {
         dst->offset = 0;
         return RBQ_OK;
     }
-    const int64_t bh = (int64_t)src->B * src->H_kv;
+    const int64_t bh = (int64_t)dst->B * dst->H_kv;
     const void* from[6] = {src->k_words, src->k_scales, src->k_biases,
                            src->v_words, src->v_scales, src->v_biases};
     void* to[6] = {dst->k_words, dst->k_scales, dst->k_biases,
@@ -283,11 +295,14 @@ extern "C" int rbq_kv_copy_prefix(const rbq_kv_cache* src, rbq_kv_cache* dst, vo
     const int wpr[6] = {kKWords, kGroups / 2, kGroups / 2, kVWords, kGroups / 2, kGroups / 2};
     CopyArgs a;
     a.n = n;
+    a.H = dst->H_kv;
+    a.b0 = b0;
+    a.bstep = bstep;
     int64_t blocks = 0;
     for (int i = 0; i < 6; ++i) {
         // the two caches' arrays must not overlap
         const char* s0 = (const char*)from[i];
-        const char* s1 = s0 + (size_t)bh * src->capacity * wpr[i] * 4;
+        const char* s1 = s0 + (size_t)src->B * src->H_kv * src->capacity * wpr[i] * 4;
         const char* d0 = (const char*)to[i];
         const char* d1 = d0 + (size_t)bh * dst->capacity * wpr[i] * 4;
         if (s0 < d1 && d0 < s1) return RBQ_EINVAL;
@@ -307,4 +322,19 @@ extern "C" int rbq_kv_copy_prefix(const rbq_kv_cache* src, rbq_kv_cache* dst, vo
     if (st != RBQ_OK) return st;
     dst->offset = n;
     return RBQ_OK;
+}
+
+}  // namespace
+}  // namespace rbq
+
+extern "C" int rbq_kv_copy_prefix(const rbq_kv_cache* src, rbq_kv_cache* dst, void* stream) {
+    if (src == nullptr || dst == nullptr) return RBQ_EINVAL;
+    if (src->B != dst->B) return RBQ_EINVAL;
+    return copy_batch(src, 0, 1, dst, stream);
+}
+
+extern "C" int rbq_kv_copy_batch(const rbq_kv_cache* src, int32_t src_b0, int32_t src_b_step,
+                                 rbq_kv_cache* dst, void* stream) {
+    if (src == nullptr || dst == nullptr) return RBQ_EINVAL;
+    return copy_batch(src, src_b0, src_b_step, dst, stream);
 }

@@ -120,7 +120,18 @@ struct MArgs {
     int Hkv, n_rep, L, G, S, causal;
     int RB;        // blocks of 8 query rows per kv head
     float qscale;  // scale * log2(e)
+    // optional mask over (query row, key): element [b][q head][row i][key t]
+    // at mask + b*msb + h*msh + i*msl + t (elements; the key stride is 1)
+    const void* mask;
+    int64_t msb, msh, msl;
+    uint32_t mask_bytes;  // extent read through a range-checked buffer resource
 };
+
+// Mask element types (the template argument MK of the attention kernel).
+constexpr int kMaskNone = 0;
+constexpr int kMaskBool = 1;     // uint8: nonzero = the key is attended
+constexpr int kMaskAddF32 = 2;   // fp32 added to the scaled scores
+constexpr int kMaskAddElem = 3;  // the same in the cache dtype (fp16 / bf16)
 
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
@@ -337,7 +348,7 @@ __device__ __forceinline__ void pv_tile(unsigned char* smem, const uint32_t wv0[
     }
 }
 
-template <int DT>
+template <int DT, int MK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(MArgs a) {
     __shared__ __align__(16) unsigned char smem[kSmemBytes];
     __shared__ __align__(16) unsigned char tbuf[kTbufBytes];
@@ -559,6 +570,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint32_t p_wr = p_slot(0, n, 0, j & 1) + 4 * hl;
     const float one = 1.0f;
 
+    // mask: byte offsets of the lane's two rows (out of range past G: such
+    // reads return zero) and the values for its keys n, 16 + n of a tile,
+    // loaded one tile ahead
+    constexpr int kMaskElem = (MK == kMaskBool) ? 1 : (MK == kMaskAddF32) ? 4 : 2;
+    __amdgpu_buffer_rsrc_t mask_r;
+    uint32_t mrow[2] = {0u, 0u};
+    uint32_t mk[2][2] = {{0u, 0u}, {0u, 0u}};
+    auto load_mask = [&](int tk, uint32_t (&m)[2][2]) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const uint32_t off = mrow[p] + (uint32_t)(tk + n + 16 * blk) * kMaskElem;
+                if constexpr (MK == kMaskBool)
+                    m[blk][p] = __builtin_amdgcn_raw_buffer_load_b8(mask_r, off, 0, 0);
+                else if constexpr (MK == kMaskAddF32)
+                    m[blk][p] = __builtin_amdgcn_raw_buffer_load_b32(mask_r, off, 0, 0);
+                else
+                    m[blk][p] = __builtin_amdgcn_raw_buffer_load_b16(mask_r, off, 0, 0);
+            }
+    };
+    if constexpr (MK != kMaskNone) {
+        mask_r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.mask), (short)0,
+                                                   (int)a.mask_bytes, 0x00020000);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int R = r0 + rb + 2 * p + hl;
+            mrow[p] = 0x80000000u;
+            if (R < a.G) {
+                const int h = kvh * a.n_rep + R / a.L;
+                mrow[p] = (uint32_t)(((int64_t)b * a.msb + (int64_t)h * a.msh +
+                                      (int64_t)(R % a.L) * a.msl) * kMaskElem);
+            }
+        }
+        if (wave < n_tiles) load_mask(t_begin + wave * kTile, mk);
+    }
+
     f32x4 O[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) O[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -584,6 +632,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         if (it + kWaves < n_tiles)
             dma_tile(wbuf, t0 + kWaves * kTile, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
+        uint32_t mk_next[2][2] = {{0u, 0u}, {0u, 0u}};
+        if constexpr (MK != kMaskNone)
+            if (it + kWaves < n_tiles) load_mask(t0 + kWaves * kTile, mk_next);
 
         // ---- value scales and biases of the lane's (key, group) -> staging,
         //      each fp16 value repeated 4 times (the 8 bytes a transposing
@@ -658,6 +709,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 sc[blk][p] = fmaf(tt, frow[p], bias);
             }
         }
+        // the mask: a false boolean skips the key, an additive value (natural
+        // log units, as the scaled scores) is added in base 2
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                if constexpr (MK == kMaskBool) {
+                    if (mk[blk][p] == 0u) sc[blk][p] = -INFINITY;
+                } else if constexpr (MK == kMaskAddF32) {
+                    sc[blk][p] = fmaf(__uint_as_float(mk[blk][p]), kLog2e, sc[blk][p]);
+                } else if constexpr (MK == kMaskAddElem) {
+                    sc[blk][p] = fmaf(elem_to_f32<DT>(mk[blk][p]), kLog2e, sc[blk][p]);
+                }
+            }
         if (!full) {
             const int kb0 = t0 + n;
 #pragma unroll
@@ -764,6 +829,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         pv_tile<DT, 13>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[13]);
         pv_tile<DT, 14>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[14]);
         pv_tile<DT, 15>(smem, cur.wv[0], cur.wv[1], sc2, st2, pa, O[15]);
+        if constexpr (MK != kMaskNone) {
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) mk[blk][p] = mk_next[blk][p];
+        }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // no transfer into the buffer in flight
 
@@ -982,8 +1053,8 @@ int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Mfm
 }
 
 int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, float scale,
-                int32_t causal, const float* rot_blocks, float* out, const MfmaPlan& p, void* ws,
-                void* stream) {
+                int32_t causal, const AttnMask& mk, const float* rot_blocks, float* out,
+                const MfmaPlan& p, void* ws, void* stream) {
     hipStream_t s = (hipStream_t)stream;
     MArgs a;
     a.q = (const uint16_t*)q;
@@ -1007,12 +1078,26 @@ int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
     a.RB = p.RB;
     a.causal = causal ? 1 : 0;
     a.qscale = scale * kLog2e;
+    a.mask = mk.ptr;
+    a.msb = mk.sb;
+    a.msh = mk.sh;
+    a.msl = mk.sl;
+    a.mask_bytes = mk.bytes;
     const int64_t units = (int64_t)c->B * c->H_kv * p.RB;
     const dim3 grid((unsigned)(units * p.S)), block(kThreads);
-    if (c->dtype == RBQ_BF16)
-        hipLaunchKernelGGL(attn_mfma_kernel<RBQ_BF16>, grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL(attn_mfma_kernel<RBQ_F16>, grid, block, 0, s, a);
+    auto launch = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, s, a); };
+    const int mt = mk.ptr == nullptr ? kMaskNone : mk.type;
+    if (c->dtype == RBQ_BF16) {
+        if (mt == kMaskNone) launch(attn_mfma_kernel<RBQ_BF16, kMaskNone>);
+        else if (mt == kMaskBool) launch(attn_mfma_kernel<RBQ_BF16, kMaskBool>);
+        else if (mt == kMaskAddF32) launch(attn_mfma_kernel<RBQ_BF16, kMaskAddF32>);
+        else launch(attn_mfma_kernel<RBQ_BF16, kMaskAddElem>);
+    } else {
+        if (mt == kMaskNone) launch(attn_mfma_kernel<RBQ_F16, kMaskNone>);
+        else if (mt == kMaskBool) launch(attn_mfma_kernel<RBQ_F16, kMaskBool>);
+        else if (mt == kMaskAddF32) launch(attn_mfma_kernel<RBQ_F16, kMaskAddF32>);
+        else launch(attn_mfma_kernel<RBQ_F16, kMaskAddElem>);
+    }
     if (p.S > 1) {
         CArgs m;
         m.rec = a.rec;
@@ -1046,6 +1131,33 @@ int check_attn(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits) {
     return RBQ_OK;
 }
 
+// Mask arguments: type, non-negative strides, and the byte extent of the
+// elements the call can read (the last row's keys [0, offset)), which must
+// fit the kernel's 31-bit buffer offsets.
+int check_mask(const rbq_kv_cache* c, int32_t H_q, int32_t L, const void* mask, int32_t type,
+               int64_t sb, int64_t sh, int64_t sl, AttnMask* m) {
+    m->ptr = mask;
+    m->type = RBQ_MASK_NONE;
+    m->sb = m->sh = m->sl = 0;
+    m->bytes = 0;
+    if (mask == nullptr) return type == RBQ_MASK_NONE ? RBQ_OK : RBQ_EINVAL;
+    if (type != RBQ_MASK_BOOL && type != RBQ_MASK_ADD_F32 && type != RBQ_MASK_ADD_DTYPE)
+        return RBQ_EINVAL;
+    if (sb < 0 || sh < 0 || sl < 0) return RBQ_EINVAL;
+    const int64_t esize = (type == RBQ_MASK_BOOL) ? 1 : (type == RBQ_MASK_ADD_F32) ? 4 : 2;
+    const int64_t last = (int64_t)(c->B - 1) * sb + (int64_t)(H_q - 1) * sh + (int64_t)(L - 1) * sl +
+                         c->offset;
+    if (sb > (int64_t)1 << 40 || sh > (int64_t)1 << 40 || sl > (int64_t)1 << 40 ||
+        last * esize > 0x7FFFFFFF - 64 * 4)
+        return RBQ_EUNSUPPORTED;
+    m->type = type;
+    m->sb = sb;
+    m->sh = sh;
+    m->sl = sl;
+    m->bytes = (uint32_t)(last * esize);
+    return RBQ_OK;
+}
+
 }  // namespace
 
 }  // namespace rbq
@@ -1067,16 +1179,29 @@ extern "C" size_t rbq_quant_attn_workspace_bytes(const rbq_kv_cache* c, int32_t 
     return mfma_plan(c, H_q, L, splits, &mp) == RBQ_OK ? mp.ws_bytes : 0;
 }
 
-extern "C" int rbq_quant_attn_decode(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L,
-                                     float scale, int32_t causal, const float* rot_blocks,
-                                     float* out, int32_t splits, void* ws, size_t ws_bytes,
-                                     void* stream) {
+extern "C" int rbq_quant_attn_decode_mask(const rbq_kv_cache* c, const void* q, int32_t H_q,
+                                          int32_t L, float scale, int32_t causal, const void* mask,
+                                          int32_t mask_type, int64_t mask_stride_b,
+                                          int64_t mask_stride_h, int64_t mask_stride_l,
+                                          const float* rot_blocks, float* out, int32_t splits,
+                                          void* ws, size_t ws_bytes, void* stream) {
     int st = check_attn(c, H_q, L, splits);
     if (st != RBQ_OK) return st;
     if (q == nullptr || out == nullptr) return RBQ_EINVAL;
+    AttnMask mk;
+    st = check_mask(c, H_q, L, mask, mask_type, mask_stride_b, mask_stride_h, mask_stride_l, &mk);
+    if (st != RBQ_OK) return st;
     MfmaPlan mp;
     st = mfma_plan(c, H_q, L, splits, &mp);
     if (st != RBQ_OK) return st;
     if (mp.ws_bytes > 0 && (ws == nullptr || ws_bytes < mp.ws_bytes)) return RBQ_EWORKSPACE;
-    return mfma_launch(c, q, H_q, L, scale, causal, rot_blocks, out, mp, ws, stream);
+    return mfma_launch(c, q, H_q, L, scale, causal, mk, rot_blocks, out, mp, ws, stream);
+}
+
+extern "C" int rbq_quant_attn_decode(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L,
+                                     float scale, int32_t causal, const float* rot_blocks,
+                                     float* out, int32_t splits, void* ws, size_t ws_bytes,
+                                     void* stream) {
+    return rbq_quant_attn_decode_mask(c, q, H_q, L, scale, causal, nullptr, RBQ_MASK_NONE, 0, 0, 0,
+                                      rot_blocks, out, splits, ws, ws_bytes, stream);
 }

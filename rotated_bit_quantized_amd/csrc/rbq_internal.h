@@ -27,6 +27,15 @@ int check_cache(const rbq_kv_cache* c);
 
 // Launch plan of the matrix-core attention path: key splits, their length,
 // blocks of 8 query rows, and the workspace for the split records.
+// Optional attention mask (rbq_quant_attn_decode_mask): element strides for
+// batch, q head and query row; `bytes` = extent the kernel may read.
+struct AttnMask {
+    const void* ptr;
+    int type;  // RBQ_MASK_*
+    int64_t sb, sh, sl;
+    uint32_t bytes;
+};
+
 struct MfmaPlan {
     int S;           // key splits
     int RB;          // blocks of 8 query rows per kv head
@@ -35,7 +44,7 @@ struct MfmaPlan {
 };
 int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, MfmaPlan* p);
 int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, float scale,
-                int32_t causal, const float* rot_blocks, float* out, const MfmaPlan& p, void* ws,
-                void* stream);
+                int32_t causal, const AttnMask& mk, const float* rot_blocks, float* out,
+                const MfmaPlan& p, void* ws, void* stream);
 
 }  // namespace rbq

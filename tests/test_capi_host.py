@@ -170,6 +170,21 @@ def test_device_entry_points_validate_before_any_device_work():
     tgt = _host_desc(B=1, H=2, cap=0, off=0)
     tgt.offset = 0
     assert lib.rbq_kv_copy_prefix(by(empty), by(tgt), None) == capi.RBQ_OK and tgt.offset == 0
+    # batch gather: source entries outside the source batch
+    two = _host_desc(B=2, H=2, cap=256, off=50, k_words=0x9000000, k_scales=0xA000000,
+                     k_biases=0xB000000, v_words=0xC000000, v_scales=0xD000000,
+                     v_biases=0xE000000)
+    assert lib.rbq_kv_copy_batch(by(d), 1, 0, by(two), None) == capi.RBQ_EINVAL
+    assert lib.rbq_kv_copy_batch(by(d), 0, 1, by(two), None) == capi.RBQ_EINVAL
+    assert lib.rbq_kv_copy_batch(by(d), -1, 1, by(two), None) == capi.RBQ_EINVAL
+    # masked attention: mask type / strides validated before any device work
+    mdec = lib.rbq_quant_attn_decode_mask
+    assert mdec(by(d), fake, 4, 1, 0.0625, 1, fake, 7, 0, 0, 0, None, fake, 0, None, 0,
+                None) == capi.RBQ_EINVAL
+    assert mdec(by(d), fake, 4, 1, 0.0625, 1, fake, capi.RBQ_MASK_BOOL, 0, -5, 0, None, fake, 0,
+                None, 0, None) == capi.RBQ_EINVAL
+    assert mdec(by(d), fake, 4, 1, 0.0625, 1, fake, capi.RBQ_MASK_ADD_F32, 0, 1 << 28, 0, None,
+                fake, 0, None, 0, None) == capi.RBQ_EUNSUPPORTED  # 3 heads x 2^28 x 4 B
 
 
 def test_status_strings():

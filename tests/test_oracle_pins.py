@@ -512,6 +512,81 @@ def test_single_key_and_identical_keys():
                                O.inverse_rotate(vh.mean(0).astype(np.float32), blocks), atol=1e-6)
 
 
+def test_array_masks():
+    # asym_quantized_sdpa's array masks: a boolean mask of the causal pattern
+    # is the causal mask (the page builds its "causal" string mask exactly so:
+    # q index >= k index); an all-true mask or an additive zero mask changes
+    # nothing; an additive constant shifts every score alike (softmax
+    # invariance); an additive -inf drops a key exactly as a false boolean.
+    blocks = seed0_blocks()
+    B, Hkv, Hq, T, L = 1, 2, 4, 70, 3
+    c = _small_cache(61, B, Hkv, T, blocks=blocks)
+    q = W.random_rows(62, (B, Hq, L, 256), "bf16").float().numpy()
+    base_c = O.attention(q, c, 1 / 16, True, blocks)
+    base_n = O.attention(q, c, 1 / 16, False, blocks)
+    qi = np.arange(T - L, T)[:, None]
+    causal = qi >= np.arange(T)[None]
+    np.testing.assert_array_equal(O.attention(q, c, 1 / 16, False, blocks, mask=causal), base_c)
+    np.testing.assert_array_equal(
+        O.attention(q, c, 1 / 16, False, blocks, mask=np.ones((L, T), bool)), base_n)
+    np.testing.assert_array_equal(
+        O.attention(q, c, 1 / 16, False, blocks, mask=np.zeros((1, 1, L, T))), base_n)
+    np.testing.assert_allclose(
+        O.attention(q, c, 1 / 16, False, blocks, mask=np.full((L, T), -7.5)), base_n, atol=1e-6)
+    rng = np.random.default_rng(63)
+    keep = rng.random((B, Hq, L, T)) < 0.6
+    keep[..., 0] = True
+    add = np.where(keep, 0.0, -np.inf)
+    np.testing.assert_array_equal(O.attention(q, c, 1 / 16, False, blocks, mask=keep),
+                                  O.attention(q, c, 1 / 16, False, blocks, mask=add))
+    # one kept key: the output is that key's value; no kept key: the page's
+    # minimum fill makes every score equal, so all keys weigh alike
+    one = np.zeros((L, T), bool)
+    one[:, 17] = True
+    _, vh = c.dequant_kv(0, 0)
+    out1 = O.attention(q, c, 1 / 16, False, blocks, mask=one)
+    np.testing.assert_allclose(out1[0, 0, 1], O.inverse_rotate(vh[17].astype(np.float32), blocks),
+                               atol=1e-6)
+    none = np.zeros((L, T), bool)
+    out0 = O.attention(q, c, 1 / 16, False, blocks, mask=none)
+    np.testing.assert_allclose(out0[0, 1, 2], O.inverse_rotate(vh.mean(0).astype(np.float32),
+                                                                 blocks), atol=1e-6)
+    # brute force on a masked row
+    kh1, vh1 = c.dequant_kv(0, 1)  # q head 3 reads kv head 1
+    kept = np.flatnonzero(keep[0, 3, 1])
+    ref = brute.attention_row(q[0, 3, 1], kh1[kept], vh1[kept], len(kept), 1 / 16, blocks)
+    got = O.attention(q, c, 1 / 16, False, blocks, mask=keep)[0, 3, 1]
+    np.testing.assert_allclose(got, ref, atol=2e-6)
+
+
+def test_tile_and_commit_tree_row():
+    # tile_caches: every batch row of the tiled cache is the batch-1 cache;
+    # commit_tree_row: trim the rejected suffix and keep the winning row, equal
+    # to a cache that saw only that path's accepted tokens.
+    blocks = seed0_blocks()
+    k, v = _tokens(64, 1, 2, 50)
+    c = _fresh(k, v, blocks)
+    O.tile_cache(c, 3)
+    assert c.offset == 50 and c.arrays["kw"].shape[0] == 3 and c.capacity == 50
+    ref = _fresh(k, v, blocks)
+    for b in range(3):
+        for name in c.arrays:
+            np.testing.assert_array_equal(c.arrays[name][b:b + 1], ref.arrays[name][:, :, :50])
+    paths = [_tokens(65 + p, 1, 2, 4) for p in range(3)]
+    kp = np.concatenate([pk for pk, _ in paths], 0)
+    vp = np.concatenate([pv for _, pv in paths], 0)
+    c.append(kp, vp, blocks)
+    assert O.commit_tree_row([c], 4, 2, 1) is True
+    win = _fresh(np.concatenate([k, paths[1][0][:, :, :2]], 2),
+                 np.concatenate([v, paths[1][1][:, :, :2]], 2), blocks)
+    _same_rows(c, win)
+    assert c.arrays["kw"].shape[0] == 1
+    with pytest.raises(ValueError):
+        O.commit_tree_row([c], 2, 3, 0)
+    with pytest.raises(ValueError):
+        O.tile_cache(_fresh(np.concatenate([k, k]), np.concatenate([v, v]), blocks), 2)
+
+
 def test_causal_row_equals_shorter_decode():
     # asym_quantized_sdpa's causal mask at the offset: row i of an L-block
     # sees keys t <= T - L + i, i.e. equals an L = 1 decode over T - L + i + 1 keys.
