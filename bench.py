@@ -113,6 +113,100 @@ def cpu_baseline(w, seconds: float = 12.0) -> dict:
     }
 
 
+def tree_verify(rbq, W, dev, rot, n_calls: int = 200) -> dict:
+    """Batched verification of P draft paths: a batch-1 cache of 10240 tokens
+    (the append_verify fill + append) tiled over P = 4 paths, 4 draft tokens
+    appended per path, then the fused attention of all paths' draft rows
+    (16 q heads / 2 kv heads) under a boolean tree mask (every draft token sees
+    the prefix and its ancestors: token 2 and 3 both follow token 1).  16 cache
+    replicas (21 MB each, 336 MB in all) so that the Infinity Cache cannot
+    serve a call.  Reports the masked call, the same call with the causal mask
+    instead, and the tile copy (1 -> 4 paths)."""
+    P, Hkv, Hq, T0, L = 4, 2, 16, 10240, 4
+    k = W.random_rows([40, 1], (1, Hkv, T0, 256), "bf16").to(dev)
+    v = W.random_rows([40, 2], (1, Hkv, T0, 256), "bf16").to(dev)
+    one = rbq.RotatedQuantKVCache(1, Hkv, device=dev, rot=rot)
+    one.append(k, v)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # tile copy, timed on its own (one batch-1 cache into 4 paths, repeatedly)
+    tiled = []
+    for _ in range(16):
+        c = rbq.RotatedQuantKVCache(1, Hkv, device=dev, rot=rot)
+        c.arrays = {n: a.clone() for n, a in one.arrays.items()}
+        c.desc = rbq.rbq_kv_cache.from_buffer_copy(one.desc)
+        c._bind(c.desc, c.arrays, one.capacity)
+        tiled.append(c)
+    dsts = []
+    for c in tiled[:2]:
+        d = rbq.RotatedQuantKVCache(1, Hkv, device=dev, rot=rot)
+        d.desc = rbq.rbq_kv_cache.from_buffer_copy(one.desc)
+        d.desc.B = P
+        d.arrays = one._alloc(one.capacity, P)
+        d._bind(d.desc, d.arrays, one.capacity)
+        dsts.append(d)
+    for i in range(4):
+        rbq.rbq_kv_copy_batch(tiled[i % 16].desc, 0, 0, dsts[i % 2].desc)
+    ev0.record(stream)
+    for i in range(40):
+        rbq.rbq_kv_copy_batch(tiled[i % 16].desc, 0, 0, dsts[i % 2].desc)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    tile_us = ev0.elapsed_time(ev1) * 1e3 / 40
+    tile_bytes = Hkv * T0 * 256 * (1 + P)
+    del dsts
+    kd = W.random_rows([41, 1], (P, Hkv, L, 256), "bf16").to(dev)
+    vd = W.random_rows([41, 2], (P, Hkv, L, 256), "bf16").to(dev)
+    for c in tiled:
+        c.tile(P)
+        c.append(kd, vd)
+    T = T0 + L
+    parent = [-1, 0, 1, 1]
+    keep = torch.zeros(L, T, dtype=torch.bool)
+    keep[:, :T0] = True
+    for i in range(L):
+        j = i
+        while j >= 0:
+            keep[i, T0 + j] = True
+            j = parent[j]
+    keep = keep.to(dev)
+    q = W.random_rows([41, 3], (P, Hq, L, 256), "bf16").to(dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    ws = tiled[0].workspace(Hq, L)
+
+    def timed(mask, causal):
+        for i in range(50):
+            c = tiled[i % 16]
+            rbq.rbq_quant_attn_decode(c.desc, q, 1 / 16, causal, rot, out, 0, ws, mask)
+        ev0.record(stream)
+        for i in range(n_calls):
+            c = tiled[i % 16]
+            rbq.rbq_quant_attn_decode(c.desc, q, 1 / 16, causal, rot, out, 0, ws, mask)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / n_calls
+
+    masked_us = timed(keep, False)
+    causal_us = timed(None, True)
+    alg = P * Hkv * T * 256 + P * Hq * L * 256 * (2 + 4) + L * T
+    gbs = alg / (masked_us * 1e-6) / 1e9
+    return {
+        "what": f"{P} draft paths x {L} tokens over {T0} cached tokens, {Hq}/{Hkv} heads, "
+                "bf16, boolean tree mask (rbq_quant_attn_decode_mask); 16 cache replicas",
+        "bound": "hbm",
+        "alg_bytes_per_call": alg,
+        "avg_us": round(masked_us, 3),
+        "achieved": round(gbs, 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(gbs / HBM_PEAK_GBS, 4),
+        "verified_tokens_per_s": round(P * L / (masked_us * 1e-6), 1),
+        "causal_mask_avg_us": round(causal_us, 3),
+        "tile_copy": {"avg_us": round(tile_us, 3), "bytes": tile_bytes,
+                      "achieved": round(tile_bytes / (tile_us * 1e-6) / 1e9, 2)},
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -235,6 +329,9 @@ def main() -> int:
     copy_gbs = copy_bytes / (copy_us * 1e-6) / 1e9
     del snaps
 
+    print("[bench] tree verification", file=sys.stderr, flush=True)
+    tree = tree_verify(rbq, W, dev, rot)
+
     nbytes = algorithmic_bytes(w, w.T)
     ms_per_step = total * 1e3 / args.steps
     value = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
@@ -289,6 +386,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(copy_gbs / HBM_PEAK_GBS, 4),
         },
+        "tree_verify": tree,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
