@@ -281,29 +281,49 @@ struct TileLoads {
 // banks.
 __device__ __forceinline__ int k_slot(int k, int c) { return 8 * k + (c ^ ((k >> 1) & 7)); }
 
-// Direct-to-LDS loads of the tile at key t0 into this wave's buffer (lane l
-// of an instruction lands at buffer offset + 16 l, or 4 l): 11 instructions,
-// each reading whole 128-byte lines.  Keys past the buffer ranges read as zero.
+// Direct-to-LDS loads of part PART of the tile at key t0 into this wave's
+// buffer (lane l of an instruction lands at buffer offset + 16 l, or 4 l),
+// each instruction reading whole 128-byte lines; keys past the buffer ranges
+// read as zero.  Part 0: K words (4 instructions), part 1: V words (3),
+// part 2: the four scale / bias arrays (4).  The loop issues the parts at
+// three points of an iteration rather than all at once: while the memory
+// system is saturated an issuing wave stalls until its requests are taken,
+// and spread out those stalls overlap more of the other waves' arithmetic.
+template <int PART>
+__device__ __forceinline__ void dma_tile_part(lds_u8* buf, int t0, int lane, __amdgpu_buffer_rsrc_t kw_r,
+                                              __amdgpu_buffer_rsrc_t ks_r, __amdgpu_buffer_rsrc_t kb_r,
+                                              __amdgpu_buffer_rsrc_t vw_r, __amdgpu_buffer_rsrc_t vs_r,
+                                              __amdgpu_buffer_rsrc_t vb_r) {
+    if constexpr (PART == 0) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int p = 64 * m + lane;
+            const int k = p >> 3;
+            const int c = (p & 7) ^ ((k >> 1) & 7);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kw_r, buf + kBufK + 1024 * m, 16,
+                                                      (t0 + k) * 128 + 16 * c, 0, 0, 0);
+        }
+    } else if constexpr (PART == 1) {
+#pragma unroll
+        for (int m = 0; m < 3; ++m)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vw_r, buf + kBufV + 1024 * m, 16,
+                                                      t0 * 96 + 16 * (64 * m + lane), 0, 0, 0);
+    } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ks_r, buf + kBufKs, 4, t0 * 8 + 4 * lane, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kb_r, buf + kBufKb, 4, t0 * 8 + 4 * lane, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vs_r, buf + kBufVs, 4, t0 * 8 + 4 * lane, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vb_r, buf + kBufVb, 4, t0 * 8 + 4 * lane, 0, 0, 0);
+    }
+}
+
+// The whole tile (the first one of each wave, before the set-up).
 __device__ __forceinline__ void dma_tile(lds_u8* buf, int t0, int lane, __amdgpu_buffer_rsrc_t kw_r,
                                          __amdgpu_buffer_rsrc_t ks_r, __amdgpu_buffer_rsrc_t kb_r,
                                          __amdgpu_buffer_rsrc_t vw_r, __amdgpu_buffer_rsrc_t vs_r,
                                          __amdgpu_buffer_rsrc_t vb_r) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int p = 64 * m + lane;
-        const int k = p >> 3;
-        const int c = (p & 7) ^ ((k >> 1) & 7);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kw_r, buf + kBufK + 1024 * m, 16,
-                                                  (t0 + k) * 128 + 16 * c, 0, 0, 0);
-    }
-#pragma unroll
-    for (int m = 0; m < 3; ++m)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vw_r, buf + kBufV + 1024 * m, 16,
-                                                  t0 * 96 + 16 * (64 * m + lane), 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ks_r, buf + kBufKs, 4, t0 * 8 + 4 * lane, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(kb_r, buf + kBufKb, 4, t0 * 8 + 4 * lane, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vs_r, buf + kBufVs, 4, t0 * 8 + 4 * lane, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vb_r, buf + kBufVb, 4, t0 * 8 + 4 * lane, 0, 0, 0);
+    dma_tile_part<0>(buf, t0, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
+    dma_tile_part<1>(buf, t0, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
+    dma_tile_part<2>(buf, t0, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
 }
 
 // The lane's operands of the buffered tile.
@@ -630,11 +650,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         TileLoads cur;
         read_tile(cur, wbuf_g, n, j);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-        if (it + kWaves < n_tiles)
-            dma_tile(wbuf, t0 + kWaves * kTile, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
+        const bool more = it + kWaves < n_tiles;  // the wave's next tile, in three parts
+        if (more)
+            dma_tile_part<0>(wbuf, t0 + kWaves * kTile, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
         uint32_t mk_next[2][2] = {{0u, 0u}, {0u, 0u}};
         if constexpr (MK != kMaskNone)
-            if (it + kWaves < n_tiles) load_mask(t0 + kWaves * kTile, mk_next);
+            if (more) load_mask(t0 + kWaves * kTile, mk_next);
 
         // ---- value scales and biases of the lane's (key, group) -> staging,
         //      each fp16 value repeated 4 times (the 8 bytes a transposing
@@ -734,6 +755,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 }
         }
 
+        if (more)
+            dma_tile_part<1>(wbuf, t0 + kWaves * kTile, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
         // ---- online softmax per row (base 2), lazy rescale: the reference
         //      moves only when the tile maximum exceeds it by more than 2^8 ----
         float mx[2];
@@ -788,6 +811,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             lds_st32(smem, p_wr + 512 * blk, hi2);
             lds_st32(smem, p_wr + 512 * blk + 16, f16_residuals(hi2, p0, p1, one));
         }
+        if (more)
+            dma_tile_part<2>(wbuf, t0 + kWaves * kTile, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
         // A operand of P.V: row n (hi rows 0-7, lo rows 8-15; within each
         // quad of rows the slot order rb + 0, 2, 1, 3) x keys 4j + e of both
         // blocks; lane 4e + q addresses (key 4j + e, part q >> 1, quad q & 1)
