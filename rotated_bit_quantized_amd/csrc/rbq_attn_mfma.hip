@@ -316,6 +316,30 @@ __device__ __forceinline__ void dma_tile_part(lds_u8* buf, int t0, int lane, __a
     }
 }
 
+// The k-th tile (counted within the split) of a wave, or n_tiles when the
+// wave has no k-th tile.  Round robin over the waves, except for the last
+// full round together with the remainder (8 to 15 tiles): positions 0-7 go
+// to waves 0-3, two each, 8-11 to waves 4-7 and 12-15 to waves 0-3 again.
+// The older half of a workgroup issues first on each SIMD and gets through
+// its tiles sooner; with the same number of tiles each, it idles at the end
+// while the younger half finishes.  The order is fixed, so results do not
+// depend on timing.
+__device__ __forceinline__ int wave_tile(int k, int wave, int n_tiles) {
+    const int rounds = n_tiles / kWaves;
+    if (rounds == 0) return (k == 0 && wave < n_tiles) ? wave : n_tiles;
+    if (k < rounds - 1) return wave + kWaves * k;
+    const int jt = k - (rounds - 1);  // index among the wave's last-round tiles
+    int pos = 2 * kWaves;             // none
+    if (wave < kWaves / 2) {
+        if (jt < 2) pos = 2 * wave + jt;
+        else if (jt == 2) pos = 12 + wave;
+    } else if (jt == 0) {
+        pos = wave + 4;
+    }
+    const int tail_n = kWaves + n_tiles % kWaves;
+    return (pos < tail_n) ? (rounds - 1) * kWaves + pos : n_tiles;
+}
+
 // The whole tile (the first one of each wave, before the set-up).
 __device__ __forceinline__ void dma_tile(lds_u8* buf, int t0, int lane, __amdgpu_buffer_rsrc_t kw_r,
                                          __amdgpu_buffer_rsrc_t ks_r, __amdgpu_buffer_rsrc_t kb_r,
@@ -416,14 +440,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const __amdgpu_buffer_rsrc_t vs_r = make_rsrc(a.vs + row0 * kGroups, (uint32_t)T * 8u);
     const __amdgpu_buffer_rsrc_t vb_r = make_rsrc(a.vb + row0 * kGroups, (uint32_t)T * 8u);
     const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
-    // unconditional: a wave without tiles reads keys of the next split or,
-    // past T, zeros from the buffer range check, and never uses them
+    const int it_first = wave_tile(0, wave, n_tiles);
     // this wave's tile buffer, filled with its first tile unconditionally (a
-    // wave without tiles reads keys of the next split or, past T, zeros, and
-    // never uses them)
+    // wave without tiles reads keys of the next split or, past T, zeros from
+    // the buffer range check, and never uses them)
     lds_u8* wbuf = (lds_u8*)tbuf + wave * kWaveAreaBytes;
     const unsigned char* wbuf_g = tbuf + wave * kWaveAreaBytes;
-    dma_tile(wbuf, t_begin + wave * kTile, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
+    dma_tile(wbuf, t_begin + it_first * kTile, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
 
     // ---- decode table: entry e = 4 fp16 codes (e >> 3k) & 7 ----
     for (int e = tid; e < 4096; e += kThreads) {
@@ -624,7 +647,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                                       (int64_t)(R % a.L) * a.msl) * kMaskElem);
             }
         }
-        if (wave < n_tiles) load_mask(t_begin + wave * kTile, mk);
+        if (it_first < n_tiles) load_mask(t_begin + it_first * kTile, mk);
     }
 
     f32x4 O[16];
@@ -642,20 +665,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     float thr[2] = {-INFINITY, -INFINITY};
     f32x4 cinit = {0.f, 0.f, 0.f, 0.f};
 
-    for (int it = wave; it < n_tiles; it += kWaves) {
+    for (int kth = 0, it = it_first; it < n_tiles; ++kth) {
         const int t0 = t_begin + it * kTile;
+        const int it_next = wave_tile(kth + 1, wave, n_tiles);
+        const int t_next = t_begin + it_next * kTile;
         // this tile's transfer is complete; its operands are read out, then the
         // buffer is refilled with the wave's next tile while this one is computed
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         TileLoads cur;
         read_tile(cur, wbuf_g, n, j);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-        const bool more = it + kWaves < n_tiles;  // the wave's next tile, in three parts
+        const bool more = it_next < n_tiles;  // the wave's next tile, in three parts
         if (more)
-            dma_tile_part<0>(wbuf, t0 + kWaves * kTile, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
+            dma_tile_part<0>(wbuf, t_next, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
         uint32_t mk_next[2][2] = {{0u, 0u}, {0u, 0u}};
         if constexpr (MK != kMaskNone)
-            if (more) load_mask(t0 + kWaves * kTile, mk_next);
+            if (more) load_mask(t_next, mk_next);
 
         // ---- value scales and biases of the lane's (key, group) -> staging,
         //      each fp16 value repeated 4 times (the 8 bytes a transposing
@@ -756,7 +781,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
 
         if (more)
-            dma_tile_part<1>(wbuf, t0 + kWaves * kTile, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
+            dma_tile_part<1>(wbuf, t_next, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
         // ---- online softmax per row (base 2), lazy rescale: the reference
         //      moves only when the tile maximum exceeds it by more than 2^8 ----
         float mx[2];
@@ -812,7 +837,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             lds_st32(smem, p_wr + 512 * blk + 16, f16_residuals(hi2, p0, p1, one));
         }
         if (more)
-            dma_tile_part<2>(wbuf, t0 + kWaves * kTile, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
+            dma_tile_part<2>(wbuf, t_next, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
         // A operand of P.V: row n (hi rows 0-7, lo rows 8-15; within each
         // quad of rows the slot order rb + 0, 2, 1, 3) x keys 4j + e of both
         // blocks; lane 4e + q addresses (key 4j + e, part q >> 1, quad q & 1)
@@ -860,6 +885,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
                 for (int p = 0; p < 2; ++p) mk[blk][p] = mk_next[blk][p];
         }
+        it = it_next;
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // no transfer into the buffer in flight
 
