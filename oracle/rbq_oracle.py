@@ -28,6 +28,14 @@ design notes):
       against the stored (rounded) scale and bias;
   R5  a zero scale divides by 1 (codes 0, dequant = bias);
   R6  attention accumulates in fp64 here (fp32 on the GPU) and returns fp32.
+
+Variants beyond the default configuration (same pages): bit widths 2/3/4/5/6/8
+(the width list in ``_packed_words``), any group size dividing head_dim (the
+cache constructor's ``group_size``), head_dim 64/128/256, the two-sided block
+rotation that the ``_quat_right_conj`` docstring describes (``mode=
+"two_sided"``), and the page's own rotation precision (``round_rotated``: the
+rotation entries and every rotated vector rounded to the input dtype, as
+``rotate_last`` does with ``R.astype(x.dtype)``).
 """
 from __future__ import annotations
 
@@ -68,6 +76,22 @@ def quat_right_conj(q) -> np.ndarray:
     ], dtype=np.float64)
 
 
+def quat_right_true_conj(q) -> np.ndarray:
+    """4x4 matrix of v -> v (x) conj(q), the map the ``_quat_right_conj``
+    docstring describes (quaternions as column vectors (w, x, y, z)).  Written
+    out from the Hamilton product with p = conj(q) = (w, -x, -y, -z):
+    v (x) p = (v0 p0 - v1 p1 - v2 p2 - v3 p3, v0 p1 + v1 p0 + v2 p3 - v3 p2,
+               v0 p2 - v1 p3 + v2 p0 + v3 p1, v0 p3 + v1 p2 - v2 p1 + v3 p0)."""
+    w, x, y, z = (float(v) for v in q)
+    p0, p1, p2, p3 = w, -x, -y, -z
+    return np.array([
+        [p0, -p1, -p2, -p3],
+        [p1, p0, p3, -p2],
+        [p2, -p3, p0, p1],
+        [p3, p2, -p1, p0],
+    ], dtype=np.float64)
+
+
 def normalize_quat(a) -> np.ndarray:
     """a / |a| in fp64: squares summed left to right, correctly rounded sqrt
     and division (reading R2)."""
@@ -90,21 +114,25 @@ def matmul4_ordered(A: np.ndarray, Bm: np.ndarray) -> np.ndarray:
     return C
 
 
-def rotation_blocks(draws: np.ndarray) -> np.ndarray:
+def rotation_blocks(draws: np.ndarray, mode: str = "printed") -> np.ndarray:
     """Blocks of the block-diagonal rotation (``build_block_so4``).
 
     draws: float32 ``[D/4, 2, 4]`` (left draw, right draw per block, in the
     page's draw order).  Returns float32 ``[D/4, 4, 4]``:
-    block b = quat_left(qL) @ quat_right_conj(qR), qL/qR the normalised draws,
-    computed in fp64 and rounded once to fp32 (reading R2)."""
+    block b = quat_left(qL) @ R(qR), qL/qR the normalised draws, computed in
+    fp64 and rounded once to fp32 (reading R2), with R = the printed
+    ``_quat_right_conj`` (mode "printed", reading R1) or the right
+    multiplication by conj(qR) that its docstring describes (mode
+    "two_sided")."""
     draws = np.asarray(draws, dtype=np.float32)
     if draws.ndim != 3 or draws.shape[1:] != (2, 4):
         raise ValueError("draws must be [D/4, 2, 4]")
+    right = {"printed": quat_right_conj, "two_sided": quat_right_true_conj}[mode]
     out = np.empty((draws.shape[0], 4, 4), dtype=np.float32)
     for b in range(draws.shape[0]):
         qL = normalize_quat(draws[b, 0])
         qR = normalize_quat(draws[b, 1])
-        out[b] = matmul4_ordered(quat_left(qL), quat_right_conj(qR)).astype(np.float32)
+        out[b] = matmul4_ordered(quat_left(qL), right(qR)).astype(np.float32)
     return out
 
 
@@ -233,11 +261,26 @@ def unpack(words: np.ndarray, bits: int, dim: int) -> np.ndarray:
     return codes.astype(np.uint8)
 
 
-def quantize_rows(x: np.ndarray, blocks, bits: int, dtype: str):
+def rotate_for_cache(x: np.ndarray, blocks, dtype: str, round_rotated: bool = False) -> np.ndarray:
+    """The rotation applied to q, k and v before they meet the cache.
+
+    Default (reading R3): rotate(x, blocks), fp32.  With ``round_rotated``
+    (the page's own precision in ``rotate_last``: ``x @ R.astype(x.dtype)``
+    returns the input dtype), the result is rounded to ``dtype``; the caller
+    passes blocks already rounded to ``dtype`` (``round_to_dtype(blocks)``).
+    ``blocks`` None = identity (x unchanged)."""
+    if blocks is None:
+        return np.asarray(x, dtype=np.float32)
+    y = rotate(x, blocks)
+    return round_to_dtype(y, dtype) if round_rotated else y
+
+
+def quantize_rows(x: np.ndarray, blocks, bits: int, dtype: str, group: int = GROUP,
+                  round_rotated: bool = False):
     """Rotate (``blocks`` may be None = identity) then quantize and pack rows.
     Returns (words uint32, scales float32, biases float32)."""
-    y = np.asarray(x, dtype=np.float32) if blocks is None else rotate(x, blocks)
-    codes, s, b = quantize(y, bits, dtype)
+    y = rotate_for_cache(x, blocks, dtype, round_rotated)
+    codes, s, b = quantize(y, bits, dtype, group)
     return pack(codes, bits), s, b
 
 
@@ -265,8 +308,10 @@ class QuantKVCache:
     (K words/scales/biases, V words/scales/biases) of shape [B, H, cap, .],
     ``offset`` rows valid.  Rows beyond ``offset`` are never read."""
 
-    def __init__(self, k_bits: int = 4, v_bits: int = 3, dtype: str = "bf16"):
+    def __init__(self, k_bits: int = 4, v_bits: int = 3, dtype: str = "bf16",
+                 group: int = GROUP, round_rotated: bool = False):
         self.k_bits, self.v_bits, self.dtype = k_bits, v_bits, dtype
+        self.group, self.round_rotated = group, round_rotated
         self.offset = 0
         self.arrays = None  # dict name -> ndarray
 
@@ -280,9 +325,9 @@ class QuantKVCache:
             return
         shapes = {
             "kw": (packed_words(D, self.k_bits), np.uint32),
-            "ks": (D // GROUP, np.float32), "kb": (D // GROUP, np.float32),
+            "ks": (D // self.group, np.float32), "kb": (D // self.group, np.float32),
             "vw": (packed_words(D, self.v_bits), np.uint32),
-            "vs": (D // GROUP, np.float32), "vb": (D // GROUP, np.float32),
+            "vs": (D // self.group, np.float32), "vb": (D // self.group, np.float32),
         }
         new = {}
         for name, (w, dt) in shapes.items():
@@ -298,8 +343,10 @@ class QuantKVCache:
         [offset, offset+n) and advance ``offset``."""
         B, H, n, D = k.shape
         self._grow(B, H, D, n)
-        kw, ks, kb = quantize_rows(k, blocks, self.k_bits, self.dtype)
-        vw, vs, vb = quantize_rows(v, blocks, self.v_bits, self.dtype)
+        kw, ks, kb = quantize_rows(k, blocks, self.k_bits, self.dtype, self.group,
+                                   self.round_rotated)
+        vw, vs, vb = quantize_rows(v, blocks, self.v_bits, self.dtype, self.group,
+                                   self.round_rotated)
         o = self.offset
         for name, val in (("kw", kw), ("ks", ks), ("kb", kb), ("vw", vw), ("vs", vs), ("vb", vb)):
             self.arrays[name][:, :, o:o + n] = val
@@ -316,11 +363,11 @@ class QuantKVCache:
     def dequant_kv(self, b: int, h: int):
         """Dequantised K and V rows [0, offset) of (b, h), fp64 [offset, D]."""
         a, o = self.arrays, self.offset
-        D = a["ks"].shape[-1] * GROUP
+        D = a["ks"].shape[-1] * self.group
         kc = unpack(a["kw"][b, h, :o], self.k_bits, D)
         vc = unpack(a["vw"][b, h, :o], self.v_bits, D)
-        return (dequantize(kc, a["ks"][b, h, :o], a["kb"][b, h, :o]),
-                dequantize(vc, a["vs"][b, h, :o], a["vb"][b, h, :o]))
+        return (dequantize(kc, a["ks"][b, h, :o], a["kb"][b, h, :o], self.group),
+                dequantize(vc, a["vs"][b, h, :o], a["vb"][b, h, :o], self.group))
 
 
 def cache_state(cache: QuantKVCache):
@@ -342,9 +389,9 @@ def set_cache_state(cache: QuantKVCache, state) -> None:
     cache.offset = cache.arrays["kw"].shape[2]
 
 
-def meta_state(cache: QuantKVCache, group: int = GROUP):
+def meta_state(cache: QuantKVCache):
     """``meta_state``: group size and bit widths as strings."""
-    return str(group), str(cache.k_bits), str(cache.v_bits)
+    return str(cache.group), str(cache.k_bits), str(cache.v_bits)
 
 
 def snapshot(caches):
@@ -388,7 +435,8 @@ def commit_verified_prefix(cache: QuantKVCache, verified_len: int, accepted_len:
 # ---------------------------------------------------------------- attention --
 
 def attention_row(q_row: np.ndarray, khat: np.ndarray, vhat: np.ndarray, n_keys: int,
-                  scale: float, blocks, mask_row=None) -> np.ndarray:
+                  scale: float, blocks, mask_row=None, dtype: str = "bf16",
+                  round_rotated: bool = False) -> np.ndarray:
     """One query row of ``asym_quantized_sdpa`` followed by the inverse rotation.
 
     q_row: [D] input-dtype values (unrotated); khat/vhat: fp64 dequantised
@@ -400,8 +448,9 @@ def attention_row(q_row: np.ndarray, khat: np.ndarray, vhat: np.ndarray, n_keys:
     a false entry's score becomes the most negative finite value (the page's
     ``finfo.min`` fill: such a key gets weight 0 unless every key of the row is
     masked, when the softmax of equal scores weights all keys alike); or
-    floating point, added to the scaled scores."""
-    qr = np.asarray(q_row, np.float32) if blocks is None else rotate(q_row, blocks)
+    floating point, added to the scaled scores.  ``round_rotated``: q' is
+    rounded to ``dtype`` (``rotate_for_cache``); the output stays fp32."""
+    qr = rotate_for_cache(q_row, blocks, dtype, round_rotated)
     qs = qr.astype(np.float64) * float(scale)
     sc = khat[:n_keys] @ qs
     if mask_row is not None:
@@ -448,7 +497,8 @@ def attention(q: np.ndarray, cache: QuantKVCache, scale: float, causal: bool, bl
         khat, vhat = deq[(b, kvh)]
         n_keys = T - L + i + 1 if causal else T
         mrow = None if mask is None else mask[b, h, i]
-        out[b, h, i] = attention_row(q[b, h, i], khat, vhat, n_keys, scale, blocks, mrow)
+        out[b, h, i] = attention_row(q[b, h, i], khat, vhat, n_keys, scale, blocks, mrow,
+                                     cache.dtype, cache.round_rotated)
     return out
 
 
