@@ -21,9 +21,13 @@
  *     return RBQ_EHIP and rbq_last_hip_error() gives the hipError_t (thread
  *     local).
  *   - Thread safety: calls on distinct caches may run concurrently.
- *   - Supported shapes in this library: head_dim 256, group 64, k_bits 4,
- *     v_bits 3, dtype fp16 or bf16, gfx950.  Anything else returns
- *     RBQ_EUNSUPPORTED.
+ *   - Supported shapes in this library (gfx950): head_dim 64, 128 or 256;
+ *     group_size 32, 64 or 128, dividing head_dim (the cache constructor's
+ *     group_size); k_bits and v_bits each one of 2, 3, 4, 5, 6, 8 (the width
+ *     list of _packed_words); dtype fp16 or bf16.  Anything else returns
+ *     RBQ_EUNSUPPORTED.  The default configuration (head_dim 256, group 64,
+ *     K 4-bit, V 3-bit) has dedicated append and attention kernels; the
+ *     others run general kernels with the same results definition.
  */
 #ifndef RBQ_H
 #define RBQ_H
@@ -48,6 +52,19 @@ extern "C" {
 #define RBQ_F16   1
 #define RBQ_BF16  2
 
+/* ---- cache flags ----
+ * RBQ_FLAG_ROUND_ROTATED: the page's own rotation precision (rotate_last on
+ * the quant_kv.py page multiplies by R.astype(x.dtype), so its result is in
+ * the input dtype): every rotated row - K and V before they are quantized,
+ * q before the attention - is rounded to the cache dtype (round half to
+ * even).  The caller passes rotation blocks already rounded to the dtype.
+ * Without the flag rotated rows stay fp32. */
+#define RBQ_FLAG_ROUND_ROTATED 1
+
+/* ---- rotation block forms (rbq_rotation_build_mode) ---- */
+#define RBQ_ROT_PRINTED    0  /* L(qL) times the matrix printed for _quat_right_conj */
+#define RBQ_ROT_TWO_SIDED  1  /* L(qL) times the right multiplication by conj(qR)   */
+
 /*
  * Cache descriptor (host struct, owned by the caller).  It mirrors the six
  * arrays of AsymmetricQuantizedKVCache (_init_quant on the quant_kv.py page):
@@ -64,7 +81,7 @@ extern "C" {
 typedef struct rbq_kv_cache {
     int32_t B, H_kv, head_dim, group_size, k_bits, v_bits;
     int32_t dtype;          /* RBQ_F16 or RBQ_BF16: type of scales/biases and of the inputs */
-    int32_t reserved;       /* must be 0 */
+    int32_t flags;          /* 0 or RBQ_FLAG_ROUND_ROTATED */
     int64_t capacity;       /* rows allocated per (b, kv head) */
     int64_t offset;         /* rows written per (b, kv head) */
     uint32_t* k_words;
@@ -90,6 +107,18 @@ typedef struct rbq_kv_cache {
  * or a zero-norm draw (nothing defined is written in that case).
  */
 int rbq_rotation_build(const float* draws, int32_t head_dim, float* blocks);
+
+/*
+ * rbq_rotation_build_mode - as rbq_rotation_build with a choice of the right
+ * factor (quant_kv.py, "SO(4) block rotation").  RBQ_ROT_PRINTED gives
+ * exactly rbq_rotation_build.  RBQ_ROT_TWO_SIDED uses the matrix of
+ * v -> v * conj(qR) (quaternions as column vectors (w, x, y, z)), the map the
+ * _quat_right_conj docstring describes; each block is then
+ * v -> qL * v * conj(qR), a general SO(4) element, while the printed matrix
+ * is the transpose of L(qR) and gives left-isoclinic blocks only.
+ * Errors: as rbq_rotation_build, and RBQ_EINVAL for an unknown mode.
+ */
+int rbq_rotation_build_mode(const float* draws, int32_t head_dim, int32_t mode, float* blocks);
 
 /*
  * rbq_kv_required_capacity - capacity (rows) the cache needs before n more
@@ -220,8 +249,16 @@ size_t rbq_quant_attn_workspace_bytes(const rbq_kv_cache* c, int32_t H_q, int32_
  *   ws          device workspace of ws_bytes >= rbq_quant_attn_workspace_bytes
  *               (may be NULL when that is 0).
  * Scores, softmax and the P.V accumulation run in fp32.  Keys [0, offset)
- * are read.  Errors: RBQ_EINVAL (null pointers, H_q % H_kv != 0, splits < 0),
- * RBQ_ERANGE (L < 1 or L > offset), RBQ_EWORKSPACE, RBQ_EUNSUPPORTED, RBQ_EHIP.
+ * are read.  Any L from 1 (decode) to offset (prefill-length blocks) is
+ * taken; L is the number of trailing cache rows the query block stands for.
+ * Kernels: the default configuration (head_dim 256, group 64, K4/V3) with at
+ * most 32 query rows per kv head (H_q / H_kv x L) runs a dedicated kernel;
+ * every other configuration and every longer block runs the general tile
+ * kernel (blocks of 64 query rows against 32-key tiles decoded once per
+ * workgroup).  With RBQ_FLAG_ROUND_ROTATED in the cache flags the rotated q
+ * is rounded to the dtype.  Errors: RBQ_EINVAL (null pointers, H_q % H_kv !=
+ * 0, splits < 0), RBQ_ERANGE (L < 1 or L > offset), RBQ_EWORKSPACE,
+ * RBQ_EUNSUPPORTED, RBQ_EHIP.
  */
 int rbq_quant_attn_decode(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L,
                           float scale, int32_t causal, const float* rot_blocks, float* out,

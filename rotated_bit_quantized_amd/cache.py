@@ -38,24 +38,37 @@ def quaternion_draws(seed: int = 0, head_dim: int = HEAD_DIM) -> np.ndarray:
     return out
 
 
-def build_block_so4(head_dim: int = HEAD_DIM, seed: int = 0, device="cuda") -> torch.Tensor:
+def build_block_so4(head_dim: int = HEAD_DIM, seed: int = 0, device="cuda",
+                    two_sided: bool = False, round_to: Optional[torch.dtype] = None) -> torch.Tensor:
     """Rotation blocks ``float32 [head_dim/4, 4, 4]`` on ``device``
-    (``build_block_so4`` without the dense matrix: only its diagonal blocks)."""
-    blocks = capi.rbq_rotation_build(quaternion_draws(seed, head_dim))
-    return torch.from_numpy(blocks).to(device)
+    (``build_block_so4`` without the dense matrix: only its diagonal blocks).
+    ``two_sided``: the right factor is the right multiplication by conj(qR)
+    that the page's ``_quat_right_conj`` docstring describes, instead of the
+    printed matrix.  ``round_to``: the blocks rounded to that dtype (the
+    page's ``R.astype(x.dtype)``; pair it with a cache made with
+    ``round_rotated=True``)."""
+    mode = capi.RBQ_ROT_TWO_SIDED if two_sided else capi.RBQ_ROT_PRINTED
+    blocks = torch.from_numpy(capi.rbq_rotation_build_mode(quaternion_draws(seed, head_dim), mode))
+    if round_to is not None:
+        blocks = blocks.to(round_to).float()
+    return blocks.to(device)
 
 
 class RotatedQuantKVCache:
-    """Rotated K4/V3 group-64 quantized KV cache on one GPU.
+    """Rotated, asymmetric quantized KV cache on one GPU (K4/V3, group 64,
+    head_dim 256 by default; head_dim 64/128/256, group 32/64/128 and widths
+    2/3/4/5/6/8 for K and V independently).
 
     ``rot`` is the device tensor of rotation blocks (or None: inputs are taken
     as already rotated and outputs stay in the rotated space, as the page's
-    cache and SDPA do)."""
+    cache and SDPA do).  ``round_rotated``: rotated rows are rounded to the
+    cache dtype (the page's own rotation precision); pass blocks rounded to
+    the dtype as well (``build_block_so4(round_to=dtype)``)."""
 
     def __init__(self, B: int, H_kv: int, dtype: torch.dtype = torch.bfloat16,
                  device="cuda", rot: Optional[torch.Tensor] = None,
                  head_dim: int = HEAD_DIM, group_size: int = GROUP,
-                 k_bits: int = K_BITS, v_bits: int = V_BITS):
+                 k_bits: int = K_BITS, v_bits: int = V_BITS, round_rotated: bool = False):
         if dtype not in capi.DTYPE_CODES:
             raise ValueError("dtype must be torch.float16 or torch.bfloat16")
         self.device = torch.device(device)
@@ -63,7 +76,8 @@ class RotatedQuantKVCache:
         self.rot = rot
         self.desc = capi.rbq_kv_cache(B=B, H_kv=H_kv, head_dim=head_dim, group_size=group_size,
                                       k_bits=k_bits, v_bits=v_bits,
-                                      dtype=capi.DTYPE_CODES[dtype], reserved=0,
+                                      dtype=capi.DTYPE_CODES[dtype],
+                                      flags=capi.RBQ_FLAG_ROUND_ROTATED if round_rotated else 0,
                                       capacity=0, offset=0)
         self.arrays = None
         self._ws = None

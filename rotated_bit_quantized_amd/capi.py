@@ -31,6 +31,11 @@ RBQ_EHIP = -6
 RBQ_F16 = 1
 RBQ_BF16 = 2
 
+RBQ_FLAG_ROUND_ROTATED = 1
+
+RBQ_ROT_PRINTED = 0
+RBQ_ROT_TWO_SIDED = 1
+
 RBQ_MASK_NONE = 0
 RBQ_MASK_BOOL = 1
 RBQ_MASK_ADD_F32 = 2
@@ -55,7 +60,7 @@ class rbq_kv_cache(ctypes.Structure):
 
     _fields_ = [
         ("B", c_int32), ("H_kv", c_int32), ("head_dim", c_int32), ("group_size", c_int32),
-        ("k_bits", c_int32), ("v_bits", c_int32), ("dtype", c_int32), ("reserved", c_int32),
+        ("k_bits", c_int32), ("v_bits", c_int32), ("dtype", c_int32), ("flags", c_int32),
         ("capacity", c_int64), ("offset", c_int64),
         ("k_words", c_void_p), ("k_scales", c_void_p), ("k_biases", c_void_p),
         ("v_words", c_void_p), ("v_scales", c_void_p), ("v_biases", c_void_p),
@@ -71,6 +76,7 @@ def _load():
     P = POINTER(rbq_kv_cache)
     sigs = {
         "rbq_rotation_build": (c_int32, [c_void_p, c_int32, c_void_p]),
+        "rbq_rotation_build_mode": (c_int32, [c_void_p, c_int32, c_int32, c_void_p]),
         "rbq_kv_required_capacity": (c_int64, [c_int64, c_int64, c_int64]),
         "rbq_kv_grow": (c_int32, [P, P, c_void_p]),
         "rbq_kv_copy_prefix": (c_int32, [P, P, c_void_p]),
@@ -136,6 +142,18 @@ def rbq_rotation_build(draws: np.ndarray) -> np.ndarray:
     out = np.empty((d.shape[0], 4, 4), dtype=np.float32)
     _check("rbq_rotation_build",
            _lib.rbq_rotation_build(d.ctypes.data, 4 * d.shape[0], out.ctypes.data))
+    return out
+
+
+def rbq_rotation_build_mode(draws: np.ndarray, mode: int) -> np.ndarray:
+    """As :func:`rbq_rotation_build` with the right factor chosen by ``mode``
+    (RBQ_ROT_PRINTED or RBQ_ROT_TWO_SIDED)."""
+    d = np.ascontiguousarray(draws, dtype=np.float32)
+    if d.ndim != 3 or d.shape[1:] != (2, 4):
+        raise ValueError("draws must be float32 [D/4, 2, 4]")
+    out = np.empty((d.shape[0], 4, 4), dtype=np.float32)
+    _check("rbq_rotation_build_mode",
+           _lib.rbq_rotation_build_mode(d.ctypes.data, 4 * d.shape[0], int(mode), out.ctypes.data))
     return out
 
 

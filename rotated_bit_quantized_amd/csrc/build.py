@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "librbq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["rbq_append.hip", "rbq_attn_mfma.hip"]
+HIP_SOURCES = ["rbq_append.hip", "rbq_attn_mfma.hip", "rbq_attn_tile.hip"]
 HOST_SOURCES = ["rbq_host.cpp"]
 # per-file extras: the attention kernels never rely on NaN semantics (masked
 # scores are -inf), which lets max reductions compile to single DPP ops

@@ -125,6 +125,7 @@ struct MArgs {
     const void* mask;
     int64_t msb, msh, msl;
     uint32_t mask_bytes;  // extent read through a range-checked buffer resource
+    int round_rot;        // RBQ_FLAG_ROUND_ROTATED: the rotated query rounded to the dtype
 };
 
 // Mask element types (the template argument MK of the attention kernel).
@@ -483,6 +484,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 Bm[4 * q4 + 3] = v.w;
             }
             rotate4(x, Bm, y);
+            if (a.round_rot) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) y[c] = elem_to_f32<DT>(f32_to_elem_bits<DT>(y[c]));
+            }
         } else {
             y[0] = x[0]; y[1] = x[1]; y[2] = x[2]; y[3] = x[3];
         }
@@ -1134,6 +1139,7 @@ int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
     a.msh = mk.sh;
     a.msl = mk.sl;
     a.mask_bytes = mk.bytes;
+    a.round_rot = (c->flags & RBQ_FLAG_ROUND_ROTATED) ? 1 : 0;
     const int64_t units = (int64_t)c->B * c->H_kv * p.RB;
     const dim3 grid((unsigned)(units * p.S)), block(kThreads);
     auto launch = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, s, a); };
@@ -1179,7 +1185,35 @@ int check_attn(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits) {
     if (st != RBQ_OK) return st;
     if (H_q <= 0 || H_q % c->H_kv != 0 || splits < 0) return RBQ_EINVAL;
     if (L < 1 || (int64_t)L > c->offset) return RBQ_ERANGE;
+    if ((int64_t)(H_q / c->H_kv) * L > 0x3FFFFFFF) return RBQ_EUNSUPPORTED;
     return RBQ_OK;
+}
+
+// Which kernel runs a call, and its plan: the dedicated kernel for the
+// default configuration up to kDedicatedMaxRows query rows per kv head, the
+// tile kernel otherwise.
+struct AttnPlan {
+    bool tile;
+    MfmaPlan mp;
+    TilePlan tp;
+    int S;
+    size_t ws_bytes;
+};
+
+int attn_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, AttnPlan* p) {
+    const int64_t G = (int64_t)(H_q / c->H_kv) * L;
+    p->tile = !(is_default_config(c) && G <= kDedicatedMaxRows);
+    int st;
+    if (p->tile) {
+        st = tile_plan(c, H_q, L, splits, &p->tp);
+        p->S = p->tp.S;
+        p->ws_bytes = p->tp.ws_bytes;
+    } else {
+        st = mfma_plan(c, H_q, L, splits, &p->mp);
+        p->S = p->mp.S;
+        p->ws_bytes = p->mp.ws_bytes;
+    }
+    return st;
 }
 
 // Mask arguments: type, non-negative strides, and the byte extent of the
@@ -1218,16 +1252,16 @@ using namespace rbq;
 extern "C" int32_t rbq_quant_attn_splits(const rbq_kv_cache* c, int32_t H_q, int32_t L) {
     int st = check_attn(c, H_q, L, 0);
     if (st != RBQ_OK) return st;
-    MfmaPlan mp;
-    st = mfma_plan(c, H_q, L, 0, &mp);
-    return st != RBQ_OK ? st : mp.S;
+    AttnPlan ap;
+    st = attn_plan(c, H_q, L, 0, &ap);
+    return st != RBQ_OK ? st : ap.S;
 }
 
 extern "C" size_t rbq_quant_attn_workspace_bytes(const rbq_kv_cache* c, int32_t H_q, int32_t L,
                                                  int32_t splits) {
     if (check_attn(c, H_q, L, splits) != RBQ_OK) return 0;
-    MfmaPlan mp;
-    return mfma_plan(c, H_q, L, splits, &mp) == RBQ_OK ? mp.ws_bytes : 0;
+    AttnPlan ap;
+    return attn_plan(c, H_q, L, splits, &ap) == RBQ_OK ? ap.ws_bytes : 0;
 }
 
 extern "C" int rbq_quant_attn_decode_mask(const rbq_kv_cache* c, const void* q, int32_t H_q,
@@ -1242,11 +1276,12 @@ extern "C" int rbq_quant_attn_decode_mask(const rbq_kv_cache* c, const void* q, 
     AttnMask mk;
     st = check_mask(c, H_q, L, mask, mask_type, mask_stride_b, mask_stride_h, mask_stride_l, &mk);
     if (st != RBQ_OK) return st;
-    MfmaPlan mp;
-    st = mfma_plan(c, H_q, L, splits, &mp);
+    AttnPlan ap;
+    st = attn_plan(c, H_q, L, splits, &ap);
     if (st != RBQ_OK) return st;
-    if (mp.ws_bytes > 0 && (ws == nullptr || ws_bytes < mp.ws_bytes)) return RBQ_EWORKSPACE;
-    return mfma_launch(c, q, H_q, L, scale, causal, mk, rot_blocks, out, mp, ws, stream);
+    if (ap.ws_bytes > 0 && (ws == nullptr || ws_bytes < ap.ws_bytes)) return RBQ_EWORKSPACE;
+    if (ap.tile) return tile_launch(c, q, H_q, L, scale, causal, mk, rot_blocks, out, ap.tp, ws, stream);
+    return mfma_launch(c, q, H_q, L, scale, causal, mk, rot_blocks, out, ap.mp, ws, stream);
 }
 
 extern "C" int rbq_quant_attn_decode(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L,

@@ -1,0 +1,726 @@
+// General fused attention over the quantized cache (asym_quantized_sdpa on
+// the quant_kv.py page, with the SO(4) rotation of q on entry and the inverse
+// rotation of the output), for every supported configuration: head_dim 64,
+// 128 or 256, group 32, 64 or 128, K and V widths 2, 3, 4, 5, 6 or 8 bits,
+// and any number of query rows per kv head (G = H_q / H_kv x L, up to
+// prefill-length blocks).
+//
+// Decomposition: one workgroup of 4 wave64s per (b, kv head, block of 64
+// query rows, key split); wave w owns query rows 16 w .. 16 w + 15 of the
+// block.  The workgroup walks 32-key tiles: all 256 threads decode the tile
+// into LDS once (K codes as bytes [key][dim], V codes as bytes transposed
+// [dim][key], as fp16 values; scales and biases as fp32 [group][key]), then every wave with
+// a live row runs its 16 rows against it, while the next tile's packed words
+// are already being loaded into registers.  The codes are converted once per
+// tile, in the decode, to fp16 (exact: integers below 2^11), so the operand
+// reads of the waves need no conversion.  (Codes taken as fp16 subnormals,
+// c * 2^-24, lose precision in the matrix cores when the other operand spans
+// a wide range, as the probabilities do.)
+//
+// All products run as 16x16x32 MFMAs.  Lane l = 16 j + n: operand lanes hold
+// row / column n and the 8 k-slots 8 j .. 8 j + 7 (the same slots in A and
+// B, so the k order within them does not matter); accumulator lane (j, n)
+// holds rows 4 j .. 4 j + 3 of column n.
+// Scores: A = query rows, rotated, times scale * log2(e) and a per-row power
+//   of two 2^E that puts the largest |q| in [2^14, 2^15), split into an fp16
+//   hi and lo part (two MFMAs); B = K codes.  One accumulator per group g of
+//   the row: score = 2^-E sum_g s_g acc_g + sum_g b_g (sum_{d in g} q_d),
+//   folded on the vector units (base-2 scores).
+// Values: A = P' = p s_{t,g} 2^F_g (the probability times the key's value
+//   scale, with a per-tile, per-group power of two that puts the largest
+//   scale in [2^14, 2^15)), split hi + lo; B = V codes of 8 keys x 16 columns
+//   (a transposed byte read).  Each tile's product is folded into the output
+//   accumulators with the softmax rescale and 2^-F_g; the group bias
+//   enters as sum_t p_t b_{t,g}, kept per lane and reduced at the end.
+// Online softmax in base 2 over the tile's 32 keys per row.  Every workgroup
+// stores a record (m, l, unnormalised o) per row; a second kernel merges the
+// key splits, normalises, rotates back and stores the fp32 output.
+// Precondition of the fp16 value path: V codes times 2^F stay finite, i.e.
+// no V scale is inf or NaN; tiny scales next to large ones in a tile lose
+// relative precision below 2^-22 of the tile's largest P'.
+#include <hip/hip_runtime.h>
+
+#include "rbq_common.h"
+
+namespace rbq {
+namespace {
+
+typedef _Float16 tf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 tf16x2 __attribute__((ext_vector_type(2)));
+typedef float tf32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t tu32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t tu32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int tWaves = 4;
+constexpr int tThreads = 64 * tWaves;
+constexpr int tTile = 32;                  // keys per tile
+constexpr int tRows = 16 * tWaves;         // query rows per workgroup
+constexpr int tMaxGroups = 8;              // head_dim / group_size <= 8
+constexpr int tVS = 2 * (tTile + 8);       // bytes per dim row of the transposed V codes
+constexpr int tPS = tTile + 4;             // floats per row of a wave's P staging
+constexpr float tLog2e = 1.44269504088896340736f;
+
+template <int D>
+struct TileLds {
+    static constexpr int KS = 2 * D + 16;                               // bytes per key row of K codes
+    static constexpr int kc = 0;                                        // K codes, fp16 [32][KS / 2]
+    static constexpr int vt = kc + tTile * KS;                          // V codes, fp16 [D][tVS / 2]
+    static constexpr int ksl = vt + D * tVS;                            // fp32 [8][32] K scales
+    static constexpr int kbl = ksl + tMaxGroups * tTile * 4;            // K biases
+    static constexpr int vsf = kbl + tMaxGroups * tTile * 4;            // V scales x 2^F
+    static constexpr int vbl = vsf + tMaxGroups * tTile * 4;            // V biases
+    static constexpr int vinv = vbl + tMaxGroups * tTile * 4;           // 2^-F per group
+    static constexpr int pst = vinv + tMaxGroups * 4;                   // [4 waves][16][tPS] fp32
+    static constexpr int qst = pst + tWaves * 16 * tPS * 4;             // [4 waves][8 groups][16 rows]
+    static constexpr int frw = qst + tWaves * tMaxGroups * 16 * 4;      // [4 waves][16] 2^-E
+    static constexpr int bytes = frw + tWaves * 16 * 4;
+};
+
+struct TArgs {
+    const uint16_t* q;
+    const uint32_t* kw;
+    const uint16_t* ks;
+    const uint16_t* kb;
+    const uint32_t* vw;
+    const uint16_t* vs;
+    const uint16_t* vb;
+    const float* rot;
+    float* rec_o;   // [units][S][64 rows][D]
+    float* rec_ml;  // [units][S][64 rows][2]
+    int64_t capacity;
+    int T, chunk, S, Hkv, n_rep, L, G, RBW, causal, round_rot;
+    int GS, kbits, vbits;
+    float qscale;  // scale * log2(e)
+    const void* mask;
+    int64_t msb, msh, msl;  // elements; key stride 1
+    uint32_t mask_bytes;
+    int mtype;  // 0 none, 1 bool (uint8), 2 fp32 additive, 3 dtype additive
+};
+
+__device__ __forceinline__ tf32x4 tmfma(tf16x8 a, tf16x8 b, tf32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// 4 code bytes -> 4 fp16 codes, exact: the half with bits 0x6400 | c is
+// 1024 + c, and 1024 is subtracted two halves at a time.
+__device__ __forceinline__ tu32x2 bytes_f16(uint32_t d) {
+    const tf16x2 k = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+    const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, d, 0x04010400u);
+    const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, d, 0x04030402u);
+    return (tu32x2){__builtin_bit_cast(uint32_t, __builtin_bit_cast(tf16x2, lo) + k),
+                    __builtin_bit_cast(uint32_t, __builtin_bit_cast(tf16x2, hi) + k)};
+}
+
+template <int CTRL>
+__device__ __forceinline__ float tdpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float tmax16(float x) {
+    x = fmaxf(x, tdpp<0xB1>(x));
+    x = fmaxf(x, tdpp<0x4E>(x));
+    x = fmaxf(x, tdpp<0x141>(x));
+    return fmaxf(x, tdpp<0x140>(x));
+}
+__device__ __forceinline__ float tsum16(float x) {
+    x += tdpp<0xB1>(x);
+    x += tdpp<0x4E>(x);
+    x += tdpp<0x141>(x);
+    return x + tdpp<0x140>(x);
+}
+
+// The 32 codes of BITS bits held in BITS consecutive words (stream bits
+// [0, 32 BITS) of the words), as 8 words of 4 bytes: byte b of word i is code
+// 4 i + b.  Code j sits at stream bits [BITS j, BITS j + BITS), little-endian.
+template <int BITS>
+__device__ __forceinline__ void unpack32(const uint32_t w[8], uint32_t out[8]) {
+    if constexpr (BITS == 8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = w[i];
+    } else if constexpr (BITS == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = w[i] & 0x0F0F0F0Fu;          // codes 8i, 8i+2, 8i+4, 8i+6
+            const uint32_t hi = (w[i] >> 4) & 0x0F0F0F0Fu;   // codes 8i+1, 8i+3, ...
+            out[2 * i] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+            out[2 * i + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+        }
+    } else {
+        constexpr uint32_t m = (1u << BITS) - 1u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t d = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int p = BITS * (4 * i + b);
+                const int wi = p >> 5, sh = p & 31;
+                uint32_t c;
+                if (sh + BITS <= 32) c = (w[wi] >> sh) & m;
+                else c = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & m;
+                d |= c << (8 * b);
+            }
+            out[i] = d;
+        }
+    }
+}
+
+__device__ __forceinline__ void unpack32_any(int bits, const uint32_t w[8], uint32_t out[8]) {
+    switch (bits) {
+        case 2: unpack32<2>(w, out); break;
+        case 3: unpack32<3>(w, out); break;
+        case 4: unpack32<4>(w, out); break;
+        case 5: unpack32<5>(w, out); break;
+        case 6: unpack32<6>(w, out); break;
+        default: unpack32<8>(w, out); break;
+    }
+}
+
+// Registers of one tile for this thread: the packed words of up to two
+// 32-code units (K and / or V), and the four scale / bias values of one
+// (key, group).
+struct TileRaw {
+    uint32_t w[2][8];
+    uint32_t meta[4];
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile_raw(const TArgs& a, int64_t row0, int t0, int tid,
+                                              TileRaw& r) {
+    constexpr int upk = D / 32;  // 32-code units per key row
+    const int kwords = D * a.kbits / 32, vwords = D * a.vbits / 32;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int u = tid + k * tThreads;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r.w[k][i] = 0u;
+        if (u < 2 * D) {
+            const bool isv = u >= D;
+            const int uu = isv ? u - D : u;
+            const int key = uu / upk, part = uu - key * upk;
+            const int t = t0 + key;
+            if (t < a.T) {
+                const int bits = isv ? a.vbits : a.kbits;
+                const uint32_t* src = (isv ? a.vw + (row0 + t) * vwords : a.kw + (row0 + t) * kwords) +
+                                      part * bits;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (i < bits) r.w[k][i] = src[i];
+            }
+        }
+    }
+    const int G = D / a.GS;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.meta[i] = 0u;
+    if (tid < tTile * G) {
+        const int g = tid / tTile, key = tid - g * tTile;
+        const int t = t0 + key;
+        if (t < a.T) {
+            const int64_t o = (row0 + t) * G + g;
+            r.meta[0] = a.ks[o];
+            r.meta[1] = a.kb[o];
+            r.meta[2] = a.vs[o];
+            r.meta[3] = a.vb[o];
+        }
+    }
+}
+
+template <int DT, int D>
+__device__ __forceinline__ void store_tile(const TArgs& a, int tid, const TileRaw& r,
+                                           unsigned char* smem) {
+    using Ly = TileLds<D>;
+    constexpr int upk = D / 32;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int u = tid + k * tThreads;
+        if (u < 2 * D) {
+            const bool isv = u >= D;
+            const int uu = isv ? u - D : u;
+            const int key = uu / upk, part = uu - key * upk;
+            uint32_t c[8];
+            unpack32_any(isv ? a.vbits : a.kbits, r.w[k], c);
+            tu32x2 h[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) h[i] = bytes_f16(c[i]);
+            if (!isv) {
+                tu32x4* dst = reinterpret_cast<tu32x4*>(smem + Ly::kc + key * Ly::KS + 64 * part);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[i] = (tu32x4){h[2 * i][0], h[2 * i][1], h[2 * i + 1][0], h[2 * i + 1][1]};
+            } else {
+                unsigned char* col = smem + Ly::vt + (32 * part) * tVS + 2 * key;
+#pragma unroll
+                for (int i = 0; i < 32; ++i)
+                    *reinterpret_cast<uint16_t*>(col + i * tVS) = (uint16_t)(h[i >> 2][(i >> 1) & 1] >> (16 * (i & 1)));
+            }
+        }
+    }
+    const int G = D / a.GS;
+    if (tid < tTile * tMaxGroups) {  // whole waves: the max below is a 32-lane butterfly
+        const int g = tid / tTile, key = tid - g * tTile;
+        const bool live = g < G;
+        const float s_k = elem_to_f32<DT>(r.meta[0]);
+        const float b_k = elem_to_f32<DT>(r.meta[1]);
+        const float s_v = elem_to_f32<DT>(r.meta[2]);
+        const float b_v = elem_to_f32<DT>(r.meta[3]);
+        float mx = live ? fabsf(s_v) : 0.f;
+#pragma unroll
+        for (int m = 1; m < 32; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+        int ex = 0;
+        if (mx > 0.f) (void)frexpf(mx, &ex);
+        const int F = (mx > 0.f) ? 15 - ex : 0;
+        if (live) {
+            float* f = reinterpret_cast<float*>(smem);
+            f[Ly::ksl / 4 + g * tTile + key] = s_k;
+            f[Ly::kbl / 4 + g * tTile + key] = b_k;
+            f[Ly::vsf / 4 + g * tTile + key] = ldexpf(s_v, F);
+            f[Ly::vbl / 4 + g * tTile + key] = b_v;
+            if (key == 0) f[Ly::vinv / 4 + g] = ldexpf(1.0f, -F);
+        }
+    }
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(tThreads) void attn_tile_kernel(TArgs a) {
+    using Ly = TileLds<D>;
+    constexpr int NC = D / 32;  // 32-dim chunks
+    constexpr int NB = D / 16;  // 16-column output blocks
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Ly::bytes];
+    float* fs = reinterpret_cast<float*>(smem);
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, n = lane & 15, j = lane >> 4;
+    const int bhr = blockIdx.x / a.S;
+    const int split = blockIdx.x - bhr * a.S;
+    const int bh = bhr / a.RBW;
+    const int r0 = tRows * (bhr - bh * a.RBW);
+    const int b = bh / a.Hkv;
+    const int kvh = bh - b * a.Hkv;
+    const int T = a.T;
+    const int G = D / a.GS;
+    const int cpg = a.GS / 32;  // chunks per group
+    const int npg = a.GS / 16;  // output blocks per group
+    const int64_t row0 = (int64_t)bh * a.capacity;
+    const int t_begin = split * a.chunk;
+    int t_end = t_begin + a.chunk;
+    if (t_end > T) t_end = T;
+    // keys past the last visible key of every row of the block are skipped
+    const int rlast = min(r0 + tRows, a.G) - 1;
+    int t_lim = t_end;
+    if (a.causal && a.mask == nullptr) {
+        const int i0 = r0 % a.L, i1 = rlast % a.L;
+        const int imax = (rlast - r0 + 1 >= a.L || i1 < i0) ? a.L - 1 : i1;
+        const int vmax = T - a.L + imax + 1;
+        if (t_lim > vmax) t_lim = vmax;
+    }
+
+    // first tile's words in flight during the set-up
+    TileRaw raw;
+    if (t_begin < t_lim) load_tile_raw<D>(a, row0, t_begin, tid, raw);
+
+    // ---- query operands: row 16 wave + n of the block, dims 32 c + 8 j + 0..7 ----
+    const int rowA = r0 + 16 * wave + n;
+    const bool wave_live = r0 + 16 * wave < a.G;
+    tf16x8 qh[NC], ql[NC];
+    {
+        float qv[NC][8];
+        const uint16_t* qrow = nullptr;
+        if (rowA < a.G) {
+            const int h = kvh * a.n_rep + rowA / a.L;
+            qrow = a.q + (((int64_t)b * a.Hkv * a.n_rep + h) * a.L + rowA % a.L) * D;
+        }
+        float mx = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if (qrow != nullptr) {
+                load4<DT>(qrow + 32 * c + 8 * j, x);
+                load4<DT>(qrow + 32 * c + 8 * j + 4, x + 4);
+            }
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                float y[4];
+                if (a.rot != nullptr) {
+                    float Bm[16];
+                    load_block(a.rot, 8 * c + 2 * j + hb, Bm);
+                    rotate4(x + 4 * hb, Bm, y);
+                    if (a.round_rot) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) y[e] = elem_to_f32<DT>(f32_to_elem_bits<DT>(y[e]));
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) y[e] = x[4 * hb + e];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    qv[c][4 * hb + e] = y[e] * a.qscale;
+                    mx = fmaxf(mx, fabsf(qv[c][4 * hb + e]));
+                }
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        int ex = 0;
+        if (mx > 0.f) (void)frexpf(mx, &ex);
+        const int E = (mx > 0.f) ? 15 - ex : 0;
+        float gsum[tMaxGroups];
+#pragma unroll
+        for (int g = 0; g < tMaxGroups; ++g) gsum[g] = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            float part = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xs = ldexpf(qv[c][e], E);
+                const _Float16 hi = (_Float16)xs;
+                qh[c][e] = hi;
+                ql[c][e] = (_Float16)(xs - (float)hi);
+                part += qv[c][e];
+            }
+            const int g = c / cpg;
+#pragma unroll
+            for (int gg = 0; gg < tMaxGroups; ++gg)
+                if (gg == g) gsum[gg] += part;
+        }
+#pragma unroll
+        for (int g = 0; g < tMaxGroups; ++g) {
+            float s = gsum[g];
+            s += __shfl_xor(s, 16);
+            s += __shfl_xor(s, 32);
+            if (j == 0 && g < G) fs[Ly::qst / 4 + (wave * tMaxGroups + g) * 16 + n] = s;
+        }
+        if (j == 0) fs[Ly::frw / 4 + wave * 16 + n] = ldexpf(1.0f, -E);
+    }
+
+    // ---- per-lane softmax rows (accumulator rows 4 j + i) ----
+    float frow[4], m_run[4], l_part[4];
+    int vis[4];
+    int64_t moff[4];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rr = 4 * j + i;
+        frow[i] = fs[Ly::frw / 4 + wave * 16 + rr];
+        m_run[i] = -INFINITY;
+        l_part[i] = 0.f;
+        const int R = r0 + 16 * wave + rr;
+        vis[i] = (R < a.G && a.causal) ? T - a.L + (R % a.L) + 1 : T;
+        moff[i] = -1;
+        if (R < a.G && a.mask != nullptr) {
+            const int h = kvh * a.n_rep + R / a.L;
+            moff[i] = (int64_t)b * a.msb + (int64_t)h * a.msh + (int64_t)(R % a.L) * a.msl;
+        }
+    }
+    const int esize = (a.mtype == 1) ? 1 : (a.mtype == 2) ? 4 : 2;
+    __amdgpu_buffer_rsrc_t mask_r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(a.mask != nullptr ? a.mask : (const void*)a.q), (short)0,
+        (int)a.mask_bytes, 0x00020000);
+
+    tf32x4 O[NB];
+#pragma unroll
+    for (int t = 0; t < NB; ++t) O[t] = (tf32x4){0.f, 0.f, 0.f, 0.f};
+    float ob[4][tMaxGroups];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g = 0; g < tMaxGroups; ++g) ob[i][g] = 0.f;
+
+    for (int t0 = t_begin; t0 < t_lim; t0 += tTile) {
+        __syncthreads();  // the previous tile's LDS reads are done
+        store_tile<DT, D>(a, tid, raw, smem);
+        __syncthreads();
+        if (t0 + tTile < t_lim) load_tile_raw<D>(a, row0, t0 + tTile, tid, raw);
+        if (!wave_live) continue;
+
+        // ---- scores ----
+        float sacc[2][4], bacc[2][4];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sacc[nb][i] = bacc[nb][i] = 0.f;
+        tf32x4 acc[2] = {(tf32x4){0.f, 0.f, 0.f, 0.f}, (tf32x4){0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const tf16x8 kb8 = *reinterpret_cast<const tf16x8*>(
+                    smem + Ly::kc + (16 * nb + n) * Ly::KS + 64 * c + 16 * j);
+                acc[nb] = tmfma(qh[c], kb8, acc[nb]);
+                acc[nb] = tmfma(ql[c], kb8, acc[nb]);
+            }
+            if ((c + 1) % cpg == 0) {  // group g complete
+                const int g = c / cpg;
+                const float s0 = fs[Ly::ksl / 4 + g * tTile + n], s1 = fs[Ly::ksl / 4 + g * tTile + 16 + n];
+                const float b0 = fs[Ly::kbl / 4 + g * tTile + n], b1 = fs[Ly::kbl / 4 + g * tTile + 16 + n];
+                const tf32x4 qs = *reinterpret_cast<const tf32x4*>(
+                    fs + Ly::qst / 4 + (wave * tMaxGroups + g) * 16 + 4 * j);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sacc[0][i] += s0 * acc[0][i];
+                    sacc[1][i] += s1 * acc[1][i];
+                    bacc[0][i] += b0 * qs[i];
+                    bacc[1][i] += b1 * qs[i];
+                }
+                acc[0] = acc[1] = (tf32x4){0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        float sc[2][4];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = t0 + 16 * nb + n;
+                float s = sacc[nb][i] * frow[i] + bacc[nb][i];
+                if (t >= t_end || t >= vis[i]) s = -INFINITY;
+                if (a.mtype != 0 && moff[i] >= 0 && s != -INFINITY) {
+                    const uint32_t off = (uint32_t)((moff[i] + t) * esize);
+                    if (a.mtype == 1) {
+                        if (__builtin_amdgcn_raw_buffer_load_b8(mask_r, off, 0, 0) == 0) s = -INFINITY;
+                    } else if (a.mtype == 2) {
+                        s += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mask_r, off, 0, 0)) * tLog2e;
+                    } else {
+                        s += elem_to_f32<DT>(__builtin_amdgcn_raw_buffer_load_b16(mask_r, off, 0, 0)) * tLog2e;
+                    }
+                }
+                sc[nb][i] = s;
+            }
+
+        // ---- online softmax (base 2) ----
+        float alpha[4], p[2][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float tmx = tmax16(fmaxf(sc[0][i], sc[1][i]));
+            const float m_new = fmaxf(m_run[i], tmx);
+            if (m_new == -INFINITY) {
+                alpha[i] = 1.f;
+                p[0][i] = p[1][i] = 0.f;
+            } else {
+                alpha[i] = exp2f(m_run[i] - m_new);
+                p[0][i] = exp2f(sc[0][i] - m_new);
+                p[1][i] = exp2f(sc[1][i] - m_new);
+            }
+            m_run[i] = m_new;
+            l_part[i] = l_part[i] * alpha[i] + (p[0][i] + p[1][i]);
+        }
+        // group biases: sum_t p_t b_{t,g}, per lane over its keys n, 16 + n
+#pragma unroll
+        for (int g = 0; g < tMaxGroups; ++g) {
+            if (g < G) {
+                const float v0 = fs[Ly::vbl / 4 + g * tTile + n], v1 = fs[Ly::vbl / 4 + g * tTile + 16 + n];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ob[i][g] = ob[i][g] * alpha[i] + (p[0][i] * v0 + p[1][i] * v1);
+            }
+        }
+        // P to the operand layout (row n, keys 8 j .. 8 j + 7) through LDS
+        float* pw = fs + Ly::pst / 4 + wave * 16 * tPS;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pw[(4 * j + i) * tPS + 16 * nb + n] = p[nb][i];
+        __builtin_amdgcn_wave_barrier();
+        const tf32x4 pa0 = *reinterpret_cast<const tf32x4*>(pw + n * tPS + 8 * j);
+        const tf32x4 pa1 = *reinterpret_cast<const tf32x4*>(pw + n * tPS + 8 * j + 4);
+
+        // ---- P V ----
+        tf16x8 ph, pl;
+        float vi = 1.f;
+#pragma unroll
+        for (int nb2 = 0; nb2 < NB; ++nb2) {
+            if (nb2 % npg == 0) {  // first output block of group g: its P' operands
+                const int g = nb2 / npg;
+                const tf32x4 x0 = *reinterpret_cast<const tf32x4*>(fs + Ly::vsf / 4 + g * tTile + 8 * j);
+                const tf32x4 x1 = *reinterpret_cast<const tf32x4*>(fs + Ly::vsf / 4 + g * tTile + 8 * j + 4);
+                vi = fs[Ly::vinv / 4 + g];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float y0 = pa0[e] * x0[e], y1 = pa1[e] * x1[e];
+                    const _Float16 h0 = (_Float16)y0, h1 = (_Float16)y1;
+                    ph[e] = h0;
+                    ph[4 + e] = h1;
+                    pl[e] = (_Float16)(y0 - (float)h0);
+                    pl[4 + e] = (_Float16)(y1 - (float)h1);
+                }
+            }
+            const tf16x8 vb8 = *reinterpret_cast<const tf16x8*>(smem + Ly::vt + (16 * nb2 + n) * tVS + 16 * j);
+            tf32x4 pv = tmfma(ph, vb8, (tf32x4){0.f, 0.f, 0.f, 0.f});
+            pv = tmfma(pl, vb8, pv);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) O[nb2][i] = O[nb2][i] * alpha[i] + pv[i] * vi;
+        }
+    }
+
+    // ---- record: (m, l) and the unnormalised o of each row ----
+    if (!wave_live) return;
+    const int64_t unit = (int64_t)bhr * a.S + split;
+    float* ro = a.rec_o + unit * tRows * D;
+    float* rml = a.rec_ml + unit * tRows * 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rr = 16 * wave + 4 * j + i;
+        const float l = tsum16(l_part[i]);
+        float obs[tMaxGroups];
+#pragma unroll
+        for (int g = 0; g < tMaxGroups; ++g) obs[g] = (g < G) ? tsum16(ob[i][g]) : 0.f;
+#pragma unroll
+        for (int nb2 = 0; nb2 < NB; ++nb2) {
+            const int g = nb2 / npg;
+            float bias = 0.f;
+#pragma unroll
+            for (int gg = 0; gg < tMaxGroups; ++gg)
+                if (gg == g) bias = obs[gg];
+            ro[rr * D + 16 * nb2 + n] = O[nb2][i] + bias;
+        }
+        if (n == 0) {
+            rml[2 * rr] = m_run[i];
+            rml[2 * rr + 1] = l;
+        }
+    }
+}
+
+struct TMArgs {
+    const float* rec_o;
+    const float* rec_ml;
+    const float* rot;
+    float* out;
+    int S, Hkv, n_rep, L, G, RBW;
+};
+
+// Merge of the key-split records of one query row (64 threads, 4 columns
+// each): m* = max_s m_s, l* = sum_s l_s 2^(m_s - m*), o = sum_s o_s 2^(m_s - m*) / l*,
+// in split order; then the inverse rotation of each 4-column block and the
+// fp32 store.
+template <int D>
+__global__ __launch_bounds__(64) void attn_tile_merge_kernel(TMArgs a) {
+    const int rowg = blockIdx.x;  // (b, kv head, row block, row)
+    const int rr = rowg % tRows;
+    const int bhr = rowg / tRows;
+    const int bh = bhr / a.RBW;
+    const int R = tRows * (bhr - bh * a.RBW) + rr;
+    if (R >= a.G) return;
+    const int k = threadIdx.x;
+    if (k >= D / 4) return;
+    const int b = bh / a.Hkv, kvh = bh - b * a.Hkv;
+    float M = -INFINITY;
+    for (int s = 0; s < a.S; ++s) M = fmaxf(M, a.rec_ml[((int64_t)bhr * a.S + s) * tRows * 2 + 2 * rr]);
+    float Ls = 0.f;
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < a.S; ++s) {
+        const int64_t u = (int64_t)bhr * a.S + s;
+        const float m = a.rec_ml[u * tRows * 2 + 2 * rr];
+        if (m == -INFINITY) continue;
+        const float w = exp2f(m - M);
+        Ls += a.rec_ml[u * tRows * 2 + 2 * rr + 1] * w;
+        const float4 v = *reinterpret_cast<const float4*>(a.rec_o + (u * tRows + rr) * D + 4 * k);
+        o[0] += v.x * w;
+        o[1] += v.y * w;
+        o[2] += v.z * w;
+        o[3] += v.w * w;
+    }
+    const float inv = 1.0f / Ls;
+    float y[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+    float z[4] = {y[0], y[1], y[2], y[3]};
+    if (a.rot != nullptr) {
+        float Bm[16];
+        load_block(a.rot, k, Bm);
+        unrotate4(y, Bm, z);
+    }
+    const int hq = kvh * a.n_rep + R / a.L;
+    float* dst = a.out + (((int64_t)b * a.Hkv * a.n_rep + hq) * a.L + R % a.L) * D + 4 * k;
+    *reinterpret_cast<float4*>(dst) = make_float4(z[0], z[1], z[2], z[3]);
+}
+
+}  // namespace
+
+int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, TilePlan* p) {
+    const int64_t G = (int64_t)(H_q / c->H_kv) * L;
+    const int64_t RBW = (G + tRows - 1) / tRows;
+    const int64_t T = c->offset;
+    const int64_t units = (int64_t)c->B * c->H_kv * RBW;
+    int64_t S = splits;
+    if (S == 0) {
+        S = (1024 + units - 1) / units;  // about four workgroups per compute unit
+        const int64_t max_s = (T + tTile - 1) / tTile;
+        if (S > max_s) S = max_s;
+    }
+    if (S < 1) S = 1;
+    int64_t chunk = (T + S - 1) / S;
+    chunk = (chunk + tTile - 1) / tTile * tTile;
+    S = (T + chunk - 1) / chunk;
+    if (units * S > 0x7FFFFFFF || units * tRows > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
+    p->S = (int)S;
+    p->RBW = (int)RBW;
+    p->chunk = chunk;
+    p->o_floats = (size_t)(units * S) * tRows * c->head_dim;
+    p->ws_bytes = (p->o_floats + (size_t)(units * S) * tRows * 2) * sizeof(float);
+    return RBQ_OK;
+}
+
+int tile_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, float scale,
+                int32_t causal, const AttnMask& mk, const float* rot_blocks, float* out,
+                const TilePlan& p, void* ws, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    TArgs a;
+    a.q = (const uint16_t*)q;
+    a.kw = c->k_words;
+    a.ks = (const uint16_t*)c->k_scales;
+    a.kb = (const uint16_t*)c->k_biases;
+    a.vw = c->v_words;
+    a.vs = (const uint16_t*)c->v_scales;
+    a.vb = (const uint16_t*)c->v_biases;
+    a.rot = rot_blocks;
+    a.rec_o = (float*)ws;
+    a.rec_ml = (float*)ws + p.o_floats;
+    a.capacity = c->capacity;
+    a.T = (int)c->offset;
+    a.chunk = (int)p.chunk;
+    a.S = p.S;
+    a.Hkv = c->H_kv;
+    a.n_rep = H_q / c->H_kv;
+    a.L = L;
+    a.G = a.n_rep * L;
+    a.RBW = p.RBW;
+    a.causal = causal ? 1 : 0;
+    a.round_rot = (c->flags & RBQ_FLAG_ROUND_ROTATED) ? 1 : 0;
+    a.GS = c->group_size;
+    a.kbits = c->k_bits;
+    a.vbits = c->v_bits;
+    a.qscale = scale * tLog2e;
+    a.mask = mk.ptr;
+    a.msb = mk.sb;
+    a.msh = mk.sh;
+    a.msl = mk.sl;
+    a.mask_bytes = mk.bytes;
+    a.mtype = mk.ptr == nullptr ? 0 : mk.type;
+    const int64_t units = (int64_t)c->B * c->H_kv * p.RBW;
+    const dim3 grid((unsigned)(units * p.S)), block(tThreads);
+    auto launch = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, s, a); };
+    const bool bf = c->dtype == RBQ_BF16;
+    switch (c->head_dim) {
+        case 64: bf ? launch(attn_tile_kernel<RBQ_BF16, 64>) : launch(attn_tile_kernel<RBQ_F16, 64>); break;
+        case 128: bf ? launch(attn_tile_kernel<RBQ_BF16, 128>) : launch(attn_tile_kernel<RBQ_F16, 128>); break;
+        default: bf ? launch(attn_tile_kernel<RBQ_BF16, 256>) : launch(attn_tile_kernel<RBQ_F16, 256>); break;
+    }
+    TMArgs m;
+    m.rec_o = a.rec_o;
+    m.rec_ml = a.rec_ml;
+    m.rot = rot_blocks;
+    m.out = out;
+    m.S = p.S;
+    m.Hkv = a.Hkv;
+    m.n_rep = a.n_rep;
+    m.L = L;
+    m.G = a.G;
+    m.RBW = p.RBW;
+    const dim3 mgrid((unsigned)(units * tRows)), mblock(64);
+    switch (c->head_dim) {
+        case 64: hipLaunchKernelGGL(attn_tile_merge_kernel<64>, mgrid, mblock, 0, s, m); break;
+        case 128: hipLaunchKernelGGL(attn_tile_merge_kernel<128>, mgrid, mblock, 0, s, m); break;
+        default: hipLaunchKernelGGL(attn_tile_merge_kernel<256>, mgrid, mblock, 0, s, m); break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        set_hip_error((int)e);
+        return RBQ_EHIP;
+    }
+    return RBQ_OK;
+}
+
+}  // namespace rbq

@@ -20,11 +20,13 @@ void set_hip_error(int err) { g_last_hip_error = err; }
 int check_cache(const rbq_kv_cache* c) {
     if (c == nullptr) return RBQ_EINVAL;
     if (c->B <= 0 || c->H_kv <= 0 || c->capacity < 0 || c->offset < 0 ||
-        c->offset > c->capacity || c->reserved != 0)
+        c->offset > c->capacity || (c->flags & ~RBQ_FLAG_ROUND_ROTATED) != 0)
         return RBQ_EINVAL;
-    if (c->head_dim != kHeadDim || c->group_size != kGroup || c->k_bits != kKBits ||
-        c->v_bits != kVBits)
-        return RBQ_EUNSUPPORTED;
+    auto width_ok = [](int b) { return b == 2 || b == 3 || b == 4 || b == 5 || b == 6 || b == 8; };
+    if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return RBQ_EUNSUPPORTED;
+    if (c->group_size != 32 && c->group_size != 64 && c->group_size != 128) return RBQ_EUNSUPPORTED;
+    if (c->head_dim % c->group_size != 0) return RBQ_EUNSUPPORTED;
+    if (!width_ok(c->k_bits) || !width_ok(c->v_bits)) return RBQ_EUNSUPPORTED;
     if (c->dtype != RBQ_F16 && c->dtype != RBQ_BF16) return RBQ_EUNSUPPORTED;
     if (c->capacity > 0 &&
         (c->k_words == nullptr || c->k_scales == nullptr || c->k_biases == nullptr ||
@@ -55,6 +57,18 @@ void quat_right_conj(const double q[4], double m[4][4]) {
     memcpy(m, rows, sizeof(rows));
 }
 
+// Matrix of v -> v * conj(q) for quaternions as column vectors (w, x, y, z):
+// the map the _quat_right_conj docstring on the same page describes.  With
+// p = conj(q) = (w, -x, -y, -z), the Hamilton product v * p has components
+// (v0 p0 - v1 p1 - v2 p2 - v3 p3, v0 p1 + v1 p0 + v2 p3 - v3 p2,
+//  v0 p2 - v1 p3 + v2 p0 + v3 p1, v0 p3 + v1 p2 - v2 p1 + v3 p0).
+void quat_right_mul_conj(const double q[4], double m[4][4]) {
+    const double p0 = q[0], p1 = -q[1], p2 = -q[2], p3 = -q[3];
+    const double rows[4][4] = {{p0, -p1, -p2, -p3}, {p1, p0, p3, -p2}, {p2, -p3, p0, p1},
+                               {p3, p2, -p1, p0}};
+    memcpy(m, rows, sizeof(rows));
+}
+
 // q = a / |a| in double: squares summed left to right, correctly rounded
 // sqrt and divisions.  Returns false for a zero vector.
 bool normalize(const float a[4], double q[4]) {
@@ -77,15 +91,21 @@ bool normalize(const float a[4], double q[4]) {
 extern "C" {
 
 int rbq_rotation_build(const float* draws, int32_t head_dim, float* blocks) {
+    return rbq_rotation_build_mode(draws, head_dim, RBQ_ROT_PRINTED, blocks);
+}
+
+int rbq_rotation_build_mode(const float* draws, int32_t head_dim, int32_t mode, float* blocks) {
     if (draws == nullptr || blocks == nullptr || head_dim <= 0 || head_dim % 4 != 0)
         return RBQ_EINVAL;
+    if (mode != RBQ_ROT_PRINTED && mode != RBQ_ROT_TWO_SIDED) return RBQ_EINVAL;
     const int nb = head_dim / 4;
     for (int b = 0; b < nb; ++b) {
         double qL[4], qR[4], Lm[4][4], Rm[4][4];
         if (!normalize(draws + b * 8, qL) || !normalize(draws + b * 8 + 4, qR))
             return RBQ_EINVAL;
         quat_left(qL, Lm);
-        quat_right_conj(qR, Rm);
+        if (mode == RBQ_ROT_PRINTED) quat_right_conj(qR, Rm);
+        else quat_right_mul_conj(qR, Rm);
         float* out = blocks + b * 16;
         for (int i = 0; i < 4; ++i) {
             for (int j = 0; j < 4; ++j) {

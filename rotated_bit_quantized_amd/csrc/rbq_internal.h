@@ -21,9 +21,26 @@ constexpr int kGroups = kHeadDim / kGroup;        // 4
 void set_hip_error(int err);
 
 // Validates the descriptor fields shared by every device entry point:
-// non-null buffers, positive B/H_kv, 0 <= offset <= capacity, reserved == 0,
-// and the supported configuration (RBQ_EUNSUPPORTED otherwise).
+// non-null buffers, positive B/H_kv, 0 <= offset <= capacity, known flags,
+// and a supported configuration (RBQ_EUNSUPPORTED otherwise).
 int check_cache(const rbq_kv_cache* c);
+
+// True for the configuration with dedicated kernels: head_dim 256, group 64,
+// K 4-bit, V 3-bit.
+inline bool is_default_config(const rbq_kv_cache* c) {
+    return c->head_dim == kHeadDim && c->group_size == kGroup && c->k_bits == kKBits &&
+           c->v_bits == kVBits;
+}
+
+// Row sizes of the six arrays in 16-bit units (a scale or bias row of one
+// group is a single 16-bit element).
+struct RowUnits {
+    int kw, meta, vw;  // K words, each scale / bias array, V words
+};
+inline RowUnits row_units(const rbq_kv_cache* c) {
+    return {c->head_dim * c->k_bits / 16, c->head_dim / c->group_size,
+            c->head_dim * c->v_bits / 16};
+}
 
 // Launch plan of the matrix-core attention path: key splits, their length,
 // blocks of 8 query rows, and the workspace for the split records.
@@ -43,6 +60,26 @@ struct MfmaPlan {
     size_t ws_bytes;
 };
 int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, MfmaPlan* p);
+
+// Launch plan of the general tile attention (every configuration, any number
+// of query rows): key splits, blocks of 64 query rows, and the workspace of
+// the split records (o floats, then (m, l) pairs).
+struct TilePlan {
+    int S;
+    int RBW;
+    int64_t chunk;
+    size_t o_floats;
+    size_t ws_bytes;
+};
+int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, TilePlan* p);
+int tile_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, float scale,
+                int32_t causal, const AttnMask& mk, const float* rot_blocks, float* out,
+                const TilePlan& p, void* ws, void* stream);
+
+// Largest number of query rows per kv head (H_q / H_kv x L) that the
+// dedicated default-configuration kernel takes; larger blocks (and every
+// other configuration) run the tile kernel.
+constexpr int kDedicatedMaxRows = 32;
 int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, float scale,
                 int32_t causal, const AttnMask& mk, const float* rot_blocks, float* out,
                 const MfmaPlan& p, void* ws, void* stream);

@@ -64,6 +64,19 @@ def test_rotation_build_other_head_dims_and_errors():
     assert capi.library().rbq_rotation_build(d.ctypes.data, 6, out.ctypes.data) == capi.RBQ_EINVAL
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_rotation_build_two_sided_bit_exact_vs_oracle(D):
+    draws = W.rotation_draws(7, D)
+    got = capi.rbq_rotation_build_mode(draws, capi.RBQ_ROT_TWO_SIDED)
+    np.testing.assert_array_equal(got, O.rotation_blocks(draws, mode="two_sided"))
+    np.testing.assert_array_equal(capi.rbq_rotation_build_mode(draws, capi.RBQ_ROT_PRINTED),
+                                  capi.rbq_rotation_build(draws))
+    d = np.ascontiguousarray(draws)
+    out = np.empty((D // 4, 4, 4), np.float32)
+    assert capi.library().rbq_rotation_build_mode(d.ctypes.data, D, 2, out.ctypes.data) == \
+        capi.RBQ_EINVAL
+
+
 def test_required_capacity_matches_oracle():
     for cap in (0, 256, 512, 8192, 10240, 10496):
         for off in sorted({0, 1, cap // 2, max(cap - 1, 0), cap, 255, 257}):
@@ -81,7 +94,7 @@ def test_required_capacity_matches_oracle():
 
 def _host_desc(B=1, H=1, cap=0, off=0, dtype=capi.RBQ_BF16, **kw):
     d = capi.rbq_kv_cache(B=B, H_kv=H, head_dim=256, group_size=64, k_bits=4, v_bits=3,
-                          dtype=dtype, reserved=0, capacity=cap, offset=off)
+                          dtype=dtype, flags=0, capacity=cap, offset=off)
     for k, v in kw.items():
         setattr(d, k, v)
     return d
@@ -129,15 +142,25 @@ def test_device_entry_points_validate_before_any_device_work():
     assert lib.rbq_kv_quant_append(by(d), None, fake, 1, None, None) == capi.RBQ_EINVAL
     assert lib.rbq_kv_quant_append(by(d), fake, fake, 0, None, None) == capi.RBQ_OK
     # unsupported configurations
-    for field, val in (("head_dim", 128), ("group_size", 32), ("k_bits", 8), ("v_bits", 4),
+    for field, val in (("head_dim", 96), ("head_dim", 512), ("group_size", 16),
+                       ("group_size", 256), ("k_bits", 7), ("k_bits", 1), ("v_bits", 16),
                        ("dtype", 7)):
         e = _host_desc(B=1, H=2, cap=256, off=100, **ptrs)
         setattr(e, field, val)
         assert lib.rbq_kv_quant_append(by(e), fake, fake, 1, None, None) == \
-            capi.RBQ_EUNSUPPORTED, field
+            capi.RBQ_EUNSUPPORTED, (field, val)
+    e = _host_desc(B=1, H=2, cap=256, off=100, head_dim=64, group_size=128, **ptrs)
+    assert lib.rbq_kv_quant_append(by(e), fake, fake, 1, None, None) == capi.RBQ_EUNSUPPORTED
+    # supported variants pass validation (here they stop at the capacity check)
+    for hd, gs, kb, vb in ((64, 32, 2, 8), (128, 64, 5, 6), (256, 128, 8, 2), (64, 64, 3, 3)):
+        e = _host_desc(B=1, H=2, cap=256, off=100, head_dim=hd, group_size=gs, k_bits=kb,
+                       v_bits=vb, **ptrs)
+        assert lib.rbq_kv_quant_append(by(e), fake, fake, 157, None, None) == capi.RBQ_ECAPACITY
     e = _host_desc(B=1, H=2, cap=256, off=100, **ptrs)
-    e.reserved = 1
+    e.flags = 2
     assert lib.rbq_kv_quant_append(by(e), fake, fake, 1, None, None) == capi.RBQ_EINVAL
+    e.flags = capi.RBQ_FLAG_ROUND_ROTATED
+    assert lib.rbq_kv_quant_append(by(e), fake, fake, 157, None, None) == capi.RBQ_ECAPACITY
     e = _host_desc(B=1, H=2, cap=256, off=300, **ptrs)
     assert lib.rbq_kv_quant_append(by(e), fake, fake, 1, None, None) == capi.RBQ_EINVAL
     # attention: H_q % H_kv, L range, splits < 0, null q/out, workspace

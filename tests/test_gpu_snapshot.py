@@ -138,7 +138,7 @@ def _raw_cache(B, H, cap, off, dtype=torch.bfloat16, seed=0):
         arrs[name] = torch.randint(-2**31, 2**31 - 1, (B, H, cap, w), dtype=torch.int32,
                                    generator=gen).to(dev)
     d = capi.rbq_kv_cache(B=B, H_kv=H, head_dim=256, group_size=64, k_bits=4, v_bits=3,
-                          dtype=capi.DTYPE_CODES[dtype], reserved=0, capacity=cap, offset=off)
+                          dtype=capi.DTYPE_CODES[dtype], flags=0, capacity=cap, offset=off)
     for name, t in arrs.items():
         setattr(d, name, t.data_ptr())
     return d, arrs

@@ -1,0 +1,189 @@
+"""GPU parity of the configuration variants through the C ABI: head_dim 64 /
+128 / 256, group 32 / 64 / 128, K and V widths 2-8, the two-sided rotation
+and the page's own rotation precision (packed words, scales and biases bit
+for bit against the oracle; attention within 2e-3), the general tile
+attention kernel on long query blocks (prefill-length L) for the default
+configuration, masks and key splits on the tile kernel, and the prefix copy
+of variant caches.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import rbq_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+rbq = pytest.importorskip("rotated_bit_quantized_amd")
+from rotated_bit_quantized_amd import capi  # noqa: E402
+
+NAMES = (("k_words", "kw"), ("k_scales", "ks"), ("k_biases", "kb"),
+         ("v_words", "vw"), ("v_scales", "vs"), ("v_biases", "vb"))
+
+# head_dim, group, k_bits, v_bits, dtype, two-sided rotation, round_rotated
+VARIANTS = [
+    (64, 32, 2, 8, "f16", False, False),
+    (128, 64, 5, 6, "bf16", True, False),
+    (256, 128, 8, 2, "bf16", False, True),
+    (128, 128, 3, 4, "f16", False, True),
+    (256, 32, 6, 5, "bf16", True, False),
+    (64, 64, 4, 3, "bf16", False, False),
+    (256, 64, 4, 3, "bf16", True, True),   # default sizes, dedicated kernels, both options
+    (256, 64, 4, 3, "f16", False, True),
+]
+
+
+def _vid(v):
+    return "D{}_g{}_k{}v{}_{}{}{}".format(v[0], v[1], v[2], v[3], v[4], "_2s" if v[5] else "",
+                                         "_rr" if v[6] else "")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return torch.device("cuda:0")
+
+
+def _setup(var, dev, B, Hkv, T, seed, chunks=(0.6,)):
+    D, gs, kb, vb, dtype, two, rr = var
+    tdt = W._TORCH_DTYPES[dtype]
+    draws = W.rotation_draws(seed, D)
+    blocks = O.rotation_blocks(draws, mode="two_sided" if two else "printed")
+    if rr:
+        blocks = O.round_to_dtype(blocks, dtype)
+    rot = rbq.build_block_so4(D, seed, dev, two_sided=two, round_to=tdt if rr else None)
+    np.testing.assert_array_equal(rot.cpu().numpy(), blocks)
+    c = rbq.RotatedQuantKVCache(B, Hkv, dtype=tdt, device=dev, rot=rot, head_dim=D,
+                                group_size=gs, k_bits=kb, v_bits=vb, round_rotated=rr)
+    oc = O.QuantKVCache(k_bits=kb, v_bits=vb, dtype=dtype, group=gs, round_rotated=rr)
+    k = W.random_rows([seed, 1], (B, Hkv, T, D), dtype, "student_t3")
+    v = W.random_rows([seed, 2], (B, Hkv, T, D), dtype)
+    cut = [0] + [int(f * T) for f in chunks] + [T]
+    for a, b in zip(cut[:-1], cut[1:]):
+        c.append(k[:, :, a:b].contiguous().to(dev), v[:, :, a:b].contiguous().to(dev))
+        oc.append(k[:, :, a:b].float().numpy(), v[:, :, a:b].float().numpy(), blocks)
+    return c, oc, blocks, rot
+
+
+def _assert_cache_equal(c, oc):
+    torch.cuda.synchronize()
+    assert (c.offset, c.capacity) == (oc.offset, oc.capacity)
+    rows = c.rows()
+    for name, oname in NAMES:
+        got = rows[name].cpu()
+        got = got.numpy().view(np.uint32) if "words" in name else got.float().numpy()
+        ref = oc.arrays[oname][:, :, :oc.offset]
+        assert got.shape == ref.shape, name
+        bad = np.argwhere(got != ref)
+        assert bad.size == 0, f"{name}: {len(bad)} mismatches, first at {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("var", VARIANTS, ids=_vid)
+def test_variant_append_bit_exact(var, dev):
+    print(f"[variant append] {_vid(var)}", flush=True)
+    c, oc, _, _ = _setup(var, dev, 2, 2, 301, 11, chunks=(0.3, 0.61))
+    _assert_cache_equal(c, oc)
+
+
+@pytest.mark.parametrize("var", VARIANTS, ids=_vid)
+def test_variant_attention(var, dev):
+    print(f"[variant attention] {_vid(var)}", flush=True)
+    D = var[0]
+    B, Hq, Hkv, T = 2, 8, 2, 333
+    c, oc, blocks, _ = _setup(var, dev, B, Hkv, T, 12)
+    for L, causal in ((1, True), (3, True), (5, False)):
+        q = W.random_rows([13, L], (B, Hq, L, D), var[4])
+        out = c.attend(q.to(dev), scale=D ** -0.5, causal=causal)
+        torch.cuda.synchronize()
+        ref = O.attention(q.float().numpy(), oc, D ** -0.5, causal, blocks)
+        err = float(np.abs(out.cpu().numpy() - ref).max())
+        assert err <= ATOL, (L, causal, err)
+
+
+@pytest.mark.parametrize("L", [70, 129])
+def test_tile_kernel_long_query_blocks(L, dev):
+    # prefill-length query blocks of the default configuration: G = 8 L rows
+    # per kv head run the tile kernel (several 64-row blocks, a ragged last one)
+    var = (256, 64, 4, 3, "bf16", False, False)
+    print(f"[tile long block] L={L}", flush=True)
+    B, Hq, Hkv, T = 1, 16, 2, 700
+    c, oc, blocks, _ = _setup(var, dev, B, Hkv, T, 14)
+    q = W.random_rows([15, L], (B, Hq, L, 256), "bf16")
+    out = c.attend(q.to(dev), scale=1 / 16, causal=True)
+    torch.cuda.synchronize()
+    ref = O.attention(q.float().numpy(), oc, 1 / 16, True, blocks)
+    err = float(np.abs(out.cpu().numpy() - ref).max())
+    assert err <= ATOL, err
+    # row 0 of the block is an L = 1 decode over the keys it sees (run by the
+    # dedicated kernel: the two kernels round differently, both within the
+    # tolerance of the oracle)
+    c.trim(L - 1)
+    oc.trim(L - 1)
+    q1 = q[:, :, :1].contiguous()
+    out1 = c.attend(q1.to(dev), scale=1 / 16, causal=True)
+    torch.cuda.synchronize()
+    ref1 = O.attention(q1.float().numpy(), oc, 1 / 16, True, blocks)
+    np.testing.assert_allclose(ref1, ref[:, :, :1], rtol=0, atol=1e-9)
+    err1 = float(np.abs(out1.cpu().numpy() - ref1).max())
+    cross = float(np.abs(out1.cpu().numpy() - out[:, :, :1].cpu().numpy()).max())
+    print(f"tile kernel error {err:.2e}, dedicated kernel {err1:.2e}, between them {cross:.2e}")
+    assert err1 <= ATOL and cross <= ATOL
+
+
+def test_tile_kernel_splits_agree(dev):
+    var = (128, 64, 5, 6, "bf16", True, False)
+    B, Hq, Hkv, T, L = 1, 4, 1, 2000, 2
+    c, oc, blocks, _ = _setup(var, dev, B, Hkv, T, 16)
+    q = W.random_rows([17, L], (B, Hq, L, 128), "bf16").to(dev)
+    outs = []
+    for S in (1, 3, 7, 63):
+        outs.append(c.attend(q, scale=128 ** -0.5, causal=True, splits=S))
+    torch.cuda.synchronize()
+    ref = O.attention(q.cpu().float().numpy(), oc, 128 ** -0.5, True, blocks)
+    for o in outs:
+        assert float(np.abs(o.cpu().numpy() - ref).max()) <= ATOL
+        assert float(np.abs(o.cpu().numpy() - outs[0].cpu().numpy()).max()) <= 1e-5
+
+
+@pytest.mark.parametrize("kind", ["bool", "f32", "dtype"])
+def test_tile_kernel_masks(kind, dev):
+    var = (64, 32, 2, 8, "f16", False, False)
+    B, Hq, Hkv, T, L = 2, 4, 2, 200, 3
+    c, oc, blocks, _ = _setup(var, dev, B, Hkv, T, 18)
+    q = W.random_rows([19, L], (B, Hq, L, 64), "f16")
+    g = np.random.default_rng(20)
+    if kind == "bool":
+        m = g.random((B, 1, L, T)) < 0.7
+        m[..., 0] = True
+        mask = torch.from_numpy(m)
+        ref_mask = m
+    else:
+        m = (g.standard_normal((1, Hq, L, T)) * 2).astype(np.float32)
+        mask = torch.from_numpy(m).to(torch.float16 if kind == "dtype" else torch.float32)
+        ref_mask = mask.float().numpy().astype(np.float64)
+    out = c.attend(q.to(dev), scale=0.125, causal=True, mask=mask.to(dev))
+    torch.cuda.synchronize()
+    ref = O.attention(q.float().numpy(), oc, 0.125, True, blocks, mask=ref_mask)
+    assert float(np.abs(out.cpu().numpy() - ref).max()) <= ATOL
+
+
+@pytest.mark.parametrize("var", [VARIANTS[0], VARIANTS[5], VARIANTS[2]], ids=_vid)
+def test_variant_snapshot_restore_and_tile(var, dev):
+    # prefix copies move 16-bit units: one-group rows (head_dim 64, group 64)
+    # are 2 bytes per scale row
+    c, oc, _, _ = _setup(var, dev, 2, 1, 77, 21)
+    snap = c.snapshot()
+    k = W.random_rows([22, 1], (2, 1, 5, var[0]), var[4]).to(dev)
+    c.append(k, k)
+    c.restore(snap)
+    _assert_cache_equal(c, oc)
+    c1, oc1, _, _ = _setup(var, dev, 1, 2, 45, 23)
+    c1.tile(3)
+    O.tile_cache(oc1, 3)
+    torch.cuda.synchronize()
+    rows = c1.rows()
+    for name, oname in NAMES:
+        got = rows[name].cpu()
+        got = got.numpy().view(np.uint32) if "words" in name else got.float().numpy()
+        np.testing.assert_array_equal(got, oc1.arrays[oname][:, :, :oc1.offset])
