@@ -207,6 +207,114 @@ def tree_verify(rbq, W, dev, rot, n_calls: int = 200) -> dict:
     }
 
 
+def prefill(rbq, W, dev, rot, n_calls: int = 10) -> dict:
+    """Prefill-length attention over the quantized cache: B=1, 16 q heads /
+    2 kv heads, head_dim 256, bf16, K4/V3 group 64; a cache of 8192 tokens,
+    a chunk of L = 2048 new tokens appended (rotated, quantized, packed), then
+    the fused attention of the chunk's 2048 query rows per head over the
+    10240 cached tokens with the causal mask at the offset (the general tile
+    kernel: 256 blocks of 64 query rows).  Algorithmic flops: 4 * head_dim
+    per (query row, visible key) (q.k and p.v, multiply-add = 2)."""
+    Hkv, Hq, T0, L, D = 2, 16, 8192, 2048, 256
+    k = W.random_rows([50, 1], (1, Hkv, T0, D), "bf16").to(dev)
+    v = W.random_rows([50, 2], (1, Hkv, T0, D), "bf16").to(dev)
+    kn = W.random_rows([50, 3], (1, Hkv, L, D), "bf16").to(dev)
+    vn = W.random_rows([50, 4], (1, Hkv, L, D), "bf16").to(dev)
+    q = W.random_rows([50, 5], (1, Hq, L, D), "bf16").to(dev)
+    c = rbq.RotatedQuantKVCache(1, Hkv, device=dev, rot=rot)
+    c.append(k, v)
+    c.reserve(L)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the chunk's append, timed on its own (append then trim, repeatedly)
+    for _ in range(3):
+        c.append(kn, vn)
+        c.trim(L)
+    ev0.record(stream)
+    for _ in range(n_calls):
+        c.append(kn, vn)
+        c.trim(L)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    append_us = ev0.elapsed_time(ev1) * 1e3 / n_calls
+    c.append(kn, vn)
+    T = T0 + L
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    ws = c.workspace(Hq, L)
+    for _ in range(2):
+        rbq.rbq_quant_attn_decode(c.desc, q, 1 / 16, True, rot, out, 0, ws)
+    ev0.record(stream)
+    for _ in range(n_calls):
+        rbq.rbq_quant_attn_decode(c.desc, q, 1 / 16, True, rot, out, 0, ws)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / n_calls
+    pairs = Hq * (L * (T - L) + L * (L + 1) // 2)  # (query row, visible key) pairs
+    flops = 4 * D * pairs
+    tfs = flops / (us * 1e-6) / 1e12
+    return {
+        "what": f"prefill chunk: {L} new tokens over {T0} cached (T={T}), B=1, {Hq}/{Hkv} heads, "
+                "head_dim 256, bf16, K4/V3 group 64, causal at the offset (tile kernel)",
+        "bound": "mfma",
+        "alg_flops_per_call": flops,
+        "avg_us": round(us, 2),
+        "achieved": round(tfs, 2),
+        "peak": 2500.0,
+        "unit": "TFLOP/s",
+        "frac": round(tfs / 2500.0, 4),
+        "note": "fp16 MFMA issued per algorithmic flop: 2 (query and probability operands "
+                "split hi + lo); the dense fp16 peak is the reference",
+        "tokens_per_s": round(L / (us * 1e-6), 1),
+        "append_chunk_us": round(append_us, 2),
+    }
+
+
+def variant_decode(rbq, W, dev, n_calls: int = 200) -> dict:
+    """Decode over a cache of another configuration (the general kernels):
+    B=8, 16 q heads / 2 kv heads, head_dim 128, group 64, K 4-bit / V 4-bit,
+    two-sided rotation, T=32768, bf16; 5 cache replicas (about 380 MB) cycled
+    so that the Infinity Cache cannot serve a call."""
+    B, Hkv, Hq, T, D, gs, kb, vb = 8, 2, 16, 32768, 128, 64, 4, 4
+    rot = rbq.build_block_so4(D, 0, dev, two_sided=True)
+    k = W.random_rows([60, 1], (B, Hkv, T, D), "bf16").to(dev)
+    v = W.random_rows([60, 2], (B, Hkv, T, D), "bf16").to(dev)
+    caches = []
+    for _ in range(5):
+        c = rbq.RotatedQuantKVCache(B, Hkv, device=dev, rot=rot, head_dim=D, group_size=gs,
+                                    k_bits=kb, v_bits=vb)
+        c.append(k, v)
+        caches.append(c)
+    del k, v
+    q = W.random_rows([60, 3], (B, Hq, 1, D), "bf16").to(dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    ws = caches[0].workspace(Hq, 1)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(20):
+        rbq.rbq_quant_attn_decode(caches[i % 5].desc, q, D ** -0.5, True, rot, out, 0, ws)
+    ev0.record(stream)
+    for i in range(n_calls):
+        rbq.rbq_quant_attn_decode(caches[i % 5].desc, q, D ** -0.5, True, rot, out, 0, ws)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / n_calls
+    row = D * kb // 8 + D * vb // 8 + 4 * (D // gs) * 2  # packed K, V and the four meta arrays
+    alg = B * Hkv * T * row + B * Hq * D * (2 + 4)
+    gbs = alg / (us * 1e-6) / 1e9
+    return {
+        "what": f"decode, B={B}, {Hq}/{Hkv} heads, head_dim {D}, group {gs}, K{kb}/V{vb}, "
+                f"two-sided rotation, T={T}, bf16 (tile kernel)",
+        "bound": "hbm",
+        "alg_bytes_per_call": alg,
+        "avg_us": round(us, 3),
+        "achieved": round(gbs, 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(gbs / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(B / (us * 1e-6), 1),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -331,6 +439,10 @@ def main() -> int:
 
     print("[bench] tree verification", file=sys.stderr, flush=True)
     tree = tree_verify(rbq, W, dev, rot)
+    print("[bench] prefill chunk", file=sys.stderr, flush=True)
+    pre = prefill(rbq, W, dev, rot)
+    print("[bench] decode, head_dim 128 K4/V4", file=sys.stderr, flush=True)
+    var = variant_decode(rbq, W, dev)
 
     nbytes = algorithmic_bytes(w, w.T)
     ms_per_step = total * 1e3 / args.steps
@@ -387,6 +499,8 @@ def main() -> int:
             "frac": round(copy_gbs / HBM_PEAK_GBS, 4),
         },
         "tree_verify": tree,
+        "prefill": pre,
+        "variant_decode": var,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)

@@ -56,21 +56,22 @@ constexpr int tThreads = 64 * tWaves;
 constexpr int tTile = 32;                  // keys per tile
 constexpr int tRows = 16 * tWaves;         // query rows per workgroup
 constexpr int tMaxGroups = 8;              // head_dim / group_size <= 8
-constexpr int tVS = 2 * (tTile + 8);       // bytes per dim row of the transposed V codes
 constexpr int tPS = tTile + 4;             // floats per row of a wave's P staging
 constexpr float tLog2e = 1.44269504088896340736f;
 
 template <int D>
 struct TileLds {
     static constexpr int KS = 2 * D + 16;                               // bytes per key row of K codes
+    static constexpr int VS = 2 * D + 32;                               // bytes per key row of V codes
     static constexpr int kc = 0;                                        // K codes, fp16 [32][KS / 2]
-    static constexpr int vt = kc + tTile * KS;                          // V codes, fp16 [D][tVS / 2]
-    static constexpr int ksl = vt + D * tVS;                            // fp32 [8][32] K scales
+    static constexpr int vc = kc + tTile * KS;                          // V codes, fp16 [32][VS / 2]
+    static constexpr int ksl = vc + tTile * VS;                         // fp32 [8][32] K scales
     static constexpr int kbl = ksl + tMaxGroups * tTile * 4;            // K biases
     static constexpr int vsf = kbl + tMaxGroups * tTile * 4;            // V scales x 2^F
     static constexpr int vbl = vsf + tMaxGroups * tTile * 4;            // V biases
     static constexpr int vinv = vbl + tMaxGroups * tTile * 4;           // 2^-F per group
-    static constexpr int pst = vinv + tMaxGroups * 4;                   // [4 waves][16][tPS] fp32
+    static constexpr int vres = vinv + tMaxGroups * 4;                  // 2^(F_new - F_old) per group
+    static constexpr int pst = vres + tMaxGroups * 4;                   // [4 waves][16][tPS] fp32
     static constexpr int qst = pst + tWaves * 16 * tPS * 4;             // [4 waves][8 groups][16 rows]
     static constexpr int frw = qst + tWaves * tMaxGroups * 16 * 4;      // [4 waves][16] 2^-E
     static constexpr int bytes = frw + tWaves * 16 * 4;
@@ -223,9 +224,17 @@ __device__ __forceinline__ void load_tile_raw(const TArgs& a, int64_t row0, int 
     }
 }
 
-template <int DT, int D>
+// The tile into LDS: K and V codes as fp16 [key][dim]; per (group, key) the
+// K scale and bias and the V bias as fp32, and the V scale times 2^F_g, with
+// F_g the running power of two of group g: chosen so that the largest V
+// scale seen so far, times 2^F_g, lies in [2^14, 2^15); when a tile raises
+// that largest scale, F_g drops and vres[g] = 2^(F_new - F_old) tells the
+// waves to rescale the output columns of group g (1 otherwise).  f_run is
+// this thread's copy of F_g (threads 32 g .. 32 g + 31 own group g; 1000 =
+// no nonzero scale yet).
+template <int DT, int D, int NG>
 __device__ __forceinline__ void store_tile(const TArgs& a, int tid, const TileRaw& r,
-                                           unsigned char* smem) {
+                                           unsigned char* smem, int& f_run) {
     using Ly = TileLds<D>;
     constexpr int upk = D / 32;
 #pragma unroll
@@ -240,48 +249,67 @@ __device__ __forceinline__ void store_tile(const TArgs& a, int tid, const TileRa
             tu32x2 h[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) h[i] = bytes_f16(c[i]);
-            if (!isv) {
-                tu32x4* dst = reinterpret_cast<tu32x4*>(smem + Ly::kc + key * Ly::KS + 64 * part);
+            tu32x4* dst = reinterpret_cast<tu32x4*>(
+                smem + (isv ? Ly::vc + key * Ly::VS : Ly::kc + key * Ly::KS) + 64 * part);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dst[i] = (tu32x4){h[2 * i][0], h[2 * i][1], h[2 * i + 1][0], h[2 * i + 1][1]};
-            } else {
-                unsigned char* col = smem + Ly::vt + (32 * part) * tVS + 2 * key;
-#pragma unroll
-                for (int i = 0; i < 32; ++i)
-                    *reinterpret_cast<uint16_t*>(col + i * tVS) = (uint16_t)(h[i >> 2][(i >> 1) & 1] >> (16 * (i & 1)));
-            }
+            for (int i = 0; i < 4; ++i)
+                dst[i] = (tu32x4){h[2 * i][0], h[2 * i][1], h[2 * i + 1][0], h[2 * i + 1][1]};
         }
     }
-    const int G = D / a.GS;
     if (tid < tTile * tMaxGroups) {  // whole waves: the max below is a 32-lane butterfly
         const int g = tid / tTile, key = tid - g * tTile;
-        const bool live = g < G;
-        const float s_k = elem_to_f32<DT>(r.meta[0]);
-        const float b_k = elem_to_f32<DT>(r.meta[1]);
+        const bool live = g < NG;
         const float s_v = elem_to_f32<DT>(r.meta[2]);
-        const float b_v = elem_to_f32<DT>(r.meta[3]);
         float mx = live ? fabsf(s_v) : 0.f;
 #pragma unroll
         for (int m = 1; m < 32; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
         int ex = 0;
         if (mx > 0.f) (void)frexpf(mx, &ex);
-        const int F = (mx > 0.f) ? 15 - ex : 0;
+        const int f_new = (mx > 0.f) ? min(f_run, 15 - ex) : f_run;
         if (live) {
             float* f = reinterpret_cast<float*>(smem);
-            f[Ly::ksl / 4 + g * tTile + key] = s_k;
-            f[Ly::kbl / 4 + g * tTile + key] = b_k;
-            f[Ly::vsf / 4 + g * tTile + key] = ldexpf(s_v, F);
-            f[Ly::vbl / 4 + g * tTile + key] = b_v;
-            if (key == 0) f[Ly::vinv / 4 + g] = ldexpf(1.0f, -F);
+            f[Ly::ksl / 4 + g * tTile + key] = elem_to_f32<DT>(r.meta[0]);
+            f[Ly::kbl / 4 + g * tTile + key] = elem_to_f32<DT>(r.meta[1]);
+            f[Ly::vsf / 4 + g * tTile + key] = (f_new == 1000) ? 0.f : ldexpf(s_v, f_new);
+            f[Ly::vbl / 4 + g * tTile + key] = elem_to_f32<DT>(r.meta[3]);
+            if (key == 0) {
+                f[Ly::vinv / 4 + g] = (f_new == 1000) ? 1.f : ldexpf(1.0f, -f_new);
+                f[Ly::vres / 4 + g] = (f_run == 1000 || f_new == f_run) ? 1.f : ldexpf(1.0f, f_new - f_run);
+            }
         }
+        f_run = f_new;
     }
 }
 
-template <int DT, int D>
+// (hi, lo) fp16 pairs of x0, x1: hi rounded toward zero by the packed
+// conversion, lo = fp16(x - hi) by one mixed-precision FMA per half
+// (x - hi is exact in fp32).
+__device__ __forceinline__ tu32x2 split_f16(float x0, float x1, float one) {
+    const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x0, x1));
+    uint32_t lo;
+    asm("v_fma_mixlo_f16 %0, -%1, %2, %3 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, -%1, %2, %4 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(lo)
+        : "v"(hi), "v"(one), "v"(x0), "v"(x1));
+    return (tu32x2){hi, lo};
+}
+
+// 4 halves of the transposing LDS read: lane i of each 16-lane group gets
+// element i & 3 of the 8 bytes addressed by lanes 4 e + (i >> 2), e = 0..3.
+__device__ __forceinline__ tu32x2 tr16_read(const unsigned char* p) {
+    typedef short ts16x4 __attribute__((ext_vector_type(4)));
+    const ts16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) ts16x4*)((__attribute__((address_space(3))) unsigned char*)p));
+    return __builtin_bit_cast(tu32x2, v);
+}
+
+template <int DT, int D, int NG>
 __global__ __launch_bounds__(tThreads) void attn_tile_kernel(TArgs a) {
     using Ly = TileLds<D>;
-    constexpr int NC = D / 32;  // 32-dim chunks
-    constexpr int NB = D / 16;  // 16-column output blocks
+    constexpr int NC = D / 32;    // 32-dim chunks
+    constexpr int NB = D / 16;    // 16-column output blocks
+    constexpr int CPG = NC / NG;  // chunks per group
+    constexpr int NPG = NB / NG;  // output blocks per group
     __shared__ __attribute__((aligned(16))) unsigned char smem[Ly::bytes];
     float* fs = reinterpret_cast<float*>(smem);
 
@@ -294,9 +322,6 @@ __global__ __launch_bounds__(tThreads) void attn_tile_kernel(TArgs a) {
     const int b = bh / a.Hkv;
     const int kvh = bh - b * a.Hkv;
     const int T = a.T;
-    const int G = D / a.GS;
-    const int cpg = a.GS / 32;  // chunks per group
-    const int npg = a.GS / 16;  // output blocks per group
     const int64_t row0 = (int64_t)bh * a.capacity;
     const int t_begin = split * a.chunk;
     int t_end = t_begin + a.chunk;
@@ -361,31 +386,26 @@ __global__ __launch_bounds__(tThreads) void attn_tile_kernel(TArgs a) {
         int ex = 0;
         if (mx > 0.f) (void)frexpf(mx, &ex);
         const int E = (mx > 0.f) ? 15 - ex : 0;
-        float gsum[tMaxGroups];
+        float gsum[NG];
 #pragma unroll
-        for (int g = 0; g < tMaxGroups; ++g) gsum[g] = 0.f;
+        for (int g = 0; g < NG; ++g) gsum[g] = 0.f;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            float part = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float xs = ldexpf(qv[c][e], E);
                 const _Float16 hi = (_Float16)xs;
                 qh[c][e] = hi;
                 ql[c][e] = (_Float16)(xs - (float)hi);
-                part += qv[c][e];
+                gsum[c / CPG] += qv[c][e];
             }
-            const int g = c / cpg;
-#pragma unroll
-            for (int gg = 0; gg < tMaxGroups; ++gg)
-                if (gg == g) gsum[gg] += part;
         }
 #pragma unroll
-        for (int g = 0; g < tMaxGroups; ++g) {
+        for (int g = 0; g < NG; ++g) {
             float s = gsum[g];
             s += __shfl_xor(s, 16);
             s += __shfl_xor(s, 32);
-            if (j == 0 && g < G) fs[Ly::qst / 4 + (wave * tMaxGroups + g) * 16 + n] = s;
+            if (j == 0) fs[Ly::qst / 4 + (wave * tMaxGroups + g) * 16 + n] = s;
         }
         if (j == 0) fs[Ly::frw / 4 + wave * 16 + n] = ldexpf(1.0f, -E);
     }
@@ -393,8 +413,9 @@ __global__ __launch_bounds__(tThreads) void attn_tile_kernel(TArgs a) {
     // ---- per-lane softmax rows (accumulator rows 4 j + i) ----
     float frow[4], m_run[4], l_part[4];
     int vis[4];
-    int64_t moff[4];
+    uint32_t moff[4];  // byte offset of the row's mask elements; 0xFFFFFFFF: no mask
     __syncthreads();
+    const int esize = (a.mtype == 1) ? 1 : (a.mtype == 2) ? 4 : 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int rr = 4 * j + i;
@@ -403,29 +424,34 @@ __global__ __launch_bounds__(tThreads) void attn_tile_kernel(TArgs a) {
         l_part[i] = 0.f;
         const int R = r0 + 16 * wave + rr;
         vis[i] = (R < a.G && a.causal) ? T - a.L + (R % a.L) + 1 : T;
-        moff[i] = -1;
+        moff[i] = 0xFFFFFFFFu;
         if (R < a.G && a.mask != nullptr) {
             const int h = kvh * a.n_rep + R / a.L;
-            moff[i] = (int64_t)b * a.msb + (int64_t)h * a.msh + (int64_t)(R % a.L) * a.msl;
+            moff[i] = (uint32_t)(((int64_t)b * a.msb + (int64_t)h * a.msh + (int64_t)(R % a.L) * a.msl) * esize);
         }
     }
-    const int esize = (a.mtype == 1) ? 1 : (a.mtype == 2) ? 4 : 2;
     __amdgpu_buffer_rsrc_t mask_r = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(a.mask != nullptr ? a.mask : (const void*)a.q), (short)0,
         (int)a.mask_bytes, 0x00020000);
 
+    // output accumulators: column group g holds sum_t p_t s_{t,g} 2^F_g c_{t,d}
     tf32x4 O[NB];
 #pragma unroll
     for (int t = 0; t < NB; ++t) O[t] = (tf32x4){0.f, 0.f, 0.f, 0.f};
-    float ob[4][tMaxGroups];
+    float ob[4][NG];  // per lane: sum over its keys of p_t b_{t,g}
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int g = 0; g < tMaxGroups; ++g) ob[i][g] = 0.f;
+        for (int g = 0; g < NG; ++g) ob[i][g] = 0.f;
+    int f_run = 1000;
+    const float one = 1.0f;
+    // this lane's address of the transposing V reads: lane 4 e + c of group j
+    // reads key 8 j + 4 h + e, columns 4 c .. 4 c + 3 of an output block
+    const unsigned char* vrd = smem + Ly::vc + (8 * j + (n >> 2)) * Ly::VS + 8 * (n & 3);
 
     for (int t0 = t_begin; t0 < t_lim; t0 += tTile) {
         __syncthreads();  // the previous tile's LDS reads are done
-        store_tile<DT, D>(a, tid, raw, smem);
+        store_tile<DT, D, NG>(a, tid, raw, smem, f_run);
         __syncthreads();
         if (t0 + tTile < t_lim) load_tile_raw<D>(a, row0, t0 + tTile, tid, raw);
         if (!wave_live) continue;
@@ -436,30 +462,30 @@ __global__ __launch_bounds__(tThreads) void attn_tile_kernel(TArgs a) {
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) sacc[nb][i] = bacc[nb][i] = 0.f;
-        tf32x4 acc[2] = {(tf32x4){0.f, 0.f, 0.f, 0.f}, (tf32x4){0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
+        for (int g = 0; g < NG; ++g) {
+            tf32x4 acc[2] = {(tf32x4){0.f, 0.f, 0.f, 0.f}, (tf32x4){0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const tf16x8 kb8 = *reinterpret_cast<const tf16x8*>(
-                    smem + Ly::kc + (16 * nb + n) * Ly::KS + 64 * c + 16 * j);
-                acc[nb] = tmfma(qh[c], kb8, acc[nb]);
-                acc[nb] = tmfma(ql[c], kb8, acc[nb]);
-            }
-            if ((c + 1) % cpg == 0) {  // group g complete
-                const int g = c / cpg;
-                const float s0 = fs[Ly::ksl / 4 + g * tTile + n], s1 = fs[Ly::ksl / 4 + g * tTile + 16 + n];
-                const float b0 = fs[Ly::kbl / 4 + g * tTile + n], b1 = fs[Ly::kbl / 4 + g * tTile + 16 + n];
-                const tf32x4 qs = *reinterpret_cast<const tf32x4*>(
-                    fs + Ly::qst / 4 + (wave * tMaxGroups + g) * 16 + 4 * j);
+            for (int cc = 0; cc < CPG; ++cc) {
+                const int c = g * CPG + cc;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sacc[0][i] += s0 * acc[0][i];
-                    sacc[1][i] += s1 * acc[1][i];
-                    bacc[0][i] += b0 * qs[i];
-                    bacc[1][i] += b1 * qs[i];
+                for (int nb = 0; nb < 2; ++nb) {
+                    const tf16x8 kb8 = *reinterpret_cast<const tf16x8*>(
+                        smem + Ly::kc + (16 * nb + n) * Ly::KS + 64 * c + 16 * j);
+                    acc[nb] = tmfma(qh[c], kb8, acc[nb]);
+                    acc[nb] = tmfma(ql[c], kb8, acc[nb]);
                 }
-                acc[0] = acc[1] = (tf32x4){0.f, 0.f, 0.f, 0.f};
+            }
+            const float s0 = fs[Ly::ksl / 4 + g * tTile + n], s1 = fs[Ly::ksl / 4 + g * tTile + 16 + n];
+            const float b0 = fs[Ly::kbl / 4 + g * tTile + n], b1 = fs[Ly::kbl / 4 + g * tTile + 16 + n];
+            const tf32x4 qs = *reinterpret_cast<const tf32x4*>(
+                fs + Ly::qst / 4 + (wave * tMaxGroups + g) * 16 + 4 * j);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sacc[0][i] += s0 * acc[0][i];
+                sacc[1][i] += s1 * acc[1][i];
+                bacc[0][i] += b0 * qs[i];
+                bacc[1][i] += b1 * qs[i];
             }
         }
         float sc[2][4];
@@ -470,8 +496,8 @@ __global__ __launch_bounds__(tThreads) void attn_tile_kernel(TArgs a) {
                 const int t = t0 + 16 * nb + n;
                 float s = sacc[nb][i] * frow[i] + bacc[nb][i];
                 if (t >= t_end || t >= vis[i]) s = -INFINITY;
-                if (a.mtype != 0 && moff[i] >= 0 && s != -INFINITY) {
-                    const uint32_t off = (uint32_t)((moff[i] + t) * esize);
+                if (a.mtype != 0 && moff[i] != 0xFFFFFFFFu && s != -INFINITY) {
+                    const uint32_t off = moff[i] + (uint32_t)t * esize;
                     if (a.mtype == 1) {
                         if (__builtin_amdgcn_raw_buffer_load_b8(mask_r, off, 0, 0) == 0) s = -INFINITY;
                     } else if (a.mtype == 2) {
@@ -483,8 +509,9 @@ __global__ __launch_bounds__(tThreads) void attn_tile_kernel(TArgs a) {
                 sc[nb][i] = s;
             }
 
-        // ---- online softmax (base 2) ----
+        // ---- online softmax (base 2, exact running maximum) ----
         float alpha[4], p[2][4];
+        bool grow = false;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float tmx = tmax16(fmaxf(sc[0][i], sc[1][i]));
@@ -497,17 +524,26 @@ __global__ __launch_bounds__(tThreads) void attn_tile_kernel(TArgs a) {
                 p[0][i] = exp2f(sc[0][i] - m_new);
                 p[1][i] = exp2f(sc[1][i] - m_new);
             }
+            grow |= m_new != m_run[i];
             m_run[i] = m_new;
             l_part[i] = l_part[i] * alpha[i] + (p[0][i] + p[1][i]);
         }
+        if (__any(grow)) {  // rescale the accumulators only when some row's maximum moved
+#pragma unroll
+            for (int t = 0; t < NB; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) O[t][i] *= alpha[i];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int g = 0; g < NG; ++g) ob[i][g] *= alpha[i];
+        }
         // group biases: sum_t p_t b_{t,g}, per lane over its keys n, 16 + n
 #pragma unroll
-        for (int g = 0; g < tMaxGroups; ++g) {
-            if (g < G) {
-                const float v0 = fs[Ly::vbl / 4 + g * tTile + n], v1 = fs[Ly::vbl / 4 + g * tTile + 16 + n];
+        for (int g = 0; g < NG; ++g) {
+            const float v0 = fs[Ly::vbl / 4 + g * tTile + n], v1 = fs[Ly::vbl / 4 + g * tTile + 16 + n];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ob[i][g] = ob[i][g] * alpha[i] + (p[0][i] * v0 + p[1][i] * v1);
-            }
+            for (int i = 0; i < 4; ++i) ob[i][g] += p[0][i] * v0 + p[1][i] * v1;
         }
         // P to the operand layout (row n, keys 8 j .. 8 j + 7) through LDS
         float* pw = fs + Ly::pst / 4 + wave * 16 * tPS;
@@ -519,31 +555,32 @@ __global__ __launch_bounds__(tThreads) void attn_tile_kernel(TArgs a) {
         const tf32x4 pa0 = *reinterpret_cast<const tf32x4*>(pw + n * tPS + 8 * j);
         const tf32x4 pa1 = *reinterpret_cast<const tf32x4*>(pw + n * tPS + 8 * j + 4);
 
-        // ---- P V ----
-        tf16x8 ph, pl;
-        float vi = 1.f;
+        // ---- P V, accumulated into O ----
 #pragma unroll
-        for (int nb2 = 0; nb2 < NB; ++nb2) {
-            if (nb2 % npg == 0) {  // first output block of group g: its P' operands
-                const int g = nb2 / npg;
-                const tf32x4 x0 = *reinterpret_cast<const tf32x4*>(fs + Ly::vsf / 4 + g * tTile + 8 * j);
-                const tf32x4 x1 = *reinterpret_cast<const tf32x4*>(fs + Ly::vsf / 4 + g * tTile + 8 * j + 4);
-                vi = fs[Ly::vinv / 4 + g];
+        for (int g = 0; g < NG; ++g) {
+            const float rs = fs[Ly::vres / 4 + g];
+            if (rs != 1.0f) {  // the group's running scale power dropped
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float y0 = pa0[e] * x0[e], y1 = pa1[e] * x1[e];
-                    const _Float16 h0 = (_Float16)y0, h1 = (_Float16)y1;
-                    ph[e] = h0;
-                    ph[4 + e] = h1;
-                    pl[e] = (_Float16)(y0 - (float)h0);
-                    pl[4 + e] = (_Float16)(y1 - (float)h1);
-                }
+                for (int t = g * NPG; t < (g + 1) * NPG; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) O[t][i] *= rs;
             }
-            const tf16x8 vb8 = *reinterpret_cast<const tf16x8*>(smem + Ly::vt + (16 * nb2 + n) * tVS + 16 * j);
-            tf32x4 pv = tmfma(ph, vb8, (tf32x4){0.f, 0.f, 0.f, 0.f});
-            pv = tmfma(pl, vb8, pv);
+            const tf32x4 x0 = *reinterpret_cast<const tf32x4*>(fs + Ly::vsf / 4 + g * tTile + 8 * j);
+            const tf32x4 x1 = *reinterpret_cast<const tf32x4*>(fs + Ly::vsf / 4 + g * tTile + 8 * j + 4);
+            tu32x2 s01 = split_f16(pa0[0] * x0[0], pa0[1] * x0[1], one);
+            tu32x2 s23 = split_f16(pa0[2] * x0[2], pa0[3] * x0[3], one);
+            tu32x2 s45 = split_f16(pa1[0] * x1[0], pa1[1] * x1[1], one);
+            tu32x2 s67 = split_f16(pa1[2] * x1[2], pa1[3] * x1[3], one);
+            const tf16x8 ph = __builtin_bit_cast(tf16x8, (tu32x4){s01[0], s23[0], s45[0], s67[0]});
+            const tf16x8 pl = __builtin_bit_cast(tf16x8, (tu32x4){s01[1], s23[1], s45[1], s67[1]});
 #pragma unroll
-            for (int i = 0; i < 4; ++i) O[nb2][i] = O[nb2][i] * alpha[i] + pv[i] * vi;
+            for (int t = g * NPG; t < (g + 1) * NPG; ++t) {
+                const tu32x2 v0 = tr16_read(vrd + 32 * t);
+                const tu32x2 v1 = tr16_read(vrd + 32 * t + 4 * Ly::VS);
+                const tf16x8 vb8 = __builtin_bit_cast(tf16x8, (tu32x4){v0[0], v0[1], v1[0], v1[1]});
+                O[t] = tmfma(ph, vb8, O[t]);
+                O[t] = tmfma(pl, vb8, O[t]);
+            }
         }
     }
 
@@ -552,21 +589,19 @@ __global__ __launch_bounds__(tThreads) void attn_tile_kernel(TArgs a) {
     const int64_t unit = (int64_t)bhr * a.S + split;
     float* ro = a.rec_o + unit * tRows * D;
     float* rml = a.rec_ml + unit * tRows * 2;
+    float vinv[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) vinv[g] = fs[Ly::vinv / 4 + g];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int rr = 16 * wave + 4 * j + i;
         const float l = tsum16(l_part[i]);
-        float obs[tMaxGroups];
 #pragma unroll
-        for (int g = 0; g < tMaxGroups; ++g) obs[g] = (g < G) ? tsum16(ob[i][g]) : 0.f;
+        for (int g = 0; g < NG; ++g) {
+            const float bias = tsum16(ob[i][g]);
 #pragma unroll
-        for (int nb2 = 0; nb2 < NB; ++nb2) {
-            const int g = nb2 / npg;
-            float bias = 0.f;
-#pragma unroll
-            for (int gg = 0; gg < tMaxGroups; ++gg)
-                if (gg == g) bias = obs[gg];
-            ro[rr * D + 16 * nb2 + n] = O[nb2][i] + bias;
+            for (int t = g * NPG; t < (g + 1) * NPG; ++t)
+                ro[rr * D + 16 * t + n] = O[t][i] * vinv[g] + bias;
         }
         if (n == 0) {
             rml[2 * rr] = m_run[i];
@@ -693,11 +728,16 @@ int tile_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
     const dim3 grid((unsigned)(units * p.S)), block(tThreads);
     auto launch = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, s, a); };
     const bool bf = c->dtype == RBQ_BF16;
-    switch (c->head_dim) {
-        case 64: bf ? launch(attn_tile_kernel<RBQ_BF16, 64>) : launch(attn_tile_kernel<RBQ_F16, 64>); break;
-        case 128: bf ? launch(attn_tile_kernel<RBQ_BF16, 128>) : launch(attn_tile_kernel<RBQ_F16, 128>); break;
-        default: bf ? launch(attn_tile_kernel<RBQ_BF16, 256>) : launch(attn_tile_kernel<RBQ_F16, 256>); break;
+    const int ng = c->head_dim / c->group_size;
+#define RBQ_TILE_CASE(D_, NG_)                                                        \
+    if (c->head_dim == D_ && ng == NG_) {                                             \
+        bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_>) : launch(attn_tile_kernel<RBQ_F16, D_, NG_>); \
+    } else
+    RBQ_TILE_CASE(64, 1) RBQ_TILE_CASE(64, 2) RBQ_TILE_CASE(128, 1) RBQ_TILE_CASE(128, 2)
+    RBQ_TILE_CASE(128, 4) RBQ_TILE_CASE(256, 2) RBQ_TILE_CASE(256, 4) RBQ_TILE_CASE(256, 8) {
+        return RBQ_EUNSUPPORTED;
     }
+#undef RBQ_TILE_CASE
     TMArgs m;
     m.rec_o = a.rec_o;
     m.rec_ml = a.rec_ml;
