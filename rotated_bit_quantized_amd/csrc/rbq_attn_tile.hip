@@ -51,15 +51,13 @@ typedef float tf32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t tu32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t tu32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int tWaves = 4;
-constexpr int tThreads = 64 * tWaves;
 constexpr int tTile = 32;                  // keys per tile
-constexpr int tRows = 16 * tWaves;         // query rows per workgroup
 constexpr int tMaxGroups = 8;              // head_dim / group_size <= 8
 constexpr int tPS = tTile + 4;             // floats per row of a wave's P staging
 constexpr float tLog2e = 1.44269504088896340736f;
 
-template <int D>
+// LDS of a workgroup of W waves (16 query rows each).
+template <int D, int W>
 struct TileLds {
     static constexpr int KS = 2 * D + 16;                               // bytes per key row of K codes
     static constexpr int VS = 2 * D + 32;                               // bytes per key row of V codes
@@ -72,9 +70,9 @@ struct TileLds {
     static constexpr int vinv = vbl + tMaxGroups * tTile * 4;           // 2^-F per group
     static constexpr int vres = vinv + tMaxGroups * 4;                  // 2^(F_new - F_old) per group
     static constexpr int pst = vres + tMaxGroups * 4;                   // [4 waves][16][tPS] fp32
-    static constexpr int qst = pst + tWaves * 16 * tPS * 4;             // [4 waves][8 groups][16 rows]
-    static constexpr int frw = qst + tWaves * tMaxGroups * 16 * 4;      // [4 waves][16] 2^-E
-    static constexpr int bytes = frw + tWaves * 16 * 4;
+    static constexpr int qst = pst + W * 16 * tPS * 4;                  // [W waves][8 groups][16 rows]
+    static constexpr int frw = qst + W * tMaxGroups * 16 * 4;           // [W waves][16] 2^-E
+    static constexpr int bytes = frw + W * 16 * 4;
 };
 
 struct TArgs {
@@ -86,8 +84,8 @@ struct TArgs {
     const uint16_t* vs;
     const uint16_t* vb;
     const float* rot;
-    float* rec_o;   // [units][S][64 rows][D]
-    float* rec_ml;  // [units][S][64 rows][2]
+    float* rec_o;   // [units][S][RW rows][D]
+    float* rec_ml;  // [units][S][RW rows][2]
     int64_t capacity;
     int T, chunk, S, Hkv, n_rep, L, G, RBW, causal, round_rot;
     int GS, kbits, vbits;
@@ -175,22 +173,21 @@ __device__ __forceinline__ void unpack32_any(int bits, const uint32_t w[8], uint
     }
 }
 
-// Registers of one tile for this thread: the packed words of up to two
-// 32-code units (K and / or V), and the four scale / bias values of one
-// (key, group).
+// Registers of two 32-code units (K and / or V packed words) of a tile.
+// Unit u < D is K unit u, u >= D V unit u - D; unit v of a row covers key
+// v / (D / 32), codes 32 (v % (D / 32)) .. + 31.
 struct TileRaw {
     uint32_t w[2][8];
-    uint32_t meta[4];
 };
 
 template <int D>
-__device__ __forceinline__ void load_tile_raw(const TArgs& a, int64_t row0, int t0, int tid,
-                                              TileRaw& r) {
+__device__ __forceinline__ void load_units(const TArgs& a, int64_t row0, int t0, int u0, int ustep,
+                                           TileRaw& r) {
     constexpr int upk = D / 32;  // 32-code units per key row
     const int kwords = D * a.kbits / 32, vwords = D * a.vbits / 32;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-        const int u = tid + k * tThreads;
+        const int u = u0 + k * ustep;
 #pragma unroll
         for (int i = 0; i < 8; ++i) r.w[k][i] = 0u;
         if (u < 2 * D) {
@@ -208,38 +205,17 @@ __device__ __forceinline__ void load_tile_raw(const TArgs& a, int64_t row0, int 
             }
         }
     }
-    const int G = D / a.GS;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.meta[i] = 0u;
-    if (tid < tTile * G) {
-        const int g = tid / tTile, key = tid - g * tTile;
-        const int t = t0 + key;
-        if (t < a.T) {
-            const int64_t o = (row0 + t) * G + g;
-            r.meta[0] = a.ks[o];
-            r.meta[1] = a.kb[o];
-            r.meta[2] = a.vs[o];
-            r.meta[3] = a.vb[o];
-        }
-    }
 }
 
-// The tile into LDS: K and V codes as fp16 [key][dim]; per (group, key) the
-// K scale and bias and the V bias as fp32, and the V scale times 2^F_g, with
-// F_g the running power of two of group g: chosen so that the largest V
-// scale seen so far, times 2^F_g, lies in [2^14, 2^15); when a tile raises
-// that largest scale, F_g drops and vres[g] = 2^(F_new - F_old) tells the
-// waves to rescale the output columns of group g (1 otherwise).  f_run is
-// this thread's copy of F_g (threads 32 g .. 32 g + 31 own group g; 1000 =
-// no nonzero scale yet).
-template <int DT, int D, int NG>
-__device__ __forceinline__ void store_tile(const TArgs& a, int tid, const TileRaw& r,
-                                           unsigned char* smem, int& f_run) {
-    using Ly = TileLds<D>;
+// K and V codes of the units into LDS as fp16 [key][dim].
+template <int D, int W>
+__device__ __forceinline__ void store_units(const TArgs& a, const TileRaw& r, int u0, int ustep,
+                                            unsigned char* smem) {
+    using Ly = TileLds<D, W>;
     constexpr int upk = D / 32;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-        const int u = tid + k * tThreads;
+        const int u = u0 + k * ustep;
         if (u < 2 * D) {
             const bool isv = u >= D;
             const int uu = isv ? u - D : u;
@@ -256,29 +232,58 @@ __device__ __forceinline__ void store_tile(const TArgs& a, int tid, const TileRa
                 dst[i] = (tu32x4){h[2 * i][0], h[2 * i][1], h[2 * i + 1][0], h[2 * i + 1][1]};
         }
     }
-    if (tid < tTile * tMaxGroups) {  // whole waves: the max below is a 32-lane butterfly
-        const int g = tid / tTile, key = tid - g * tTile;
-        const bool live = g < NG;
-        const float s_v = elem_to_f32<DT>(r.meta[2]);
-        float mx = live ? fabsf(s_v) : 0.f;
+}
+
+// Scale / bias item m of a tile: group m / 32, key m % 32 (m < 256).
+template <int NG>
+__device__ __forceinline__ void load_meta(const TArgs& a, int64_t row0, int t0, int m,
+                                          uint32_t meta[4]) {
 #pragma unroll
-        for (int m = 1; m < 32; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
-        int ex = 0;
-        if (mx > 0.f) (void)frexpf(mx, &ex);
-        const int f_new = (mx > 0.f) ? min(f_run, 15 - ex) : f_run;
-        if (live) {
-            float* f = reinterpret_cast<float*>(smem);
-            f[Ly::ksl / 4 + g * tTile + key] = elem_to_f32<DT>(r.meta[0]);
-            f[Ly::kbl / 4 + g * tTile + key] = elem_to_f32<DT>(r.meta[1]);
-            f[Ly::vsf / 4 + g * tTile + key] = (f_new == 1000) ? 0.f : ldexpf(s_v, f_new);
-            f[Ly::vbl / 4 + g * tTile + key] = elem_to_f32<DT>(r.meta[3]);
-            if (key == 0) {
-                f[Ly::vinv / 4 + g] = (f_new == 1000) ? 1.f : ldexpf(1.0f, -f_new);
-                f[Ly::vres / 4 + g] = (f_run == 1000 || f_new == f_run) ? 1.f : ldexpf(1.0f, f_new - f_run);
-            }
-        }
-        f_run = f_new;
+    for (int i = 0; i < 4; ++i) meta[i] = 0u;
+    const int g = m / tTile, key = m - g * tTile;
+    const int t = t0 + key;
+    if (g < NG && t < a.T) {
+        const int64_t o = (row0 + t) * NG + g;
+        meta[0] = a.ks[o];
+        meta[1] = a.kb[o];
+        meta[2] = a.vs[o];
+        meta[3] = a.vb[o];
     }
+}
+
+// Per (group, key) the K scale and bias and the V bias as fp32, and the V
+// scale times 2^F_g, with F_g the running power of two of group g: chosen
+// so that the largest V scale seen so far, times 2^F_g, lies in [2^14,
+// 2^15); when a tile raises that largest scale, F_g drops and vres[g] =
+// 2^(F_new - F_old) tells the waves to rescale the output columns of group g
+// (1 otherwise).  f_run is this thread's copy of F_g (1000 = no nonzero
+// scale yet).  Called by all 64 lanes of a wave with items m = 64 q + lane
+// (the maximum is a butterfly over the 32 lanes of a group).
+template <int DT, int D, int W, int NG>
+__device__ __forceinline__ void store_meta(const uint32_t meta[4], int m, unsigned char* smem,
+                                           int& f_run) {
+    using Ly = TileLds<D, W>;
+    const int g = m / tTile, key = m - g * tTile;
+    const bool live = g < NG;
+    const float s_v = elem_to_f32<DT>(meta[2]);
+    float mx = live ? fabsf(s_v) : 0.f;
+#pragma unroll
+    for (int k = 1; k < 32; k <<= 1) mx = fmaxf(mx, __shfl_xor(mx, k));
+    int ex = 0;
+    if (mx > 0.f) (void)frexpf(mx, &ex);
+    const int f_new = (mx > 0.f) ? min(f_run, 15 - ex) : f_run;
+    if (live) {
+        float* f = reinterpret_cast<float*>(smem);
+        f[Ly::ksl / 4 + g * tTile + key] = elem_to_f32<DT>(meta[0]);
+        f[Ly::kbl / 4 + g * tTile + key] = elem_to_f32<DT>(meta[1]);
+        f[Ly::vsf / 4 + g * tTile + key] = (f_new == 1000) ? 0.f : ldexpf(s_v, f_new);
+        f[Ly::vbl / 4 + g * tTile + key] = elem_to_f32<DT>(meta[3]);
+        if (key == 0) {
+            f[Ly::vinv / 4 + g] = (f_new == 1000) ? 1.f : ldexpf(1.0f, -f_new);
+            f[Ly::vres / 4 + g] = (f_run == 1000 || f_new == f_run) ? 1.f : ldexpf(1.0f, f_new - f_run);
+        }
+    }
+    f_run = f_new;
 }
 
 // (hi, lo) fp16 pairs of x0, x1: hi rounded toward zero by the packed
@@ -303,9 +308,16 @@ __device__ __forceinline__ tu32x2 tr16_read(const unsigned char* p) {
     return __builtin_bit_cast(tu32x2, v);
 }
 
-template <int DT, int D, int NG>
-__global__ __launch_bounds__(tThreads) void attn_tile_kernel(TArgs a) {
-    using Ly = TileLds<D>;
+// W = 4: long query blocks (64 rows per workgroup share every decoded tile);
+// W = 1: up to 16 rows per kv head (decode, short verify blocks): one wave
+// per workgroup decodes and computes its own tiles, so the compute units run
+// many independent waves instead of one computing wave per four.
+template <int DT, int D, int NG, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_tile_kernel(TArgs a) {
+    using Ly = TileLds<D, W>;
+    constexpr int kThr = 64 * W;
+    constexpr int kRW = 16 * W;  // query rows per workgroup
     constexpr int NC = D / 32;    // 32-dim chunks
     constexpr int NB = D / 16;    // 16-column output blocks
     constexpr int CPG = NC / NG;  // chunks per group
@@ -318,7 +330,7 @@ __global__ __launch_bounds__(tThreads) void attn_tile_kernel(TArgs a) {
     const int bhr = blockIdx.x / a.S;
     const int split = blockIdx.x - bhr * a.S;
     const int bh = bhr / a.RBW;
-    const int r0 = tRows * (bhr - bh * a.RBW);
+    const int r0 = kRW * (bhr - bh * a.RBW);
     const int b = bh / a.Hkv;
     const int kvh = bh - b * a.Hkv;
     const int T = a.T;
@@ -327,7 +339,7 @@ __global__ __launch_bounds__(tThreads) void attn_tile_kernel(TArgs a) {
     int t_end = t_begin + a.chunk;
     if (t_end > T) t_end = T;
     // keys past the last visible key of every row of the block are skipped
-    const int rlast = min(r0 + tRows, a.G) - 1;
+    const int rlast = min(r0 + kRW, a.G) - 1;
     int t_lim = t_end;
     if (a.causal && a.mask == nullptr) {
         const int i0 = r0 % a.L, i1 = rlast % a.L;
@@ -336,9 +348,14 @@ __global__ __launch_bounds__(tThreads) void attn_tile_kernel(TArgs a) {
         if (t_lim > vmax) t_lim = vmax;
     }
 
-    // first tile's words in flight during the set-up
+    // W = 4: the first tile's words (two units and one scale / bias item per
+    // thread) in flight during the set-up, later always one tile ahead
     TileRaw raw;
-    if (t_begin < t_lim) load_tile_raw<D>(a, row0, t_begin, tid, raw);
+    uint32_t meta[4];
+    if (W == 4 && t_begin < t_lim) {
+        load_units<D>(a, row0, t_begin, tid, kThr, raw);
+        load_meta<NG>(a, row0, t_begin, tid, meta);
+    }
 
     // ---- query operands: row 16 wave + n of the block, dims 32 c + 8 j + 0..7 ----
     const int rowA = r0 + 16 * wave + n;
@@ -443,7 +460,9 @@ __global__ __launch_bounds__(tThreads) void attn_tile_kernel(TArgs a) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int g = 0; g < NG; ++g) ob[i][g] = 0.f;
-    int f_run = 1000;
+    int f_run[256 / kThr];  // running scale powers of the groups of this thread's items
+#pragma unroll
+    for (int q = 0; q < 256 / kThr; ++q) f_run[q] = 1000;
     const float one = 1.0f;
     // this lane's address of the transposing V reads: lane 4 e + c of group j
     // reads key 8 j + 4 h + e, columns 4 c .. 4 c + 3 of an output block
@@ -451,9 +470,28 @@ __global__ __launch_bounds__(tThreads) void attn_tile_kernel(TArgs a) {
 
     for (int t0 = t_begin; t0 < t_lim; t0 += tTile) {
         __syncthreads();  // the previous tile's LDS reads are done
-        store_tile<DT, D, NG>(a, tid, raw, smem, f_run);
-        __syncthreads();
-        if (t0 + tTile < t_lim) load_tile_raw<D>(a, row0, t0 + tTile, tid, raw);
+        if constexpr (W == 4) {
+            store_units<D, W>(a, raw, tid, kThr, smem);
+            store_meta<DT, D, W, NG>(meta, tid, smem, f_run[0]);
+            __syncthreads();
+            if (t0 + tTile < t_lim) {
+                load_units<D>(a, row0, t0 + tTile, tid, kThr, raw);
+                load_meta<NG>(a, row0, t0 + tTile, tid, meta);
+            }
+        } else {
+            // one wave: its 2 D units in pairs (u, u + 64), then its 4 items
+#pragma unroll
+            for (int u0 = 0; u0 < 2 * D; u0 += 128) {
+                load_units<D>(a, row0, t0, u0 + tid, 64, raw);
+                store_units<D, W>(a, raw, u0 + tid, 64, smem);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                load_meta<NG>(a, row0, t0, 64 * q + tid, meta);
+                store_meta<DT, D, W, NG>(meta, 64 * q + tid, smem, f_run[q]);
+            }
+            __syncthreads();
+        }
         if (!wave_live) continue;
 
         // ---- scores ----
@@ -587,15 +625,17 @@ __global__ __launch_bounds__(tThreads) void attn_tile_kernel(TArgs a) {
     // ---- record: (m, l) and the unnormalised o of each row ----
     if (!wave_live) return;
     const int64_t unit = (int64_t)bhr * a.S + split;
-    float* ro = a.rec_o + unit * tRows * D;
-    float* rml = a.rec_ml + unit * tRows * 2;
+    float* ro = a.rec_o + unit * kRW * D;
+    float* rml = a.rec_ml + unit * kRW * 2;
     float vinv[NG];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) vinv[g] = fs[Ly::vinv / 4 + g];
+    for (int g = 0; g < NG; ++g)  // the scale powers after the last tile (none: 1, O is 0)
+        vinv[g] = (t_begin < t_lim) ? fs[Ly::vinv / 4 + g] : 1.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int rr = 16 * wave + 4 * j + i;
         const float l = tsum16(l_part[i]);
+        if (r0 + rr >= a.G) continue;  // past the last query row: nothing to record
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             const float bias = tsum16(ob[i][g]);
@@ -615,7 +655,7 @@ struct TMArgs {
     const float* rec_ml;
     const float* rot;
     float* out;
-    int S, Hkv, n_rep, L, G, RBW;
+    int S, Hkv, n_rep, L, G, RBW, RW;
 };
 
 // Merge of the key-split records of one query row (64 threads, 4 columns
@@ -625,25 +665,26 @@ struct TMArgs {
 template <int D>
 __global__ __launch_bounds__(64) void attn_tile_merge_kernel(TMArgs a) {
     const int rowg = blockIdx.x;  // (b, kv head, row block, row)
-    const int rr = rowg % tRows;
-    const int bhr = rowg / tRows;
+    const int RW = a.RW;
+    const int rr = rowg % RW;
+    const int bhr = rowg / RW;
     const int bh = bhr / a.RBW;
-    const int R = tRows * (bhr - bh * a.RBW) + rr;
+    const int R = RW * (bhr - bh * a.RBW) + rr;
     if (R >= a.G) return;
     const int k = threadIdx.x;
     if (k >= D / 4) return;
     const int b = bh / a.Hkv, kvh = bh - b * a.Hkv;
     float M = -INFINITY;
-    for (int s = 0; s < a.S; ++s) M = fmaxf(M, a.rec_ml[((int64_t)bhr * a.S + s) * tRows * 2 + 2 * rr]);
+    for (int s = 0; s < a.S; ++s) M = fmaxf(M, a.rec_ml[((int64_t)bhr * a.S + s) * RW * 2 + 2 * rr]);
     float Ls = 0.f;
     float o[4] = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < a.S; ++s) {
         const int64_t u = (int64_t)bhr * a.S + s;
-        const float m = a.rec_ml[u * tRows * 2 + 2 * rr];
+        const float m = a.rec_ml[u * RW * 2 + 2 * rr];
         if (m == -INFINITY) continue;
         const float w = exp2f(m - M);
-        Ls += a.rec_ml[u * tRows * 2 + 2 * rr + 1] * w;
-        const float4 v = *reinterpret_cast<const float4*>(a.rec_o + (u * tRows + rr) * D + 4 * k);
+        Ls += a.rec_ml[u * RW * 2 + 2 * rr + 1] * w;
+        const float4 v = *reinterpret_cast<const float4*>(a.rec_o + (u * RW + rr) * D + 4 * k);
         o[0] += v.x * w;
         o[1] += v.y * w;
         o[2] += v.z * w;
@@ -666,12 +707,16 @@ __global__ __launch_bounds__(64) void attn_tile_merge_kernel(TMArgs a) {
 
 int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, TilePlan* p) {
     const int64_t G = (int64_t)(H_q / c->H_kv) * L;
-    const int64_t RBW = (G + tRows - 1) / tRows;
+    const int W = (G <= 16) ? 1 : 4;  // waves per workgroup, 16 rows each
+    const int64_t RW = 16 * W;
+    const int64_t RBW = (G + RW - 1) / RW;
     const int64_t T = c->offset;
     const int64_t units = (int64_t)c->B * c->H_kv * RBW;
     int64_t S = splits;
     if (S == 0) {
-        S = (1024 + units - 1) / units;  // about four workgroups per compute unit
+        // about four workgroups per compute unit (of four waves, or of one:
+        // more, shorter single-wave splits lose more to set-up and records)
+        S = (1024 + units - 1) / units;
         const int64_t max_s = (T + tTile - 1) / tTile;
         if (S > max_s) S = max_s;
     }
@@ -679,12 +724,13 @@ int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Til
     int64_t chunk = (T + S - 1) / S;
     chunk = (chunk + tTile - 1) / tTile * tTile;
     S = (T + chunk - 1) / chunk;
-    if (units * S > 0x7FFFFFFF || units * tRows > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
+    if (units * S > 0x7FFFFFFF || units * RW > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
     p->S = (int)S;
     p->RBW = (int)RBW;
+    p->W = W;
     p->chunk = chunk;
-    p->o_floats = (size_t)(units * S) * tRows * c->head_dim;
-    p->ws_bytes = (p->o_floats + (size_t)(units * S) * tRows * 2) * sizeof(float);
+    p->o_floats = (size_t)(units * S) * RW * c->head_dim;
+    p->ws_bytes = (p->o_floats + (size_t)(units * S) * RW * 2) * sizeof(float);
     return RBQ_OK;
 }
 
@@ -725,13 +771,16 @@ int tile_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
     a.mask_bytes = mk.bytes;
     a.mtype = mk.ptr == nullptr ? 0 : mk.type;
     const int64_t units = (int64_t)c->B * c->H_kv * p.RBW;
-    const dim3 grid((unsigned)(units * p.S)), block(tThreads);
+    const dim3 grid((unsigned)(units * p.S)), block(64 * p.W);
     auto launch = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, s, a); };
     const bool bf = c->dtype == RBQ_BF16;
     const int ng = c->head_dim / c->group_size;
-#define RBQ_TILE_CASE(D_, NG_)                                                        \
-    if (c->head_dim == D_ && ng == NG_) {                                             \
-        bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_>) : launch(attn_tile_kernel<RBQ_F16, D_, NG_>); \
+#define RBQ_TILE_CASE(D_, NG_)                                                                    \
+    if (c->head_dim == D_ && ng == NG_) {                                                         \
+        if (p.W == 4)                                                                             \
+            bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_, 4>) : launch(attn_tile_kernel<RBQ_F16, D_, NG_, 4>); \
+        else                                                                                      \
+            bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_, 1>) : launch(attn_tile_kernel<RBQ_F16, D_, NG_, 1>); \
     } else
     RBQ_TILE_CASE(64, 1) RBQ_TILE_CASE(64, 2) RBQ_TILE_CASE(128, 1) RBQ_TILE_CASE(128, 2)
     RBQ_TILE_CASE(128, 4) RBQ_TILE_CASE(256, 2) RBQ_TILE_CASE(256, 4) RBQ_TILE_CASE(256, 8) {
@@ -749,7 +798,8 @@ int tile_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
     m.L = L;
     m.G = a.G;
     m.RBW = p.RBW;
-    const dim3 mgrid((unsigned)(units * tRows)), mblock(64);
+    m.RW = 16 * p.W;
+    const dim3 mgrid((unsigned)(units * 16 * p.W)), mblock(64);
     switch (c->head_dim) {
         case 64: hipLaunchKernelGGL(attn_tile_merge_kernel<64>, mgrid, mblock, 0, s, m); break;
         case 128: hipLaunchKernelGGL(attn_tile_merge_kernel<128>, mgrid, mblock, 0, s, m); break;

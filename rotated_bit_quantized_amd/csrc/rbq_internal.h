@@ -62,9 +62,11 @@ struct MfmaPlan {
 int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, MfmaPlan* p);
 
 // Launch plan of the general tile attention (every configuration, any number
-// of query rows): key splits, blocks of 64 query rows, and the workspace of
-// the split records (o floats, then (m, l) pairs).
+// of query rows): waves per workgroup (16 query rows each: 1 up to 16 rows
+// per kv head, else 4), key splits, row blocks, and the workspace of the
+// split records (o floats, then (m, l) pairs).
 struct TilePlan {
+    int W;
     int S;
     int RBW;
     int64_t chunk;
