@@ -173,55 +173,124 @@ __device__ __forceinline__ void unpack32_any(int bits, const uint32_t w[8], uint
     }
 }
 
-// Registers of two 32-code units (K and / or V packed words) of a tile.
-// Unit u < D is K unit u, u >= D V unit u - D; unit v of a row covers key
-// v / (D / 32), codes 32 (v % (D / 32)) .. + 31.
-struct TileRaw {
-    uint32_t w[2][8];
+typedef __attribute__((address_space(3))) unsigned char tlds_u8;
+
+// Raw tile staging (a separate LDS array, filled by direct-to-LDS loads: the
+// compiler can then tell its transfers from every other LDS access): the
+// tile's K words, V words (key-major, as in memory) and its four scale /
+// bias arrays [key][group], 16-bit.
+template <int D, int NG>
+struct RawLds {
+    static constexpr int kw = 0;                    // up to 32 keys x D/4 words (8-bit codes)
+    static constexpr int vw = kw + 32 * D;
+    static constexpr int meta = vw + 32 * D;        // 4 arrays x 32 keys x NG x 2 B
+    static constexpr int meta_bytes = 64 * NG;      // one array
+    static constexpr int bytes = meta + 4 * meta_bytes;
 };
 
-template <int D>
-__device__ __forceinline__ void load_units(const TArgs& a, int64_t row0, int t0, int u0, int ustep,
-                                           TileRaw& r) {
-    constexpr int upk = D / 32;  // 32-code units per key row
-    const int kwords = D * a.kbits / 32, vwords = D * a.vbits / 32;
+// Buffer resources of one (b, kv head) slab: the six arrays from row 0,
+// ranges T rows (keys past T read as zero).
+struct TRsrc {
+    __amdgpu_buffer_rsrc_t kw, vw, m[4];
+    bool k16, v16;  // 16-byte transfers of the word arrays, else 4-byte
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tmake_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// Issue the direct-to-LDS transfers of the tile at key t0 (wave `wave` of
+// W takes every W-th instruction; each instruction moves 64 lanes x 16 or 4
+// bytes to consecutive LDS bytes).
+template <int D, int NG, int W>
+__device__ __forceinline__ void issue_tile(const TArgs& a, const TRsrc& rs, int t0, int wave,
+                                           int lane, tlds_u8* rawb) {
+    using R = RawLds<D, NG>;
+    // fully unrolled over the largest instruction counts (8-bit codes), each
+    // instruction predicated on a uniform condition (a loop around the
+    // transfers makes the compiler wait for the earlier ones at its head);
+    // one lane offset per array, the instruction's chunk in the scalar offset
+    constexpr int kMax16 = D / 32;  // 16-byte instructions of one word array
+    constexpr int kMax4 = D / 8;    // 4-byte instructions of one word array
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int u = u0 + k * ustep;
+    for (int kv = 0; kv < 2; ++kv) {
+        const int words = kv ? D * a.vbits / 32 : D * a.kbits / 32;
+        const __amdgpu_buffer_rsrc_t r = kv ? rs.vw : rs.kw;
+        tlds_u8* dst = rawb + (kv ? R::vw : R::kw);
+        const uint32_t base = (uint32_t)t0 * words * 4u;
+        if (kv ? rs.v16 : rs.k16) {
+            const int nch = 8 * words;  // 16-byte chunks of the tile
+            const uint32_t voff = base + 16u * lane;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) r.w[k][i] = 0u;
-        if (u < 2 * D) {
-            const bool isv = u >= D;
-            const int uu = isv ? u - D : u;
-            const int key = uu / upk, part = uu - key * upk;
-            const int t = t0 + key;
-            if (t < a.T) {
-                const int bits = isv ? a.vbits : a.kbits;
-                const uint32_t* src = (isv ? a.vw + (row0 + t) * vwords : a.kw + (row0 + t) * kwords) +
-                                      part * bits;
+            for (int m = 0; m < kMax16; ++m)
+                if (m % W == wave && 64 * m < nch && (64 * m + 64 <= nch || lane < nch - 64 * m))
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + 1024 * m, 16, voff, 1024 * m, 0, 0);
+        } else {
+            const int nch = 32 * words;  // 4-byte chunks
+            const uint32_t voff = base + 4u * lane;
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    if (i < bits) r.w[k][i] = src[i];
-            }
+            for (int m = 0; m < kMax4; ++m)
+                if (m % W == wave && 64 * m < nch && (64 * m + 64 <= nch || lane < nch - 64 * m))
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + 256 * m, 4, voff, 256 * m, 0, 0);
         }
+    }
+    // the four scale / bias arrays: 32 keys x NG halves each = 16 NG words
+    // (NG = 1: 2-byte rows, loaded into registers instead, as a 4-byte chunk
+    // could straddle the end of row T - 1)
+    if constexpr (NG > 1) {
+        const uint32_t moff = (uint32_t)t0 * NG * 2u + 4u * lane;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int h = 0; h < (16 * NG + 63) / 64; ++h)
+                if ((4 * k + h) % W == wave && 64 * h + lane < 16 * NG)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.m[k], rawb + R::meta + k * R::meta_bytes + 256 * h,
+                                                              4, moff, 256 * h, 0, 0);
     }
 }
 
-// K and V codes of the units into LDS as fp16 [key][dim].
-template <int D, int W>
-__device__ __forceinline__ void store_units(const TArgs& a, const TileRaw& r, int u0, int ustep,
+// NG = 1: the scale / bias halves of key t0 + m (m < 32) into registers.
+__device__ __forceinline__ void load_meta1(const TArgs& a, int64_t row0, int t0, int m, uint32_t meta[4]) {
+    const int t = t0 + m;
+    const uint16_t* src[4] = {a.ks, a.kb, a.vs, a.vb};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) meta[i] = (t < a.T) ? src[i][row0 + t] : 0u;
+}
+
+// The packed words of unit u (u < D: K unit u, else V unit u - D; unit v of
+// a row covers key v / (D / 32), codes 32 (v % (D / 32)) .. + 31).
+template <int D, int NG>
+__device__ __forceinline__ void read_unit(const TArgs& a, const unsigned char* rawb, int u,
+                                          uint32_t w[8]) {
+    using R = RawLds<D, NG>;
+    constexpr int upk = D / 32;
+    const bool isv = u >= D;
+    const int uu = isv ? u - D : u;
+    const int key = uu / upk, part = uu - key * upk;
+    const int bits = isv ? a.vbits : a.kbits;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(rawb + (isv ? R::vw : R::kw)) +
+                          key * (D * bits / 32) + part * bits;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = (i < bits) ? src[i] : 0u;
+}
+
+// K and V codes of the tile into LDS as fp16 [key][dim], from the staged
+// words: units u = tid, tid + threads, ...
+template <int D, int W, int NG>
+__device__ __forceinline__ void store_units(const TArgs& a, const unsigned char* rawb, int tid,
                                             unsigned char* smem) {
     using Ly = TileLds<D, W>;
     constexpr int upk = D / 32;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int u = u0 + k * ustep;
-        if (u < 2 * D) {
+    for (int u = tid; u < 2 * D; u += 64 * W) {
+        {
             const bool isv = u >= D;
             const int uu = isv ? u - D : u;
             const int key = uu / upk, part = uu - key * upk;
+            uint32_t w[8];
+            read_unit<D, NG>(a, rawb, u, w);
             uint32_t c[8];
-            unpack32_any(isv ? a.vbits : a.kbits, r.w[k], c);
+            unpack32_any(isv ? a.vbits : a.kbits, w, c);
             tu32x2 h[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) h[i] = bytes_f16(c[i]);
@@ -234,21 +303,16 @@ __device__ __forceinline__ void store_units(const TArgs& a, const TileRaw& r, in
     }
 }
 
-// Scale / bias item m of a tile: group m / 32, key m % 32 (m < 256).
-template <int NG>
-__device__ __forceinline__ void load_meta(const TArgs& a, int64_t row0, int t0, int m,
-                                          uint32_t meta[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) meta[i] = 0u;
+// Scale / bias item m of the staged tile: group m / 32, key m % 32.
+template <int D, int NG>
+__device__ __forceinline__ void read_meta(const unsigned char* rawb, int m, uint32_t meta[4]) {
+    using R = RawLds<D, NG>;
     const int g = m / tTile, key = m - g * tTile;
-    const int t = t0 + key;
-    if (g < NG && t < a.T) {
-        const int64_t o = (row0 + t) * NG + g;
-        meta[0] = a.ks[o];
-        meta[1] = a.kb[o];
-        meta[2] = a.vs[o];
-        meta[3] = a.vb[o];
-    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        meta[i] = (g < NG) ? *reinterpret_cast<const uint16_t*>(rawb + R::meta + i * R::meta_bytes +
+                                                                  2 * (key * NG + g))
+                           : 0u;
 }
 
 // Per (group, key) the K scale and bias and the V bias as fp32, and the V
@@ -323,6 +387,7 @@ void attn_tile_kernel(TArgs a) {
     constexpr int CPG = NC / NG;  // chunks per group
     constexpr int NPG = NB / NG;  // output blocks per group
     __shared__ __attribute__((aligned(16))) unsigned char smem[Ly::bytes];
+    __shared__ __attribute__((aligned(16))) unsigned char rawb[RawLds<D, NG>::bytes];
     float* fs = reinterpret_cast<float*>(smem);
 
     const int tid = threadIdx.x;
@@ -348,13 +413,28 @@ void attn_tile_kernel(TArgs a) {
         if (t_lim > vmax) t_lim = vmax;
     }
 
-    // W = 4: the first tile's words (two units and one scale / bias item per
-    // thread) in flight during the set-up, later always one tile ahead
-    TileRaw raw;
-    uint32_t meta[4];
-    if (W == 4 && t_begin < t_lim) {
-        load_units<D>(a, row0, t_begin, tid, kThr, raw);
-        load_meta<NG>(a, row0, t_begin, tid, meta);
+    // the first tile's transfers in flight during the set-up, later always
+    // the next tile's during the compute of one
+    TRsrc rs;
+    {
+        const int kwords = D * a.kbits / 32, vwords = D * a.vbits / 32;
+        const uint32_t* kbase = a.kw + row0 * kwords;
+        const uint32_t* vbase = a.vw + row0 * vwords;
+        rs.kw = tmake_rsrc(kbase, (uint32_t)T * kwords * 4u);
+        rs.vw = tmake_rsrc(vbase, (uint32_t)T * vwords * 4u);
+        // 16-byte transfers need 16-byte aligned slabs and rows (a chunk must
+        // not straddle the end of row T - 1: past the range it reads as zero)
+        rs.k16 = (reinterpret_cast<uintptr_t>(kbase) & 15) == 0 && kwords % 4 == 0;
+        rs.v16 = (reinterpret_cast<uintptr_t>(vbase) & 15) == 0 && vwords % 4 == 0;
+        const uint16_t* mb[4] = {a.ks, a.kb, a.vs, a.vb};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) rs.m[k] = tmake_rsrc(mb[k] + row0 * NG, (uint32_t)T * NG * 2u);
+    }
+    tlds_u8* rawl = (tlds_u8*)rawb;
+    uint32_t meta1[4] = {0u, 0u, 0u, 0u};  // NG = 1: this thread's item, loaded a tile ahead
+    if (t_begin < t_lim) {
+        issue_tile<D, NG, W>(a, rs, t_begin, wave, lane, rawl);
+        if (NG == 1 && tid < 32) load_meta1(a, row0, t_begin, tid, meta1);
     }
 
     // ---- query operands: row 16 wave + n of the block, dims 32 c + 8 j + 0..7 ----
@@ -460,37 +540,39 @@ void attn_tile_kernel(TArgs a) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int g = 0; g < NG; ++g) ob[i][g] = 0.f;
-    int f_run[256 / kThr];  // running scale powers of the groups of this thread's items
+    constexpr int NIT = (32 * NG + kThr - 1) / kThr;  // scale / bias items per thread
+    int f_run[NIT];  // running scale powers of the groups of this thread's items
 #pragma unroll
-    for (int q = 0; q < 256 / kThr; ++q) f_run[q] = 1000;
+    for (int q = 0; q < NIT; ++q) f_run[q] = 1000;
     const float one = 1.0f;
     // this lane's address of the transposing V reads: lane 4 e + c of group j
     // reads key 8 j + 4 h + e, columns 4 c .. 4 c + 3 of an output block
     const unsigned char* vrd = smem + Ly::vc + (8 * j + (n >> 2)) * Ly::VS + 8 * (n & 3);
 
     for (int t0 = t_begin; t0 < t_lim; t0 += tTile) {
-        __syncthreads();  // the previous tile's LDS reads are done
-        if constexpr (W == 4) {
-            store_units<D, W>(a, raw, tid, kThr, smem);
-            store_meta<DT, D, W, NG>(meta, tid, smem, f_run[0]);
-            __syncthreads();
-            if (t0 + tTile < t_lim) {
-                load_units<D>(a, row0, t0 + tTile, tid, kThr, raw);
-                load_meta<NG>(a, row0, t0 + tTile, tid, meta);
-            }
-        } else {
-            // one wave: its 2 D units in pairs (u, u + 64), then its 4 items
+        // the tile's transfers have landed (each wave waits for its own; the
+        // barrier for all) and the previous tile's LDS reads are done
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+        store_units<D, W, NG>(a, rawb, tid, smem);
 #pragma unroll
-            for (int u0 = 0; u0 < 2 * D; u0 += 128) {
-                load_units<D>(a, row0, t0, u0 + tid, 64, raw);
-                store_units<D, W>(a, raw, u0 + tid, 64, smem);
-            }
+        for (int q = 0; q < NIT; ++q) {
+            const int m = q * kThr + tid;
+            if (m < 32 * NG) {  // whole 32-lane groups
+                uint32_t meta[4];
+                if constexpr (NG == 1) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                load_meta<NG>(a, row0, t0, 64 * q + tid, meta);
-                store_meta<DT, D, W, NG>(meta, 64 * q + tid, smem, f_run[q]);
+                    for (int i = 0; i < 4; ++i) meta[i] = meta1[i];
+                } else {
+                    read_meta<D, NG>(rawb, m, meta);
+                }
+                store_meta<DT, D, W, NG>(meta, m, smem, f_run[q]);
             }
-            __syncthreads();
+        }
+        __syncthreads();  // codes in place; the staging area is free
+        if (t0 + tTile < t_lim) {
+            issue_tile<D, NG, W>(a, rs, t0 + tTile, wave, lane, rawl);
+            if (NG == 1 && tid < 32) load_meta1(a, row0, t0 + tTile, tid, meta1);
         }
         if (!wave_live) continue;
 
@@ -725,6 +807,9 @@ int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Til
     chunk = (chunk + tTile - 1) / tTile * tTile;
     S = (T + chunk - 1) / chunk;
     if (units * S > 0x7FFFFFFF || units * RW > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
+    // 32-bit buffer offsets of the tile transfers, up to one tile past T
+    const int64_t bits = c->k_bits > c->v_bits ? c->k_bits : c->v_bits;
+    if ((T + tTile) * (int64_t)c->head_dim * bits / 8 > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
     p->S = (int)S;
     p->RBW = (int)RBW;
     p->W = W;

@@ -187,3 +187,26 @@ def test_variant_snapshot_restore_and_tile(var, dev):
         got = rows[name].cpu()
         got = got.numpy().view(np.uint32) if "words" in name else got.float().numpy()
         np.testing.assert_array_equal(got, oc1.arrays[oname][:, :, :oc1.offset])
+
+
+@pytest.mark.parametrize("var", [VARIANTS[3], VARIANTS[5], VARIANTS[1]], ids=_vid)
+def test_tile_kernel_exact_capacity_cache(var, dev):
+    # A cache restored from a snapshot into fresh buffers holds exactly
+    # `offset` rows (odd here): the slabs of the six arrays are not 16-byte
+    # aligned and the last key row ends the buffer, so the tile transfers take
+    # their 4-byte path and must not read past row T - 1.
+    D = var[0]
+    B, Hq, Hkv, T = 2, 8, 2, 257
+    c, oc, blocks, rot = _setup(var, dev, B, Hkv, T, 24)
+    snap = c.snapshot()
+    e = rbq.RotatedQuantKVCache(B, Hkv, dtype=W._TORCH_DTYPES[var[4]], device=dev, rot=rot,
+                                head_dim=D, group_size=var[1], k_bits=var[2], v_bits=var[3],
+                                round_rotated=var[6])
+    e.restore(snap)
+    assert e.capacity == e.offset == T
+    for L in (1, 3, 17):
+        q = W.random_rows([25, L], (B, Hq, L, D), var[4])
+        out = e.attend(q.to(dev), scale=D ** -0.5, causal=True)
+        torch.cuda.synchronize()
+        ref = O.attention(q.float().numpy(), oc, D ** -0.5, True, blocks)
+        assert float(np.abs(out.cpu().numpy() - ref).max()) <= ATOL, L
