@@ -73,7 +73,9 @@ extern "C" {
  *   k_biases dtype  [B][H_kv][capacity][head_dim/group_size]
  *   v_words  uint32 [B][H_kv][capacity][head_dim*v_bits/32]   (24 words at D=256)
  *   v_scales, v_biases as for K.
- * All six are contiguous device buffers (row stride = capacity rows).  Each
+ * All six are contiguous device buffers (row stride = capacity rows); the
+ * word arrays start 16-byte aligned, the scale and bias arrays 4-byte
+ * aligned (RBQ_EINVAL otherwise; every device allocation is).  Each
  * packed row is a little-endian bit stream: bit t of code j is bit
  * ((bits*j + t) mod 32) of word (bits*j + t) / 32.  Rows [0, offset) are
  * valid; rows at or beyond offset are never read.
@@ -248,6 +250,8 @@ size_t rbq_quant_attn_workspace_bytes(const rbq_kv_cache* c, int32_t H_q, int32_
  *               depend on it beyond fp32 rounding).
  *   ws          device workspace of ws_bytes >= rbq_quant_attn_workspace_bytes
  *               (may be NULL when that is 0).
+ *   Alignment: q 8-byte, out, rot_blocks and ws 16-byte aligned (RBQ_EINVAL
+ *               otherwise).
  * Scores, softmax and the P.V accumulation run in fp32.  Keys [0, offset)
  * are read.  Any L from 1 (decode) to offset (prefill-length blocks) is
  * taken; L is the number of trailing cache rows the query block stands for.

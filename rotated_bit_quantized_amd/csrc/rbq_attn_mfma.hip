@@ -1273,6 +1273,9 @@ extern "C" int rbq_quant_attn_decode_mask(const rbq_kv_cache* c, const void* q, 
     int st = check_attn(c, H_q, L, splits);
     if (st != RBQ_OK) return st;
     if (q == nullptr || out == nullptr) return RBQ_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(q) & 7) != 0 || (reinterpret_cast<uintptr_t>(out) & 15) != 0 ||
+        (reinterpret_cast<uintptr_t>(rot_blocks) & 15) != 0 || (reinterpret_cast<uintptr_t>(ws) & 15) != 0)
+        return RBQ_EINVAL;
     AttnMask mk;
     st = check_mask(c, H_q, L, mask, mask_type, mask_stride_b, mask_stride_h, mask_stride_l, &mk);
     if (st != RBQ_OK) return st;

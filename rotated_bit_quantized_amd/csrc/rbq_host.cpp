@@ -32,6 +32,12 @@ int check_cache(const rbq_kv_cache* c) {
         (c->k_words == nullptr || c->k_scales == nullptr || c->k_biases == nullptr ||
          c->v_words == nullptr || c->v_scales == nullptr || c->v_biases == nullptr))
         return RBQ_EINVAL;
+    // the kernels move the word arrays in 16-byte and the scale / bias arrays
+    // in 4-byte pieces from the array bases
+    auto misaligned = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; };
+    if (misaligned(c->k_words, 16) || misaligned(c->v_words, 16) || misaligned(c->k_scales, 4) ||
+        misaligned(c->k_biases, 4) || misaligned(c->v_scales, 4) || misaligned(c->v_biases, 4))
+        return RBQ_EINVAL;
     return RBQ_OK;
 }
 

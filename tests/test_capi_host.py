@@ -156,6 +156,12 @@ def test_device_entry_points_validate_before_any_device_work():
         e = _host_desc(B=1, H=2, cap=256, off=100, head_dim=hd, group_size=gs, k_bits=kb,
                        v_bits=vb, **ptrs)
         assert lib.rbq_kv_quant_append(by(e), fake, fake, 157, None, None) == capi.RBQ_ECAPACITY
+    # misaligned arrays (the kernels move words in 16-byte, scales in 4-byte pieces)
+    for field, val in (("k_words", fake + 4), ("v_words", fake + 8), ("k_scales", fake + 2),
+                       ("v_biases", fake + 2)):
+        e = _host_desc(B=1, H=2, cap=256, off=100, **ptrs)
+        setattr(e, field, val)
+        assert lib.rbq_kv_quant_append(by(e), fake, fake, 1, None, None) == capi.RBQ_EINVAL, field
     e = _host_desc(B=1, H=2, cap=256, off=100, **ptrs)
     e.flags = 2
     assert lib.rbq_kv_quant_append(by(e), fake, fake, 1, None, None) == capi.RBQ_EINVAL
@@ -170,6 +176,11 @@ def test_device_entry_points_validate_before_any_device_work():
     assert dec(by(d), fake, 4, 101, 0.0625, 1, None, fake, 0, None, 0, None) == capi.RBQ_ERANGE
     assert dec(by(d), fake, 4, 1, 0.0625, 1, None, fake, -2, None, 0, None) == capi.RBQ_EINVAL
     assert dec(by(d), None, 4, 1, 0.0625, 1, None, fake, 0, None, 0, None) == capi.RBQ_EINVAL
+    # misaligned q / out / rotation blocks / workspace
+    assert dec(by(d), fake + 4, 4, 1, 0.0625, 1, None, fake, 0, None, 0, None) == capi.RBQ_EINVAL
+    assert dec(by(d), fake, 4, 1, 0.0625, 1, None, fake + 8, 0, None, 0, None) == capi.RBQ_EINVAL
+    assert dec(by(d), fake, 4, 1, 0.0625, 1, fake + 4, fake, 0, None, 0, None) == capi.RBQ_EINVAL
+    assert dec(by(d), fake, 4, 1, 0.0625, 1, None, fake, 0, fake + 4, 1 << 30, None) == capi.RBQ_EINVAL
     need = lib.rbq_quant_attn_workspace_bytes(by(d), 4, 1, 8)
     assert need > 0
     assert dec(by(d), fake, 4, 1, 0.0625, 1, None, fake, 8, None, 0, None) == capi.RBQ_EWORKSPACE
