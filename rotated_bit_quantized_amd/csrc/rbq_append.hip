@@ -162,19 +162,23 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void quant_append_kernel(
     const int64_t src = row * kHeadDim + lane * 4;
     const int64_t dst = bh * capacity + offset + t;
 
+    // both rows' loads first: K and V are independent chains the wave interleaves
+    float xk[4], xv[4];
+    load4<DT>(k + src, xk);
+    load4<DT>(v + src, xv);
     float Bm[16];
     load_block(rot, lane, Bm);
 
-    float x[4], y[4];
-    load4<DT>(k + src, x);
-    rotate4(x, Bm, y);
-    if (round_rot) round_row<DT>(y);
-    quantize_pack_row<DT, kKBits>(y, lane, kw + dst * kKWords, ks + dst * kGroups,
+    float yk[4], yv[4];
+    rotate4(xk, Bm, yk);
+    rotate4(xv, Bm, yv);
+    if (round_rot) {
+        round_row<DT>(yk);
+        round_row<DT>(yv);
+    }
+    quantize_pack_row<DT, kKBits>(yk, lane, kw + dst * kKWords, ks + dst * kGroups,
                                   kb + dst * kGroups);
-    load4<DT>(v + src, x);
-    rotate4(x, Bm, y);
-    if (round_rot) round_row<DT>(y);
-    quantize_pack_row<DT, kVBits>(y, lane, vw + dst * kVWords, vs + dst * kGroups,
+    quantize_pack_row<DT, kVBits>(yv, lane, vw + dst * kVWords, vs + dst * kGroups,
                                   vb + dst * kGroups);
 }
 
