@@ -210,3 +210,48 @@ def test_tile_kernel_exact_capacity_cache(var, dev):
         torch.cuda.synchronize()
         ref = O.attention(q.float().numpy(), oc, D ** -0.5, True, blocks)
         assert float(np.abs(out.cpu().numpy() - ref).max()) <= ATOL, L
+
+
+def test_tile_kernel_full_prefill_block(dev):
+    # L = offset: every cached row is a query row (row 0 sees one key); four-wave
+    # blocks with a ragged last block
+    var = (128, 32, 3, 5, "bf16", True, False)
+    B, Hq, Hkv, T = 1, 4, 2, 100
+    c, oc, blocks, _ = _setup(var, dev, B, Hkv, T, 26)
+    q = W.random_rows([27, T], (B, Hq, T, 128), "bf16")
+    out = c.attend(q.to(dev), scale=128 ** -0.5, causal=True)
+    torch.cuda.synchronize()
+    ref = O.attention(q.float().numpy(), oc, 128 ** -0.5, True, blocks)
+    assert float(np.abs(out.cpu().numpy() - ref).max()) <= ATOL
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_tile_kernel_four_wave_mask_and_splits(splits, dev):
+    # 24 query rows per kv head (four-wave blocks) with a boolean tree-like mask
+    var = (256, 64, 4, 3, "f16", False, False)
+    B, Hq, Hkv, T, L = 2, 8, 2, 500, 6
+    c, oc, blocks, _ = _setup(var, dev, B, Hkv, T, 28)
+    q = W.random_rows([29, L], (B, Hq, L, 256), "f16")
+    keep = np.ones((1, 1, L, T), bool)
+    keep[..., T - L:] = np.tril(np.ones((L, L), bool))
+    keep[..., 0, T - L + 3:] = False
+    keep[..., 2, T - L + 1] = False
+    out = c.attend(q.to(dev), scale=1 / 16, causal=False, mask=torch.from_numpy(keep).to(dev),
+                   splits=splits)
+    torch.cuda.synchronize()
+    ref = O.attention(q.float().numpy(), oc, 1 / 16, False, blocks, mask=keep)
+    assert float(np.abs(out.cpu().numpy() - ref).max()) <= ATOL
+
+
+@pytest.mark.parametrize("var", [VARIANTS[0], VARIANTS[4]], ids=_vid)
+def test_tile_kernel_single_key(var, dev):
+    # one cached row: the output is that row's dequantised V, rotated back
+    D = var[0]
+    c, oc, blocks, _ = _setup(var, dev, 1, 1, 1, 30, chunks=())
+    q = W.random_rows([31, 1], (1, 2, 1, D), var[4])
+    out = c.attend(q.to(dev), scale=D ** -0.5, causal=True)
+    torch.cuda.synchronize()
+    ref = O.attention(q.float().numpy(), oc, D ** -0.5, True, blocks)
+    vhat = O.inverse_rotate(oc.dequant_kv(0, 0)[1][0].astype(np.float32), blocks)
+    np.testing.assert_allclose(ref[0, 0, 0], vhat, rtol=0, atol=1e-6)
+    assert float(np.abs(out.cpu().numpy() - ref).max()) <= ATOL
