@@ -52,26 +52,25 @@ typedef uint32_t tu32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t tu32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int tTile = 32;                  // keys per tile
-constexpr int tMaxGroups = 8;              // head_dim / group_size <= 8
 constexpr int tPS = tTile + 4;             // floats per row of a wave's P staging
 constexpr float tLog2e = 1.44269504088896340736f;
 
-// LDS of a workgroup of W waves (16 query rows each).
-template <int D, int W>
+// LDS of a workgroup of W waves (16 query rows each), NG groups per row.
+template <int D, int W, int NG>
 struct TileLds {
     static constexpr int KS = 2 * D + 16;                               // bytes per key row of K codes
     static constexpr int VS = 2 * D + 32;                               // bytes per key row of V codes
     static constexpr int kc = 0;                                        // K codes, fp16 [32][KS / 2]
     static constexpr int vc = kc + tTile * KS;                          // V codes, fp16 [32][VS / 2]
-    static constexpr int ksl = vc + tTile * VS;                         // fp32 [8][32] K scales
-    static constexpr int kbl = ksl + tMaxGroups * tTile * 4;            // K biases
-    static constexpr int vsf = kbl + tMaxGroups * tTile * 4;            // V scales x 2^F
-    static constexpr int vbl = vsf + tMaxGroups * tTile * 4;            // V biases
-    static constexpr int vinv = vbl + tMaxGroups * tTile * 4;           // 2^-F per group
-    static constexpr int vres = vinv + tMaxGroups * 4;                  // 2^(F_new - F_old) per group
-    static constexpr int pst = vres + tMaxGroups * 4;                   // [4 waves][16][tPS] fp32
-    static constexpr int qst = pst + W * 16 * tPS * 4;                  // [W waves][8 groups][16 rows]
-    static constexpr int frw = qst + W * tMaxGroups * 16 * 4;           // [W waves][16] 2^-E
+    static constexpr int ksl = vc + tTile * VS;                         // fp32 [NG][32] K scales
+    static constexpr int kbl = ksl + NG * tTile * 4;                    // K biases
+    static constexpr int vsf = kbl + NG * tTile * 4;                    // V scales x 2^F
+    static constexpr int vbl = vsf + NG * tTile * 4;                    // V biases
+    static constexpr int vinv = vbl + NG * tTile * 4;                   // 2^-F per group
+    static constexpr int vres = vinv + NG * 4;                          // 2^(F_new - F_old) per group
+    static constexpr int pst = vres + NG * 4;                           // [W waves][16][tPS] fp32
+    static constexpr int qst = pst + W * 16 * tPS * 4;                  // [W waves][NG groups][16 rows]
+    static constexpr int frw = qst + W * NG * 16 * 4;                   // [W waves][16] 2^-E
     static constexpr int bytes = frw + W * 16 * 4;
 };
 
@@ -279,7 +278,7 @@ __device__ __forceinline__ void read_unit(const TArgs& a, const unsigned char* r
 template <int D, int W, int NG>
 __device__ __forceinline__ void store_units(const TArgs& a, const unsigned char* rawb, int tid,
                                             unsigned char* smem) {
-    using Ly = TileLds<D, W>;
+    using Ly = TileLds<D, W, NG>;
     constexpr int upk = D / 32;
 #pragma unroll
     for (int u = tid; u < 2 * D; u += 64 * W) {
@@ -326,7 +325,7 @@ __device__ __forceinline__ void read_meta(const unsigned char* rawb, int m, uint
 template <int DT, int D, int W, int NG>
 __device__ __forceinline__ void store_meta(const uint32_t meta[4], int m, unsigned char* smem,
                                            int& f_run) {
-    using Ly = TileLds<D, W>;
+    using Ly = TileLds<D, W, NG>;
     const int g = m / tTile, key = m - g * tTile;
     const bool live = g < NG;
     const float s_v = elem_to_f32<DT>(meta[2]);
@@ -379,7 +378,7 @@ __device__ __forceinline__ tu32x2 tr16_read(const unsigned char* p) {
 template <int DT, int D, int NG, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_tile_kernel(TArgs a) {
-    using Ly = TileLds<D, W>;
+    using Ly = TileLds<D, W, NG>;
     constexpr int kThr = 64 * W;
     constexpr int kRW = 16 * W;  // query rows per workgroup
     constexpr int NC = D / 32;    // 32-dim chunks
@@ -502,7 +501,7 @@ void attn_tile_kernel(TArgs a) {
             float s = gsum[g];
             s += __shfl_xor(s, 16);
             s += __shfl_xor(s, 32);
-            if (j == 0) fs[Ly::qst / 4 + (wave * tMaxGroups + g) * 16 + n] = s;
+            if (j == 0) fs[Ly::qst / 4 + (wave * NG + g) * 16 + n] = s;
         }
         if (j == 0) fs[Ly::frw / 4 + wave * 16 + n] = ldexpf(1.0f, -E);
     }
@@ -599,7 +598,7 @@ void attn_tile_kernel(TArgs a) {
             const float s0 = fs[Ly::ksl / 4 + g * tTile + n], s1 = fs[Ly::ksl / 4 + g * tTile + 16 + n];
             const float b0 = fs[Ly::kbl / 4 + g * tTile + n], b1 = fs[Ly::kbl / 4 + g * tTile + 16 + n];
             const tf32x4 qs = *reinterpret_cast<const tf32x4*>(
-                fs + Ly::qst / 4 + (wave * tMaxGroups + g) * 16 + 4 * j);
+                fs + Ly::qst / 4 + (wave * NG + g) * 16 + 4 * j);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 sacc[0][i] += s0 * acc[0][i];
@@ -740,52 +739,116 @@ struct TMArgs {
     int S, Hkv, n_rep, L, G, RBW, RW;
 };
 
-// Merge of the key-split records of one query row (64 threads, 4 columns
-// each): m* = max_s m_s, l* = sum_s l_s 2^(m_s - m*), o = sum_s o_s 2^(m_s - m*) / l*,
-// in split order; then the inverse rotation of each 4-column block and the
-// fp32 store.
+constexpr int tMaxSplits = 1024;  // key splits of one call (the merge keeps a weight per split)
+
+// Reduction over the 256 threads of a block through LDS slot array `red`.
+template <bool MAX>
+__device__ __forceinline__ float block_reduce(float x, float* red) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const float y = __shfl_xor(x, m);
+        x = MAX ? fmaxf(x, y) : x + y;
+    }
+    const int tid = threadIdx.x;
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = x;
+    __syncthreads();
+    x = red[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) x = MAX ? fmaxf(x, red[w]) : x + red[w];
+    return x;
+}
+
+// Merge of the key-split records of one query row (256 threads): m* =
+// max_s m_s, weights w_s = 2^(m_s - m*) (0 for an empty split), l* =
+// sum_s l_s w_s, o = sum_s w_s o_s / l*, the sum taken over split groups
+// s = g mod (256 / (D / 4)) by thread (column quad, group) and the groups
+// then added in order; then the inverse rotation of each 4-column block and
+// the fp32 store.
 template <int D>
-__global__ __launch_bounds__(64) void attn_tile_merge_kernel(TMArgs a) {
+__global__ __launch_bounds__(256) void attn_tile_merge_kernel(TMArgs a) {
+    constexpr int NQ = D / 4;     // column quads
+    constexpr int NSG = 256 / NQ;  // split groups
+    __shared__ float wsh[tMaxSplits];
+    __shared__ float red[4];
+    __shared__ float4 part[NSG][NQ];
     const int rowg = blockIdx.x;  // (b, kv head, row block, row)
     const int RW = a.RW;
     const int rr = rowg % RW;
     const int bhr = rowg / RW;
     const int bh = bhr / a.RBW;
     const int R = RW * (bhr - bh * a.RBW) + rr;
-    if (R >= a.G) return;
-    const int k = threadIdx.x;
-    if (k >= D / 4) return;
+    if (R >= a.G) return;  // uniform: one row per block
+    const int tid = threadIdx.x;
     const int b = bh / a.Hkv, kvh = bh - b * a.Hkv;
-    float M = -INFINITY;
-    for (int s = 0; s < a.S; ++s) M = fmaxf(M, a.rec_ml[((int64_t)bhr * a.S + s) * RW * 2 + 2 * rr]);
-    float Ls = 0.f;
+    const float* ml = a.rec_ml + (int64_t)bhr * a.S * RW * 2 + 2 * rr;
+    float mx = -INFINITY;
+    for (int s = tid; s < a.S; s += 256) mx = fmaxf(mx, ml[(int64_t)s * RW * 2]);
+    const float M = block_reduce<true>(mx, red);
+    float lsum = 0.f;
+    for (int s = tid; s < a.S; s += 256) {
+        const float m = ml[(int64_t)s * RW * 2];
+        const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+        wsh[s] = w;
+        lsum += ml[(int64_t)s * RW * 2 + 1] * w;
+    }
+    const float Ls = block_reduce<false>(lsum, red);  // its barriers also publish wsh
+    const int k = tid % NQ, sg = tid / NQ;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float* ro = a.rec_o + ((int64_t)bhr * a.S * RW + rr) * D + 4 * k;
+    for (int s = sg; s < a.S; s += NSG) {
+        const float w = wsh[s];
+        const float4 v = *reinterpret_cast<const float4*>(ro + (int64_t)s * RW * D);
+        acc.x += v.x * w;
+        acc.y += v.y * w;
+        acc.z += v.z * w;
+        acc.w += v.w * w;
+    }
+    part[sg][k] = acc;
+    __syncthreads();
+    if (tid >= NQ) return;
     float o[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < a.S; ++s) {
-        const int64_t u = (int64_t)bhr * a.S + s;
-        const float m = a.rec_ml[u * RW * 2 + 2 * rr];
-        if (m == -INFINITY) continue;
-        const float w = exp2f(m - M);
-        Ls += a.rec_ml[u * RW * 2 + 2 * rr + 1] * w;
-        const float4 v = *reinterpret_cast<const float4*>(a.rec_o + (u * RW + rr) * D + 4 * k);
-        o[0] += v.x * w;
-        o[1] += v.y * w;
-        o[2] += v.z * w;
-        o[3] += v.w * w;
+#pragma unroll
+    for (int g = 0; g < NSG; ++g) {
+        const float4 p = part[g][tid];
+        o[0] += p.x;
+        o[1] += p.y;
+        o[2] += p.z;
+        o[3] += p.w;
     }
     const float inv = 1.0f / Ls;
     float y[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
     float z[4] = {y[0], y[1], y[2], y[3]};
     if (a.rot != nullptr) {
         float Bm[16];
-        load_block(a.rot, k, Bm);
+        load_block(a.rot, tid, Bm);
         unrotate4(y, Bm, z);
     }
     const int hq = kvh * a.n_rep + R / a.L;
-    float* dst = a.out + (((int64_t)b * a.Hkv * a.n_rep + hq) * a.L + R % a.L) * D + 4 * k;
+    float* dst = a.out + (((int64_t)b * a.Hkv * a.n_rep + hq) * a.L + R % a.L) * D + 4 * tid;
     *reinterpret_cast<float4*>(dst) = make_float4(z[0], z[1], z[2], z[3]);
 }
 
 }  // namespace
+
+// Workgroups of one shape that fit a compute unit: LDS (160 KiB) and two
+// waves per SIMD at most.
+template <int D, int NG, int W>
+constexpr int tile_fit() {
+    constexpr int lds = TileLds<D, W, NG>::bytes + RawLds<D, NG>::bytes;
+    constexpr int by_lds = 160 * 1024 / lds;
+    constexpr int by_waves = 8 / W;
+    return by_lds < by_waves ? by_lds : by_waves;
+}
+
+static int tile_workgroups_per_cu(int D, int ng, int W) {
+#define RBQ_FIT(D_, NG_)                                                   \
+    if (D == D_ && ng == NG_) return W == 4 ? tile_fit<D_, NG_, 4>() : tile_fit<D_, NG_, 1>();
+    RBQ_FIT(64, 1) RBQ_FIT(64, 2) RBQ_FIT(128, 1) RBQ_FIT(128, 2) RBQ_FIT(128, 4)
+    RBQ_FIT(256, 2) RBQ_FIT(256, 4) RBQ_FIT(256, 8)
+#undef RBQ_FIT
+    return 1;
+}
 
 int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, TilePlan* p) {
     const int64_t G = (int64_t)(H_q / c->H_kv) * L;
@@ -796,13 +859,17 @@ int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Til
     const int64_t units = (int64_t)c->B * c->H_kv * RBW;
     int64_t S = splits;
     if (S == 0) {
-        // about four workgroups per compute unit (of four waves, or of one:
-        // more, shorter single-wave splits lose more to set-up and records)
-        S = (1024 + units - 1) / units;
+        // one round of workgroups over the 256 compute units, as many per
+        // unit as LDS and registers allow (longer splits lose less to set-up
+        // and records than a second round gains)
+        const int ng = c->head_dim / c->group_size;
+        const int per_cu = tile_workgroups_per_cu(c->head_dim, ng, W);
+        S = (256 * per_cu + units - 1) / units;
         const int64_t max_s = (T + tTile - 1) / tTile;
         if (S > max_s) S = max_s;
     }
     if (S < 1) S = 1;
+    if (S > tMaxSplits) S = tMaxSplits;
     int64_t chunk = (T + S - 1) / S;
     chunk = (chunk + tTile - 1) / tTile * tTile;
     S = (T + chunk - 1) / chunk;
@@ -884,7 +951,7 @@ int tile_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
     m.G = a.G;
     m.RBW = p.RBW;
     m.RW = 16 * p.W;
-    const dim3 mgrid((unsigned)(units * 16 * p.W)), mblock(64);
+    const dim3 mgrid((unsigned)(units * 16 * p.W)), mblock(256);
     switch (c->head_dim) {
         case 64: hipLaunchKernelGGL(attn_tile_merge_kernel<64>, mgrid, mblock, 0, s, m); break;
         case 128: hipLaunchKernelGGL(attn_tile_merge_kernel<128>, mgrid, mblock, 0, s, m); break;
