@@ -269,8 +269,34 @@ __device__ __forceinline__ void read_unit(const TArgs& a, const unsigned char* r
     const int bits = isv ? a.vbits : a.kbits;
     const uint32_t* src = reinterpret_cast<const uint32_t*>(rawb + (isv ? R::vw : R::kw)) +
                           key * (D * bits / 32) + part * bits;
+    // consecutive lanes read consecutive units (bits words apart): 2-, 4- and
+    // 8-bit units as whole 8- or 16-byte reads (word reads at a stride of 4
+    // or 8 words would hit the same banks), the others word by word (odd
+    // strides spread over all banks)
+    if (bits == 4) {
+        const tu32x4 v = *reinterpret_cast<const tu32x4*>(src);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = (i < bits) ? src[i] : 0u;
+        for (int i = 0; i < 4; ++i) w[i] = v[i];
+#pragma unroll
+        for (int i = 4; i < 8; ++i) w[i] = 0u;
+    } else if (bits == 8) {
+        const tu32x4 v0 = *reinterpret_cast<const tu32x4*>(src);
+        const tu32x4 v1 = *reinterpret_cast<const tu32x4*>(src + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w[i] = v0[i];
+            w[4 + i] = v1[i];
+        }
+    } else if (bits == 2) {
+        const tu32x2 v = *reinterpret_cast<const tu32x2*>(src);
+        w[0] = v[0];
+        w[1] = v[1];
+#pragma unroll
+        for (int i = 2; i < 8; ++i) w[i] = 0u;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = (i < bits) ? src[i] : 0u;
+    }
 }
 
 // K and V codes of the tile into LDS as fp16 [key][dim], from the staged
