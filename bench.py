@@ -327,6 +327,9 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph (on this stack a replay "
                          "costs more than the two launches it holds)")
+    ap.add_argument("--leg", choices=["prefill", "variant_decode", "tree_verify"],
+                    help="run only this secondary measurement and print its object "
+                         "(for profiling it on its own; not the benchmark line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -336,6 +339,16 @@ def main() -> int:
     import rotated_bit_quantized_amd as rbq
     from rotated_bit_quantized_amd import capi
     import workloads as W
+
+    if args.leg is not None:
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        rot = rbq.build_block_so4(256, W.ROTATION_SEED, dev)
+        leg = {"prefill": lambda: prefill(rbq, W, dev, rot),
+               "variant_decode": lambda: variant_decode(rbq, W, dev),
+               "tree_verify": lambda: tree_verify(rbq, W, dev, rot)}[args.leg]
+        print(json.dumps({args.leg: leg()}), flush=True)
+        return 0
 
     w = W.WORKLOADS[3]
     dev = torch.device("cuda:0")
