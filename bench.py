@@ -207,21 +207,27 @@ def tree_verify(rbq, W, dev, rot, n_calls: int = 200) -> dict:
     }
 
 
-def prefill(rbq, W, dev, rot, n_calls: int = 10) -> dict:
+def prefill(rbq, W, dev, rot, n_calls: int = 10, head_dim: int = 256) -> dict:
     """Prefill-length attention over the quantized cache: B=1, 16 q heads /
     2 kv heads, head_dim 256, bf16, K4/V3 group 64; a cache of 8192 tokens,
     a chunk of L = 2048 new tokens appended (rotated, quantized, packed), then
     the fused attention of the chunk's 2048 query rows per head over the
-    10240 cached tokens with the causal mask at the offset (the general tile
-    kernel: 256 blocks of 64 query rows).  Algorithmic flops: 4 * head_dim
-    per (query row, visible key) (q.k and p.v, multiply-add = 2)."""
-    Hkv, Hq, T0, L, D = 2, 16, 8192, 2048, 256
+    10240 cached tokens with the causal mask at the offset (the dedicated
+    kernel's 8-row blocks).  With ``head_dim=128`` the cache is head_dim 128,
+    group 64, K4/V4, two-sided rotation (the tile kernel's 64-row blocks).
+    Algorithmic flops: 4 * head_dim per (query row, visible key) (q.k and
+    p.v, multiply-add = 2)."""
+    Hkv, Hq, T0, L = 2, 16, 8192, 2048
+    D = head_dim
+    if D != 256:
+        rot = rbq.build_block_so4(D, 0, dev, two_sided=True)
+    cfg = {} if D == 256 else dict(head_dim=D, group_size=64, k_bits=4, v_bits=4)
     k = W.random_rows([50, 1], (1, Hkv, T0, D), "bf16").to(dev)
     v = W.random_rows([50, 2], (1, Hkv, T0, D), "bf16").to(dev)
     kn = W.random_rows([50, 3], (1, Hkv, L, D), "bf16").to(dev)
     vn = W.random_rows([50, 4], (1, Hkv, L, D), "bf16").to(dev)
     q = W.random_rows([50, 5], (1, Hq, L, D), "bf16").to(dev)
-    c = rbq.RotatedQuantKVCache(1, Hkv, device=dev, rot=rot)
+    c = rbq.RotatedQuantKVCache(1, Hkv, device=dev, rot=rot, **cfg)
     c.append(k, v)
     c.reserve(L)
     stream = torch.cuda.current_stream()
@@ -242,10 +248,10 @@ def prefill(rbq, W, dev, rot, n_calls: int = 10) -> dict:
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     ws = c.workspace(Hq, L)
     for _ in range(2):
-        rbq.rbq_quant_attn_decode(c.desc, q, 1 / 16, True, rot, out, 0, ws)
+        rbq.rbq_quant_attn_decode(c.desc, q, D ** -0.5, True, rot, out, 0, ws)
     ev0.record(stream)
     for _ in range(n_calls):
-        rbq.rbq_quant_attn_decode(c.desc, q, 1 / 16, True, rot, out, 0, ws)
+        rbq.rbq_quant_attn_decode(c.desc, q, D ** -0.5, True, rot, out, 0, ws)
     ev1.record(stream)
     torch.cuda.synchronize()
     us = ev0.elapsed_time(ev1) * 1e3 / n_calls
@@ -253,8 +259,12 @@ def prefill(rbq, W, dev, rot, n_calls: int = 10) -> dict:
     flops = 4 * D * pairs
     tfs = flops / (us * 1e-6) / 1e12
     return {
-        "what": f"prefill chunk: {L} new tokens over {T0} cached (T={T}), B=1, {Hq}/{Hkv} heads, "
-                "head_dim 256, bf16, K4/V3 group 64, causal at the offset (tile kernel)",
+        "what": (f"prefill chunk: {L} new tokens over {T0} cached (T={T}), B=1, {Hq}/{Hkv} heads, "
+                 "head_dim 256, bf16, K4/V3 group 64, causal at the offset (the dedicated kernel: "
+                 "4096 blocks of 8 query rows)") if D == 256 else
+                (f"prefill chunk: {L} new tokens over {T0} cached (T={T}), B=1, {Hq}/{Hkv} heads, "
+                 "head_dim 128, bf16, K4/V4 group 64, two-sided rotation, causal at the offset "
+                 "(the tile kernel: 512 blocks of 64 query rows)"),
         "bound": "mfma",
         "alg_flops_per_call": flops,
         "avg_us": round(us, 2),
@@ -327,7 +337,7 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph (on this stack a replay "
                          "costs more than the two launches it holds)")
-    ap.add_argument("--leg", choices=["prefill", "variant_decode", "tree_verify"],
+    ap.add_argument("--leg", choices=["prefill", "variant_decode", "variant_prefill", "tree_verify"],
                     help="run only this secondary measurement and print its object "
                          "(for profiling it on its own; not the benchmark line)")
     args = ap.parse_args()
@@ -346,6 +356,7 @@ def main() -> int:
         rot = rbq.build_block_so4(256, W.ROTATION_SEED, dev)
         leg = {"prefill": lambda: prefill(rbq, W, dev, rot),
                "variant_decode": lambda: variant_decode(rbq, W, dev),
+               "variant_prefill": lambda: prefill(rbq, W, dev, rot, head_dim=128),
                "tree_verify": lambda: tree_verify(rbq, W, dev, rot)}[args.leg]
         print(json.dumps({args.leg: leg()}), flush=True)
         return 0
@@ -454,8 +465,9 @@ def main() -> int:
     tree = tree_verify(rbq, W, dev, rot)
     print("[bench] prefill chunk", file=sys.stderr, flush=True)
     pre = prefill(rbq, W, dev, rot)
-    print("[bench] decode, head_dim 128 K4/V4", file=sys.stderr, flush=True)
+    print("[bench] decode and prefill, head_dim 128 K4/V4", file=sys.stderr, flush=True)
     var = variant_decode(rbq, W, dev)
+    pre128 = prefill(rbq, W, dev, rot, head_dim=128)
 
     nbytes = algorithmic_bytes(w, w.T)
     ms_per_step = total * 1e3 / args.steps
@@ -514,6 +526,7 @@ def main() -> int:
         "tree_verify": tree,
         "prefill": pre,
         "variant_decode": var,
+        "variant_prefill": pre128,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)

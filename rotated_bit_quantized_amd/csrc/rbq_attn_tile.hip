@@ -85,6 +85,7 @@ struct TArgs {
     const float* rot;
     float* rec_o;   // [units][S][RW rows][D]
     float* rec_ml;  // [units][S][RW rows][2]
+    float* out;     // with one split the workgroups store the output directly
     int64_t capacity;
     int T, chunk, S, Hkv, n_rep, L, G, RBW, causal, round_rot;
     int GS, kbits, vbits;
@@ -729,8 +730,44 @@ void attn_tile_kernel(TArgs a) {
         }
     }
 
-    // ---- record: (m, l) and the unnormalised o of each row ----
+    // ---- record: (m, l) and the unnormalised o of each row; with one split
+    //      the normalised row itself, rotated back (a rotation block's four
+    //      columns sit in one lane quad: DPP broadcasts, fp64 sum) ----
     if (!wave_live) return;
+    if (a.S == 1) {
+        float vinv1[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) vinv1[g] = (t_begin < t_lim) ? fs[Ly::vinv / 4 + g] : 1.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int R = r0 + 16 * wave + 4 * j + i;
+            const float inv = 1.0f / tsum16(l_part[i]);
+            if (R >= a.G) continue;  // uniform over the 16 lanes of the row
+            const int hq = kvh * a.n_rep + R / a.L;
+            float* orow = a.out + (((int64_t)b * a.Hkv * a.n_rep + hq) * a.L + R % a.L) * D;
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const float bias = tsum16(ob[i][g]);
+#pragma unroll
+                for (int t = g * NPG; t < (g + 1) * NPG; ++t) {
+                    const int col = 16 * t + n;
+                    const float y = (O[t][i] * vinv1[g] + bias) * inv;
+                    float z = y;
+                    if (a.rot != nullptr) {
+                        const float4 v = *reinterpret_cast<const float4*>(a.rot + 16 * (col >> 2) + 4 * (col & 3));
+                        const float y0 = tdpp<0x00>(y), y1 = tdpp<0x55>(y), y2 = tdpp<0xAA>(y), y3 = tdpp<0xFF>(y);
+                        double s2 = (double)y0 * (double)v.x;
+                        s2 = s2 + (double)y1 * (double)v.y;
+                        s2 = s2 + (double)y2 * (double)v.z;
+                        s2 = s2 + (double)y3 * (double)v.w;
+                        z = (float)s2;
+                    }
+                    orow[col] = z;
+                }
+            }
+        }
+        return;
+    }
     const int64_t unit = (int64_t)bhr * a.S + split;
     float* ro = a.rec_o + unit * kRW * D;
     float* rml = a.rec_ml + unit * kRW * 2;
@@ -871,6 +908,9 @@ static int tile_workgroups_per_cu(int D, int ng, int W) {
 #define RBQ_FIT(D_, NG_)                                                   \
     if (D == D_ && ng == NG_) return W == 4 ? tile_fit<D_, NG_, 4>() : tile_fit<D_, NG_, 1>();
     RBQ_FIT(64, 1) RBQ_FIT(64, 2) RBQ_FIT(128, 1) RBQ_FIT(128, 2) RBQ_FIT(128, 4)
+#undef RBQ_FIT
+#define RBQ_FIT(D_, NG_) \
+    if (D == D_ && ng == NG_) return tile_fit<D_, NG_, 4>();
     RBQ_FIT(256, 2) RBQ_FIT(256, 4) RBQ_FIT(256, 8)
 #undef RBQ_FIT
     return 1;
@@ -878,7 +918,12 @@ static int tile_workgroups_per_cu(int D, int ng, int W) {
 
 int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, TilePlan* p) {
     const int64_t G = (int64_t)(H_q / c->H_kv) * L;
-    const int W = (G <= 16) ? 1 : 4;  // waves per workgroup, 16 rows each
+    // waves per workgroup, 16 rows each: one wave for up to 16 rows at
+    // head_dim <= 128; at head_dim 256 always four (the one-wave kernels fit
+    // only two workgroups per compute unit there, and one of their builds,
+    // 4 groups per row, gave wrong results that changed with the
+    // optimisation level: that shape is not used)
+    const int W = (G <= 16 && c->head_dim <= 128) ? 1 : 4;
     const int64_t RW = 16 * W;
     const int64_t RBW = (G + RW - 1) / RW;
     const int64_t T = c->offset;
@@ -908,7 +953,8 @@ int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Til
     p->W = W;
     p->chunk = chunk;
     p->o_floats = (size_t)(units * S) * RW * c->head_dim;
-    p->ws_bytes = (p->o_floats + (size_t)(units * S) * RW * 2) * sizeof(float);
+    // one split: the attention kernel stores the output itself
+    p->ws_bytes = (S == 1) ? 0 : (p->o_floats + (size_t)(units * S) * RW * 2) * sizeof(float);
     return RBQ_OK;
 }
 
@@ -927,6 +973,7 @@ int tile_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
     a.rot = rot_blocks;
     a.rec_o = (float*)ws;
     a.rec_ml = (float*)ws + p.o_floats;
+    a.out = out;
     a.capacity = c->capacity;
     a.T = (int)c->offset;
     a.chunk = (int)p.chunk;
@@ -960,11 +1007,24 @@ int tile_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
         else                                                                                      \
             bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_, 1>) : launch(attn_tile_kernel<RBQ_F16, D_, NG_, 1>); \
     } else
+#define RBQ_TILE_CASE4(D_, NG_)                                                                   \
+    if (c->head_dim == D_ && ng == NG_) {                                                         \
+        bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_, 4>) : launch(attn_tile_kernel<RBQ_F16, D_, NG_, 4>); \
+    } else
     RBQ_TILE_CASE(64, 1) RBQ_TILE_CASE(64, 2) RBQ_TILE_CASE(128, 1) RBQ_TILE_CASE(128, 2)
-    RBQ_TILE_CASE(128, 4) RBQ_TILE_CASE(256, 2) RBQ_TILE_CASE(256, 4) RBQ_TILE_CASE(256, 8) {
+    RBQ_TILE_CASE(128, 4) RBQ_TILE_CASE4(256, 2) RBQ_TILE_CASE4(256, 4) RBQ_TILE_CASE4(256, 8) {
         return RBQ_EUNSUPPORTED;
     }
 #undef RBQ_TILE_CASE
+#undef RBQ_TILE_CASE4
+    if (p.S == 1) {
+        const hipError_t e1 = hipGetLastError();
+        if (e1 != hipSuccess) {
+            set_hip_error((int)e1);
+            return RBQ_EHIP;
+        }
+        return RBQ_OK;
+    }
     TMArgs m;
     m.rec_o = a.rec_o;
     m.rec_ml = a.rec_ml;

@@ -31,6 +31,8 @@ VARIANTS = [
     (256, 32, 6, 5, "bf16", True, False),
     (64, 64, 4, 3, "bf16", False, False),
     (256, 64, 4, 3, "bf16", True, True),   # default sizes, dedicated kernels, both options
+    (128, 32, 4, 4, "bf16", False, False),
+    (256, 64, 4, 4, "f16", True, False),   # head_dim 256, 4 groups: four-wave blocks also for 1-16 rows
     (256, 64, 4, 3, "f16", False, True),
 ]
 
@@ -101,12 +103,14 @@ def test_variant_attention(var, dev):
         assert err <= ATOL, (L, causal, err)
 
 
+@pytest.mark.parametrize("var", [(256, 64, 4, 3, "bf16", False, False),
+                                 (256, 64, 4, 4, "bf16", False, False)], ids=_vid)
 @pytest.mark.parametrize("L", [70, 129])
-def test_tile_kernel_long_query_blocks(L, dev):
-    # prefill-length query blocks of the default configuration: G = 8 L rows
-    # per kv head run the tile kernel (several 64-row blocks, a ragged last one)
-    var = (256, 64, 4, 3, "bf16", False, False)
-    print(f"[tile long block] L={L}", flush=True)
+def test_long_query_blocks(L, var, dev):
+    # prefill-length query blocks: G = 8 L rows per kv head (the default
+    # configuration in 8-row blocks of the dedicated kernel; K4/V4 in 64-row
+    # blocks of the tile kernel, a ragged last one)
+    print(f"[long block] {_vid(var)} L={L}", flush=True)
     B, Hq, Hkv, T = 1, 16, 2, 700
     c, oc, blocks, _ = _setup(var, dev, B, Hkv, T, 14)
     q = W.random_rows([15, L], (B, Hq, L, 256), "bf16")
@@ -115,9 +119,9 @@ def test_tile_kernel_long_query_blocks(L, dev):
     ref = O.attention(q.float().numpy(), oc, 1 / 16, True, blocks)
     err = float(np.abs(out.cpu().numpy() - ref).max())
     assert err <= ATOL, err
-    # row 0 of the block is an L = 1 decode over the keys it sees (run by the
-    # dedicated kernel: the two kernels round differently, both within the
-    # tolerance of the oracle)
+    # row 0 of the block is an L = 1 decode over the keys it sees (a call of
+    # another shape, which rounds differently: both within the tolerance of
+    # the oracle)
     c.trim(L - 1)
     oc.trim(L - 1)
     q1 = q[:, :, :1].contiguous()
@@ -127,7 +131,7 @@ def test_tile_kernel_long_query_blocks(L, dev):
     np.testing.assert_allclose(ref1, ref[:, :, :1], rtol=0, atol=1e-9)
     err1 = float(np.abs(out1.cpu().numpy() - ref1).max())
     cross = float(np.abs(out1.cpu().numpy() - out[:, :, :1].cpu().numpy()).max())
-    print(f"tile kernel error {err:.2e}, dedicated kernel {err1:.2e}, between them {cross:.2e}")
+    print(f"block error {err:.2e}, decode of row 0 {err1:.2e}, between them {cross:.2e}")
     assert err1 <= ATOL and cross <= ATOL
 
 
@@ -228,18 +232,18 @@ def test_tile_kernel_full_prefill_block(dev):
 @pytest.mark.parametrize("splits", [1, 4])
 def test_tile_kernel_four_wave_mask_and_splits(splits, dev):
     # 24 query rows per kv head (four-wave blocks) with a boolean tree-like mask
-    var = (256, 64, 4, 3, "f16", False, False)
+    var = (128, 64, 4, 3, "f16", False, False)
     B, Hq, Hkv, T, L = 2, 8, 2, 500, 6
     c, oc, blocks, _ = _setup(var, dev, B, Hkv, T, 28)
-    q = W.random_rows([29, L], (B, Hq, L, 256), "f16")
+    q = W.random_rows([29, L], (B, Hq, L, 128), "f16")
     keep = np.ones((1, 1, L, T), bool)
     keep[..., T - L:] = np.tril(np.ones((L, L), bool))
     keep[..., 0, T - L + 3:] = False
     keep[..., 2, T - L + 1] = False
-    out = c.attend(q.to(dev), scale=1 / 16, causal=False, mask=torch.from_numpy(keep).to(dev),
+    out = c.attend(q.to(dev), scale=128 ** -0.5, causal=False, mask=torch.from_numpy(keep).to(dev),
                    splits=splits)
     torch.cuda.synchronize()
-    ref = O.attention(q.float().numpy(), oc, 1 / 16, False, blocks, mask=keep)
+    ref = O.attention(q.float().numpy(), oc, 128 ** -0.5, False, blocks, mask=keep)
     assert float(np.abs(out.cpu().numpy() - ref).max()) <= ATOL
 
 
