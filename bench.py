@@ -6,9 +6,12 @@ group 64, K 4-bit / V 3-bit): the current token's K/V rows are rotated,
 quantized, packed and appended at row T-1 (so attention sees T tokens), the
 fused attention of the rotated query over the packed cache runs with the
 causal mask at the offset and the inverse rotation of its output, and the
-token is trimmed again so every step sees the same T.  The rotation blocks
-are built once before timing.  The step's launches are issued from Python
-(``--graph`` replays them from a captured HIP graph instead).
+token is trimmed again so every step sees the same T.  The append and the
+attention are one library call (``rbq_kv_append_attn_decode``: the attention
+kernel writes the token's rows itself); the same step as two calls is timed
+beside it.  The rotation blocks are built once before timing.  The step's
+launches are issued from Python (``--graph`` replays them from a captured HIP
+graph instead).
 
 Inputs are synthetic (``workloads``), resident in HBM before timing.  The
 cache is replicated (default 4 copies, 512 MiB) and the steps cycle through
@@ -383,30 +386,42 @@ def main() -> int:
         caches.append(c)
     assert base.capacity >= w.T
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    ws = base.workspace(w.Hq, w.L, args.splits)
-    ws = None if ws is None else ws.clone()
-    splits_used = capi.rbq_quant_attn_splits(base.desc, w.Hq, w.L) if args.splits == 0 \
+    after = capi.rbq_kv_cache.from_buffer_copy(base.desc)
+    after.offset = w.T  # the attention runs over T rows
+    nb_ws = capi.rbq_quant_attn_workspace_bytes(after, w.Hq, w.L, args.splits)
+    ws = torch.empty(nb_ws, dtype=torch.uint8, device=dev) if nb_ws else None
+    splits_used = capi.rbq_quant_attn_splits(after, w.Hq, w.L) if args.splits == 0 \
         else args.splits
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
+    # One step: the token's rows appended at row T-1 and the attention over T
+    # rows in one library call (the attention kernel writes the rows itself),
+    # then the trim back to T-1 (host-side bookkeeping).  `step_two_calls` is
+    # the same step as the append call followed by the attention call.
     def step(i):
+        c = caches[i % len(caches)]
+        capi.rbq_kv_append_attn_decode(c.desc, k_new, v_new, q, 1 / 16, True, rot, out,
+                                       args.splits, ws)
+        capi.rbq_kv_trim(c.desc, 1)
+
+    def step_two_calls(i):
         c = caches[i % len(caches)]
         capi.rbq_kv_quant_append(c.desc, k_new, v_new, rot)
         capi.rbq_quant_attn_decode(c.desc, q, 1 / 16, True, rot, out, args.splits, ws)
         capi.rbq_kv_trim(c.desc, 1)
 
-    # --graph: one HIP graph per cache replica holds the step's two launches
-    # (append at row T-1, attention over T rows) with their arguments as
-    # captured; the trim back to T-1 is host-side bookkeeping only.
+    # --graph: one HIP graph per cache replica holds the step's launches with
+    # their arguments as captured; the trim back to T-1 is host-side
+    # bookkeeping only.
     graphs = []
     if args.graph:
         cap = torch.cuda.Stream()
         for c in caches:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
-                capi.rbq_kv_quant_append(c.desc, k_new, v_new, rot)
-                capi.rbq_quant_attn_decode(c.desc, q, 1 / 16, True, rot, out, args.splits, ws)
+                capi.rbq_kv_append_attn_decode(c.desc, k_new, v_new, q, 1 / 16, True, rot, out,
+                                               args.splits, ws)
             capi.rbq_kv_trim(c.desc, 1)
             graphs.append(g)
         torch.cuda.synchronize()
@@ -425,6 +440,15 @@ def main() -> int:
         run(i)
     torch.cuda.synchronize()
     total = time.perf_counter() - t0
+    # the same number of steps as two calls (append, then attention)
+    for i in range(min(args.warmup, 200)):
+        step_two_calls(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step_two_calls(i)
+    torch.cuda.synchronize()
+    total_two = time.perf_counter() - t0
 
     # The attention kernel alone: back-to-back launches on the stream it runs
     # on, HIP events at both ends (an event pair around every launch would add
@@ -511,7 +535,13 @@ def main() -> int:
             "alg_bytes_per_launch": nbytes["attn"],
             "avg_launch_us": round(attn_avg_s * 1e6, 3),
         },
-        "step": "HIP graph replay (append + attention)" if graphs else "eager launches",
+        "step": ("HIP graph replay" if graphs else "eager launches") +
+                " of rbq_kv_append_attn_decode (append of the token and attention in one call)",
+        "two_call_step": {
+            "what": "the same step as rbq_kv_quant_append + rbq_quant_attn_decode (eager)",
+            "ms_per_step": round(total_two * 1e3 / args.steps, 5),
+            "value": round(nbytes["step"] / (total_two / args.steps) / 1e9, 2),
+        },
         "snapshot": {
             "what": f"cache snapshot: prefix copy of the six arrays, {w.T - 1} rows x "
                     f"{w.B * w.Hkv} (b, kv head) slabs (rbq_kv_copy_prefix, copy_prefix_kernel)",

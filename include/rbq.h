@@ -268,6 +268,30 @@ int rbq_quant_attn_decode(const rbq_kv_cache* c, const void* q, int32_t H_q, int
                           float scale, int32_t causal, const float* rot_blocks, float* out,
                           int32_t splits, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * rbq_kv_append_attn_decode - one decode (or verify) step: rbq_kv_quant_append
+ * of n rows followed by rbq_quant_attn_decode over the cache that results,
+ * with the same rot_blocks (the cache update of update_and_fetch and
+ * asym_quantized_sdpa on the quant_kv.py page, as one decoding step runs
+ * them).  The cache rows written, c->offset and out are what those two calls
+ * give, bit for bit.
+ *   k, v, n     as rbq_kv_quant_append (k, v may be NULL when n == 0).
+ *   q ... ws    as rbq_quant_attn_decode, for the cache after the append:
+ *               L <= offset + n, and ws_bytes >= rbq_quant_attn_workspace_bytes
+ *               of a descriptor whose offset is offset + n.
+ * In the default configuration with H_q / H_kv x L <= 8 and 1 <= n <= 8
+ * (k and v 8-byte aligned) the attention kernel quantizes and writes the n
+ * rows itself: the workgroup whose key range holds a row writes it before
+ * reading it, and no other workgroup reads it; one launch fewer than the two
+ * calls.  Otherwise the two calls run as they are.  Every argument is
+ * checked before anything is launched; on error nothing is written and
+ * c->offset is unchanged.  Errors: those of both calls.
+ */
+int rbq_kv_append_attn_decode(rbq_kv_cache* c, const void* k, const void* v, int64_t n,
+                              const void* q, int32_t H_q, int32_t L, float scale, int32_t causal,
+                              const float* rot_blocks, float* out, int32_t splits, void* ws,
+                              size_t ws_bytes, void* stream);
+
 /* ---- attention mask element types (rbq_quant_attn_decode_mask) ---- */
 #define RBQ_MASK_NONE      0
 #define RBQ_MASK_BOOL      1  /* uint8: nonzero = the key is attended, 0 = skipped          */

@@ -174,6 +174,28 @@ class RotatedQuantKVCache:
         capi.rbq_quant_attn_decode(self.desc, q, scale, causal, self.rot, out, splits, ws, mask)
         return out
 
+    def append_attend(self, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor,
+                      scale: Optional[float] = None, causal: bool = True, splits: int = 0,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """One decoding step: ``append(k, v)`` then ``attend(q)`` in one library
+        call (the attention kernel writes the new rows itself where it can)."""
+        n = k.shape[2]
+        self.reserve(n)
+        if scale is None:
+            scale = self.desc.head_dim ** -0.5
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
+        after = capi.rbq_kv_cache.from_buffer_copy(self.desc)
+        after.offset += n
+        nb = capi.rbq_quant_attn_workspace_bytes(after, q.shape[1], q.shape[2], splits)
+        ws = None
+        if nb > 0:
+            if self._ws is None or self._ws.numel() < nb:
+                self._ws = torch.empty(nb, dtype=torch.uint8, device=self.device)
+            ws = self._ws
+        capi.rbq_kv_append_attn_decode(self.desc, k, v, q, scale, causal, self.rot, out, splits, ws)
+        return out
+
     # -- batched verification of draft paths (mtp/kv_cache.py) -----------------
     def _regather(self, B: int, src_b0: int, src_b_step: int) -> None:
         """Replace the buffers by new ones of batch B, same capacity, whose

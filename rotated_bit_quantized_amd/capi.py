@@ -89,6 +89,9 @@ def _load():
         "rbq_quant_attn_decode": (c_int32, [P, c_void_p, c_int32, c_int32, c_float, c_int32,
                                             c_void_p, c_void_p, c_int32, c_void_p, c_size_t,
                                             c_void_p]),
+        "rbq_kv_append_attn_decode": (c_int32, [P, c_void_p, c_void_p, c_int64, c_void_p, c_int32,
+                                                c_int32, c_float, c_int32, c_void_p, c_void_p,
+                                                c_int32, c_void_p, c_size_t, c_void_p]),
         "rbq_quant_attn_decode_mask": (c_int32, [P, c_void_p, c_int32, c_int32, c_float, c_int32,
                                                  c_void_p, c_int32, c_int64, c_int64, c_int64,
                                                  c_void_p, c_void_p, c_int32, c_void_p, c_size_t,
@@ -272,6 +275,37 @@ def rbq_quant_attn_decode(desc: rbq_kv_cache, q: torch.Tensor, scale: float, cau
            _lib.rbq_quant_attn_decode_mask(ctypes.byref(desc), qp, q.shape[1], q.shape[2],
                                            float(scale), 1 if causal else 0, mp, mt, sb, sh, sl,
                                            rp, op, int(splits), wp, wn, _stream()))
+
+
+def rbq_kv_append_attn_decode(desc: rbq_kv_cache, k: torch.Tensor, v: torch.Tensor,
+                              q: torch.Tensor, scale: float, causal: bool, rot_blocks,
+                              out: torch.Tensor, splits: int = 0,
+                              ws: torch.Tensor = None) -> None:
+    """rbq_kv_quant_append(desc, k, v) then rbq_quant_attn_decode(desc, q, ...)
+    as one call (one launch fewer where the attention kernel writes the rows
+    itself).  ws: at least ``rbq_quant_attn_workspace_bytes`` of the cache
+    after the append.  Advances ``desc.offset`` by n."""
+    if k.shape != v.shape or k.dim() != 4:
+        raise ValueError("k and v must both be [B, H_kv, n, head_dim]")
+    if (k.shape[0], k.shape[1], k.shape[3]) != (desc.B, desc.H_kv, desc.head_dim):
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match the cache")
+    if q.dim() != 4 or q.shape[0] != desc.B or q.shape[3] != desc.head_dim:
+        raise ValueError(f"q shape {tuple(q.shape)} does not match the cache")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    dt = _TORCH_OF[desc.dtype]
+    kp = _dev_ptr(k, dt, "k")
+    vp = _dev_ptr(v, dt, "v")
+    qp = _dev_ptr(q, dt, "q")
+    op = _dev_ptr(out, torch.float32, "out")
+    rp = None if rot_blocks is None else _dev_ptr(rot_blocks, torch.float32, "rot_blocks")
+    wp, wn = None, 0
+    if ws is not None:
+        wp, wn = _dev_ptr(ws, None, "ws"), ws.numel() * ws.element_size()
+    _check("rbq_kv_append_attn_decode",
+           _lib.rbq_kv_append_attn_decode(ctypes.byref(desc), kp, vp, k.shape[2], qp, q.shape[1],
+                                          q.shape[2], float(scale), 1 if causal else 0, rp, op,
+                                          int(splits), wp, wn, _stream()))
 
 
 _TORCH_OF = {RBQ_F16: torch.float16, RBQ_BF16: torch.bfloat16}

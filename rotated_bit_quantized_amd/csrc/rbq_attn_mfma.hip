@@ -47,6 +47,7 @@
 #include <hip/hip_runtime.h>
 
 #include "rbq_common.h"
+#include "rbq_quantize.h"
 
 namespace rbq {
 namespace {
@@ -126,6 +127,12 @@ struct MArgs {
     int64_t msb, msh, msl;
     uint32_t mask_bytes;  // extent read through a range-checked buffer resource
     int round_rot;        // RBQ_FLAG_ROUND_ROTATED: the rotated query rounded to the dtype
+    // fused append (no mask, one block of rows per kv head): rows
+    // [T - n_new, T) of the cache are quantized from kn / vn
+    // ([B][H_kv][n_new][256], unrotated) and written by this launch
+    const uint16_t* kn;
+    const uint16_t* vn;
+    int n_new;
 };
 
 // Mask element types (the template argument MK of the attention kernel).
@@ -442,12 +449,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const __amdgpu_buffer_rsrc_t vb_r = make_rsrc(a.vb + row0 * kGroups, (uint32_t)T * 8u);
     const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
     const int it_first = wave_tile(0, wave, n_tiles);
+    // fused append: the appended rows [T - n_new, T) that fall in this split,
+    // [app_lo, app_lo + n_app), are quantized and written by this workgroup,
+    // row app_lo + w by wave w, before any transfer of the workgroup reads
+    // them (no other workgroup reads them: one block of rows per kv head)
+    int app_lo = t_end, n_app = 0;
+    uint2 kraw = make_uint2(0u, 0u), vraw = make_uint2(0u, 0u);
+    if constexpr (MK == kMaskNone) {
+        if (a.n_new > 0) {
+            app_lo = max(T - a.n_new, t_begin);
+            n_app = max(t_end - app_lo, 0);
+            if (wave < n_app) {
+                const int64_t src =
+                    ((int64_t)bh * a.n_new + (app_lo + wave - (T - a.n_new))) * kHeadDim + 4 * lane;
+                kraw = *reinterpret_cast<const uint2*>(a.kn + src);
+                vraw = *reinterpret_cast<const uint2*>(a.vn + src);
+            }
+        }
+    }
     // this wave's tile buffer, filled with its first tile unconditionally (a
     // wave without tiles reads keys of the next split or, past T, zeros from
-    // the buffer range check, and never uses them)
+    // the buffer range check, and never uses them); a first tile that holds
+    // an appended row is transferred after the set-up, once the row is written
     lds_u8* wbuf = (lds_u8*)tbuf + wave * kWaveAreaBytes;
     const unsigned char* wbuf_g = tbuf + wave * kWaveAreaBytes;
-    dma_tile(wbuf, t_begin + it_first * kTile, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
+    const int t_first = t_begin + it_first * kTile;
+    const bool defer_first = n_app > 0 && t_first < app_lo + n_app && t_first + kTile > app_lo;
+    if (!defer_first) dma_tile(wbuf, t_first, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
 
     // ---- decode table: entry e = 4 fp16 codes (e >> 3k) & 7 ----
     for (int e = tid; e < 4096; e += kThreads) {
@@ -505,6 +533,47 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             if (mx > 0.f) (void)frexpf(mx, &ex);
             qstat[wave * 8 + 4] = __int_as_float((mx > 0.f) ? 15 - ex : 0);
         }
+    }
+    if (wave < n_app) {
+        // the appended row: rotated by the same blocks (from LDS), rounded to
+        // the dtype when the cache asks for it, quantized and packed as the
+        // append kernel does
+        const float xk[4] = {elem_to_f32<DT>(kraw.x), elem_to_f32<DT>(kraw.x >> 16),
+                             elem_to_f32<DT>(kraw.y), elem_to_f32<DT>(kraw.y >> 16)};
+        const float xv[4] = {elem_to_f32<DT>(vraw.x), elem_to_f32<DT>(vraw.x >> 16),
+                             elem_to_f32<DT>(vraw.y), elem_to_f32<DT>(vraw.y >> 16)};
+        float yk[4], yv[4];
+        if (rotated) {
+            float Bm[16];
+            const float4* blk = reinterpret_cast<const float4*>(rot_lds + 16 * lane);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float4 v = blk[q4];
+                Bm[4 * q4] = v.x;
+                Bm[4 * q4 + 1] = v.y;
+                Bm[4 * q4 + 2] = v.z;
+                Bm[4 * q4 + 3] = v.w;
+            }
+            rotate4(xk, Bm, yk);
+            rotate4(xv, Bm, yv);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                yk[c] = xk[c];
+                yv[c] = xv[c];
+            }
+        }
+        if (a.round_rot) {
+            round_row<DT>(yk);
+            round_row<DT>(yv);
+        }
+        const int64_t dst = row0 + app_lo + wave;
+        quantize_pack_row<DT, kKBits>(yk, lane, const_cast<uint32_t*>(a.kw) + dst * kKWords,
+                                      const_cast<uint16_t*>(a.ks) + dst * kGroups,
+                                      const_cast<uint16_t*>(a.kb) + dst * kGroups);
+        quantize_pack_row<DT, kVBits>(yv, lane, const_cast<uint32_t*>(a.vw) + dst * kVWords,
+                                      const_cast<uint16_t*>(a.vs) + dst * kGroups,
+                                      const_cast<uint16_t*>(a.vb) + dst * kGroups);
     }
     lds_barrier();
     // ---- score operands, one (group g, half h2) set per wave: slot k of
@@ -594,7 +663,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         vis[p] = (R < a.G && a.causal) ? T - a.L + (R % a.L) + 1 : T;
     }
     const int vis_min = min(vis[0], vis[1]);
+    // the appended rows' stores are complete (written to the L2, which every
+    // transfer of this compute unit reads through) before the barrier; the
+    // transfers that read them are issued after it
+    if (wave < n_app) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();  // query operands complete; query rows no longer read
+    if (defer_first) dma_tile(wbuf, t_first, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
     // the 8 score operand sets, held in registers for the whole tile loop
     f16x8 qa_r[4][2];
 #pragma unroll
@@ -1110,9 +1184,12 @@ int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Mfm
 
 int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, float scale,
                 int32_t causal, const AttnMask& mk, const float* rot_blocks, float* out,
-                const MfmaPlan& p, void* ws, void* stream) {
+                const MfmaPlan& p, void* ws, void* stream, const FusedAppend* app) {
     hipStream_t s = (hipStream_t)stream;
     MArgs a;
+    a.kn = app ? (const uint16_t*)app->k : nullptr;
+    a.vn = app ? (const uint16_t*)app->v : nullptr;
+    a.n_new = app ? app->n : 0;
     a.q = (const uint16_t*)q;
     a.kw = c->k_words;
     a.ks = (const uint16_t*)c->k_scales;
@@ -1285,6 +1362,49 @@ extern "C" int rbq_quant_attn_decode_mask(const rbq_kv_cache* c, const void* q, 
     if (ap.ws_bytes > 0 && (ws == nullptr || ws_bytes < ap.ws_bytes)) return RBQ_EWORKSPACE;
     if (ap.tile) return tile_launch(c, q, H_q, L, scale, causal, mk, rot_blocks, out, ap.tp, ws, stream);
     return mfma_launch(c, q, H_q, L, scale, causal, mk, rot_blocks, out, ap.mp, ws, stream);
+}
+
+extern "C" int rbq_kv_append_attn_decode(rbq_kv_cache* c, const void* k, const void* v,
+                                         int64_t n, const void* q, int32_t H_q, int32_t L,
+                                         float scale, int32_t causal, const float* rot_blocks,
+                                         float* out, int32_t splits, void* ws, size_t ws_bytes,
+                                         void* stream) {
+    // every argument of both steps is checked before anything is launched
+    int st = check_cache(c);
+    if (st != RBQ_OK) return st;
+    if (n < 0) return RBQ_EINVAL;
+    if (n > 0 && (k == nullptr || v == nullptr)) return RBQ_EINVAL;
+    if (c->offset + n > c->capacity) return RBQ_ECAPACITY;
+    rbq_kv_cache after = *c;
+    after.offset += n;
+    st = check_attn(&after, H_q, L, splits);
+    if (st != RBQ_OK) return st;
+    if (q == nullptr || out == nullptr) return RBQ_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(q) & 7) != 0 || (reinterpret_cast<uintptr_t>(out) & 15) != 0 ||
+        (reinterpret_cast<uintptr_t>(rot_blocks) & 15) != 0 || (reinterpret_cast<uintptr_t>(ws) & 15) != 0)
+        return RBQ_EINVAL;
+    AttnPlan ap;
+    st = attn_plan(&after, H_q, L, splits, &ap);
+    if (st != RBQ_OK) return st;
+    if (ap.ws_bytes > 0 && (ws == nullptr || ws_bytes < ap.ws_bytes)) return RBQ_EWORKSPACE;
+    const bool fused = n > 0 && !ap.tile && ap.mp.RB == 1 && n <= kWaves &&
+                       (reinterpret_cast<uintptr_t>(k) & 7) == 0 &&
+                       (reinterpret_cast<uintptr_t>(v) & 7) == 0;
+    if (!fused) {
+        // the two steps as two launches: the append kernel, then the attention
+        st = rbq_kv_quant_append(c, k, v, n, rot_blocks, stream);
+        if (st != RBQ_OK) return st;
+        return rbq_quant_attn_decode(c, q, H_q, L, scale, causal, rot_blocks, out, splits, ws,
+                                     ws_bytes, stream);
+    }
+    AttnMask mk;
+    st = check_mask(&after, H_q, L, nullptr, RBQ_MASK_NONE, 0, 0, 0, &mk);
+    if (st != RBQ_OK) return st;
+    const FusedAppend fa = {k, v, (int)n};
+    st = mfma_launch(&after, q, H_q, L, scale, causal, mk, rot_blocks, out, ap.mp, ws, stream, &fa);
+    if (st != RBQ_OK) return st;
+    c->offset += n;
+    return RBQ_OK;
 }
 
 extern "C" int rbq_quant_attn_decode(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L,

@@ -83,8 +83,16 @@ int tile_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
 // it is 1.4-1.7x faster from 64 to 2048 rows and equal on a 2048-token
 // prefill chunk.  Every other configuration runs the tile kernel.
 constexpr int kDedicatedMaxRows = 0x3FFFFFFF;
+// Rows appended by the attention launch itself (the dedicated kernel, no
+// mask, one block of query rows per kv head): the last n cache rows below
+// c->offset are quantized from k / v ([B][H_kv][n][256], unrotated).
+struct FusedAppend {
+    const void* k;
+    const void* v;
+    int n;
+};
 int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, float scale,
                 int32_t causal, const AttnMask& mk, const float* rot_blocks, float* out,
-                const MfmaPlan& p, void* ws, void* stream);
+                const MfmaPlan& p, void* ws, void* stream, const FusedAppend* app = nullptr);
 
 }  // namespace rbq

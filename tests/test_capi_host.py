@@ -188,6 +188,36 @@ def test_device_entry_points_validate_before_any_device_work():
         capi.RBQ_EWORKSPACE
     assert lib.rbq_quant_attn_splits(by(d), 4, 1) >= 1
     assert lib.rbq_quant_attn_splits(by(d), 3, 1) == capi.RBQ_EINVAL
+    # append + attention in one call: every argument of both steps is checked
+    # before a launch, and an error leaves the offset where it was
+    fused = lib.rbq_kv_append_attn_decode
+    off0 = d.offset
+    args = lambda **kw: dict(dict(k=fake, v=fake, n=1, q=fake, H_q=4, L=1, rot=None, out=fake,
+                                  splits=0, ws=fake, nb=1 << 30), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return fused(by(d), a["k"], a["v"], a["n"], a["q"], a["H_q"], a["L"], 0.0625, 1,
+                     a["rot"], a["out"], a["splits"], a["ws"], a["nb"], None)
+
+    assert call(n=-1) == capi.RBQ_EINVAL
+    assert call(k=None) == capi.RBQ_EINVAL
+    assert call(v=None) == capi.RBQ_EINVAL
+    assert call(n=157) == capi.RBQ_ECAPACITY
+    assert call(H_q=3) == capi.RBQ_EINVAL
+    assert call(L=0) == capi.RBQ_ERANGE
+    assert call(n=2, L=103) == capi.RBQ_ERANGE  # the block may reach the appended rows only
+    assert call(q=None) == capi.RBQ_EINVAL
+    assert call(q=fake + 4) == capi.RBQ_EINVAL
+    assert call(out=fake + 8) == capi.RBQ_EINVAL
+    assert call(rot=fake + 4) == capi.RBQ_EINVAL
+    assert call(splits=-1) == capi.RBQ_EINVAL
+    assert call(splits=8, ws=None, nb=0) == capi.RBQ_EWORKSPACE
+    after = _host_desc(B=1, H=2, cap=256, off=off0 + 1, **ptrs)
+    need1 = lib.rbq_quant_attn_workspace_bytes(by(after), 4, 1, 8)
+    assert need1 > 0
+    assert call(splits=8, nb=need1 - 1) == capi.RBQ_EWORKSPACE
+    assert d.offset == off0
     # grow: mismatched descriptors
     g = _host_desc(B=2, H=2, cap=512, off=0, **ptrs)
     assert lib.rbq_kv_grow(by(d), by(g), None) == capi.RBQ_EINVAL
