@@ -470,12 +470,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // this wave's tile buffer, filled with its first tile unconditionally (a
     // wave without tiles reads keys of the next split or, past T, zeros from
     // the buffer range check, and never uses them); a first tile that holds
-    // an appended row is transferred after the set-up, once the row is written
+    // an appended row is transferred after the set-up, once the row is
+    // written, and the transfer issued here then reads past T (zeros, no
+    // memory access): the same instructions on every path, so that the
+    // compiler's waits for the query loads leave the tile in flight
     lds_u8* wbuf = (lds_u8*)tbuf + wave * kWaveAreaBytes;
     const unsigned char* wbuf_g = tbuf + wave * kWaveAreaBytes;
     const int t_first = t_begin + it_first * kTile;
     const bool defer_first = n_app > 0 && t_first < app_lo + n_app && t_first + kTile > app_lo;
-    if (!defer_first) dma_tile(wbuf, t_first, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
+    dma_tile(wbuf, defer_first ? T : t_first, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
 
     // ---- decode table: entry e = 4 fp16 codes (e >> 3k) & 7 ----
     for (int e = tid; e < 4096; e += kThreads) {
@@ -665,8 +668,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int vis_min = min(vis[0], vis[1]);
     // the appended rows' stores are complete (written to the L2, which every
     // transfer of this compute unit reads through) before the barrier; the
-    // transfers that read them are issued after it
-    if (wave < n_app) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // transfers that read them are issued after it (a deferring wave's
+    // placeholder transfer has landed before its buffer is refilled)
+    if (wave < n_app || defer_first) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();  // query operands complete; query rows no longer read
     if (defer_first) dma_tile(wbuf, t_first, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
     // the 8 score operand sets, held in registers for the whole tile loop
