@@ -90,6 +90,7 @@ struct TArgs {
     int T, chunk, S, Hkv, n_rep, L, G, RBW, causal, round_rot;
     int GS, kbits, vbits;
     float qscale;  // scale * log2(e)
+    int raw_vw, raw_meta;  // staging offsets of the V words and the scale / bias arrays
     const void* mask;
     int64_t msb, msh, msl;  // elements; key stride 1
     uint32_t mask_bytes;
@@ -177,16 +178,20 @@ typedef __attribute__((address_space(3))) unsigned char tlds_u8;
 
 // Raw tile staging (a separate LDS array, filled by direct-to-LDS loads: the
 // compiler can then tell its transfers from every other LDS access): the
-// tile's K words, V words (key-major, as in memory) and its four scale /
-// bias arrays [key][group], 16-bit.
+// tile's K words at 0, V words at raw_vw (key-major, as in memory) and its
+// four scale / bias arrays [key][group], 16-bit, at raw_meta.  Sized by the
+// call's widths (dynamic LDS): 32 keys x D x bits / 8 bytes per word array.
 template <int D, int NG>
 struct RawLds {
-    static constexpr int kw = 0;                    // up to 32 keys x D/4 words (8-bit codes)
-    static constexpr int vw = kw + 32 * D;
-    static constexpr int meta = vw + 32 * D;        // 4 arrays x 32 keys x NG x 2 B
-    static constexpr int meta_bytes = 64 * NG;      // one array
-    static constexpr int bytes = meta + 4 * meta_bytes;
+    static constexpr int meta_bytes = 64 * NG;      // one scale / bias array
 };
+__host__ __device__ constexpr int raw_vw_off(int D, int kbits) { return 4 * D * kbits; }
+__host__ __device__ constexpr int raw_meta_off(int D, int kbits, int vbits) {
+    return 4 * D * (kbits + vbits);
+}
+__host__ __device__ constexpr int raw_bytes(int D, int NG, int kbits, int vbits) {
+    return raw_meta_off(D, kbits, vbits) + 4 * 64 * NG;
+}
 
 // Buffer resources of one (b, kv head) slab: the six arrays from row 0,
 // ranges T rows (keys past T read as zero).
@@ -216,7 +221,7 @@ __device__ __forceinline__ void issue_tile(const TArgs& a, const TRsrc& rs, int 
     for (int kv = 0; kv < 2; ++kv) {
         const int words = kv ? D * a.vbits / 32 : D * a.kbits / 32;
         const __amdgpu_buffer_rsrc_t r = kv ? rs.vw : rs.kw;
-        tlds_u8* dst = rawb + (kv ? R::vw : R::kw);
+        tlds_u8* dst = rawb + (kv ? a.raw_vw : 0);
         const uint32_t base = (uint32_t)t0 * words * 4u;
         if (kv ? rs.v16 : rs.k16) {
             const int nch = 8 * words;  // 16-byte chunks of the tile
@@ -244,7 +249,7 @@ __device__ __forceinline__ void issue_tile(const TArgs& a, const TRsrc& rs, int 
 #pragma unroll
             for (int h = 0; h < (16 * NG + 63) / 64; ++h)
                 if ((4 * k + h) % W == wave && 64 * h + lane < 16 * NG)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.m[k], rawb + R::meta + k * R::meta_bytes + 256 * h,
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.m[k], rawb + a.raw_meta + k * R::meta_bytes + 256 * h,
                                                               4, moff, 256 * h, 0, 0);
     }
 }
@@ -268,7 +273,7 @@ __device__ __forceinline__ void read_unit(const TArgs& a, const unsigned char* r
     const int uu = isv ? u - D : u;
     const int key = uu / upk, part = uu - key * upk;
     const int bits = isv ? a.vbits : a.kbits;
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(rawb + (isv ? R::vw : R::kw)) +
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(rawb + (isv ? a.raw_vw : 0)) +
                           key * (D * bits / 32) + part * bits;
     // consecutive lanes read consecutive units (bits words apart): 2-, 4- and
     // 8-bit units as whole 8- or 16-byte reads (word reads at a stride of 4
@@ -331,12 +336,13 @@ __device__ __forceinline__ void store_units(const TArgs& a, const unsigned char*
 
 // Scale / bias item m of the staged tile: group m / 32, key m % 32.
 template <int D, int NG>
-__device__ __forceinline__ void read_meta(const unsigned char* rawb, int m, uint32_t meta[4]) {
+__device__ __forceinline__ void read_meta(const unsigned char* rawb, int raw_meta, int m,
+                                          uint32_t meta[4]) {
     using R = RawLds<D, NG>;
     const int g = m / tTile, key = m - g * tTile;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        meta[i] = (g < NG) ? *reinterpret_cast<const uint16_t*>(rawb + R::meta + i * R::meta_bytes +
+        meta[i] = (g < NG) ? *reinterpret_cast<const uint16_t*>(rawb + raw_meta + i * R::meta_bytes +
                                                                   2 * (key * NG + g))
                            : 0u;
 }
@@ -413,7 +419,7 @@ void attn_tile_kernel(TArgs a) {
     constexpr int CPG = NC / NG;  // chunks per group
     constexpr int NPG = NB / NG;  // output blocks per group
     __shared__ __attribute__((aligned(16))) unsigned char smem[Ly::bytes];
-    __shared__ __attribute__((aligned(16))) unsigned char rawb[RawLds<D, NG>::bytes];
+    extern __shared__ __attribute__((aligned(16))) unsigned char rawb[];  // raw_bytes(...) at launch
     float* fs = reinterpret_cast<float*>(smem);
 
     const int tid = threadIdx.x;
@@ -590,7 +596,7 @@ void attn_tile_kernel(TArgs a) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) meta[i] = meta1[i];
                 } else {
-                    read_meta<D, NG>(rawb, m, meta);
+                    read_meta<D, NG>(rawb, a.raw_meta, m, meta);
                 }
                 store_meta<DT, D, W, NG>(meta, m, smem, f_run[q]);
             }
@@ -894,23 +900,25 @@ __global__ __launch_bounds__(256) void attn_tile_merge_kernel(TMArgs a) {
 
 }  // namespace
 
-// Workgroups of one shape that fit a compute unit: LDS (160 KiB) and two
-// waves per SIMD at most.
+// Workgroups of one shape that fit a compute unit: LDS (160 KiB, the tile
+// arrays and the staging for the call's widths) and two waves per SIMD at
+// most.
 template <int D, int NG, int W>
-constexpr int tile_fit() {
-    constexpr int lds = TileLds<D, W, NG>::bytes + RawLds<D, NG>::bytes;
-    constexpr int by_lds = 160 * 1024 / lds;
-    constexpr int by_waves = 8 / W;
+int tile_fit(int kbits, int vbits) {
+    const int lds = TileLds<D, W, NG>::bytes + raw_bytes(D, NG, kbits, vbits);
+    const int by_lds = 160 * 1024 / lds;
+    const int by_waves = 8 / W;
     return by_lds < by_waves ? by_lds : by_waves;
 }
 
-static int tile_workgroups_per_cu(int D, int ng, int W) {
+static int tile_workgroups_per_cu(int D, int ng, int W, int kbits, int vbits) {
 #define RBQ_FIT(D_, NG_)                                                   \
-    if (D == D_ && ng == NG_) return W == 4 ? tile_fit<D_, NG_, 4>() : tile_fit<D_, NG_, 1>();
+    if (D == D_ && ng == NG_)                                              \
+        return W == 4 ? tile_fit<D_, NG_, 4>(kbits, vbits) : tile_fit<D_, NG_, 1>(kbits, vbits);
     RBQ_FIT(64, 1) RBQ_FIT(64, 2) RBQ_FIT(128, 1) RBQ_FIT(128, 2) RBQ_FIT(128, 4)
 #undef RBQ_FIT
 #define RBQ_FIT(D_, NG_) \
-    if (D == D_ && ng == NG_) return tile_fit<D_, NG_, 4>();
+    if (D == D_ && ng == NG_) return tile_fit<D_, NG_, 4>(kbits, vbits);
     RBQ_FIT(256, 2) RBQ_FIT(256, 4) RBQ_FIT(256, 8)
 #undef RBQ_FIT
     return 1;
@@ -934,7 +942,7 @@ int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Til
         // unit as LDS and registers allow (longer splits lose less to set-up
         // and records than a second round gains)
         const int ng = c->head_dim / c->group_size;
-        const int per_cu = tile_workgroups_per_cu(c->head_dim, ng, W);
+        const int per_cu = tile_workgroups_per_cu(c->head_dim, ng, W, c->k_bits, c->v_bits);
         S = (256 * per_cu + units - 1) / units;
         const int64_t max_s = (T + tTile - 1) / tTile;
         if (S > max_s) S = max_s;
@@ -989,6 +997,10 @@ int tile_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
     a.kbits = c->k_bits;
     a.vbits = c->v_bits;
     a.qscale = scale * tLog2e;
+    a.raw_vw = raw_vw_off(c->head_dim, c->k_bits);
+    a.raw_meta = raw_meta_off(c->head_dim, c->k_bits, c->v_bits);
+    const int ng = c->head_dim / c->group_size;
+    const size_t dyn = (size_t)raw_bytes(c->head_dim, ng, c->k_bits, c->v_bits);
     a.mask = mk.ptr;
     a.msb = mk.sb;
     a.msh = mk.sh;
@@ -997,9 +1009,8 @@ int tile_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
     a.mtype = mk.ptr == nullptr ? 0 : mk.type;
     const int64_t units = (int64_t)c->B * c->H_kv * p.RBW;
     const dim3 grid((unsigned)(units * p.S)), block(64 * p.W);
-    auto launch = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, s, a); };
+    auto launch = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, dyn, s, a); };
     const bool bf = c->dtype == RBQ_BF16;
-    const int ng = c->head_dim / c->group_size;
 #define RBQ_TILE_CASE(D_, NG_)                                                                    \
     if (c->head_dim == D_ && ng == NG_) {                                                         \
         if (p.W == 4)                                                                             \

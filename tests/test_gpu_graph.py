@@ -1,4 +1,5 @@
-"""GPU: the decode step (append one token, attend) captured in a HIP graph.
+"""GPU: the decode step (append one token, attend; as two calls and as the
+one-call step) captured in a HIP graph.
 
 The launches read their arguments as captured: a replay appends the token at
 the captured row again and attends over the same rows, so every replay must
@@ -27,12 +28,13 @@ def _cache(dev, rot, B, Hkv, T, seed):
     return c
 
 
+@pytest.mark.parametrize("one_call", [False, True], ids=["two_calls", "one_call"])
 @pytest.mark.parametrize("T", [300, 5000])
-def test_step_graph_replays_equal_eager(T):
+def test_step_graph_replays_equal_eager(T, one_call):
     dev = torch.device("cuda:0")
     rot = rbq.build_block_so4(256, W.ROTATION_SEED, dev)
     B, Hkv, Hq = 2, 2, 16
-    print(f"graph step B={B} Hq={Hq} Hkv={Hkv} T={T}", flush=True)
+    print(f"graph step B={B} Hq={Hq} Hkv={Hkv} T={T} one_call={one_call}", flush=True)
     c = _cache(dev, rot, B, Hkv, T - 1, 1)
     other = _cache(dev, rot, B, Hkv, T, 2)
     g = torch.Generator().manual_seed(3)
@@ -45,6 +47,9 @@ def test_step_graph_replays_equal_eager(T):
     ws_other = torch.zeros_like(ws) if ws is not None else None
 
     def step():
+        if one_call:  # the attention kernel appends the token itself
+            capi.rbq_kv_append_attn_decode(c.desc, k1, v1, q, 1 / 16, True, rot, out, 0, ws)
+            return
         capi.rbq_kv_quant_append(c.desc, k1, v1, rot)
         capi.rbq_quant_attn_decode(c.desc, q, 1 / 16, True, rot, out, 0, ws)
 
