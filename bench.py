@@ -210,6 +210,59 @@ def tree_verify(rbq, W, dev, rot, n_calls: int = 200) -> dict:
     }
 
 
+def append_throughput(rbq, W, dev, rot, n_calls: int = 32) -> dict:
+    """The append (a2 + a3) of a prefill chunk on the append+verify shapes:
+    B=4, 16 q heads / 2 kv heads, head_dim 256, bf16, K4/V3 group 64, 2048
+    new tokens after 8192 cached; 16 input sets (268 MB) and 4 caches cycled
+    so that the Infinity Cache cannot serve the inputs; append then trim,
+    HIP events around the back-to-back appends.  Bytes: the bf16 K and V
+    rows read plus the packed rows written."""
+    B, Hkv, T0, n, D = 4, 2, 8192, 2048, 256
+    k = W.random_rows([70, 1], (B, Hkv, T0, D), "bf16").to(dev)
+    v = W.random_rows([70, 2], (B, Hkv, T0, D), "bf16").to(dev)
+    caches = []
+    for _ in range(4):
+        c = rbq.RotatedQuantKVCache(B, Hkv, device=dev, rot=rot)
+        c.append(k, v)
+        c.reserve(n)
+        caches.append(c)
+    del k, v
+    base = W.random_rows([70, 3], (B, Hkv, n, D), "bf16").to(dev)
+    ins = [(base.roll(i, dims=3).contiguous(), base.roll(-i, dims=3).contiguous()) for i in range(16)]
+    stream = torch.cuda.current_stream()
+    for i in range(8):
+        c = caches[i % 4]
+        rbq.rbq_kv_quant_append(c.desc, ins[i % 16][0], ins[i % 16][1], rot)
+        rbq.rbq_kv_trim(c.desc, n)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(n_calls):
+        c = caches[i % 4]
+        rbq.rbq_kv_quant_append(c.desc, ins[i % 16][0], ins[i % 16][1], rot)
+        rbq.rbq_kv_trim(c.desc, n)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / n_calls
+    rows = B * Hkv * n
+    nbytes = rows * (2 * D * 2 + 256)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {
+        "what": f"append of {n} tokens after {T0} cached, B={B}, {Hkv} kv heads, head_dim 256, bf16, "
+                "K4/V3 group 64 (rbq_kv_quant_append: rotate, quantize, pack, write)",
+        "bound": "alu",
+        "note": "VALU-bound, not HBM-bound: about 640 instructions per row and wave (fp64 "
+                "rotation, ten correctly rounded divisions, group min/max shuffles, packing); "
+                "frac is against the HBM peak, for context",
+        "bytes_per_call": nbytes,
+        "avg_us": round(us, 3),
+        "achieved": round(gbs, 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(gbs / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(B * n / (us * 1e-6), 1),
+    }
+
+
 def prefill(rbq, W, dev, rot, n_calls: int = 10, head_dim: int = 256) -> dict:
     """Prefill-length attention over the quantized cache: B=1, 16 q heads /
     2 kv heads, head_dim 256, bf16, K4/V3 group 64; a cache of 8192 tokens,
@@ -340,7 +393,8 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph (on this stack a replay "
                          "costs more than the two launches it holds)")
-    ap.add_argument("--leg", choices=["prefill", "variant_decode", "variant_prefill", "tree_verify"],
+    ap.add_argument("--leg", choices=["prefill", "variant_decode", "variant_prefill", "tree_verify",
+                                      "append"],
                     help="run only this secondary measurement and print its object "
                          "(for profiling it on its own; not the benchmark line)")
     args = ap.parse_args()
@@ -360,7 +414,8 @@ def main() -> int:
         leg = {"prefill": lambda: prefill(rbq, W, dev, rot),
                "variant_decode": lambda: variant_decode(rbq, W, dev),
                "variant_prefill": lambda: prefill(rbq, W, dev, rot, head_dim=128),
-               "tree_verify": lambda: tree_verify(rbq, W, dev, rot)}[args.leg]
+               "tree_verify": lambda: tree_verify(rbq, W, dev, rot),
+               "append": lambda: append_throughput(rbq, W, dev, rot)}[args.leg]
         print(json.dumps({args.leg: leg()}), flush=True)
         return 0
 
@@ -489,6 +544,8 @@ def main() -> int:
     tree = tree_verify(rbq, W, dev, rot)
     print("[bench] prefill chunk", file=sys.stderr, flush=True)
     pre = prefill(rbq, W, dev, rot)
+    print("[bench] append of a prefill chunk", file=sys.stderr, flush=True)
+    app = append_throughput(rbq, W, dev, rot)
     print("[bench] decode and prefill, head_dim 128 K4/V4", file=sys.stderr, flush=True)
     var = variant_decode(rbq, W, dev)
     pre128 = prefill(rbq, W, dev, rot, head_dim=128)
@@ -557,6 +614,7 @@ def main() -> int:
         "prefill": pre,
         "variant_decode": var,
         "variant_prefill": pre128,
+        "append": app,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)

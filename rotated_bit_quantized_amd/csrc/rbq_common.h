@@ -30,8 +30,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 
 // fp32 -> fp16 bits, round half to even (the hardware conversion in the
-// default rounding mode; subnormal halves are kept).
+// default rounding mode; subnormal halves are kept).  The empty asm makes the
+// fp32 value opaque: without it the compiler turned an fp64 -> fp32 rounding
+// followed by this one into a single fp64 -> fp16 rounding, which differs
+// where the two roundings compound (rotated rows rounded to fp16).
 __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+    asm("" : "+v"(f));
     const _Float16 h = (_Float16)f;
     return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }

@@ -239,6 +239,28 @@ def test_chunked_appends_equal_one_shot(dev, rot):
         assert torch.equal(a.rows()[name], b.rows()[name]), name
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_long_ragged_append_bit_exact(dtype, dev, rot, blocks):
+    """A long append (4102 rows: a ragged last workgroup) equals the oracle bit
+    for bit and equals the same rows appended in two chunks."""
+    B, Hkv, T = 1, 2, 2051
+    print(f"[long append] {dtype} rows={B * Hkv * T}", flush=True)
+    tdt = W._TORCH_DTYPES[dtype]
+    k = W.random_rows([8, 1], (B, Hkv, T, 256), dtype, "student_t3")
+    v = W.random_rows([8, 2], (B, Hkv, T, 256), dtype)
+    a = rbq.RotatedQuantKVCache(B, Hkv, dtype=tdt, device=dev, rot=rot)
+    a.append(k.to(dev), v.to(dev))
+    b = rbq.RotatedQuantKVCache(B, Hkv, dtype=tdt, device=dev, rot=rot)
+    for s0, e0 in ((0, 1000), (1000, T)):
+        b.append(k[:, :, s0:e0].contiguous().to(dev), v[:, :, s0:e0].contiguous().to(dev))
+    torch.cuda.synchronize()
+    for name in a.arrays:
+        assert torch.equal(a.rows()[name], b.rows()[name]), name
+    for h in range(Hkv):
+        ref = R.oracle_rows(k[0, h].float().numpy(), v[0, h].float().numpy(), blocks, dtype)
+        R.assert_slab_equal(R.device_rows(a, 0, h), ref, f"slab h={h}")
+
+
 def test_trim_then_append_equals_fresh_cache(dev, rot):
     B, Hkv, T = 1, 2, 300
     k = W.random_rows([7, 1], (B, Hkv, T, 256), "bf16")
