@@ -850,22 +850,59 @@ __global__ __launch_bounds__(256) void attn_tile_merge_kernel(TMArgs a) {
     if (R >= a.G) return;  // uniform: one row per block
     const int tid = threadIdx.x;
     const int b = bh / a.Hkv, kvh = bh - b * a.Hkv;
+    // the rotation block of this thread's column quad, loaded first (it is
+    // needed last and depends on nothing)
+    float Bm[16];
+    load_block(a.rot, tid < NQ ? tid : 0, Bm);
+    // (m, l) of the splits tid, tid + 256, ... (tMaxSplits / 256 at most),
+    // loaded once
+    constexpr int kPer = tMaxSplits / 256;
     const float* ml = a.rec_ml + (int64_t)bhr * a.S * RW * 2 + 2 * rr;
+    float mv[kPer], lv[kPer];
     float mx = -INFINITY;
-    for (int s = tid; s < a.S; s += 256) mx = fmaxf(mx, ml[(int64_t)s * RW * 2]);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int s = tid + 256 * i;
+        mv[i] = -INFINITY;
+        lv[i] = 0.f;
+        if (s < a.S) {
+            const float2 p = *reinterpret_cast<const float2*>(ml + (int64_t)s * RW * 2);
+            mv[i] = p.x;
+            lv[i] = p.y;
+        }
+        mx = fmaxf(mx, mv[i]);
+    }
     const float M = block_reduce<true>(mx, red);
     float lsum = 0.f;
-    for (int s = tid; s < a.S; s += 256) {
-        const float m = ml[(int64_t)s * RW * 2];
-        const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-        wsh[s] = w;
-        lsum += ml[(int64_t)s * RW * 2 + 1] * w;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int s = tid + 256 * i;
+        const float w = (mv[i] == -INFINITY) ? 0.f : exp2f(mv[i] - M);
+        if (s < a.S) wsh[s] = w;
+        lsum += lv[i] * w;
     }
     const float Ls = block_reduce<false>(lsum, red);  // its barriers also publish wsh
     const int k = tid % NQ, sg = tid / NQ;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     const float* ro = a.rec_o + ((int64_t)bhr * a.S * RW + rr) * D + 4 * k;
-    for (int s = sg; s < a.S; s += NSG) {
+    // the split records of this thread, four loads in flight at a time
+    // (summed in split order as before)
+    int s = sg;
+    for (; s + 3 * NSG < a.S; s += 4 * NSG) {
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            v[u] = *reinterpret_cast<const float4*>(ro + (int64_t)(s + u * NSG) * RW * D);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float w = wsh[s + u * NSG];
+            acc.x += v[u].x * w;
+            acc.y += v[u].y * w;
+            acc.z += v[u].z * w;
+            acc.w += v[u].w * w;
+        }
+    }
+    for (; s < a.S; s += NSG) {
         const float w = wsh[s];
         const float4 v = *reinterpret_cast<const float4*>(ro + (int64_t)s * RW * D);
         acc.x += v.x * w;
@@ -888,11 +925,7 @@ __global__ __launch_bounds__(256) void attn_tile_merge_kernel(TMArgs a) {
     const float inv = 1.0f / Ls;
     float y[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
     float z[4] = {y[0], y[1], y[2], y[3]};
-    if (a.rot != nullptr) {
-        float Bm[16];
-        load_block(a.rot, tid, Bm);
-        unrotate4(y, Bm, z);
-    }
+    if (a.rot != nullptr) unrotate4(y, Bm, z);
     const int hq = kvh * a.n_rep + R / a.L;
     float* dst = a.out + (((int64_t)b * a.Hkv * a.n_rep + hq) * a.L + R % a.L) * D + 4 * tid;
     *reinterpret_cast<float4*>(dst) = make_float4(z[0], z[1], z[2], z[3]);
