@@ -1087,10 +1087,18 @@ struct CArgs {
     int S, Hkv, n_rep, L, G, RB;
 };
 
-__global__ __launch_bounds__(128) void attn_mfma_merge_kernel(CArgs a) {
-    __shared__ float wts[kRows * 16];
-    __shared__ float stat[2 * kRows];
-    const int tid = threadIdx.x;
+// NGR groups of 128 threads each take every NGR-th round of 16 records
+// (group g: records 16 g .. 16 g + 15, then 16 (g + NGR) ..), with the same
+// round count in every group so that all threads meet the same barriers (a
+// round past the last record has no members and weight 0); the groups'
+// (M, L, o) are then combined in group order.  NGR = 1 for up to 16 splits.
+template <int NGR>
+__global__ __launch_bounds__(128 * NGR) void attn_mfma_merge_kernel(CArgs a) {
+    __shared__ float wts[NGR][kRows * 16];
+    __shared__ float stat[NGR][2 * kRows];
+    __shared__ float cmb[NGR > 1 ? NGR - 1 : 1][3][4][128];  // groups 1.. : M, L, o per (row i, thread)
+    const int grp = threadIdx.x >> 7;
+    const int tid = threadIdx.x & 127;
     const int bhr = blockIdx.x >> 2;
     const int bh = bhr / a.RB;
     const int r0 = 8 * (bhr - bh * a.RB);
@@ -1108,26 +1116,28 @@ __global__ __launch_bounds__(128) void attn_mfma_merge_kernel(CArgs a) {
         Ls[i] = 0.f;
         acc[i] = 0.f;
     }
-    for (int m0 = 0; m0 < a.S; m0 += 16) {
-        const int members = (a.S - m0 < 16) ? a.S - m0 : 16;
+    const int rounds = (a.S + 16 * NGR - 1) / (16 * NGR);
+    for (int rd = 0; rd < rounds; ++rd) {
+        const int m0 = 16 * (grp + NGR * rd);
+        const int members = (a.S - m0 < 16) ? a.S - m0 : 16;  // <= 0: an empty round
         float2 ml = make_float2(-INFINITY, 0.f);
         if (wmbr < members)
             ml = *reinterpret_cast<const float2*>(base + (int64_t)(m0 + wmbr) * kRecFloats + 2 * wrow);
         float4 o[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-            const int mbr = m0 + ((k < members) ? k : 0);
+            const int mbr = (k < members) ? m0 + k : 0;
             o[k] = *reinterpret_cast<const float4*>(base + (int64_t)mbr * kRecFloats + 2 * kRows +
                                                     col * kRows + 4 * h);
         }
         const float Mx = max16(ml.x);
         const float wv = (ml.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml.x - Mx);
         const float Lsum = sum16(wv * ml.y);
-        lds_barrier();  // the previous block's weights are read
-        wts[wrow * 16 + wmbr] = wv;
+        lds_barrier();  // the previous round's weights are read
+        wts[grp][wrow * 16 + wmbr] = wv;
         if (wmbr == 0) {
-            stat[wrow] = Mx;
-            stat[kRows + wrow] = Lsum;
+            stat[grp][wrow] = Mx;
+            stat[grp][kRows + wrow] = Lsum;
         }
         lds_barrier();
 #pragma unroll
@@ -1137,9 +1147,9 @@ __global__ __launch_bounds__(128) void attn_mfma_merge_kernel(CArgs a) {
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
                 const float ok = (i == 0) ? o[k].x : (i == 1) ? o[k].y : (i == 2) ? o[k].z : o[k].w;
-                ac = fmaf(wts[row * 16 + k], ok, ac);
+                ac = fmaf(wts[grp][row * 16 + k], ok, ac);
             }
-            const float Mc = stat[row], Lc = stat[kRows + row];
+            const float Mc = stat[grp][row], Lc = stat[grp][kRows + row];
             const float Mn = fmaxf(M[i], Mc);
             const float fa = (M[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M[i] - Mn);
             const float fc = (Mc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(Mc - Mn);
@@ -1147,6 +1157,30 @@ __global__ __launch_bounds__(128) void attn_mfma_merge_kernel(CArgs a) {
             acc[i] = fmaf(ac, fc, acc[i] * fa);
             M[i] = Mn;
         }
+    }
+    if constexpr (NGR > 1) {
+        if (grp > 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                cmb[grp - 1][0][i][tid] = M[i];
+                cmb[grp - 1][1][i][tid] = Ls[i];
+                cmb[grp - 1][2][i][tid] = acc[i];
+            }
+        }
+        lds_barrier();
+        if (grp > 0) return;
+#pragma unroll
+        for (int g = 1; g < NGR; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float Mc = cmb[g - 1][0][i][tid];
+                const float Mn = fmaxf(M[i], Mc);
+                const float fa = (M[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M[i] - Mn);
+                const float fc = (Mc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(Mc - Mn);
+                Ls[i] = fmaf(cmb[g - 1][1][i][tid], fc, Ls[i] * fa);
+                acc[i] = fmaf(cmb[g - 1][2][i][tid], fc, acc[i] * fa);
+                M[i] = Mn;
+            }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -1247,7 +1281,14 @@ int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
         m.L = L;
         m.G = a.G;
         m.RB = a.RB;
-        hipLaunchKernelGGL(attn_mfma_merge_kernel, dim3((unsigned)(units * 4)), dim3(128), 0, s, m);
+        // up to 16 splits: one group of 128 threads; more: 2 or 4 groups side
+        // by side, so that a long key range (many splits of few kv heads) is
+        // merged in S / 64 rounds of loads instead of S / 16 (8 groups would
+        // spill registers at 1024 threads)
+        const dim3 mg((unsigned)(units * 4));
+        if (p.S <= 16) hipLaunchKernelGGL(attn_mfma_merge_kernel<1>, mg, dim3(128), 0, s, m);
+        else if (p.S <= 32) hipLaunchKernelGGL(attn_mfma_merge_kernel<2>, mg, dim3(256), 0, s, m);
+        else hipLaunchKernelGGL(attn_mfma_merge_kernel<4>, mg, dim3(512), 0, s, m);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
