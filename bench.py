@@ -210,6 +210,55 @@ def tree_verify(rbq, W, dev, rot, n_calls: int = 200) -> dict:
     }
 
 
+def long_context(rbq, W, dev, rot, n_calls: int = 300) -> dict:
+    """Decode over the long-context workload: B=1, 16 q heads / 2 kv heads,
+    head_dim 256, T=262144, bf16, Student-t (nu = 3) K, K4/V3 group 64: the
+    key range of each kv head split 128 ways and merged by log-sum-exp.  Four
+    cache replicas (512 MiB) cycled against the Infinity Cache; HIP events
+    around back-to-back calls (after 600 warm-up calls).  Bytes: as the
+    batched decode, 256 per token and kv head plus q and out."""
+    w = W.WORKLOADS[5]
+    k, v = W.fill_tokens(w)
+    base = rbq.RotatedQuantKVCache(w.B, w.Hkv, dtype=w.torch_dtype, device=dev, rot=rot)
+    base.append(k.to(dev), v.to(dev))
+    del k, v
+    caches = [base]
+    for _ in range(3):
+        c = rbq.RotatedQuantKVCache(w.B, w.Hkv, dtype=w.torch_dtype, device=dev, rot=rot)
+        c.arrays = {n: a.clone() for n, a in base.arrays.items()}
+        c.desc = rbq.capi.rbq_kv_cache.from_buffer_copy(base.desc)
+        c._bind(c.desc, c.arrays, base.capacity)
+        caches.append(c)
+    q = W.queries(w).to(dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    ws = base.workspace(w.Hq, w.L)
+    S = rbq.capi.rbq_quant_attn_splits(base.desc, w.Hq, w.L)
+    stream = torch.cuda.current_stream()
+    for i in range(600):
+        rbq.capi.rbq_quant_attn_decode(caches[i % 4].desc, q, 1 / 16, True, rot, out, 0, ws)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(n_calls):
+        rbq.capi.rbq_quant_attn_decode(caches[i % 4].desc, q, 1 / 16, True, rot, out, 0, ws)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / n_calls
+    alg = w.B * w.Hkv * w.T * 256 + w.B * w.Hq * w.D * (2 + 4)
+    gbs = alg / (us * 1e-6) / 1e9
+    return {
+        "what": f"decode, B=1, {w.Hq}/{w.Hkv} heads, head_dim 256, T={w.T}, bf16, Student-t K, "
+                f"K4/V3 group 64, {S} key splits per kv head",
+        "bound": "hbm",
+        "alg_bytes_per_call": alg,
+        "avg_us": round(us, 3),
+        "achieved": round(gbs, 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(gbs / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(w.B / (us * 1e-6), 1),
+    }
+
+
 def append_throughput(rbq, W, dev, rot, n_calls: int = 32) -> dict:
     """The append (a2 + a3) of a prefill chunk on the append+verify shapes:
     B=4, 16 q heads / 2 kv heads, head_dim 256, bf16, K4/V3 group 64, 2048
@@ -394,7 +443,7 @@ def main() -> int:
                     help="replay each step from a captured HIP graph (on this stack a replay "
                          "costs more than the two launches it holds)")
     ap.add_argument("--leg", choices=["prefill", "variant_decode", "variant_prefill", "tree_verify",
-                                      "append"],
+                                      "append", "long_context"],
                     help="run only this secondary measurement and print its object "
                          "(for profiling it on its own; not the benchmark line)")
     args = ap.parse_args()
@@ -415,7 +464,8 @@ def main() -> int:
                "variant_decode": lambda: variant_decode(rbq, W, dev),
                "variant_prefill": lambda: prefill(rbq, W, dev, rot, head_dim=128),
                "tree_verify": lambda: tree_verify(rbq, W, dev, rot),
-               "append": lambda: append_throughput(rbq, W, dev, rot)}[args.leg]
+               "append": lambda: append_throughput(rbq, W, dev, rot),
+               "long_context": lambda: long_context(rbq, W, dev, rot)}[args.leg]
         print(json.dumps({args.leg: leg()}), flush=True)
         return 0
 
@@ -546,6 +596,8 @@ def main() -> int:
     pre = prefill(rbq, W, dev, rot)
     print("[bench] append of a prefill chunk", file=sys.stderr, flush=True)
     app = append_throughput(rbq, W, dev, rot)
+    print("[bench] long context", file=sys.stderr, flush=True)
+    lng = long_context(rbq, W, dev, rot)
     print("[bench] decode and prefill, head_dim 128 K4/V4", file=sys.stderr, flush=True)
     var = variant_decode(rbq, W, dev)
     pre128 = prefill(rbq, W, dev, rot, head_dim=128)
@@ -615,6 +667,7 @@ def main() -> int:
         "variant_decode": var,
         "variant_prefill": pre128,
         "append": app,
+        "long_context": lng,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
