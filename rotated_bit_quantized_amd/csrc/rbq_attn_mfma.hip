@@ -68,6 +68,7 @@ constexpr int kRows = 8;                                   // query rows per kv 
 // split record in the workspace: (m, l) per row, then o column-major
 // [256 columns][8 rows]
 constexpr int kRecFloats = 2 * kRows + kRows * kHeadDim;
+constexpr int kMergeNarrowUnits = 32;  // below this many units the merge takes 32-column blocks
 // wave record in LDS, in its own region so that a wave stores it as soon as
 // its tiles are done: o column-major [256 columns][2 row quads][4 rows], the
 // row quad of column c stored at slot quad ^ ((c >> 3) & 1) (conflict-free
@@ -1092,26 +1093,33 @@ struct CArgs {
 // round count in every group so that all threads meet the same barriers (a
 // round past the last record has no members and weight 0); the groups'
 // (M, L, o) are then combined in group order.  NGR = 1 for up to 16 splits.
-template <int NGR>
+// RPT rows per thread: 4 (a workgroup per 64 columns, thread = (column,
+// rows 4h .. 4h+3)) or 2 (per 32 columns, thread = (column, rows 2h, 2h+1)),
+// the latter for calls with few (b, kv head) units, where the merge runs on
+// few compute units.
+template <int NGR, int RPT>
 __global__ __launch_bounds__(128 * NGR) void attn_mfma_merge_kernel(CArgs a) {
+    constexpr int kCols = 128 * RPT / kRows;  // columns per workgroup: 64 or 32
+    constexpr int kCB = kHeadDim / kCols;     // column blocks per (b, kv head, 8 rows)
+    typedef float vecR __attribute__((ext_vector_type(RPT)));
     __shared__ float wts[NGR][kRows * 16];
     __shared__ float stat[NGR][2 * kRows];
-    __shared__ float cmb[NGR > 1 ? NGR - 1 : 1][3][4][128];  // groups 1.. : M, L, o per (row i, thread)
+    __shared__ float cmb[NGR > 1 ? NGR - 1 : 1][3][RPT][128];  // groups 1.. : M, L, o per (row i, thread)
     const int grp = threadIdx.x >> 7;
     const int tid = threadIdx.x & 127;
-    const int bhr = blockIdx.x >> 2;
+    const int bhr = blockIdx.x / kCB;
     const int bh = bhr / a.RB;
     const int r0 = 8 * (bhr - bh * a.RB);
-    const int col = ((blockIdx.x & 3) << 6) + (tid & 63);
-    const int h = tid >> 6;
+    const int col = (blockIdx.x - bhr * kCB) * kCols + (tid % kCols);
+    const int h = tid / kCols;  // rows RPT h .. RPT h + RPT - 1
     const int b = bh / a.Hkv;
     const int kvh = bh - b * a.Hkv;
     const float* base = a.rec + (int64_t)bhr * a.S * kRecFloats;
     const int wrow = tid >> 4, wmbr = tid & 15;
     const float4 rv = rot_row(a.rot, col);
-    float M[4], Ls[4], acc[4];
+    float M[RPT], Ls[RPT], acc[RPT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < RPT; ++i) {
         M[i] = -INFINITY;
         Ls[i] = 0.f;
         acc[i] = 0.f;
@@ -1123,12 +1131,12 @@ __global__ __launch_bounds__(128 * NGR) void attn_mfma_merge_kernel(CArgs a) {
         float2 ml = make_float2(-INFINITY, 0.f);
         if (wmbr < members)
             ml = *reinterpret_cast<const float2*>(base + (int64_t)(m0 + wmbr) * kRecFloats + 2 * wrow);
-        float4 o[16];
+        vecR o[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             const int mbr = (k < members) ? m0 + k : 0;
-            o[k] = *reinterpret_cast<const float4*>(base + (int64_t)mbr * kRecFloats + 2 * kRows +
-                                                    col * kRows + 4 * h);
+            o[k] = *reinterpret_cast<const vecR*>(base + (int64_t)mbr * kRecFloats + 2 * kRows +
+                                                  col * kRows + RPT * h);
         }
         const float Mx = max16(ml.x);
         const float wv = (ml.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml.x - Mx);
@@ -1141,14 +1149,11 @@ __global__ __launch_bounds__(128 * NGR) void attn_mfma_merge_kernel(CArgs a) {
         }
         lds_barrier();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 4 * h + i;
+        for (int i = 0; i < RPT; ++i) {
+            const int row = RPT * h + i;
             float ac = 0.f;
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const float ok = (i == 0) ? o[k].x : (i == 1) ? o[k].y : (i == 2) ? o[k].z : o[k].w;
-                ac = fmaf(wts[grp][row * 16 + k], ok, ac);
-            }
+            for (int k = 0; k < 16; ++k) ac = fmaf(wts[grp][row * 16 + k], o[k][i], ac);
             const float Mc = stat[grp][row], Lc = stat[grp][kRows + row];
             const float Mn = fmaxf(M[i], Mc);
             const float fa = (M[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M[i] - Mn);
@@ -1161,7 +1166,7 @@ __global__ __launch_bounds__(128 * NGR) void attn_mfma_merge_kernel(CArgs a) {
     if constexpr (NGR > 1) {
         if (grp > 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < RPT; ++i) {
                 cmb[grp - 1][0][i][tid] = M[i];
                 cmb[grp - 1][1][i][tid] = Ls[i];
                 cmb[grp - 1][2][i][tid] = acc[i];
@@ -1172,7 +1177,7 @@ __global__ __launch_bounds__(128 * NGR) void attn_mfma_merge_kernel(CArgs a) {
 #pragma unroll
         for (int g = 1; g < NGR; ++g)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < RPT; ++i) {
                 const float Mc = cmb[g - 1][0][i][tid];
                 const float Mn = fmaxf(M[i], Mc);
                 const float fa = (M[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M[i] - Mn);
@@ -1183,9 +1188,9 @@ __global__ __launch_bounds__(128 * NGR) void attn_mfma_merge_kernel(CArgs a) {
             }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        store_out(a.out, a.rot != nullptr, rv, b, a.Hkv, a.n_rep, a.L, a.G, kvh, col, r0 + 4 * h + i,
-                  acc[i], Ls[i]);
+    for (int i = 0; i < RPT; ++i)
+        store_out(a.out, a.rot != nullptr, rv, b, a.Hkv, a.n_rep, a.L, a.G, kvh, col,
+                  r0 + RPT * h + i, acc[i], Ls[i]);
 }
 
 }  // namespace
@@ -1285,10 +1290,19 @@ int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
         // by side, so that a long key range (many splits of few kv heads) is
         // merged in S / 64 rounds of loads instead of S / 16 (8 groups would
         // spill registers at 1024 threads)
-        const dim3 mg((unsigned)(units * 4));
-        if (p.S <= 16) hipLaunchKernelGGL(attn_mfma_merge_kernel<1>, mg, dim3(128), 0, s, m);
-        else if (p.S <= 32) hipLaunchKernelGGL(attn_mfma_merge_kernel<2>, mg, dim3(256), 0, s, m);
-        else hipLaunchKernelGGL(attn_mfma_merge_kernel<4>, mg, dim3(512), 0, s, m);
+        // few (b, kv head, 8 rows) units: 32 columns per workgroup, twice the
+        // workgroups
+        const bool narrow = units < kMergeNarrowUnits;
+        const dim3 mg((unsigned)(units * (narrow ? 8 : 4)));
+        auto go = [&](auto k1, auto k2, auto k4) {
+            if (p.S <= 16) hipLaunchKernelGGL(k1, mg, dim3(128), 0, s, m);
+            else if (p.S <= 32) hipLaunchKernelGGL(k2, mg, dim3(256), 0, s, m);
+            else hipLaunchKernelGGL(k4, mg, dim3(512), 0, s, m);
+        };
+        if (narrow)
+            go(attn_mfma_merge_kernel<1, 2>, attn_mfma_merge_kernel<2, 2>, attn_mfma_merge_kernel<4, 2>);
+        else
+            go(attn_mfma_merge_kernel<1, 4>, attn_mfma_merge_kernel<2, 4>, attn_mfma_merge_kernel<4, 4>);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
