@@ -68,7 +68,7 @@ constexpr int kRows = 8;                                   // query rows per kv 
 // split record in the workspace: (m, l) per row, then o column-major
 // [256 columns][8 rows]
 constexpr int kRecFloats = 2 * kRows + kRows * kHeadDim;
-constexpr int kMergeNarrowUnits = 32;  // below this many units the merge takes 32-column blocks
+constexpr int kMergeNarrowUnits = 64;  // below this many units the merge takes 32-column blocks
 // wave record in LDS, in its own region so that a wave stores it as soon as
 // its tiles are done: o column-major [256 columns][2 row quads][4 rows], the
 // row quad of column c stored at slot quad ^ ((c >> 3) & 1) (conflict-free
