@@ -7,6 +7,26 @@
 
 namespace rbq {
 
+// min / max over the 16 lanes of a DPP row (one group of 64 values, 4 per
+// lane): quad swaps, then the half-row and row mirrors; every lane ends with
+// the result (min and max are exact, so the order does not matter).
+template <int CTRL>
+__device__ __forceinline__ float qdpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float qmin16(float x) {
+    x = fminf(x, qdpp<0xB1>(x));   // quad_perm 1,0,3,2
+    x = fminf(x, qdpp<0x4E>(x));   // quad_perm 2,3,0,1
+    x = fminf(x, qdpp<0x141>(x));  // row_half_mirror
+    return fminf(x, qdpp<0x140>(x));  // row_mirror
+}
+__device__ __forceinline__ float qmax16(float x) {
+    x = fmaxf(x, qdpp<0xB1>(x));
+    x = fmaxf(x, qdpp<0x4E>(x));
+    x = fmaxf(x, qdpp<0x141>(x));
+    return fmaxf(x, qdpp<0x140>(x));
+}
+
 // Quantize and pack one row of 256 values held 4 per lane.
 // The arithmetic is the quantizer definition step by step, each step one
 // IEEE fp32 operation: min/max (exact), (max - min) / (2^bits - 1) with a
@@ -18,13 +38,8 @@ __device__ __forceinline__ void quantize_pack_row(const float y[4], int lane,
                                                   uint16_t* __restrict__ scales,
                                                   uint16_t* __restrict__ biases) {
     constexpr float kLevels = (float)((1 << BITS) - 1);
-    float mn = fminf(fminf(y[0], y[1]), fminf(y[2], y[3]));
-    float mx = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-        mn = fminf(mn, __shfl_xor(mn, m));
-        mx = fmaxf(mx, __shfl_xor(mx, m));
-    }
+    const float mn = qmin16(fminf(fminf(y[0], y[1]), fminf(y[2], y[3])));
+    const float mx = qmax16(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])));
     const float s32 = __fdiv_rn(mx - mn, kLevels);
     const uint32_t s_bits = f32_to_elem_bits<DT>(s32);
     const uint32_t b_bits = f32_to_elem_bits<DT>(mn);
