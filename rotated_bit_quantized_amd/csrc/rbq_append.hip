@@ -88,7 +88,10 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void quant_append_kernel(
     uint16_t* __restrict__ vb, int64_t capacity, int64_t offset, int64_t rows_total,
     int round_rot) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    // the wave's row, wave-uniform (readfirstlane): its index arithmetic,
+    // a 64-bit division included, runs on the scalar unit
+    const int64_t row =
+        (int64_t)blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (row >= rows_total) return;  // uniform per wave
     const int64_t bh = row / n;
     const int64_t t = row - bh * n;
@@ -126,7 +129,10 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void quant_append_any_kernel(
     uint16_t* __restrict__ kb, uint32_t* __restrict__ vw, uint16_t* __restrict__ vs,
     uint16_t* __restrict__ vb, int64_t capacity, int64_t offset, int64_t rows_total, AnyCfg g) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    // the wave's row, wave-uniform (readfirstlane): its index arithmetic,
+    // a 64-bit division included, runs on the scalar unit
+    const int64_t row =
+        (int64_t)blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (row >= rows_total) return;  // uniform per wave
     const int64_t bh = row / n;
     const int64_t t = row - bh * n;
