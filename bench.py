@@ -299,9 +299,9 @@ def append_throughput(rbq, W, dev, rot, n_calls: int = 32) -> dict:
         "what": f"append of {n} tokens after {T0} cached, B={B}, {Hkv} kv heads, head_dim 256, bf16, "
                 "K4/V3 group 64 (rbq_kv_quant_append: rotate, quantize, pack, write)",
         "bound": "alu",
-        "note": "VALU-bound, not HBM-bound: about 640 instructions per row and wave (fp64 "
-                "rotation, ten correctly rounded divisions, group min/max shuffles, packing); "
-                "frac is against the HBM peak, for context",
+        "note": "VALU-bound, not HBM-bound: about 470 vector instructions per row and wave "
+                "(fp64 rotation, group min/max, codes, packing); frac is against the HBM peak, "
+                "for context",
         "bytes_per_call": nbytes,
         "avg_us": round(us, 3),
         "achieved": round(gbs, 2),

@@ -10,6 +10,23 @@ namespace rbq {
 // min / max over the 16 lanes of a DPP row (one group of 64 values, 4 per
 // lane): quad swaps, then the half-row and row mirrors; every lane ends with
 // the result (min and max are exact, so the order does not matter).
+// rint(fdiv_rn(x, s)), the code before clipping, with the correctly rounded
+// division only where it can matter: q = x * rcp(s) is within a few ulp of
+// x / s, so unless q lies within tol (at least 8 ulp) of a half-integer, the
+// correctly rounded quotient rounds to the same integer.  Ties, near-ties
+// and non-finite q (rcp of an fp32-denormal scale) take the exact division.
+__device__ __forceinline__ float quant_code(float x, float s, float rinv) {
+    const float q = x * rinv;
+    const float fr = q - floorf(q);
+    const float tol = fmaxf(fabsf(q), 1.0f) * 0x1p-20f;
+    float c = rintf(q);
+    const bool near = !(fabsf(fr - 0.5f) > tol);
+    if (__any(near)) {  // rare: a wave-uniform branch, so the division is skipped otherwise
+        if (near) c = rintf(__fdiv_rn(x, s));
+    }
+    return c;
+}
+
 template <int CTRL>
 __device__ __forceinline__ float qdpp(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
@@ -47,10 +64,11 @@ __device__ __forceinline__ void quantize_pack_row(const float y[4], int lane,
     const float beta = elem_to_f32<DT>(b_bits);
     const float sdiv = (s == 0.0f) ? 1.0f : s;
 
+    const float rinv = __builtin_amdgcn_rcpf(sdiv);
     uint32_t chunk = 0;  // 4 codes = 4*BITS bits, code i at bit BITS*i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float c = rintf(__fdiv_rn(y[i] - beta, sdiv));
+        float c = quant_code(y[i] - beta, sdiv, rinv);
         c = fminf(fmaxf(c, 0.0f), kLevels);
         chunk |= (uint32_t)c << (BITS * i);
     }
