@@ -45,10 +45,11 @@ __device__ __forceinline__ void quantize_pack_row_any(const float y[4], int lane
     const float beta = elem_to_f32<DT>(b_bits);
     const float sdiv = (s == 0.0f) ? 1.0f : s;
 
+    const float rinv = __builtin_amdgcn_rcpf(sdiv);
     uint32_t chunk = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float c = rintf(__fdiv_rn(y[i] - beta, sdiv));
+        float c = quant_code(y[i] - beta, sdiv, rinv);
         c = fminf(fmaxf(c, 0.0f), levels);
         chunk |= (uint32_t)c << (bits * i);
     }
