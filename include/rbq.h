@@ -57,7 +57,8 @@ extern "C" {
  * the quant_kv.py page multiplies by R.astype(x.dtype), so its result is in
  * the input dtype): every rotated row - K and V before they are quantized,
  * q before the attention - is rounded to the cache dtype (round half to
- * even).  The caller passes rotation blocks already rounded to the dtype.
+ * even).  The caller passes rotation blocks already rounded to the dtype
+ * (rbq_rotation_round).
  * Without the flag rotated rows stay fp32. */
 #define RBQ_FLAG_ROUND_ROTATED 1
 
@@ -121,6 +122,21 @@ int rbq_rotation_build(const float* draws, int32_t head_dim, float* blocks);
  * Errors: as rbq_rotation_build, and RBQ_EINVAL for an unknown mode.
  */
 int rbq_rotation_build_mode(const float* draws, int32_t head_dim, int32_t mode, float* blocks);
+
+/*
+ * rbq_rotation_round - the rotation blocks rounded to the cache dtype, in
+ * place: the page's own rotation precision (rotate_last on the quant_kv.py
+ * page multiplies by R.astype(x.dtype)), to be used with a cache whose flags
+ * hold RBQ_FLAG_ROUND_ROTATED.  Host only.
+ *   blocks  host float [head_dim/4][4][4] (from rbq_rotation_build or
+ *           rbq_rotation_build_mode); each entry is replaced by its
+ *           round-half-to-even value in `dtype`, which a float holds exactly.
+ *   dtype   RBQ_F16 or RBQ_BF16.
+ * Errors: RBQ_EINVAL for null blocks, head_dim <= 0, head_dim % 4 != 0 or a
+ * non-finite entry (then nothing is changed); RBQ_EUNSUPPORTED for another
+ * dtype.
+ */
+int rbq_rotation_round(float* blocks, int32_t head_dim, int32_t dtype);
 
 /*
  * rbq_kv_required_capacity - capacity (rows) the cache needs before n more

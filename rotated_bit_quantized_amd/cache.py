@@ -48,10 +48,12 @@ def build_block_so4(head_dim: int = HEAD_DIM, seed: int = 0, device="cuda",
     page's ``R.astype(x.dtype)``; pair it with a cache made with
     ``round_rotated=True``)."""
     mode = capi.RBQ_ROT_TWO_SIDED if two_sided else capi.RBQ_ROT_PRINTED
-    blocks = torch.from_numpy(capi.rbq_rotation_build_mode(quaternion_draws(seed, head_dim), mode))
+    blocks = capi.rbq_rotation_build_mode(quaternion_draws(seed, head_dim), mode)
     if round_to is not None:
-        blocks = blocks.to(round_to).float()
-    return blocks.to(device)
+        if round_to not in capi.DTYPE_CODES:
+            raise ValueError("round_to must be torch.float16 or torch.bfloat16")
+        blocks = capi.rbq_rotation_round(blocks, capi.DTYPE_CODES[round_to])
+    return torch.from_numpy(blocks).to(device)
 
 
 class RotatedQuantKVCache:

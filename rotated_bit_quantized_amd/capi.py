@@ -77,6 +77,7 @@ def _load():
     sigs = {
         "rbq_rotation_build": (c_int32, [c_void_p, c_int32, c_void_p]),
         "rbq_rotation_build_mode": (c_int32, [c_void_p, c_int32, c_int32, c_void_p]),
+        "rbq_rotation_round": (c_int32, [c_void_p, c_int32, c_int32]),
         "rbq_kv_required_capacity": (c_int64, [c_int64, c_int64, c_int64]),
         "rbq_kv_grow": (c_int32, [P, P, c_void_p]),
         "rbq_kv_copy_prefix": (c_int32, [P, P, c_void_p]),
@@ -158,6 +159,16 @@ def rbq_rotation_build_mode(draws: np.ndarray, mode: int) -> np.ndarray:
     _check("rbq_rotation_build_mode",
            _lib.rbq_rotation_build_mode(d.ctypes.data, 4 * d.shape[0], int(mode), out.ctypes.data))
     return out
+
+
+def rbq_rotation_round(blocks: np.ndarray, dtype: int) -> np.ndarray:
+    """A copy of the blocks ``float32 [D/4, 4, 4]`` with every entry rounded
+    half to even to the cache dtype (RBQ_F16 or RBQ_BF16), host only."""
+    b = np.array(blocks, dtype=np.float32, order="C", copy=True)
+    if b.ndim != 3 or b.shape[1:] != (4, 4):
+        raise ValueError("blocks must be float32 [D/4, 4, 4]")
+    _check("rbq_rotation_round", _lib.rbq_rotation_round(b.ctypes.data, 4 * b.shape[0], int(dtype)))
+    return b
 
 
 def rbq_kv_required_capacity(capacity: int, offset: int, n: int) -> int:

@@ -41,9 +41,13 @@
 //   scaled in fp16 (exact for bf16 scales: 3 + 8 significant bits; fp16
 //   scales are split into an exact 8-bit head and 3-bit tail); the group bias
 //   enters as sum_t p_t b_{t,g} through one more MFMA.
-// Precondition of the fp16 value path: V group ranges (max - min of the
-// rotated values) and |V bias| stay below 65504; larger values overflow to
-// inf and show up as non-finite outputs.
+// Range of the fp16 value path: the V scales and biases enter the fp16
+// operands times 2^-F, with F a per-wave power of two that stays 0 while
+// every |scale| and |bias| seen is below 2^13 and otherwise grows so that
+// they stay below 2^13 * 2^F (codes times scales then stay below 65504); the
+// accumulators are rescaled when F grows and the wave's record is taken
+// back to unit scale.  So any finite bf16 values are taken, as long as the
+// fp32 accumulators (the probability-weighted sums of values) stay finite.
 #include <hip/hip_runtime.h>
 
 #include "rbq_common.h"
@@ -748,6 +752,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     float l_part[2] = {0.f, 0.f};
     float thr[2] = {-INFINITY, -INFINITY};
     f32x4 cinit = {0.f, 0.f, 0.f, 0.f};
+    // the value operands' power of two (wave-uniform): O and Ob hold the
+    // products in units of 2^v_f; v_lim = 2^(13 + v_f)
+    int v_f = 0;
+    float v_lim = 8192.0f;
 
     for (int kth = 0, it = it_first; it < n_tiles; ++kth) {
         const int t0 = t_begin + it * kTile;
@@ -768,24 +776,62 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
         // ---- value scales and biases of the lane's (key, group) -> staging,
         //      each fp16 value repeated 4 times (the 8 bytes a transposing
-        //      read takes one element of) ----
+        //      read takes one element of).  They enter the fp16 operands
+        //      times 2^-F: F stays 0 until some |scale| or |bias| reaches
+        //      2^13 * 2^F, then grows so that every one stays below 2^13
+        //      (codes times scales below 7 * 2^13 < 65504) and the
+        //      accumulators are rescaled to the new unit ----
+        float vsf[2], vbf[2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            vsf[blk] = elem_to_f32<DT>(cur.vsb[blk]);
+            vbf[blk] = elem_to_f32<DT>(cur.vbb[blk]);
+        }
+        {
+            const float vm = fmaxf(fmaxf(fabsf(vsf[0]), fabsf(vsf[1])), fmaxf(fabsf(vbf[0]), fabsf(vbf[1])));
+            if (__any(vm >= v_lim)) {  // rare: a wave-uniform branch
+                float wm = max16(vm);
+                wm = fmaxf(wm, __shfl_xor(wm, 16));
+                wm = fmaxf(wm, __shfl_xor(wm, 32));
+                int ex = 0;
+                (void)frexpf(wm, &ex);  // wm < 2^ex
+                const int f_new = __builtin_amdgcn_readfirstlane(max(v_f, ex - 13));
+                const float r = ldexpf(1.0f, v_f - f_new);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) O[t][c] *= r;
+                    Ob[c] *= r;
+                }
+                v_f = f_new;
+                v_lim = ldexpf(1.0f, 13 + v_f);
+            }
+            if (v_f != 0) {
+                const float pf = ldexpf(1.0f, -v_f);
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk) {
+                    vsf[blk] *= pf;
+                    vbf[blk] *= pf;
+                }
+            }
+        }
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             const uint32_t off = (blk * 64 + lane) << 3;
             uint32_t s2, b2;
             if constexpr (DT == RBQ_BF16) {
                 const uint32_t x = __builtin_bit_cast(
-                    uint32_t, (f16x2){(_Float16)bf16_bits_to_f32(cur.vsb[blk]),
-                                      (_Float16)bf16_bits_to_f32(cur.vbb[blk])});
+                    uint32_t, (f16x2){(_Float16)vsf[blk], (_Float16)vbf[blk]});
                 s2 = __builtin_amdgcn_perm(x, x, 0x01000100u);  // low half twice
                 b2 = __builtin_amdgcn_perm(x, x, 0x03020302u);  // high half twice
             } else {
-                // head: top 8 significant bits; tail: the other 3 (both exact)
-                const uint32_t sh = cur.vsb[blk] & 0xFFF8u;
+                // head: top 8 significant bits; tail: the other 3 (both exact
+                // unless the scaled value falls below the fp16 normal range)
+                const uint32_t sh = f32_to_f16_bits(vsf[blk]) & 0xFFF8u;
                 const uint32_t st = __builtin_bit_cast(
-                    uint16_t, (_Float16)(f16_bits_to_f32(cur.vsb[blk]) - f16_bits_to_f32(sh)));
+                    uint16_t, (_Float16)(vsf[blk] - f16_bits_to_f32(sh)));
                 s2 = sh * 0x10001u;
-                b2 = (cur.vbb[blk] & 0xFFFFu) * 0x10001u;
+                b2 = f32_to_f16_bits(vbf[blk]) * 0x10001u;
                 lds_st32(smem, t_off + off, st * 0x10001u);
                 lds_st32(smem, t_off + off + 4, st * 0x10001u);
             }
@@ -980,10 +1026,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     float* wrec = reinterpret_cast<float*>(tbuf) + wave * kWaveRecFloats;
     float* wob = wrec + kHeadDim * kRows;
     float* wml = wob + kGroups * kRows;
-    auto comb = [](float x, float y) -> float {
+    // the value products back from units of 2^v_f (exact: a power of two)
+    const float v_unit = ldexpf(1.0f, v_f);
+    auto comb = [v_unit](float x, float y) -> float {
         const auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false,
                                                          false);
-        return __uint_as_float(s2[0]) + __uint_as_float(s2[1]);
+        return (__uint_as_float(s2[0]) + __uint_as_float(s2[1])) * v_unit;
     };
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
@@ -1061,9 +1109,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (a.S == 1) {
         const float4 rv = rot_row(a.rot, col);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            store_out(a.out, rotated, rv, b, a.Hkv, a.n_rep, a.L, a.G, kvh, col, r0 + 4 * h + i,
-                      acc[i], Ls[i]);
+        for (int i = 0; i < 4; ++i) {
+            float av = acc[i], lv = Ls[i];
+            if constexpr (MK == kMaskBool) {
+                // a row whose every key the mask drops: the mean of its keys
+                const int R = r0 + 4 * h + i;
+                if (lv == 0.f && R < a.G) {
+                    const int nv = a.causal ? T - a.L + (R % a.L) + 1 : T;
+                    av = value_column_mean<DT>(a.vw, a.vs, a.vb, row0, nv, col, kVBits, kVWords,
+                                               kGroups, kGroup);
+                    lv = 1.f;
+                }
+            }
+            store_out(a.out, rotated, rv, b, a.Hkv, a.n_rep, a.L, a.G, kvh, col, r0 + 4 * h + i, av,
+                      lv);
+        }
         return;
     }
     float* rp = a.rec + ((int64_t)bhr * a.S + split) * kRecFloats;
@@ -1086,6 +1146,13 @@ struct CArgs {
     const float* rot;
     float* out;
     int S, Hkv, n_rep, L, G, RB;
+    // boolean-mask calls: rows without a kept key take the mean of their
+    // keys' values (value_column_mean) from the cache
+    int bool_mask, dt, T, causal;
+    int64_t capacity;
+    const uint32_t* vw;
+    const uint16_t* vs;
+    const uint16_t* vb;
 };
 
 // NGR groups of 128 threads each take every NGR-th round of 16 records
@@ -1188,9 +1255,22 @@ __global__ __launch_bounds__(128 * NGR) void attn_mfma_merge_kernel(CArgs a) {
             }
     }
 #pragma unroll
-    for (int i = 0; i < RPT; ++i)
-        store_out(a.out, a.rot != nullptr, rv, b, a.Hkv, a.n_rep, a.L, a.G, kvh, col,
-                  r0 + RPT * h + i, acc[i], Ls[i]);
+    for (int i = 0; i < RPT; ++i) {
+        float av = acc[i], lv = Ls[i];
+        const int R = r0 + RPT * h + i;
+        if (a.bool_mask && lv == 0.f && R < a.G) {
+            // no kept key in any split: the mean of the row's keys
+            const int nv = a.causal ? a.T - a.L + (R % a.L) + 1 : a.T;
+            const int64_t row0 = (int64_t)bh * a.capacity;
+            av = (a.dt == RBQ_BF16)
+                     ? value_column_mean<RBQ_BF16>(a.vw, a.vs, a.vb, row0, nv, col, kVBits, kVWords,
+                                                   kGroups, kGroup)
+                     : value_column_mean<RBQ_F16>(a.vw, a.vs, a.vb, row0, nv, col, kVBits, kVWords,
+                                                  kGroups, kGroup);
+            lv = 1.f;
+        }
+        store_out(a.out, a.rot != nullptr, rv, b, a.Hkv, a.n_rep, a.L, a.G, kvh, col, R, av, lv);
+    }
 }
 
 }  // namespace
@@ -1286,6 +1366,14 @@ int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
         m.L = L;
         m.G = a.G;
         m.RB = a.RB;
+        m.bool_mask = (mt == kMaskBool) ? 1 : 0;
+        m.dt = c->dtype;
+        m.T = a.T;
+        m.causal = a.causal;
+        m.capacity = c->capacity;
+        m.vw = a.vw;
+        m.vs = a.vs;
+        m.vb = a.vb;
         // up to 16 splits: one group of 128 threads; more: 2 or 4 groups side
         // by side, so that a long key range (many splits of few kv heads) is
         // merged in S / 64 rounds of loads instead of S / 16 (8 groups would

@@ -747,8 +747,12 @@ void attn_tile_kernel(TArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int R = r0 + 16 * wave + 4 * j + i;
-            const float inv = 1.0f / tsum16(l_part[i]);
+            const float lsum = tsum16(l_part[i]);
+            const float inv = 1.0f / lsum;
             if (R >= a.G) continue;  // uniform over the 16 lanes of the row
+            // a boolean mask dropped every key of the row: the mean of its keys
+            const bool uniform = a.mtype == 1 && lsum == 0.f;
+            const int nv = a.causal ? T - a.L + (R % a.L) + 1 : T;
             const int hq = kvh * a.n_rep + R / a.L;
             float* orow = a.out + (((int64_t)b * a.Hkv * a.n_rep + hq) * a.L + R % a.L) * D;
 #pragma unroll
@@ -757,7 +761,10 @@ void attn_tile_kernel(TArgs a) {
 #pragma unroll
                 for (int t = g * NPG; t < (g + 1) * NPG; ++t) {
                     const int col = 16 * t + n;
-                    const float y = (O[t][i] * vinv1[g] + bias) * inv;
+                    float y = (O[t][i] * vinv1[g] + bias) * inv;
+                    if (uniform)
+                        y = value_column_mean<DT>(a.vw, a.vs, a.vb, row0, nv, col, a.vbits,
+                                                  D * a.vbits / 32, NG, a.GS);
                     float z = y;
                     if (a.rot != nullptr) {
                         const float4 v = *reinterpret_cast<const float4*>(a.rot + 16 * (col >> 2) + 4 * (col & 3));
@@ -806,6 +813,13 @@ struct TMArgs {
     const float* rot;
     float* out;
     int S, Hkv, n_rep, L, G, RBW, RW;
+    // boolean-mask calls: rows without a kept key take the mean of their
+    // keys' values (value_column_mean) from the cache
+    int bool_mask, dt, T, causal, vbits, GS;
+    int64_t capacity;
+    const uint32_t* vw;
+    const uint16_t* vs;
+    const uint16_t* vb;
 };
 
 constexpr int tMaxSplits = 1024;  // key splits of one call (the merge keeps a weight per split)
@@ -924,6 +938,19 @@ __global__ __launch_bounds__(256) void attn_tile_merge_kernel(TMArgs a) {
     }
     const float inv = 1.0f / Ls;
     float y[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+    if (a.bool_mask && Ls == 0.f) {
+        // no kept key in any split: the mean of the row's keys
+        const int nv = a.causal ? a.T - a.L + (R % a.L) + 1 : a.T;
+        const int64_t row0 = (int64_t)bh * a.capacity;
+        const int vwords = D * a.vbits / 32, ng = D / a.GS;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            y[e] = (a.dt == RBQ_BF16)
+                       ? value_column_mean<RBQ_BF16>(a.vw, a.vs, a.vb, row0, nv, 4 * tid + e, a.vbits,
+                                                     vwords, ng, a.GS)
+                       : value_column_mean<RBQ_F16>(a.vw, a.vs, a.vb, row0, nv, 4 * tid + e, a.vbits,
+                                                    vwords, ng, a.GS);
+    }
     float z[4] = {y[0], y[1], y[2], y[3]};
     if (a.rot != nullptr) unrotate4(y, Bm, z);
     const int hq = kvh * a.n_rep + R / a.L;
@@ -1081,6 +1108,16 @@ int tile_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
     m.G = a.G;
     m.RBW = p.RBW;
     m.RW = 16 * p.W;
+    m.bool_mask = (a.mtype == RBQ_MASK_BOOL) ? 1 : 0;
+    m.dt = c->dtype;
+    m.T = a.T;
+    m.causal = a.causal;
+    m.vbits = c->v_bits;
+    m.GS = c->group_size;
+    m.capacity = c->capacity;
+    m.vw = a.vw;
+    m.vs = a.vs;
+    m.vb = a.vb;
     const dim3 mgrid((unsigned)(units * 16 * p.W)), mblock(256);
     switch (c->head_dim) {
         case 64: hipLaunchKernelGGL(attn_tile_merge_kernel<64>, mgrid, mblock, 0, s, m); break;

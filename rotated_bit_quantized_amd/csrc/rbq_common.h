@@ -90,6 +90,36 @@ __device__ __forceinline__ void load_block(const float* __restrict__ rot, int bl
     }
 }
 
+// Mean of the dequantised values c * s + b of column `col` over the keys
+// [0, n) of one (b, kv head) slab whose first row is `row0` (n >= 1), summed
+// in fp64 in key order and rounded once to fp32.  The SDPA on the quant_kv.py
+// page fills the scores a boolean mask drops with the dtype's most negative
+// value before its softmax, so a query row whose every key is dropped weights
+// all of its keys alike: its output is this mean.  The attention kernels skip
+// dropped keys, find such a row (no key kept, row sum 0) in their last stage
+// and take this loop there instead; it runs only for such rows.
+//   vw [rows][vwords] packed V words (little-endian bit stream of vbits-bit
+//   codes), vs / vb [rows][ng] V scales and biases of groups of gs columns.
+template <int DT>
+__device__ float value_column_mean(const uint32_t* vw, const uint16_t* vs,
+                                                const uint16_t* vb, int64_t row0, int n, int col,
+                                                int vbits, int vwords, int ng, int gs) {
+    const int p = vbits * col, wi = p >> 5, sh = p & 31;
+    const bool straddle = sh + vbits > 32;
+    const uint32_t m = (1u << vbits) - 1u;
+    const int g = col / gs;
+    double s = 0.0;
+    for (int t = 0; t < n; ++t) {
+        const int64_t r = row0 + t;
+        const uint32_t* w = vw + r * vwords;
+        uint32_t bits = w[wi] >> sh;
+        if (straddle) bits |= w[wi + 1] << (32 - sh);
+        const double c = (double)(bits & m);
+        s += c * (double)elem_to_f32<DT>(vs[r * ng + g]) + (double)elem_to_f32<DT>(vb[r * ng + g]);
+    }
+    return (float)(s / (double)n);
+}
+
 // Four consecutive input elements (8 bytes, 8-byte aligned) as floats.
 template <int DT>
 __device__ __forceinline__ void load4(const uint16_t* __restrict__ p, float x[4]) {

@@ -92,9 +92,37 @@ bool normalize(const float a[4], double q[4]) {
     return true;
 }
 
+// x rounded half to even to the grid of a binary format with `mant_bits`
+// fraction bits, smallest normal exponent `emin` (subnormals below it) and
+// largest finite value `maxval`; beyond it the result is an infinity.  The
+// scaling by powers of two and the rounding to an integer are exact in double
+// for every float x, and nearbyint rounds half to even in the default mode.
+float round_to_format(float x, int mant_bits, int emin, double maxval) {
+    if (x == 0.0f) return x;
+    int e = 0;
+    (void)frexp((double)x, &e);  // |x| in [2^(e-1), 2^e)
+    int ex = e - 1;
+    if (ex < emin) ex = emin;
+    const double q = ldexp(nearbyint(ldexp((double)x, mant_bits - ex)), ex - mant_bits);
+    if (fabs(q) > maxval) return x < 0 ? -INFINITY : INFINITY;
+    return (float)q;
+}
+
 }  // namespace
 
 extern "C" {
+
+int rbq_rotation_round(float* blocks, int32_t head_dim, int32_t dtype) {
+    if (blocks == nullptr || head_dim <= 0 || head_dim % 4 != 0) return RBQ_EINVAL;
+    if (dtype != RBQ_F16 && dtype != RBQ_BF16) return RBQ_EUNSUPPORTED;
+    const int n = head_dim * 4;
+    for (int i = 0; i < n; ++i)
+        if (!isfinite(blocks[i])) return RBQ_EINVAL;
+    for (int i = 0; i < n; ++i)
+        blocks[i] = (dtype == RBQ_F16) ? round_to_format(blocks[i], 10, -14, 65504.0)
+                                       : round_to_format(blocks[i], 7, -126, 0x1.FEp127);
+    return RBQ_OK;
+}
 
 int rbq_rotation_build(const float* draws, int32_t head_dim, float* blocks) {
     return rbq_rotation_build_mode(draws, head_dim, RBQ_ROT_PRINTED, blocks);

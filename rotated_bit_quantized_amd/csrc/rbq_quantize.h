@@ -15,12 +15,16 @@ namespace rbq {
 // x / s, so unless q lies within tol (at least 8 ulp) of a half-integer, the
 // correctly rounded quotient rounds to the same integer.  Ties, near-ties
 // and non-finite q (rcp of an fp32-denormal scale) take the exact division.
+// A non-finite q is found from its exponent bits (an integer test), so that
+// the decision holds in every translation unit, also one built with
+// -fno-honor-nans, where a float compare against a NaN may be folded.
 __device__ __forceinline__ float quant_code(float x, float s, float rinv) {
     const float q = x * rinv;
     const float fr = q - floorf(q);
     const float tol = fmaxf(fabsf(q), 1.0f) * 0x1p-20f;
     float c = rintf(q);
-    const bool near = !(fabsf(fr - 0.5f) > tol);
+    const bool nonfinite = (__float_as_uint(q) & 0x7F800000u) == 0x7F800000u;
+    const bool near = nonfinite || !(fabsf(fr - 0.5f) > tol);
     if (__any(near)) {  // rare: a wave-uniform branch, so the division is skipped otherwise
         if (near) c = rintf(__fdiv_rn(x, s));
     }

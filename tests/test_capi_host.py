@@ -77,6 +77,48 @@ def test_rotation_build_two_sided_bit_exact_vs_oracle(D):
         capi.RBQ_EINVAL
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("mode", ["printed", "two_sided"])
+def test_rotation_round_bit_exact_vs_oracle(dtype, mode):
+    # the page's own rotation precision: blocks rounded to the cache dtype by
+    # the library, against the oracle's rounding of the oracle's blocks
+    code = capi.RBQ_BF16 if dtype == "bf16" else capi.RBQ_F16
+    for D, seed in ((256, 0), (128, 5), (64, 9)):
+        draws = W.rotation_draws(seed, D)
+        cmode = capi.RBQ_ROT_TWO_SIDED if mode == "two_sided" else capi.RBQ_ROT_PRINTED
+        got = capi.rbq_rotation_round(capi.rbq_rotation_build_mode(draws, cmode), code)
+        want = O.round_to_dtype(O.rotation_blocks(draws, mode=mode), dtype)
+        np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_rotation_round_ties_subnormals_overflow(dtype):
+    # the rounding on its own, over values that are not rotation entries:
+    # exact ties, fp16 subnormal halves, values that round up to the next
+    # power of two and past the largest finite value
+    code = capi.RBQ_BF16 if dtype == "bf16" else capi.RBQ_F16
+    rng = np.random.default_rng(31)
+    x = np.concatenate([
+        rng.standard_normal(4000) * 10.0 ** rng.integers(-9, 6, 4000),
+        np.float32(1.0) + np.float32(2.0 ** -11) * np.arange(-8, 9),   # fp16 ties around 1
+        np.float32(1.0) + np.float32(2.0 ** -8) * np.arange(-8, 9),    # bf16 ties around 1
+        np.float32(2.0 ** -24) * np.arange(0, 40) / 4,                  # fp16 subnormal ties
+        np.array([65504.0, 65519.0, 65520.0, 65536.0, 3.3e38, -65520.0, 2.0 ** -25,
+                  3.0 * 2.0 ** -26, 0.0, -0.0]),
+    ]).astype(np.float32)
+    x = x[: (x.size // 64) * 64].reshape(-1, 4, 4)
+    with np.errstate(over="ignore"):
+        want = O.round_to_dtype(x, dtype)
+    got = capi.rbq_rotation_round(x, code)
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+    bad = np.ones((1, 4, 4), np.float32)
+    bad[0, 1, 2] = np.inf
+    with pytest.raises(capi.RbqError):
+        capi.rbq_rotation_round(bad, code)
+    assert capi.library().rbq_rotation_round(bad.ctypes.data, 4, 7) == capi.RBQ_EUNSUPPORTED
+    assert capi.library().rbq_rotation_round(None, 4, code) == capi.RBQ_EINVAL
+
+
 def test_required_capacity_matches_oracle():
     for cap in (0, 256, 512, 8192, 10240, 10496):
         for off in sorted({0, 1, cap // 2, max(cap - 1, 0), cap, 255, 257}):

@@ -53,3 +53,24 @@ def _rule_holds_near(x, s):
         tol = np.maximum(np.abs(q), np.float32(1.0)) * np.float32(2.0 ** -20)
         fast = np.abs(fr - np.float32(0.5)) > tol
         assert np.array_equal(np.rint(q)[fast], exact[fast])
+
+
+def test_rule_with_subnormal_scales():
+    # scales in the fp32 subnormal range (groups whose range is about 1e-38):
+    # the reciprocal overflows, q = x * r is inf or NaN, and the exponent-bit
+    # test sends the code to the correctly rounded division; where q stays
+    # finite the rule above still holds
+    rng = np.random.default_rng(20262)
+    s = (rng.uniform(1e-45, 1.2e-38, 100000)).astype(np.float32)
+    s = s[s > 0]
+    x = (rng.uniform(0.0, 1.0, s.size) * 15 * s).astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        exact = np.rint((x / s).astype(np.float32))
+        r = (np.float32(1.0) / s).astype(np.float32)
+        q = (x * r).astype(np.float32)
+        nonfinite = (q.view(np.uint32) & np.uint32(0x7F800000)) == np.uint32(0x7F800000)
+        assert nonfinite.any() and np.array_equal(nonfinite, ~np.isfinite(q))
+        fr = q - np.floor(q)
+        tol = np.maximum(np.abs(q), np.float32(1.0)) * np.float32(2.0 ** -20)
+        fast = ~nonfinite & (np.abs(fr - np.float32(0.5)) > tol)
+    assert np.array_equal(np.rint(q)[fast], exact[fast])

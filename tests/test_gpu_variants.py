@@ -259,3 +259,26 @@ def test_tile_kernel_single_key(var, dev):
     vhat = O.inverse_rotate(oc.dequant_kv(0, 0)[1][0].astype(np.float32), blocks)
     np.testing.assert_allclose(ref[0, 0, 0], vhat, rtol=0, atol=1e-6)
     assert float(np.abs(out.cpu().numpy() - ref).max()) <= ATOL
+
+
+# single-wave tile workgroups (up to 16 rows per kv head at head_dim <= 128)
+# with one split, so that each workgroup walks many tiles (the running scale
+# powers and the staging transfers are carried across all of them): 4 groups
+# per row (two scale / bias items per thread) and 2 groups per row
+@pytest.mark.parametrize("var", [(128, 32, 4, 4, "bf16", False, False),
+                                 (128, 32, 3, 5, "f16", True, False),
+                                 (128, 64, 4, 4, "bf16", True, False)], ids=_vid)
+@pytest.mark.parametrize("splits", [1, 2])
+def test_single_wave_tile_kernel_many_tiles(var, splits, dev):
+    print(f"[single-wave tiles] {_vid(var)} splits={splits}", flush=True)
+    D = var[0]
+    B, Hq, Hkv, T = 1, 16, 2, 2900   # 91 tiles of 32 keys per split at splits=1
+    c, oc, blocks, _ = _setup(var, dev, B, Hkv, T, 32)
+    assert capi.rbq_quant_attn_splits(c.desc, Hq, 1) >= 1
+    for L in (1, 2):
+        q = W.random_rows([33, L], (B, Hq, L, D), var[4])
+        out = c.attend(q.to(dev), scale=D ** -0.5, causal=True, splits=splits)
+        torch.cuda.synchronize()
+        ref = O.attention(q.float().numpy(), oc, D ** -0.5, True, blocks)
+        err = float(np.abs(out.cpu().numpy() - ref).max())
+        assert err <= ATOL, (L, err)
