@@ -12,7 +12,9 @@
  *   - Return value: RBQ_OK (0) or a negative RBQ_E* status; functions that
  *     return a count return it when >= 0 and a negative status otherwise.
  *     Nothing throws across the ABI.  rbq_status_string() names a status.
- *   - Memory: the library allocates no device memory and owns no buffer.
+ *   - Memory: the library allocates no device memory and owns no buffer,
+ *     except the fixed scratch array of rbq_quant_attn_decode_noalloc
+ *     (RBQ_SCRATCH_BYTES per device, part of the loaded code object).
  *     Every pointer is owned by the caller.  "device" pointers are HIP device
  *     allocations on the current device; "host" pointers are ordinary memory.
  *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the legacy
@@ -47,6 +49,11 @@ extern "C" {
 #define RBQ_ERANGE        -4  /* L < 1 or L > offset (no visible key for some query row)    */
 #define RBQ_EWORKSPACE    -5  /* workspace missing or smaller than required                 */
 #define RBQ_EHIP          -6  /* a HIP call or kernel launch failed                         */
+#define RBQ_ESCRATCH      -7  /* the call needs more than the fixed scratch array holds     */
+
+/* Bytes of the fixed device scratch array of rbq_quant_attn_decode_noalloc
+ * (one per device the library runs on, held until the process ends). */
+#define RBQ_SCRATCH_BYTES (8u << 20)
 
 /* ---- element types of the key/value/query inputs and of scales/biases ---- */
 #define RBQ_F16   1
@@ -307,6 +314,26 @@ int rbq_kv_append_attn_decode(rbq_kv_cache* c, const void* k, const void* v, int
                               const void* q, int32_t H_q, int32_t L, float scale, int32_t causal,
                               const float* rot_blocks, float* out, int32_t splits, void* ws,
                               size_t ws_bytes, void* stream);
+
+/*
+ * rbq_quant_attn_decode_noalloc - rbq_quant_attn_decode without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * split records live in a fixed device array of RBQ_SCRATCH_BYTES, one per
+ * device, whose address the library takes (hipGetSymbolAddress) on the first
+ * call on each device; the call itself allocates nothing.  Arguments,
+ * kernels and results are those of rbq_quant_attn_decode with the same
+ * splits (out is bit for bit the same).  The array keeps the last call's
+ * contents and nothing in it needs clearing, but every call on one device
+ * shares it: calls whose device work overlaps in time on one device (other
+ * streams, other threads) race and must be serialised by the caller.
+ * Errors: as rbq_quant_attn_decode, and RBQ_ESCRATCH when the call needs
+ * more than RBQ_SCRATCH_BYTES of split records
+ * (rbq_quant_attn_workspace_bytes tells; nothing is launched then).
+ */
+int rbq_quant_attn_decode_noalloc(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L,
+                                  float scale, int32_t causal, const float* rot_blocks,
+                                  float* out, int32_t splits, void* stream);
 
 /* ---- attention mask element types (rbq_quant_attn_decode_mask) ---- */
 #define RBQ_MASK_NONE      0

@@ -27,6 +27,9 @@ RBQ_ECAPACITY = -3
 RBQ_ERANGE = -4
 RBQ_EWORKSPACE = -5
 RBQ_EHIP = -6
+RBQ_ESCRATCH = -7
+
+RBQ_SCRATCH_BYTES = 8 << 20  # fixed scratch array of rbq_quant_attn_decode_noalloc, per device
 
 RBQ_F16 = 1
 RBQ_BF16 = 2
@@ -90,6 +93,9 @@ def _load():
         "rbq_quant_attn_decode": (c_int32, [P, c_void_p, c_int32, c_int32, c_float, c_int32,
                                             c_void_p, c_void_p, c_int32, c_void_p, c_size_t,
                                             c_void_p]),
+        "rbq_quant_attn_decode_noalloc": (c_int32, [P, c_void_p, c_int32, c_int32, c_float,
+                                                    c_int32, c_void_p, c_void_p, c_int32,
+                                                    c_void_p]),
         "rbq_kv_append_attn_decode": (c_int32, [P, c_void_p, c_void_p, c_int64, c_void_p, c_int32,
                                                 c_int32, c_float, c_int32, c_void_p, c_void_p,
                                                 c_int32, c_void_p, c_size_t, c_void_p]),
@@ -286,6 +292,25 @@ def rbq_quant_attn_decode(desc: rbq_kv_cache, q: torch.Tensor, scale: float, cau
            _lib.rbq_quant_attn_decode_mask(ctypes.byref(desc), qp, q.shape[1], q.shape[2],
                                            float(scale), 1 if causal else 0, mp, mt, sb, sh, sl,
                                            rp, op, int(splits), wp, wn, _stream()))
+
+
+def rbq_quant_attn_decode_noalloc(desc: rbq_kv_cache, q: torch.Tensor, scale: float,
+                                  causal: bool, rot_blocks, out: torch.Tensor,
+                                  splits: int = 0) -> None:
+    """rbq_quant_attn_decode with the split records in the library's fixed
+    device scratch array (no workspace argument; the call allocates nothing).
+    Calls that overlap on one device share that array and must not overlap."""
+    if q.dim() != 4 or q.shape[0] != desc.B or q.shape[3] != desc.head_dim:
+        raise ValueError(f"q shape {tuple(q.shape)} does not match the cache")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    qp = _dev_ptr(q, _TORCH_OF[desc.dtype], "q")
+    op = _dev_ptr(out, torch.float32, "out")
+    rp = None if rot_blocks is None else _dev_ptr(rot_blocks, torch.float32, "rot_blocks")
+    _check("rbq_quant_attn_decode_noalloc",
+           _lib.rbq_quant_attn_decode_noalloc(ctypes.byref(desc), qp, q.shape[1], q.shape[2],
+                                              float(scale), 1 if causal else 0, rp, op,
+                                              int(splits), _stream()))
 
 
 def rbq_kv_append_attn_decode(desc: rbq_kv_cache, k: torch.Tensor, v: torch.Tensor,

@@ -50,6 +50,9 @@
 // fp32 accumulators (the probability-weighted sums of values) stay finite.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "rbq_common.h"
 #include "rbq_quantize.h"
 
@@ -1467,6 +1470,76 @@ int check_mask(const rbq_kv_cache* c, int32_t H_q, int32_t L, const void* mask, 
     return RBQ_OK;
 }
 
+// ---- the fixed scratch array of rbq_quant_attn_decode_noalloc ----
+// The split records of that entry point live here instead of in a caller's
+// workspace: RBQ_SCRATCH_BYTES per device, allocated with the code object and
+// held until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is a stand-in, not a device address): the device
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current and kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[RBQ_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array.
+int scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        set_hip_error((int)e);
+        return RBQ_EHIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return RBQ_EUNSUPPORTED;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || p == nullptr) {
+                set_hip_error((int)e);
+                return RBQ_EHIP;
+            }
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return RBQ_OK;
+}
+
+// Checks, plan and launch of one attention call with the split records in
+// `ws` (ws_fixed: the scratch array, whose size is RBQ_SCRATCH_BYTES).
+int attn_call(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, float scale,
+              int32_t causal, const void* mask, int32_t mask_type, int64_t msb, int64_t msh,
+              int64_t msl, const float* rot_blocks, float* out, int32_t splits, void* ws,
+              size_t ws_bytes, bool ws_fixed, void* stream) {
+    int st = check_attn(c, H_q, L, splits);
+    if (st != RBQ_OK) return st;
+    if (q == nullptr || out == nullptr) return RBQ_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(q) & 7) != 0 || (reinterpret_cast<uintptr_t>(out) & 15) != 0 ||
+        (reinterpret_cast<uintptr_t>(rot_blocks) & 15) != 0 || (reinterpret_cast<uintptr_t>(ws) & 15) != 0)
+        return RBQ_EINVAL;
+    AttnMask mk;
+    st = check_mask(c, H_q, L, mask, mask_type, msb, msh, msl, &mk);
+    if (st != RBQ_OK) return st;
+    AttnPlan ap;
+    st = attn_plan(c, H_q, L, splits, &ap);
+    if (st != RBQ_OK) return st;
+    if (ws_fixed) {
+        if (ap.ws_bytes > RBQ_SCRATCH_BYTES) return RBQ_ESCRATCH;
+        if (ap.ws_bytes > 0) {
+            st = scratch_address(&ws);
+            if (st != RBQ_OK) return st;
+        }
+    } else if (ap.ws_bytes > 0 && (ws == nullptr || ws_bytes < ap.ws_bytes)) {
+        return RBQ_EWORKSPACE;
+    }
+    if (ap.tile) return tile_launch(c, q, H_q, L, scale, causal, mk, rot_blocks, out, ap.tp, ws, stream);
+    return mfma_launch(c, q, H_q, L, scale, causal, mk, rot_blocks, out, ap.mp, ws, stream);
+}
+
 }  // namespace
 
 }  // namespace rbq
@@ -1494,21 +1567,16 @@ extern "C" int rbq_quant_attn_decode_mask(const rbq_kv_cache* c, const void* q, 
                                           int64_t mask_stride_h, int64_t mask_stride_l,
                                           const float* rot_blocks, float* out, int32_t splits,
                                           void* ws, size_t ws_bytes, void* stream) {
-    int st = check_attn(c, H_q, L, splits);
-    if (st != RBQ_OK) return st;
-    if (q == nullptr || out == nullptr) return RBQ_EINVAL;
-    if ((reinterpret_cast<uintptr_t>(q) & 7) != 0 || (reinterpret_cast<uintptr_t>(out) & 15) != 0 ||
-        (reinterpret_cast<uintptr_t>(rot_blocks) & 15) != 0 || (reinterpret_cast<uintptr_t>(ws) & 15) != 0)
-        return RBQ_EINVAL;
-    AttnMask mk;
-    st = check_mask(c, H_q, L, mask, mask_type, mask_stride_b, mask_stride_h, mask_stride_l, &mk);
-    if (st != RBQ_OK) return st;
-    AttnPlan ap;
-    st = attn_plan(c, H_q, L, splits, &ap);
-    if (st != RBQ_OK) return st;
-    if (ap.ws_bytes > 0 && (ws == nullptr || ws_bytes < ap.ws_bytes)) return RBQ_EWORKSPACE;
-    if (ap.tile) return tile_launch(c, q, H_q, L, scale, causal, mk, rot_blocks, out, ap.tp, ws, stream);
-    return mfma_launch(c, q, H_q, L, scale, causal, mk, rot_blocks, out, ap.mp, ws, stream);
+    return attn_call(c, q, H_q, L, scale, causal, mask, mask_type, mask_stride_b, mask_stride_h,
+                     mask_stride_l, rot_blocks, out, splits, ws, ws_bytes, false, stream);
+}
+
+extern "C" int rbq_quant_attn_decode_noalloc(const rbq_kv_cache* c, const void* q, int32_t H_q,
+                                             int32_t L, float scale, int32_t causal,
+                                             const float* rot_blocks, float* out, int32_t splits,
+                                             void* stream) {
+    return attn_call(c, q, H_q, L, scale, causal, nullptr, RBQ_MASK_NONE, 0, 0, 0, rot_blocks, out,
+                     splits, nullptr, 0, true, stream);
 }
 
 extern "C" int rbq_kv_append_attn_decode(rbq_kv_cache* c, const void* k, const void* v,

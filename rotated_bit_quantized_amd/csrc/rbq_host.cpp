@@ -186,6 +186,7 @@ const char* rbq_status_string(int status) {
         case RBQ_ERANGE: return "query block length out of range (need 1 <= L <= offset)";
         case RBQ_EWORKSPACE: return "workspace missing or too small";
         case RBQ_EHIP: return "HIP runtime error";
+        case RBQ_ESCRATCH: return "the call needs more than the fixed scratch array holds";
         default: return "unknown status";
     }
 }
