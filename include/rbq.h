@@ -27,7 +27,10 @@
  *     group_size 32, 64 or 128, dividing head_dim (the cache constructor's
  *     group_size); k_bits and v_bits each one of 2, 3, 4, 5, 6, 8 (the width
  *     list of _packed_words); dtype fp16 or bf16.  Anything else returns
- *     RBQ_EUNSUPPORTED.  The default configuration (head_dim 256, group 64,
+ *     RBQ_EUNSUPPORTED, as do descriptors beyond these size limits (far
+ *     beyond any device memory; they keep every size computation inside 64
+ *     bits): capacity <= 2^40 rows, B * H_kv < 2^31 slabs, and
+ *     B * H_kv * capacity <= 2^44 rows.  The default configuration (head_dim 256, group 64,
  *     K 4-bit, V 3-bit) has dedicated append and attention kernels; the
  *     others run general kernels with the same results definition.
  */
@@ -152,7 +155,8 @@ int rbq_rotation_round(float* blocks, int32_t head_dim, int32_t dtype);
  * ceil(n/256)*256 rows are added to the buffer, which is first cut back to
  * `offset` rows when offset % 256 != 0.  capacity == 0 means no buffer yet.
  * Returns the capacity, or RBQ_EINVAL when n < 0, offset < 0 or
- * offset > capacity.  Host only.
+ * offset > capacity, RBQ_EUNSUPPORTED when capacity, n or the result exceed
+ * 2^40 rows.  Host only.
  */
 int64_t rbq_kv_required_capacity(int64_t capacity, int64_t offset, int64_t n);
 

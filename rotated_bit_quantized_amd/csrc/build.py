@@ -17,6 +17,10 @@ ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librbq.so")
+# the streaming-read probe (a measurement helper, not the method) is a library
+# of its own
+PROBE_SOURCE = "rbq_probe.hip"
+PROBE_LIB = os.path.join(PKG, "librbq_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -68,6 +72,11 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     shutil.move(tmp, LIB)
+    pobj = os.path.join(OUT_DIR, PROBE_SOURCE + ".o")
+    _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(HERE, PROBE_SOURCE), "-o", pobj], verbose)
+    ptmp = PROBE_LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", ptmp, pobj], verbose)
+    shutil.move(ptmp, PROBE_LIB)
     return LIB
 
 

@@ -253,8 +253,8 @@ extern "C" int rbq_kv_quant_append(rbq_kv_cache* c, const void* k, const void* v
     if (n < 0) return RBQ_EINVAL;
     if (n == 0) return RBQ_OK;
     if (k == nullptr || v == nullptr) return RBQ_EINVAL;
-    if (c->offset + n > c->capacity) return RBQ_ECAPACITY;
-    const int64_t rows = (int64_t)c->B * c->H_kv * n;
+    if (n > c->capacity - c->offset) return RBQ_ECAPACITY;
+    const int64_t rows = (int64_t)c->B * c->H_kv * n;  // <= kMaxTotalRows (check_cache)
     const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
     if (blocks > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;

@@ -305,6 +305,14 @@ __device__ __forceinline__ int k_slot(int k, int c) { return 8 * k + (c ^ ((k >>
 // three points of an iteration rather than all at once: while the memory
 // system is saturated an issuing wave stalls until its requests are taken,
 // and spread out those stalls overlap more of the other waves' arithmetic.
+// Cache policy of the tile transfers: non-temporal (each cache byte is read
+// once per call; the hint keeps the stream from displacing other lines and
+// raises the read rate of a plain scan on this GPU by about 7 %).
+#ifndef RBQ_TILE_CPOL
+#define RBQ_TILE_CPOL 2
+#endif
+constexpr int kTileCPol = RBQ_TILE_CPOL;
+
 template <int PART>
 __device__ __forceinline__ void dma_tile_part(lds_u8* buf, int t0, int lane, __amdgpu_buffer_rsrc_t kw_r,
                                               __amdgpu_buffer_rsrc_t ks_r, __amdgpu_buffer_rsrc_t kb_r,
@@ -317,18 +325,18 @@ __device__ __forceinline__ void dma_tile_part(lds_u8* buf, int t0, int lane, __a
             const int k = p >> 3;
             const int c = (p & 7) ^ ((k >> 1) & 7);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(kw_r, buf + kBufK + 1024 * m, 16,
-                                                      (t0 + k) * 128 + 16 * c, 0, 0, 0);
+                                                      (t0 + k) * 128 + 16 * c, 0, 0, kTileCPol);
         }
     } else if constexpr (PART == 1) {
 #pragma unroll
         for (int m = 0; m < 3; ++m)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vw_r, buf + kBufV + 1024 * m, 16,
-                                                      t0 * 96 + 16 * (64 * m + lane), 0, 0, 0);
+                                                      t0 * 96 + 16 * (64 * m + lane), 0, 0, kTileCPol);
     } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ks_r, buf + kBufKs, 4, t0 * 8 + 4 * lane, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kb_r, buf + kBufKb, 4, t0 * 8 + 4 * lane, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vs_r, buf + kBufVs, 4, t0 * 8 + 4 * lane, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vb_r, buf + kBufVb, 4, t0 * 8 + 4 * lane, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ks_r, buf + kBufKs, 4, t0 * 8 + 4 * lane, 0, 0, kTileCPol);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kb_r, buf + kBufKb, 4, t0 * 8 + 4 * lane, 0, 0, kTileCPol);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vs_r, buf + kBufVs, 4, t0 * 8 + 4 * lane, 0, 0, kTileCPol);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vb_r, buf + kBufVb, 4, t0 * 8 + 4 * lane, 0, 0, kTileCPol);
     }
 }
 
@@ -1298,7 +1306,7 @@ int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Mfm
     const int64_t unit = (splits == 0) ? (int64_t)kWaves * kTile : (int64_t)kTile;
     chunk = (chunk + unit - 1) / unit * unit;
     S = (T + chunk - 1) / chunk;
-    if (units * S > 0x7FFFFFFF || RB > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
+    if (units > 0x7FFFFFFF || units * S > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
     // 32-bit buffer offsets, also for the tile reads past T (at most 4 tiles)
     if ((T + kWaves * kTile) * (int64_t)(kKWords * 4) > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
     p->S = (int)S;
@@ -1456,12 +1464,13 @@ int check_mask(const rbq_kv_cache* c, int32_t H_q, int32_t L, const void* mask, 
     if (type != RBQ_MASK_BOOL && type != RBQ_MASK_ADD_F32 && type != RBQ_MASK_ADD_DTYPE)
         return RBQ_EINVAL;
     if (sb < 0 || sh < 0 || sl < 0) return RBQ_EINVAL;
-    const int64_t esize = (type == RBQ_MASK_BOOL) ? 1 : (type == RBQ_MASK_ADD_F32) ? 4 : 2;
-    const int64_t last = (int64_t)(c->B - 1) * sb + (int64_t)(H_q - 1) * sh + (int64_t)(L - 1) * sl +
-                         c->offset;
-    if (sb > (int64_t)1 << 40 || sh > (int64_t)1 << 40 || sl > (int64_t)1 << 40 ||
-        last * esize > 0x7FFFFFFF - 64 * 4)
+    if (sb > (int64_t)1 << 40 || sh > (int64_t)1 << 40 || sl > (int64_t)1 << 40)
         return RBQ_EUNSUPPORTED;
+    const int64_t esize = (type == RBQ_MASK_BOOL) ? 1 : (type == RBQ_MASK_ADD_F32) ? 4 : 2;
+    // each term below 2^31 * 2^40: the sum in 128 bits
+    const __int128 last = (__int128)(c->B - 1) * sb + (__int128)(H_q - 1) * sh +
+                          (__int128)(L - 1) * sl + c->offset;
+    if (last * esize > 0x7FFFFFFF - 64 * 4) return RBQ_EUNSUPPORTED;
     m->type = type;
     m->sb = sb;
     m->sh = sh;

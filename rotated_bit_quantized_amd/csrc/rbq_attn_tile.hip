@@ -52,6 +52,7 @@ typedef uint32_t tu32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t tu32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int tTile = 32;                  // keys per tile
+constexpr int tCPolNT = 2;                 // tile transfers: non-temporal (read once per call)
 constexpr int tPS = tTile + 4;             // floats per row of a wave's P staging
 constexpr float tLog2e = 1.44269504088896340736f;
 
@@ -229,14 +230,14 @@ __device__ __forceinline__ void issue_tile(const TArgs& a, const TRsrc& rs, int 
 #pragma unroll
             for (int m = 0; m < kMax16; ++m)
                 if (m % W == wave && 64 * m < nch && (64 * m + 64 <= nch || lane < nch - 64 * m))
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + 1024 * m, 16, voff, 1024 * m, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + 1024 * m, 16, voff, 1024 * m, 0, tCPolNT);
         } else {
             const int nch = 32 * words;  // 4-byte chunks
             const uint32_t voff = base + 4u * lane;
 #pragma unroll
             for (int m = 0; m < kMax4; ++m)
                 if (m % W == wave && 64 * m < nch && (64 * m + 64 <= nch || lane < nch - 64 * m))
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + 256 * m, 4, voff, 256 * m, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + 256 * m, 4, voff, 256 * m, 0, tCPolNT);
         }
     }
     // the four scale / bias arrays: 32 keys x NG halves each = 16 NG words
@@ -250,7 +251,7 @@ __device__ __forceinline__ void issue_tile(const TArgs& a, const TRsrc& rs, int 
             for (int h = 0; h < (16 * NG + 63) / 64; ++h)
                 if ((4 * k + h) % W == wave && 64 * h + lane < 16 * NG)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.m[k], rawb + a.raw_meta + k * R::meta_bytes + 256 * h,
-                                                              4, moff, 256 * h, 0, 0);
+                                                              4, moff, 256 * h, 0, tCPolNT);
     }
 }
 
@@ -1012,7 +1013,8 @@ int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Til
     int64_t chunk = (T + S - 1) / S;
     chunk = (chunk + tTile - 1) / tTile * tTile;
     S = (T + chunk - 1) / chunk;
-    if (units * S > 0x7FFFFFFF || units * RW > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
+    if (units > 0x7FFFFFFF || units * S > 0x7FFFFFFF || units * RW > 0x7FFFFFFF)
+        return RBQ_EUNSUPPORTED;
     // 32-bit buffer offsets of the tile transfers, up to one tile past T
     const int64_t bits = c->k_bits > c->v_bits ? c->k_bits : c->v_bits;
     if ((T + tTile) * (int64_t)c->head_dim * bits / 8 > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;

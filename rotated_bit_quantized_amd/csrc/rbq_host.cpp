@@ -28,6 +28,9 @@ int check_cache(const rbq_kv_cache* c) {
     if (c->head_dim % c->group_size != 0) return RBQ_EUNSUPPORTED;
     if (!width_ok(c->k_bits) || !width_ok(c->v_bits)) return RBQ_EUNSUPPORTED;
     if (c->dtype != RBQ_F16 && c->dtype != RBQ_BF16) return RBQ_EUNSUPPORTED;
+    const int64_t slabs = (int64_t)c->B * c->H_kv;
+    if (c->capacity > kMaxRows || slabs > kMaxSlabs || c->capacity > kMaxTotalRows / slabs)
+        return RBQ_EUNSUPPORTED;
     if (c->capacity > 0 &&
         (c->k_words == nullptr || c->k_scales == nullptr || c->k_biases == nullptr ||
          c->v_words == nullptr || c->v_scales == nullptr || c->v_biases == nullptr))
@@ -156,10 +159,12 @@ int rbq_rotation_build_mode(const float* draws, int32_t head_dim, int32_t mode, 
 
 int64_t rbq_kv_required_capacity(int64_t capacity, int64_t offset, int64_t n) {
     if (n < 0 || offset < 0 || capacity < 0 || offset > capacity) return RBQ_EINVAL;
+    if (capacity > kMaxRows || n > kMaxRows) return RBQ_EUNSUPPORTED;
     if (capacity > 0 && offset + n <= capacity) return capacity;
     const int64_t new_steps = (n + kStep - 1) / kStep * kStep;
     if (capacity == 0) return new_steps;
     const int64_t kept = (offset % kStep != 0) ? offset : capacity;
+    if (kept + new_steps > kMaxRows) return RBQ_EUNSUPPORTED;
     return kept + new_steps;
 }
 

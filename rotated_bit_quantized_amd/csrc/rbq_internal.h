@@ -17,6 +17,15 @@ constexpr int kKWords = kHeadDim * kKBits / 32;   // 32
 constexpr int kVWords = kHeadDim * kVBits / 32;   // 24
 constexpr int kGroups = kHeadDim / kGroup;        // 4
 
+// Size limits of a descriptor (RBQ_EUNSUPPORTED beyond them): rows per
+// (b, kv head), (b, kv head) slabs, and rows of all slabs together.  Far
+// beyond any device memory, they keep every size and offset computation of
+// the host code and the kernels inside int64 (and the grids inside their
+// 32-bit counts, which the launch planning checks on its own).
+constexpr int64_t kMaxRows = (int64_t)1 << 40;
+constexpr int64_t kMaxSlabs = ((int64_t)1 << 31) - 1;
+constexpr int64_t kMaxTotalRows = (int64_t)1 << 44;
+
 // Records the hipError_t of the last failed HIP call on this thread.
 void set_hip_error(int err);
 
