@@ -50,6 +50,7 @@
 // fp32 accumulators (the probability-weighted sums of values) stay finite.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -75,7 +76,8 @@ constexpr int kRows = 8;                                   // query rows per kv 
 // split record in the workspace: (m, l) per row, then o column-major
 // [256 columns][8 rows]
 constexpr int kRecFloats = 2 * kRows + kRows * kHeadDim;
-constexpr int kMergeNarrowUnits = 64;  // below this many units the merge takes 32-column blocks
+constexpr int kMergeNarrowUnits = 64;
+constexpr int64_t kGridYZ = 65535;  // workgroups per grid dimension y or z of one launch  // below this many units the merge takes 32-column blocks
 // wave record in LDS, in its own region so that a wave stores it as soon as
 // its tiles are done: o column-major [256 columns][2 row quads][4 rows], the
 // row quad of column c stored at slot quad ^ ((c >> 3) & 1) (conflict-free
@@ -114,6 +116,8 @@ static_assert(kThreads * 2 == kHeadDim * 4, "8 bytes of the rotation blocks per 
 static_assert(kThreads == 2 * kHeadDim && kRows == 8, "merge: one column and 4 rows per thread");
 
 struct MArgs {
+    // the fields the prologue needs come first, so that they arrive in one
+    // batch of scalar loads
     const uint16_t* q;
     const uint32_t* kw;
     const uint16_t* ks;
@@ -122,25 +126,26 @@ struct MArgs {
     const uint16_t* vs;
     const uint16_t* vb;
     const float* rot;
-    float* out;
-    float* rec;
-    int64_t capacity;
-    int T, chunk;
-    int Hkv, n_rep, L, G, S, causal;
-    int RB;        // blocks of 8 query rows per kv head
-    float qscale;  // scale * log2(e)
-    // optional mask over (query row, key): element [b][q head][row i][key t]
-    // at mask + b*msb + h*msh + i*msl + t (elements; the key stride is 1)
-    const void* mask;
-    int64_t msb, msh, msl;
-    uint32_t mask_bytes;  // extent read through a range-checked buffer resource
-    int round_rot;        // RBQ_FLAG_ROUND_ROTATED: the rotated query rounded to the dtype
     // fused append (no mask, one block of rows per kv head): rows
     // [T - n_new, T) of the cache are quantized from kn / vn
     // ([B][H_kv][n_new][256], unrotated) and written by this launch
     const uint16_t* kn;
     const uint16_t* vn;
+    int64_t capacity;
+    int T, chunk;
+    int Hkv, n_rep, L, G, S, causal;
+    int RB;        // blocks of 8 query rows per kv head
+    int rb0, bh0;  // first row block and (b, kv head) of this launch (grid y and z)
     int n_new;
+    int round_rot; // RBQ_FLAG_ROUND_ROTATED: the rotated query rounded to the dtype
+    float qscale;  // scale * log2(e)
+    float* out;
+    float* rec;
+    // optional mask over (query row, key): element [b][q head][row i][key t]
+    // at mask + b*msb + h*msh + i*msl + t (elements; the key stride is 1)
+    const void* mask;
+    int64_t msb, msh, msl;
+    uint32_t mask_bytes;  // extent read through a range-checked buffer resource
 };
 
 // Mask element types (the template argument MK of the attention kernel).
@@ -212,9 +217,8 @@ __device__ __forceinline__ float4 rot_row(const float* rot, int col) {
 // row < G.  The 4 columns of a rotation block lie in one lane quad (lane & 3
 // = col & 3): z = sum_k y[block column k] * B[col & 3][k], in fp64, with
 // v = B[col & 3] from rot_row.
-__device__ __forceinline__ void store_out(float* out, bool rotated, float4 v, int b, int Hkv,
-                                          int n_rep, int L, int G, int kvh, int col, int row,
-                                          float acc, float Ls) {
+__device__ __forceinline__ void store_out(float* out, bool rotated, float4 v, int bh, int G,
+                                          int col, int row, float acc, float Ls) {
     const float y = acc * (1.0f / Ls);
     float z = y;
     if (rotated) {
@@ -225,10 +229,9 @@ __device__ __forceinline__ void store_out(float* out, bool rotated, float4 v, in
         s2 = s2 + (double)y3 * (double)v.w;
         z = (float)s2;
     }
-    if (row < G) {
-        const int hq = kvh * n_rep + row / L;
-        out[(((int64_t)b * Hkv * n_rep + hq) * L + row % L) * kHeadDim + col] = z;
-    }
+    // the G rows of kv head bh are its n_rep q heads' L rows in (head, row)
+    // order, i.e. rows bh * G + row of [B][H_q][L][D]
+    if (row < G) out[((int64_t)bh * G + row) * kHeadDim + col] = z;
 }
 
 // Workgroup barrier that orders LDS accesses only: the waves exchange data
@@ -312,6 +315,10 @@ __device__ __forceinline__ int k_slot(int k, int c) { return 8 * k + (c ^ ((k >>
 #define RBQ_TILE_CPOL 2
 #endif
 constexpr int kTileCPol = RBQ_TILE_CPOL;
+#ifndef RBQ_DMA_AT_TOP
+#define RBQ_DMA_AT_TOP 0
+#endif
+constexpr bool kDmaAtTop = RBQ_DMA_AT_TOP != 0;
 
 template <int PART>
 __device__ __forceinline__ void dma_tile_part(lds_u8* buf, int t0, int lane, __amdgpu_buffer_rsrc_t kw_r,
@@ -421,6 +428,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __shared__ __align__(16) unsigned char smem[kSmemBytes];
     __shared__ __align__(16) unsigned char tbuf[kTbufBytes];
 
+    // Every argument the prologue uses, loaded in one batch of scalar loads:
+    // left to itself the compiler loads each field where it is first used,
+    // one round trip of the scalar memory path each, and the first tile
+    // transfer waited behind three of them.
+    asm volatile("" ::"s"(a.q), "s"(a.kw), "s"(a.ks), "s"(a.kb), "s"(a.vw), "s"(a.vs), "s"(a.vb),
+                 "s"(a.rot), "s"(a.capacity), "s"(a.T), "s"(a.chunk), "s"(a.Hkv), "s"(a.n_rep),
+                 "s"(a.L), "s"(a.G), "s"(a.S), "s"(a.RB), "s"(a.kn), "s"(a.vn), "s"(a.n_new),
+                 "s"(a.causal), "s"(a.round_rot), "s"(a.rb0), "s"(a.bh0));
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -430,29 +445,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const bool lo_part = n >= 8;
     const int rb = 4 * (j & 1);         // accumulator rows of this lane: rb .. rb+3
 
-    const int bhr = blockIdx.x / a.S;           // (b, kv head, block of 8 rows)
-    const int split = blockIdx.x - bhr * a.S;
-    const int bh = bhr / a.RB;
-    const int r0 = 8 * (bhr - bh * a.RB);       // first query row of the block
-    const int b = bh / a.Hkv;
-    const int kvh = bh - b * a.Hkv;
+    // grid: x = key split, y = block of 8 query rows, z = (b, kv head)
+    const int split = blockIdx.x;
+    const int rblk = a.rb0 + blockIdx.y;
+    const int bh = a.bh0 + blockIdx.z;
+    const int bhr = bh * a.RB + rblk;           // (b, kv head, block of 8 rows)
+    const int r0 = 8 * rblk;                    // first query row of the block
     const int T = a.T;
     const int t_begin = split * a.chunk;
     const int t_end = (t_begin + a.chunk < T) ? t_begin + a.chunk : T;
 
-    // ---- loads first: query row `wave`, 4-element block `lane`, and 8 bytes
-    //      of the rotation blocks (the workgroup reads them once, not once
-    //      per wave: every workgroup reads the same 4 KB); then the wave's
-    //      first tile.  Their latency overlaps the table build, and waiting
-    //      for the query does not wait for the tile. ----
+    // ---- loads first: query row `wave` (row bh * G + R of q: the G rows of
+    //      a kv head are its q heads' L rows), 4-element block `lane`, and 8
+    //      bytes of the rotation blocks (the workgroup reads them once, not
+    //      once per wave: every workgroup reads the same 4 KB); then, with as
+    //      little scalar work as possible in between, the wave's first tile.
+    //      Their latency overlaps the table build, and waiting for the query
+    //      does not wait for the tile. ----
     uint2 qraw = make_uint2(0u, 0u);
-    if (r0 + wave < a.G) {
-        const int R = r0 + wave;
-        const int h = kvh * a.n_rep + R / a.L;
-        const uint16_t* qrow =
-            a.q + (((int64_t)b * a.Hkv * a.n_rep + h) * a.L + R % a.L) * kHeadDim;
-        qraw = *reinterpret_cast<const uint2*>(qrow + 4 * lane);
-    }
+    if (r0 + wave < a.G)
+        qraw = *reinterpret_cast<const uint2*>(
+            a.q + ((int64_t)bh * a.G + r0 + wave) * kHeadDim + 4 * lane);
     const bool rotated = a.rot != nullptr;
     float2 rot2 = make_float2(0.f, 0.f);
     if (rotated) rot2 = reinterpret_cast<const float2*>(a.rot)[tid];
@@ -470,31 +483,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // row app_lo + w by wave w, before any transfer of the workgroup reads
     // them (no other workgroup reads them: one block of rows per kv head)
     int app_lo = t_end, n_app = 0;
-    uint2 kraw = make_uint2(0u, 0u), vraw = make_uint2(0u, 0u);
     if constexpr (MK == kMaskNone) {
         if (a.n_new > 0) {
             app_lo = max(T - a.n_new, t_begin);
             n_app = max(t_end - app_lo, 0);
-            if (wave < n_app) {
-                const int64_t src =
-                    ((int64_t)bh * a.n_new + (app_lo + wave - (T - a.n_new))) * kHeadDim + 4 * lane;
-                kraw = *reinterpret_cast<const uint2*>(a.kn + src);
-                vraw = *reinterpret_cast<const uint2*>(a.vn + src);
-            }
         }
     }
-    // this wave's tile buffer, filled with its first tile unconditionally (a
-    // wave without tiles reads keys of the next split or, past T, zeros from
-    // the buffer range check, and never uses them); a first tile that holds
-    // an appended row is transferred after the set-up, once the row is
-    // written, and the transfer issued here then reads past T (zeros, no
-    // memory access): the same instructions on every path, so that the
-    // compiler's waits for the query loads leave the tile in flight
     lds_u8* wbuf = (lds_u8*)tbuf + wave * kWaveAreaBytes;
     const unsigned char* wbuf_g = tbuf + wave * kWaveAreaBytes;
     const int t_first = t_begin + it_first * kTile;
     const bool defer_first = n_app > 0 && t_first < app_lo + n_app && t_first + kTile > app_lo;
     dma_tile(wbuf, defer_first ? T : t_first, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
+    // the appended row of this wave, unrotated
+    uint2 kraw = make_uint2(0u, 0u), vraw = make_uint2(0u, 0u);
+    if constexpr (MK == kMaskNone) {
+        if (wave < n_app) {
+            const int64_t src =
+                ((int64_t)bh * a.n_new + (app_lo + wave - (T - a.n_new))) * kHeadDim + 4 * lane;
+            kraw = *reinterpret_cast<const uint2*>(a.kn + src);
+            vraw = *reinterpret_cast<const uint2*>(a.vn + src);
+        }
+    }
 
     // ---- decode table: entry e = 4 fp16 codes (e >> 3k) & 7 ----
     for (int e = tid; e < 4096; e += kThreads) {
@@ -741,7 +750,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             const int R = r0 + rb + 2 * p + hl;
             mrow[p] = 0x80000000u;
             if (R < a.G) {
-                const int h = kvh * a.n_rep + R / a.L;
+                const int b = bh / a.Hkv;
+                const int h = (bh - b * a.Hkv) * a.n_rep + R / a.L;
                 mrow[p] = (uint32_t)(((int64_t)b * a.msb + (int64_t)h * a.msh +
                                       (int64_t)(R % a.L) * a.msl) * kMaskElem);
             }
@@ -779,8 +789,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         read_tile(cur, wbuf_g, n, j);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         const bool more = it_next < n_tiles;  // the wave's next tile, in three parts
-        if (more)
+        if (more) {
             dma_tile_part<0>(wbuf, t_next, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
+            if constexpr (kDmaAtTop) {
+                dma_tile_part<1>(wbuf, t_next, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
+                dma_tile_part<2>(wbuf, t_next, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
+            }
+        }
         uint32_t mk_next[2][2] = {{0u, 0u}, {0u, 0u}};
         if constexpr (MK != kMaskNone)
             if (more) load_mask(t_next, mk_next);
@@ -921,7 +936,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 }
         }
 
-        if (more)
+        if (!kDmaAtTop && more)
             dma_tile_part<1>(wbuf, t_next, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
         // ---- online softmax per row (base 2), lazy rescale: the reference
         //      moves only when the tile maximum exceeds it by more than 2^8 ----
@@ -977,7 +992,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             lds_st32(smem, p_wr + 512 * blk, hi2);
             lds_st32(smem, p_wr + 512 * blk + 16, f16_residuals(hi2, p0, p1, one));
         }
-        if (more)
+        if (!kDmaAtTop && more)
             dma_tile_part<2>(wbuf, t_next, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
         // A operand of P.V: row n (hi rows 0-7, lo rows 8-15; within each
         // quad of rows the slot order rb + 0, 2, 1, 3) x keys 4j + e of both
@@ -1132,8 +1147,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     lv = 1.f;
                 }
             }
-            store_out(a.out, rotated, rv, b, a.Hkv, a.n_rep, a.L, a.G, kvh, col, r0 + 4 * h + i, av,
-                      lv);
+            store_out(a.out, rotated, rv, bh, a.G, col, r0 + 4 * h + i, av, lv);
         }
         return;
     }
@@ -1190,8 +1204,6 @@ __global__ __launch_bounds__(128 * NGR) void attn_mfma_merge_kernel(CArgs a) {
     const int r0 = 8 * (bhr - bh * a.RB);
     const int col = (blockIdx.x - bhr * kCB) * kCols + (tid % kCols);
     const int h = tid / kCols;  // rows RPT h .. RPT h + RPT - 1
-    const int b = bh / a.Hkv;
-    const int kvh = bh - b * a.Hkv;
     const float* base = a.rec + (int64_t)bhr * a.S * kRecFloats;
     const int wrow = tid >> 4, wmbr = tid & 15;
     const float4 rv = rot_row(a.rot, col);
@@ -1280,7 +1292,7 @@ __global__ __launch_bounds__(128 * NGR) void attn_mfma_merge_kernel(CArgs a) {
                                                   kGroups, kGroup);
             lv = 1.f;
         }
-        store_out(a.out, a.rot != nullptr, rv, b, a.Hkv, a.n_rep, a.L, a.G, kvh, col, R, av, lv);
+        store_out(a.out, a.rot != nullptr, rv, bh, a.G, col, R, av, lv);
     }
 }
 
@@ -1352,9 +1364,20 @@ int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
     a.mask_bytes = mk.bytes;
     a.round_rot = (c->flags & RBQ_FLAG_ROUND_ROTATED) ? 1 : 0;
     const int64_t units = (int64_t)c->B * c->H_kv * p.RB;
-    const dim3 grid((unsigned)(units * p.S)), block(kThreads);
-    auto launch = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, s, a); };
+    // grid x = key split, y = row block, z = (b, kv head); y and z in pieces
+    // of at most kGridYZ, launched one after another with their offsets
+    const int64_t BH = (int64_t)c->B * c->H_kv;
     const int mt = mk.ptr == nullptr ? kMaskNone : mk.type;
+    auto launch = [&](auto kernel) {
+        for (int64_t bh0 = 0; bh0 < BH; bh0 += kGridYZ)
+            for (int64_t rb0 = 0; rb0 < p.RB; rb0 += kGridYZ) {
+                a.bh0 = (int)bh0;
+                a.rb0 = (int)rb0;
+                const dim3 grid((unsigned)p.S, (unsigned)std::min<int64_t>(kGridYZ, p.RB - rb0),
+                                (unsigned)std::min<int64_t>(kGridYZ, BH - bh0));
+                hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s, a);
+            }
+    };
     if (c->dtype == RBQ_BF16) {
         if (mt == kMaskNone) launch(attn_mfma_kernel<RBQ_BF16, kMaskNone>);
         else if (mt == kMaskBool) launch(attn_mfma_kernel<RBQ_BF16, kMaskBool>);
