@@ -315,10 +315,6 @@ __device__ __forceinline__ int k_slot(int k, int c) { return 8 * k + (c ^ ((k >>
 #define RBQ_TILE_CPOL 2
 #endif
 constexpr int kTileCPol = RBQ_TILE_CPOL;
-#ifndef RBQ_DMA_AT_TOP
-#define RBQ_DMA_AT_TOP 0
-#endif
-constexpr bool kDmaAtTop = RBQ_DMA_AT_TOP != 0;
 
 template <int PART>
 __device__ __forceinline__ void dma_tile_part(lds_u8* buf, int t0, int lane, __amdgpu_buffer_rsrc_t kw_r,
@@ -789,13 +785,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         read_tile(cur, wbuf_g, n, j);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         const bool more = it_next < n_tiles;  // the wave's next tile, in three parts
-        if (more) {
+        if (more)
             dma_tile_part<0>(wbuf, t_next, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
-            if constexpr (kDmaAtTop) {
-                dma_tile_part<1>(wbuf, t_next, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
-                dma_tile_part<2>(wbuf, t_next, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
-            }
-        }
         uint32_t mk_next[2][2] = {{0u, 0u}, {0u, 0u}};
         if constexpr (MK != kMaskNone)
             if (more) load_mask(t_next, mk_next);
@@ -936,7 +927,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 }
         }
 
-        if (!kDmaAtTop && more)
+        if (more)
             dma_tile_part<1>(wbuf, t_next, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
         // ---- online softmax per row (base 2), lazy rescale: the reference
         //      moves only when the tile maximum exceeds it by more than 2^8 ----
@@ -992,7 +983,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             lds_st32(smem, p_wr + 512 * blk, hi2);
             lds_st32(smem, p_wr + 512 * blk + 16, f16_residuals(hi2, p0, p1, one));
         }
-        if (!kDmaAtTop && more)
+        if (more)
             dma_tile_part<2>(wbuf, t_next, lane, kw_r, ks_r, kb_r, vw_r, vs_r, vb_r);
         // A operand of P.V: row n (hi rows 0-7, lo rows 8-15; within each
         // quad of rows the slot order rb + 0, 2, 1, 3) x keys 4j + e of both
