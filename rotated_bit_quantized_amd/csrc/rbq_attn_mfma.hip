@@ -311,10 +311,7 @@ __device__ __forceinline__ int k_slot(int k, int c) { return 8 * k + (c ^ ((k >>
 // Cache policy of the tile transfers: non-temporal (each cache byte is read
 // once per call; the hint keeps the stream from displacing other lines and
 // raises the read rate of a plain scan on this GPU by about 7 %).
-#ifndef RBQ_TILE_CPOL
-#define RBQ_TILE_CPOL 2
-#endif
-constexpr int kTileCPol = RBQ_TILE_CPOL;
+constexpr int kTileCPol = 2;
 
 template <int PART>
 __device__ __forceinline__ void dma_tile_part(lds_u8* buf, int t0, int lane, __amdgpu_buffer_rsrc_t kw_r,
