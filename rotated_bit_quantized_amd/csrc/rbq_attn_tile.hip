@@ -980,7 +980,8 @@ static int tile_workgroups_per_cu(int D, int ng, int W, int kbits, int vbits) {
 #undef RBQ_FIT
 #define RBQ_FIT(D_, NG_) \
     if (D == D_ && ng == NG_) return tile_fit<D_, NG_, 4>(kbits, vbits);
-    RBQ_FIT(256, 2) RBQ_FIT(256, 4) RBQ_FIT(256, 8)
+    RBQ_FIT(256, 2) RBQ_FIT(256, 4)
+    if (D == 256 && ng == 8) return W == 4 ? tile_fit<256, 8, 4>(kbits, vbits) : tile_fit<256, 8, 1>(kbits, vbits);
 #undef RBQ_FIT
     return 1;
 }
@@ -988,11 +989,17 @@ static int tile_workgroups_per_cu(int D, int ng, int W, int kbits, int vbits) {
 int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, TilePlan* p) {
     const int64_t G = (int64_t)(H_q / c->H_kv) * L;
     // waves per workgroup, 16 rows each: one wave for up to 16 rows at
-    // head_dim <= 128; at head_dim 256 always four (the one-wave kernels fit
-    // only two workgroups per compute unit there, and one of their builds,
-    // 4 groups per row, gave wrong results that changed with the
-    // optimisation level: that shape is not used)
-    const int W = (G <= 16 && c->head_dim <= 128) ? 1 : 4;
+    // head_dim <= 128 and at head_dim 256 with 8 groups per row (1.4x faster
+    // there than four-wave blocks); four otherwise.  At head_dim 256 the
+    // one-wave builds hold more than 256 registers, so they run one wave per
+    // SIMD with part of their state in the accumulation registers: with 2
+    // groups per row that is slower than four-wave blocks, and the build for
+    // 4 groups per row gives wrong results (errors up to 0.5 that grow with
+    // the tiles a workgroup walks) that the 2- and 8-group builds of the same
+    // source do not show and that no difference in the source explains: that
+    // build is not used
+    const int ng = c->head_dim / c->group_size;
+    const int W = (G <= 16 && (c->head_dim <= 128 || ng == 8)) ? 1 : 4;
     const int64_t RW = 16 * W;
     const int64_t RBW = (G + RW - 1) / RW;
     const int64_t T = c->offset;
@@ -1002,7 +1009,6 @@ int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Til
         // one round of workgroups over the 256 compute units, as many per
         // unit as LDS and registers allow (longer splits lose less to set-up
         // and records than a second round gains)
-        const int ng = c->head_dim / c->group_size;
         const int per_cu = tile_workgroups_per_cu(c->head_dim, ng, W, c->k_bits, c->v_bits);
         S = (256 * per_cu + units - 1) / units;
         const int64_t max_s = (T + tTile - 1) / tTile;
@@ -1085,7 +1091,7 @@ int tile_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
         bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_, 4>) : launch(attn_tile_kernel<RBQ_F16, D_, NG_, 4>); \
     } else
     RBQ_TILE_CASE(64, 1) RBQ_TILE_CASE(64, 2) RBQ_TILE_CASE(128, 1) RBQ_TILE_CASE(128, 2)
-    RBQ_TILE_CASE(128, 4) RBQ_TILE_CASE4(256, 2) RBQ_TILE_CASE4(256, 4) RBQ_TILE_CASE4(256, 8) {
+    RBQ_TILE_CASE(128, 4) RBQ_TILE_CASE4(256, 2) RBQ_TILE_CASE4(256, 4) RBQ_TILE_CASE(256, 8) {
         return RBQ_EUNSUPPORTED;
     }
 #undef RBQ_TILE_CASE

@@ -261,13 +261,16 @@ def test_tile_kernel_single_key(var, dev):
     assert float(np.abs(out.cpu().numpy() - ref).max()) <= ATOL
 
 
-# single-wave tile workgroups (up to 16 rows per kv head at head_dim <= 128)
-# with one split, so that each workgroup walks many tiles (the running scale
-# powers and the staging transfers are carried across all of them): 4 groups
-# per row (two scale / bias items per thread) and 2 groups per row
+# single-wave tile workgroups (up to 16 rows per kv head at head_dim <= 128,
+# and at head_dim 256 with 8 groups per row) with one split, so that each
+# workgroup walks many tiles (the running scale powers and the staging
+# transfers are carried across all of them): 4 groups per row (two scale /
+# bias items per thread), 2 and 8
 @pytest.mark.parametrize("var", [(128, 32, 4, 4, "bf16", False, False),
                                  (128, 32, 3, 5, "f16", True, False),
-                                 (128, 64, 4, 4, "bf16", True, False)], ids=_vid)
+                                 (128, 64, 4, 4, "bf16", True, False),
+                                 (256, 32, 4, 4, "bf16", False, False),
+                                 (256, 32, 6, 2, "f16", True, False)], ids=_vid)
 @pytest.mark.parametrize("splits", [1, 2])
 def test_single_wave_tile_kernel_many_tiles(var, splits, dev):
     print(f"[single-wave tiles] {_vid(var)} splits={splits}", flush=True)
