@@ -1294,16 +1294,28 @@ int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Mfm
     const int64_t T = c->offset;
     const int64_t units = (int64_t)c->B * c->H_kv * RB;
     int64_t S = splits;
+    bool xcd_shared = false;
     if (S == 0) {
         S = (256 + units - 1) / units;  // about one workgroup per compute unit
         const int64_t max_s = (T + kWaves * kTile - 1) / (kWaves * kTile);
         if (S > max_s) S = max_s;
+        // Several row blocks per (b, kv head): a split count that is a multiple
+        // of 8 puts the row blocks of one (b, kv head, split) on one XCD, so
+        // that they read their common tiles through that XCD's L2 (workgroups
+        // go to the 8 XCDs round robin by linear index, and the split is the
+        // fastest grid index).
+        const int64_t s8 = (S + 7) / 8 * 8;
+        if (RB > 1 && S > 1 && s8 <= max_s) {
+            S = s8;
+            xcd_shared = true;
+        }
     }
     if (S < 1) S = 1;
     int64_t chunk = (T + S - 1) / S;
-    // automatic plans give every split whole rounds of the 8 waves; an explicit
-    // split count is kept as closely as whole tiles allow
-    const int64_t unit = (splits == 0) ? (int64_t)kWaves * kTile : (int64_t)kTile;
+    // automatic plans give every split whole rounds of the 8 waves (whole
+    // tiles where the split count is kept a multiple of 8); an explicit split
+    // count is kept as closely as whole tiles allow
+    const int64_t unit = (splits == 0 && !xcd_shared) ? (int64_t)kWaves * kTile : (int64_t)kTile;
     chunk = (chunk + unit - 1) / unit * unit;
     S = (T + chunk - 1) / chunk;
     if (units > 0x7FFFFFFF || units * S > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;

@@ -293,6 +293,34 @@ def test_device_entry_points_validate_before_any_device_work():
                 fake, 0, None, 0, None) == capi.RBQ_EUNSUPPORTED  # 3 heads x 2^28 x 4 B
 
 
+def test_automatic_split_counts():
+    """The automatic plan of the default configuration: about one workgroup per
+    compute unit, whole 256-key rounds per split with one block of 8 query rows
+    per kv head; with several row blocks a multiple of 8 splits (whole 32-key
+    tiles), so that the row blocks of one (b, kv head, split) share an XCD."""
+    lib = capi.library()
+    fake = 0x1000
+    ptrs = dict(k_words=fake, k_scales=fake, k_biases=fake, v_words=fake, v_scales=fake,
+                v_biases=fake)
+    by = ctypes.byref
+    cases = [  # B, T, H_q, L, splits
+        (8, 32768, 16, 1, 16),    # 16 (b, kv head) units, 2048 keys each
+        (1, 262144, 16, 1, 128),
+        (1, 4096, 16, 1, 16),
+        (1, 256, 2, 1, 1),        # one round of 8 tiles: one split
+        (4, 10244, 16, 4, 8),     # 4 row blocks per kv head: 8 splits of 41 tiles
+        (4, 10242, 16, 2, 16),    # 2 row blocks: 16 splits of 21 tiles
+        (8, 1000, 16, 2, 4),      # 8 splits would leave waves without a tile: rounds
+        (1, 10240, 16, 2048, 1),  # 4096 row blocks fill the chip alone
+    ]
+    for B, T, hq, L, want in cases:
+        d = _host_desc(B=B, H=2, cap=T + 256, off=T, **ptrs)
+        assert lib.rbq_quant_attn_splits(by(d), hq, L) == want, (B, T, hq, L)
+        ws = lib.rbq_quant_attn_workspace_bytes(by(d), hq, L, 0)
+        rb = (hq // 2 * L + 7) // 8
+        assert ws == (0 if want == 1 else B * 2 * rb * want * (16 + 8 * 256) * 4)
+
+
 def test_status_strings():
     lib = capi.library()
     for st in range(0, -7, -1):
