@@ -358,11 +358,12 @@ int rbq_quant_attn_decode_noalloc(const rbq_kv_cache* c, const void* q, int32_t 
  *                broadcasts.  Strides are >= 0 and the elements read must lie
  *                in the first 2^31 - 256 bytes (else RBQ_EUNSUPPORTED).
  *   causal       applies as well when nonzero (both must keep a key).
- * A query row whose every key is skipped has no key to attend: its output is
- * NaN (the page fills skipped scores with the dtype's minimum, so it would
- * average all keys with equal weight; rows of a verification always see the
- * cached prefix).  Errors: as rbq_quant_attn_decode, and RBQ_EINVAL for a bad
- * mask type or negative stride.
+ * A query row whose every key the boolean mask skips gives, as the page's
+ * fill of skipped scores with the dtype's minimum does, the mean of the
+ * dequantized values of its keys (those the causal rule leaves it, else all
+ * offset keys), with equal weights, rotated back; a skipped key next to a
+ * kept one has weight 0.  Errors: as rbq_quant_attn_decode, and RBQ_EINVAL
+ * for a bad mask type or negative stride.
  */
 int rbq_quant_attn_decode_mask(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L,
                                float scale, int32_t causal, const void* mask, int32_t mask_type,
