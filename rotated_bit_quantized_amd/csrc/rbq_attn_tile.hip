@@ -50,6 +50,7 @@ typedef _Float16 tf16x2 __attribute__((ext_vector_type(2)));
 typedef float tf32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t tu32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t tu32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t tu32x3 __attribute__((ext_vector_type(3)));
 
 constexpr int tTile = 32;                  // keys per tile
 constexpr int tCPolNT = 2;                 // tile transfers: non-temporal (read once per call)
@@ -405,14 +406,105 @@ __device__ __forceinline__ tu32x2 tr16_read(const unsigned char* p) {
     return __builtin_bit_cast(tu32x2, v);
 }
 
+// Single-wave workgroups with the widths fixed at compile time (KB, VB > 0,
+// head_dim up to 128): each lane loads the packed words of the units it
+// decodes, and the scale / bias halves of its items, straight into
+// registers, two tiles ahead (two register sets), instead of through an LDS
+// staging array: the compiler then tracks every load by its registers and
+// waits for exactly the tile it decodes, and the LDS a staging array would
+// take is left for more workgroups per compute unit.  Lane l holds units
+// l * UPL .. l * UPL + UPL - 1 of K and of V, all of one key: its words are
+// one contiguous piece of the tile, loaded whole (past the buffer's range,
+// keys at or after T, it reads as zero).
+template <int D, int NG, int KB, int VB>
+struct RegTile {
+    static constexpr int UPL = D / 64;               // K (and V) units per lane
+    static constexpr int NKW = UPL * KB, NVW = UPL * VB;
+    static constexpr int NIT = (32 * NG + 63) / 64;  // scale / bias items per lane
+    uint32_t kw[NKW];
+    uint32_t vw[NVW];
+    uint32_t meta[NIT][4];
+};
+
+// N consecutive words at byte offset off of buffer r, in as few loads as
+// their count allows (non-temporal, as the staged transfers)
+template <int N>
+__device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* w) {
+#pragma unroll
+    for (int i = 0; i + 4 <= N; i += 4) {
+        const tu32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * i, 0, tCPolNT);
+        w[i] = v[0];
+        w[i + 1] = v[1];
+        w[i + 2] = v[2];
+        w[i + 3] = v[3];
+    }
+    constexpr int b = N / 4 * 4;
+    if constexpr (N - b == 3) {
+        const tu32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, off + 4 * b, 0, tCPolNT);
+        w[b] = v[0];
+        w[b + 1] = v[1];
+        w[b + 2] = v[2];
+    } else if constexpr (N - b == 2) {
+        const tu32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off + 4 * b, 0, tCPolNT);
+        w[b] = v[0];
+        w[b + 1] = v[1];
+    } else if constexpr (N - b == 1) {
+        w[b] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * b, 0, tCPolNT);
+    }
+}
+
+// The register loads of the tile at key t0 (item m = 64 q + lane: group
+// m / 32, key m % 32; items past the groups read from outside the range,
+// i.e. zero).
+template <int D, int NG, int KB, int VB>
+__device__ __forceinline__ void reg_load(RegTile<D, NG, KB, VB>& R, const TRsrc& rs, int t0, int lane) {
+    using RT = RegTile<D, NG, KB, VB>;
+    load_words<RT::NKW>(rs.kw, ((uint32_t)t0 * (D * KB / 32) + (uint32_t)lane * RT::NKW) * 4u, R.kw);
+    load_words<RT::NVW>(rs.vw, ((uint32_t)t0 * (D * VB / 32) + (uint32_t)lane * RT::NVW) * 4u, R.vw);
+#pragma unroll
+    for (int q = 0; q < RT::NIT; ++q) {
+        const int m = 64 * q + lane;
+        const int g = m / tTile, key = m - g * tTile;
+        const uint32_t off = (g < NG) ? ((uint32_t)(t0 + key) * NG + g) * 2u : 0xFFFFFFF0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) R.meta[q][i] = __builtin_amdgcn_raw_buffer_load_b16(rs.m[i], off, 0, tCPolNT);
+    }
+}
+
+// Decode this lane's BITS-bit units (words w[UPL * BITS]) into fp16 codes
+// at dst + key * row_bytes + 64 * part.
+template <int BITS, int D>
+__device__ __forceinline__ void reg_decode_units(const uint32_t* words, int lane, unsigned char* dst,
+                                                 int row_bytes) {
+    constexpr int UPL = D / 64, upk = D / 32;
+#pragma unroll
+    for (int i = 0; i < UPL; ++i) {
+        const int u = lane * UPL + i;
+        const int key = u / upk, part = u - key * upk;
+        uint32_t w[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) w[b] = (b < BITS) ? words[i * BITS + b] : 0u;
+        uint32_t c[8];
+        unpack32<BITS>(w, c);
+        tu32x2 h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = bytes_f16(c[e]);
+        tu32x4* d = reinterpret_cast<tu32x4*>(dst + key * row_bytes + 64 * part);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = (tu32x4){h[2 * e][0], h[2 * e][1], h[2 * e + 1][0], h[2 * e + 1][1]};
+    }
+}
+
 // W = 4: long query blocks (64 rows per workgroup share every decoded tile);
 // W = 1: up to 16 rows per kv head (decode, short verify blocks): one wave
 // per workgroup decodes and computes its own tiles, so the compute units run
 // many independent waves instead of one computing wave per four.
-template <int DT, int D, int NG, int W>
+template <int DT, int D, int NG, int W, int KB = 0, int VB = 0>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_tile_kernel(TArgs a) {
     using Ly = TileLds<D, W, NG>;
+    constexpr bool RP = KB > 0;  // register-staged tiles (single wave, widths fixed)
+    static_assert(!RP || (W == 1 && D <= 128 && VB > 0), "register staging: one wave, head_dim <= 128");
     constexpr int kThr = 64 * W;
     constexpr int kRW = 16 * W;  // query rows per workgroup
     constexpr int NC = D / 32;    // 32-dim chunks
@@ -465,13 +557,24 @@ void attn_tile_kernel(TArgs a) {
     }
     tlds_u8* rawl = (tlds_u8*)rawb;
     uint32_t meta1[4] = {0u, 0u, 0u, 0u};  // NG = 1: this thread's item, loaded a tile ahead
-    if (t_begin < t_lim) {
+    // register staging: the first two tiles; later loads go to the last tile
+    // of the split when they would pass it (their data is not used)
+    const int t_last = (t_lim > t_begin) ? t_begin + (t_lim - 1 - t_begin) / tTile * tTile : t_begin;
+    RegTile<D, NG, RP ? KB : 4, RP ? VB : 4> reg_a, reg_b;
+    if constexpr (RP) {
+        reg_load(reg_a, rs, t_begin, lane);
+        reg_load(reg_b, rs, min(t_begin + tTile, t_last), lane);
+    } else if (t_begin < t_lim) {
         issue_tile<D, NG, W>(a, rs, t_begin, wave, lane, rawl);
         if (NG == 1 && tid < 32) load_meta1(a, row0, t_begin, tid, meta1);
     }
 
     // ---- query operands: row 16 wave + n of the block, dims 32 c + 8 j + 0..7 ----
-    const int rowA = r0 + 16 * wave + n;
+    // paired rows (register-staged shape, at most 8 rows per kv head):
+    // operand rows 0-7 hold the hi parts of the 8 query rows, rows 8-15 their
+    // lo parts, so one MFMA takes both and the accumulators' hi and lo rows
+    // are added by a lane-half swap
+    const int rowA = RP ? r0 + (n & 7) : r0 + 16 * wave + n;
     const bool wave_live = r0 + 16 * wave < a.G;
     tf16x8 qh[NC], ql[NC];
     {
@@ -530,6 +633,11 @@ void attn_tile_kernel(TArgs a) {
                 gsum[c / CPG] += qv[c][e];
             }
         }
+        if constexpr (RP) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                if (n >= 8) qh[c] = ql[c];
+        }
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             float s = gsum[g];
@@ -546,9 +654,12 @@ void attn_tile_kernel(TArgs a) {
     uint32_t moff[4];  // byte offset of the row's mask elements; 0xFFFFFFFF: no mask
     __syncthreads();
     const int esize = (a.mtype == 1) ? 1 : (a.mtype == 2) ? 4 : 2;
+    // paired rows: lane (j, n) keeps the softmax state of rows
+    // rb + 2 p + hl (rb = 4 (j & 1), hl = j >> 1), p = 0, 1
+    const int rb = 4 * (j & 1), hl = j >> 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int rr = 4 * j + i;
+        const int rr = RP ? rb + 2 * (i & 1) + hl : 4 * j + i;
         frow[i] = fs[Ly::frw / 4 + wave * 16 + rr];
         m_run[i] = -INFINITY;
         l_part[i] = 0.f;
@@ -582,33 +693,8 @@ void attn_tile_kernel(TArgs a) {
     // reads key 8 j + 4 h + e, columns 4 c .. 4 c + 3 of an output block
     const unsigned char* vrd = smem + Ly::vc + (8 * j + (n >> 2)) * Ly::VS + 8 * (n & 3);
 
-    for (int t0 = t_begin; t0 < t_lim; t0 += tTile) {
-        // the tile's transfers have landed (each wave waits for its own; the
-        // barrier for all) and the previous tile's LDS reads are done
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        __syncthreads();
-        store_units<D, W, NG>(a, rawb, tid, smem);
-#pragma unroll
-        for (int q = 0; q < NIT; ++q) {
-            const int m = q * kThr + tid;
-            if (m < 32 * NG) {  // whole 32-lane groups
-                uint32_t meta[4];
-                if constexpr (NG == 1) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) meta[i] = meta1[i];
-                } else {
-                    read_meta<D, NG>(rawb, a.raw_meta, m, meta);
-                }
-                store_meta<DT, D, W, NG>(meta, m, smem, f_run[q]);
-            }
-        }
-        __syncthreads();  // codes in place; the staging area is free
-        if (t0 + tTile < t_lim) {
-            issue_tile<D, NG, W>(a, rs, t0 + tTile, wave, lane, rawl);
-            if (NG == 1 && tid < 32) load_meta1(a, row0, t0 + tTile, tid, meta1);
-        }
-        if (!wave_live) continue;
-
+    // the arithmetic of one tile whose codes, scales and biases are in LDS
+    auto compute_tile = [&](const int t0) __attribute__((always_inline)) {
         // ---- scores ----
         float sacc[2][4], bacc[2][4];
 #pragma unroll
@@ -735,6 +821,273 @@ void attn_tile_kernel(TArgs a) {
                 O[t] = tmfma(pl, vb8, O[t]);
             }
         }
+    };
+    // the same with paired rows: one MFMA per operand pair (hi and lo rows
+    // together), two softmax rows per lane
+    auto compute_tile_pr = [&](const int t0) __attribute__((always_inline)) {
+        // ---- scores: accumulator rows 4 j + i (j < 2: hi parts of rows
+        //      rb + i, j >= 2: lo parts), column = key ----
+        float sacc[2][4];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sacc[nb][i] = 0.f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            tf32x4 acc[2] = {(tf32x4){0.f, 0.f, 0.f, 0.f}, (tf32x4){0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int cc = 0; cc < CPG; ++cc) {
+                const int c = g * CPG + cc;
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    const tf16x8 kb8 = *reinterpret_cast<const tf16x8*>(
+                        smem + Ly::kc + (16 * nb + n) * Ly::KS + 64 * c + 16 * j);
+                    acc[nb] = tmfma(qh[c], kb8, acc[nb]);
+                }
+            }
+            const float s0 = fs[Ly::ksl / 4 + g * tTile + n], s1 = fs[Ly::ksl / 4 + g * tTile + 16 + n];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sacc[0][i] += s0 * acc[0][i];
+                sacc[1][i] += s1 * acc[1][i];
+            }
+        }
+        // hi + lo by one lane-half swap per register pair: the lane's row p
+        // (rb + 2 p + hl) of key 16 nb + n
+        float sc[2][2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(
+                    __float_as_uint(sacc[nb][2 * pp]), __float_as_uint(sacc[nb][2 * pp + 1]), false, false);
+                const float tt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                const int rr = rb + 2 * pp + hl;
+                float bias = 0.f;
+#pragma unroll
+                for (int g = 0; g < NG; ++g)
+                    bias += fs[Ly::kbl / 4 + g * tTile + 16 * nb + n] * fs[Ly::qst / 4 + g * 16 + rr];
+                const int t = t0 + 16 * nb + n;
+                float sv = tt * frow[pp] + bias;
+                if (t >= t_end || t >= vis[pp]) sv = -INFINITY;
+                if (a.mtype != 0 && moff[pp] != 0xFFFFFFFFu && sv != -INFINITY) {
+                    const uint32_t off = moff[pp] + (uint32_t)t * esize;
+                    if (a.mtype == 1) {
+                        if (__builtin_amdgcn_raw_buffer_load_b8(mask_r, off, 0, 0) == 0) sv = -INFINITY;
+                    } else if (a.mtype == 2) {
+                        sv += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mask_r, off, 0, 0)) * tLog2e;
+                    } else {
+                        sv += elem_to_f32<DT>(__builtin_amdgcn_raw_buffer_load_b16(mask_r, off, 0, 0)) * tLog2e;
+                    }
+                }
+                sc[nb][pp] = sv;
+            }
+
+        // ---- online softmax of the lane's two rows (base 2, exact running
+        //      maximum) ----
+        float alpha[2], pr[2][2];
+        bool grow = false;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            const float tmx = tmax16(fmaxf(sc[0][pp], sc[1][pp]));
+            const float m_new = fmaxf(m_run[pp], tmx);
+            if (m_new == -INFINITY) {
+                alpha[pp] = 1.f;
+                pr[0][pp] = pr[1][pp] = 0.f;
+            } else {
+                alpha[pp] = exp2f(m_run[pp] - m_new);
+                pr[0][pp] = exp2f(sc[0][pp] - m_new);
+                pr[1][pp] = exp2f(sc[1][pp] - m_new);
+            }
+            grow |= m_new != m_run[pp];
+            m_run[pp] = m_new;
+            l_part[pp] = l_part[pp] * alpha[pp] + (pr[0][pp] + pr[1][pp]);
+        }
+        if (__any(grow)) {
+            // accumulator register i holds row rb + i (hi or lo part); rows
+            // rb + hl and rb + 2 + hl are this lane's, the others its
+            // partner's (lane ^ 32)
+            const float pa0 = __shfl_xor(alpha[0], 32), pa1 = __shfl_xor(alpha[1], 32);
+            const float alc[4] = {hl ? pa0 : alpha[0], hl ? alpha[0] : pa0, hl ? pa1 : alpha[1],
+                                  hl ? alpha[1] : pa1};
+#pragma unroll
+            for (int t = 0; t < NB; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) O[t][i] *= alc[i];
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+                for (int g = 0; g < NG; ++g) ob[pp][g] *= alpha[pp];
+        }
+        // group biases: sum_t p_t b_{t,g} per lane over its keys n, 16 + n
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const float v0 = fs[Ly::vbl / 4 + g * tTile + n], v1 = fs[Ly::vbl / 4 + g * tTile + 16 + n];
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) ob[pp][g] += pr[0][pp] * v0 + pr[1][pp] * v1;
+        }
+        // P to the operand layout through LDS: operand row n reads query row
+        // n & 7, keys 8 j .. 8 j + 7 (rows 8-15 take the lo parts below)
+        float* pw = fs + Ly::pst / 4 + wave * 16 * tPS;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) pw[(rb + 2 * pp + hl) * tPS + 16 * nb + n] = pr[nb][pp];
+        __builtin_amdgcn_wave_barrier();
+        const tf32x4 pa0 = *reinterpret_cast<const tf32x4*>(pw + (n & 7) * tPS + 8 * j);
+        const tf32x4 pa1 = *reinterpret_cast<const tf32x4*>(pw + (n & 7) * tPS + 8 * j + 4);
+        const bool lo_row = n >= 8;
+
+        // ---- P V, accumulated into O (one MFMA per output block) ----
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const float rsg = fs[Ly::vres / 4 + g];
+            if (rsg != 1.0f) {  // the group's running scale power dropped
+#pragma unroll
+                for (int t = g * NPG; t < (g + 1) * NPG; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) O[t][i] *= rsg;
+            }
+            const tf32x4 x0 = *reinterpret_cast<const tf32x4*>(fs + Ly::vsf / 4 + g * tTile + 8 * j);
+            const tf32x4 x1 = *reinterpret_cast<const tf32x4*>(fs + Ly::vsf / 4 + g * tTile + 8 * j + 4);
+            const tu32x2 s01 = split_f16(pa0[0] * x0[0], pa0[1] * x0[1], one);
+            const tu32x2 s23 = split_f16(pa0[2] * x0[2], pa0[3] * x0[3], one);
+            const tu32x2 s45 = split_f16(pa1[0] * x1[0], pa1[1] * x1[1], one);
+            const tu32x2 s67 = split_f16(pa1[2] * x1[2], pa1[3] * x1[3], one);
+            const tf16x8 pp8 = __builtin_bit_cast(
+                tf16x8, (tu32x4){lo_row ? s01[1] : s01[0], lo_row ? s23[1] : s23[0],
+                                 lo_row ? s45[1] : s45[0], lo_row ? s67[1] : s67[0]});
+#pragma unroll
+            for (int t = g * NPG; t < (g + 1) * NPG; ++t) {
+                const tu32x2 v0 = tr16_read(vrd + 32 * t);
+                const tu32x2 v1 = tr16_read(vrd + 32 * t + 4 * Ly::VS);
+                const tf16x8 vb8 = __builtin_bit_cast(tf16x8, (tu32x4){v0[0], v0[1], v1[0], v1[1]});
+                O[t] = tmfma(pp8, vb8, O[t]);
+            }
+        }
+    };
+    if constexpr (!RP) {
+        for (int t0 = t_begin; t0 < t_lim; t0 += tTile) {
+            // the tile's transfers have landed (each wave waits for its own; the
+            // barrier for all) and the previous tile's LDS reads are done
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            __syncthreads();
+            store_units<D, W, NG>(a, rawb, tid, smem);
+#pragma unroll
+            for (int q = 0; q < NIT; ++q) {
+                const int m = q * kThr + tid;
+                if (m < 32 * NG) {  // whole 32-lane groups
+                    uint32_t meta[4];
+                    if constexpr (NG == 1) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) meta[i] = meta1[i];
+                    } else {
+                        read_meta<D, NG>(rawb, a.raw_meta, m, meta);
+                    }
+                    store_meta<DT, D, W, NG>(meta, m, smem, f_run[q]);
+                }
+            }
+            __syncthreads();  // codes in place; the staging area is free
+            if (t0 + tTile < t_lim) {
+                issue_tile<D, NG, W>(a, rs, t0 + tTile, wave, lane, rawl);
+                if (NG == 1 && tid < 32) load_meta1(a, row0, t0 + tTile, tid, meta1);
+            }
+            if (!wave_live) continue;
+            compute_tile(t0);
+        }
+    } else {
+        // one tile from a register set: decode it into LDS, refill the set
+        // with the tile two ahead, compute (LDS-only barriers: the register
+        // loads in flight stay in flight)
+        auto step = [&](const int t0, RegTile<D, NG, KB, VB>& R) __attribute__((always_inline)) {
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            reg_decode_units<KB, D>(R.kw, lane, smem + Ly::kc, Ly::KS);
+            reg_decode_units<VB, D>(R.vw, lane, smem + Ly::vc, Ly::VS);
+#pragma unroll
+            for (int q = 0; q < NIT; ++q) {
+                const int m = q * kThr + tid;
+                if (m < 32 * NG) store_meta<DT, D, W, NG>(R.meta[q], m, smem, f_run[q]);
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            reg_load(R, rs, min(t0 + 2 * tTile, t_last), lane);
+            compute_tile_pr(t0);
+        };
+        int t0 = t_begin;
+        for (; t0 + tTile < t_lim; t0 += 2 * tTile) {
+            step(t0, reg_a);
+            step(t0 + tTile, reg_b);
+        }
+        if (t0 < t_lim) step(t0, reg_a);
+    }
+
+    if constexpr (RP) {
+        // paired rows: the hi and lo parts of output row rb + 2 p + hl come
+        // together by one lane-half swap (every lane takes part before any
+        // lane stores); then as below
+        float vinv[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) vinv[g] = (t_begin < t_lim) ? fs[Ly::vinv / 4 + g] : 1.f;
+        float lsum[2], bsum[2][NG];
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            lsum[pp] = tsum16(l_part[pp]);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) bsum[pp][g] = tsum16(ob[pp][g]);
+        }
+        auto comb = [](float x, float y) -> float {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+            return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        };
+        if (a.S == 1) {
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                const int R = r0 + rb + 2 * pp + hl;
+                const float inv = 1.0f / lsum[pp];
+                // a boolean mask dropped every key of the row: the mean of its keys
+                const bool uniform = a.mtype == 1 && lsum[pp] == 0.f && R < a.G;
+                const int nv = a.causal ? T - a.L + (R % a.L) + 1 : T;
+                const int hq = kvh * a.n_rep + R / a.L;
+                float* orow = a.out + (((int64_t)b * a.Hkv * a.n_rep + hq) * a.L + R % a.L) * D;
+#pragma unroll
+                for (int t = 0; t < NB; ++t) {
+                    const int g = t / NPG;
+                    const int col = 16 * t + n;
+                    float y = (comb(O[t][2 * pp], O[t][2 * pp + 1]) * vinv[g] + bsum[pp][g]) * inv;
+                    if (uniform)
+                        y = value_column_mean<DT>(a.vw, a.vs, a.vb, row0, nv, col, a.vbits,
+                                                  D * a.vbits / 32, NG, a.GS);
+                    float z = y;
+                    if (a.rot != nullptr) {
+                        const float4 v = *reinterpret_cast<const float4*>(a.rot + 16 * (col >> 2) + 4 * (col & 3));
+                        const float y0 = tdpp<0x00>(y), y1 = tdpp<0x55>(y), y2 = tdpp<0xAA>(y), y3 = tdpp<0xFF>(y);
+                        double s2 = (double)y0 * (double)v.x;
+                        s2 = s2 + (double)y1 * (double)v.y;
+                        s2 = s2 + (double)y2 * (double)v.z;
+                        s2 = s2 + (double)y3 * (double)v.w;
+                        z = (float)s2;
+                    }
+                    if (R < a.G) orow[col] = z;
+                }
+            }
+            return;
+        }
+        const int64_t unit = (int64_t)bhr * a.S + split;
+        float* ro = a.rec_o + unit * kRW * D;
+        float* rml = a.rec_ml + unit * kRW * 2;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            const int rr = rb + 2 * pp + hl;
+#pragma unroll
+            for (int t = 0; t < NB; ++t) {
+                const float val = comb(O[t][2 * pp], O[t][2 * pp + 1]) * vinv[t / NPG] + bsum[pp][t / NPG];
+                if (r0 + rr < a.G) ro[rr * D + 16 * t + n] = val;
+            }
+            if (n == 0 && r0 + rr < a.G) {
+                rml[2 * rr] = m_run[pp];
+                rml[2 * rr + 1] = lsum[pp];
+            }
+        }
+        return;
     }
 
     // ---- record: (m, l) and the unnormalised o of each row; with one split
@@ -965,23 +1318,25 @@ __global__ __launch_bounds__(256) void attn_tile_merge_kernel(TMArgs a) {
 // arrays and the staging for the call's widths) and two waves per SIMD at
 // most.
 template <int D, int NG, int W>
-int tile_fit(int kbits, int vbits) {
-    const int lds = TileLds<D, W, NG>::bytes + raw_bytes(D, NG, kbits, vbits);
+int tile_fit(int kbits, int vbits, bool reg) {
+    // register-staged tiles need no staging array
+    const int lds = TileLds<D, W, NG>::bytes + (reg ? 0 : raw_bytes(D, NG, kbits, vbits));
     const int by_lds = 160 * 1024 / lds;
     const int by_waves = 8 / W;
     return by_lds < by_waves ? by_lds : by_waves;
 }
 
-static int tile_workgroups_per_cu(int D, int ng, int W, int kbits, int vbits) {
+static int tile_workgroups_per_cu(int D, int ng, int W, int kbits, int vbits, bool reg) {
 #define RBQ_FIT(D_, NG_)                                                   \
     if (D == D_ && ng == NG_)                                              \
-        return W == 4 ? tile_fit<D_, NG_, 4>(kbits, vbits) : tile_fit<D_, NG_, 1>(kbits, vbits);
+        return W == 4 ? tile_fit<D_, NG_, 4>(kbits, vbits, false) : tile_fit<D_, NG_, 1>(kbits, vbits, reg);
     RBQ_FIT(64, 1) RBQ_FIT(64, 2) RBQ_FIT(128, 1) RBQ_FIT(128, 2) RBQ_FIT(128, 4)
 #undef RBQ_FIT
 #define RBQ_FIT(D_, NG_) \
-    if (D == D_ && ng == NG_) return tile_fit<D_, NG_, 4>(kbits, vbits);
+    if (D == D_ && ng == NG_) return tile_fit<D_, NG_, 4>(kbits, vbits, false);
     RBQ_FIT(256, 2) RBQ_FIT(256, 4)
-    if (D == 256 && ng == 8) return W == 4 ? tile_fit<256, 8, 4>(kbits, vbits) : tile_fit<256, 8, 1>(kbits, vbits);
+    if (D == 256 && ng == 8)
+        return W == 4 ? tile_fit<256, 8, 4>(kbits, vbits, false) : tile_fit<256, 8, 1>(kbits, vbits, false);
 #undef RBQ_FIT
     return 1;
 }
@@ -1000,6 +1355,10 @@ int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Til
     // build is not used
     const int ng = c->head_dim / c->group_size;
     const int W = (G <= 16 && (c->head_dim <= 128 || ng == 8)) ? 1 : 4;
+    // up to 8 rows per kv head at head_dim <= 128 with 4-bit K and V codes:
+    // single-wave workgroups with register-staged tiles (the widths fixed at
+    // compile time) and paired hi / lo operand rows
+    const bool reg = W == 1 && G <= 8 && c->head_dim <= 128 && c->k_bits == 4 && c->v_bits == 4;
     const int64_t RW = 16 * W;
     const int64_t RBW = (G + RW - 1) / RW;
     const int64_t T = c->offset;
@@ -1009,7 +1368,7 @@ int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Til
         // one round of workgroups over the 256 compute units, as many per
         // unit as LDS and registers allow (longer splits lose less to set-up
         // and records than a second round gains)
-        const int per_cu = tile_workgroups_per_cu(c->head_dim, ng, W, c->k_bits, c->v_bits);
+        const int per_cu = tile_workgroups_per_cu(c->head_dim, ng, W, c->k_bits, c->v_bits, reg);
         S = (256 * per_cu + units - 1) / units;
         const int64_t max_s = (T + tTile - 1) / tTile;
         if (S > max_s) S = max_s;
@@ -1027,6 +1386,7 @@ int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Til
     p->S = (int)S;
     p->RBW = (int)RBW;
     p->W = W;
+    p->reg = reg ? 1 : 0;
     p->chunk = chunk;
     p->o_floats = (size_t)(units * S) * RW * c->head_dim;
     // one split: the attention kernel stores the output itself
@@ -1068,7 +1428,7 @@ int tile_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
     a.raw_vw = raw_vw_off(c->head_dim, c->k_bits);
     a.raw_meta = raw_meta_off(c->head_dim, c->k_bits, c->v_bits);
     const int ng = c->head_dim / c->group_size;
-    const size_t dyn = (size_t)raw_bytes(c->head_dim, ng, c->k_bits, c->v_bits);
+    const size_t dyn = p.reg ? 0 : (size_t)raw_bytes(c->head_dim, ng, c->k_bits, c->v_bits);
     a.mask = mk.ptr;
     a.msb = mk.sb;
     a.msh = mk.sh;
@@ -1083,6 +1443,9 @@ int tile_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
     if (c->head_dim == D_ && ng == NG_) {                                                         \
         if (p.W == 4)                                                                             \
             bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_, 4>) : launch(attn_tile_kernel<RBQ_F16, D_, NG_, 4>); \
+        else if (p.reg && D_ <= 128)                                                              \
+            bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_, 1, (D_ <= 128 ? 4 : 0), (D_ <= 128 ? 4 : 0)>)          \
+               : launch(attn_tile_kernel<RBQ_F16, D_, NG_, 1, (D_ <= 128 ? 4 : 0), (D_ <= 128 ? 4 : 0)>);          \
         else                                                                                      \
             bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_, 1>) : launch(attn_tile_kernel<RBQ_F16, D_, NG_, 1>); \
     } else

@@ -76,6 +76,7 @@ int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Mfm
 // split records (o floats, then (m, l) pairs).
 struct TilePlan {
     int W;
+    int reg;  // single-wave workgroups with register-staged tiles (fixed widths)
     int S;
     int RBW;
     int64_t chunk;
