@@ -58,9 +58,12 @@ constexpr int tPS = tTile + 4;             // floats per row of a wave's P stagi
 constexpr float tLog2e = 1.44269504088896340736f;
 
 // LDS of a workgroup of W waves (16 query rows each), NG groups per row.
-template <int D, int W, int NG>
+// RK (register-staged shape): the K rows hold the packed 4-bit words as they
+// are (D / 8 words, padded to D / 8 + 4: conflict-free 4-byte reads of 16
+// keys x 4 words), the codes entering the matrix cores in place.
+template <int D, int W, int NG, bool RK = false>
 struct TileLds {
-    static constexpr int KS = 2 * D + 16;                               // bytes per key row of K codes
+    static constexpr int KS = RK ? D / 2 + 16 : 2 * D + 16;            // bytes per key row of K codes
     static constexpr int VS = 2 * D + 32;                               // bytes per key row of V codes
     static constexpr int kc = 0;                                        // K codes, fp16 [32][KS / 2]
     static constexpr int vc = kc + tTile * KS;                          // V codes, fp16 [32][VS / 2]
@@ -357,10 +360,10 @@ __device__ __forceinline__ void read_meta(const unsigned char* rawb, int raw_met
 // (1 otherwise).  f_run is this thread's copy of F_g (1000 = no nonzero
 // scale yet).  Called by all 64 lanes of a wave with items m = 64 q + lane
 // (the maximum is a butterfly over the 32 lanes of a group).
-template <int DT, int D, int W, int NG>
+template <int DT, int D, int W, int NG, bool RK = false>
 __device__ __forceinline__ void store_meta(const uint32_t meta[4], int m, unsigned char* smem,
                                            int& f_run) {
-    using Ly = TileLds<D, W, NG>;
+    using Ly = TileLds<D, W, NG, RK>;
     const int g = m / tTile, key = m - g * tTile;
     const bool live = g < NG;
     const float s_v = elem_to_f32<DT>(meta[2]);
@@ -502,9 +505,10 @@ __device__ __forceinline__ void reg_decode_units(const uint32_t* words, int lane
 template <int DT, int D, int NG, int W, int KB = 0, int VB = 0>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_tile_kernel(TArgs a) {
-    using Ly = TileLds<D, W, NG>;
     constexpr bool RP = KB > 0;  // register-staged tiles (single wave, widths fixed)
-    static_assert(!RP || (W == 1 && D <= 128 && VB > 0), "register staging: one wave, head_dim <= 128");
+    using Ly = TileLds<D, W, NG, RP>;
+    static_assert(!RP || (W == 1 && D <= 128 && KB == 4 && VB > 0),
+                  "register staging: one wave, head_dim <= 128, 4-bit K codes entering the MFMAs in place");
     constexpr int kThr = 64 * W;
     constexpr int kRW = 16 * W;  // query rows per workgroup
     constexpr int NC = D / 32;    // 32-dim chunks
@@ -626,17 +630,22 @@ void attn_tile_kernel(TArgs a) {
         for (int c = 0; c < NC; ++c) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float xs = ldexpf(qv[c][e], E);
-                const _Float16 hi = (_Float16)xs;
-                qh[c][e] = hi;
-                ql[c][e] = (_Float16)(xs - (float)hi);
                 gsum[c / CPG] += qv[c][e];
+                if constexpr (RP) {
+                    // slot e takes dim kPerm[e] of the block times 1 or 1/16
+                    // (the K operand's nibble order and factors); rows 8-15
+                    // of the operand take the lo parts
+                    constexpr int kPerm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+                    const float xs = ldexpf(qv[c][kPerm[e]], E) * ((e & 2) ? 0.0625f : 1.0f);
+                    const _Float16 hi = (_Float16)xs;
+                    qh[c][e] = (n >= 8) ? (_Float16)(xs - (float)hi) : hi;
+                } else {
+                    const float xs = ldexpf(qv[c][e], E);
+                    const _Float16 hi = (_Float16)xs;
+                    qh[c][e] = hi;
+                    ql[c][e] = (_Float16)(xs - (float)hi);
+                }
             }
-        }
-        if constexpr (RP) {
-#pragma unroll
-            for (int c = 0; c < NC; ++c)
-                if (n >= 8) qh[c] = ql[c];
         }
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
@@ -840,9 +849,15 @@ void attn_tile_kernel(TArgs a) {
                 const int c = g * CPG + cc;
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) {
-                    const tf16x8 kb8 = *reinterpret_cast<const tf16x8*>(
-                        smem + Ly::kc + (16 * nb + n) * Ly::KS + 64 * c + 16 * j);
-                    acc[nb] = tmfma(qh[c], kb8, acc[nb]);
+                    // word 4 c + j of key 16 nb + n: its nibble pairs masked
+                    // in place are fp16 subnormals c 2^-24 (nibbles 0, 4 and
+                    // 2, 6) or 16 c 2^-24 (1, 5 and 3, 7), matching the query
+                    // operand's slot order and factors
+                    const uint32_t w = *reinterpret_cast<const uint32_t*>(
+                        smem + Ly::kc + (16 * nb + n) * Ly::KS + 4 * (4 * c + j));
+                    const uint32_t w8 = w >> 8;
+                    const tu32x4 kv = {w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u};
+                    acc[nb] = tmfma(qh[c], __builtin_bit_cast(tf16x8, kv), acc[nb]);
                 }
             }
             const float s0 = fs[Ly::ksl / 4 + g * tTile + n], s1 = fs[Ly::ksl / 4 + g * tTile + 16 + n];
@@ -868,7 +883,7 @@ void attn_tile_kernel(TArgs a) {
                 for (int g = 0; g < NG; ++g)
                     bias += fs[Ly::kbl / 4 + g * tTile + 16 * nb + n] * fs[Ly::qst / 4 + g * 16 + rr];
                 const int t = t0 + 16 * nb + n;
-                float sv = tt * frow[pp] + bias;
+                float sv = tt * 16777216.0f * frow[pp] + bias;  // codes entered as c 2^-24
                 if (t >= t_end || t >= vis[pp]) sv = -INFINITY;
                 if (a.mtype != 0 && moff[pp] != 0xFFFFFFFFu && sv != -INFINITY) {
                     const uint32_t off = moff[pp] + (uint32_t)t * esize;
@@ -895,9 +910,9 @@ void attn_tile_kernel(TArgs a) {
                 alpha[pp] = 1.f;
                 pr[0][pp] = pr[1][pp] = 0.f;
             } else {
-                alpha[pp] = exp2f(m_run[pp] - m_new);
-                pr[0][pp] = exp2f(sc[0][pp] - m_new);
-                pr[1][pp] = exp2f(sc[1][pp] - m_new);
+                alpha[pp] = __builtin_amdgcn_exp2f(m_run[pp] - m_new);
+                pr[0][pp] = __builtin_amdgcn_exp2f(sc[0][pp] - m_new);
+                pr[1][pp] = __builtin_amdgcn_exp2f(sc[1][pp] - m_new);
             }
             grow |= m_new != m_run[pp];
             m_run[pp] = m_new;
@@ -1001,12 +1016,21 @@ void attn_tile_kernel(TArgs a) {
         // loads in flight stay in flight)
         auto step = [&](const int t0, RegTile<D, NG, KB, VB>& R) __attribute__((always_inline)) {
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            reg_decode_units<KB, D>(R.kw, lane, smem + Ly::kc, Ly::KS);
+            {
+                // K words as they are: this lane's units of key u / (D / 32)
+                constexpr int UPL = D / 64, upk = D / 32;
+                const int u = lane * UPL;
+                const int key = u / upk, part = u - key * upk;
+                tu32x4* kd = reinterpret_cast<tu32x4*>(smem + Ly::kc + key * Ly::KS + 16 * part);
+#pragma unroll
+                for (int e = 0; e < UPL; ++e)
+                    kd[e] = (tu32x4){R.kw[4 * e], R.kw[4 * e + 1], R.kw[4 * e + 2], R.kw[4 * e + 3]};
+            }
             reg_decode_units<VB, D>(R.vw, lane, smem + Ly::vc, Ly::VS);
 #pragma unroll
             for (int q = 0; q < NIT; ++q) {
                 const int m = q * kThr + tid;
-                if (m < 32 * NG) store_meta<DT, D, W, NG>(R.meta[q], m, smem, f_run[q]);
+                if (m < 32 * NG) store_meta<DT, D, W, NG, RP>(R.meta[q], m, smem, f_run[q]);
             }
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             reg_load(R, rs, min(t0 + 2 * tTile, t_last), lane);
@@ -1320,7 +1344,8 @@ __global__ __launch_bounds__(256) void attn_tile_merge_kernel(TMArgs a) {
 template <int D, int NG, int W>
 int tile_fit(int kbits, int vbits, bool reg) {
     // register-staged tiles need no staging array
-    const int lds = TileLds<D, W, NG>::bytes + (reg ? 0 : raw_bytes(D, NG, kbits, vbits));
+    const int lds = reg ? TileLds<D, W, NG, true>::bytes
+                        : TileLds<D, W, NG>::bytes + raw_bytes(D, NG, kbits, vbits);
     const int by_lds = 160 * 1024 / lds;
     const int by_waves = 8 / W;
     return by_lds < by_waves ? by_lds : by_waves;
