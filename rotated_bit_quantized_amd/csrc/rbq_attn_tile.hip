@@ -559,6 +559,38 @@ void attn_tile_kernel(TArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) rs.m[k] = tmake_rsrc(mb[k] + row0 * NG, (uint32_t)T * NG * 2u);
     }
+    // the query row and the rotation matrix are loaded before the tile
+    // transfers: loads complete in issue order, so a wait for them would
+    // otherwise wait for the tiles too.  Query row: 16 wave + n of the block
+    // (paired rows: n & 7), dims 32 c + 8 j + 0..7; the rotation matrix (D
+    // float4s) is loaded once per workgroup and passed through LDS.
+    const int rowA = RP ? r0 + (n & 7) : r0 + 16 * wave + n;
+    const bool wave_live = r0 + 16 * wave < a.G;
+    float xq[NC][8];
+    {
+        const uint16_t* qrow = nullptr;
+        if (rowA < a.G) {
+            const int h = kvh * a.n_rep + rowA / a.L;
+            qrow = a.q + (((int64_t)b * a.Hkv * a.n_rep + h) * a.L + rowA % a.L) * D;
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xq[c][e] = 0.f;
+            if (qrow != nullptr) {
+                load4<DT>(qrow + 32 * c + 8 * j, xq[c]);
+                load4<DT>(qrow + 32 * c + 8 * j + 4, xq[c] + 4);
+            }
+        }
+    }
+    constexpr int NRS = (D + kThr - 1) / kThr;  // float4s of the rotation matrix per thread
+    float4 rsl[NRS];
+#pragma unroll
+    for (int i = 0; i < NRS; ++i) {
+        const int idx = tid + kThr * i;
+        rsl[i] = (a.rot != nullptr && idx < D) ? reinterpret_cast<const float4*>(a.rot)[idx]
+                                               : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     tlds_u8* rawl = (tlds_u8*)rawb;
     uint32_t meta1[4] = {0u, 0u, 0u, 0u};  // NG = 1: this thread's item, loaded a tile ahead
     // register staging: the first two tiles; later loads go to the last tile
@@ -573,35 +605,42 @@ void attn_tile_kernel(TArgs a) {
         if (NG == 1 && tid < 32) load_meta1(a, row0, t_begin, tid, meta1);
     }
 
-    // ---- query operands: row 16 wave + n of the block, dims 32 c + 8 j + 0..7 ----
-    // paired rows (register-staged shape, at most 8 rows per kv head):
-    // operand rows 0-7 hold the hi parts of the 8 query rows, rows 8-15 their
-    // lo parts, so one MFMA takes both and the accumulators' hi and lo rows
-    // are added by a lane-half swap
-    const int rowA = RP ? r0 + (n & 7) : r0 + 16 * wave + n;
-    const bool wave_live = r0 + 16 * wave < a.G;
+    // the rotation matrix into the K code area (free until the first tile
+    // is decoded)
+    static_assert(tTile * Ly::KS >= 16 * D, "the rotation matrix fits the K code area");
+    float* rotl = reinterpret_cast<float*>(smem + Ly::kc);
+#pragma unroll
+    for (int i = 0; i < NRS; ++i) {
+        const int idx = tid + kThr * i;
+        if (idx < D) reinterpret_cast<float4*>(rotl)[idx] = rsl[i];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // LDS only
+
+    // ---- query operands (paired rows in the register-staged shape, at most
+    //      8 rows per kv head: operand rows 0-7 hold the hi parts of the 8
+    //      query rows, rows 8-15 their lo parts, so one MFMA takes both and
+    //      the accumulators' hi and lo rows are added by a lane-half swap) ----
     tf16x8 qh[NC], ql[NC];
     {
         float qv[NC][8];
-        const uint16_t* qrow = nullptr;
-        if (rowA < a.G) {
-            const int h = kvh * a.n_rep + rowA / a.L;
-            qrow = a.q + (((int64_t)b * a.Hkv * a.n_rep + h) * a.L + rowA % a.L) * D;
-        }
         float mx = 0.f;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            if (qrow != nullptr) {
-                load4<DT>(qrow + 32 * c + 8 * j, x);
-                load4<DT>(qrow + 32 * c + 8 * j + 4, x + 4);
-            }
+            const float* x = xq[c];
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb) {
                 float y[4];
                 if (a.rot != nullptr) {
                     float Bm[16];
-                    load_block(a.rot, 8 * c + 2 * j + hb, Bm);
+                    const float4* bp = reinterpret_cast<const float4*>(rotl + 16 * (8 * c + 2 * j + hb));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float4 bv = bp[r];
+                        Bm[4 * r] = bv.x;
+                        Bm[4 * r + 1] = bv.y;
+                        Bm[4 * r + 2] = bv.z;
+                        Bm[4 * r + 3] = bv.w;
+                    }
                     rotate4(x + 4 * hb, Bm, y);
                     if (a.round_rot) {
 #pragma unroll
@@ -661,7 +700,8 @@ void attn_tile_kernel(TArgs a) {
     float frow[4], m_run[4], l_part[4];
     int vis[4];
     uint32_t moff[4];  // byte offset of the row's mask elements; 0xFFFFFFFF: no mask
-    __syncthreads();
+    // LDS only: __syncthreads would also wait for the tile transfers in flight
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const int esize = (a.mtype == 1) ? 1 : (a.mtype == 2) ? 4 : 2;
     // paired rows: lane (j, n) keeps the softmax state of rows
     // rb + 2 p + hl (rb = 4 (j & 1), hl = j >> 1), p = 0, 1
@@ -1246,6 +1286,19 @@ __global__ __launch_bounds__(256) void attn_tile_merge_kernel(TMArgs a) {
     // needed last and depends on nothing)
     float Bm[16];
     load_block(a.rot, tid < NQ ? tid : 0, Bm);
+    // the first kFirst records of this thread (column quad k, splits sg,
+    // sg + NSG, ...) are loaded before the split weights are reduced, so that
+    // their latency overlaps the reductions
+    const int k = tid % NQ, sg = tid / NQ;
+    const float* ro = a.rec_o + ((int64_t)bhr * a.S * RW + rr) * D + 4 * k;
+    constexpr int kFirst = 16;
+    float4 v1[kFirst];
+#pragma unroll
+    for (int u = 0; u < kFirst; ++u) {
+        const int s1 = sg + u * NSG;
+        v1[u] = (s1 < a.S) ? *reinterpret_cast<const float4*>(ro + (int64_t)s1 * RW * D)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     // (m, l) of the splits tid, tid + 256, ... (tMaxSplits / 256 at most),
     // loaded once
     constexpr int kPer = tMaxSplits / 256;
@@ -1274,12 +1327,19 @@ __global__ __launch_bounds__(256) void attn_tile_merge_kernel(TMArgs a) {
         lsum += lv[i] * w;
     }
     const float Ls = block_reduce<false>(lsum, red);  // its barriers also publish wsh
-    const int k = tid % NQ, sg = tid / NQ;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float* ro = a.rec_o + ((int64_t)bhr * a.S * RW + rr) * D + 4 * k;
-    // the split records of this thread, four loads in flight at a time
-    // (summed in split order as before)
-    int s = sg;
+    // the thread's records in split order: the first kFirst, then the rest
+    // four loads in flight at a time
+#pragma unroll
+    for (int u = 0; u < kFirst; ++u) {
+        const int s1 = sg + u * NSG;
+        const float w = (s1 < a.S) ? wsh[s1] : 0.f;
+        acc.x += v1[u].x * w;
+        acc.y += v1[u].y * w;
+        acc.z += v1[u].z * w;
+        acc.w += v1[u].w * w;
+    }
+    int s = sg + kFirst * NSG;
     for (; s + 3 * NSG < a.S; s += 4 * NSG) {
         float4 v[4];
 #pragma unroll
