@@ -1319,6 +1319,9 @@ int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Mfm
     chunk = (chunk + unit - 1) / unit * unit;
     S = (T + chunk - 1) / chunk;
     if (units > 0x7FFFFFFF || units * S > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
+    // the merge kernel's one launch: at most 2^32 - 1 work-items along x (8
+    // column blocks x 512 threads per unit at most)
+    if (S > 1 && units * 8 * 512 > 0xFFFFFFFFll) return RBQ_EUNSUPPORTED;
     // 32-bit buffer offsets, also for the tile reads past T (at most 4 tiles)
     if ((T + kWaves * kTile) * (int64_t)(kKWords * 4) > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
     p->S = (int)S;

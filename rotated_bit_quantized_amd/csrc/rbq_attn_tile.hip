@@ -1465,6 +1465,10 @@ int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Til
     S = (T + chunk - 1) / chunk;
     if (units > 0x7FFFFFFF || units * S > 0x7FFFFFFF || units * RW > 0x7FFFFFFF)
         return RBQ_EUNSUPPORTED;
+    // one launch of each kernel: at most 2^32 - 1 work-items along x
+    if (units * S * 64 * W > 0xFFFFFFFFll ||
+        (S > 1 && units * 16 * W * 256 > 0xFFFFFFFFll))
+        return RBQ_EUNSUPPORTED;
     // 32-bit buffer offsets of the tile transfers, up to one tile past T
     const int64_t bits = c->k_bits > c->v_bits ? c->k_bits : c->v_bits;
     if ((T + tTile) * (int64_t)c->head_dim * bits / 8 > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;

@@ -321,6 +321,29 @@ def test_automatic_split_counts():
         assert ws == (0 if want == 1 else B * 2 * rb * want * (16 + 8 * 256) * 4)
 
 
+def test_launch_sizes_are_bounded():
+    """Calls whose kernels would need more than 2^32 - 1 work-items along x in
+    one launch are refused before any device work."""
+    lib = capi.library()
+    fake = 0x1000
+    ptrs = dict(k_words=fake, k_scales=fake, k_biases=fake, v_words=fake, v_scales=fake,
+                v_biases=fake)
+    by = ctypes.byref
+    dec = lib.rbq_quant_attn_decode
+    # default configuration, 2^21 (b, kv head) units: with key splits the
+    # merge kernel would need 2^21 x 8 x 512 work-items
+    d = _host_desc(B=1 << 20, H=2, cap=4096, off=4096, **ptrs)
+    assert dec(by(d), fake, 4, 1, 0.0625, 1, None, fake, 2, fake, 1 << 62, None) == \
+        capi.RBQ_EUNSUPPORTED
+    assert lib.rbq_quant_attn_splits(by(d), 4, 1) == 1  # one split: no merge, planned
+    # head_dim 128 K4/V4: 2^21 units, one 256-thread merge workgroup per row
+    # (16 per unit)
+    e = _host_desc(B=1 << 20, H=2, cap=4096, off=4096, head_dim=128, group_size=64, k_bits=4,
+                   v_bits=4, **ptrs)
+    assert dec(by(e), fake, 16, 1, 0.0884, 1, None, fake, 2, fake, 1 << 62, None) == \
+        capi.RBQ_EUNSUPPORTED
+
+
 def test_status_strings():
     lib = capi.library()
     for st in range(0, -7, -1):
