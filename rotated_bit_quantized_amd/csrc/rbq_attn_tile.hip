@@ -367,9 +367,11 @@ __device__ __forceinline__ void store_meta(const uint32_t meta[4], int m, unsign
     const int g = m / tTile, key = m - g * tTile;
     const bool live = g < NG;
     const float s_v = elem_to_f32<DT>(meta[2]);
-    float mx = live ? fabsf(s_v) : 0.f;
-#pragma unroll
-    for (int k = 1; k < 32; k <<= 1) mx = fmaxf(mx, __shfl_xor(mx, k));
+    // the maximum over the 32 lanes of a group: over each 16-lane row by DPP,
+    // then across the row pair by one row swap
+    float mx = tmax16(live ? fabsf(s_v) : 0.f);
+    const auto rsw = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(rsw[0]), __uint_as_float(rsw[1]));
     int ex = 0;
     if (mx > 0.f) (void)frexpf(mx, &ex);
     const int f_new = (mx > 0.f) ? min(f_run, 15 - ex) : f_run;
@@ -703,6 +705,7 @@ void attn_tile_kernel(TArgs a) {
     // LDS only: __syncthreads would also wait for the tile transfers in flight
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const int esize = (a.mtype == 1) ? 1 : (a.mtype == 2) ? 4 : 2;
+    const int vis_lo = a.causal ? T - a.L + 1 : T;  // the first row's visible keys
     // paired rows: lane (j, n) keeps the softmax state of rows
     // rb + 2 p + hl (rb = 4 (j & 1), hl = j >> 1), p = 0, 1
     const int rb = 4 * (j & 1), hl = j >> 1;
@@ -908,7 +911,9 @@ void attn_tile_kernel(TArgs a) {
             }
         }
         // hi + lo by one lane-half swap per register pair: the lane's row p
-        // (rb + 2 p + hl) of key 16 nb + n
+        // (rb + 2 p + hl) of key 16 nb + n; keys past the split or past a
+        // row's last visible key only in a tile that reaches them
+        const bool full = t0 + tTile <= t_end && t0 + tTile <= vis_lo;
         float sc[2][2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
@@ -924,7 +929,7 @@ void attn_tile_kernel(TArgs a) {
                     bias += fs[Ly::kbl / 4 + g * tTile + 16 * nb + n] * fs[Ly::qst / 4 + g * 16 + rr];
                 const int t = t0 + 16 * nb + n;
                 float sv = tt * 16777216.0f * frow[pp] + bias;  // codes entered as c 2^-24
-                if (t >= t_end || t >= vis[pp]) sv = -INFINITY;
+                if (!full && (t >= t_end || t >= vis[pp])) sv = -INFINITY;
                 if (a.mtype != 0 && moff[pp] != 0xFFFFFFFFu && sv != -INFINITY) {
                     const uint32_t off = moff[pp] + (uint32_t)t * esize;
                     if (a.mtype == 1) {
