@@ -811,9 +811,11 @@ void attn_tile_kernel(TArgs a) {
                 alpha[i] = 1.f;
                 p[0][i] = p[1][i] = 0.f;
             } else {
-                alpha[i] = exp2f(m_run[i] - m_new);
-                p[0][i] = exp2f(sc[0][i] - m_new);
-                p[1][i] = exp2f(sc[1][i] - m_new);
+                // hardware exp2 (results below 2^-126, weights negligible
+                // next to the row's largest, flush to zero)
+                alpha[i] = __builtin_amdgcn_exp2f(m_run[i] - m_new);
+                p[0][i] = __builtin_amdgcn_exp2f(sc[0][i] - m_new);
+                p[1][i] = __builtin_amdgcn_exp2f(sc[1][i] - m_new);
             }
             grow |= m_new != m_run[i];
             m_run[i] = m_new;
