@@ -342,15 +342,20 @@ __device__ __forceinline__ void dma_tile_part(lds_u8* buf, int t0, int lane, __a
 
 // The k-th tile (counted within the split) of a wave, or n_tiles when the
 // wave has no k-th tile.  Round robin over the waves, except for the last
-// full round together with the remainder (8 to 15 tiles): positions 0-7 go
-// to waves 0-3, two each, 8-11 to waves 4-7 and 12-15 to waves 0-3 again.
-// The older half of a workgroup issues first on each SIMD and gets through
-// its tiles sooner; with the same number of tiles each, it idles at the end
-// while the younger half finishes.  The order is fixed, so results do not
-// depend on timing.
+// full round together with the remainder (8 to 15 tiles) when there are
+// earlier rounds: positions 0-7 go to waves 0-3, two each, 8-11 to waves 4-7
+// and 12-15 to waves 0-3 again.  The older half of a workgroup issues first
+// on each SIMD and gets through its tiles sooner; with the same number of
+// tiles each, it idles at the end while the younger half finishes.  A split
+// of a single round stays round robin: there every wave's first tile is in
+// flight from the start, and two tiles in a row on half the waves would
+// double the wait.  The order is fixed, so results do not depend on timing.
 __device__ __forceinline__ int wave_tile(int k, int wave, int n_tiles) {
     const int rounds = n_tiles / kWaves;
-    if (rounds == 0) return (k == 0 && wave < n_tiles) ? wave : n_tiles;
+    if (rounds <= 1) {
+        const int t = wave + kWaves * k;
+        return (t < n_tiles) ? t : n_tiles;
+    }
     if (k < rounds - 1) return wave + kWaves * k;
     const int jt = k - (rounds - 1);  // index among the wave's last-round tiles
     int pos = 2 * kWaves;             // none
