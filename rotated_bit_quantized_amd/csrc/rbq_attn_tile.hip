@@ -595,13 +595,15 @@ void attn_tile_kernel(TArgs a) {
     }
     tlds_u8* rawl = (tlds_u8*)rawb;
     uint32_t meta1[4] = {0u, 0u, 0u, 0u};  // NG = 1: this thread's item, loaded a tile ahead
-    // register staging: the first two tiles; later loads go to the last tile
-    // of the split when they would pass it (their data is not used)
+    // register staging: the first two tiles; a load that would pass the
+    // split's last tile reads at row T instead, past the buffers' ranges (it
+    // returns zeros without touching memory; its data is not used)
     const int t_last = (t_lim > t_begin) ? t_begin + (t_lim - 1 - t_begin) / tTile * tTile : t_begin;
+    auto next_tile = [&](int t) { return t <= t_last ? t : T; };
     RegTile<D, NG, RP ? KB : 4, RP ? VB : 4> reg_a, reg_b;
     if constexpr (RP) {
         reg_load(reg_a, rs, t_begin, lane);
-        reg_load(reg_b, rs, min(t_begin + tTile, t_last), lane);
+        reg_load(reg_b, rs, next_tile(t_begin + tTile), lane);
     } else if (t_begin < t_lim) {
         issue_tile<D, NG, W>(a, rs, t_begin, wave, lane, rawl);
         if (NG == 1 && tid < 32) load_meta1(a, row0, t_begin, tid, meta1);
@@ -1080,7 +1082,7 @@ void attn_tile_kernel(TArgs a) {
                 if (m < 32 * NG) store_meta<DT, D, W, NG, RP>(R.meta[q], m, smem, f_run[q]);
             }
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            reg_load(R, rs, min(t0 + 2 * tTile, t_last), lane);
+            reg_load(R, rs, next_tile(t0 + 2 * tTile), lane);
             compute_tile_pr(t0);
         };
         int t0 = t_begin;
