@@ -1449,10 +1449,12 @@ int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Til
     // build is not used
     const int ng = c->head_dim / c->group_size;
     const int W = (G <= 16 && (c->head_dim <= 128 || ng == 8)) ? 1 : 4;
-    // up to 8 rows per kv head at head_dim <= 128 with 4-bit K and V codes:
-    // single-wave workgroups with register-staged tiles (the widths fixed at
-    // compile time) and paired hi / lo operand rows
-    const bool reg = W == 1 && G <= 8 && c->head_dim <= 128 && c->k_bits == 4 && c->v_bits == 4;
+    // up to 8 rows per kv head at head_dim <= 128 with 4-bit K codes (they
+    // enter the MFMAs in place) and 2-, 3- or 4-bit V codes: single-wave
+    // workgroups with register-staged tiles (the widths fixed at compile
+    // time) and paired hi / lo operand rows
+    const bool reg = W == 1 && G <= 8 && c->head_dim <= 128 && c->k_bits == 4 && c->v_bits >= 2 &&
+                     c->v_bits <= 4;
     const int64_t RW = 16 * W;
     const int64_t RBW = (G + RW - 1) / RW;
     const int64_t T = c->offset;
@@ -1490,6 +1492,20 @@ int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Til
     // one split: the attention kernel stores the output itself
     p->ws_bytes = (S == 1) ? 0 : (p->o_floats + (size_t)(units * S) * RW * 2) * sizeof(float);
     return RBQ_OK;
+}
+
+// The register-staged kernels of head_dim D (at most 128), NG groups per
+// row, 4-bit K and vbits-bit V (2, 3 or 4).
+template <int D, int NG, typename F>
+static void launch_reg(F&& launch, bool bf, int vbits) {
+    if constexpr (D <= 128) {
+        if (vbits == 2)
+            bf ? launch(attn_tile_kernel<RBQ_BF16, D, NG, 1, 4, 2>) : launch(attn_tile_kernel<RBQ_F16, D, NG, 1, 4, 2>);
+        else if (vbits == 3)
+            bf ? launch(attn_tile_kernel<RBQ_BF16, D, NG, 1, 4, 3>) : launch(attn_tile_kernel<RBQ_F16, D, NG, 1, 4, 3>);
+        else
+            bf ? launch(attn_tile_kernel<RBQ_BF16, D, NG, 1, 4, 4>) : launch(attn_tile_kernel<RBQ_F16, D, NG, 1, 4, 4>);
+    }
 }
 
 int tile_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, float scale,
@@ -1542,8 +1558,7 @@ int tile_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
         if (p.W == 4)                                                                             \
             bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_, 4>) : launch(attn_tile_kernel<RBQ_F16, D_, NG_, 4>); \
         else if (p.reg && D_ <= 128)                                                              \
-            bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_, 1, (D_ <= 128 ? 4 : 0), (D_ <= 128 ? 4 : 0)>)          \
-               : launch(attn_tile_kernel<RBQ_F16, D_, NG_, 1, (D_ <= 128 ? 4 : 0), (D_ <= 128 ? 4 : 0)>);          \
+            launch_reg<D_, NG_>(launch, bf, c->v_bits);                                            \
         else                                                                                      \
             bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_, 1>) : launch(attn_tile_kernel<RBQ_F16, D_, NG_, 1>); \
     } else

@@ -1,14 +1,15 @@
 """GPU parity of the tile kernel's register-staged shape against the oracle.
 
-Up to 8 query rows per kv head with 4-bit K and V codes at head_dim 64 and
-128 run single-wave workgroups that load each tile's packed words and scale /
-bias halves into registers two tiles ahead and pair the hi and lo parts of
-the query rows in one matrix operand.  Covered here: both head dims, every
-group count (1, 2 and 4 groups per row), both dtypes, both rotations and the
-page's rotation precision; 4 and 8 rows per kv head (GQA rows and causal
-verify rows), a ragged last tile, one split (many tiles per workgroup: both
-register sets and the odd last tile), automatic and explicit splits; an
-additive mask and a boolean mask with rows that keep no key.
+Up to 8 query rows per kv head with 4-bit K codes and 2-, 3- or 4-bit V
+codes at head_dim 64 and 128 run single-wave workgroups that load each
+tile's packed words and scale / bias halves into registers two tiles ahead
+and pair the hi and lo parts of the query rows in one matrix operand.
+Covered here: both head dims, every group count (1, 2 and 4 groups per row),
+the three V widths, both dtypes, both rotations and the page's rotation
+precision; 4 and 8 rows per kv head (GQA rows and causal verify rows), a
+ragged last tile, one split (many tiles per workgroup: both register sets
+and the odd last tile), automatic and explicit splits; an additive mask and
+a boolean mask with rows that keep no key.
 """
 import numpy as np
 import pytest
@@ -29,13 +30,17 @@ VARS = [
     (128, 128, 4, 4, "f16", False, True),
     (128, 32, 4, 4, "bf16", True, False),
     (128, 64, 4, 4, "bf16", True, True),
+    (128, 64, 4, 3, "bf16", False, False),
+    (64, 32, 4, 2, "f16", True, False),
+    (128, 32, 4, 3, "f16", False, True),
 ]
 # (B, H_q, H_kv, L): rows per kv head G = H_q / H_kv * L
 SHAPES = [(2, 8, 2, 1), (1, 4, 1, 2), (1, 16, 2, 1)]
 
 
 def _vid(v):
-    return "D{}_g{}_{}{}{}".format(v[0], v[1], v[4], "_2s" if v[5] else "", "_rr" if v[6] else "")
+    return "D{}_g{}_v{}_{}{}{}".format(v[0], v[1], v[3], v[4], "_2s" if v[5] else "",
+                                      "_rr" if v[6] else "")
 
 
 @pytest.fixture(scope="module")
