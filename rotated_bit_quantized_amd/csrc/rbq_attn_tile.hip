@@ -782,13 +782,19 @@ void attn_tile_kernel(TArgs a) {
             }
         }
         float sc[2][4];
+        // keys past the split or past a row's last visible key only in a
+        // tile that reaches them (one vote over the wave)
+        bool lane_full = t0 + tTile <= t_end;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lane_full = lane_full && t0 + tTile <= vis[i];
+        const bool full = __all(lane_full);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = t0 + 16 * nb + n;
                 float s = sacc[nb][i] * frow[i] + bacc[nb][i];
-                if (t >= t_end || t >= vis[i]) s = -INFINITY;
+                if (!full && (t >= t_end || t >= vis[i])) s = -INFINITY;
                 if (a.mtype != 0 && moff[i] != 0xFFFFFFFFu && s != -INFINITY) {
                     const uint32_t off = moff[i] + (uint32_t)t * esize;
                     if (a.mtype == 1) {
