@@ -306,11 +306,11 @@ int rbq_quant_attn_decode(const rbq_kv_cache* c, const void* q, int32_t H_q, int
  *   q ... ws    as rbq_quant_attn_decode, for the cache after the append:
  *               L <= offset + n, and ws_bytes >= rbq_quant_attn_workspace_bytes
  *               of a descriptor whose offset is offset + n.
- * In the default configuration with H_q / H_kv x L <= 8 and 1 <= n <= 8
- * (k and v 8-byte aligned) the attention kernel quantizes and writes the n
- * rows itself: the workgroup whose key range holds a row writes it before
- * reading it, and no other workgroup reads it; one launch fewer than the two
- * calls.  Otherwise the two calls run as they are.  Every argument is
+ * In the default configuration with 1 <= n <= 8 (k and v 8-byte aligned)
+ * the attention kernel quantizes and writes the n rows itself: the
+ * workgroups whose key range holds a row (one per block of 8 query rows of
+ * the kv head) each write it, the same bytes, before reading it; one launch
+ * fewer than the two calls.  Otherwise the two calls run as they are.  Every argument is
  * checked before anything is launched; on error nothing is written and
  * c->offset is unchanged.  Errors: those of both calls.
  */

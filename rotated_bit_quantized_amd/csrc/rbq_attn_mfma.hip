@@ -126,9 +126,9 @@ struct MArgs {
     const uint16_t* vs;
     const uint16_t* vb;
     const float* rot;
-    // fused append (no mask, one block of rows per kv head): rows
-    // [T - n_new, T) of the cache are quantized from kn / vn
-    // ([B][H_kv][n_new][256], unrotated) and written by this launch
+    // fused append (no mask): rows [T - n_new, T) of the cache are quantized
+    // from kn / vn ([B][H_kv][n_new][256], unrotated) and written by this
+    // launch
     const uint16_t* kn;
     const uint16_t* vn;
     int64_t capacity;
@@ -479,7 +479,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // fused append: the appended rows [T - n_new, T) that fall in this split,
     // [app_lo, app_lo + n_app), are quantized and written by this workgroup,
     // row app_lo + w by wave w, before any transfer of the workgroup reads
-    // them (no other workgroup reads them: one block of rows per kv head)
+    // them.  With several blocks of query rows per kv head, the workgroup of
+    // every block quantizes and writes the rows of its split itself: the
+    // same code on the same inputs writes the same bytes, and each workgroup
+    // reads only after its own stores are complete, so no workgroup depends
+    // on another
     int app_lo = t_end, n_app = 0;
     if constexpr (MK == kMaskNone) {
         if (a.n_new > 0) {
@@ -1642,7 +1646,7 @@ extern "C" int rbq_kv_append_attn_decode(rbq_kv_cache* c, const void* k, const v
     st = attn_plan(&after, H_q, L, splits, &ap);
     if (st != RBQ_OK) return st;
     if (ap.ws_bytes > 0 && (ws == nullptr || ws_bytes < ap.ws_bytes)) return RBQ_EWORKSPACE;
-    const bool fused = n > 0 && !ap.tile && ap.mp.RB == 1 && n <= kWaves &&
+    const bool fused = n > 0 && !ap.tile && n <= kWaves &&
                        (reinterpret_cast<uintptr_t>(k) & 7) == 0 &&
                        (reinterpret_cast<uintptr_t>(v) & 7) == 0;
     if (!fused) {

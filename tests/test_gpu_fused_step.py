@@ -6,8 +6,9 @@ itself, the cache rows and the output must equal those of the two calls
 within the attention tolerance; the shapes cover appended rows in the last
 tile of a long split, rows that straddle two key splits, rows inside the
 first tile of a workgroup (whose transfer then waits for them), one split
-with the output stored directly, no rotation, the page's rotation precision,
-fp16, and the shapes that run as two launches.
+with the output stored directly, several blocks of query rows per kv head
+(every block's workgroups write the rows of their split), no rotation, the
+page's rotation precision, fp16, and the shape that runs as two launches.
 """
 import numpy as np
 import pytest
@@ -33,7 +34,10 @@ CASES = [
     ("bf16", False, False, 2, 2, 2, 2, 8, 8, 0),       # T = 10: appended rows in the first tile
     ("bf16", True, True, 1, 16, 2, 256, 1, 1, 0),      # the append grows the buffers first
     ("f16", False, True, 1, 8, 1, 700, 1, 1, 3),       # explicit splits, one kv head
-    ("bf16", False, True, 1, 16, 2, 300, 2, 2, 0),     # 16 rows per kv head: two launches
+    ("bf16", False, True, 1, 16, 2, 300, 2, 2, 0),     # 16 rows per kv head (two row blocks)
+    ("bf16", False, True, 4, 16, 2, 10240, 4, 4, 0),   # the verify block: 32 rows, 4 row blocks
+    ("f16", True, True, 2, 16, 2, 507, 6, 4, 5),       # 4 row blocks, rows 507-512 straddle
+                                                       # the splits [384, 512) and [512, 513)
     ("bf16", False, True, 1, 16, 2, 300, 9, 1, 0),     # 9 rows appended: two launches
 ]
 
