@@ -107,3 +107,38 @@ def test_register_staged_tiles_masks(splits, dev):
     ref = O.attention(q.float().numpy(), oc, 128 ** -0.5, True, blocks, mask=keep)
     err = float(np.abs(out.cpu().numpy() - ref).max())
     assert err <= ATOL, ("boolean", err)
+
+
+@pytest.mark.parametrize("T", [1, 31, 32, 33, 65])
+@pytest.mark.parametrize("splits", [0, 1, 7])
+def test_register_staged_tiles_short_caches(T, splits, dev):
+    # fewer keys than one tile, exactly one, one and a bit, two and a bit;
+    # explicit splits beyond the tile count
+    var = (128, 64, 4, 3, "bf16", True, False)
+    B, Hq, Hkv, L = 1, 16, 2, 1
+    print(f"[register tiles] short cache T={T} splits={splits}", flush=True)
+    c, oc, blocks = _setup(var, dev, B, Hkv, T, 47)
+    q = W.random_rows([48, T], (B, Hq, L, 128), "bf16")
+    out = c.attend(q.to(dev), scale=128 ** -0.5, causal=True, splits=splits)
+    torch.cuda.synchronize()
+    ref = O.attention(q.float().numpy(), oc, 128 ** -0.5, True, blocks)
+    err = float(np.abs(out.cpu().numpy() - ref).max())
+    assert err <= ATOL, err
+
+
+def test_register_staged_tiles_decode_steps(dev):
+    # the one-call step on this configuration (the append kernel, then the
+    # attention), several steps in a row over a growing cache
+    var = (64, 32, 4, 4, "f16", False, False)
+    B, Hq, Hkv, T0 = 2, 8, 2, 250
+    c, oc, blocks = _setup(var, dev, B, Hkv, T0, 49)
+    for step in range(4):
+        kn = W.random_rows([50, step], (B, Hkv, 1, 64), "f16", "student_t3")
+        vn = W.random_rows([51, step], (B, Hkv, 1, 64), "f16")
+        q = W.random_rows([52, step], (B, Hq, 1, 64), "f16")
+        out = c.append_attend(kn.to(dev), vn.to(dev), q.to(dev), scale=0.125, causal=True)
+        torch.cuda.synchronize()
+        oc.append(kn.float().numpy(), vn.float().numpy(), blocks)
+        ref = O.attention(q.float().numpy(), oc, 0.125, True, blocks)
+        err = float(np.abs(out.cpu().numpy() - ref).max())
+        assert err <= ATOL, (step, err)
