@@ -5,17 +5,24 @@
 // and any number of query rows per kv head (G = H_q / H_kv x L, up to
 // prefill-length blocks).
 //
-// Decomposition: one workgroup of 4 wave64s per (b, kv head, block of 64
-// query rows, key split); wave w owns query rows 16 w .. 16 w + 15 of the
-// block.  The workgroup walks 32-key tiles: all 256 threads decode the tile
-// into LDS once (K codes as bytes [key][dim], V codes as bytes transposed
-// [dim][key], as fp16 values; scales and biases as fp32 [group][key]), then every wave with
-// a live row runs its 16 rows against it, while the next tile's packed words
-// are already being loaded into registers.  The codes are converted once per
-// tile, in the decode, to fp16 (exact: integers below 2^11), so the operand
-// reads of the waves need no conversion.  (Codes taken as fp16 subnormals,
-// c * 2^-24, lose precision in the matrix cores when the other operand spans
-// a wide range, as the probabilities do.)
+// Decomposition, three shapes, one workgroup per (b, kv head, block of
+// query rows, key split), walking 32-key tiles:
+// - four waves, 64 query rows (long blocks): wave w owns rows 16 w .. 16 w +
+//   15 of the block; all 256 threads decode each tile into LDS once (K and V
+//   codes as fp16 [key][dim]; scales and biases as fp32 [group][key]) from
+//   a staging array filled by direct-to-LDS transfers one tile ahead, then
+//   every wave with a live row runs its 16 rows against it;
+// - one wave, up to 16 rows (short blocks): the same per wave;
+// - one wave, up to 8 rows, 4-bit K codes and 2- to 4-bit V codes at
+//   head_dim 64 or 128 (register-staged): each lane loads the packed words
+//   of its units straight into registers two tiles ahead; the hi and lo
+//   parts of the 8 query rows share one operand (rows 0-7 and 8-15) and K
+//   codes enter the score MFMAs in place (nibble pairs masked as fp16
+//   subnormals, the query operand permuted and scaled to match).
+// V codes are converted once per tile to fp16 (exact: integers below 2^11),
+// so the operand reads need no conversion.  (V codes taken as fp16
+// subnormals, c * 2^-24, lose precision in the matrix cores when the other
+// operand spans a wide range, as the probabilities do.)
 //
 // All products run as 16x16x32 MFMAs.  Lane l = 16 j + n: operand lanes hold
 // row / column n and the 8 k-slots 8 j .. 8 j + 7 (the same slots in A and
@@ -23,7 +30,7 @@
 // holds rows 4 j .. 4 j + 3 of column n.
 // Scores: A = query rows, rotated, times scale * log2(e) and a per-row power
 //   of two 2^E that puts the largest |q| in [2^14, 2^15), split into an fp16
-//   hi and lo part (two MFMAs); B = K codes.  One accumulator per group g of
+//   hi and lo part (two MFMAs, or one with paired rows); B = K codes.  One accumulator per group g of
 //   the row: score = 2^-E sum_g s_g acc_g + sum_g b_g (sum_{d in g} q_d),
 //   folded on the vector units (base-2 scores).
 // Values: A = P' = p s_{t,g} 2^F_g (the probability times the key's value
