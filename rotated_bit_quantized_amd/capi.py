@@ -344,4 +344,37 @@ def rbq_kv_append_attn_decode(desc: rbq_kv_cache, k: torch.Tensor, v: torch.Tens
                                           int(splits), wp, wn, _stream()))
 
 
+def prepare_append_attn_decode(desc: rbq_kv_cache, k: torch.Tensor, v: torch.Tensor,
+                               q: torch.Tensor, scale: float, causal: bool, rot_blocks,
+                               out: torch.Tensor, splits: int = 0, ws: torch.Tensor = None):
+    """``rbq_kv_append_attn_decode`` with its arguments checked and marshalled
+    once, for a loop that repeats the same step on caches of ``desc``'s shape
+    (the tensors must stay alive and in place; the stream is the current one
+    now).  Returns ``call(desc)``, which makes the library call on that cache
+    descriptor and raises on a nonzero status."""
+    if k.shape != v.shape or k.dim() != 4:
+        raise ValueError("k and v must both be [B, H_kv, n, head_dim]")
+    if (k.shape[0], k.shape[1], k.shape[3]) != (desc.B, desc.H_kv, desc.head_dim):
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match the cache")
+    if q.dim() != 4 or q.shape[0] != desc.B or q.shape[3] != desc.head_dim:
+        raise ValueError(f"q shape {tuple(q.shape)} does not match the cache")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    dt = _TORCH_OF[desc.dtype]
+    args = (_dev_ptr(k, dt, "k"), _dev_ptr(v, dt, "v"), k.shape[2], _dev_ptr(q, dt, "q"),
+            q.shape[1], q.shape[2], float(scale), 1 if causal else 0,
+            None if rot_blocks is None else _dev_ptr(rot_blocks, torch.float32, "rot_blocks"),
+            _dev_ptr(out, torch.float32, "out"), int(splits),
+            None if ws is None else _dev_ptr(ws, None, "ws"),
+            0 if ws is None else ws.numel() * ws.element_size(), _stream())
+    fn = _lib.rbq_kv_append_attn_decode
+
+    def call(d: rbq_kv_cache) -> None:
+        st = fn(ctypes.byref(d), *args)
+        if st != RBQ_OK:
+            _check("rbq_kv_append_attn_decode", st)
+
+    return call
+
+
 _TORCH_OF = {RBQ_F16: torch.float16, RBQ_BF16: torch.bfloat16}

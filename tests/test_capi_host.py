@@ -344,6 +344,21 @@ def test_launch_sizes_are_bounded():
         capi.RBQ_EUNSUPPORTED
 
 
+def test_prepared_step_checks_its_arguments():
+    import torch
+    d = _host_desc(B=1, H=2, cap=256, off=100, k_words=0x1000, k_scales=0x1000, k_biases=0x1000,
+                   v_words=0x1000, v_scales=0x1000, v_biases=0x1000)
+    k = torch.zeros(1, 2, 1, 256, dtype=torch.bfloat16)
+    q = torch.zeros(1, 4, 1, 256, dtype=torch.bfloat16)
+    out = torch.zeros(1, 4, 1, 256, dtype=torch.float32)
+    with pytest.raises(ValueError):  # host tensors
+        capi.prepare_append_attn_decode(d, k, k, q, 0.0625, True, None, out)
+    with pytest.raises(ValueError):  # k / v shapes differ
+        capi.prepare_append_attn_decode(d, k, k[:, :1], q, 0.0625, True, None, out)
+    with pytest.raises(ValueError):  # out shape
+        capi.prepare_append_attn_decode(d, k, k, q, 0.0625, True, None, out[:, :2])
+
+
 def test_status_strings():
     lib = capi.library()
     for st in range(0, -7, -1):

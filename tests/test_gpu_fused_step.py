@@ -149,3 +149,29 @@ def test_fused_step_n0_is_the_attention(dev):
     torch.cuda.synchronize()
     assert c1.offset == 500
     assert torch.equal(out1, out2)
+
+
+def test_prepared_step_equals_the_binding_call(dev):
+    # the step with its arguments marshalled once (the benchmark's loop) makes
+    # the same library call: rows and output bit for bit
+    case = ("bf16", False, True, 2, 16, 2, 777, 1, 1, 0)
+    print("[fused step] prepared call", flush=True)
+    (c1, c2), _, _, (kn, vn), q = _caches(case, dev, 24)
+    kd, vd, qd = kn.to(dev), vn.to(dev), q.to(dev)
+    after = capi.rbq_kv_cache.from_buffer_copy(c1.desc)
+    after.offset += 1
+    nb = capi.rbq_quant_attn_workspace_bytes(after, 16, 1, 0)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+    out1 = torch.empty(qd.shape, dtype=torch.float32, device=dev)
+    out2 = torch.empty_like(out1)
+    c1.reserve(1)
+    c2.reserve(1)
+    call = capi.prepare_append_attn_decode(c1.desc, kd, vd, qd, 1 / 16, True, c1.rot, out1, 0, ws)
+    call(c1.desc)
+    capi.rbq_kv_append_attn_decode(c2.desc, kd, vd, qd, 1 / 16, True, c2.rot, out2, 0, ws)
+    torch.cuda.synchronize()
+    assert c1.offset == c2.offset
+    assert torch.equal(out1, out2)
+    r1, r2 = _rows(c1), _rows(c2)
+    for name, _ in NAMES:
+        assert torch.equal(r1[name], r2[name]), name
