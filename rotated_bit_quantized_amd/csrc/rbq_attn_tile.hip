@@ -510,11 +510,14 @@ __device__ __forceinline__ void reg_decode_units(const uint32_t* words, int lane
 // W = 4: long query blocks (64 rows per workgroup share every decoded tile);
 // W = 1: up to 16 rows per kv head (decode, short verify blocks): one wave
 // per workgroup decodes and computes its own tiles, so the compute units run
-// many independent waves instead of one computing wave per four.
-template <int DT, int D, int NG, int W, int KB = 0, int VB = 0>
+// many independent waves instead of one computing wave per four.  PRF: at
+// most 8 rows per kv head, paired hi / lo operand rows (implied by KB > 0).
+template <int DT, int D, int NG, int W, int KB = 0, int VB = 0, int PRF = 0>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_tile_kernel(TArgs a) {
     constexpr bool RP = KB > 0;  // register-staged tiles (single wave, widths fixed)
+    constexpr bool PR = RP || PRF > 0;  // paired rows (single wave, at most 8 rows)
+    static_assert(!PR || W == 1, "paired rows: one wave");
     using Ly = TileLds<D, W, NG, RP>;
     static_assert(!RP || (W == 1 && D <= 128 && KB == 4 && VB > 0),
                   "register staging: one wave, head_dim <= 128, 4-bit K codes entering the MFMAs in place");
@@ -573,7 +576,7 @@ void attn_tile_kernel(TArgs a) {
     // otherwise wait for the tiles too.  Query row: 16 wave + n of the block
     // (paired rows: n & 7), dims 32 c + 8 j + 0..7; the rotation matrix (D
     // float4s) is loaded once per workgroup and passed through LDS.
-    const int rowA = RP ? r0 + (n & 7) : r0 + 16 * wave + n;
+    const int rowA = PR ? r0 + (n & 7) : r0 + 16 * wave + n;
     const bool wave_live = r0 + 16 * wave < a.G;
     float xq[NC][8];
     {
@@ -689,6 +692,11 @@ void attn_tile_kernel(TArgs a) {
                     const float xs = ldexpf(qv[c][kPerm[e]], E) * ((e & 2) ? 0.0625f : 1.0f);
                     const _Float16 hi = (_Float16)xs;
                     qh[c][e] = (n >= 8) ? (_Float16)(xs - (float)hi) : hi;
+                } else if constexpr (PR) {
+                    // natural dim order; rows 8-15 of the operand take the lo parts
+                    const float xs = ldexpf(qv[c][e], E);
+                    const _Float16 hi = (_Float16)xs;
+                    qh[c][e] = (n >= 8) ? (_Float16)(xs - (float)hi) : hi;
                 } else {
                     const float xs = ldexpf(qv[c][e], E);
                     const _Float16 hi = (_Float16)xs;
@@ -720,7 +728,7 @@ void attn_tile_kernel(TArgs a) {
     const int rb = 4 * (j & 1), hl = j >> 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int rr = RP ? rb + 2 * (i & 1) + hl : 4 * j + i;
+        const int rr = PR ? rb + 2 * (i & 1) + hl : 4 * j + i;
         frow[i] = fs[Ly::frw / 4 + wave * 16 + rr];
         m_run[i] = -INFINITY;
         l_part[i] = 0.f;
@@ -909,15 +917,23 @@ void attn_tile_kernel(TArgs a) {
                 const int c = g * CPG + cc;
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) {
-                    // word 4 c + j of key 16 nb + n: its nibble pairs masked
-                    // in place are fp16 subnormals c 2^-24 (nibbles 0, 4 and
-                    // 2, 6) or 16 c 2^-24 (1, 5 and 3, 7), matching the query
-                    // operand's slot order and factors
-                    const uint32_t w = *reinterpret_cast<const uint32_t*>(
-                        smem + Ly::kc + (16 * nb + n) * Ly::KS + 4 * (4 * c + j));
-                    const uint32_t w8 = w >> 8;
-                    const tu32x4 kv = {w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u};
-                    acc[nb] = tmfma(qh[c], __builtin_bit_cast(tf16x8, kv), acc[nb]);
+                    if constexpr (RP) {
+                        // word 4 c + j of key 16 nb + n: its nibble pairs
+                        // masked in place are fp16 subnormals c 2^-24
+                        // (nibbles 0, 4 and 2, 6) or 16 c 2^-24 (1, 5 and
+                        // 3, 7), matching the query operand's slot order and
+                        // factors
+                        const uint32_t w = *reinterpret_cast<const uint32_t*>(
+                            smem + Ly::kc + (16 * nb + n) * Ly::KS + 4 * (4 * c + j));
+                        const uint32_t w8 = w >> 8;
+                        const tu32x4 kv = {w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u};
+                        acc[nb] = tmfma(qh[c], __builtin_bit_cast(tf16x8, kv), acc[nb]);
+                    } else {
+                        // the decoded codes, dims 32 c + 8 j .. 32 c + 8 j + 7
+                        const tf16x8 kb8 = *reinterpret_cast<const tf16x8*>(
+                            smem + Ly::kc + (16 * nb + n) * Ly::KS + 64 * c + 16 * j);
+                        acc[nb] = tmfma(qh[c], kb8, acc[nb]);
+                    }
                 }
             }
             const float s0 = fs[Ly::ksl / 4 + g * tTile + n], s1 = fs[Ly::ksl / 4 + g * tTile + 16 + n];
@@ -945,7 +961,8 @@ void attn_tile_kernel(TArgs a) {
                 for (int g = 0; g < NG; ++g)
                     bias += fs[Ly::kbl / 4 + g * tTile + 16 * nb + n] * fs[Ly::qst / 4 + g * 16 + rr];
                 const int t = t0 + 16 * nb + n;
-                float sv = tt * 16777216.0f * frow[pp] + bias;  // codes entered as c 2^-24
+                // codes in place entered as c 2^-24
+                float sv = tt * (RP ? 16777216.0f : 1.0f) * frow[pp] + bias;
                 if (!full && (t >= t_end || t >= vis[pp])) sv = -INFINITY;
                 if (a.mtype != 0 && moff[pp] != 0xFFFFFFFFu && sv != -INFINITY) {
                     const uint32_t off = moff[pp] + (uint32_t)t * esize;
@@ -1070,7 +1087,10 @@ void attn_tile_kernel(TArgs a) {
                 if (NG == 1 && tid < 32) load_meta1(a, row0, t0 + tTile, tid, meta1);
             }
             if (!wave_live) continue;
-            compute_tile(t0);
+            if constexpr (PR)
+                compute_tile_pr(t0);
+            else
+                compute_tile(t0);
         }
     } else {
         // one tile from a register set: decode it into LDS, refill the set
@@ -1106,7 +1126,7 @@ void attn_tile_kernel(TArgs a) {
         if (t0 < t_lim) step(t0, reg_a);
     }
 
-    if constexpr (RP) {
+    if constexpr (PR) {
         // paired rows: the hi and lo parts of output row rb + 2 p + hl come
         // together by one lane-half swap (every lane takes part before any
         // lane stores); then as below
@@ -1468,6 +1488,8 @@ int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Til
     // time) and paired hi / lo operand rows
     const bool reg = W == 1 && G <= 8 && c->head_dim <= 128 && c->k_bits == 4 && c->v_bits >= 2 &&
                      c->v_bits <= 4;
+    // other widths and head dims, up to 8 rows: staged tiles, paired rows
+    const bool pr = W == 1 && G <= 8 && !reg;
     const int64_t RW = 16 * W;
     const int64_t RBW = (G + RW - 1) / RW;
     const int64_t T = c->offset;
@@ -1500,6 +1522,7 @@ int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Til
     p->RBW = (int)RBW;
     p->W = W;
     p->reg = reg ? 1 : 0;
+    p->pr = pr ? 1 : 0;
     p->chunk = chunk;
     p->o_floats = (size_t)(units * S) * RW * c->head_dim;
     // one split: the attention kernel stores the output itself
@@ -1572,6 +1595,9 @@ int tile_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
             bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_, 4>) : launch(attn_tile_kernel<RBQ_F16, D_, NG_, 4>); \
         else if (p.reg && D_ <= 128)                                                              \
             launch_reg<D_, NG_>(launch, bf, c->v_bits);                                            \
+        else if (p.pr)                                                                            \
+            bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_, 1, 0, 0, 1>)                         \
+               : launch(attn_tile_kernel<RBQ_F16, D_, NG_, 1, 0, 0, 1>);                          \
         else                                                                                      \
             bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_, 1>) : launch(attn_tile_kernel<RBQ_F16, D_, NG_, 1>); \
     } else

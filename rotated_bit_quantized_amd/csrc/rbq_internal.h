@@ -77,6 +77,7 @@ int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Mfm
 struct TilePlan {
     int W;
     int reg;  // single-wave workgroups with register-staged tiles (fixed widths)
+    int pr;   // single-wave workgroups, staged tiles, paired hi / lo operand rows
     int S;
     int RBW;
     int64_t chunk;
