@@ -25,11 +25,11 @@ PROBE_LIB = os.path.join(PKG, "librbq_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["rbq_append.hip", "rbq_attn_mfma.hip", "rbq_attn_tile.hip"]
+HIP_SOURCES = ["rbq_append.hip", "rbq_attn_mfma.hip", "rbq_attn_prefill.hip", "rbq_attn_tile.hip"]
 HOST_SOURCES = ["rbq_host.cpp"]
 # per-file extras: the attention kernels never rely on NaN semantics (masked
 # scores are -inf), which lets max reductions compile to single DPP ops
-HIP_FILE_FLAGS = {"rbq_attn_mfma.hip": ["-fno-honor-nans"]}
+HIP_FILE_FLAGS = {"rbq_attn_mfma.hip": ["-fno-honor-nans"], "rbq_attn_prefill.hip": ["-fno-honor-nans"]}
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",

@@ -75,7 +75,8 @@ constexpr int kTile = 32;                                  // keys per wave iter
 constexpr int kRows = 8;                                   // query rows per kv head
 // split record in the workspace: (m, l) per row, then o column-major
 // [256 columns][8 rows]
-constexpr int kRecFloats = 2 * kRows + kRows * kHeadDim;
+constexpr int kRecFloats = kRecordFloats;
+static_assert(kRecFloats == 2 * kRows + kRows * kHeadDim, "split record layout");
 constexpr int kMergeNarrowUnits = 64;
 constexpr int64_t kGridYZ = 65535;  // workgroups per grid dimension y or z of one launch  // below this many units the merge takes 32-column blocks
 // wave record in LDS, in its own region so that a wave stores it as soon as
@@ -1340,6 +1341,50 @@ int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Mfm
     return RBQ_OK;
 }
 
+// The merge of the split records of an attention call (one record per
+// (b, kv head, block of 8 query rows, split), kRecordFloats floats each):
+// normalisation, inverse rotation and the output rows.
+void merge_launch(const rbq_kv_cache* c, const float* rec, const float* rot_blocks, float* out,
+                  int S, int RB, int n_rep, int L, int causal, int mask_type, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t units = (int64_t)c->B * c->H_kv * RB;
+    CArgs m;
+    m.rec = rec;
+    m.rot = rot_blocks;
+    m.out = out;
+    m.S = S;
+    m.Hkv = c->H_kv;
+    m.n_rep = n_rep;
+    m.L = L;
+    m.G = n_rep * L;
+    m.RB = RB;
+    m.bool_mask = (mask_type == kMaskBool) ? 1 : 0;
+    m.dt = c->dtype;
+    m.T = (int)c->offset;
+    m.causal = causal ? 1 : 0;
+    m.capacity = c->capacity;
+    m.vw = c->v_words;
+    m.vs = (const uint16_t*)c->v_scales;
+    m.vb = (const uint16_t*)c->v_biases;
+    // up to 16 splits: one group of 128 threads; more: 2 or 4 groups side
+    // by side, so that a long key range (many splits of few kv heads) is
+    // merged in S / 64 rounds of loads instead of S / 16 (8 groups would
+    // spill registers at 1024 threads)
+    // few (b, kv head, 8 rows) units: 32 columns per workgroup, twice the
+    // workgroups
+    const bool narrow = units < kMergeNarrowUnits;
+    const dim3 mg((unsigned)(units * (narrow ? 8 : 4)));
+    auto go = [&](auto k1, auto k2, auto k4) {
+        if (S <= 16) hipLaunchKernelGGL(k1, mg, dim3(128), 0, s, m);
+        else if (S <= 32) hipLaunchKernelGGL(k2, mg, dim3(256), 0, s, m);
+        else hipLaunchKernelGGL(k4, mg, dim3(512), 0, s, m);
+    };
+    if (narrow)
+        go(attn_mfma_merge_kernel<1, 2>, attn_mfma_merge_kernel<2, 2>, attn_mfma_merge_kernel<4, 2>);
+    else
+        go(attn_mfma_merge_kernel<1, 4>, attn_mfma_merge_kernel<2, 4>, attn_mfma_merge_kernel<4, 4>);
+}
+
 int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, float scale,
                 int32_t causal, const AttnMask& mk, const float* rot_blocks, float* out,
                 const MfmaPlan& p, void* ws, void* stream, const FusedAppend* app) {
@@ -1375,7 +1420,6 @@ int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
     a.msl = mk.sl;
     a.mask_bytes = mk.bytes;
     a.round_rot = (c->flags & RBQ_FLAG_ROUND_ROTATED) ? 1 : 0;
-    const int64_t units = (int64_t)c->B * c->H_kv * p.RB;
     // grid x = key split, y = row block, z = (b, kv head); y and z in pieces
     // of at most kGridYZ, launched one after another with their offsets
     const int64_t BH = (int64_t)c->B * c->H_kv;
@@ -1401,43 +1445,7 @@ int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
         else if (mt == kMaskAddF32) launch(attn_mfma_kernel<RBQ_F16, kMaskAddF32>);
         else launch(attn_mfma_kernel<RBQ_F16, kMaskAddElem>);
     }
-    if (p.S > 1) {
-        CArgs m;
-        m.rec = a.rec;
-        m.rot = rot_blocks;
-        m.out = out;
-        m.S = p.S;
-        m.Hkv = a.Hkv;
-        m.n_rep = a.n_rep;
-        m.L = L;
-        m.G = a.G;
-        m.RB = a.RB;
-        m.bool_mask = (mt == kMaskBool) ? 1 : 0;
-        m.dt = c->dtype;
-        m.T = a.T;
-        m.causal = a.causal;
-        m.capacity = c->capacity;
-        m.vw = a.vw;
-        m.vs = a.vs;
-        m.vb = a.vb;
-        // up to 16 splits: one group of 128 threads; more: 2 or 4 groups side
-        // by side, so that a long key range (many splits of few kv heads) is
-        // merged in S / 64 rounds of loads instead of S / 16 (8 groups would
-        // spill registers at 1024 threads)
-        // few (b, kv head, 8 rows) units: 32 columns per workgroup, twice the
-        // workgroups
-        const bool narrow = units < kMergeNarrowUnits;
-        const dim3 mg((unsigned)(units * (narrow ? 8 : 4)));
-        auto go = [&](auto k1, auto k2, auto k4) {
-            if (p.S <= 16) hipLaunchKernelGGL(k1, mg, dim3(128), 0, s, m);
-            else if (p.S <= 32) hipLaunchKernelGGL(k2, mg, dim3(256), 0, s, m);
-            else hipLaunchKernelGGL(k4, mg, dim3(512), 0, s, m);
-        };
-        if (narrow)
-            go(attn_mfma_merge_kernel<1, 2>, attn_mfma_merge_kernel<2, 2>, attn_mfma_merge_kernel<4, 2>);
-        else
-            go(attn_mfma_merge_kernel<1, 4>, attn_mfma_merge_kernel<2, 4>, attn_mfma_merge_kernel<4, 4>);
-    }
+    if (p.S > 1) merge_launch(c, a.rec, rot_blocks, out, p.S, p.RB, a.n_rep, L, a.causal, mt, stream);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
         set_hip_error((int)e);
@@ -1459,11 +1467,13 @@ int check_attn(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits) {
     return RBQ_OK;
 }
 
-// Which kernel runs a call, and its plan: the dedicated kernel for the
-// default configuration up to kDedicatedMaxRows query rows per kv head, the
-// tile kernel otherwise.
+// Which kernel runs a call, and its plan: for the default configuration the
+// dedicated kernel, or from kPrefillMinRows query rows per kv head with a
+// bf16 cache the prefill kernel; the tile kernel for every other
+// configuration.
 struct AttnPlan {
     bool tile;
+    bool prefill;
     MfmaPlan mp;
     TilePlan tp;
     int S;
@@ -1473,8 +1483,13 @@ struct AttnPlan {
 int attn_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, AttnPlan* p) {
     const int64_t G = (int64_t)(H_q / c->H_kv) * L;
     p->tile = !(is_default_config(c) && G <= kDedicatedMaxRows);
+    p->prefill = !p->tile && c->dtype == RBQ_BF16 && G >= kPrefillMinRows;
     int st;
-    if (p->tile) {
+    if (p->prefill) {
+        st = prefill_plan(c, H_q, L, splits, &p->mp);
+        p->S = p->mp.S;
+        p->ws_bytes = p->mp.ws_bytes;
+    } else if (p->tile) {
         st = tile_plan(c, H_q, L, splits, &p->tp);
         p->S = p->tp.S;
         p->ws_bytes = p->tp.ws_bytes;
@@ -1581,6 +1596,7 @@ int attn_call(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, floa
         return RBQ_EWORKSPACE;
     }
     if (ap.tile) return tile_launch(c, q, H_q, L, scale, causal, mk, rot_blocks, out, ap.tp, ws, stream);
+    if (ap.prefill) return prefill_launch(c, q, H_q, L, scale, causal, mk, rot_blocks, out, ap.mp, ws, stream);
     return mfma_launch(c, q, H_q, L, scale, causal, mk, rot_blocks, out, ap.mp, ws, stream);
 }
 
@@ -1646,7 +1662,7 @@ extern "C" int rbq_kv_append_attn_decode(rbq_kv_cache* c, const void* k, const v
     st = attn_plan(&after, H_q, L, splits, &ap);
     if (st != RBQ_OK) return st;
     if (ap.ws_bytes > 0 && (ws == nullptr || ws_bytes < ap.ws_bytes)) return RBQ_EWORKSPACE;
-    const bool fused = n > 0 && !ap.tile && n <= kWaves &&
+    const bool fused = n > 0 && !ap.tile && !ap.prefill && n <= kWaves &&
                        (reinterpret_cast<uintptr_t>(k) & 7) == 0 &&
                        (reinterpret_cast<uintptr_t>(v) & 7) == 0;
     if (!fused) {

@@ -1,0 +1,733 @@
+// Prefill-length attention over the packed K4/V3 cache (asym_quantized_sdpa
+// on the quant_kv.py page with many query rows per kv head: a prompt chunk
+// of L tokens attending to the cache and to itself, causal at the offset) on
+// the gfx950 matrix cores, for bf16 caches of the default configuration.
+//
+// Decomposition: one workgroup of 8 wave64s per (b, kv head, block of 128
+// query rows, key split); wave w takes rows 16 w .. 16 w + 15 of the block,
+// lane l = 16 j + n row n.  The workgroup walks the split's 32-key tiles:
+// each tile is transferred once into LDS (direct-to-LDS, the next tile in
+// flight while one is computed), decoded once, and then used by all 128
+// rows, so the per-key work (unpacking, scaling) is spread over 128 rows
+// instead of the 8 of the decode kernel.
+//
+// Both products are computed transposed, so that each lane holds one query
+// row throughout (the softmax statistics, the probabilities and the output
+// accumulators of row n live in lanes n, n + 16, n + 32, n + 48):
+//   S^T = K Q^T: A = K codes of 16 keys (row = key), in place as fp16
+//     subnormals (masking nibble pairs of a packed word gives c 2^-24 or
+//     16 c 2^-24), B = the query (column = query row), hi and lo fp16 parts
+//     scaled by a power of two per row, dims permuted and scaled by 1 or 1/16
+//     to match the nibble masks.  One accumulator per 64-dim group g; the
+//     score of (key t, row r) is 2^(24 - E_r) sum_g s_{t,g} acc_g plus
+//     sum_g b_{t,g} sum_{d in g} q_{r,d} (one bf16 MFMA of the raw K bias
+//     words against exact limbs of the query's group sums).  Accumulator
+//     register i of lane (j, n) holds key 16 kb + 4 j + i of row n.
+//   O^T = V'^T P^T: B = P^T, whose k-slot e of lane (j, n) is the lane's own
+//     probability (kb = e / 4, i = e % 4), i.e. key 4 j + e (e < 4) or
+//     16 + 4 j + e - 4: no transposition of P.  A = V'^T, V' = s_{t,g} 2^F_g
+//     c_{t,d} in fp16, stored in LDS with its key rows in that same order
+//     and read by the transposing LDS read (ds_read_b64_tr_b16).  For bf16
+//     scales V' is exact (8 + 3 significant bits), with F_g a power of two
+//     per group, from the split's largest |scale| and |bias|, that keeps
+//     every V' and bias below 2^13 * 7 < 65504; the group bias enters as
+//     sum_t p_t b_{t,g} 2^F_g through one more MFMA.  P enters as fp16 hi +
+//     lo (two MFMAs), so P V' is exact up to fp32 accumulation.
+// Online softmax in base 2 per row, the reference maximum moved only when a
+// tile's maximum exceeds it by more than 8 (probabilities stay below 2^8).
+// With one split the workgroup normalises, rotates back and stores the
+// rows; with several it stores the records the merge kernel reads.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "rbq_common.h"
+#include "rbq_internal.h"
+
+namespace rbq {
+namespace {
+
+typedef _Float16 pf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 pf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 pbf16x8 __attribute__((ext_vector_type(8)));
+typedef float pf32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t pu32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t pu32x2 __attribute__((ext_vector_type(2)));
+typedef short ps16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned char plds_u8;
+
+constexpr int kPW = 8;                // waves per workgroup
+constexpr int kPT = 64 * kPW;         // threads
+constexpr int kPRows = 16 * kPW;      // query rows per workgroup
+constexpr int kPTile = 32;            // keys per tile
+constexpr int64_t kPGridYZ = 65535;   // workgroups per grid dimension y or z of one launch
+constexpr float kPLog2e = 1.44269504088896340736f;
+// One tile as the memory holds it (a raw buffer): K words (16-byte chunks
+// of a key permuted, see k_chunk), V words, K scales, K biases, V scales,
+// V biases.
+constexpr int kRK = 0, kRV = 4096, kRKs = 7168, kRKb = 7424, kRVs = 7680, kRVb = 7936;
+constexpr int kRawBytes = 8192;
+// Decoded V' rows: 672 bytes apart, rows 8-15 and 24-31 shifted by 128
+// bytes, so that the transposing reads of 32 lanes (rows 8 j' + e of two
+// lane groups j') fall on distinct banks
+constexpr int kVRow = 672;
+__host__ __device__ constexpr int v_off(int r) { return r * kVRow + ((r >> 3) & 1) * 128; }
+// LDS layout (bytes)
+constexpr int kOffV = 2 * kRawBytes;                      // V' [32 rows][kVRow], fp16
+constexpr int kOffKs = kOffV + kPTile * kVRow + 128;      // K scales, fp32 [4 groups][32 keys]
+constexpr int kOffVb = kOffKs + kGroups * kPTile * 4;     // V bias operand, fp16 [4 groups][32 rows]
+constexpr int kOffRot = kOffVb + kGroups * kPTile * 2;    // rotation blocks, fp32 [64][4][4]
+constexpr int kOffRed = kOffRot + kHeadDim * 16;          // group maxima [8 waves][4]
+constexpr int kPBytes = kOffRed + kPW * 4 * 4;
+static_assert(kPBytes <= 64 * 1024, "LDS of one workgroup");
+static_assert(kRecordFloats == 2 * 8 + 8 * kHeadDim, "split record layout");
+
+struct PArgs {
+    const uint16_t* q;
+    const uint32_t* kw;
+    const uint16_t* ks;
+    const uint16_t* kb;
+    const uint32_t* vw;
+    const uint16_t* vs;
+    const uint16_t* vb;
+    const float* rot;
+    float* out;
+    float* rec;
+    const void* mask;
+    int64_t msb, msh, msl;
+    uint32_t mask_bytes;
+    int64_t capacity;
+    int T, chunk, S, Hkv, n_rep, L, G, RB, RW, causal, round_rot;
+    int rw0, bh0;  // first row block and (b, kv head) of this launch (grid y and z)
+    float qscale;
+};
+
+__device__ __forceinline__ pf32x4 mfma_f16(pf16x8 a, pf16x8 b, pf32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ pf32x4 mfma_bf16(pu32x4 a, pu32x4 b, pf32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(pbf16x8, a),
+                                                     __builtin_bit_cast(pbf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t prsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// LDS transposing read of 8 bytes at byte offset `off`: lane i of each
+// 16-lane group gets element i & 3 of the 8 bytes addressed by lanes
+// 4 e + (i >> 2) of its group, as element e.
+__device__ __forceinline__ pu32x2 tr_read(const unsigned char* smem, uint32_t off) {
+    const ps16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) ps16x4*)((plds_u8*)smem + off));
+    return __builtin_bit_cast(pu32x2, v);
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_ld(const unsigned char* smem, uint32_t off) {
+    return *(const __attribute__((address_space(3))) T*)((const plds_u8*)smem + off);
+}
+template <typename T>
+__device__ __forceinline__ void lds_st(unsigned char* smem, uint32_t off, T v) {
+    *(__attribute__((address_space(3))) T*)((plds_u8*)smem + off) = v;
+}
+
+// max / sum over the 4 lanes n, n + 16, n + 32, n + 48 (one row)
+__device__ __forceinline__ float row_max4(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row_sum4(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// (fp16(p0 - h0), fp16(p1 - h1)) for hi2 = (h0, h1) the fp16 roundings of
+// p0, p1: fma(-h, 1, p) with h taken as fp16 and p as fp32, rounded once
+// (p - h is exact in fp32).  `one` holds 1.0f.
+__device__ __forceinline__ uint32_t lo_parts(uint32_t hi2, float p0, float p1, float one) {
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, -%1, %2, %3 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, -%1, %2, %4 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(r)
+        : "v"(hi2), "v"(one), "v"(p0), "v"(p1));
+    return r;
+}
+
+// 16-byte slot of K word chunk c (words 4c .. 4c+3) of tile key k in a raw
+// buffer: the chunks of a key permuted by (k >> 1) & 7, so that the 8-byte
+// reads of 32 lanes (16 keys x 2 halves of a chunk) hit distinct banks.
+__device__ __forceinline__ int k_chunk(int k, int c) { return 8 * k + (c ^ ((k >> 1) & 7)); }
+
+// Row of key k in the decoded V' tile: row 8 j + e holds key 4 j + e
+// (e < 4) or 16 + 4 j + e - 4 (e >= 4), the k-slot order of the P operand.
+__device__ __forceinline__ int v_row(int k) { return 8 * ((k & 15) >> 2) + (k & 3) + 4 * (k >> 4); }
+
+// Direct-to-LDS transfer of the tile at key t0 into raw buffer `buf` (lane l
+// of an instruction lands at offset + 16 l or 4 l): waves 0-3 a quarter of
+// the K words each, waves 4-6 a third of the V words, wave 7 the four
+// scale / bias arrays.  Keys past the buffer ranges read as zero.
+__device__ __forceinline__ void issue_tile(plds_u8* buf, int t0, int wave, int lane,
+                                           __amdgpu_buffer_rsrc_t kw_r, __amdgpu_buffer_rsrc_t vw_r,
+                                           const __amdgpu_buffer_rsrc_t m_r[4]) {
+    if (wave < 4) {
+        const int p = 64 * wave + lane;
+        const int k = p >> 3;
+        const int c = (p & 7) ^ ((k >> 1) & 7);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kw_r, buf + kRK + 1024 * wave, 16,
+                                                  (t0 + k) * 128 + 16 * c, 0, 0, 0);
+    } else if (wave < 7) {
+        const int m = wave - 4;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vw_r, buf + kRV + 1024 * m, 16,
+                                                  t0 * 96 + 16 * (64 * m + lane), 0, 0, 0);
+    } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(m_r[0], buf + kRKs, 4, t0 * 8 + 4 * lane, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(m_r[1], buf + kRKb, 4, t0 * 8 + 4 * lane, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(m_r[2], buf + kRVs, 4, t0 * 8 + 4 * lane, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(m_r[3], buf + kRVb, 4, t0 * 8 + 4 * lane, 0, 0, 0);
+    }
+}
+
+template <int MK>
+__global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_prefill_kernel(PArgs a) {
+    __shared__ __align__(16) unsigned char smem[kPBytes];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane >> 4, n = lane & 15;
+
+    // grid: x = key split, y = block of 128 query rows, z = (b, kv head)
+    const int split = blockIdx.x;
+    const int rw = a.rw0 + blockIdx.y;
+    const int bh = a.bh0 + blockIdx.z;
+    const int r0 = kPRows * rw;
+    const int T = a.T;
+    const int t_begin = split * a.chunk;
+    const int t_end = min(t_begin + a.chunk, T);
+    // keys past the last visible key of every row of the block are skipped
+    int t_lim = t_end;
+    if (a.causal) {
+        const int rlast = min(r0 + kPRows, a.G) - 1;
+        const int i0 = r0 % a.L, i1 = rlast % a.L;
+        const int imax = (rlast - r0 + 1 >= a.L || i1 < i0) ? a.L - 1 : i1;
+        t_lim = min(t_lim, T - a.L + imax + 1);
+    }
+    const int64_t row0 = (int64_t)bh * a.capacity;
+    const __amdgpu_buffer_rsrc_t kw_r = prsrc(a.kw + row0 * kKWords, (uint32_t)T * 128u);
+    const __amdgpu_buffer_rsrc_t vw_r = prsrc(a.vw + row0 * kVWords, (uint32_t)T * 96u);
+    __amdgpu_buffer_rsrc_t m_r[4];
+    m_r[0] = prsrc(a.ks + row0 * kGroups, (uint32_t)T * 8u);
+    m_r[1] = prsrc(a.kb + row0 * kGroups, (uint32_t)T * 8u);
+    m_r[2] = prsrc(a.vs + row0 * kGroups, (uint32_t)T * 8u);
+    m_r[3] = prsrc(a.vb + row0 * kGroups, (uint32_t)T * 8u);
+
+    // the first tile in flight during the set-up
+    if (t_begin < t_lim) issue_tile((plds_u8*)smem, t_begin, wave, lane, kw_r, vw_r, m_r);
+
+    // ---- the query row of this lane (dims 64 g + 16 j .. 64 g + 16 j + 15)
+    //      and the rotation blocks into LDS ----
+    const int R = r0 + 16 * wave + n;
+    const bool row_ok = R < a.G;
+    float x[4][16];
+    {
+        const uint16_t* qr = a.q + ((int64_t)bh * a.G + (row_ok ? R : 0)) * kHeadDim;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                if (row_ok) {
+                    load4<RBQ_BF16>(qr + 64 * g + 16 * j + 4 * q4, x[g] + 4 * q4);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[g][4 * q4 + e] = 0.f;
+                }
+            }
+    }
+    const bool rotated = a.rot != nullptr;
+    // (64 blocks of 16 floats: one float4 per thread of the first 256)
+    static_assert(kHeadDim <= kPT, "one float4 of the rotation blocks per thread");
+    if (rotated && tid < kHeadDim)
+        lds_st<pf32x4>(smem, kOffRot + 16 * tid, reinterpret_cast<const pf32x4*>(a.rot)[tid]);
+
+    // ---- F_g: the power of two that keeps the split's V scales and biases
+    //      of group g below 2^13 (over the keys this workgroup reads) ----
+    float vmx[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int t = t_begin + tid; t < t_lim; t += kPT) {
+        const uint2 s2 = *reinterpret_cast<const uint2*>(a.vs + (row0 + t) * kGroups);
+        const uint2 b2 = *reinterpret_cast<const uint2*>(a.vb + (row0 + t) * kGroups);
+        const uint32_t sw[4] = {s2.x, s2.x >> 16, s2.y, s2.y >> 16};
+        const uint32_t bw[4] = {b2.x, b2.x >> 16, b2.y, b2.y >> 16};
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            vmx[g] = fmaxf(vmx[g], fmaxf(fabsf(bf16_bits_to_f32(sw[g] & 0xFFFFu)),
+                                         fabsf(bf16_bits_to_f32(bw[g] & 0xFFFFu))));
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) vmx[g] = fmaxf(vmx[g], __shfl_xor(vmx[g], o));
+    }
+    if (lane == 0) lds_st<pf32x4>(smem, kOffRed + 16 * wave, (pf32x4){vmx[0], vmx[1], vmx[2], vmx[3]});
+    __syncthreads();  // rotation blocks and group maxima in LDS
+    float vunit[4], vinv[4];
+    {
+        float mx[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kPW; ++w) {
+            const pf32x4 v = lds_ld<pf32x4>(smem, kOffRed + 16 * w);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) mx[g] = fmaxf(mx[g], v[g]);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            int ex = 0;
+            if (mx[g] > 0.f) (void)frexpf(mx[g], &ex);  // mx < 2^ex
+            const int F = (mx[g] > 0.f) ? 13 - ex : 0;
+            vunit[g] = ldexpf(1.0f, F);
+            vinv[g] = ldexpf(1.0f, -F);
+        }
+    }
+
+    // ---- rotate, round (when the cache asks for it), scale by scale *
+    //      log2(e); E: the power of two that brings the row's largest |q|
+    //      into [2^14, 2^15); the group sums ----
+    float E_f;
+    pf16x8 qh[4][2], ql[4][2];
+    pu32x4 qb = {0u, 0u, 0u, 0u};
+    {
+        float mx = 0.f;
+        float gsum[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            gsum[g] = 0.f;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                float y[4];
+                if (rotated) {
+                    float Bm[16];
+                    const int blk = 16 * g + 4 * j + q4;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const pf32x4 v = lds_ld<pf32x4>(smem, kOffRot + 64 * blk + 16 * r);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) Bm[4 * r + e] = v[e];
+                    }
+                    rotate4(x[g] + 4 * q4, Bm, y);
+                    if (a.round_rot) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) y[e] = bf16_bits_to_f32(f32_to_bf16_bits(y[e]));
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) y[e] = x[g][4 * q4 + e];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float v = y[e] * a.qscale;
+                    x[g][4 * q4 + e] = v;
+                    mx = fmaxf(mx, fabsf(v));
+                    gsum[g] += v;
+                }
+            }
+        }
+        mx = row_max4(mx);
+        int ex = 0;
+        if (mx > 0.f) (void)frexpf(mx, &ex);
+        const int E = (mx > 0.f) ? 15 - ex : 0;
+        E_f = ldexpf(1.0f, 24 - E);
+        // score operands: word 8 g + 2 j + h2 of a key covers dims
+        // 64 g + 16 j + 8 h2 + 0..7; slot e takes dim kPerm[e] of those, times
+        // 1/16 where the nibble mask leaves 16 c
+        constexpr int kPerm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float xs = ldexpf(x[g][8 * h2 + kPerm[e]], E) * ((e & 2) ? 0.0625f : 1.0f);
+                    const _Float16 hi = (_Float16)xs;
+                    qh[g][h2][e] = hi;
+                    ql[g][h2][e] = (_Float16)(xs - (float)hi);
+                }
+        // bias operand: lane group j < 3 holds limb j of the 4 group sums
+        // (exact three-limb bf16 split) in k-slots 0-3
+        uint32_t lb[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float s = row_sum4(gsum[g]);
+            const uint32_t u = __float_as_uint(s);
+            const float hi = __uint_as_float(u & 0xFFFF0000u);
+            const uint32_t u2 = __float_as_uint(s - hi);
+            const float mid = __uint_as_float(u2 & 0xFFFF0000u);
+            lb[g] = (j == 0) ? u >> 16 : (j == 1) ? u2 >> 16 : (j == 2) ? f32_to_bf16_bits(s - hi - mid) : 0u;
+        }
+        qb = (pu32x4){lb[0] | lb[1] << 16, lb[2] | lb[3] << 16, 0u, 0u};
+    }
+    const float frow = E_f;
+    // causal visibility of the lane's row, and the smallest over the wave's rows
+    const int vis = (row_ok && a.causal) ? T - a.L + (R % a.L) + 1 : T;
+    int vis_min = row_ok ? vis : T;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) vis_min = min(vis_min, __shfl_xor(vis_min, o));
+    vis_min = __builtin_amdgcn_readfirstlane(vis_min);
+    const bool wave_live = r0 + 16 * wave < a.G;
+
+    // mask: byte offset of the lane's row (reads past the range return zero)
+    constexpr int kME = (MK == RBQ_MASK_BOOL) ? 1 : (MK == RBQ_MASK_ADD_F32) ? 4 : 2;
+    __amdgpu_buffer_rsrc_t mask_r;
+    uint32_t mrow = 0x80000000u;
+    if constexpr (MK != RBQ_MASK_NONE) {
+        mask_r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.mask), (short)0,
+                                                   (int)a.mask_bytes, 0x00020000);
+        if (row_ok) {
+            const int b = bh / a.Hkv;
+            const int h = (bh - b * a.Hkv) * a.n_rep + R / a.L;
+            mrow = (uint32_t)(((int64_t)b * a.msb + (int64_t)h * a.msh + (int64_t)(R % a.L) * a.msl) * kME);
+        }
+    }
+
+    pf32x4 O[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) O[t] = (pf32x4){0.f, 0.f, 0.f, 0.f};
+    pf32x4 Ob = {0.f, 0.f, 0.f, 0.f};
+    float m_ref = -INFINITY, thr = -INFINITY, l_part = 0.f;
+    const float one = 1.0f;
+    const pf32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    // this lane's transposing-read address in the V' tile: lane 4 e + q of a
+    // group reads row 8 j + e, columns 4 q .. 4 q + 3 of an output block
+    const uint32_t vrd = kOffV + v_off(8 * j + (n >> 2)) + 8 * (n & 3);
+
+    int buf = 0;
+    for (int t0 = t_begin; t0 < t_lim; t0 += kPTile, buf ^= 1) {
+        const uint32_t raw = buf * kRawBytes;
+        // this tile's transfers have landed (each wave waits for its own, the
+        // barrier for all); every wave is done with the previous tile
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+        // ---- decode: V' rows (thread = key t >> 4, dims 16 (t & 15) ..),
+        //      K scales to fp32, V bias operand ----
+        {
+            const int k = tid >> 4, p = tid & 15, g = p >> 2;
+            const int wi = (3 * p) >> 1, sh = 16 * (p & 1);
+            const uint32_t w0 = lds_ld<uint32_t>(smem, raw + kRV + 96 * k + 4 * wi);
+            const uint32_t w1 = lds_ld<uint32_t>(smem, raw + kRV + 96 * k + 4 * wi + 4);
+            const uint64_t bits = (((uint64_t)w1 << 32) | w0) >> sh;
+            const uint32_t sv = lds_ld<uint16_t>(smem, raw + kRVs + 8 * k + 2 * g);
+            const float sf = bf16_bits_to_f32(sv) * (g == 0 ? vunit[0] : g == 1 ? vunit[1] : g == 2 ? vunit[2] : vunit[3]);
+            uint32_t h[8];
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                const float c0 = (float)(uint32_t)((bits >> (6 * d)) & 7u);
+                const float c1 = (float)(uint32_t)((bits >> (6 * d + 3)) & 7u);
+                h[d] = __builtin_bit_cast(uint32_t, (pf16x2){(_Float16)(c0 * sf), (_Float16)(c1 * sf)});
+            }
+            const uint32_t dst = kOffV + v_off(v_row(k)) + 32 * p;
+            lds_st<pu32x4>(smem, dst, (pu32x4){h[0], h[1], h[2], h[3]});
+            lds_st<pu32x4>(smem, dst + 16, (pu32x4){h[4], h[5], h[6], h[7]});
+            if (tid < 128) {
+                const int kk = tid >> 2, gg = tid & 3;
+                const uint32_t s = lds_ld<uint16_t>(smem, raw + kRKs + 8 * kk + 2 * gg);
+                lds_st<float>(smem, kOffKs + 4 * (gg * kPTile + kk), bf16_bits_to_f32(s));
+            } else if (tid < 256) {
+                const int kk = (tid - 128) >> 2, gg = tid & 3;
+                const uint32_t b = lds_ld<uint16_t>(smem, raw + kRVb + 8 * kk + 2 * gg);
+                const float bu = bf16_bits_to_f32(b) *
+                                 (gg == 0 ? vunit[0] : gg == 1 ? vunit[1] : gg == 2 ? vunit[2] : vunit[3]);
+                lds_st<uint16_t>(smem, kOffVb + 2 * (gg * kPTile + v_row(kk)),
+                                 __builtin_bit_cast(uint16_t, (_Float16)bu));
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // LDS only
+        // the next tile into the other raw buffer (the previous tile's, which
+        // every wave finished before the barrier at the top)
+        if (t0 + kPTile < t_lim)
+            issue_tile((plds_u8*)smem + (buf ^ 1) * kRawBytes, t0 + kPTile, wave, lane, kw_r, vw_r, m_r);
+        if (!wave_live) continue;
+
+        // mask values of the lane's row for keys t0 + 16 kb + 4 j + i
+        uint32_t mv[2][4];
+        if constexpr (MK != RBQ_MASK_NONE) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t off = mrow + (uint32_t)(t0 + 16 * kb + 4 * j + i) * kME;
+                    if constexpr (MK == RBQ_MASK_BOOL)
+                        mv[kb][i] = __builtin_amdgcn_raw_buffer_load_b8(mask_r, off, 0, 0);
+                    else if constexpr (MK == RBQ_MASK_ADD_F32)
+                        mv[kb][i] = __builtin_amdgcn_raw_buffer_load_b32(mask_r, off, 0, 0);
+                    else
+                        mv[kb][i] = __builtin_amdgcn_raw_buffer_load_b16(mask_r, off, 0, 0);
+                }
+        }
+
+        // ---- scores S^T: register i of lane (j, n) = key 16 kb + 4 j + i, row n ----
+        float sc[2][4];
+        const bool full = t0 + kPTile <= t_end && t0 + kPTile <= vis_min;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int key = 16 * kb + n;
+            pf32x4 acc[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const pu32x2 w2 = lds_ld<pu32x2>(smem, raw + kRK + 16 * k_chunk(key, 2 * g + (j >> 1)) + 8 * (j & 1));
+                acc[g] = zero4;
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const uint32_t w = w2[h2];
+                    const uint32_t w8 = w >> 8;
+                    const pu32x4 kv = {w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u};
+                    const pf16x8 kop = __builtin_bit_cast(pf16x8, kv);
+                    acc[g] = mfma_f16(kop, qh[g][h2], acc[g]);
+                    acc[g] = mfma_f16(kop, ql[g][h2], acc[g]);
+                }
+            }
+            const pu32x2 kbw = lds_ld<pu32x2>(smem, raw + kRKb + 8 * key);
+            const pf32x4 cb = mfma_bf16((pu32x4){kbw[0], kbw[1], 0u, 0u}, qb, zero4);
+            pf32x4 s4[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) s4[g] = lds_ld<pf32x4>(smem, kOffKs + 4 * (g * kPTile + 16 * kb + 4 * j));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float t = s4[0][i] * acc[0][i];
+                t = fmaf(s4[1][i], acc[1][i], t);
+                t = fmaf(s4[2][i], acc[2][i], t);
+                t = fmaf(s4[3][i], acc[3][i], t);
+                float s = fmaf(t, frow, cb[i]);
+                if constexpr (MK == RBQ_MASK_BOOL) {
+                    if (mv[kb][i] == 0u) s = -INFINITY;
+                } else if constexpr (MK == RBQ_MASK_ADD_F32) {
+                    s = fmaf(__uint_as_float(mv[kb][i]), kPLog2e, s);
+                } else if constexpr (MK == RBQ_MASK_ADD_DTYPE) {
+                    s = fmaf(bf16_bits_to_f32(mv[kb][i]), kPLog2e, s);
+                }
+                sc[kb][i] = s;
+            }
+        }
+        // keys past the split or past the row's last visible key, only in a
+        // tile that reaches them
+        if (__builtin_expect(!full, 0)) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tk = t0 + 16 * kb + 4 * j + i;
+                    if (!(tk < t_end && tk < vis)) sc[kb][i] = -INFINITY;
+                }
+        }
+
+        // ---- online softmax of row n (base 2; the reference moves only when
+        //      the tile's maximum exceeds it by more than 8) ----
+        float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        mx = row_max4(mx);
+        const bool need = mx > thr;
+        if (__any(need)) {
+            float al = 1.0f;
+            if (need) {
+                al = __builtin_amdgcn_exp2f(m_ref - mx);  // 0 before the first key
+                m_ref = mx;
+                thr = mx + 8.0f;
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) O[t][i] *= al;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Ob[i] *= al;
+            l_part *= al;
+        }
+        const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
+        float p[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[kb][i] = __builtin_amdgcn_exp2f(sc[kb][i] - mu);
+                l_part += p[kb][i];
+            }
+        // P^T operand: k-slot e = (kb e / 4, register e % 4), fp16 hi + lo
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+                const float p0 = p[kb][2 * q2], p1 = p[kb][2 * q2 + 1];
+                const uint32_t hi2 = __builtin_bit_cast(uint32_t, (pf16x2){(_Float16)p0, (_Float16)p1});
+                hw[2 * kb + q2] = hi2;
+                lw[2 * kb + q2] = lo_parts(hi2, p0, p1, one);
+            }
+        const pf16x8 ph = __builtin_bit_cast(pf16x8, (pu32x4){hw[0], hw[1], hw[2], hw[3]});
+        const pf16x8 pl = __builtin_bit_cast(pf16x8, (pu32x4){lw[0], lw[1], lw[2], lw[3]});
+
+        // ---- O^T += V'^T P^T (register i of block t: dim 16 t + 4 j + i) ----
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const pu32x2 v0 = tr_read(smem, vrd + 32 * t);
+            const pu32x2 v1 = tr_read(smem, vrd + 32 * t + 4 * kVRow);
+            const pf16x8 vop = __builtin_bit_cast(pf16x8, (pu32x4){v0[0], v0[1], v1[0], v1[1]});
+            O[t] = mfma_f16(vop, ph, O[t]);
+            O[t] = mfma_f16(vop, pl, O[t]);
+        }
+        {
+            // group biases: A row g < 4 = b_{key, g} 2^F_g over the k-slots
+            pu32x4 vb4 = {0u, 0u, 0u, 0u};
+            if (n < 4) vb4 = lds_ld<pu32x4>(smem, kOffVb + 2 * (n * kPTile + 8 * j));
+            const pf16x8 vbop = __builtin_bit_cast(pf16x8, vb4);
+            Ob = mfma_f16(vbop, ph, Ob);
+            Ob = mfma_f16(vbop, pl, Ob);
+        }
+    }
+    // no transfer into LDS in flight past the loop
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+    // ---- epilogue: row sums, group biases (register g of lanes j = 0) ----
+    const float l = row_sum4(l_part);
+    float obg[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) obg[g] = row_sum4(Ob[g]);
+    if (!row_ok) return;
+    if (a.S == 1) {
+        const float inv = 1.0f / l;
+        // a boolean mask dropped every key of the row: the mean of its keys
+        const bool uniform = MK == RBQ_MASK_BOOL && l == 0.f;
+        float* orow = a.out + ((int64_t)bh * a.G + R) * kHeadDim;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int g = t >> 2;
+            float y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = (O[t][i] + obg[g]) * vinv[g] * inv;
+            if (uniform) {
+                const int nv = a.causal ? T - a.L + (R % a.L) + 1 : T;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    y[i] = value_column_mean<RBQ_BF16>(a.vw, a.vs, a.vb, row0, nv, 16 * t + 4 * j + i,
+                                                       kVBits, kVWords, kGroups, kGroup);
+            }
+            float z[4] = {y[0], y[1], y[2], y[3]};
+            if (rotated) {
+                float Bm[16];
+                const int blk = 4 * t + j;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const pf32x4 v = lds_ld<pf32x4>(smem, kOffRot + 64 * blk + 16 * r);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Bm[4 * r + e] = v[e];
+                }
+                unrotate4(y, Bm, z);
+            }
+            *reinterpret_cast<float4*>(orow + 16 * t + 4 * j) = make_float4(z[0], z[1], z[2], z[3]);
+        }
+        return;
+    }
+    // this split's record of the lane's row (block of 8 rows R >> 3, row R & 7)
+    float* rec = a.rec + ((int64_t)(bh * a.RB + (R >> 3)) * a.S + split) * kRecordFloats;
+    const int ri = R & 7;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        const int g = t >> 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rec[16 + (16 * t + 4 * j + i) * 8 + ri] = (O[t][i] + obg[g]) * vinv[g];
+    }
+    if (j == 0) *reinterpret_cast<float2*>(rec + 2 * ri) = make_float2(m_ref, l);
+}
+
+}  // namespace
+
+// ---- host side ----
+
+int prefill_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, MfmaPlan* p) {
+    const int64_t G = (int64_t)(H_q / c->H_kv) * L;
+    const int64_t RB = (G + 7) / 8;                 // blocks of 8 rows (the records)
+    const int64_t RW = (G + kPRows - 1) / kPRows;   // blocks of 128 rows (the workgroups)
+    const int64_t T = c->offset;
+    const int64_t units = (int64_t)c->B * c->H_kv * RW;
+    int64_t S = splits;
+    if (S == 0) {
+        S = (256 + units - 1) / units;  // about one workgroup per compute unit
+        const int64_t max_s = (T + 8 * kPTile - 1) / (8 * kPTile);
+        if (S > max_s) S = max_s;
+    }
+    if (S < 1) S = 1;
+    int64_t chunk = (T + S - 1) / S;
+    chunk = (chunk + kPTile - 1) / kPTile * kPTile;
+    S = (T + chunk - 1) / chunk;
+    const int64_t rec_units = (int64_t)c->B * c->H_kv * RB;
+    if (units * S > 0x7FFFFFFF || rec_units * S > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
+    // the merge kernel's one launch: at most 2^32 - 1 work-items along x
+    if (S > 1 && rec_units * 8 * 512 > 0xFFFFFFFFll) return RBQ_EUNSUPPORTED;
+    // 32-bit buffer offsets, up to one tile past T
+    if ((T + kPTile) * (int64_t)(kKWords * 4) > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
+    p->S = (int)S;
+    p->RB = (int)RB;
+    p->chunk = chunk;
+    p->ws_bytes = (S == 1) ? 0 : (size_t)rec_units * S * kRecordFloats * sizeof(float);
+    return RBQ_OK;
+}
+
+int prefill_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, float scale,
+                   int32_t causal, const AttnMask& mk, const float* rot_blocks, float* out,
+                   const MfmaPlan& p, void* ws, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    PArgs a;
+    a.q = (const uint16_t*)q;
+    a.kw = c->k_words;
+    a.ks = (const uint16_t*)c->k_scales;
+    a.kb = (const uint16_t*)c->k_biases;
+    a.vw = c->v_words;
+    a.vs = (const uint16_t*)c->v_scales;
+    a.vb = (const uint16_t*)c->v_biases;
+    a.rot = rot_blocks;
+    a.out = out;
+    a.rec = (float*)ws;
+    a.mask = mk.ptr;
+    a.msb = mk.sb;
+    a.msh = mk.sh;
+    a.msl = mk.sl;
+    a.mask_bytes = mk.bytes;
+    a.capacity = c->capacity;
+    a.T = (int)c->offset;
+    a.chunk = (int)p.chunk;
+    a.S = p.S;
+    a.Hkv = c->H_kv;
+    a.n_rep = H_q / c->H_kv;
+    a.L = L;
+    a.G = a.n_rep * L;
+    a.RB = p.RB;
+    a.RW = (a.G + kPRows - 1) / kPRows;
+    a.causal = causal ? 1 : 0;
+    a.round_rot = (c->flags & RBQ_FLAG_ROUND_ROTATED) ? 1 : 0;
+    a.qscale = scale * kPLog2e;
+    const int64_t BH = (int64_t)c->B * c->H_kv;
+    const int mt = mk.ptr == nullptr ? RBQ_MASK_NONE : mk.type;
+    auto launch = [&](auto kernel) {
+        for (int64_t bh0 = 0; bh0 < BH; bh0 += kPGridYZ)
+            for (int64_t rw0 = 0; rw0 < a.RW; rw0 += kPGridYZ) {
+                a.bh0 = (int)bh0;
+                a.rw0 = (int)rw0;
+                const dim3 grid((unsigned)p.S, (unsigned)std::min<int64_t>(kPGridYZ, a.RW - rw0),
+                                (unsigned)std::min<int64_t>(kPGridYZ, BH - bh0));
+                hipLaunchKernelGGL(kernel, grid, dim3(kPT), 0, s, a);
+            }
+    };
+    if (mt == RBQ_MASK_NONE) launch(attn_prefill_kernel<RBQ_MASK_NONE>);
+    else if (mt == RBQ_MASK_BOOL) launch(attn_prefill_kernel<RBQ_MASK_BOOL>);
+    else if (mt == RBQ_MASK_ADD_F32) launch(attn_prefill_kernel<RBQ_MASK_ADD_F32>);
+    else launch(attn_prefill_kernel<RBQ_MASK_ADD_DTYPE>);
+    if (p.S > 1) merge_launch(c, a.rec, rot_blocks, out, p.S, p.RB, a.n_rep, L, a.causal, mt, stream);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        set_hip_error((int)e);
+        return RBQ_EHIP;
+    }
+    return RBQ_OK;
+}
+
+}  // namespace rbq

@@ -70,6 +70,26 @@ struct MfmaPlan {
 };
 int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, MfmaPlan* p);
 
+// Split record of the attention kernels of the default configuration, one
+// per (b, kv head, block of 8 query rows, key split): (m, l) of the 8 rows
+// (m the row's reference score in base 2, l its sum of 2^(score - m)), then
+// the unnormalised output column-major [256 columns][8 rows].
+constexpr int kRecordFloats = 2 * 8 + 8 * kHeadDim;
+// The merge of the records of a call with S > 1 splits (RB blocks of 8 rows
+// per kv head): normalisation, inverse rotation, output rows; mask_type
+// RBQ_MASK_BOOL: rows without a kept key take the mean of their keys' values.
+void merge_launch(const rbq_kv_cache* c, const float* rec, const float* rot_blocks, float* out,
+                  int S, int RB, int n_rep, int L, int causal, int mask_type, void* stream);
+
+// Prefill-length attention of the default configuration with bf16 caches
+// (blocks of 128 query rows per kv head sharing each decoded tile): used from
+// kPrefillMinRows query rows per kv head.
+constexpr int64_t kPrefillMinRows = 96;
+int prefill_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, MfmaPlan* p);
+int prefill_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, float scale,
+                   int32_t causal, const AttnMask& mk, const float* rot_blocks, float* out,
+                   const MfmaPlan& p, void* ws, void* stream);
+
 // Launch plan of the general tile attention (every configuration, any number
 // of query rows): waves per workgroup (16 query rows each: 1 up to 16 rows
 // per kv head, else 4), key splits, row blocks, and the workspace of the

@@ -38,7 +38,7 @@ def test_host_code_under_asan_and_ubsan(tmp_path):
     # the HIP sources with each sanitizer flag for the host pass only (the
     # device code is built as usual; the driver runs with no visible GPU)
     host_san = [x for f in SAN for x in ("-Xarch_host", f)]
-    for src in ("rbq_append.hip", "rbq_attn_mfma.hip", "rbq_attn_tile.hip"):
+    for src in ("rbq_append.hip", "rbq_attn_mfma.hip", "rbq_attn_prefill.hip", "rbq_attn_tile.hip"):
         o = str(tmp_path / (src + ".o"))
         _run([HIPCC, "--offload-arch=gfx950", "-std=c++17", "-O1", "-g", *host_san, *inc,
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-c",
