@@ -56,7 +56,8 @@ typedef uint32_t pu32x2 __attribute__((ext_vector_type(2)));
 typedef short ps16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char plds_u8;
 
-constexpr int kPW = 8;                // waves per workgroup
+constexpr int kPW = 8;                // waves per workgroup (4 or 8)
+static_assert(kPW == 4 || kPW == 8, "4 or 8 waves");
 constexpr int kPT = 64 * kPW;         // threads
 constexpr int kPRows = 16 * kPW;      // query rows per workgroup
 constexpr int kPTile = 32;            // keys per tile
@@ -72,14 +73,18 @@ constexpr int kRawBytes = 8192;
 // lane groups j') fall on distinct banks
 constexpr int kVRow = 672;
 __host__ __device__ constexpr int v_off(int r) { return r * kVRow + ((r >> 3) & 1) * 128; }
-// LDS layout (bytes)
-constexpr int kOffV = 2 * kRawBytes;                      // V' [32 rows][kVRow], fp16
-constexpr int kOffKs = kOffV + kPTile * kVRow + 128;      // K scales, fp32 [4 groups][32 keys]
-constexpr int kOffVb = kOffKs + kGroups * kPTile * 4;     // V bias operand, fp16 [4 groups][32 rows]
-constexpr int kOffRot = kOffVb + kGroups * kPTile * 2;    // rotation blocks, fp32 [64][4][4]
+// LDS layout (bytes): three raw tile buffers (tile i + 2 in flight while
+// tile i + 1 is decoded and tile i computed), two decoded tiles
+constexpr int kNRaw = 3;
+constexpr int kDecBytes = kPTile * kVRow + 128;           // V' [32 rows], fp16 (rows at v_off)
+constexpr int kOffV = kNRaw * kRawBytes;                  // 2 x V'
+constexpr int kOffKs = kOffV + 2 * kDecBytes;             // 2 x K scales, fp32 [4 groups][32 keys]
+constexpr int kOffVb = kOffKs + 2 * kGroups * kPTile * 4; // 2 x V bias operand, fp16 [4 groups][32 rows]
+constexpr int kOffRot = kOffVb + 2 * kGroups * kPTile * 2; // rotation blocks, fp32 [64][4][4]
 constexpr int kOffRed = kOffRot + kHeadDim * 16;          // group maxima [8 waves][4]
-constexpr int kPBytes = kOffRed + kPW * 4 * 4;
-static_assert(kPBytes <= 64 * 1024, "LDS of one workgroup");
+constexpr int kOffUnit = kOffRed + 8 * 4 * 4;            // 2^F_g, then 2^-F_g
+constexpr int kPBytes = kOffUnit + 8 * 4;
+static_assert(kPBytes <= 160 * 1024, "LDS of one compute unit");
 static_assert(kRecordFloats == 2 * 8 + 8 * kHeadDim, "split record layout");
 
 struct PArgs {
@@ -169,27 +174,31 @@ __device__ __forceinline__ int k_chunk(int k, int c) { return 8 * k + (c ^ ((k >
 __device__ __forceinline__ int v_row(int k) { return 8 * ((k & 15) >> 2) + (k & 3) + 4 * (k >> 4); }
 
 // Direct-to-LDS transfer of the tile at key t0 into raw buffer `buf` (lane l
-// of an instruction lands at offset + 16 l or 4 l): waves 0-3 a quarter of
-// the K words each, waves 4-6 a third of the V words, wave 7 the four
-// scale / bias arrays.  Keys past the buffer ranges read as zero.
+// of an instruction lands at offset + 16 l or 4 l): 11 instructions, wave w
+// issuing numbers w, w + kPW, ...: 0-3 a quarter of the K words each, 4-6 a
+// third of the V words, 7-10 the four scale / bias arrays.  Keys past the
+// buffer ranges read as zero.
 __device__ __forceinline__ void issue_tile(plds_u8* buf, int t0, int wave, int lane,
                                            __amdgpu_buffer_rsrc_t kw_r, __amdgpu_buffer_rsrc_t vw_r,
                                            const __amdgpu_buffer_rsrc_t m_r[4]) {
-    if (wave < 4) {
-        const int p = 64 * wave + lane;
-        const int k = p >> 3;
-        const int c = (p & 7) ^ ((k >> 1) & 7);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kw_r, buf + kRK + 1024 * wave, 16,
-                                                  (t0 + k) * 128 + 16 * c, 0, 0, 0);
-    } else if (wave < 7) {
-        const int m = wave - 4;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vw_r, buf + kRV + 1024 * m, 16,
-                                                  t0 * 96 + 16 * (64 * m + lane), 0, 0, 0);
-    } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(m_r[0], buf + kRKs, 4, t0 * 8 + 4 * lane, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(m_r[1], buf + kRKb, 4, t0 * 8 + 4 * lane, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(m_r[2], buf + kRVs, 4, t0 * 8 + 4 * lane, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(m_r[3], buf + kRVb, 4, t0 * 8 + 4 * lane, 0, 0, 0);
+#pragma unroll
+    for (int x = 0; x < 11; x += kPW) {
+        const int idx = x + wave;
+        if (idx < 4) {
+            const int p = 64 * idx + lane;
+            const int k = p >> 3;
+            const int c = (p & 7) ^ ((k >> 1) & 7);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kw_r, buf + kRK + 1024 * idx, 16,
+                                                      (t0 + k) * 128 + 16 * c, 0, 0, 0);
+        } else if (idx < 7) {
+            const int m = idx - 4;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vw_r, buf + kRV + 1024 * m, 16,
+                                                      t0 * 96 + 16 * (64 * m + lane), 0, 0, 0);
+        } else if (idx < 11) {
+            const int m = idx - 7;
+            const uint32_t dst = (m == 0) ? kRKs : (m == 1) ? kRKb : (m == 2) ? kRVs : kRVb;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(m_r[m], buf + dst, 4, t0 * 8 + 4 * lane, 0, 0, 0);
+        }
     }
 }
 
@@ -274,7 +283,6 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     if (lane == 0) lds_st<pf32x4>(smem, kOffRed + 16 * wave, (pf32x4){vmx[0], vmx[1], vmx[2], vmx[3]});
     __syncthreads();  // rotation blocks and group maxima in LDS
-    float vunit[4], vinv[4];
     {
         float mx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -288,8 +296,10 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             int ex = 0;
             if (mx[g] > 0.f) (void)frexpf(mx[g], &ex);  // mx < 2^ex
             const int F = (mx[g] > 0.f) ? 13 - ex : 0;
-            vunit[g] = ldexpf(1.0f, F);
-            vinv[g] = ldexpf(1.0f, -F);
+            if (tid == g) {
+                lds_st<float>(smem, kOffUnit + 4 * g, ldexpf(1.0f, F));
+                lds_st<float>(smem, kOffUnit + 16 + 4 * g, ldexpf(1.0f, -F));
+            }
         }
     }
 
@@ -403,23 +413,20 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // group reads row 8 j + e, columns 4 q .. 4 q + 3 of an output block
     const uint32_t vrd = kOffV + v_off(8 * j + (n >> 2)) + 8 * (n & 3);
 
-    int buf = 0;
-    for (int t0 = t_begin; t0 < t_lim; t0 += kPTile, buf ^= 1) {
-        const uint32_t raw = buf * kRawBytes;
-        // this tile's transfers have landed (each wave waits for its own, the
-        // barrier for all); every wave is done with the previous tile
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
-        // ---- decode: V' rows (thread = key t >> 4, dims 16 (t & 15) ..),
-        //      K scales to fp32, V bias operand ----
-        {
-            const int k = tid >> 4, p = tid & 15, g = p >> 2;
+    // decode of the tile in raw buffer `raw` into decoded buffer `db`: V' rows
+    // (item = key i >> 4, dims 16 (i & 15) .., 512 items over the threads), K
+    // scales to fp32 (waves 0-1), V bias operand (waves 2-3)
+    auto decode_tile = [&](const unsigned char* raw, const int db) __attribute__((always_inline)) {
+#pragma unroll
+        for (int item = tid; item < 512; item += kPT) {
+            const int k = item >> 4, p = item & 15, g = p >> 2;
             const int wi = (3 * p) >> 1, sh = 16 * (p & 1);
-            const uint32_t w0 = lds_ld<uint32_t>(smem, raw + kRV + 96 * k + 4 * wi);
-            const uint32_t w1 = lds_ld<uint32_t>(smem, raw + kRV + 96 * k + 4 * wi + 4);
+            const uint32_t w0 = lds_ld<uint32_t>(raw, kRV + 96 * k + 4 * wi);
+            const uint32_t w1 = lds_ld<uint32_t>(raw, kRV + 96 * k + 4 * wi + 4);
             const uint64_t bits = (((uint64_t)w1 << 32) | w0) >> sh;
-            const uint32_t sv = lds_ld<uint16_t>(smem, raw + kRVs + 8 * k + 2 * g);
-            const float sf = bf16_bits_to_f32(sv) * (g == 0 ? vunit[0] : g == 1 ? vunit[1] : g == 2 ? vunit[2] : vunit[3]);
+            const uint32_t sv = lds_ld<uint16_t>(raw, kRVs + 8 * k + 2 * g);
+            const float sf = bf16_bits_to_f32(sv) * lds_ld<float>(smem, kOffUnit + 4 * g);
+            // code times scale times 2^F_g: exact in fp32, then in fp16
             uint32_t h[8];
 #pragma unroll
             for (int d = 0; d < 8; ++d) {
@@ -427,28 +434,47 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const float c1 = (float)(uint32_t)((bits >> (6 * d + 3)) & 7u);
                 h[d] = __builtin_bit_cast(uint32_t, (pf16x2){(_Float16)(c0 * sf), (_Float16)(c1 * sf)});
             }
-            const uint32_t dst = kOffV + v_off(v_row(k)) + 32 * p;
+            const uint32_t dst = kOffV + db * kDecBytes + v_off(v_row(k)) + 32 * p;
             lds_st<pu32x4>(smem, dst, (pu32x4){h[0], h[1], h[2], h[3]});
             lds_st<pu32x4>(smem, dst + 16, (pu32x4){h[4], h[5], h[6], h[7]});
-            if (tid < 128) {
-                const int kk = tid >> 2, gg = tid & 3;
-                const uint32_t s = lds_ld<uint16_t>(smem, raw + kRKs + 8 * kk + 2 * gg);
-                lds_st<float>(smem, kOffKs + 4 * (gg * kPTile + kk), bf16_bits_to_f32(s));
-            } else if (tid < 256) {
-                const int kk = (tid - 128) >> 2, gg = tid & 3;
-                const uint32_t b = lds_ld<uint16_t>(smem, raw + kRVb + 8 * kk + 2 * gg);
-                const float bu = bf16_bits_to_f32(b) *
-                                 (gg == 0 ? vunit[0] : gg == 1 ? vunit[1] : gg == 2 ? vunit[2] : vunit[3]);
-                lds_st<uint16_t>(smem, kOffVb + 2 * (gg * kPTile + v_row(kk)),
-                                 __builtin_bit_cast(uint16_t, (_Float16)bu));
-            }
         }
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // LDS only
-        // the next tile into the other raw buffer (the previous tile's, which
-        // every wave finished before the barrier at the top)
-        if (t0 + kPTile < t_lim)
-            issue_tile((plds_u8*)smem + (buf ^ 1) * kRawBytes, t0 + kPTile, wave, lane, kw_r, vw_r, m_r);
-        if (!wave_live) continue;
+        if (wave < 2) {
+            const int kk = tid >> 2, gg = tid & 3;
+            const uint32_t sk = lds_ld<uint16_t>(raw, kRKs + 8 * kk + 2 * gg);
+            lds_st<float>(smem, kOffKs + db * 512 + 4 * (gg * kPTile + kk), bf16_bits_to_f32(sk));
+        } else if (wave < 4) {
+            const int kk = (tid - 128) >> 2, gg = tid & 3;
+            const uint32_t b = lds_ld<uint16_t>(raw, kRVb + 8 * kk + 2 * gg);
+            const float bu = bf16_bits_to_f32(b) * lds_ld<float>(smem, kOffUnit + 4 * gg);
+            lds_st<uint16_t>(smem, kOffVb + db * 256 + 2 * (gg * kPTile + v_row(kk)),
+                             __builtin_bit_cast(uint16_t, (_Float16)bu));
+        }
+    };
+    const int n_tiles = (t_lim > t_begin) ? (t_lim - t_begin + kPTile - 1) / kPTile : 0;
+    // the second tile in flight too; the first decoded before the loop
+    if (n_tiles > 1)
+        issue_tile((plds_u8*)smem + kRawBytes, t_begin + kPTile, wave, lane, kw_r, vw_r, m_r);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (n_tiles > 0) decode_tile(smem, 0);
+
+    for (int it = 0; it < n_tiles; ++it) {
+        // raw buffer it % 3 holds tile it, (it + 1) % 3 tile it + 1 (landed at
+        // the barrier), (it + 2) % 3 receives tile it + 2
+        const unsigned char* raw = smem + (it % kNRaw) * kRawBytes;
+        const unsigned char* raw_next = smem + ((it + 1) % kNRaw) * kRawBytes;
+        plds_u8* raw_dma = (plds_u8*)smem + ((it + 2) % kNRaw) * kRawBytes;
+        const int t0 = t_begin + it * kPTile;
+        const int db = it & 1;
+        // tile it + 1 has landed (each wave waits for its own transfers, the
+        // barrier for all), tile it is decoded, every wave is done with tile
+        // it - 1 (its raw and decoded buffers are free)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const bool dec_next = it + 1 < n_tiles;
+        if (it + 2 < n_tiles) issue_tile(raw_dma, t0 + 2 * kPTile, wave, lane, kw_r, vw_r, m_r);
+        if (!wave_live) {
+            if (dec_next) decode_tile(raw_next, db ^ 1);
+            continue;
+        }
 
         // mask values of the lane's row for keys t0 + 16 kb + 4 j + i
         uint32_t mv[2][4];
@@ -476,7 +502,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             pf32x4 acc[4];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const pu32x2 w2 = lds_ld<pu32x2>(smem, raw + kRK + 16 * k_chunk(key, 2 * g + (j >> 1)) + 8 * (j & 1));
+                const pu32x2 w2 = lds_ld<pu32x2>(raw, kRK + 16 * k_chunk(key, 2 * g + (j >> 1)) + 8 * (j & 1));
                 acc[g] = zero4;
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) {
@@ -488,11 +514,14 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     acc[g] = mfma_f16(kop, ql[g][h2], acc[g]);
                 }
             }
-            const pu32x2 kbw = lds_ld<pu32x2>(smem, raw + kRKb + 8 * key);
+            const pu32x2 kbw = lds_ld<pu32x2>(raw, kRKb + 8 * key);
             const pf32x4 cb = mfma_bf16((pu32x4){kbw[0], kbw[1], 0u, 0u}, qb, zero4);
+            // the next tile's decode while the matrix cores work on these
+            // products (its buffers are not read by this tile)
+            if (kb == 1 && dec_next) decode_tile(raw_next, db ^ 1);
             pf32x4 s4[4];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) s4[g] = lds_ld<pf32x4>(smem, kOffKs + 4 * (g * kPTile + 16 * kb + 4 * j));
+            for (int g = 0; g < 4; ++g) s4[g] = lds_ld<pf32x4>(smem, kOffKs + db * 512 + 4 * (g * kPTile + 16 * kb + 4 * j));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float t = s4[0][i] * acc[0][i];
@@ -567,10 +596,11 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const pf16x8 pl = __builtin_bit_cast(pf16x8, (pu32x4){lw[0], lw[1], lw[2], lw[3]});
 
         // ---- O^T += V'^T P^T (register i of block t: dim 16 t + 4 j + i) ----
+        const uint32_t vdb = vrd + db * kDecBytes;
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            const pu32x2 v0 = tr_read(smem, vrd + 32 * t);
-            const pu32x2 v1 = tr_read(smem, vrd + 32 * t + 4 * kVRow);
+            const pu32x2 v0 = tr_read(smem, vdb + 32 * t);
+            const pu32x2 v1 = tr_read(smem, vdb + 32 * t + 4 * kVRow);
             const pf16x8 vop = __builtin_bit_cast(pf16x8, (pu32x4){v0[0], v0[1], v1[0], v1[1]});
             O[t] = mfma_f16(vop, ph, O[t]);
             O[t] = mfma_f16(vop, pl, O[t]);
@@ -578,7 +608,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         {
             // group biases: A row g < 4 = b_{key, g} 2^F_g over the k-slots
             pu32x4 vb4 = {0u, 0u, 0u, 0u};
-            if (n < 4) vb4 = lds_ld<pu32x4>(smem, kOffVb + 2 * (n * kPTile + 8 * j));
+            if (n < 4) vb4 = lds_ld<pu32x4>(smem, kOffVb + db * 256 + 2 * (n * kPTile + 8 * j));
             const pf16x8 vbop = __builtin_bit_cast(pf16x8, vb4);
             Ob = mfma_f16(vbop, ph, Ob);
             Ob = mfma_f16(vbop, pl, Ob);
@@ -593,6 +623,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int g = 0; g < 4; ++g) obg[g] = row_sum4(Ob[g]);
     if (!row_ok) return;
+    const pf32x4 vinv = lds_ld<pf32x4>(smem, kOffUnit + 16);
     if (a.S == 1) {
         const float inv = 1.0f / l;
         // a boolean mask dropped every key of the row: the mean of its keys
