@@ -564,8 +564,8 @@ def prefill(rbq, W, dev, rot, n_calls: int = 10, head_dim: int = 256) -> dict:
     2 kv heads, head_dim 256, bf16, K4/V3 group 64; a cache of 8192 tokens,
     a chunk of L = 2048 new tokens appended (rotated, quantized, packed), then
     the fused attention of the chunk's 2048 query rows per head over the
-    10240 cached tokens with the causal mask at the offset (the dedicated
-    kernel's 8-row blocks).  With ``head_dim=128`` the cache is head_dim 128,
+    10240 cached tokens with the causal mask at the offset (the prefill
+    kernel's 128-row blocks).  With ``head_dim=128`` the cache is head_dim 128,
     group 64, K4/V4, two-sided rotation (the tile kernel's 64-row blocks).
     Algorithmic flops: 4 * head_dim per (query row, visible key) (q.k and
     p.v, multiply-add = 2)."""
@@ -612,8 +612,8 @@ def prefill(rbq, W, dev, rot, n_calls: int = 10, head_dim: int = 256) -> dict:
     tfs = flops / (us * 1e-6) / 1e12
     return {
         "what": (f"prefill chunk: {L} new tokens over {T0} cached (T={T}), B=1, {Hq}/{Hkv} heads, "
-                 "head_dim 256, bf16, K4/V3 group 64, causal at the offset (the dedicated kernel: "
-                 "4096 blocks of 8 query rows)") if D == 256 else
+                 "head_dim 256, bf16, K4/V3 group 64, causal at the offset (the prefill kernel: "
+                 "256 blocks of 128 query rows)") if D == 256 else
                 (f"prefill chunk: {L} new tokens over {T0} cached (T={T}), B=1, {Hq}/{Hkv} heads, "
                  "head_dim 128, bf16, K4/V4 group 64, two-sided rotation, causal at the offset "
                  "(the tile kernel: 512 blocks of 64 query rows)"),
