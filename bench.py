@@ -566,7 +566,7 @@ def prefill(rbq, W, dev, rot, n_calls: int = 10, head_dim: int = 256) -> dict:
     the fused attention of the chunk's 2048 query rows per head over the
     10240 cached tokens with the causal mask at the offset (the prefill
     kernel's 128-row blocks).  With ``head_dim=128`` the cache is head_dim 128,
-    group 64, K4/V4, two-sided rotation (the tile kernel's 64-row blocks).
+    group 64, K4/V4, two-sided rotation (the same kernel's head_dim-128 build).
     Algorithmic flops: 4 * head_dim per (query row, visible key) (q.k and
     p.v, multiply-add = 2)."""
     Hkv, Hq, T0, L = 2, 16, 8192, 2048
@@ -616,7 +616,7 @@ def prefill(rbq, W, dev, rot, n_calls: int = 10, head_dim: int = 256) -> dict:
                  "256 blocks of 128 query rows)") if D == 256 else
                 (f"prefill chunk: {L} new tokens over {T0} cached (T={T}), B=1, {Hq}/{Hkv} heads, "
                  "head_dim 128, bf16, K4/V4 group 64, two-sided rotation, causal at the offset "
-                 "(the tile kernel: 512 blocks of 64 query rows)"),
+                 "(the prefill kernel: 256 blocks of 128 query rows)"),
         "bound": "mfma",
         "alg_flops_per_call": flops,
         "avg_us": round(us, 2),

@@ -1467,10 +1467,10 @@ int check_attn(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits) {
     return RBQ_OK;
 }
 
-// Which kernel runs a call, and its plan: for the default configuration the
-// dedicated kernel, or from kPrefillMinRows query rows per kv head with a
-// bf16 cache the prefill kernel; the tile kernel for every other
-// configuration.
+// Which kernel runs a call, and its plan: the prefill kernel where it takes
+// the call (prefill_takes: from kPrefillMinRows query rows per kv head, bf16,
+// 4-bit K in groups of 64); otherwise the dedicated kernel for the default
+// configuration and the tile kernel for every other.
 struct AttnPlan {
     bool tile;
     bool prefill;
@@ -1482,8 +1482,8 @@ struct AttnPlan {
 
 int attn_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, AttnPlan* p) {
     const int64_t G = (int64_t)(H_q / c->H_kv) * L;
-    p->tile = !(is_default_config(c) && G <= kDedicatedMaxRows);
-    p->prefill = !p->tile && c->dtype == RBQ_BF16 && G >= kPrefillMinRows;
+    p->prefill = prefill_takes(c, H_q, L, splits);
+    p->tile = !p->prefill && !(is_default_config(c) && G <= kDedicatedMaxRows);
     int st;
     if (p->prefill) {
         st = prefill_plan(c, H_q, L, splits, &p->mp);

@@ -63,28 +63,49 @@ constexpr int kPRows = 16 * kPW;      // query rows per workgroup
 constexpr int kPTile = 32;            // keys per tile
 constexpr int64_t kPGridYZ = 65535;   // workgroups per grid dimension y or z of one launch
 constexpr float kPLog2e = 1.44269504088896340736f;
-// One tile as the memory holds it (a raw buffer): K words (16-byte chunks
-// of a key permuted, see k_chunk), V words, K scales, K biases, V scales,
-// V biases.
-constexpr int kRK = 0, kRV = 4096, kRKs = 7168, kRKb = 7424, kRVs = 7680, kRVb = 7936;
-constexpr int kRawBytes = 8192;
-// Decoded V' rows: 672 bytes apart, rows 8-15 and 24-31 shifted by 128
-// bytes, so that the transposing reads of 32 lanes (rows 8 j' + e of two
-// lane groups j') fall on distinct banks
-constexpr int kVRow = 672;
-__host__ __device__ constexpr int v_off(int r) { return r * kVRow + ((r >> 3) & 1) * 128; }
-// LDS layout (bytes): three raw tile buffers (tile i + 2 in flight while
-// tile i + 1 is decoded and tile i computed), two decoded tiles
-constexpr int kNRaw = 3;
-constexpr int kDecBytes = kPTile * kVRow + 128;           // V' [32 rows], fp16 (rows at v_off)
-constexpr int kOffV = kNRaw * kRawBytes;                  // 2 x V'
-constexpr int kOffKs = kOffV + 2 * kDecBytes;             // 2 x K scales, fp32 [4 groups][32 keys]
-constexpr int kOffVb = kOffKs + 2 * kGroups * kPTile * 4; // 2 x V bias operand, fp16 [4 groups][32 rows]
-constexpr int kOffRot = kOffVb + 2 * kGroups * kPTile * 2; // rotation blocks, fp32 [64][4][4]
-constexpr int kOffRed = kOffRot + kHeadDim * 16;          // group maxima [8 waves][4]
-constexpr int kOffUnit = kOffRed + 8 * 4 * 4;            // 2^F_g, then 2^-F_g
-constexpr int kPBytes = kOffUnit + 8 * 4;
-static_assert(kPBytes <= 160 * 1024, "LDS of one compute unit");
+// Layout of one configuration: head_dim D (128 or 256), groups of 64 dims,
+// 4-bit K codes, VB-bit V codes (2, 3 or 4).
+//   A raw buffer holds one tile as the memory holds it: K words (16-byte
+//   chunks of a key permuted, see k_chunk), V words, K scales, K biases, V
+//   scales, V biases.  LDS (bytes): three raw buffers (tile i + 2 in flight
+//   while tile i + 1 is decoded and tile i computed), two decoded tiles (V',
+//   and for 4-bit codes its residual V'', see the decode), K scales and V
+//   bias operands of both, the rotation blocks, group maxima, scale powers.
+template <int D, int VB>
+struct PCfg {
+    static constexpr int NG = D / 64;                     // groups of 64 dims
+    static constexpr int NB = D / 16;                     // 16-dim output blocks
+    static constexpr int CPK = D / 32;                    // 16-byte K chunks per key
+    static constexpr int KPB = 512 / D;                   // keys per 256 bytes of K words
+    static constexpr int VWK = D * VB / 32;               // V words per key
+    static constexpr int RK = 0;
+    static constexpr int RV = RK + kPTile * D / 2;
+    static constexpr int RKs = RV + kPTile * VWK * 4;
+    static constexpr int MB = kPTile * NG * 2;            // bytes of each scale / bias array
+    static constexpr int RKb = RKs + MB, RVs = RKb + MB, RVb = RVs + MB;
+    static constexpr int RAW = (RVb + MB + 15) / 16 * 16;
+    static constexpr bool VSPLIT = VB > 3;                // 4 + 8 significant bits: V' + V''
+    static constexpr int NDEC = VSPLIT ? 2 : 1;           // decoded arrays per tile
+    // decoded rows: 2 D + 160 bytes apart, rows 8-15 and 24-31 shifted by 128
+    // bytes, so that the transposing reads of 32 lanes (rows 8 j' + e of two
+    // lane groups j') fall on distinct banks
+    static constexpr int VROW = 2 * D + 160;
+    static constexpr int DEC = kPTile * VROW + 128;       // one decoded array
+    static constexpr int OffV = 3 * RAW;
+    static constexpr int OffKs = OffV + 2 * NDEC * DEC;   // fp32 [NG][32] per tile
+    static constexpr int OffVb = OffKs + 2 * NG * kPTile * 4;  // fp16 [NG][32] per tile
+    static constexpr int OffRot = OffVb + 2 * NG * kPTile * 2;
+    static constexpr int OffRed = OffRot + D * 16;        // [8 waves][4] group maxima
+    static constexpr int OffUnit = OffRed + kPW * 16;     // 2^F_g, then 2^-F_g
+    static constexpr int BYTES = OffUnit + 32;
+    static constexpr int KI = D / 64;                     // K transfers (64 lanes x 16 bytes)
+    static constexpr int VCH = kPTile * VWK / 4;          // 16-byte V chunks
+    static constexpr int VI = (VCH + 63) / 64;            // V transfers
+    static constexpr int NI = KI + VI + 4;                // + one per scale / bias array
+    static_assert(BYTES <= 160 * 1024, "LDS of one compute unit");
+    static_assert(D <= kPT, "one float4 of the rotation blocks per thread");
+    __host__ __device__ static constexpr int v_off(int r) { return r * VROW + ((r >> 3) & 1) * 128; }
+};
 static_assert(kRecordFloats == 2 * 8 + 8 * kHeadDim, "split record layout");
 
 struct PArgs {
@@ -129,6 +150,16 @@ __device__ __forceinline__ pu32x2 tr_read(const unsigned char* smem, uint32_t of
     return __builtin_bit_cast(pu32x2, v);
 }
 
+// Direct-to-LDS buffer loads of 16 or 4 bytes per lane (wrapped: called with
+// template-dependent arguments the builtin stops the host pass from
+// instantiating the kernel)
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, plds_u8* dst, int off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, plds_u8* dst, int off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, off, 0, 0, 0);
+}
+
 template <typename T>
 __device__ __forceinline__ T lds_ld(const unsigned char* smem, uint32_t off) {
     return *(const __attribute__((address_space(3))) T*)((const plds_u8*)smem + off);
@@ -165,46 +196,24 @@ __device__ __forceinline__ uint32_t lo_parts(uint32_t hi2, float p0, float p1, f
 }
 
 // 16-byte slot of K word chunk c (words 4c .. 4c+3) of tile key k in a raw
-// buffer: the chunks of a key permuted by (k >> 1) & 7, so that the 8-byte
-// reads of 32 lanes (16 keys x 2 halves of a chunk) hit distinct banks.
-__device__ __forceinline__ int k_chunk(int k, int c) { return 8 * k + (c ^ ((k >> 1) & 7)); }
+// buffer: the chunks of a key permuted by (k / KPB) mod CPK, so that the
+// 8-byte reads of 32 lanes (16 keys x 2 halves of a chunk) hit distinct
+// banks.
+template <int D>
+__device__ __forceinline__ int k_chunk(int k, int c) {
+    constexpr int CPK = D / 32, KPB = 512 / D;
+    return CPK * k + (c ^ ((k / KPB) & (CPK - 1)));
+}
 
 // Row of key k in the decoded V' tile: row 8 j + e holds key 4 j + e
 // (e < 4) or 16 + 4 j + e - 4 (e >= 4), the k-slot order of the P operand.
 __device__ __forceinline__ int v_row(int k) { return 8 * ((k & 15) >> 2) + (k & 3) + 4 * (k >> 4); }
 
-// Direct-to-LDS transfer of the tile at key t0 into raw buffer `buf` (lane l
-// of an instruction lands at offset + 16 l or 4 l): 11 instructions, wave w
-// issuing numbers w, w + kPW, ...: 0-3 a quarter of the K words each, 4-6 a
-// third of the V words, 7-10 the four scale / bias arrays.  Keys past the
-// buffer ranges read as zero.
-__device__ __forceinline__ void issue_tile(plds_u8* buf, int t0, int wave, int lane,
-                                           __amdgpu_buffer_rsrc_t kw_r, __amdgpu_buffer_rsrc_t vw_r,
-                                           const __amdgpu_buffer_rsrc_t m_r[4]) {
-#pragma unroll
-    for (int x = 0; x < 11; x += kPW) {
-        const int idx = x + wave;
-        if (idx < 4) {
-            const int p = 64 * idx + lane;
-            const int k = p >> 3;
-            const int c = (p & 7) ^ ((k >> 1) & 7);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kw_r, buf + kRK + 1024 * idx, 16,
-                                                      (t0 + k) * 128 + 16 * c, 0, 0, 0);
-        } else if (idx < 7) {
-            const int m = idx - 4;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vw_r, buf + kRV + 1024 * m, 16,
-                                                      t0 * 96 + 16 * (64 * m + lane), 0, 0, 0);
-        } else if (idx < 11) {
-            const int m = idx - 7;
-            const uint32_t dst = (m == 0) ? kRKs : (m == 1) ? kRKb : (m == 2) ? kRVs : kRVb;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(m_r[m], buf + dst, 4, t0 * 8 + 4 * lane, 0, 0, 0);
-        }
-    }
-}
-
-template <int MK>
+template <int MK, int D, int VB>
 __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_prefill_kernel(PArgs a) {
-    __shared__ __align__(16) unsigned char smem[kPBytes];
+    using C = PCfg<D, VB>;
+    constexpr int NG = C::NG, NB = C::NB;
+    __shared__ __align__(16) unsigned char smem[C::BYTES];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -227,26 +236,52 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         t_lim = min(t_lim, T - a.L + imax + 1);
     }
     const int64_t row0 = (int64_t)bh * a.capacity;
-    const __amdgpu_buffer_rsrc_t kw_r = prsrc(a.kw + row0 * kKWords, (uint32_t)T * 128u);
-    const __amdgpu_buffer_rsrc_t vw_r = prsrc(a.vw + row0 * kVWords, (uint32_t)T * 96u);
+    const __amdgpu_buffer_rsrc_t kw_r = prsrc(a.kw + row0 * (D / 8), (uint32_t)T * (D / 2));
+    const __amdgpu_buffer_rsrc_t vw_r = prsrc(a.vw + row0 * C::VWK, (uint32_t)T * (C::VWK * 4));
     __amdgpu_buffer_rsrc_t m_r[4];
-    m_r[0] = prsrc(a.ks + row0 * kGroups, (uint32_t)T * 8u);
-    m_r[1] = prsrc(a.kb + row0 * kGroups, (uint32_t)T * 8u);
-    m_r[2] = prsrc(a.vs + row0 * kGroups, (uint32_t)T * 8u);
-    m_r[3] = prsrc(a.vb + row0 * kGroups, (uint32_t)T * 8u);
+    m_r[0] = prsrc(a.ks + row0 * NG, (uint32_t)T * (2 * NG));
+    m_r[1] = prsrc(a.kb + row0 * NG, (uint32_t)T * (2 * NG));
+    m_r[2] = prsrc(a.vs + row0 * NG, (uint32_t)T * (2 * NG));
+    m_r[3] = prsrc(a.vb + row0 * NG, (uint32_t)T * (2 * NG));
 
+    // Direct-to-LDS transfer of the tile at key t0 into raw buffer `buf` (lane
+    // l of an instruction lands at offset + 16 l or 4 l): NI instructions,
+    // wave w issuing numbers w, w + kPW, ...: the K words in 64-lane pieces,
+    // the V words likewise (the last piece on fewer lanes where it is short),
+    // then one per scale / bias array.  Keys past the buffer ranges read as
+    // zero.
+    auto issue_tile = [&](plds_u8* buf, const int t0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int x = 0; x < C::NI; x += kPW) {
+            const int idx = x + wave;
+            if (idx < C::KI) {
+                const int p = 64 * idx + lane;
+                const int k = p / C::CPK;
+                const int c = (p % C::CPK) ^ ((k / C::KPB) & (C::CPK - 1));
+                lds_dma16(kw_r, buf + C::RK + 1024 * idx, (t0 + k) * (D / 2) + 16 * c);
+            } else if (idx < C::KI + C::VI) {
+                const int m = idx - C::KI;
+                if (64 * m + lane < C::VCH)
+                    lds_dma16(vw_r, buf + C::RV + 1024 * m, t0 * (C::VWK * 4) + 16 * (64 * m + lane));
+            } else if (idx < C::NI) {
+                const int m = idx - C::KI - C::VI;
+                const uint32_t dst = (m == 0) ? C::RKs : (m == 1) ? C::RKb : (m == 2) ? C::RVs : C::RVb;
+                if (lane < 16 * NG) lds_dma4(m_r[m], buf + dst, t0 * (2 * NG) + 4 * lane);
+            }
+        }
+    };
     // the first tile in flight during the set-up
-    if (t_begin < t_lim) issue_tile((plds_u8*)smem, t_begin, wave, lane, kw_r, vw_r, m_r);
+    if (t_begin < t_lim) issue_tile((plds_u8*)smem, t_begin);
 
     // ---- the query row of this lane (dims 64 g + 16 j .. 64 g + 16 j + 15)
     //      and the rotation blocks into LDS ----
     const int R = r0 + 16 * wave + n;
     const bool row_ok = R < a.G;
-    float x[4][16];
+    float x[NG][16];
     {
-        const uint16_t* qr = a.q + ((int64_t)bh * a.G + (row_ok ? R : 0)) * kHeadDim;
+        const uint16_t* qr = a.q + ((int64_t)bh * a.G + (row_ok ? R : 0)) * D;
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int g = 0; g < NG; ++g)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 if (row_ok) {
@@ -258,36 +293,31 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
     }
     const bool rotated = a.rot != nullptr;
-    // (64 blocks of 16 floats: one float4 per thread of the first 256)
-    static_assert(kHeadDim <= kPT, "one float4 of the rotation blocks per thread");
-    if (rotated && tid < kHeadDim)
-        lds_st<pf32x4>(smem, kOffRot + 16 * tid, reinterpret_cast<const pf32x4*>(a.rot)[tid]);
+    // (D / 4 blocks of 16 floats: one float4 per thread of the first D)
+    if (rotated && tid < D)
+        lds_st<pf32x4>(smem, C::OffRot + 16 * tid, reinterpret_cast<const pf32x4*>(a.rot)[tid]);
 
     // ---- F_g: the power of two that keeps the split's V scales and biases
     //      of group g below 2^13 (over the keys this workgroup reads) ----
     float vmx[4] = {0.f, 0.f, 0.f, 0.f};
     for (int t = t_begin + tid; t < t_lim; t += kPT) {
-        const uint2 s2 = *reinterpret_cast<const uint2*>(a.vs + (row0 + t) * kGroups);
-        const uint2 b2 = *reinterpret_cast<const uint2*>(a.vb + (row0 + t) * kGroups);
-        const uint32_t sw[4] = {s2.x, s2.x >> 16, s2.y, s2.y >> 16};
-        const uint32_t bw[4] = {b2.x, b2.x >> 16, b2.y, b2.y >> 16};
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-            vmx[g] = fmaxf(vmx[g], fmaxf(fabsf(bf16_bits_to_f32(sw[g] & 0xFFFFu)),
-                                         fabsf(bf16_bits_to_f32(bw[g] & 0xFFFFu))));
+        for (int g = 0; g < NG; ++g)
+            vmx[g] = fmaxf(vmx[g], fmaxf(fabsf(bf16_bits_to_f32(a.vs[(row0 + t) * NG + g])),
+                                         fabsf(bf16_bits_to_f32(a.vb[(row0 + t) * NG + g]))));
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) vmx[g] = fmaxf(vmx[g], __shfl_xor(vmx[g], o));
     }
-    if (lane == 0) lds_st<pf32x4>(smem, kOffRed + 16 * wave, (pf32x4){vmx[0], vmx[1], vmx[2], vmx[3]});
+    if (lane == 0) lds_st<pf32x4>(smem, C::OffRed + 16 * wave, (pf32x4){vmx[0], vmx[1], vmx[2], vmx[3]});
     __syncthreads();  // rotation blocks and group maxima in LDS
     {
         float mx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < kPW; ++w) {
-            const pf32x4 v = lds_ld<pf32x4>(smem, kOffRed + 16 * w);
+            const pf32x4 v = lds_ld<pf32x4>(smem, C::OffRed + 16 * w);
 #pragma unroll
             for (int g = 0; g < 4; ++g) mx[g] = fmaxf(mx[g], v[g]);
         }
@@ -297,8 +327,8 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (mx[g] > 0.f) (void)frexpf(mx[g], &ex);  // mx < 2^ex
             const int F = (mx[g] > 0.f) ? 13 - ex : 0;
             if (tid == g) {
-                lds_st<float>(smem, kOffUnit + 4 * g, ldexpf(1.0f, F));
-                lds_st<float>(smem, kOffUnit + 16 + 4 * g, ldexpf(1.0f, -F));
+                lds_st<float>(smem, C::OffUnit + 4 * g, ldexpf(1.0f, F));
+                lds_st<float>(smem, C::OffUnit + 16 + 4 * g, ldexpf(1.0f, -F));
             }
         }
     }
@@ -307,13 +337,13 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     //      log2(e); E: the power of two that brings the row's largest |q|
     //      into [2^14, 2^15); the group sums ----
     float E_f;
-    pf16x8 qh[4][2], ql[4][2];
+    pf16x8 qh[NG][2], ql[NG][2];
     pu32x4 qb = {0u, 0u, 0u, 0u};
     {
         float mx = 0.f;
-        float gsum[4];
+        float gsum[NG];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int g = 0; g < NG; ++g) {
             gsum[g] = 0.f;
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
@@ -323,7 +353,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     const int blk = 16 * g + 4 * j + q4;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const pf32x4 v = lds_ld<pf32x4>(smem, kOffRot + 64 * blk + 16 * r);
+                        const pf32x4 v = lds_ld<pf32x4>(smem, C::OffRot + 64 * blk + 16 * r);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) Bm[4 * r + e] = v[e];
                     }
@@ -355,7 +385,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // 1/16 where the nibble mask leaves 16 c
         constexpr int kPerm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int g = 0; g < NG; ++g)
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -365,11 +395,11 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     qh[g][h2][e] = hi;
                     ql[g][h2][e] = (_Float16)(xs - (float)hi);
                 }
-        // bias operand: lane group j < 3 holds limb j of the 4 group sums
-        // (exact three-limb bf16 split) in k-slots 0-3
-        uint32_t lb[4];
+        // bias operand: lane group j < 3 holds limb j of the NG group sums
+        // (exact three-limb bf16 split) in k-slots 0 .. NG - 1
+        uint32_t lb[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int g = 0; g < NG; ++g) {
             const float s = row_sum4(gsum[g]);
             const uint32_t u = __float_as_uint(s);
             const float hi = __uint_as_float(u & 0xFFFF0000u);
@@ -402,67 +432,85 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     }
 
-    pf32x4 O[16];
+    pf32x4 O[NB];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) O[t] = (pf32x4){0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NB; ++t) O[t] = (pf32x4){0.f, 0.f, 0.f, 0.f};
     pf32x4 Ob = {0.f, 0.f, 0.f, 0.f};
     float m_ref = -INFINITY, thr = -INFINITY, l_part = 0.f;
     const float one = 1.0f;
     const pf32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     // this lane's transposing-read address in the V' tile: lane 4 e + q of a
     // group reads row 8 j + e, columns 4 q .. 4 q + 3 of an output block
-    const uint32_t vrd = kOffV + v_off(8 * j + (n >> 2)) + 8 * (n & 3);
+    const uint32_t vrd = C::OffV + C::v_off(8 * j + (n >> 2)) + 8 * (n & 3);
 
-    // decode of the tile in raw buffer `raw` into decoded buffer `db`: V' rows
-    // (item = key i >> 4, dims 16 (i & 15) .., 512 items over the threads), K
-    // scales to fp32 (waves 0-1), V bias operand (waves 2-3)
+    // decode of the tile in raw buffer `raw` into decoded tile `db`: V' rows
+    // (item = key i / (D / 16), dims 16 (i mod (D / 16)) .., 2 D items over
+    // the threads), K scales to fp32 (waves 0-1), V bias operand (waves 2-3).
+    // V' = code x scale x 2^F_g, exact in fp32; in fp16 exact for up to 3-bit
+    // codes (8 + 3 significant bits); 4-bit codes keep the residual V'' =
+    // V' - fp16(V') (exact) in a second array
     auto decode_tile = [&](const unsigned char* raw, const int db) __attribute__((always_inline)) {
+        constexpr int IPK = D / 16;  // items per key
 #pragma unroll
-        for (int item = tid; item < 512; item += kPT) {
-            const int k = item >> 4, p = item & 15, g = p >> 2;
-            const int wi = (3 * p) >> 1, sh = 16 * (p & 1);
-            const uint32_t w0 = lds_ld<uint32_t>(raw, kRV + 96 * k + 4 * wi);
-            const uint32_t w1 = lds_ld<uint32_t>(raw, kRV + 96 * k + 4 * wi + 4);
+        for (int item = tid; item < 2 * D; item += kPT) {
+            const int k = item / IPK, p = item % IPK, g = p >> 2;
+            const int bit0 = 16 * VB * p;
+            const int wi = bit0 >> 5, sh = bit0 & 31;
+            const uint32_t w0 = lds_ld<uint32_t>(raw, C::RV + 4 * (C::VWK * k + wi));
+            const uint32_t w1 = lds_ld<uint32_t>(raw, C::RV + 4 * (C::VWK * k + wi + 1));
             const uint64_t bits = (((uint64_t)w1 << 32) | w0) >> sh;
-            const uint32_t sv = lds_ld<uint16_t>(raw, kRVs + 8 * k + 2 * g);
-            const float sf = bf16_bits_to_f32(sv) * lds_ld<float>(smem, kOffUnit + 4 * g);
-            // code times scale times 2^F_g: exact in fp32, then in fp16
-            uint32_t h[8];
+            const uint32_t sv = lds_ld<uint16_t>(raw, C::RVs + 2 * (NG * k + g));
+            const float sf = bf16_bits_to_f32(sv) * lds_ld<float>(smem, C::OffUnit + 4 * g);
+            constexpr uint32_t cm = (1u << VB) - 1u;
+            uint32_t h[8], hl[8];
 #pragma unroll
             for (int d = 0; d < 8; ++d) {
-                const float c0 = (float)(uint32_t)((bits >> (6 * d)) & 7u);
-                const float c1 = (float)(uint32_t)((bits >> (6 * d + 3)) & 7u);
-                h[d] = __builtin_bit_cast(uint32_t, (pf16x2){(_Float16)(c0 * sf), (_Float16)(c1 * sf)});
+                const float v0 = (float)(uint32_t)((bits >> (VB * 2 * d)) & cm) * sf;
+                const float v1 = (float)(uint32_t)((bits >> (VB * (2 * d + 1))) & cm) * sf;
+                const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
+                h[d] = __builtin_bit_cast(uint32_t, (pf16x2){h0, h1});
+                if constexpr (C::VSPLIT)
+                    hl[d] = __builtin_bit_cast(uint32_t, (pf16x2){(_Float16)(v0 - (float)h0),
+                                                                  (_Float16)(v1 - (float)h1)});
             }
-            const uint32_t dst = kOffV + db * kDecBytes + v_off(v_row(k)) + 32 * p;
+            const uint32_t dst = C::OffV + db * C::NDEC * C::DEC + C::v_off(v_row(k)) + 32 * p;
             lds_st<pu32x4>(smem, dst, (pu32x4){h[0], h[1], h[2], h[3]});
             lds_st<pu32x4>(smem, dst + 16, (pu32x4){h[4], h[5], h[6], h[7]});
+            if constexpr (C::VSPLIT) {
+                lds_st<pu32x4>(smem, dst + C::DEC, (pu32x4){hl[0], hl[1], hl[2], hl[3]});
+                lds_st<pu32x4>(smem, dst + C::DEC + 16, (pu32x4){hl[4], hl[5], hl[6], hl[7]});
+            }
         }
         if (wave < 2) {
-            const int kk = tid >> 2, gg = tid & 3;
-            const uint32_t sk = lds_ld<uint16_t>(raw, kRKs + 8 * kk + 2 * gg);
-            lds_st<float>(smem, kOffKs + db * 512 + 4 * (gg * kPTile + kk), bf16_bits_to_f32(sk));
+            if (tid < kPTile * NG) {
+                const int kk = tid / NG, gg = tid % NG;
+                const uint32_t sk = lds_ld<uint16_t>(raw, C::RKs + 2 * (NG * kk + gg));
+                lds_st<float>(smem, C::OffKs + db * (NG * kPTile * 4) + 4 * (gg * kPTile + kk),
+                              bf16_bits_to_f32(sk));
+            }
         } else if (wave < 4) {
-            const int kk = (tid - 128) >> 2, gg = tid & 3;
-            const uint32_t b = lds_ld<uint16_t>(raw, kRVb + 8 * kk + 2 * gg);
-            const float bu = bf16_bits_to_f32(b) * lds_ld<float>(smem, kOffUnit + 4 * gg);
-            lds_st<uint16_t>(smem, kOffVb + db * 256 + 2 * (gg * kPTile + v_row(kk)),
-                             __builtin_bit_cast(uint16_t, (_Float16)bu));
+            if (tid - 128 < kPTile * NG) {
+                const int kk = (tid - 128) / NG, gg = (tid - 128) % NG;
+                const uint32_t b = lds_ld<uint16_t>(raw, C::RVb + 2 * (NG * kk + gg));
+                const float bu = bf16_bits_to_f32(b) * lds_ld<float>(smem, C::OffUnit + 4 * gg);
+                lds_st<uint16_t>(smem, C::OffVb + db * (NG * kPTile * 2) + 2 * (gg * kPTile + v_row(kk)),
+                                 __builtin_bit_cast(uint16_t, (_Float16)bu));
+            }
         }
     };
     const int n_tiles = (t_lim > t_begin) ? (t_lim - t_begin + kPTile - 1) / kPTile : 0;
     // the second tile in flight too; the first decoded before the loop
     if (n_tiles > 1)
-        issue_tile((plds_u8*)smem + kRawBytes, t_begin + kPTile, wave, lane, kw_r, vw_r, m_r);
+        issue_tile((plds_u8*)smem + C::RAW, t_begin + kPTile);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (n_tiles > 0) decode_tile(smem, 0);
 
     for (int it = 0; it < n_tiles; ++it) {
         // raw buffer it % 3 holds tile it, (it + 1) % 3 tile it + 1 (landed at
         // the barrier), (it + 2) % 3 receives tile it + 2
-        const unsigned char* raw = smem + (it % kNRaw) * kRawBytes;
-        const unsigned char* raw_next = smem + ((it + 1) % kNRaw) * kRawBytes;
-        plds_u8* raw_dma = (plds_u8*)smem + ((it + 2) % kNRaw) * kRawBytes;
+        const unsigned char* raw = smem + (it % 3) * C::RAW;
+        const unsigned char* raw_next = smem + ((it + 1) % 3) * C::RAW;
+        plds_u8* raw_dma = (plds_u8*)smem + ((it + 2) % 3) * C::RAW;
         const int t0 = t_begin + it * kPTile;
         const int db = it & 1;
         // tile it + 1 has landed (each wave waits for its own transfers, the
@@ -470,7 +518,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // it - 1 (its raw and decoded buffers are free)
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         const bool dec_next = it + 1 < n_tiles;
-        if (it + 2 < n_tiles) issue_tile(raw_dma, t0 + 2 * kPTile, wave, lane, kw_r, vw_r, m_r);
+        if (it + 2 < n_tiles) issue_tile(raw_dma, t0 + 2 * kPTile);
         if (!wave_live) {
             if (dec_next) decode_tile(raw_next, db ^ 1);
             continue;
@@ -499,10 +547,10 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int key = 16 * kb + n;
-            pf32x4 acc[4];
+            pf32x4 acc[NG];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const pu32x2 w2 = lds_ld<pu32x2>(raw, kRK + 16 * k_chunk(key, 2 * g + (j >> 1)) + 8 * (j & 1));
+            for (int g = 0; g < NG; ++g) {
+                const pu32x2 w2 = lds_ld<pu32x2>(raw, C::RK + 16 * k_chunk<D>(key, 2 * g + (j >> 1)) + 8 * (j & 1));
                 acc[g] = zero4;
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) {
@@ -514,20 +562,27 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     acc[g] = mfma_f16(kop, ql[g][h2], acc[g]);
                 }
             }
-            const pu32x2 kbw = lds_ld<pu32x2>(raw, kRKb + 8 * key);
-            const pf32x4 cb = mfma_bf16((pu32x4){kbw[0], kbw[1], 0u, 0u}, qb, zero4);
+            // the key's NG bias halves in k-slots 0 .. NG - 1
+            pu32x4 kbop = {0u, 0u, 0u, 0u};
+            if constexpr (NG == 4) {
+                const pu32x2 kbw = lds_ld<pu32x2>(raw, C::RKb + 8 * key);
+                kbop = (pu32x4){kbw[0], kbw[1], 0u, 0u};
+            } else {
+                kbop = (pu32x4){lds_ld<uint32_t>(raw, C::RKb + 4 * key), 0u, 0u, 0u};
+            }
+            const pf32x4 cb = mfma_bf16(kbop, qb, zero4);
             // the next tile's decode while the matrix cores work on these
             // products (its buffers are not read by this tile)
             if (kb == 1 && dec_next) decode_tile(raw_next, db ^ 1);
-            pf32x4 s4[4];
+            pf32x4 s4[NG];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) s4[g] = lds_ld<pf32x4>(smem, kOffKs + db * 512 + 4 * (g * kPTile + 16 * kb + 4 * j));
+            for (int g = 0; g < NG; ++g)
+                s4[g] = lds_ld<pf32x4>(smem, C::OffKs + db * (NG * kPTile * 4) + 4 * (g * kPTile + 16 * kb + 4 * j));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float t = s4[0][i] * acc[0][i];
-                t = fmaf(s4[1][i], acc[1][i], t);
-                t = fmaf(s4[2][i], acc[2][i], t);
-                t = fmaf(s4[3][i], acc[3][i], t);
+#pragma unroll
+                for (int g = 1; g < NG; ++g) t = fmaf(s4[g][i], acc[g][i], t);
                 float s = fmaf(t, frow, cb[i]);
                 if constexpr (MK == RBQ_MASK_BOOL) {
                     if (mv[kb][i] == 0u) s = -INFINITY;
@@ -565,7 +620,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 thr = mx + 8.0f;
             }
 #pragma unroll
-            for (int t = 0; t < 16; ++t)
+            for (int t = 0; t < NB; ++t)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) O[t][i] *= al;
 #pragma unroll
@@ -596,19 +651,26 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const pf16x8 pl = __builtin_bit_cast(pf16x8, (pu32x4){lw[0], lw[1], lw[2], lw[3]});
 
         // ---- O^T += V'^T P^T (register i of block t: dim 16 t + 4 j + i) ----
-        const uint32_t vdb = vrd + db * kDecBytes;
+        const uint32_t vdb = vrd + db * C::NDEC * C::DEC;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
+        for (int t = 0; t < NB; ++t) {
             const pu32x2 v0 = tr_read(smem, vdb + 32 * t);
-            const pu32x2 v1 = tr_read(smem, vdb + 32 * t + 4 * kVRow);
+            const pu32x2 v1 = tr_read(smem, vdb + 32 * t + 4 * C::VROW);
             const pf16x8 vop = __builtin_bit_cast(pf16x8, (pu32x4){v0[0], v0[1], v1[0], v1[1]});
             O[t] = mfma_f16(vop, ph, O[t]);
             O[t] = mfma_f16(vop, pl, O[t]);
+            if constexpr (C::VSPLIT) {
+                // the residual against the hi part of P (its lo part's
+                // product is below 2^-22 of the term)
+                const pu32x2 r0 = tr_read(smem, vdb + C::DEC + 32 * t);
+                const pu32x2 r1 = tr_read(smem, vdb + C::DEC + 32 * t + 4 * C::VROW);
+                O[t] = mfma_f16(__builtin_bit_cast(pf16x8, (pu32x4){r0[0], r0[1], r1[0], r1[1]}), ph, O[t]);
+            }
         }
         {
             // group biases: A row g < 4 = b_{key, g} 2^F_g over the k-slots
             pu32x4 vb4 = {0u, 0u, 0u, 0u};
-            if (n < 4) vb4 = lds_ld<pu32x4>(smem, kOffVb + db * 256 + 2 * (n * kPTile + 8 * j));
+            if (n < NG) vb4 = lds_ld<pu32x4>(smem, C::OffVb + db * (NG * kPTile * 2) + 2 * (n * kPTile + 8 * j));
             const pf16x8 vbop = __builtin_bit_cast(pf16x8, vb4);
             Ob = mfma_f16(vbop, ph, Ob);
             Ob = mfma_f16(vbop, pl, Ob);
@@ -621,16 +683,16 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float l = row_sum4(l_part);
     float obg[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) obg[g] = row_sum4(Ob[g]);
+    for (int g = 0; g < 4; ++g) obg[g] = row_sum4(Ob[g]);  // groups past NG: 0
     if (!row_ok) return;
-    const pf32x4 vinv = lds_ld<pf32x4>(smem, kOffUnit + 16);
+    const pf32x4 vinv = lds_ld<pf32x4>(smem, C::OffUnit + 16);
     if (a.S == 1) {
         const float inv = 1.0f / l;
         // a boolean mask dropped every key of the row: the mean of its keys
         const bool uniform = MK == RBQ_MASK_BOOL && l == 0.f;
-        float* orow = a.out + ((int64_t)bh * a.G + R) * kHeadDim;
+        float* orow = a.out + ((int64_t)bh * a.G + R) * D;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
+        for (int t = 0; t < NB; ++t) {
             const int g = t >> 2;
             float y[4];
 #pragma unroll
@@ -640,7 +702,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     y[i] = value_column_mean<RBQ_BF16>(a.vw, a.vs, a.vb, row0, nv, 16 * t + 4 * j + i,
-                                                       kVBits, kVWords, kGroups, kGroup);
+                                                       VB, C::VWK, NG, 64);
             }
             float z[4] = {y[0], y[1], y[2], y[3]};
             if (rotated) {
@@ -648,7 +710,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const int blk = 4 * t + j;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const pf32x4 v = lds_ld<pf32x4>(smem, kOffRot + 64 * blk + 16 * r);
+                    const pf32x4 v = lds_ld<pf32x4>(smem, C::OffRot + 64 * blk + 16 * r);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) Bm[4 * r + e] = v[e];
                 }
@@ -658,21 +720,46 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         return;
     }
-    // this split's record of the lane's row (block of 8 rows R >> 3, row R & 7)
-    float* rec = a.rec + ((int64_t)(bh * a.RB + (R >> 3)) * a.S + split) * kRecordFloats;
-    const int ri = R & 7;
+    // this split's record of the lane's row (block of 8 rows R >> 3, row R &
+    // 7); key splits only in the default layout (the plan keeps one split
+    // otherwise)
+    if constexpr (D == kHeadDim) {
+        float* rec = a.rec + ((int64_t)(bh * a.RB + (R >> 3)) * a.S + split) * kRecordFloats;
+        const int ri = R & 7;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-        const int g = t >> 2;
+        for (int t = 0; t < NB; ++t) {
+            const int g = t >> 2;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rec[16 + (16 * t + 4 * j + i) * 8 + ri] = (O[t][i] + obg[g]) * vinv[g];
+            for (int i = 0; i < 4; ++i) rec[16 + (16 * t + 4 * j + i) * 8 + ri] = (O[t][i] + obg[g]) * vinv[g];
+        }
+        if (j == 0) *reinterpret_cast<float2*>(rec + 2 * ri) = make_float2(m_ref, l);
     }
-    if (j == 0) *reinterpret_cast<float2*>(rec + 2 * ri) = make_float2(m_ref, l);
 }
 
 }  // namespace
 
 // ---- host side ----
+
+// The kernel of layout (D, VB) for mask type mt, handed to `launch`.
+template <int D, int VB, typename F>
+static void launch_masked(int mt, F&& launch) {
+    if (mt == RBQ_MASK_NONE) launch(attn_prefill_kernel<RBQ_MASK_NONE, D, VB>);
+    else if (mt == RBQ_MASK_BOOL) launch(attn_prefill_kernel<RBQ_MASK_BOOL, D, VB>);
+    else if (mt == RBQ_MASK_ADD_F32) launch(attn_prefill_kernel<RBQ_MASK_ADD_F32, D, VB>);
+    else launch(attn_prefill_kernel<RBQ_MASK_ADD_DTYPE, D, VB>);
+}
+
+bool prefill_takes(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits) {
+    const int64_t G = (int64_t)(H_q / c->H_kv) * L;
+    if (G < kPrefillMinRows || c->dtype != RBQ_BF16 || c->k_bits != 4 || c->group_size != 64 ||
+        (c->head_dim != 128 && c->head_dim != 256) || c->v_bits < 2 || c->v_bits > 4)
+        return false;
+    if (is_default_config(c)) return true;
+    // other layouts: one key split (no records), i.e. an explicit single
+    // split or workgroups that fill the compute units by themselves
+    const int64_t units = (int64_t)c->B * c->H_kv * ((G + kPRows - 1) / kPRows);
+    return splits == 1 || (splits == 0 && units >= 256);
+}
 
 int prefill_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, MfmaPlan* p) {
     const int64_t G = (int64_t)(H_q / c->H_kv) * L;
@@ -695,7 +782,10 @@ int prefill_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, 
     // the merge kernel's one launch: at most 2^32 - 1 work-items along x
     if (S > 1 && rec_units * 8 * 512 > 0xFFFFFFFFll) return RBQ_EUNSUPPORTED;
     // 32-bit buffer offsets, up to one tile past T
-    if ((T + kPTile) * (int64_t)(kKWords * 4) > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
+    const int64_t row_bytes = (int64_t)c->head_dim * (c->k_bits > c->v_bits ? c->k_bits : c->v_bits) / 8;
+    if ((T + kPTile) * row_bytes > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
+    // split records exist for the default layout only
+    if (S > 1 && !is_default_config(c)) return RBQ_EUNSUPPORTED;
     p->S = (int)S;
     p->RB = (int)RB;
     p->chunk = chunk;
@@ -748,10 +838,15 @@ int prefill_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L,
                 hipLaunchKernelGGL(kernel, grid, dim3(kPT), 0, s, a);
             }
     };
-    if (mt == RBQ_MASK_NONE) launch(attn_prefill_kernel<RBQ_MASK_NONE>);
-    else if (mt == RBQ_MASK_BOOL) launch(attn_prefill_kernel<RBQ_MASK_BOOL>);
-    else if (mt == RBQ_MASK_ADD_F32) launch(attn_prefill_kernel<RBQ_MASK_ADD_F32>);
-    else launch(attn_prefill_kernel<RBQ_MASK_ADD_DTYPE>);
+    if (c->head_dim == 256) {
+        if (c->v_bits == 3) launch_masked<256, 3>(mt, launch);
+        else if (c->v_bits == 4) launch_masked<256, 4>(mt, launch);
+        else launch_masked<256, 2>(mt, launch);
+    } else {
+        if (c->v_bits == 3) launch_masked<128, 3>(mt, launch);
+        else if (c->v_bits == 4) launch_masked<128, 4>(mt, launch);
+        else launch_masked<128, 2>(mt, launch);
+    }
     if (p.S > 1) merge_launch(c, a.rec, rot_blocks, out, p.S, p.RB, a.n_rep, L, a.causal, mt, stream);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {

@@ -81,10 +81,13 @@ constexpr int kRecordFloats = 2 * 8 + 8 * kHeadDim;
 void merge_launch(const rbq_kv_cache* c, const float* rec, const float* rot_blocks, float* out,
                   int S, int RB, int n_rep, int L, int causal, int mask_type, void* stream);
 
-// Prefill-length attention of the default configuration with bf16 caches
-// (blocks of 128 query rows per kv head sharing each decoded tile): used from
-// kPrefillMinRows query rows per kv head.
+// Prefill-length attention over bf16 caches with 4-bit K codes in groups of
+// 64 (head_dim 128 or 256, V codes of 2 to 4 bits), blocks of 128 query rows
+// per kv head sharing each decoded tile: used from kPrefillMinRows query rows
+// per kv head, in the default configuration with any split count, in the
+// others with one split (prefill_takes).
 constexpr int64_t kPrefillMinRows = 96;
+bool prefill_takes(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits);
 int prefill_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, MfmaPlan* p);
 int prefill_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, float scale,
                    int32_t causal, const AttnMask& mk, const float* rot_blocks, float* out,

@@ -5,7 +5,7 @@ it times (automatic key splits), against the oracle on sampled outputs:
   B=1, 16 q heads / 2 kv heads, then the attention of the chunk's 2048 query
   rows per head with the causal mask at the offset; head_dim 256 K4/V3 (the
   prefill kernel's 128-row blocks) and head_dim 128 K4/V4 with the two-sided
-  rotation (the tile kernel's 64-row blocks); query rows sampled over heads
+  rotation (the same kernel's head_dim-128 build); query rows sampled over heads
   and positions (first rows, block edges, last rows);
 - the head_dim-128 decode: B=8, 16/2 heads, group 64, K4/V4, two-sided
   rotation, T=32768 (the tile kernel); whole (b, kv head) slabs sampled.

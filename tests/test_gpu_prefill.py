@@ -1,6 +1,6 @@
-"""GPU parity of the prefill kernel (default configuration, bf16 caches, from
-96 query rows per kv head: blocks of 128 rows sharing each decoded tile)
-against the oracle, every output element:
+"""GPU parity of the prefill kernel (bf16 caches with 4-bit K codes in groups
+of 64, from 96 query rows per kv head: blocks of 128 rows sharing each
+decoded tile) against the oracle, every output element:
 
 - row counts at the threshold (96), one whole block (128), a ragged last
   block (200 rows: 128 + 72), many blocks (1200 rows over a cache that holds
@@ -14,7 +14,11 @@ against the oracle, every output element:
 - V values far beyond the fp16 range of the value operands (the per-group
   powers of two);
 - the one-call step with a chunk of 16 appended rows (append kernel, then
-  the prefill kernel): rows bit-exact, outputs within the tolerance.
+  the prefill kernel): rows bit-exact, outputs within the tolerance;
+- the other layouts it takes with one key split: head_dim 128 and 256 with
+  2-, 3- and 4-bit V codes (4-bit: the fp16 value operand and its residual),
+  masks, large V values, and a call whose 256 workgroups take the automatic
+  plan.
 """
 import numpy as np
 import pytest
@@ -174,3 +178,91 @@ def test_prefill_plan_is_used(dev):
     g, _, _ = _pair(dev, 98, 1, 2, 10240)
     assert rbq.rbq_quant_attn_splits(g.desc, 16, 2048) == 1
     assert rbq.rbq_quant_attn_splits(g.desc, 16, 16) > 1
+
+
+# other layouts the prefill kernel takes (bf16, 4-bit K in groups of 64, one
+# key split): (head_dim, v_bits, B, H_q, H_kv, L, T0, causal, splits, rotation, rounded)
+LAYOUTS = [
+    (128, 4, 1, 16, 2, 16, 300, True, 1, "two_sided", False),
+    (128, 3, 1, 8, 2, 50, 133, True, 1, "printed", True),
+    (128, 2, 2, 16, 2, 12, 200, False, 1, "printed", False),
+    (256, 4, 1, 16, 2, 16, 250, True, 1, "two_sided", False),
+    (256, 2, 1, 16, 2, 12, 180, True, 1, None, False),
+    (128, 4, 2, 16, 8, 1024, 76, True, 0, "two_sided", False),  # 256 workgroups: automatic plan
+]
+
+
+def _lid(c):
+    return "D{}_v{}_B{}_H{}-{}_L{}_T{}_{}_s{}_{}{}".format(
+        c[0], c[1], c[2], c[3], c[4], c[5], c[6], "causal" if c[7] else "full", c[8], c[9] or "norot",
+        "_rr" if c[10] else "")
+
+
+def _layout_pair(dev, seed, D, vb, B, Hkv, T, rot_mode, rr, vscale=1.0):
+    blocks = rot = None
+    if rot_mode is not None:
+        blocks = O.rotation_blocks(W.rotation_draws(seed, D), mode=rot_mode)
+        if rr:
+            blocks = O.round_to_dtype(blocks, "bf16")
+        rot = rbq.build_block_so4(D, seed, dev, two_sided=rot_mode == "two_sided",
+                                  round_to=torch.bfloat16 if rr else None)
+    g = rbq.RotatedQuantKVCache(B, Hkv, device=dev, rot=rot, head_dim=D, group_size=64, k_bits=4,
+                                v_bits=vb, round_rotated=rr)
+    o = O.QuantKVCache(k_bits=4, v_bits=vb, dtype="bf16", group=64, round_rotated=rr)
+    k = W.random_rows([seed, 1], (B, Hkv, T, D), "bf16", "student_t3")
+    v = W.random_rows([seed, 2], (B, Hkv, T, D), "bf16", scale=vscale)
+    g.append(k.to(dev), v.to(dev))
+    o.append(k.float().numpy(), v.float().numpy(), blocks)
+    return g, o, blocks
+
+
+@pytest.mark.parametrize("case", LAYOUTS, ids=_lid)
+def test_prefill_other_layouts(case, dev):
+    D, vb, B, Hq, Hkv, L, T0, causal, splits, rot_mode, rr = case
+    print(f"[prefill layout] {_lid(case)}", flush=True)
+    g, o, blocks = _layout_pair(dev, 70, D, vb, B, Hkv, T0 + L, rot_mode, rr)
+    q = W.random_rows([71, L], (B, Hq, L, D), "bf16")
+    out = g.attend(q.to(dev), scale=D ** -0.5, causal=causal, splits=splits)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    want = O.attention(q.float().numpy(), o, D ** -0.5, causal, blocks)
+    err = float(np.abs(got - want).max())
+    assert err <= ATOL, err
+
+
+@pytest.mark.parametrize("kind", ["bool", "f32"])
+def test_prefill_other_layout_masks(kind, dev):
+    D, vb, B, Hq, Hkv, L, T = 128, 4, 2, 16, 2, 16, 333
+    print(f"[prefill layout mask] {kind}", flush=True)
+    g, o, blocks = _layout_pair(dev, 72, D, vb, B, Hkv, T, "two_sided", False)
+    q = W.random_rows([73, 0], (B, Hq, L, D), "bf16")
+    rng = np.random.default_rng(74)
+    if kind == "bool":
+        m = rng.random((B, Hq, L, T)) < 0.4
+        m[0, 3, 5, :] = False
+        m[1, :, 0, :] = False
+    else:
+        m = rng.normal(0.0, 2.0, size=(B, Hq, L, T)).astype(np.float32)
+    out = g.attend(q.to(dev), scale=D ** -0.5, causal=True, mask=torch.from_numpy(m).to(dev), splits=1)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    want = O.attention(q.float().numpy(), o, D ** -0.5, True, blocks, mask=m)
+    err = float(np.abs(got - want).max())
+    assert err <= ATOL, err
+
+
+def test_prefill_other_layout_large_values(dev):
+    # 4-bit V codes: V' and its residual carry code x scale exactly
+    print("[prefill layout] large V", flush=True)
+    D, vb, B, Hq, Hkv, L, T = 128, 4, 1, 16, 2, 16, 400
+    g, o, blocks = _layout_pair(dev, 75, D, vb, B, Hkv, T, "printed", False, vscale=1e5)
+    q = W.random_rows([76, 0], (B, Hq, L, D), "bf16")
+    out = g.attend(q.to(dev), scale=D ** -0.5, causal=True, splits=1)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    want = O.attention(q.float().numpy(), o, D ** -0.5, True, blocks)
+    err = float(np.abs(got - want).max()) / 1e5
+    assert err <= ATOL, err
