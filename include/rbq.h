@@ -282,11 +282,18 @@ size_t rbq_quant_attn_workspace_bytes(const rbq_kv_cache* c, int32_t H_q, int32_
  * Scores, softmax and the P.V accumulation run in fp32.  Keys [0, offset)
  * are read.  Any L from 1 (decode) to offset (prefill-length blocks) is
  * taken; L is the number of trailing cache rows the query block stands for.
- * Kernels: the default configuration (head_dim 256, group 64, K4/V3) runs a
- * dedicated kernel (blocks of 8 query rows per kv head); every other
- * configuration runs the general tile kernel (one wave per 16 rows up to
- * 16 rows per kv head, else blocks of 64 query rows against 32-key tiles
- * decoded once per workgroup).  With RBQ_FLAG_ROUND_ROTATED in the cache flags the rotated q
+ * Kernels: from 96 query rows per kv head (H_q / H_kv x L) over a bf16
+ * cache with 4-bit K codes in groups of 64 (head_dim 128 or 256, 2- to 4-bit
+ * V codes) a prefill kernel (blocks of 128 query rows sharing each decoded
+ * 32-key tile; in layouts other than the default only with one key split:
+ * splits == 1, or an automatic plan whose blocks fill the GPU); otherwise
+ * the default configuration (head_dim 256, group 64, K4/V3) runs a dedicated
+ * kernel (blocks of 8 query rows per kv head) and every other configuration
+ * the general tile kernel (one wave per 16 rows up to 16 rows per kv head,
+ * else blocks of 64 query rows against 32-key tiles decoded once per
+ * workgroup).  The choice depends only on the cache descriptor, H_q, L and
+ * splits, so rbq_quant_attn_splits and rbq_quant_attn_workspace_bytes
+ * describe the call.  With RBQ_FLAG_ROUND_ROTATED in the cache flags the rotated q
  * is rounded to the dtype.  Errors: RBQ_EINVAL (null pointers, H_q % H_kv !=
  * 0, splits < 0), RBQ_ERANGE (L < 1 or L > offset), RBQ_EWORKSPACE,
  * RBQ_EUNSUPPORTED, RBQ_EHIP.

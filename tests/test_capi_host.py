@@ -364,3 +364,46 @@ def test_status_strings():
     for st in range(0, -7, -1):
         assert lib.rbq_status_string(st).decode() not in ("", "unknown status")
     assert lib.rbq_status_string(-99).decode() == "unknown status"
+
+
+def test_prefill_plan_selection():
+    """Which plan a call gets: from 96 query rows per kv head over a bf16 cache
+    with 4-bit K in groups of 64 the prefill kernel's (128-row blocks, split
+    records of 8 rows in the default layout, one split in the others); below
+    that, or with an fp16 cache, the dedicated kernel's (8-row blocks, a
+    multiple of 8 splits with several row blocks); other widths the tile
+    kernel's."""
+    lib = capi.library()
+    fake = 0x1000
+    ptrs = dict(k_words=fake, k_scales=fake, k_biases=fake, v_words=fake, v_scales=fake,
+                v_biases=fake)
+    by = ctypes.byref
+    rec = (16 + 8 * 256) * 4
+    # default layout, bf16, 96 rows per kv head (16 q heads / 2, L = 12): two
+    # 128-row blocks, 128 splits capped at one 256-key round each (40)
+    d = _host_desc(B=1, H=2, cap=10496, off=10240, **ptrs)
+    assert lib.rbq_quant_attn_splits(by(d), 16, 12) == 40
+    assert lib.rbq_quant_attn_workspace_bytes(by(d), 16, 12, 0) == 2 * 12 * 40 * rec
+    # 88 rows: the dedicated kernel, 11 row blocks -> 16 splits
+    assert lib.rbq_quant_attn_splits(by(d), 16, 11) == 16
+    # the same 96 rows over an fp16 cache: the dedicated kernel
+    d16 = _host_desc(B=1, H=2, cap=10496, off=10240, dtype=capi.RBQ_F16, **ptrs)
+    assert lib.rbq_quant_attn_splits(by(d16), 16, 12) == 16
+    assert lib.rbq_quant_attn_workspace_bytes(by(d16), 16, 12, 0) == 2 * 12 * 16 * rec
+    # head_dim 128, K4/V4, group 64, bf16: 2048-token chunk of 16 q heads / 2
+    # (256 blocks of 128 rows): the prefill kernel, one split, no workspace
+    d128 = _host_desc(B=1, H=2, cap=10496, off=10240, **ptrs)
+    d128.head_dim, d128.v_bits = 128, 4
+    assert lib.rbq_quant_attn_splits(by(d128), 16, 2048) == 1
+    assert lib.rbq_quant_attn_workspace_bytes(by(d128), 16, 2048, 0) == 0
+    # 256 rows per kv head (32 blocks): too few for one split -> the tile
+    # kernel's plan (key splits, records); an explicit single split -> the
+    # prefill kernel without records
+    assert lib.rbq_quant_attn_splits(by(d128), 16, 32) > 1
+    assert lib.rbq_quant_attn_workspace_bytes(by(d128), 16, 32, 0) > 0
+    assert lib.rbq_quant_attn_workspace_bytes(by(d128), 16, 32, 1) == 0
+    # 5-bit K codes: the tile kernel
+    d5 = _host_desc(B=1, H=2, cap=10496, off=10240, **ptrs)
+    d5.head_dim, d5.k_bits, d5.v_bits = 128, 5, 4
+    assert lib.rbq_quant_attn_workspace_bytes(by(d5), 16, 2048, 1) == 0
+    assert lib.rbq_quant_attn_splits(by(d5), 16, 2048) >= 1
