@@ -154,3 +154,25 @@ def test_tiny_groups_bit_exact(n, dev):
     got = out.cpu().numpy()
     assert np.isfinite(got).all()
     assert float(np.abs(got - want).max()) <= ATOL
+
+
+def test_all_masked_rows_with_128_splits(dev):
+    # a long key range over few (b, kv head) units: 128 key splits merged by
+    # the merge kernel's 4 thread groups in two rounds, rows that keep no key
+    print("[all-masked rows] 128 splits", flush=True)
+    B, Hq, Hkv, T, L = 1, 16, 2, 4096, 2
+    g, o, blocks = _pair(dev, 85, B, Hkv, T)
+    q = W.random_rows([85, 3], (B, Hq, L, 256), "bf16")
+    rng = np.random.default_rng(86)
+    m = rng.random((B, Hq, L, T)) < 0.5
+    m[0, 2, 1, :] = False
+    m[0, 9, 0, :] = False
+    for mask, ref in ((torch.from_numpy(m), m), (None, None)):
+        out = g.attend(q.to(dev), scale=1 / 16, causal=True, splits=128,
+                       mask=None if mask is None else mask.to(dev))
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.isfinite(got).all()
+        want = O.attention(q.float().numpy(), o, 1 / 16, True, blocks, mask=ref)
+        err = float(np.abs(got - want).max())
+        assert err <= ATOL, err
