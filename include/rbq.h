@@ -289,8 +289,9 @@ size_t rbq_quant_attn_workspace_bytes(const rbq_kv_cache* c, int32_t H_q, int32_
  * splits == 1, or an automatic plan whose blocks fill the GPU); otherwise
  * the default configuration (head_dim 256, group 64, K4/V3) runs a dedicated
  * kernel (blocks of 8 query rows per kv head) and every other configuration
- * the general tile kernel (one wave per 16 rows up to 16 rows per kv head,
- * else blocks of 64 query rows against 32-key tiles decoded once per
+ * the general tile kernel (one wave per workgroup up to 8 query rows per kv
+ * head, and up to 16 at head_dim 64 or 128 or in groups of 32 at head_dim
+ * 256; else blocks of 64 query rows against 32-key tiles decoded once per
  * workgroup).  The choice depends only on the cache descriptor, H_q, L and
  * splits, so rbq_quant_attn_splits and rbq_quant_attn_workspace_bytes
  * describe the call.  With RBQ_FLAG_ROUND_ROTATED in the cache flags the rotated q

@@ -1460,28 +1460,28 @@ static int tile_workgroups_per_cu(int D, int ng, int W, int kbits, int vbits, bo
     RBQ_FIT(64, 1) RBQ_FIT(64, 2) RBQ_FIT(128, 1) RBQ_FIT(128, 2) RBQ_FIT(128, 4)
 #undef RBQ_FIT
 #define RBQ_FIT(D_, NG_) \
-    if (D == D_ && ng == NG_) return tile_fit<D_, NG_, 4>(kbits, vbits, false);
-    RBQ_FIT(256, 2) RBQ_FIT(256, 4)
-    if (D == 256 && ng == 8)
-        return W == 4 ? tile_fit<256, 8, 4>(kbits, vbits, false) : tile_fit<256, 8, 1>(kbits, vbits, false);
+    if (D == D_ && ng == NG_) return W == 4 ? tile_fit<D_, NG_, 4>(kbits, vbits, false) : tile_fit<D_, NG_, 1>(kbits, vbits, false);
+    RBQ_FIT(256, 2) RBQ_FIT(256, 4) RBQ_FIT(256, 8)
 #undef RBQ_FIT
     return 1;
 }
 
 int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, TilePlan* p) {
     const int64_t G = (int64_t)(H_q / c->H_kv) * L;
-    // waves per workgroup, 16 rows each: one wave for up to 16 rows at
-    // head_dim <= 128 and at head_dim 256 with 8 groups per row (1.4x faster
-    // there than four-wave blocks); four otherwise.  At head_dim 256 the
-    // one-wave builds hold more than 256 registers, so they run one wave per
-    // SIMD with part of their state in the accumulation registers: with 2
-    // groups per row that is slower than four-wave blocks, and the build for
-    // 4 groups per row gives wrong results (errors up to 0.5 that grow with
-    // the tiles a workgroup walks) that the 2- and 8-group builds of the same
-    // source do not show and that no difference in the source explains: that
-    // build is not used
+    // waves per workgroup, 16 rows each: one wave for up to 8 rows (paired
+    // hi / lo operand rows; at head_dim 256 with 4 groups per row 7 % faster
+    // than four-wave blocks, with 2 groups 1.5 %), and for up to 16 rows at
+    // head_dim <= 128 and at head_dim 256 with 8 groups per row (1.4x
+    // faster there); four otherwise.  At head_dim 256 the one-wave builds
+    // hold more than 256 registers, so they run one wave per SIMD with part
+    // of their state in the accumulation registers: for 9 to 16 rows with 2
+    // groups per row that is slower than four-wave blocks, and the unpaired
+    // build for 4 groups per row gives wrong results (errors up to 0.7 that
+    // grow with the tiles a workgroup walks) that the paired builds and the
+    // 2- and 8-group builds of the same source do not show and that no
+    // difference in the source explains: that build is not used
     const int ng = c->head_dim / c->group_size;
-    const int W = (G <= 16 && (c->head_dim <= 128 || ng == 8)) ? 1 : 4;
+    const int W = (G <= 8 || (G <= 16 && (c->head_dim <= 128 || ng == 8))) ? 1 : 4;
     // up to 8 rows per kv head at head_dim <= 128 with 4-bit K codes (they
     // enter the MFMAs in place) and 2-, 3- or 4-bit V codes: single-wave
     // workgroups with register-staged tiles (the widths fixed at compile
@@ -1601,16 +1601,25 @@ int tile_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, fl
         else                                                                                      \
             bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_, 1>) : launch(attn_tile_kernel<RBQ_F16, D_, NG_, 1>); \
     } else
+#define RBQ_TILE_CASE_PR(D_, NG_)                                                                 \
+    if (c->head_dim == D_ && ng == NG_) {                                                         \
+        if (p.W == 4)                                                                             \
+            bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_, 4>) : launch(attn_tile_kernel<RBQ_F16, D_, NG_, 4>); \
+        else                                                                                      \
+            bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_, 1, 0, 0, 1>)                         \
+               : launch(attn_tile_kernel<RBQ_F16, D_, NG_, 1, 0, 0, 1>);                          \
+    } else
 #define RBQ_TILE_CASE4(D_, NG_)                                                                   \
     if (c->head_dim == D_ && ng == NG_) {                                                         \
         bf ? launch(attn_tile_kernel<RBQ_BF16, D_, NG_, 4>) : launch(attn_tile_kernel<RBQ_F16, D_, NG_, 4>); \
     } else
     RBQ_TILE_CASE(64, 1) RBQ_TILE_CASE(64, 2) RBQ_TILE_CASE(128, 1) RBQ_TILE_CASE(128, 2)
-    RBQ_TILE_CASE(128, 4) RBQ_TILE_CASE4(256, 2) RBQ_TILE_CASE4(256, 4) RBQ_TILE_CASE(256, 8) {
+    RBQ_TILE_CASE(128, 4) RBQ_TILE_CASE_PR(256, 2) RBQ_TILE_CASE_PR(256, 4) RBQ_TILE_CASE(256, 8) {
         return RBQ_EUNSUPPORTED;
     }
 #undef RBQ_TILE_CASE
 #undef RBQ_TILE_CASE4
+#undef RBQ_TILE_CASE_PR
     if (p.S == 1) {
         const hipError_t e1 = hipGetLastError();
         if (e1 != hipSuccess) {

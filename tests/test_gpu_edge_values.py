@@ -65,7 +65,8 @@ def _rows_equal(g, o, what):
 
 # (head_dim, group, k_bits, v_bits, dtype, B, H_q, H_kv, T, L): the dedicated
 # kernel (8-row blocks) and the tile kernel in both shapes (one wave for up to
-# 16 rows per kv head at head_dim 128, four waves otherwise)
+# 16 rows per kv head at head_dim 128 and up to 8 at head_dim 256 with 4
+# groups, four waves otherwise)
 MASK_CASES = [
     (256, 64, 4, 3, "bf16", 2, 16, 2, 1000, 4),
     (256, 64, 4, 3, "f16", 1, 8, 1, 333, 2),

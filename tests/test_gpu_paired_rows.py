@@ -2,8 +2,8 @@
 
 Calls with at most 8 query rows per kv head whose widths or head dim the
 register-staged shape does not take (K codes other than 4 bits, V codes
-above 4 bits, head_dim 256 with 8 groups) decode each tile into LDS and
-pair the hi and lo parts of the query rows in one matrix operand.  Covered
+above 4 bits, head_dim 256) decode each tile into LDS and pair the hi and
+lo parts of the query rows in one matrix operand.  Covered
 here: head_dim 64, 128 and 256, 1, 2, 4 and 8 groups per row, K and V widths
 from 2 to 8 bits, both dtypes, both rotations and the page's rotation
 precision; 1, 4 and 8 rows per kv head (GQA rows and causal verify rows), a
@@ -30,6 +30,8 @@ VARS = [
     (128, 128, 3, 2, "f16", False, False),
     (128, 32, 5, 6, "bf16", False, True),
     (64, 32, 4, 5, "f16", False, False),
+    (256, 64, 4, 4, "bf16", True, False),
+    (256, 128, 4, 2, "f16", False, True),
 ]
 # (B, H_q, H_kv, L): rows per kv head G = H_q / H_kv * L
 SHAPES = [(2, 8, 2, 1), (1, 4, 1, 2), (1, 16, 2, 1), (1, 2, 2, 1)]
@@ -80,10 +82,11 @@ def test_paired_rows_staged(var, splits, dev):
 
 
 @pytest.mark.parametrize("splits", [0, 1])
-def test_paired_rows_staged_masks(splits, dev):
-    var = (256, 32, 6, 5, "bf16", True, False)
+@pytest.mark.parametrize("var", [(256, 32, 6, 5, "bf16", True, False),
+                                 (256, 64, 4, 4, "bf16", True, False)], ids=_vid)
+def test_paired_rows_staged_masks(var, splits, dev):
     B, Hq, Hkv, L, T = 2, 8, 2, 2, 555
-    print(f"[paired rows] masks splits={splits}", flush=True)
+    print(f"[paired rows] masks {_vid(var)} splits={splits}", flush=True)
     c, oc, blocks = _setup(var, dev, B, Hkv, T, 65)
     q = W.random_rows([66, 0], (B, Hq, L, 256), "bf16")
     rng = np.random.default_rng([66, 1])

@@ -32,7 +32,7 @@ VARIANTS = [
     (64, 64, 4, 3, "bf16", False, False),
     (256, 64, 4, 3, "bf16", True, True),   # default sizes, dedicated kernels, both options
     (128, 32, 4, 4, "bf16", False, False),
-    (256, 64, 4, 4, "f16", True, False),   # head_dim 256, 4 groups: four-wave blocks also for 1-16 rows
+    (256, 64, 4, 4, "f16", True, False),   # head_dim 256, 4 groups: paired single-wave rows up to 8 rows
     (256, 64, 4, 3, "f16", False, True),
 ]
 
@@ -262,15 +262,20 @@ def test_tile_kernel_single_key(var, dev):
 
 
 # single-wave tile workgroups (up to 16 rows per kv head at head_dim <= 128,
-# and at head_dim 256 with 8 groups per row) with one split, so that each
-# workgroup walks many tiles (the running scale powers and the staging
+# and at head_dim 256 with 8 groups per row; up to 8 rows, paired hi / lo
+# operand rows, at head_dim 256 with 2 and 4 groups) with one split, so that
+# each workgroup walks many tiles (the running scale powers and the staging
 # transfers are carried across all of them): 4 groups per row (two scale /
-# bias items per thread), 2 and 8
+# bias items per thread), 2 and 8; at head_dim 256 with 2 or 4 groups, L = 2
+# (16 rows) runs the four-wave shape over the same keys
 @pytest.mark.parametrize("var", [(128, 32, 4, 4, "bf16", False, False),
                                  (128, 32, 3, 5, "f16", True, False),
                                  (128, 64, 4, 4, "bf16", True, False),
                                  (256, 32, 4, 4, "bf16", False, False),
-                                 (256, 32, 6, 2, "f16", True, False)], ids=_vid)
+                                 (256, 32, 6, 2, "f16", True, False),
+                                 (256, 64, 4, 4, "f16", True, False),
+                                 (256, 64, 5, 2, "bf16", False, False),
+                                 (256, 128, 4, 3, "bf16", True, False)], ids=_vid)
 @pytest.mark.parametrize("splits", [1, 2])
 def test_single_wave_tile_kernel_many_tiles(var, splits, dev):
     print(f"[single-wave tiles] {_vid(var)} splits={splits}", flush=True)
