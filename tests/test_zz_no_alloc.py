@@ -3,8 +3,9 @@
 array) against rbq_quant_attn_decode with a workspace, through the C ABI:
 two calls in a row, the second on a smaller input, each output bit for bit
 that of the workspace call (same kernels, same split plan) and within the
-tolerance of the oracle; and a call that needs more than the fixed array is
-refused before anything is launched."""
+tolerance of the oracle, for the 8-row blocks, the tile kernel and the
+prefill kernel's split records; and a call that needs more than the fixed
+array is refused before anything is launched."""
 import numpy as np
 import pytest
 import torch
@@ -54,6 +55,32 @@ def test_noalloc_matches_the_workspace_call_twice(D):
         torch.cuda.synchronize()
         assert torch.equal(got, want), float((got - want).abs().max())
         ref = O.attention(q.cpu().float().numpy(), oc, D ** -0.5, True, blocks)
+        assert float(np.abs(got.cpu().numpy() - ref).max()) <= ATOL
+
+
+def test_noalloc_prefill_kernel_records_then_a_smaller_call():
+    # 128 query rows per kv head (the prefill kernel) over few (b, kv head)
+    # units: key splits whose records go to the array; then a call of 48
+    # rows (8-row blocks) whose records overwrite the first call's
+    dev = torch.device("cuda:0")
+    print("[no-alloc attention] prefill kernel", flush=True)
+    blocks = O.rotation_blocks(W.rotation_draws(1, 256))
+    rot = rbq.build_block_so4(256, 1, dev)
+    shapes = [(1, 16, 2, 3000, 16), (1, 8, 2, 900, 12)]
+    for n, (B, Hq, Hkv, T, L) in enumerate(shapes):
+        c, oc = _cache(dev, 95 + n, B, Hkv, T, blocks, rot)
+        q = W.random_rows([95 + n, 3], (B, Hq, L, 256), "bf16").to(dev)
+        assert capi.rbq_quant_attn_splits(c.desc, Hq, L) > 1
+        need = capi.rbq_quant_attn_workspace_bytes(c.desc, Hq, L, 0)
+        assert 0 < need <= capi.RBQ_SCRATCH_BYTES
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        want = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        got = torch.full(q.shape, float("nan"), dtype=torch.float32, device=dev)
+        capi.rbq_quant_attn_decode(c.desc, q, 1 / 16, True, rot, want, 0, ws)
+        capi.rbq_quant_attn_decode_noalloc(c.desc, q, 1 / 16, True, rot, got, 0)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), float((got - want).abs().max())
+        ref = O.attention(q.cpu().float().numpy(), oc, 1 / 16, True, blocks)
         assert float(np.abs(got.cpu().numpy() - ref).max()) <= ATOL
 
 
