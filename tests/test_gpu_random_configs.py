@@ -6,7 +6,10 @@ against the oracle and the attention within 2e-3 of it.  The draws reach
 every attention kernel (the dedicated 8-row blocks, the tile kernel's
 single-wave, paired-row, register-staged and four-wave shapes, the prefill
 kernel) with shapes no hand-written case picked; a few draws are steered
-to 96 or more rows per kv head so that the prefill kernel takes them.
+to 96 or more rows per kv head so that the prefill kernel takes them.  Also
+seeded random sequences of cache operations (appends, trims, attention
+calls, one-call decoding steps, snapshots and restores), the cache compared
+with the oracle's after every operation.
 """
 import numpy as np
 import pytest
@@ -112,3 +115,81 @@ def test_random_configuration(cfg, dev):
     ref = O.attention(q.float().numpy(), oc, scale, True, blocks, mask=m_np)
     err = float(np.abs(out.cpu().numpy() - ref).max())
     assert err <= ATOL, err
+
+
+def _assert_same_cache(c, oc, what):
+    assert c.offset == oc.offset, (what, c.offset, oc.offset)
+    if oc.offset == 0:
+        return
+    rows = c.rows()
+    for name, oname in NAMES:
+        got = rows[name].cpu()
+        got = got.numpy().view(np.uint32) if "words" in name else got.float().numpy()
+        ref = oc.arrays[oname][:, :, :oc.offset]
+        assert np.array_equal(got, ref), f"{what}, {name}: {int((got != ref).sum())} mismatches"
+
+
+# random sequences of cache operations on a random configuration: appends of
+# 1-200 rows, trims, attention calls, one-call decoding steps (append n rows
+# and attend with L = n rows, causal at the new offset), snapshots and
+# restores; the cache against the oracle's after every operation
+@pytest.mark.parametrize("seed", range(24))
+def test_random_operation_sequence(seed, dev):
+    rng = np.random.default_rng([2027, seed])
+    D = int(rng.choice([64, 128, 256]))
+    gs = int(rng.choice([g for g in (32, 64, 128) if g <= D]))
+    kb, vb = int(rng.choice(BITS)), int(rng.choice(BITS))
+    if rng.random() < 0.4:
+        D, gs, kb, vb = 256, 64, 4, 3
+    dtype = str(rng.choice(["bf16", "f16"]))
+    two = bool(rng.random() < 0.4)
+    B, Hkv = int(rng.integers(1, 3)), int(rng.choice([1, 2]))
+    Hq = Hkv * int(rng.choice([1, 2, 8]))
+    print(f"[random operations] seed {seed}: D{D} g{gs} k{kb}v{vb} {dtype} B{B} H{Hq}-{Hkv}",
+          flush=True)
+    tdt = W._TORCH_DTYPES[dtype]
+    blocks = O.rotation_blocks(W.rotation_draws(seed, D), mode="two_sided" if two else "printed")
+    rot = rbq.build_block_so4(D, seed, dev, two_sided=two)
+    c = rbq.RotatedQuantKVCache(B, Hkv, dtype=tdt, device=dev, rot=rot, head_dim=D,
+                                group_size=gs, k_bits=kb, v_bits=vb)
+    oc = O.QuantKVCache(k_bits=kb, v_bits=vb, dtype=dtype, group=gs)
+    snap = None
+    for step in range(10):
+        op = str(rng.choice(["append", "append", "trim", "attend", "step", "snapshot", "restore"]))
+        if c.offset == 0 and op in ("attend", "trim", "snapshot"):
+            op = "append"
+        what = f"step {step} {op}"
+        if op in ("append", "step"):
+            n = int(rng.integers(1, 201)) if op == "append" else int(rng.integers(1, 5))
+            k = W.random_rows([seed, step, 1], (B, Hkv, n, D), dtype, "student_t3")
+            v = W.random_rows([seed, step, 2], (B, Hkv, n, D), dtype)
+            if op == "append":
+                c.append(k.to(dev), v.to(dev))
+                oc.append(k.float().numpy(), v.float().numpy(), blocks)
+            else:
+                q = W.random_rows([seed, step, 3], (B, Hq, n, D), dtype)
+                out = c.append_attend(k.to(dev), v.to(dev), q.to(dev), scale=D ** -0.5, causal=True)
+                torch.cuda.synchronize()
+                oc.append(k.float().numpy(), v.float().numpy(), blocks)
+                ref = O.attention(q.float().numpy(), oc, D ** -0.5, True, blocks)
+                err = float(np.abs(out.cpu().numpy() - ref).max())
+                assert err <= ATOL, (what, err)
+        elif op == "trim":
+            n = int(rng.integers(0, c.offset + 1))
+            assert c.trim(n) == oc.trim(n)
+        elif op == "attend":
+            L = int(rng.integers(1, min(c.offset, 16) + 1))
+            splits = int(rng.choice([0, 1, 3]))
+            q = W.random_rows([seed, step, 4], (B, Hq, L, D), dtype)
+            out = c.attend(q.to(dev), scale=D ** -0.5, causal=True, splits=splits)
+            torch.cuda.synchronize()
+            ref = O.attention(q.float().numpy(), oc, D ** -0.5, True, blocks)
+            err = float(np.abs(out.cpu().numpy() - ref).max())
+            assert err <= ATOL, (what, err)
+        elif op == "snapshot":
+            snap = (c.snapshot(), O.snapshot([oc]))
+        elif op == "restore" and snap is not None:
+            c.restore(snap[0])
+            O.restore([oc], snap[1])
+        torch.cuda.synchronize()
+        _assert_same_cache(c, oc, what)
