@@ -1479,7 +1479,10 @@ int tile_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Til
     // build for 4 groups per row gives wrong results (errors up to 0.7 that
     // grow with the tiles a workgroup walks) that the paired builds and the
     // 2- and 8-group builds of the same source do not show and that no
-    // difference in the source explains: that build is not used
+    // difference in the source explains; built with the matrix results kept
+    // in VGPRs instead of AGPRs the same source gives the right results, and
+    // for 9 to 16 rows it is no faster than four-wave blocks: that build is
+    // not used
     const int ng = c->head_dim / c->group_size;
     const int W = (G <= 8 || (G <= 16 && (c->head_dim <= 128 || ng == 8))) ? 1 : 4;
     // up to 8 rows per kv head at head_dim <= 128 with 4-bit K codes (they
