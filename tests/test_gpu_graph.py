@@ -1,5 +1,7 @@
 """GPU: the decode step (append one token, attend; as two calls and as the
-one-call step) captured in a HIP graph.
+one-call step) captured in a HIP graph, and attention calls of the prefill
+kernel, the tile kernel and the entry point that allocates nothing captured
+the same way.
 
 The launches read their arguments as captured: a replay appends the token at
 the captured row again and attends over the same rows, so every replay must
@@ -76,3 +78,68 @@ def test_step_graph_replays_equal_eager(T, one_call):
         torch.cuda.synchronize()
         assert torch.equal(out, want), f"replay {r}: output differs from the eager step"
         assert torch.equal(c.arrays["k_words"][:, :, T - 1], words), f"replay {r}: appended row"
+
+
+# (kind, head_dim, group, k_bits, v_bits, B, H_q, H_kv, T, L): attention calls
+# of the other kernels captured the same way: the prefill kernel with key
+# splits and the record merge (128 rows per kv head), the tile kernel (a
+# head_dim-128 K4/V4 decode, register-staged tiles, and a long block of a
+# 5/6-bit layout, four-wave tiles) and the entry point that allocates nothing
+# (its records in the library's fixed array) on the 8-row blocks and on the
+# prefill kernel
+GRAPH_CALLS = [
+    ("prefill", 256, 64, 4, 3, 1, 16, 2, 3000, 16),
+    ("tile_decode", 128, 64, 4, 4, 2, 16, 2, 4000, 1),
+    ("tile_block", 128, 32, 5, 6, 1, 8, 2, 900, 24),
+    ("noalloc_decode", 256, 64, 4, 3, 2, 16, 2, 5000, 1),
+    ("noalloc_prefill", 256, 64, 4, 3, 1, 16, 2, 3000, 16),
+]
+
+
+@pytest.mark.parametrize("case", GRAPH_CALLS, ids=[c[0] for c in GRAPH_CALLS])
+def test_attention_graph_replays_equal_eager(case):
+    kind, D, gs, kb, vb, B, Hq, Hkv, T, L = case
+    dev = torch.device("cuda:0")
+    print(f"graph attention {kind}: D={D} g{gs} k{kb}v{vb} B={B} Hq={Hq} Hkv={Hkv} T={T} L={L}",
+          flush=True)
+    rot = rbq.build_block_so4(D, W.ROTATION_SEED, dev)
+    g = torch.Generator().manual_seed(11)
+    k = torch.randn(B, Hkv, T, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, T, D, generator=g).to(torch.bfloat16)
+    c = rbq.RotatedQuantKVCache(B, Hkv, device=dev, rot=rot, head_dim=D, group_size=gs,
+                                k_bits=kb, v_bits=vb)
+    c.append(k.to(dev), v.to(dev))
+    other = rbq.RotatedQuantKVCache(B, Hkv, device=dev, rot=rot, head_dim=D, group_size=gs,
+                                    k_bits=kb, v_bits=vb)
+    other.append(v.to(dev), k.to(dev))
+    q = torch.randn(B, Hq, L, D, generator=g).to(torch.bfloat16).to(dev)
+    out = torch.empty(B, Hq, L, D, dtype=torch.float32, device=dev)
+    out_other = torch.empty_like(out)
+    noalloc = kind.startswith("noalloc")
+    assert capi.rbq_quant_attn_splits(c.desc, Hq, L) > 1
+    ws = None if noalloc else c.workspace(Hq, L)
+    ws_other = None if noalloc else torch.zeros_like(ws)
+    scale = D ** -0.5
+
+    def call(cache, o, w):
+        if noalloc:
+            capi.rbq_quant_attn_decode_noalloc(cache.desc, q, scale, True, rot, o, 0)
+        else:
+            capi.rbq_quant_attn_decode(cache.desc, q, scale, True, rot, o, 0, w)
+
+    call(c, out, ws)
+    torch.cuda.synchronize()
+    want = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    out.zero_()
+    with torch.cuda.graph(graph, stream=cap):
+        call(c, out, ws)
+    torch.cuda.synchronize()
+    for r in range(4):
+        out.fill_(float("nan"))
+        graph.replay()
+        # eager work between replays (with the fixed array: the same array)
+        call(other, out_other, ws_other)
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), f"replay {r}: output differs from the eager call"
