@@ -104,6 +104,7 @@ def timed_windows(fn, untimed: int, n_windows: int, per_window: int) -> dict:
     return {"median": round(statistics.median(vals), 3),
             "p10": round(float(np.percentile(vals, 10)), 3),
             "p90": round(float(np.percentile(vals, 90)), 3),
+            "mean": round(statistics.fmean(vals), 3),
             "untimed_calls": untimed, "windows": n_windows, "calls_per_window": per_window}
 
 
@@ -426,8 +427,6 @@ def tree_verify(rbq, W, dev, rot, n_calls: int = 200) -> dict:
     v = W.random_rows([40, 2], (1, Hkv, T0, 256), "bf16").to(dev)
     one = rbq.RotatedQuantKVCache(1, Hkv, device=dev, rot=rot)
     one.append(k, v)
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     # tile copy, timed on its own (one batch-1 cache into 4 paths, repeatedly)
     tiled = []
     for _ in range(16):
@@ -444,14 +443,9 @@ def tree_verify(rbq, W, dev, rot, n_calls: int = 200) -> dict:
         d.arrays = one._alloc(one.capacity, P)
         d._bind(d.desc, d.arrays, one.capacity)
         dsts.append(d)
-    for i in range(4):
-        rbq.rbq_kv_copy_batch(tiled[i % 16].desc, 0, 0, dsts[i % 2].desc)
-    ev0.record(stream)
-    for i in range(40):
-        rbq.rbq_kv_copy_batch(tiled[i % 16].desc, 0, 0, dsts[i % 2].desc)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    tile_us = ev0.elapsed_time(ev1) * 1e3 / 40
+    tile_t = timed_windows(lambda i: rbq.rbq_kv_copy_batch(tiled[i % 16].desc, 0, 0, dsts[i % 2].desc),
+                           untimed=4, n_windows=5, per_window=8)
+    tile_us = tile_t["mean"]
     tile_bytes = Hkv * T0 * 256 * (1 + P)
     del dsts
     kd = W.random_rows([41, 1], (P, Hkv, L, 256), "bf16").to(dev)
@@ -474,19 +468,14 @@ def tree_verify(rbq, W, dev, rot, n_calls: int = 200) -> dict:
     ws = tiled[0].workspace(Hq, L)
 
     def timed(mask, causal):
-        for i in range(50):
-            c = tiled[i % 16]
-            rbq.rbq_quant_attn_decode(c.desc, q, 1 / 16, causal, rot, out, 0, ws, mask)
-        ev0.record(stream)
-        for i in range(n_calls):
-            c = tiled[i % 16]
-            rbq.rbq_quant_attn_decode(c.desc, q, 1 / 16, causal, rot, out, 0, ws, mask)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) * 1e3 / n_calls
+        return timed_windows(
+            lambda i: rbq.rbq_quant_attn_decode(tiled[i % 16].desc, q, 1 / 16, causal, rot, out, 0,
+                                                ws, mask),
+            untimed=50, n_windows=10, per_window=n_calls // 10)
 
-    masked_us = timed(keep, False)
-    causal_us = timed(None, True)
+    masked_t = timed(keep, False)
+    causal_t = timed(None, True)
+    masked_us, causal_us = masked_t["mean"], causal_t["mean"]
     alg = P * Hkv * T * 256 + P * Hq * L * 256 * (2 + 4) + L * T
     gbs = alg / (masked_us * 1e-6) / 1e9
     return {
@@ -495,13 +484,15 @@ def tree_verify(rbq, W, dev, rot, n_calls: int = 200) -> dict:
         "bound": "hbm",
         "alg_bytes_per_call": alg,
         "avg_us": round(masked_us, 3),
+        "us": masked_t,
         "achieved": round(gbs, 2),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(gbs / HBM_PEAK_GBS, 4),
         "verified_tokens_per_s": round(P * L / (masked_us * 1e-6), 1),
         "causal_mask_avg_us": round(causal_us, 3),
-        "tile_copy": {"avg_us": round(tile_us, 3), "bytes": tile_bytes,
+        "causal_mask_us": causal_t,
+        "tile_copy": {"avg_us": round(tile_us, 3), "us": tile_t, "bytes": tile_bytes,
                       "achieved": round(tile_bytes / (tile_us * 1e-6) / 1e9, 2)},
     }
 
@@ -525,20 +516,13 @@ def append_throughput(rbq, W, dev, rot, n_calls: int = 32) -> dict:
     del k, v
     base = W.random_rows([70, 3], (B, Hkv, n, D), "bf16").to(dev)
     ins = [(base.roll(i, dims=3).contiguous(), base.roll(-i, dims=3).contiguous()) for i in range(16)]
-    stream = torch.cuda.current_stream()
-    for i in range(8):
+    def one(i):
         c = caches[i % 4]
         rbq.rbq_kv_quant_append(c.desc, ins[i % 16][0], ins[i % 16][1], rot)
         rbq.rbq_kv_trim(c.desc, n)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(n_calls):
-        c = caches[i % 4]
-        rbq.rbq_kv_quant_append(c.desc, ins[i % 16][0], ins[i % 16][1], rot)
-        rbq.rbq_kv_trim(c.desc, n)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    us = ev0.elapsed_time(ev1) * 1e3 / n_calls
+
+    t = timed_windows(one, untimed=8, n_windows=4, per_window=n_calls // 4)
+    us = t["mean"]
     rows = B * Hkv * n
     nbytes = rows * (2 * D * 2 + 256)
     gbs = nbytes / (us * 1e-6) / 1e9
@@ -551,6 +535,7 @@ def append_throughput(rbq, W, dev, rot, n_calls: int = 32) -> dict:
                 "for context",
         "bytes_per_call": nbytes,
         "avg_us": round(us, 3),
+        "us": t,
         "achieved": round(gbs, 2),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
@@ -599,14 +584,9 @@ def prefill(rbq, W, dev, rot, n_calls: int = 10, head_dim: int = 256) -> dict:
     T = T0 + L
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     ws = c.workspace(Hq, L)
-    for _ in range(2):
-        rbq.rbq_quant_attn_decode(c.desc, q, D ** -0.5, True, rot, out, 0, ws)
-    ev0.record(stream)
-    for _ in range(n_calls):
-        rbq.rbq_quant_attn_decode(c.desc, q, D ** -0.5, True, rot, out, 0, ws)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    us = ev0.elapsed_time(ev1) * 1e3 / n_calls
+    t = timed_windows(lambda i: rbq.rbq_quant_attn_decode(c.desc, q, D ** -0.5, True, rot, out, 0, ws),
+                      untimed=2, n_windows=5, per_window=n_calls // 5)
+    us = t["mean"]
     pairs = Hq * (L * (T - L) + L * (L + 1) // 2)  # (query row, visible key) pairs
     flops = 4 * D * pairs
     tfs = flops / (us * 1e-6) / 1e12
@@ -620,6 +600,7 @@ def prefill(rbq, W, dev, rot, n_calls: int = 10, head_dim: int = 256) -> dict:
         "bound": "mfma",
         "alg_flops_per_call": flops,
         "avg_us": round(us, 2),
+        "us": t,
         "achieved": round(tfs, 2),
         "peak": 2500.0,
         "unit": "TFLOP/s",
@@ -650,16 +631,10 @@ def variant_decode(rbq, W, dev, n_calls: int = 200) -> dict:
     q = W.random_rows([60, 3], (B, Hq, 1, D), "bf16").to(dev)
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     ws = caches[0].workspace(Hq, 1)
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for i in range(20):
-        rbq.rbq_quant_attn_decode(caches[i % 5].desc, q, D ** -0.5, True, rot, out, 0, ws)
-    ev0.record(stream)
-    for i in range(n_calls):
-        rbq.rbq_quant_attn_decode(caches[i % 5].desc, q, D ** -0.5, True, rot, out, 0, ws)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    us = ev0.elapsed_time(ev1) * 1e3 / n_calls
+    t = timed_windows(
+        lambda i: rbq.rbq_quant_attn_decode(caches[i % 5].desc, q, D ** -0.5, True, rot, out, 0, ws),
+        untimed=20, n_windows=10, per_window=n_calls // 10)
+    us = t["mean"]
     row = D * kb // 8 + D * vb // 8 + 4 * (D // gs) * 2  # packed K, V and the four meta arrays
     alg = B * Hkv * T * row + B * Hq * D * (2 + 4)
     gbs = alg / (us * 1e-6) / 1e9
@@ -669,6 +644,7 @@ def variant_decode(rbq, W, dev, n_calls: int = 200) -> dict:
         "bound": "hbm",
         "alg_bytes_per_call": alg,
         "avg_us": round(us, 3),
+        "us": t,
         "achieved": round(gbs, 2),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
