@@ -47,6 +47,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 ATTN_SRC = os.path.join(ROOT, "rotated_bit_quantized_amd", "csrc", "rbq_attn_mfma.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_batched_decode.json")
+APPEND_ALU_FILE = os.path.join(ROOT, "profiles", "append_prefill_chunk_alu.json")
+# vector lane operations per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+# (a wave64 instruction holds its SIMD 4 cycles; x 2 flops per FMA gives the
+# 78.6 TFLOP/s fp64 and unpacked fp32 vector peak)
+VALU_PEAK_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 PROBE_LIB = os.path.join(ROOT, "rotated_bit_quantized_amd", "librbq_probe.so")
 SETTLE_CALLS = 3000   # untimed steps that bring the GPU clock to its steady state first
 
@@ -80,6 +85,20 @@ def measured_traffic(per_launch_alg: float):
     if t.get("kernel_source_sha256_16") != source_hash(ATTN_SRC):
         return None
     return t.get("bytes_per_launch")
+
+
+def append_issue_cycles():
+    """VALU issue cycles per appended row from the committed counter summary
+    of the append kernel, if it was taken on the current kernel sources."""
+    try:
+        with open(APPEND_ALU_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    now = [source_hash(os.path.join(ROOT, p)) for p in t.get("kernel_sources", [])]
+    if not now or now != t.get("kernel_sources_sha256_16"):
+        return None
+    return t.get("valu_issue_cycles_per_row")
 
 
 def timed_windows(fn, untimed: int, n_windows: int, per_window: int) -> dict:
@@ -526,13 +545,25 @@ def append_throughput(rbq, W, dev, rot, n_calls: int = 32) -> dict:
     rows = B * Hkv * n
     nbytes = rows * (2 * D * 2 + 256)
     gbs = nbytes / (us * 1e-6) / 1e9
+    cyc = append_issue_cycles()
+    alu = None
+    if cyc is not None:
+        # lane operations the call's vector instructions occupy (issue cycles
+        # x 16 lanes) per second, against the chip's lane-operation rate
+        tl = rows * cyc * 16 / (us * 1e-6) / 1e12
+        alu = {"bound": "alu", "achieved": round(tl, 2), "peak": round(VALU_PEAK_TLANEOPS, 2),
+               "unit": "T VALU lane-op/s", "frac": round(tl / VALU_PEAK_TLANEOPS, 4),
+               "issue_cycles_per_row": cyc,
+               "from": "profiles/append_prefill_chunk_alu.json (rocprofv3 SQ counters)"}
     return {
         "what": f"append of {n} tokens after {T0} cached, B={B}, {Hkv} kv heads, head_dim 256, bf16, "
                 "K4/V3 group 64 (rbq_kv_quant_append: rotate, quantize, pack, write)",
         "bound": "alu",
-        "note": "VALU-bound, not HBM-bound: about 470 vector instructions per row and wave "
-                "(fp64 rotation, group min/max, codes, packing); frac is against the HBM peak, "
-                "for context",
+        "note": "bound by vector issue, not HBM: 422 vector instructions per row and wave "
+                "(fp64 rotation, group min/max, codes, packing); `roofline` is against the "
+                "vector lane-operation peak (null when the kernel sources changed since the "
+                "counters were taken), achieved / peak / frac against the HBM peak, for context",
+        "roofline": alu,
         "bytes_per_call": nbytes,
         "avg_us": round(us, 3),
         "us": t,
