@@ -463,7 +463,7 @@ def tree_verify(rbq, W, dev, rot, n_calls: int = 200) -> dict:
         d._bind(d.desc, d.arrays, one.capacity)
         dsts.append(d)
     tile_t = timed_windows(lambda i: rbq.rbq_kv_copy_batch(tiled[i % 16].desc, 0, 0, dsts[i % 2].desc),
-                           untimed=4, n_windows=5, per_window=8)
+                           untimed=4, n_windows=5, per_window=20)
     tile_us = tile_t["mean"]
     tile_bytes = Hkv * T0 * 256 * (1 + P)
     del dsts
@@ -490,7 +490,7 @@ def tree_verify(rbq, W, dev, rot, n_calls: int = 200) -> dict:
         return timed_windows(
             lambda i: rbq.rbq_quant_attn_decode(tiled[i % 16].desc, q, 1 / 16, causal, rot, out, 0,
                                                 ws, mask),
-            untimed=50, n_windows=10, per_window=n_calls // 10)
+            untimed=50, n_windows=10, per_window=n_calls // 4)
 
     masked_t = timed(keep, False)
     causal_t = timed(None, True)
@@ -540,7 +540,7 @@ def append_throughput(rbq, W, dev, rot, n_calls: int = 32) -> dict:
         rbq.rbq_kv_quant_append(c.desc, ins[i % 16][0], ins[i % 16][1], rot)
         rbq.rbq_kv_trim(c.desc, n)
 
-    t = timed_windows(one, untimed=8, n_windows=4, per_window=n_calls // 4)
+    t = timed_windows(one, untimed=8, n_windows=5, per_window=n_calls)
     us = t["mean"]
     rows = B * Hkv * n
     nbytes = rows * (2 * D * 2 + 256)
@@ -664,7 +664,7 @@ def variant_decode(rbq, W, dev, n_calls: int = 200) -> dict:
     ws = caches[0].workspace(Hq, 1)
     t = timed_windows(
         lambda i: rbq.rbq_quant_attn_decode(caches[i % 5].desc, q, D ** -0.5, True, rot, out, 0, ws),
-        untimed=20, n_windows=10, per_window=n_calls // 10)
+        untimed=20, n_windows=10, per_window=n_calls // 4)
     us = t["mean"]
     row = D * kb // 8 + D * vb // 8 + 4 * (D // gs) * 2  # packed K, V and the four meta arrays
     alg = B * Hkv * T * row + B * Hq * D * (2 + 4)
