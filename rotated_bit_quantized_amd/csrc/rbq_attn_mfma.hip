@@ -218,6 +218,7 @@ __device__ __forceinline__ float4 rot_row(const float* rot, int col) {
 // row < G.  The 4 columns of a rotation block lie in one lane quad (lane & 3
 // = col & 3): z = sum_k y[block column k] * B[col & 3][k], in fp64, with
 // v = B[col & 3] from rot_row.
+template <int D = kHeadDim>
 __device__ __forceinline__ void store_out(float* out, bool rotated, float4 v, int bh, int G,
                                           int col, int row, float acc, float Ls) {
     const float y = acc * (1.0f / Ls);
@@ -232,7 +233,7 @@ __device__ __forceinline__ void store_out(float* out, bool rotated, float4 v, in
     }
     // the G rows of kv head bh are its n_rep q heads' L rows in (head, row)
     // order, i.e. rows bh * G + row of [B][H_q][L][D]
-    if (row < G) out[((int64_t)bh * G + row) * kHeadDim + col] = z;
+    if (row < G) out[((int64_t)bh * G + row) * D + col] = z;
 }
 
 // Workgroup barrier that orders LDS accesses only: the waves exchange data
@@ -1176,6 +1177,7 @@ struct CArgs {
     const uint32_t* vw;
     const uint16_t* vs;
     const uint16_t* vb;
+    int vbits, vwords, ngroups, group;  // the cache's V layout
 };
 
 // NGR groups of 128 threads each take every NGR-th round of 16 records
@@ -1187,10 +1189,11 @@ struct CArgs {
 // rows 4h .. 4h+3)) or 2 (per 32 columns, thread = (column, rows 2h, 2h+1)),
 // the latter for calls with few (b, kv head) units, where the merge runs on
 // few compute units.
-template <int NGR, int RPT>
+template <int NGR, int RPT, int D>
 __global__ __launch_bounds__(128 * NGR) void attn_mfma_merge_kernel(CArgs a) {
     constexpr int kCols = 128 * RPT / kRows;  // columns per workgroup: 64 or 32
-    constexpr int kCB = kHeadDim / kCols;     // column blocks per (b, kv head, 8 rows)
+    constexpr int kCB = D / kCols;            // column blocks per (b, kv head, 8 rows)
+    constexpr int RF = 2 * kRows + kRows * D;  // floats per split record of head_dim D
     typedef float vecR __attribute__((ext_vector_type(RPT)));
     __shared__ float wts[NGR][kRows * 16];
     __shared__ float stat[NGR][2 * kRows];
@@ -1202,7 +1205,7 @@ __global__ __launch_bounds__(128 * NGR) void attn_mfma_merge_kernel(CArgs a) {
     const int r0 = 8 * (bhr - bh * a.RB);
     const int col = (blockIdx.x - bhr * kCB) * kCols + (tid % kCols);
     const int h = tid / kCols;  // rows RPT h .. RPT h + RPT - 1
-    const float* base = a.rec + (int64_t)bhr * a.S * kRecFloats;
+    const float* base = a.rec + (int64_t)bhr * a.S * RF;
     const int wrow = tid >> 4, wmbr = tid & 15;
     const float4 rv = rot_row(a.rot, col);
     float M[RPT], Ls[RPT], acc[RPT];
@@ -1218,12 +1221,12 @@ __global__ __launch_bounds__(128 * NGR) void attn_mfma_merge_kernel(CArgs a) {
         const int members = (a.S - m0 < 16) ? a.S - m0 : 16;  // <= 0: an empty round
         float2 ml = make_float2(-INFINITY, 0.f);
         if (wmbr < members)
-            ml = *reinterpret_cast<const float2*>(base + (int64_t)(m0 + wmbr) * kRecFloats + 2 * wrow);
+            ml = *reinterpret_cast<const float2*>(base + (int64_t)(m0 + wmbr) * RF + 2 * wrow);
         vecR o[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             const int mbr = (k < members) ? m0 + k : 0;
-            o[k] = *reinterpret_cast<const vecR*>(base + (int64_t)mbr * kRecFloats + 2 * kRows +
+            o[k] = *reinterpret_cast<const vecR*>(base + (int64_t)mbr * RF + 2 * kRows +
                                                   col * kRows + RPT * h);
         }
         const float Mx = max16(ml.x);
@@ -1284,13 +1287,13 @@ __global__ __launch_bounds__(128 * NGR) void attn_mfma_merge_kernel(CArgs a) {
             const int nv = a.causal ? a.T - a.L + (R % a.L) + 1 : a.T;
             const int64_t row0 = (int64_t)bh * a.capacity;
             av = (a.dt == RBQ_BF16)
-                     ? value_column_mean<RBQ_BF16>(a.vw, a.vs, a.vb, row0, nv, col, kVBits, kVWords,
-                                                   kGroups, kGroup)
-                     : value_column_mean<RBQ_F16>(a.vw, a.vs, a.vb, row0, nv, col, kVBits, kVWords,
-                                                  kGroups, kGroup);
+                     ? value_column_mean<RBQ_BF16>(a.vw, a.vs, a.vb, row0, nv, col, a.vbits, a.vwords,
+                                                   a.ngroups, a.group)
+                     : value_column_mean<RBQ_F16>(a.vw, a.vs, a.vb, row0, nv, col, a.vbits, a.vwords,
+                                                  a.ngroups, a.group);
             lv = 1.f;
         }
-        store_out(a.out, a.rot != nullptr, rv, bh, a.G, col, R, av, lv);
+        store_out<D>(a.out, a.rot != nullptr, rv, bh, a.G, col, R, av, lv);
     }
 }
 
@@ -1366,23 +1369,41 @@ void merge_launch(const rbq_kv_cache* c, const float* rec, const float* rot_bloc
     m.vw = c->v_words;
     m.vs = (const uint16_t*)c->v_scales;
     m.vb = (const uint16_t*)c->v_biases;
+    m.vbits = c->v_bits;
+    m.vwords = c->head_dim * c->v_bits / 32;
+    m.ngroups = c->head_dim / c->group_size;
+    m.group = c->group_size;
     // up to 16 splits: one group of 128 threads; more: 2 or 4 groups side
     // by side, so that a long key range (many splits of few kv heads) is
     // merged in S / 64 rounds of loads instead of S / 16 (8 groups would
     // spill registers at 1024 threads)
     // few (b, kv head, 8 rows) units: 32 columns per workgroup, twice the
     // workgroups
+    // (records of head_dim 256 or 128: the dedicated kernel's, or the prefill
+    // kernel's for either head dim)
     const bool narrow = units < kMergeNarrowUnits;
-    const dim3 mg((unsigned)(units * (narrow ? 8 : 4)));
+    const int colblocks = c->head_dim / (narrow ? 32 : 64);
+    const dim3 mg((unsigned)(units * colblocks));
     auto go = [&](auto k1, auto k2, auto k4) {
         if (S <= 16) hipLaunchKernelGGL(k1, mg, dim3(128), 0, s, m);
         else if (S <= 32) hipLaunchKernelGGL(k2, mg, dim3(256), 0, s, m);
         else hipLaunchKernelGGL(k4, mg, dim3(512), 0, s, m);
     };
-    if (narrow)
-        go(attn_mfma_merge_kernel<1, 2>, attn_mfma_merge_kernel<2, 2>, attn_mfma_merge_kernel<4, 2>);
-    else
-        go(attn_mfma_merge_kernel<1, 4>, attn_mfma_merge_kernel<2, 4>, attn_mfma_merge_kernel<4, 4>);
+    if (c->head_dim == kHeadDim) {
+        if (narrow)
+            go(attn_mfma_merge_kernel<1, 2, kHeadDim>, attn_mfma_merge_kernel<2, 2, kHeadDim>,
+               attn_mfma_merge_kernel<4, 2, kHeadDim>);
+        else
+            go(attn_mfma_merge_kernel<1, 4, kHeadDim>, attn_mfma_merge_kernel<2, 4, kHeadDim>,
+               attn_mfma_merge_kernel<4, 4, kHeadDim>);
+    } else {
+        if (narrow)
+            go(attn_mfma_merge_kernel<1, 2, 128>, attn_mfma_merge_kernel<2, 2, 128>,
+               attn_mfma_merge_kernel<4, 2, 128>);
+        else
+            go(attn_mfma_merge_kernel<1, 4, 128>, attn_mfma_merge_kernel<2, 4, 128>,
+               attn_mfma_merge_kernel<4, 4, 128>);
+    }
 }
 
 int mfma_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, float scale,
@@ -1482,7 +1503,7 @@ struct AttnPlan {
 
 int attn_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, AttnPlan* p) {
     const int64_t G = (int64_t)(H_q / c->H_kv) * L;
-    p->prefill = prefill_takes(c, H_q, L, splits);
+    p->prefill = prefill_takes(c, H_q, L);
     p->tile = !p->prefill && !(is_default_config(c) && G <= kDedicatedMaxRows);
     int st;
     if (p->prefill) {

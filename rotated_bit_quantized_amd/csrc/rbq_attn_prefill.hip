@@ -720,20 +720,17 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         return;
     }
-    // this split's record of the lane's row (block of 8 rows R >> 3, row R &
-    // 7); key splits only in the default layout (the plan keeps one split
-    // otherwise)
-    if constexpr (D == kHeadDim) {
-        float* rec = a.rec + ((int64_t)(bh * a.RB + (R >> 3)) * a.S + split) * kRecordFloats;
-        const int ri = R & 7;
+    // this split's record of the lane's row (block of 8 rows R >> 3, row R & 7)
+    constexpr int RF = record_floats(D);
+    float* rec = a.rec + ((int64_t)(bh * a.RB + (R >> 3)) * a.S + split) * RF;
+    const int ri = R & 7;
 #pragma unroll
-        for (int t = 0; t < NB; ++t) {
-            const int g = t >> 2;
+    for (int t = 0; t < NB; ++t) {
+        const int g = t >> 2;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rec[16 + (16 * t + 4 * j + i) * 8 + ri] = (O[t][i] + obg[g]) * vinv[g];
-        }
-        if (j == 0) *reinterpret_cast<float2*>(rec + 2 * ri) = make_float2(m_ref, l);
+        for (int i = 0; i < 4; ++i) rec[16 + (16 * t + 4 * j + i) * 8 + ri] = (O[t][i] + obg[g]) * vinv[g];
     }
+    if (j == 0) *reinterpret_cast<float2*>(rec + 2 * ri) = make_float2(m_ref, l);
 }
 
 }  // namespace
@@ -749,16 +746,12 @@ static void launch_masked(int mt, F&& launch) {
     else launch(attn_prefill_kernel<RBQ_MASK_ADD_DTYPE, D, VB>);
 }
 
-bool prefill_takes(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits) {
+bool prefill_takes(const rbq_kv_cache* c, int32_t H_q, int32_t L) {
     const int64_t G = (int64_t)(H_q / c->H_kv) * L;
     if (G < kPrefillMinRows || c->dtype != RBQ_BF16 || c->k_bits != 4 || c->group_size != 64 ||
         (c->head_dim != 128 && c->head_dim != 256) || c->v_bits < 2 || c->v_bits > 4)
         return false;
-    if (is_default_config(c)) return true;
-    // other layouts: one key split (no records), i.e. an explicit single
-    // split or workgroups that fill the compute units by themselves
-    const int64_t units = (int64_t)c->B * c->H_kv * ((G + kPRows - 1) / kPRows);
-    return splits == 1 || (splits == 0 && units >= 256);
+    return true;
 }
 
 int prefill_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, MfmaPlan* p) {
@@ -784,12 +777,10 @@ int prefill_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, 
     // 32-bit buffer offsets, up to one tile past T
     const int64_t row_bytes = (int64_t)c->head_dim * (c->k_bits > c->v_bits ? c->k_bits : c->v_bits) / 8;
     if ((T + kPTile) * row_bytes > 0x7FFFFFFF) return RBQ_EUNSUPPORTED;
-    // split records exist for the default layout only
-    if (S > 1 && !is_default_config(c)) return RBQ_EUNSUPPORTED;
     p->S = (int)S;
     p->RB = (int)RB;
     p->chunk = chunk;
-    p->ws_bytes = (S == 1) ? 0 : (size_t)rec_units * S * kRecordFloats * sizeof(float);
+    p->ws_bytes = (S == 1) ? 0 : (size_t)rec_units * S * record_floats(c->head_dim) * sizeof(float);
     return RBQ_OK;
 }
 

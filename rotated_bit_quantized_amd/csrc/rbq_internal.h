@@ -70,24 +70,26 @@ struct MfmaPlan {
 };
 int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, MfmaPlan* p);
 
-// Split record of the attention kernels of the default configuration, one
-// per (b, kv head, block of 8 query rows, key split): (m, l) of the 8 rows
-// (m the row's reference score in base 2, l its sum of 2^(score - m)), then
-// the unnormalised output column-major [256 columns][8 rows].
-constexpr int kRecordFloats = 2 * 8 + 8 * kHeadDim;
+// Split record of the dedicated and prefill attention kernels, one per (b,
+// kv head, block of 8 query rows, key split): (m, l) of the 8 rows (m the
+// row's reference score in base 2, l its sum of 2^(score - m)), then the
+// unnormalised output column-major [head_dim columns][8 rows]; floats per
+// record at head_dim D: record_floats(D) (kRecordFloats at 256).
+constexpr int record_floats(int D) { return 2 * 8 + 8 * D; }
+constexpr int kRecordFloats = record_floats(kHeadDim);
 // The merge of the records of a call with S > 1 splits (RB blocks of 8 rows
-// per kv head): normalisation, inverse rotation, output rows; mask_type
-// RBQ_MASK_BOOL: rows without a kept key take the mean of their keys' values.
+// per kv head; head_dim 256 or 128, the cache's V layout for the rows below):
+// normalisation, inverse rotation, output rows; mask_type RBQ_MASK_BOOL: rows
+// without a kept key take the mean of their keys' values.
 void merge_launch(const rbq_kv_cache* c, const float* rec, const float* rot_blocks, float* out,
                   int S, int RB, int n_rep, int L, int causal, int mask_type, void* stream);
 
 // Prefill-length attention over bf16 caches with 4-bit K codes in groups of
 // 64 (head_dim 128 or 256, V codes of 2 to 4 bits), blocks of 128 query rows
 // per kv head sharing each decoded tile: used from kPrefillMinRows query rows
-// per kv head, in the default configuration with any split count, in the
-// others with one split (prefill_takes).
+// per kv head (prefill_takes), with any split count.
 constexpr int64_t kPrefillMinRows = 96;
-bool prefill_takes(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits);
+bool prefill_takes(const rbq_kv_cache* c, int32_t H_q, int32_t L);
 int prefill_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, MfmaPlan* p);
 int prefill_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L, float scale,
                    int32_t causal, const AttnMask& mk, const float* rot_blocks, float* out,

@@ -369,7 +369,7 @@ def test_status_strings():
 def test_prefill_plan_selection():
     """Which plan a call gets: from 96 query rows per kv head over a bf16 cache
     with 4-bit K in groups of 64 the prefill kernel's (128-row blocks, split
-    records of 8 rows in the default layout, one split in the others); below
+    records of 8 rows at head_dim 256 and 128); below
     that, or with an fp16 cache, the dedicated kernel's (8-row blocks, a
     multiple of 8 splits with several row blocks); other widths the tile
     kernel's."""
@@ -396,11 +396,12 @@ def test_prefill_plan_selection():
     d128.head_dim, d128.v_bits = 128, 4
     assert lib.rbq_quant_attn_splits(by(d128), 16, 2048) == 1
     assert lib.rbq_quant_attn_workspace_bytes(by(d128), 16, 2048, 0) == 0
-    # 256 rows per kv head (32 blocks): too few for one split -> the tile
-    # kernel's plan (key splits, records); an explicit single split -> the
-    # prefill kernel without records
-    assert lib.rbq_quant_attn_splits(by(d128), 16, 32) > 1
-    assert lib.rbq_quant_attn_workspace_bytes(by(d128), 16, 32, 0) > 0
+    # 256 rows per kv head (2 blocks of 128): the prefill kernel with key
+    # splits (40, one 256-key round each) and records of head_dim 128; an
+    # explicit single split: no records
+    rec128 = (16 + 8 * 128) * 4
+    assert lib.rbq_quant_attn_splits(by(d128), 16, 32) == 40
+    assert lib.rbq_quant_attn_workspace_bytes(by(d128), 16, 32, 0) == 2 * 32 * 40 * rec128
     assert lib.rbq_quant_attn_workspace_bytes(by(d128), 16, 32, 1) == 0
     # 5-bit K codes: the tile kernel
     d5 = _host_desc(B=1, H=2, cap=10496, off=10240, **ptrs)

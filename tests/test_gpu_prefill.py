@@ -15,9 +15,11 @@ decoded tile) against the oracle, every output element:
   powers of two);
 - the one-call step with a chunk of 16 appended rows (append kernel, then
   the prefill kernel): rows bit-exact, outputs within the tolerance;
-- the other layouts it takes with one key split: head_dim 128 and 256 with
-  2-, 3- and 4-bit V codes (4-bit: the fp16 value operand and its residual),
-  masks, large V values, and a call whose 256 workgroups take the automatic
+- the other layouts it takes, with one and with several key splits (records
+  of head_dim 128 and 256): head_dim 128 and 256 with 2-, 3- and 4-bit V
+  codes (4-bit: the fp16 value operand and its residual), masks (rows that
+  keep no key take the mean of their keys in the merge too), large V values,
+  and a call whose 256 workgroups take the automatic
   plan.
 """
 import numpy as np
@@ -180,8 +182,10 @@ def test_prefill_plan_is_used(dev):
     assert rbq.rbq_quant_attn_splits(g.desc, 16, 16) > 1
 
 
-# other layouts the prefill kernel takes (bf16, 4-bit K in groups of 64, one
-# key split): (head_dim, v_bits, B, H_q, H_kv, L, T0, causal, splits, rotation, rounded)
+# other layouts the prefill kernel takes (bf16, 4-bit K in groups of 64): one
+# key split (outputs stored by the attention kernel), explicit and automatic
+# splits (records of head_dim 128 or 256 merged by the merge kernel):
+# (head_dim, v_bits, B, H_q, H_kv, L, T0, causal, splits, rotation, rounded)
 LAYOUTS = [
     (128, 4, 1, 16, 2, 16, 300, True, 1, "two_sided", False),
     (128, 3, 1, 8, 2, 50, 133, True, 1, "printed", True),
@@ -189,6 +193,11 @@ LAYOUTS = [
     (256, 4, 1, 16, 2, 16, 250, True, 1, "two_sided", False),
     (256, 2, 1, 16, 2, 12, 180, True, 1, None, False),
     (128, 4, 2, 16, 8, 1024, 76, True, 0, "two_sided", False),  # 256 workgroups: automatic plan
+    (128, 4, 1, 16, 2, 16, 3000, True, 0, "two_sided", False),  # automatic splits, records
+    (128, 3, 2, 8, 2, 50, 700, True, 5, "printed", True),
+    (128, 2, 1, 16, 2, 40, 2600, False, 0, "printed", False),
+    (256, 4, 1, 16, 2, 16, 2500, True, 0, "two_sided", False),
+    (256, 2, 1, 16, 2, 12, 1800, True, 7, None, False),
 ]
 
 
@@ -231,10 +240,11 @@ def test_prefill_other_layouts(case, dev):
     assert err <= ATOL, err
 
 
+@pytest.mark.parametrize("splits", [1, 0])
 @pytest.mark.parametrize("kind", ["bool", "f32"])
-def test_prefill_other_layout_masks(kind, dev):
-    D, vb, B, Hq, Hkv, L, T = 128, 4, 2, 16, 2, 16, 333
-    print(f"[prefill layout mask] {kind}", flush=True)
+def test_prefill_other_layout_masks(kind, splits, dev):
+    D, vb, B, Hq, Hkv, L, T = 128, 4, 2, 16, 2, 16, 2333
+    print(f"[prefill layout mask] {kind} splits={splits}", flush=True)
     g, o, blocks = _layout_pair(dev, 72, D, vb, B, Hkv, T, "two_sided", False)
     q = W.random_rows([73, 0], (B, Hq, L, D), "bf16")
     rng = np.random.default_rng(74)
@@ -244,8 +254,11 @@ def test_prefill_other_layout_masks(kind, dev):
         m[1, :, 0, :] = False
     else:
         m = rng.normal(0.0, 2.0, size=(B, Hq, L, T)).astype(np.float32)
-    out = g.attend(q.to(dev), scale=D ** -0.5, causal=True, mask=torch.from_numpy(m).to(dev), splits=1)
+    out = g.attend(q.to(dev), scale=D ** -0.5, causal=True, mask=torch.from_numpy(m).to(dev),
+                   splits=splits)
     torch.cuda.synchronize()
+    if splits == 0:
+        assert rbq.rbq_quant_attn_splits(g.desc, Hq, L) > 1
     got = out.cpu().numpy()
     assert np.isfinite(got).all()
     want = O.attention(q.float().numpy(), o, D ** -0.5, True, blocks, mask=m)
@@ -259,10 +272,11 @@ def test_prefill_other_layout_large_values(dev):
     D, vb, B, Hq, Hkv, L, T = 128, 4, 1, 16, 2, 16, 400
     g, o, blocks = _layout_pair(dev, 75, D, vb, B, Hkv, T, "printed", False, vscale=1e5)
     q = W.random_rows([76, 0], (B, Hq, L, D), "bf16")
-    out = g.attend(q.to(dev), scale=D ** -0.5, causal=True, splits=1)
-    torch.cuda.synchronize()
-    got = out.cpu().numpy()
-    assert np.isfinite(got).all()
     want = O.attention(q.float().numpy(), o, D ** -0.5, True, blocks)
-    err = float(np.abs(got - want).max()) / 1e5
-    assert err <= ATOL, err
+    for splits in (1, 3):
+        out = g.attend(q.to(dev), scale=D ** -0.5, causal=True, splits=splits)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.isfinite(got).all()
+        err = float(np.abs(got - want).max()) / 1e5
+        assert err <= ATOL, (splits, err)
