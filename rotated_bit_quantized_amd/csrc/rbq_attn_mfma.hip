@@ -1379,8 +1379,8 @@ void merge_launch(const rbq_kv_cache* c, const float* rec, const float* rot_bloc
     // spill registers at 1024 threads)
     // few (b, kv head, 8 rows) units: 32 columns per workgroup, twice the
     // workgroups
-    // (records of head_dim 256 or 128: the dedicated kernel's, or the prefill
-    // kernel's for either head dim)
+    // (records of head_dim 256: the dedicated kernel's or the prefill
+    // kernel's; 128 or 64: the prefill kernel's)
     const bool narrow = units < kMergeNarrowUnits;
     const int colblocks = c->head_dim / (narrow ? 32 : 64);
     const dim3 mg((unsigned)(units * colblocks));
@@ -1396,13 +1396,20 @@ void merge_launch(const rbq_kv_cache* c, const float* rec, const float* rot_bloc
         else
             go(attn_mfma_merge_kernel<1, 4, kHeadDim>, attn_mfma_merge_kernel<2, 4, kHeadDim>,
                attn_mfma_merge_kernel<4, 4, kHeadDim>);
-    } else {
+    } else if (c->head_dim == 128) {
         if (narrow)
             go(attn_mfma_merge_kernel<1, 2, 128>, attn_mfma_merge_kernel<2, 2, 128>,
                attn_mfma_merge_kernel<4, 2, 128>);
         else
             go(attn_mfma_merge_kernel<1, 4, 128>, attn_mfma_merge_kernel<2, 4, 128>,
                attn_mfma_merge_kernel<4, 4, 128>);
+    } else {
+        if (narrow)
+            go(attn_mfma_merge_kernel<1, 2, 64>, attn_mfma_merge_kernel<2, 2, 64>,
+               attn_mfma_merge_kernel<4, 2, 64>);
+        else
+            go(attn_mfma_merge_kernel<1, 4, 64>, attn_mfma_merge_kernel<2, 4, 64>,
+               attn_mfma_merge_kernel<4, 4, 64>);
     }
 }
 

@@ -63,7 +63,7 @@ constexpr int kPRows = 16 * kPW;      // query rows per workgroup
 constexpr int kPTile = 32;            // keys per tile
 constexpr int64_t kPGridYZ = 65535;   // workgroups per grid dimension y or z of one launch
 constexpr float kPLog2e = 1.44269504088896340736f;
-// Layout of one configuration: head_dim D (128 or 256), groups of 64 dims,
+// Layout of one configuration: head_dim D (64, 128 or 256), groups of 64 dims,
 // 4-bit K codes, VB-bit V codes (2, 3 or 4).
 //   A raw buffer holds one tile as the memory holds it: K words (16-byte
 //   chunks of a key permuted, see k_chunk), V words, K scales, K biases, V
@@ -449,8 +449,17 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // V' = code x scale x 2^F_g, exact in fp32; in fp16 exact for up to 3-bit
     // codes (8 + 3 significant bits); 4-bit codes keep the residual V'' =
     // V' - fp16(V') (exact) in a second array
-    auto decode_tile = [&](const unsigned char* raw, const int db) __attribute__((always_inline)) {
+    // With one group per row (head_dim 64) the scale and bias arrays hold 2
+    // bytes per key, and the 4-byte transfers of a tile that ends at an odd
+    // key count T take the pair (T - 1, T) as one word outside the range:
+    // it reads as zero, key T - 1's halves included.  The decode of that tile
+    // takes key T - 1's four halves from memory instead and puts its K bias
+    // into the raw buffer, where the score products read it.
+    auto decode_tile = [&](const unsigned char* raw, const int db, const int t0) __attribute__((always_inline)) {
         constexpr int IPK = D / 16;  // items per key
+        const int klast = T - 1 - t0;
+        const bool fix_last = NG == 1 && (T & 1) && klast >= 0 && klast < kPTile;
+        const int64_t last = row0 + T - 1;  // (one group: element index = row)
 #pragma unroll
         for (int item = tid; item < 2 * D; item += kPT) {
             const int k = item / IPK, p = item % IPK, g = p >> 2;
@@ -459,7 +468,8 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const uint32_t w0 = lds_ld<uint32_t>(raw, C::RV + 4 * (C::VWK * k + wi));
             const uint32_t w1 = lds_ld<uint32_t>(raw, C::RV + 4 * (C::VWK * k + wi + 1));
             const uint64_t bits = (((uint64_t)w1 << 32) | w0) >> sh;
-            const uint32_t sv = lds_ld<uint16_t>(raw, C::RVs + 2 * (NG * k + g));
+            const uint32_t sv = (fix_last && k == klast) ? (uint32_t)a.vs[last]
+                                                         : lds_ld<uint16_t>(raw, C::RVs + 2 * (NG * k + g));
             const float sf = bf16_bits_to_f32(sv) * lds_ld<float>(smem, C::OffUnit + 4 * g);
             constexpr uint32_t cm = (1u << VB) - 1u;
             uint32_t h[8], hl[8];
@@ -484,14 +494,19 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (wave < 2) {
             if (tid < kPTile * NG) {
                 const int kk = tid / NG, gg = tid % NG;
-                const uint32_t sk = lds_ld<uint16_t>(raw, C::RKs + 2 * (NG * kk + gg));
+                uint32_t sk = lds_ld<uint16_t>(raw, C::RKs + 2 * (NG * kk + gg));
+                if (fix_last && kk == klast) {
+                    sk = a.ks[last];
+                    lds_st<uint16_t>(const_cast<unsigned char*>(raw), C::RKb + 2 * kk, a.kb[last]);
+                }
                 lds_st<float>(smem, C::OffKs + db * (NG * kPTile * 4) + 4 * (gg * kPTile + kk),
                               bf16_bits_to_f32(sk));
             }
         } else if (wave < 4) {
             if (tid - 128 < kPTile * NG) {
                 const int kk = (tid - 128) / NG, gg = (tid - 128) % NG;
-                const uint32_t b = lds_ld<uint16_t>(raw, C::RVb + 2 * (NG * kk + gg));
+                const uint32_t b = (fix_last && kk == klast) ? (uint32_t)a.vb[last]
+                                                             : lds_ld<uint16_t>(raw, C::RVb + 2 * (NG * kk + gg));
                 const float bu = bf16_bits_to_f32(b) * lds_ld<float>(smem, C::OffUnit + 4 * gg);
                 lds_st<uint16_t>(smem, C::OffVb + db * (NG * kPTile * 2) + 2 * (gg * kPTile + v_row(kk)),
                                  __builtin_bit_cast(uint16_t, (_Float16)bu));
@@ -503,7 +518,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (n_tiles > 1)
         issue_tile((plds_u8*)smem + C::RAW, t_begin + kPTile);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (n_tiles > 0) decode_tile(smem, 0);
+    if (n_tiles > 0) decode_tile(smem, 0, t_begin);
 
     for (int it = 0; it < n_tiles; ++it) {
         // raw buffer it % 3 holds tile it, (it + 1) % 3 tile it + 1 (landed at
@@ -520,7 +535,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const bool dec_next = it + 1 < n_tiles;
         if (it + 2 < n_tiles) issue_tile(raw_dma, t0 + 2 * kPTile);
         if (!wave_live) {
-            if (dec_next) decode_tile(raw_next, db ^ 1);
+            if (dec_next) decode_tile(raw_next, db ^ 1, t0 + kPTile);
             continue;
         }
 
@@ -567,13 +582,15 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if constexpr (NG == 4) {
                 const pu32x2 kbw = lds_ld<pu32x2>(raw, C::RKb + 8 * key);
                 kbop = (pu32x4){kbw[0], kbw[1], 0u, 0u};
-            } else {
+            } else if constexpr (NG == 2) {
                 kbop = (pu32x4){lds_ld<uint32_t>(raw, C::RKb + 4 * key), 0u, 0u, 0u};
+            } else {
+                kbop = (pu32x4){(uint32_t)lds_ld<uint16_t>(raw, C::RKb + 2 * key), 0u, 0u, 0u};
             }
             const pf32x4 cb = mfma_bf16(kbop, qb, zero4);
             // the next tile's decode while the matrix cores work on these
             // products (its buffers are not read by this tile)
-            if (kb == 1 && dec_next) decode_tile(raw_next, db ^ 1);
+            if (kb == 1 && dec_next) decode_tile(raw_next, db ^ 1, t0 + kPTile);
             pf32x4 s4[NG];
 #pragma unroll
             for (int g = 0; g < NG; ++g)
@@ -749,7 +766,8 @@ static void launch_masked(int mt, F&& launch) {
 bool prefill_takes(const rbq_kv_cache* c, int32_t H_q, int32_t L) {
     const int64_t G = (int64_t)(H_q / c->H_kv) * L;
     if (G < kPrefillMinRows || c->dtype != RBQ_BF16 || c->k_bits != 4 || c->group_size != 64 ||
-        (c->head_dim != 128 && c->head_dim != 256) || c->v_bits < 2 || c->v_bits > 4)
+        (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) || c->v_bits < 2 ||
+        c->v_bits > 4)
         return false;
     return true;
 }
@@ -833,10 +851,14 @@ int prefill_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L,
         if (c->v_bits == 3) launch_masked<256, 3>(mt, launch);
         else if (c->v_bits == 4) launch_masked<256, 4>(mt, launch);
         else launch_masked<256, 2>(mt, launch);
-    } else {
+    } else if (c->head_dim == 128) {
         if (c->v_bits == 3) launch_masked<128, 3>(mt, launch);
         else if (c->v_bits == 4) launch_masked<128, 4>(mt, launch);
         else launch_masked<128, 2>(mt, launch);
+    } else {
+        if (c->v_bits == 3) launch_masked<64, 3>(mt, launch);
+        else if (c->v_bits == 4) launch_masked<64, 4>(mt, launch);
+        else launch_masked<64, 2>(mt, launch);
     }
     if (p.S > 1) merge_launch(c, a.rec, rot_blocks, out, p.S, p.RB, a.n_rep, L, a.causal, mt, stream);
     const hipError_t e = hipGetLastError();

@@ -78,14 +78,14 @@ int mfma_plan(const rbq_kv_cache* c, int32_t H_q, int32_t L, int32_t splits, Mfm
 constexpr int record_floats(int D) { return 2 * 8 + 8 * D; }
 constexpr int kRecordFloats = record_floats(kHeadDim);
 // The merge of the records of a call with S > 1 splits (RB blocks of 8 rows
-// per kv head; head_dim 256 or 128, the cache's V layout for the rows below):
+// per kv head; head_dim 256, 128 or 64, the cache's V layout for the rows below):
 // normalisation, inverse rotation, output rows; mask_type RBQ_MASK_BOOL: rows
 // without a kept key take the mean of their keys' values.
 void merge_launch(const rbq_kv_cache* c, const float* rec, const float* rot_blocks, float* out,
                   int S, int RB, int n_rep, int L, int causal, int mask_type, void* stream);
 
 // Prefill-length attention over bf16 caches with 4-bit K codes in groups of
-// 64 (head_dim 128 or 256, V codes of 2 to 4 bits), blocks of 128 query rows
+// 64 (head_dim 64, 128 or 256, V codes of 2 to 4 bits), blocks of 128 query rows
 // per kv head sharing each decoded tile: used from kPrefillMinRows query rows
 // per kv head (prefill_takes), with any split count.
 constexpr int64_t kPrefillMinRows = 96;

@@ -16,7 +16,7 @@ decoded tile) against the oracle, every output element:
 - the one-call step with a chunk of 16 appended rows (append kernel, then
   the prefill kernel): rows bit-exact, outputs within the tolerance;
 - the other layouts it takes, with one and with several key splits (records
-  of head_dim 128 and 256): head_dim 128 and 256 with 2-, 3- and 4-bit V
+  of head_dim 64, 128 and 256): head_dim 64, 128 and 256 with 2-, 3- and 4-bit V
   codes (4-bit: the fp16 value operand and its residual), masks (rows that
   keep no key take the mean of their keys in the merge too), large V values,
   and a call whose 256 workgroups take the automatic
@@ -184,7 +184,7 @@ def test_prefill_plan_is_used(dev):
 
 # other layouts the prefill kernel takes (bf16, 4-bit K in groups of 64): one
 # key split (outputs stored by the attention kernel), explicit and automatic
-# splits (records of head_dim 128 or 256 merged by the merge kernel):
+# splits (records of head_dim 64, 128 or 256 merged by the merge kernel):
 # (head_dim, v_bits, B, H_q, H_kv, L, T0, causal, splits, rotation, rounded)
 LAYOUTS = [
     (128, 4, 1, 16, 2, 16, 300, True, 1, "two_sided", False),
@@ -198,6 +198,13 @@ LAYOUTS = [
     (128, 2, 1, 16, 2, 40, 2600, False, 0, "printed", False),
     (256, 4, 1, 16, 2, 16, 2500, True, 0, "two_sided", False),
     (256, 2, 1, 16, 2, 12, 1800, True, 7, None, False),
+    (64, 4, 1, 16, 2, 16, 300, True, 1, "two_sided", False),    # head_dim 64: one group
+    (64, 3, 2, 8, 2, 50, 700, True, 0, "printed", True),
+    (64, 2, 1, 16, 2, 40, 1000, False, 3, None, False),
+    # head_dim 64 with an odd key count: the last key's 2-byte scales share a
+    # word with the key past the end
+    (64, 2, 2, 8, 1, 15, 338, True, 0, "two_sided", True),
+    (64, 4, 1, 16, 2, 12, 301, False, 1, None, False),
 ]
 
 

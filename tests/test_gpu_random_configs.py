@@ -33,7 +33,7 @@ def _draw(i):
     B, Hkv, n_rep, T, chunks, L, splits, mask)."""
     rng = np.random.default_rng([2026, i])
     prefill = i % 8 == 7
-    D = int(rng.choice([64, 128, 256])) if not prefill else int(rng.choice([128, 256]))
+    D = int(rng.choice([64, 128, 256]))
     groups = [g for g in (32, 64, 128) if g <= D]
     gs = int(rng.choice(groups)) if not prefill else 64
     kb = int(rng.choice(BITS)) if not prefill else 4
