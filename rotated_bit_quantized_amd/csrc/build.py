@@ -6,6 +6,7 @@ Python binding: ``rotated_bit_quantized_amd/librbq.so``.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -59,21 +60,26 @@ def _run(cmd, verbose):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
+    jobs = []  # (command, object), compiled side by side
     objs = []
     for src in HOST_SOURCES:
         obj = os.path.join(OUT_DIR, src + ".o")
-        _run(["g++", *HOST_FLAGS, "-c", os.path.join(HERE, src), "-o", obj], verbose)
+        jobs.append(["g++", *HOST_FLAGS, "-c", os.path.join(HERE, src), "-o", obj])
         objs.append(obj)
     for src in HIP_SOURCES:
         obj = os.path.join(OUT_DIR, src + ".o")
-        _run([HIPCC, *HIP_FLAGS, *HIP_FILE_FLAGS.get(src, []), "-c", os.path.join(HERE, src), "-o",
-              obj], verbose)
+        jobs.append([HIPCC, *HIP_FLAGS, *HIP_FILE_FLAGS.get(src, []), "-c", os.path.join(HERE, src),
+                     "-o", obj])
         objs.append(obj)
+    pobj = os.path.join(OUT_DIR, PROBE_SOURCE + ".o")
+    jobs.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(HERE, PROBE_SOURCE), "-o", pobj])
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as pool:
+        for f in [pool.submit(_run, cmd, verbose) for cmd in jobs]:
+            f.result()
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     shutil.move(tmp, LIB)
-    pobj = os.path.join(OUT_DIR, PROBE_SOURCE + ".o")
-    _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(HERE, PROBE_SOURCE), "-o", pobj], verbose)
     ptmp = PROBE_LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", ptmp, pobj], verbose)
     shutil.move(ptmp, PROBE_LIB)

@@ -1,7 +1,8 @@
 // Prefill-length attention over the packed K4/V3 cache (asym_quantized_sdpa
 // on the quant_kv.py page with many query rows per kv head: a prompt chunk
 // of L tokens attending to the cache and to itself, causal at the offset) on
-// the gfx950 matrix cores, for bf16 caches of the default configuration.
+// the gfx950 matrix cores, for bf16 and fp16 caches with 4-bit K codes in
+// groups of 64 (head_dim 64, 128 or 256, 2- to 4-bit V codes).
 //
 // Decomposition: one workgroup of 8 wave64s per (b, kv head, block of 128
 // query rows, key split); wave w takes rows 16 w .. 16 w + 15 of the block,
@@ -70,8 +71,9 @@ constexpr float kPLog2e = 1.44269504088896340736f;
 //   scales, V biases.  LDS (bytes): three raw buffers (tile i + 2 in flight
 //   while tile i + 1 is decoded and tile i computed), two decoded tiles (V',
 //   and for 4-bit codes its residual V'', see the decode), K scales and V
-//   bias operands of both, the rotation blocks, group maxima, scale powers.
-template <int D, int VB>
+//   bias operands of both, the rotation blocks, group maxima, scale powers;
+//   with fp16 caches also the K biases of both as bf16 hi and lo parts.
+template <int D, int VB, int DT>
 struct PCfg {
     static constexpr int NG = D / 64;                     // groups of 64 dims
     static constexpr int NB = D / 16;                     // 16-dim output blocks
@@ -84,7 +86,9 @@ struct PCfg {
     static constexpr int MB = kPTile * NG * 2;            // bytes of each scale / bias array
     static constexpr int RKb = RKs + MB, RVs = RKb + MB, RVb = RVs + MB;
     static constexpr int RAW = (RVb + MB + 15) / 16 * 16;
-    static constexpr bool VSPLIT = VB > 3;                // 4 + 8 significant bits: V' + V''
+    // V' = code x scale: up to 3 + 8 significant bits with bf16 scales (one
+    // fp16 array), up to 4 + 8 or VB + 11 otherwise (V' + its residual V'')
+    static constexpr bool VSPLIT = VB > 3 || DT == RBQ_F16;
     static constexpr int NDEC = VSPLIT ? 2 : 1;           // decoded arrays per tile
     // decoded rows: 2 D + 160 bytes apart, rows 8-15 and 24-31 shifted by 128
     // bytes, so that the transposing reads of 32 lanes (rows 8 j' + e of two
@@ -94,7 +98,8 @@ struct PCfg {
     static constexpr int OffV = 3 * RAW;
     static constexpr int OffKs = OffV + 2 * NDEC * DEC;   // fp32 [NG][32] per tile
     static constexpr int OffVb = OffKs + 2 * NG * kPTile * 4;  // fp16 [NG][32] per tile
-    static constexpr int OffRot = OffVb + 2 * NG * kPTile * 2;
+    static constexpr int OffKb2 = OffVb + 2 * NG * kPTile * 2;  // fp16 caches: bf16 [32][2 NG] per tile
+    static constexpr int OffRot = OffKb2 + (DT == RBQ_F16 ? 2 * kPTile * 2 * NG * 2 : 0);
     static constexpr int OffRed = OffRot + D * 16;        // [8 waves][4] group maxima
     static constexpr int OffUnit = OffRed + kPW * 16;     // 2^F_g, then 2^-F_g
     static constexpr int BYTES = OffUnit + 32;
@@ -209,9 +214,9 @@ __device__ __forceinline__ int k_chunk(int k, int c) {
 // (e < 4) or 16 + 4 j + e - 4 (e >= 4), the k-slot order of the P operand.
 __device__ __forceinline__ int v_row(int k) { return 8 * ((k & 15) >> 2) + (k & 3) + 4 * (k >> 4); }
 
-template <int MK, int D, int VB>
+template <int MK, int D, int VB, int DT>
 __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_prefill_kernel(PArgs a) {
-    using C = PCfg<D, VB>;
+    using C = PCfg<D, VB, DT>;
     constexpr int NG = C::NG, NB = C::NB;
     __shared__ __align__(16) unsigned char smem[C::BYTES];
     const int tid = threadIdx.x;
@@ -285,7 +290,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 if (row_ok) {
-                    load4<RBQ_BF16>(qr + 64 * g + 16 * j + 4 * q4, x[g] + 4 * q4);
+                    load4<DT>(qr + 64 * g + 16 * j + 4 * q4, x[g] + 4 * q4);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) x[g][4 * q4 + e] = 0.f;
@@ -303,8 +308,8 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int t = t_begin + tid; t < t_lim; t += kPT) {
 #pragma unroll
         for (int g = 0; g < NG; ++g)
-            vmx[g] = fmaxf(vmx[g], fmaxf(fabsf(bf16_bits_to_f32(a.vs[(row0 + t) * NG + g])),
-                                         fabsf(bf16_bits_to_f32(a.vb[(row0 + t) * NG + g]))));
+            vmx[g] = fmaxf(vmx[g], fmaxf(fabsf(elem_to_f32<DT>(a.vs[(row0 + t) * NG + g])),
+                                         fabsf(elem_to_f32<DT>(a.vb[(row0 + t) * NG + g]))));
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -360,7 +365,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     rotate4(x[g] + 4 * q4, Bm, y);
                     if (a.round_rot) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) y[e] = bf16_bits_to_f32(f32_to_bf16_bits(y[e]));
+                        for (int e = 0; e < 4; ++e) y[e] = elem_to_f32<DT>(f32_to_elem_bits<DT>(y[e]));
                     }
                 } else {
 #pragma unroll
@@ -396,8 +401,10 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     ql[g][h2][e] = (_Float16)(xs - (float)hi);
                 }
         // bias operand: lane group j < 3 holds limb j of the NG group sums
-        // (exact three-limb bf16 split) in k-slots 0 .. NG - 1
-        uint32_t lb[4] = {0u, 0u, 0u, 0u};
+        // (exact three-limb bf16 split) in k-slots 0 .. NG - 1; with fp16
+        // caches again in k-slots NG .. 2 NG - 1, against the lo parts of the
+        // K biases (an fp16 bias is its bf16 truncation plus an exact bf16 rest)
+        uint32_t lb[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             const float s = row_sum4(gsum[g]);
@@ -406,8 +413,9 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const uint32_t u2 = __float_as_uint(s - hi);
             const float mid = __uint_as_float(u2 & 0xFFFF0000u);
             lb[g] = (j == 0) ? u >> 16 : (j == 1) ? u2 >> 16 : (j == 2) ? f32_to_bf16_bits(s - hi - mid) : 0u;
+            if constexpr (DT == RBQ_F16) lb[NG + g] = lb[g];
         }
-        qb = (pu32x4){lb[0] | lb[1] << 16, lb[2] | lb[3] << 16, 0u, 0u};
+        qb = (pu32x4){lb[0] | lb[1] << 16, lb[2] | lb[3] << 16, lb[4] | lb[5] << 16, lb[6] | lb[7] << 16};
     }
     const float frow = E_f;
     // causal visibility of the lane's row, and the smallest over the wave's rows
@@ -470,7 +478,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const uint64_t bits = (((uint64_t)w1 << 32) | w0) >> sh;
             const uint32_t sv = (fix_last && k == klast) ? (uint32_t)a.vs[last]
                                                          : lds_ld<uint16_t>(raw, C::RVs + 2 * (NG * k + g));
-            const float sf = bf16_bits_to_f32(sv) * lds_ld<float>(smem, C::OffUnit + 4 * g);
+            const float sf = elem_to_f32<DT>(sv) * lds_ld<float>(smem, C::OffUnit + 4 * g);
             constexpr uint32_t cm = (1u << VB) - 1u;
             uint32_t h[8], hl[8];
 #pragma unroll
@@ -495,19 +503,32 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (tid < kPTile * NG) {
                 const int kk = tid / NG, gg = tid % NG;
                 uint32_t sk = lds_ld<uint16_t>(raw, C::RKs + 2 * (NG * kk + gg));
+                uint32_t bk = 0u;
+                if constexpr (DT == RBQ_F16) bk = lds_ld<uint16_t>(raw, C::RKb + 2 * (NG * kk + gg));
                 if (fix_last && kk == klast) {
                     sk = a.ks[last];
-                    lds_st<uint16_t>(const_cast<unsigned char*>(raw), C::RKb + 2 * kk, a.kb[last]);
+                    bk = a.kb[last];
+                    if constexpr (DT == RBQ_BF16)
+                        lds_st<uint16_t>(const_cast<unsigned char*>(raw), C::RKb + 2 * kk, (uint16_t)bk);
+                }
+                if constexpr (DT == RBQ_F16) {
+                    // bf16 truncation of the fp16 bias and the exact bf16 rest
+                    const float bf = elem_to_f32<RBQ_F16>(bk);
+                    const uint32_t hb = __float_as_uint(bf) & 0xFFFF0000u;
+                    const uint32_t lo = __float_as_uint(bf - __uint_as_float(hb)) >> 16;
+                    const uint32_t kb2 = C::OffKb2 + db * (kPTile * 2 * NG * 2) + 2 * (2 * NG * kk);
+                    lds_st<uint16_t>(smem, kb2 + 2 * gg, (uint16_t)(hb >> 16));
+                    lds_st<uint16_t>(smem, kb2 + 2 * (NG + gg), (uint16_t)lo);
                 }
                 lds_st<float>(smem, C::OffKs + db * (NG * kPTile * 4) + 4 * (gg * kPTile + kk),
-                              bf16_bits_to_f32(sk));
+                              elem_to_f32<DT>(sk));
             }
         } else if (wave < 4) {
             if (tid - 128 < kPTile * NG) {
                 const int kk = (tid - 128) / NG, gg = (tid - 128) % NG;
                 const uint32_t b = (fix_last && kk == klast) ? (uint32_t)a.vb[last]
                                                              : lds_ld<uint16_t>(raw, C::RVb + 2 * (NG * kk + gg));
-                const float bu = bf16_bits_to_f32(b) * lds_ld<float>(smem, C::OffUnit + 4 * gg);
+                const float bu = elem_to_f32<DT>(b) * lds_ld<float>(smem, C::OffUnit + 4 * gg);
                 lds_st<uint16_t>(smem, C::OffVb + db * (NG * kPTile * 2) + 2 * (gg * kPTile + v_row(kk)),
                                  __builtin_bit_cast(uint16_t, (_Float16)bu));
             }
@@ -577,9 +598,20 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     acc[g] = mfma_f16(kop, ql[g][h2], acc[g]);
                 }
             }
-            // the key's NG bias halves in k-slots 0 .. NG - 1
+            // the key's NG bias halves in k-slots 0 .. NG - 1 (fp16 caches:
+            // their bf16 hi parts there and the lo parts in NG .. 2 NG - 1)
             pu32x4 kbop = {0u, 0u, 0u, 0u};
-            if constexpr (NG == 4) {
+            if constexpr (DT == RBQ_F16) {
+                const uint32_t kb2 = C::OffKb2 + db * (kPTile * 2 * NG * 2) + 2 * (2 * NG * key);
+                if constexpr (NG == 4) {
+                    kbop = lds_ld<pu32x4>(smem, kb2);
+                } else if constexpr (NG == 2) {
+                    const pu32x2 w = lds_ld<pu32x2>(smem, kb2);
+                    kbop = (pu32x4){w[0], w[1], 0u, 0u};
+                } else {
+                    kbop = (pu32x4){lds_ld<uint32_t>(smem, kb2), 0u, 0u, 0u};
+                }
+            } else if constexpr (NG == 4) {
                 const pu32x2 kbw = lds_ld<pu32x2>(raw, C::RKb + 8 * key);
                 kbop = (pu32x4){kbw[0], kbw[1], 0u, 0u};
             } else if constexpr (NG == 2) {
@@ -606,7 +638,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 } else if constexpr (MK == RBQ_MASK_ADD_F32) {
                     s = fmaf(__uint_as_float(mv[kb][i]), kPLog2e, s);
                 } else if constexpr (MK == RBQ_MASK_ADD_DTYPE) {
-                    s = fmaf(bf16_bits_to_f32(mv[kb][i]), kPLog2e, s);
+                    s = fmaf(elem_to_f32<DT>(mv[kb][i]), kPLog2e, s);
                 }
                 sc[kb][i] = s;
             }
@@ -718,7 +750,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const int nv = a.causal ? T - a.L + (R % a.L) + 1 : T;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    y[i] = value_column_mean<RBQ_BF16>(a.vw, a.vs, a.vb, row0, nv, 16 * t + 4 * j + i,
+                    y[i] = value_column_mean<DT>(a.vw, a.vs, a.vb, row0, nv, 16 * t + 4 * j + i,
                                                        VB, C::VWK, NG, 64);
             }
             float z[4] = {y[0], y[1], y[2], y[3]};
@@ -754,18 +786,38 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // ---- host side ----
 
-// The kernel of layout (D, VB) for mask type mt, handed to `launch`.
-template <int D, int VB, typename F>
+// The kernel of layout (D, VB) and cache dtype DT for mask type mt, handed
+// to `launch`.
+template <int D, int VB, int DT, typename F>
 static void launch_masked(int mt, F&& launch) {
-    if (mt == RBQ_MASK_NONE) launch(attn_prefill_kernel<RBQ_MASK_NONE, D, VB>);
-    else if (mt == RBQ_MASK_BOOL) launch(attn_prefill_kernel<RBQ_MASK_BOOL, D, VB>);
-    else if (mt == RBQ_MASK_ADD_F32) launch(attn_prefill_kernel<RBQ_MASK_ADD_F32, D, VB>);
-    else launch(attn_prefill_kernel<RBQ_MASK_ADD_DTYPE, D, VB>);
+    if (mt == RBQ_MASK_NONE) launch(attn_prefill_kernel<RBQ_MASK_NONE, D, VB, DT>);
+    else if (mt == RBQ_MASK_BOOL) launch(attn_prefill_kernel<RBQ_MASK_BOOL, D, VB, DT>);
+    else if (mt == RBQ_MASK_ADD_F32) launch(attn_prefill_kernel<RBQ_MASK_ADD_F32, D, VB, DT>);
+    else launch(attn_prefill_kernel<RBQ_MASK_ADD_DTYPE, D, VB, DT>);
+}
+
+// The kernel of the cache's head_dim and V width, for cache dtype DT.
+template <int DT, typename F>
+static void launch_layout(const rbq_kv_cache* c, int mt, F&& launch) {
+    if (c->head_dim == 256) {
+        if (c->v_bits == 3) launch_masked<256, 3, DT>(mt, launch);
+        else if (c->v_bits == 4) launch_masked<256, 4, DT>(mt, launch);
+        else launch_masked<256, 2, DT>(mt, launch);
+    } else if (c->head_dim == 128) {
+        if (c->v_bits == 3) launch_masked<128, 3, DT>(mt, launch);
+        else if (c->v_bits == 4) launch_masked<128, 4, DT>(mt, launch);
+        else launch_masked<128, 2, DT>(mt, launch);
+    } else {
+        if (c->v_bits == 3) launch_masked<64, 3, DT>(mt, launch);
+        else if (c->v_bits == 4) launch_masked<64, 4, DT>(mt, launch);
+        else launch_masked<64, 2, DT>(mt, launch);
+    }
 }
 
 bool prefill_takes(const rbq_kv_cache* c, int32_t H_q, int32_t L) {
     const int64_t G = (int64_t)(H_q / c->H_kv) * L;
-    if (G < kPrefillMinRows || c->dtype != RBQ_BF16 || c->k_bits != 4 || c->group_size != 64 ||
+    if (G < kPrefillMinRows || (c->dtype != RBQ_BF16 && c->dtype != RBQ_F16) || c->k_bits != 4 ||
+        c->group_size != 64 ||
         (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) || c->v_bits < 2 ||
         c->v_bits > 4)
         return false;
@@ -847,19 +899,8 @@ int prefill_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L,
                 hipLaunchKernelGGL(kernel, grid, dim3(kPT), 0, s, a);
             }
     };
-    if (c->head_dim == 256) {
-        if (c->v_bits == 3) launch_masked<256, 3>(mt, launch);
-        else if (c->v_bits == 4) launch_masked<256, 4>(mt, launch);
-        else launch_masked<256, 2>(mt, launch);
-    } else if (c->head_dim == 128) {
-        if (c->v_bits == 3) launch_masked<128, 3>(mt, launch);
-        else if (c->v_bits == 4) launch_masked<128, 4>(mt, launch);
-        else launch_masked<128, 2>(mt, launch);
-    } else {
-        if (c->v_bits == 3) launch_masked<64, 3>(mt, launch);
-        else if (c->v_bits == 4) launch_masked<64, 4>(mt, launch);
-        else launch_masked<64, 2>(mt, launch);
-    }
+    if (c->dtype == RBQ_BF16) launch_layout<RBQ_BF16>(c, mt, launch);
+    else launch_layout<RBQ_F16>(c, mt, launch);
     if (p.S > 1) merge_launch(c, a.rec, rot_blocks, out, p.S, p.RB, a.n_rep, L, a.causal, mt, stream);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {

@@ -367,12 +367,11 @@ def test_status_strings():
 
 
 def test_prefill_plan_selection():
-    """Which plan a call gets: from 96 query rows per kv head over a bf16 cache
-    with 4-bit K in groups of 64 the prefill kernel's (128-row blocks, split
-    records of 8 rows at head_dim 256 and 128); below
-    that, or with an fp16 cache, the dedicated kernel's (8-row blocks, a
-    multiple of 8 splits with several row blocks); other widths the tile
-    kernel's."""
+    """Which plan a call gets: from 96 query rows per kv head over a bf16 or
+    fp16 cache with 4-bit K in groups of 64 the prefill kernel's (128-row
+    blocks, split records of 8 rows at head_dim 256, 128 and 64); below that
+    the dedicated kernel's (8-row blocks, a multiple of 8 splits with several
+    row blocks); other widths the tile kernel's."""
     lib = capi.library()
     fake = 0x1000
     ptrs = dict(k_words=fake, k_scales=fake, k_biases=fake, v_words=fake, v_scales=fake,
@@ -386,10 +385,12 @@ def test_prefill_plan_selection():
     assert lib.rbq_quant_attn_workspace_bytes(by(d), 16, 12, 0) == 2 * 12 * 40 * rec
     # 88 rows: the dedicated kernel, 11 row blocks -> 16 splits
     assert lib.rbq_quant_attn_splits(by(d), 16, 11) == 16
-    # the same 96 rows over an fp16 cache: the dedicated kernel
+    # the same 96 rows over an fp16 cache: the prefill kernel too; 88 rows:
+    # the dedicated kernel
     d16 = _host_desc(B=1, H=2, cap=10496, off=10240, dtype=capi.RBQ_F16, **ptrs)
-    assert lib.rbq_quant_attn_splits(by(d16), 16, 12) == 16
-    assert lib.rbq_quant_attn_workspace_bytes(by(d16), 16, 12, 0) == 2 * 12 * 16 * rec
+    assert lib.rbq_quant_attn_splits(by(d16), 16, 12) == 40
+    assert lib.rbq_quant_attn_workspace_bytes(by(d16), 16, 12, 0) == 2 * 12 * 40 * rec
+    assert lib.rbq_quant_attn_splits(by(d16), 16, 11) == 16
     # head_dim 128, K4/V4, group 64, bf16: 2048-token chunk of 16 q heads / 2
     # (256 blocks of 128 rows): the prefill kernel, one split, no workspace
     d128 = _host_desc(B=1, H=2, cap=10496, off=10240, **ptrs)

@@ -214,19 +214,20 @@ def _lid(c):
         "_rr" if c[10] else "")
 
 
-def _layout_pair(dev, seed, D, vb, B, Hkv, T, rot_mode, rr, vscale=1.0):
+def _layout_pair(dev, seed, D, vb, B, Hkv, T, rot_mode, rr, vscale=1.0, dtype="bf16"):
+    tdt = W._TORCH_DTYPES[dtype]
     blocks = rot = None
     if rot_mode is not None:
         blocks = O.rotation_blocks(W.rotation_draws(seed, D), mode=rot_mode)
         if rr:
-            blocks = O.round_to_dtype(blocks, "bf16")
+            blocks = O.round_to_dtype(blocks, dtype)
         rot = rbq.build_block_so4(D, seed, dev, two_sided=rot_mode == "two_sided",
-                                  round_to=torch.bfloat16 if rr else None)
-    g = rbq.RotatedQuantKVCache(B, Hkv, device=dev, rot=rot, head_dim=D, group_size=64, k_bits=4,
-                                v_bits=vb, round_rotated=rr)
-    o = O.QuantKVCache(k_bits=4, v_bits=vb, dtype="bf16", group=64, round_rotated=rr)
-    k = W.random_rows([seed, 1], (B, Hkv, T, D), "bf16", "student_t3")
-    v = W.random_rows([seed, 2], (B, Hkv, T, D), "bf16", scale=vscale)
+                                  round_to=tdt if rr else None)
+    g = rbq.RotatedQuantKVCache(B, Hkv, dtype=tdt, device=dev, rot=rot, head_dim=D, group_size=64,
+                                k_bits=4, v_bits=vb, round_rotated=rr)
+    o = O.QuantKVCache(k_bits=4, v_bits=vb, dtype=dtype, group=64, round_rotated=rr)
+    k = W.random_rows([seed, 1], (B, Hkv, T, D), dtype, "student_t3")
+    v = W.random_rows([seed, 2], (B, Hkv, T, D), dtype, scale=vscale)
     g.append(k.to(dev), v.to(dev))
     o.append(k.float().numpy(), v.float().numpy(), blocks)
     return g, o, blocks
@@ -286,4 +287,77 @@ def test_prefill_other_layout_large_values(dev):
         got = out.cpu().numpy()
         assert np.isfinite(got).all()
         err = float(np.abs(got - want).max()) / 1e5
+        assert err <= ATOL, (splits, err)
+
+
+# fp16 caches (the scales and biases in fp16: V' and its exact residual for
+# every V width, the K biases as bf16 hi and lo parts in the bias product):
+# (head_dim, v_bits, B, H_q, H_kv, L, T0, causal, splits, rotation, rounded)
+FP16_CASES = [
+    (256, 3, 1, 16, 2, 16, 300, True, 1, "printed", False),   # the default layout
+    (256, 3, 2, 8, 2, 50, 700, True, 0, "two_sided", True),
+    (128, 4, 1, 16, 2, 16, 3000, True, 0, "two_sided", False),
+    (128, 2, 1, 16, 2, 12, 200, False, 3, "printed", False),
+    (64, 2, 1, 16, 2, 15, 338, True, 0, None, False),          # odd key count
+    (64, 3, 2, 8, 1, 20, 400, True, 1, "printed", True),
+]
+
+
+@pytest.mark.parametrize("case", FP16_CASES, ids=_lid)
+def test_prefill_fp16_caches(case, dev):
+    D, vb, B, Hq, Hkv, L, T0, causal, splits, rot_mode, rr = case
+    print(f"[prefill fp16] {_lid(case)}", flush=True)
+    g, o, blocks = _layout_pair(dev, 80, D, vb, B, Hkv, T0 + L, rot_mode, rr, dtype="f16")
+    q = W.random_rows([81, L], (B, Hq, L, D), "f16")
+    out = g.attend(q.to(dev), scale=D ** -0.5, causal=causal, splits=splits)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    want = O.attention(q.float().numpy(), o, D ** -0.5, causal, blocks)
+    err = float(np.abs(got - want).max())
+    assert err <= ATOL, err
+
+
+@pytest.mark.parametrize("kind", ["bool", "f32", "f16"])
+def test_prefill_fp16_masks(kind, dev):
+    D, vb, B, Hq, Hkv, L, T = 256, 3, 2, 16, 2, 16, 1333
+    print(f"[prefill fp16 mask] {kind}", flush=True)
+    g, o, blocks = _layout_pair(dev, 82, D, vb, B, Hkv, T, "printed", False, dtype="f16")
+    q = W.random_rows([83, 0], (B, Hq, L, D), "f16")
+    rng = np.random.default_rng(84)
+    if kind == "bool":
+        m = rng.random((B, Hq, L, T)) < 0.4
+        m[0, 3, 5, :] = False
+        m[1, :, 0, :] = False
+        md = torch.from_numpy(m)
+    else:
+        m = rng.normal(0.0, 2.0, size=(B, Hq, L, T)).astype(np.float32)
+        md = torch.from_numpy(m)
+        if kind == "f16":
+            md = md.to(torch.float16)
+            m = md.float().numpy()
+    for splits in (1, 0):
+        out = g.attend(q.to(dev), scale=D ** -0.5, causal=True, mask=md.to(dev), splits=splits)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.isfinite(got).all()
+        want = O.attention(q.float().numpy(), o, D ** -0.5, True, blocks, mask=m)
+        err = float(np.abs(got - want).max())
+        assert err <= ATOL, (splits, err)
+
+
+def test_prefill_fp16_large_values(dev):
+    # fp16 V values near the top of the fp16 range: scales and biases times
+    # the powers of two stay finite, the residual keeps code x scale exact
+    print("[prefill fp16] large V", flush=True)
+    D, vb, B, Hq, Hkv, L, T = 256, 3, 1, 16, 2, 16, 500
+    g, o, blocks = _layout_pair(dev, 85, D, vb, B, Hkv, T, "printed", False, vscale=1e4, dtype="f16")
+    q = W.random_rows([86, 0], (B, Hq, L, D), "f16")
+    want = O.attention(q.float().numpy(), o, D ** -0.5, True, blocks)
+    for splits in (1, 3):
+        out = g.attend(q.to(dev), scale=D ** -0.5, causal=True, splits=splits)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.isfinite(got).all()
+        err = float(np.abs(got - want).max()) / 1e4
         assert err <= ATOL, (splits, err)
