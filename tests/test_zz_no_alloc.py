@@ -58,18 +58,21 @@ def test_noalloc_matches_the_workspace_call_twice(D):
         assert float(np.abs(got.cpu().numpy() - ref).max()) <= ATOL
 
 
-def test_noalloc_prefill_kernel_records_then_a_smaller_call():
+@pytest.mark.parametrize("D", [256, 64])
+def test_noalloc_prefill_kernel_records_then_a_smaller_call(D):
     # 128 query rows per kv head (the prefill kernel) over few (b, kv head)
     # units: key splits whose records go to the array; then a call of 48
-    # rows (8-row blocks) whose records overwrite the first call's
+    # rows (8-row blocks at head_dim 256, the tile kernel at 64) whose records
+    # overwrite the first call's
     dev = torch.device("cuda:0")
-    print("[no-alloc attention] prefill kernel", flush=True)
-    blocks = O.rotation_blocks(W.rotation_draws(1, 256))
-    rot = rbq.build_block_so4(256, 1, dev)
+    print(f"[no-alloc attention] prefill kernel, head_dim {D}", flush=True)
+    cfg = {} if D == 256 else dict(head_dim=D, group_size=64, k_bits=4, v_bits=4)
+    blocks = O.rotation_blocks(W.rotation_draws(1, D))
+    rot = rbq.build_block_so4(D, 1, dev)
     shapes = [(1, 16, 2, 3000, 16), (1, 8, 2, 900, 12)]
     for n, (B, Hq, Hkv, T, L) in enumerate(shapes):
-        c, oc = _cache(dev, 95 + n, B, Hkv, T, blocks, rot)
-        q = W.random_rows([95 + n, 3], (B, Hq, L, 256), "bf16").to(dev)
+        c, oc = _cache(dev, 95 + n, B, Hkv, T, blocks, rot, **cfg)
+        q = W.random_rows([95 + n, 3], (B, Hq, L, D), "bf16").to(dev)
         assert capi.rbq_quant_attn_splits(c.desc, Hq, L) > 1
         need = capi.rbq_quant_attn_workspace_bytes(c.desc, Hq, L, 0)
         assert 0 < need <= capi.RBQ_SCRATCH_BYTES
