@@ -283,7 +283,7 @@ size_t rbq_quant_attn_workspace_bytes(const rbq_kv_cache* c, int32_t H_q, int32_
  * are read.  Any L from 1 (decode) to offset (prefill-length blocks) is
  * taken; L is the number of trailing cache rows the query block stands for.
  * Kernels: from 96 query rows per kv head (H_q / H_kv x L) over a bf16 or
- * fp16 cache with 4-bit K codes in groups of 64 (head_dim 64, 128 or 256, 2- to 4-bit
+ * fp16 cache with 4-bit K codes in groups of 64 or 128 (head_dim 64, 128 or 256, 2- to 4-bit
  * V codes) a prefill kernel (blocks of 128 query rows sharing each decoded
  * 32-key tile, key splits merged as for the dedicated kernel); otherwise
  * the default configuration (head_dim 256, group 64, K4/V3) runs a dedicated

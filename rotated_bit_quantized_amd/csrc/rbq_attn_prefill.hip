@@ -2,7 +2,7 @@
 // on the quant_kv.py page with many query rows per kv head: a prompt chunk
 // of L tokens attending to the cache and to itself, causal at the offset) on
 // the gfx950 matrix cores, for bf16 and fp16 caches with 4-bit K codes in
-// groups of 64 (head_dim 64, 128 or 256, 2- to 4-bit V codes).
+// groups of 64 or 128 (head_dim 64, 128 or 256, 2- to 4-bit V codes).
 //
 // Decomposition: one workgroup of 8 wave64s per (b, kv head, block of 128
 // query rows, key split); wave w takes rows 16 w .. 16 w + 15 of the block,
@@ -64,7 +64,7 @@ constexpr int kPRows = 16 * kPW;      // query rows per workgroup
 constexpr int kPTile = 32;            // keys per tile
 constexpr int64_t kPGridYZ = 65535;   // workgroups per grid dimension y or z of one launch
 constexpr float kPLog2e = 1.44269504088896340736f;
-// Layout of one configuration: head_dim D (64, 128 or 256), groups of 64 dims,
+// Layout of one configuration: head_dim D (64, 128 or 256), blocks of 64 dims,
 // 4-bit K codes, VB-bit V codes (2, 3 or 4).
 //   A raw buffer holds one tile as the memory holds it: K words (16-byte
 //   chunks of a key permuted, see k_chunk), V words, K scales, K biases, V
@@ -75,7 +75,7 @@ constexpr float kPLog2e = 1.44269504088896340736f;
 //   with fp16 caches also the K biases of both as bf16 hi and lo parts.
 template <int D, int VB, int DT>
 struct PCfg {
-    static constexpr int NG = D / 64;                     // groups of 64 dims
+    static constexpr int NG = D / 64;                     // blocks of 64 dims (groups of 64)
     static constexpr int NB = D / 16;                     // 16-dim output blocks
     static constexpr int CPK = D / 32;                    // 16-byte K chunks per key
     static constexpr int KPB = 512 / D;                   // keys per 256 bytes of K words
@@ -130,6 +130,7 @@ struct PArgs {
     int64_t capacity;
     int T, chunk, S, Hkv, n_rep, L, G, RB, RW, causal, round_rot;
     int rw0, bh0;  // first row block and (b, kv head) of this launch (grid y and z)
+    int gs_shift;  // log2(group / 64): groups of 64 (0) or 128 (1) dims
     float qscale;
 };
 
@@ -241,13 +242,19 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         t_lim = min(t_lim, T - a.L + imax + 1);
     }
     const int64_t row0 = (int64_t)bh * a.capacity;
+    // the kernel works in blocks of 64 dims (NG per row); the cache's scale
+    // and bias arrays hold NGS = NG >> gsh values per row, one per group of
+    // 64 << gsh dims, and block g takes value g >> gsh (a group of 128 dims is
+    // two blocks with its scale and bias: the same sums)
+    const int gsh = a.gs_shift;
+    const int NGS = NG >> gsh;
     const __amdgpu_buffer_rsrc_t kw_r = prsrc(a.kw + row0 * (D / 8), (uint32_t)T * (D / 2));
     const __amdgpu_buffer_rsrc_t vw_r = prsrc(a.vw + row0 * C::VWK, (uint32_t)T * (C::VWK * 4));
     __amdgpu_buffer_rsrc_t m_r[4];
-    m_r[0] = prsrc(a.ks + row0 * NG, (uint32_t)T * (2 * NG));
-    m_r[1] = prsrc(a.kb + row0 * NG, (uint32_t)T * (2 * NG));
-    m_r[2] = prsrc(a.vs + row0 * NG, (uint32_t)T * (2 * NG));
-    m_r[3] = prsrc(a.vb + row0 * NG, (uint32_t)T * (2 * NG));
+    m_r[0] = prsrc(a.ks + row0 * NGS, (uint32_t)T * (2 * NGS));
+    m_r[1] = prsrc(a.kb + row0 * NGS, (uint32_t)T * (2 * NGS));
+    m_r[2] = prsrc(a.vs + row0 * NGS, (uint32_t)T * (2 * NGS));
+    m_r[3] = prsrc(a.vb + row0 * NGS, (uint32_t)T * (2 * NGS));
 
     // Direct-to-LDS transfer of the tile at key t0 into raw buffer `buf` (lane
     // l of an instruction lands at offset + 16 l or 4 l): NI instructions,
@@ -271,7 +278,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             } else if (idx < C::NI) {
                 const int m = idx - C::KI - C::VI;
                 const uint32_t dst = (m == 0) ? C::RKs : (m == 1) ? C::RKb : (m == 2) ? C::RVs : C::RVb;
-                if (lane < 16 * NG) lds_dma4(m_r[m], buf + dst, t0 * (2 * NG) + 4 * lane);
+                if (lane < 16 * NGS) lds_dma4(m_r[m], buf + dst, t0 * (2 * NGS) + 4 * lane);
             }
         }
     };
@@ -308,8 +315,8 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int t = t_begin + tid; t < t_lim; t += kPT) {
 #pragma unroll
         for (int g = 0; g < NG; ++g)
-            vmx[g] = fmaxf(vmx[g], fmaxf(fabsf(elem_to_f32<DT>(a.vs[(row0 + t) * NG + g])),
-                                         fabsf(elem_to_f32<DT>(a.vb[(row0 + t) * NG + g]))));
+            vmx[g] = fmaxf(vmx[g], fmaxf(fabsf(elem_to_f32<DT>(a.vs[(row0 + t) * NGS + (g >> gsh)])),
+                                         fabsf(elem_to_f32<DT>(a.vb[(row0 + t) * NGS + (g >> gsh)]))));
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -457,8 +464,9 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // V' = code x scale x 2^F_g, exact in fp32; in fp16 exact for up to 3-bit
     // codes (8 + 3 significant bits); 4-bit codes keep the residual V'' =
     // V' - fp16(V') (exact) in a second array
-    // With one group per row (head_dim 64) the scale and bias arrays hold 2
-    // bytes per key, and the 4-byte transfers of a tile that ends at an odd
+    // With one group per row (head_dim 64, or 128 in groups of 128) the scale
+    // and bias arrays hold 2 bytes per key, and the 4-byte transfers of a tile
+    // that ends at an odd
     // key count T take the pair (T - 1, T) as one word outside the range:
     // it reads as zero, key T - 1's halves included.  The decode of that tile
     // takes key T - 1's four halves from memory instead and puts its K bias
@@ -466,7 +474,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto decode_tile = [&](const unsigned char* raw, const int db, const int t0) __attribute__((always_inline)) {
         constexpr int IPK = D / 16;  // items per key
         const int klast = T - 1 - t0;
-        const bool fix_last = NG == 1 && (T & 1) && klast >= 0 && klast < kPTile;
+        const bool fix_last = NGS == 1 && (T & 1) && klast >= 0 && klast < kPTile;
         const int64_t last = row0 + T - 1;  // (one group: element index = row)
 #pragma unroll
         for (int item = tid; item < 2 * D; item += kPT) {
@@ -477,7 +485,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const uint32_t w1 = lds_ld<uint32_t>(raw, C::RV + 4 * (C::VWK * k + wi + 1));
             const uint64_t bits = (((uint64_t)w1 << 32) | w0) >> sh;
             const uint32_t sv = (fix_last && k == klast) ? (uint32_t)a.vs[last]
-                                                         : lds_ld<uint16_t>(raw, C::RVs + 2 * (NG * k + g));
+                                                         : lds_ld<uint16_t>(raw, C::RVs + 2 * (NGS * k + (g >> gsh)));
             const float sf = elem_to_f32<DT>(sv) * lds_ld<float>(smem, C::OffUnit + 4 * g);
             constexpr uint32_t cm = (1u << VB) - 1u;
             uint32_t h[8], hl[8];
@@ -502,9 +510,9 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (wave < 2) {
             if (tid < kPTile * NG) {
                 const int kk = tid / NG, gg = tid % NG;
-                uint32_t sk = lds_ld<uint16_t>(raw, C::RKs + 2 * (NG * kk + gg));
+                uint32_t sk = lds_ld<uint16_t>(raw, C::RKs + 2 * (NGS * kk + (gg >> gsh)));
                 uint32_t bk = 0u;
-                if constexpr (DT == RBQ_F16) bk = lds_ld<uint16_t>(raw, C::RKb + 2 * (NG * kk + gg));
+                if constexpr (DT == RBQ_F16) bk = lds_ld<uint16_t>(raw, C::RKb + 2 * (NGS * kk + (gg >> gsh)));
                 if (fix_last && kk == klast) {
                     sk = a.ks[last];
                     bk = a.kb[last];
@@ -527,7 +535,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (tid - 128 < kPTile * NG) {
                 const int kk = (tid - 128) / NG, gg = (tid - 128) % NG;
                 const uint32_t b = (fix_last && kk == klast) ? (uint32_t)a.vb[last]
-                                                             : lds_ld<uint16_t>(raw, C::RVb + 2 * (NG * kk + gg));
+                                                             : lds_ld<uint16_t>(raw, C::RVb + 2 * (NGS * kk + (gg >> gsh)));
                 const float bu = elem_to_f32<DT>(b) * lds_ld<float>(smem, C::OffUnit + 4 * gg);
                 lds_st<uint16_t>(smem, C::OffVb + db * (NG * kPTile * 2) + 2 * (gg * kPTile + v_row(kk)),
                                  __builtin_bit_cast(uint16_t, (_Float16)bu));
@@ -612,10 +620,18 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     kbop = (pu32x4){lds_ld<uint32_t>(smem, kb2), 0u, 0u, 0u};
                 }
             } else if constexpr (NG == 4) {
-                const pu32x2 kbw = lds_ld<pu32x2>(raw, C::RKb + 8 * key);
-                kbop = (pu32x4){kbw[0], kbw[1], 0u, 0u};
+                if (gsh == 0) {
+                    const pu32x2 kbw = lds_ld<pu32x2>(raw, C::RKb + 8 * key);
+                    kbop = (pu32x4){kbw[0], kbw[1], 0u, 0u};
+                } else {  // two groups of 128: each half for both its blocks
+                    const uint32_t w = lds_ld<uint32_t>(raw, C::RKb + 4 * key);
+                    kbop = (pu32x4){(w & 0xFFFFu) * 0x10001u, (w >> 16) * 0x10001u, 0u, 0u};
+                }
             } else if constexpr (NG == 2) {
-                kbop = (pu32x4){lds_ld<uint32_t>(raw, C::RKb + 4 * key), 0u, 0u, 0u};
+                if (gsh == 0)
+                    kbop = (pu32x4){lds_ld<uint32_t>(raw, C::RKb + 4 * key), 0u, 0u, 0u};
+                else
+                    kbop = (pu32x4){(uint32_t)lds_ld<uint16_t>(raw, C::RKb + 2 * key) * 0x10001u, 0u, 0u, 0u};
             } else {
                 kbop = (pu32x4){(uint32_t)lds_ld<uint16_t>(raw, C::RKb + 2 * key), 0u, 0u, 0u};
             }
@@ -751,7 +767,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     y[i] = value_column_mean<DT>(a.vw, a.vs, a.vb, row0, nv, 16 * t + 4 * j + i,
-                                                       VB, C::VWK, NG, 64);
+                                                       VB, C::VWK, NGS, 64 << gsh);
             }
             float z[4] = {y[0], y[1], y[2], y[3]};
             if (rotated) {
@@ -817,7 +833,7 @@ static void launch_layout(const rbq_kv_cache* c, int mt, F&& launch) {
 bool prefill_takes(const rbq_kv_cache* c, int32_t H_q, int32_t L) {
     const int64_t G = (int64_t)(H_q / c->H_kv) * L;
     if (G < kPrefillMinRows || (c->dtype != RBQ_BF16 && c->dtype != RBQ_F16) || c->k_bits != 4 ||
-        c->group_size != 64 ||
+        (c->group_size != 64 && c->group_size != 128) || c->group_size > c->head_dim ||
         (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) || c->v_bits < 2 ||
         c->v_bits > 4)
         return false;
@@ -887,6 +903,7 @@ int prefill_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L,
     a.causal = causal ? 1 : 0;
     a.round_rot = (c->flags & RBQ_FLAG_ROUND_ROTATED) ? 1 : 0;
     a.qscale = scale * kPLog2e;
+    a.gs_shift = c->group_size == 128 ? 1 : 0;
     const int64_t BH = (int64_t)c->B * c->H_kv;
     const int mt = mk.ptr == nullptr ? RBQ_MASK_NONE : mk.type;
     auto launch = [&](auto kernel) {

@@ -85,7 +85,7 @@ void merge_launch(const rbq_kv_cache* c, const float* rec, const float* rot_bloc
                   int S, int RB, int n_rep, int L, int causal, int mask_type, void* stream);
 
 // Prefill-length attention over bf16 or fp16 caches with 4-bit K codes in groups of
-// 64 (head_dim 64, 128 or 256, V codes of 2 to 4 bits), blocks of 128 query rows
+// 64 or 128 (head_dim 64, 128 or 256, V codes of 2 to 4 bits), blocks of 128 query rows
 // per kv head sharing each decoded tile: used from kPrefillMinRows query rows
 // per kv head (prefill_takes), with any split count.
 constexpr int64_t kPrefillMinRows = 96;

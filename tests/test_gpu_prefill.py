@@ -182,7 +182,8 @@ def test_prefill_plan_is_used(dev):
     assert rbq.rbq_quant_attn_splits(g.desc, 16, 16) > 1
 
 
-# other layouts the prefill kernel takes (bf16, 4-bit K in groups of 64): one
+# other layouts the prefill kernel takes (bf16, 4-bit K in groups of 64; groups
+# of 128 and fp16 caches below): one
 # key split (outputs stored by the attention kernel), explicit and automatic
 # splits (records of head_dim 64, 128 or 256 merged by the merge kernel):
 # (head_dim, v_bits, B, H_q, H_kv, L, T0, causal, splits, rotation, rounded)
@@ -214,7 +215,7 @@ def _lid(c):
         "_rr" if c[10] else "")
 
 
-def _layout_pair(dev, seed, D, vb, B, Hkv, T, rot_mode, rr, vscale=1.0, dtype="bf16"):
+def _layout_pair(dev, seed, D, vb, B, Hkv, T, rot_mode, rr, vscale=1.0, dtype="bf16", group=64):
     tdt = W._TORCH_DTYPES[dtype]
     blocks = rot = None
     if rot_mode is not None:
@@ -223,9 +224,9 @@ def _layout_pair(dev, seed, D, vb, B, Hkv, T, rot_mode, rr, vscale=1.0, dtype="b
             blocks = O.round_to_dtype(blocks, dtype)
         rot = rbq.build_block_so4(D, seed, dev, two_sided=rot_mode == "two_sided",
                                   round_to=tdt if rr else None)
-    g = rbq.RotatedQuantKVCache(B, Hkv, dtype=tdt, device=dev, rot=rot, head_dim=D, group_size=64,
+    g = rbq.RotatedQuantKVCache(B, Hkv, dtype=tdt, device=dev, rot=rot, head_dim=D, group_size=group,
                                 k_bits=4, v_bits=vb, round_rotated=rr)
-    o = O.QuantKVCache(k_bits=4, v_bits=vb, dtype=dtype, group=64, round_rotated=rr)
+    o = O.QuantKVCache(k_bits=4, v_bits=vb, dtype=dtype, group=group, round_rotated=rr)
     k = W.random_rows([seed, 1], (B, Hkv, T, D), dtype, "student_t3")
     v = W.random_rows([seed, 2], (B, Hkv, T, D), dtype, scale=vscale)
     g.append(k.to(dev), v.to(dev))
@@ -360,4 +361,54 @@ def test_prefill_fp16_large_values(dev):
         got = out.cpu().numpy()
         assert np.isfinite(got).all()
         err = float(np.abs(got - want).max()) / 1e4
+        assert err <= ATOL, (splits, err)
+
+
+# groups of 128 dims (two 64-dim blocks of the kernel sharing a scale and a
+# bias): (head_dim, v_bits, dtype, B, H_q, H_kv, L, T0, causal, splits, rotation, rounded)
+G128_CASES = [
+    (256, 3, "bf16", 1, 16, 2, 16, 300, True, 1, "printed", False),
+    (256, 4, "bf16", 2, 8, 2, 50, 700, True, 0, "two_sided", True),
+    (128, 2, "bf16", 1, 16, 2, 15, 338, True, 0, "two_sided", False),   # odd key count, 2-byte scales
+    (128, 3, "f16", 1, 16, 2, 12, 201, False, 3, None, False),
+    (256, 2, "f16", 1, 16, 2, 16, 1001, True, 0, "printed", False),
+]
+
+
+def _gid(c):
+    return "D{}_v{}_{}_B{}_H{}-{}_L{}_T{}_{}_s{}_{}{}".format(
+        c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[7], "causal" if c[8] else "full", c[9],
+        c[10] or "norot", "_rr" if c[11] else "")
+
+
+@pytest.mark.parametrize("case", G128_CASES, ids=_gid)
+def test_prefill_groups_of_128(case, dev):
+    D, vb, dtype, B, Hq, Hkv, L, T0, causal, splits, rot_mode, rr = case
+    print(f"[prefill group 128] {_gid(case)}", flush=True)
+    g, o, blocks = _layout_pair(dev, 90, D, vb, B, Hkv, T0 + L, rot_mode, rr, dtype=dtype, group=128)
+    q = W.random_rows([91, L], (B, Hq, L, D), dtype)
+    out = g.attend(q.to(dev), scale=D ** -0.5, causal=causal, splits=splits)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    want = O.attention(q.float().numpy(), o, D ** -0.5, causal, blocks)
+    err = float(np.abs(got - want).max())
+    assert err <= ATOL, err
+
+
+def test_prefill_groups_of_128_bool_mask(dev):
+    D, vb, B, Hq, Hkv, L, T = 128, 4, 2, 16, 2, 16, 1333
+    print("[prefill group 128] boolean mask", flush=True)
+    g, o, blocks = _layout_pair(dev, 92, D, vb, B, Hkv, T, "two_sided", False, group=128)
+    q = W.random_rows([93, 0], (B, Hq, L, D), "bf16")
+    rng = np.random.default_rng(94)
+    m = rng.random((B, Hq, L, T)) < 0.4
+    m[0, 3, 5, :] = False
+    m[1, :, 0, :] = False
+    for splits in (1, 0):
+        out = g.attend(q.to(dev), scale=D ** -0.5, causal=True, mask=torch.from_numpy(m).to(dev),
+                       splits=splits)
+        torch.cuda.synchronize()
+        want = O.attention(q.float().numpy(), o, D ** -0.5, True, blocks, mask=m)
+        err = float(np.abs(out.cpu().numpy() - want).max())
         assert err <= ATOL, (splits, err)
