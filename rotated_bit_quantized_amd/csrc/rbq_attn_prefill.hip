@@ -130,7 +130,6 @@ struct PArgs {
     int64_t capacity;
     int T, chunk, S, Hkv, n_rep, L, G, RB, RW, causal, round_rot;
     int rw0, bh0;  // first row block and (b, kv head) of this launch (grid y and z)
-    int gs_shift;  // log2(group / 64): groups of 64 (0) or 128 (1) dims
     float qscale;
 };
 
@@ -215,7 +214,7 @@ __device__ __forceinline__ int k_chunk(int k, int c) {
 // (e < 4) or 16 + 4 j + e - 4 (e >= 4), the k-slot order of the P operand.
 __device__ __forceinline__ int v_row(int k) { return 8 * ((k & 15) >> 2) + (k & 3) + 4 * (k >> 4); }
 
-template <int MK, int D, int VB, int DT>
+template <int MK, int D, int VB, int DT, int GSH>
 __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_prefill_kernel(PArgs a) {
     using C = PCfg<D, VB, DT>;
     constexpr int NG = C::NG, NB = C::NB;
@@ -243,11 +242,12 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     const int64_t row0 = (int64_t)bh * a.capacity;
     // the kernel works in blocks of 64 dims (NG per row); the cache's scale
-    // and bias arrays hold NGS = NG >> gsh values per row, one per group of
-    // 64 << gsh dims, and block g takes value g >> gsh (a group of 128 dims is
+    // and bias arrays hold NGS = NG >> GSH values per row, one per group of
+    // 64 << GSH dims, and block g takes value g >> GSH (a group of 128 dims is
     // two blocks with its scale and bias: the same sums)
-    const int gsh = a.gs_shift;
-    const int NGS = NG >> gsh;
+    constexpr int gsh = GSH;
+    constexpr int NGS = NG >> gsh;
+    static_assert(NGS >= 1, "a group spans at most the head");
     const __amdgpu_buffer_rsrc_t kw_r = prsrc(a.kw + row0 * (D / 8), (uint32_t)T * (D / 2));
     const __amdgpu_buffer_rsrc_t vw_r = prsrc(a.vw + row0 * C::VWK, (uint32_t)T * (C::VWK * 4));
     __amdgpu_buffer_rsrc_t m_r[4];
@@ -620,7 +620,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     kbop = (pu32x4){lds_ld<uint32_t>(smem, kb2), 0u, 0u, 0u};
                 }
             } else if constexpr (NG == 4) {
-                if (gsh == 0) {
+                if constexpr (gsh == 0) {
                     const pu32x2 kbw = lds_ld<pu32x2>(raw, C::RKb + 8 * key);
                     kbop = (pu32x4){kbw[0], kbw[1], 0u, 0u};
                 } else {  // two groups of 128: each half for both its blocks
@@ -628,7 +628,7 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     kbop = (pu32x4){(w & 0xFFFFu) * 0x10001u, (w >> 16) * 0x10001u, 0u, 0u};
                 }
             } else if constexpr (NG == 2) {
-                if (gsh == 0)
+                if constexpr (gsh == 0)
                     kbop = (pu32x4){lds_ld<uint32_t>(raw, C::RKb + 4 * key), 0u, 0u, 0u};
                 else
                     kbop = (pu32x4){(uint32_t)lds_ld<uint16_t>(raw, C::RKb + 2 * key) * 0x10001u, 0u, 0u, 0u};
@@ -804,29 +804,34 @@ __global__ __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // The kernel of layout (D, VB) and cache dtype DT for mask type mt, handed
 // to `launch`.
-template <int D, int VB, int DT, typename F>
+template <int D, int VB, int DT, int GSH, typename F>
 static void launch_masked(int mt, F&& launch) {
-    if (mt == RBQ_MASK_NONE) launch(attn_prefill_kernel<RBQ_MASK_NONE, D, VB, DT>);
-    else if (mt == RBQ_MASK_BOOL) launch(attn_prefill_kernel<RBQ_MASK_BOOL, D, VB, DT>);
-    else if (mt == RBQ_MASK_ADD_F32) launch(attn_prefill_kernel<RBQ_MASK_ADD_F32, D, VB, DT>);
-    else launch(attn_prefill_kernel<RBQ_MASK_ADD_DTYPE, D, VB, DT>);
+    if (mt == RBQ_MASK_NONE) launch(attn_prefill_kernel<RBQ_MASK_NONE, D, VB, DT, GSH>);
+    else if (mt == RBQ_MASK_BOOL) launch(attn_prefill_kernel<RBQ_MASK_BOOL, D, VB, DT, GSH>);
+    else if (mt == RBQ_MASK_ADD_F32) launch(attn_prefill_kernel<RBQ_MASK_ADD_F32, D, VB, DT, GSH>);
+    else launch(attn_prefill_kernel<RBQ_MASK_ADD_DTYPE, D, VB, DT, GSH>);
 }
 
-// The kernel of the cache's head_dim and V width, for cache dtype DT.
+// The kernel of V width VB and group shift GSH (groups of 64 << GSH dims).
+template <int D, int DT, int GSH, typename F>
+static void launch_width(const rbq_kv_cache* c, int mt, F&& launch) {
+    if (c->v_bits == 3) launch_masked<D, 3, DT, GSH>(mt, launch);
+    else if (c->v_bits == 4) launch_masked<D, 4, DT, GSH>(mt, launch);
+    else launch_masked<D, 2, DT, GSH>(mt, launch);
+}
+
+// The kernel of the cache's head_dim, group size and V width, for cache dtype DT.
 template <int DT, typename F>
 static void launch_layout(const rbq_kv_cache* c, int mt, F&& launch) {
+    const bool g128 = c->group_size == 128;
     if (c->head_dim == 256) {
-        if (c->v_bits == 3) launch_masked<256, 3, DT>(mt, launch);
-        else if (c->v_bits == 4) launch_masked<256, 4, DT>(mt, launch);
-        else launch_masked<256, 2, DT>(mt, launch);
+        if (g128) launch_width<256, DT, 1>(c, mt, launch);
+        else launch_width<256, DT, 0>(c, mt, launch);
     } else if (c->head_dim == 128) {
-        if (c->v_bits == 3) launch_masked<128, 3, DT>(mt, launch);
-        else if (c->v_bits == 4) launch_masked<128, 4, DT>(mt, launch);
-        else launch_masked<128, 2, DT>(mt, launch);
-    } else {
-        if (c->v_bits == 3) launch_masked<64, 3, DT>(mt, launch);
-        else if (c->v_bits == 4) launch_masked<64, 4, DT>(mt, launch);
-        else launch_masked<64, 2, DT>(mt, launch);
+        if (g128) launch_width<128, DT, 1>(c, mt, launch);
+        else launch_width<128, DT, 0>(c, mt, launch);
+    } else {  // groups of 128 dims exceed a head of 64: not taken
+        launch_width<64, DT, 0>(c, mt, launch);
     }
 }
 
@@ -903,7 +908,6 @@ int prefill_launch(const rbq_kv_cache* c, const void* q, int32_t H_q, int32_t L,
     a.causal = causal ? 1 : 0;
     a.round_rot = (c->flags & RBQ_FLAG_ROUND_ROTATED) ? 1 : 0;
     a.qscale = scale * kPLog2e;
-    a.gs_shift = c->group_size == 128 ? 1 : 0;
     const int64_t BH = (int64_t)c->B * c->H_kv;
     const int mt = mk.ptr == nullptr ? RBQ_MASK_NONE : mk.type;
     auto launch = [&](auto kernel) {
