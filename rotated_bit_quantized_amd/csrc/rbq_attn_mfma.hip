@@ -77,8 +77,8 @@ constexpr int kRows = 8;                                   // query rows per kv 
 // [256 columns][8 rows]
 constexpr int kRecFloats = kRecordFloats;
 static_assert(kRecFloats == 2 * kRows + kRows * kHeadDim, "split record layout");
-constexpr int kMergeNarrowUnits = 64;
-constexpr int64_t kGridYZ = 65535;  // workgroups per grid dimension y or z of one launch  // below this many units the merge takes 32-column blocks
+constexpr int kMergeNarrowUnits = 64;  // below this many units the merge takes 32-column blocks
+constexpr int64_t kGridYZ = 65535;      // workgroups per grid dimension y or z of one launch
 // wave record in LDS, in its own region so that a wave stores it as soon as
 // its tiles are done: o column-major [256 columns][2 row quads][4 rows], the
 // row quad of column c stored at slot quad ^ ((c >> 3) & 1) (conflict-free

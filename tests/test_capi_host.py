@@ -368,7 +368,7 @@ def test_status_strings():
 
 def test_prefill_plan_selection():
     """Which plan a call gets: from 96 query rows per kv head over a bf16 or
-    fp16 cache with 4-bit K in groups of 64 the prefill kernel's (128-row
+    fp16 cache with 4-bit K in groups of 64 or 128 the prefill kernel's (128-row
     blocks, split records of 8 rows at head_dim 256, 128 and 64); below that
     the dedicated kernel's (8-row blocks, a multiple of 8 splits with several
     row blocks); other widths the tile kernel's."""
@@ -404,6 +404,21 @@ def test_prefill_plan_selection():
     assert lib.rbq_quant_attn_splits(by(d128), 16, 32) == 40
     assert lib.rbq_quant_attn_workspace_bytes(by(d128), 16, 32, 0) == 2 * 32 * 40 * rec128
     assert lib.rbq_quant_attn_workspace_bytes(by(d128), 16, 32, 1) == 0
+    # groups of 128 dims: the prefill kernel from 96 rows (same splits and
+    # records as groups of 64), the tile kernel below (the dedicated kernel
+    # takes groups of 64 only); groups of 32: the tile kernel at any row count
+    g128 = _host_desc(B=1, H=2, cap=10496, off=10240, **ptrs)
+    g128.group_size = 128
+    assert lib.rbq_quant_attn_splits(by(g128), 16, 12) == 40
+    assert lib.rbq_quant_attn_workspace_bytes(by(g128), 16, 12, 0) == 2 * 12 * 40 * rec
+    assert lib.rbq_quant_attn_splits(by(g128), 16, 11) not in (16, 40)
+    assert lib.rbq_quant_attn_splits(by(g128), 16, 2048) == 1
+    g32 = _host_desc(B=1, H=2, cap=10496, off=10240, **ptrs)
+    g32.group_size = 32
+    assert lib.rbq_quant_attn_splits(by(g32), 16, 12) == lib.rbq_quant_attn_splits(by(g128), 16, 11)
+    # a group of 128 over a head of 64: a layout not built
+    g128.head_dim = 64
+    assert lib.rbq_quant_attn_splits(by(g128), 16, 12) == capi.RBQ_EUNSUPPORTED
     # 5-bit K codes: the tile kernel
     d5 = _host_desc(B=1, H=2, cap=10496, off=10240, **ptrs)
     d5.head_dim, d5.k_bits, d5.v_bits = 128, 5, 4

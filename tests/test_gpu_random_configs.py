@@ -6,7 +6,8 @@ against the oracle and the attention within 2e-3 of it.  The draws reach
 every attention kernel (the dedicated 8-row blocks, the tile kernel's
 single-wave, paired-row, register-staged and four-wave shapes, the prefill
 kernel) with shapes no hand-written case picked; a few draws are steered
-to 96 or more rows per kv head so that the prefill kernel takes them.  Also
+to 96 or more rows per kv head, 4-bit K and groups of 64 or 128 so that the
+prefill kernel takes them (bf16 or fp16, any head_dim).  Also
 seeded random sequences of cache operations (appends, trims, attention
 calls, one-call decoding steps, snapshots and restores), the cache compared
 with the oracle's after every operation.
@@ -35,12 +36,12 @@ def _draw(i):
     prefill = i % 8 == 7
     D = int(rng.choice([64, 128, 256]))
     groups = [g for g in (32, 64, 128) if g <= D]
-    gs = int(rng.choice(groups)) if not prefill else 64
+    gs = int(rng.choice(groups)) if not prefill else int(rng.choice([g for g in (64, 128) if g <= D]))
     kb = int(rng.choice(BITS)) if not prefill else 4
     vb = int(rng.choice(BITS)) if not prefill else int(rng.choice([2, 3, 4]))
     if not prefill and rng.random() < 0.3:
         D, gs, kb, vb = 256, 64, 4, 3  # the default layout now and then
-    dtype = "bf16" if prefill else str(rng.choice(["bf16", "f16"]))
+    dtype = str(rng.choice(["bf16", "f16"]))
     two = bool(rng.random() < 0.4)
     rr = bool(rng.random() < 0.25)
     B = int(rng.integers(1, 3))
