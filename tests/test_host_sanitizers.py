@@ -6,6 +6,7 @@ code only) and driven with extreme shapes and strides, with no GPU visible
 launch and nothing runs on a device)
 (``tests/sanitize/rbq_host_sanitize.cpp``).  A sanitizer report aborts the
 driver; the test needs its exit status 0."""
+import concurrent.futures
 import os
 import subprocess
 
@@ -36,14 +37,16 @@ def test_host_code_under_asan_and_ubsan(tmp_path):
           "-o", o])
     objs.append(o)
     # the HIP sources with each sanitizer flag for the host pass only (the
-    # device code is built as usual; the driver runs with no visible GPU)
+    # device code is built as usual; the driver runs with no visible GPU);
+    # the four compiles side by side
     host_san = [x for f in SAN for x in ("-Xarch_host", f)]
-    for src in ("rbq_append.hip", "rbq_attn_mfma.hip", "rbq_attn_prefill.hip", "rbq_attn_tile.hip"):
-        o = str(tmp_path / (src + ".o"))
-        _run([HIPCC, "--offload-arch=gfx950", "-std=c++17", "-O1", "-g", *host_san, *inc,
-              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-c",
-              os.path.join(CSRC, src), "-o", o])
-        objs.append(o)
+    srcs = ("rbq_append.hip", "rbq_attn_mfma.hip", "rbq_attn_prefill.hip", "rbq_attn_tile.hip")
+    cmds = [[HIPCC, "--offload-arch=gfx950", "-std=c++17", "-O1", "-g",
+             *host_san, *inc, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-c",
+             os.path.join(CSRC, src), "-o", str(tmp_path / (src + ".o"))] for src in srcs]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as pool:
+        list(pool.map(_run, cmds))
+    objs += [str(tmp_path / (src + ".o")) for src in srcs]
     drv = os.path.join(ROOT, "tests", "sanitize", "rbq_host_sanitize.cpp")
     exe = str(tmp_path / "rbq_host_sanitize")
     _run([CLANGXX, "-std=c++17", "-O1", "-g", *SAN, *inc, drv, *objs, "-o", exe,
